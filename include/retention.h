@@ -1,0 +1,145 @@
+/*
+ * retention.h -- C ABI of libretention, the MI355X (gfx950) library for
+ * chunkwise causal retention, its recurrent decode step and causal linear
+ * attention with the elu+1 feature map.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major, last index fastest:
+ *      q, k      [B][H][T][dk]        v, out    [B][H][T][dv]
+ *      state     [B][H][dk][dv]       (rows index key features, columns value
+ *                                      dimensions; always fp32)
+ *    Device pointers must be 16-byte aligned.
+ *  - dtype is RET_F32 or RET_BF16 and applies to q, k, v and out.  Products
+ *    accumulate in fp32 and the state is fp32; out is rounded once, to
+ *    nearest even, on store.
+ *  - gamma is a HOST array of H floats, read during the call; each value must
+ *    lie in (0, 1].  gamma = 1 is plain (unnormalised) causal linear
+ *    attention with the identity feature map.
+ *  - stream is a hipStream_t (passed as void*); NULL means the default
+ *    stream.  Calls are asynchronous: they enqueue kernels on the stream and
+ *    return.  Results are visible after the stream is synchronised.
+ *  - Ownership: the caller allocates and owns every buffer.  The library
+ *    allocates no device memory and keeps no pointer after the call returns.
+ *  - Errors: the return value is RET_OK (0) or a negative RET_ERR_* code.
+ *    Argument errors are detected on the host before anything is enqueued, so
+ *    a failed call has no effect.  RET_ERR_HIP reports a failed launch.  A
+ *    human-readable message for the last error of the calling thread is
+ *    returned by retention_last_error().  Inputs are never modified (except
+ *    state in retention_decode_step, which is updated in place).
+ *
+ * Sources (page title, then passage):
+ *   "RetNet" (bembew.net): the single-head definition O = (Q K^T (.) D) V with
+ *       D_nm = gamma^(n-m) for n >= m; "Recurrent Representation"
+ *       (S_n = gamma S_{n-1} + K_n^T V_n, O_n = Q_n S_n); "Chunked Recurrent
+ *       Representation"; "Multi-Scale Retention" (one gamma per head).
+ *   "Efficient and Sparse Transformers" (temporalbook 12.5), section 6: the
+ *       parallel, recurrent and chunkwise forms; gamma = 1 as linear attention.
+ *   "Linear attention" (zerotofrontier 21.2): box "Causal linear attention,
+ *       recurrent form" (S, z, eps) and the decode-step interface.
+ */
+#ifndef RETENTION_H
+#define RETENTION_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RET_ABI_VERSION 1
+
+/* element types of q, k, v, out */
+#define RET_F32 0
+#define RET_BF16 1
+
+/* feature maps for linear_attn_fwd */
+#define RET_PHI_ELU1 1 /* phi(x) = x + 1 for x > 0, e^x otherwise */
+
+/* return codes */
+#define RET_OK 0
+#define RET_ERR_NULL (-1)      /* a required pointer is NULL */
+#define RET_ERR_SHAPE (-2)     /* unsupported or inconsistent sizes */
+#define RET_ERR_DTYPE (-3)     /* unknown dtype */
+#define RET_ERR_CHUNK (-4)     /* unsupported chunk length */
+#define RET_ERR_GAMMA (-5)     /* a decay value outside (0, 1] or not finite */
+#define RET_ERR_PHI (-6)       /* unknown feature map */
+#define RET_ERR_ALIGN (-7)     /* a device pointer is not 16-byte aligned */
+#define RET_ERR_ALIAS (-8)     /* an output overlaps an input or another output */
+#define RET_ERR_HIP (-10)      /* the HIP runtime rejected a launch */
+
+/*
+ * retention_fwd -- causal retention over whole sequences, chunkwise form,
+ * from a zero initial state.
+ *
+ *   out[b,h,t,:] = sum_{s<=t} gamma[h]^(t-s) (q[b,h,t,:] . k[b,h,s,:]) v[b,h,s,:]
+ *
+ * ("RetNet", single-head definition and "Chunked Recurrent Representation";
+ * "Efficient and Sparse Transformers", section 6, "Chunkwise form".)  Inside a
+ * chunk of `chunk` tokens the masked, decayed Q K^T V is computed in parallel;
+ * across chunks a fp32 dk x dv state per (b, h) is carried with
+ * S <- gamma^c S + (K (.) zeta)^T V.  The result does not depend on `chunk`
+ * beyond rounding.
+ *
+ *   q, k, v      device, [B][H][T][dk|dv], dtype
+ *   gamma        host, H floats in (0, 1]
+ *   chunk        64 or 128
+ *   out          device, [B][H][T][dv], dtype (written)
+ *   final_state  device, [B][H][dk][dv] fp32, the state after token T-1
+ *                (written); may be NULL.  T = 0 writes zeros.
+ *   dk, dv       each 64 or 128; dv must be a multiple of 16
+ *   T            >= 0, any value (a short last chunk is handled exactly)
+ */
+int retention_fwd(const void *q, const void *k, const void *v, const float *gamma,
+                  int chunk, void *out, float *final_state, int B, int H, int T,
+                  int dk, int dv, int dtype, void *stream);
+
+/*
+ * retention_decode_step -- one recurrent step for N sequences x H heads,
+ * updating state in place, then reading the output from the updated state:
+ *
+ *   S <- gamma[h] S + k v^T,   out = q S
+ *
+ * ("RetNet", "Recurrent Representation"; "Efficient and Sparse
+ * Transformers", section 6, recurrent form and its minimal recurrent step.)
+ *
+ *   q, k    device, [N][H][dk], dtype       v, out  device, [N][H][dv], dtype
+ *   state   device, [N][H][dk][dv] fp32, read and written in place
+ *   gamma   host, H floats in (0, 1]
+ *   dk, dv  each 64 or 128
+ */
+int retention_decode_step(const void *q, const void *k, const void *v,
+                          const float *gamma, float *state, void *out, int N, int H,
+                          int dk, int dv, int dtype, void *stream);
+
+/*
+ * linear_attn_fwd -- causal linear attention with a positive feature map and
+ * its normaliser, chunkwise (internal chunk 128):
+ *
+ *   S_t = S_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t),
+ *   out_t = S_t^T phi(q_t) / (z_t^T phi(q_t) + eps)
+ *
+ * ("Linear attention", box "Causal linear attention, recurrent form", and
+ * theorem "Recurrent and parallel forms agree".)  Zero initial S and z.
+ *
+ *   q, k, v  device, [B][H][T][dk|dv], dtype     out  device, [B][H][T][dv]
+ *   phi      RET_PHI_ELU1
+ *   eps      >= 0 (the pages use 1e-6)
+ *   dk, dv   each 64 or 128; T >= 0
+ */
+int linear_attn_fwd(const void *q, const void *k, const void *v, int phi, void *out,
+                    int B, int H, int T, int dk, int dv, int dtype, float eps,
+                    void *stream);
+
+/* Message describing the last error returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next call on that thread. */
+const char *retention_last_error(void);
+
+/* RET_ABI_VERSION of the loaded library. */
+int retention_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RETENTION_H */

@@ -1,1 +1,204 @@
-"""MI355X-native chunkwise retention / causal linear attention (placeholder)."""
+"""MI355X-native chunkwise retention and causal linear attention.
+
+Thin Python binding over ``libretention.so`` (C ABI in ``include/retention.h``).
+This module only marshals arguments: it checks that tensors are CUDA (HIP)
+tensors of the right dtype and layout, allocates outputs with PyTorch when the
+caller does not pass them, and hands raw device pointers plus the current HIP
+stream to the library.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback path.  If the library is not built, every
+call raises.
+
+Functions
+---------
+retention_fwd(q, k, v, gamma, chunk=64)        -> (out, final_state)
+retention_decode_step(q, k, v, gamma, state)   -> out      (state updated in place)
+linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+import torch
+
+__all__ = ["retention_fwd", "retention_decode_step", "linear_attn_fwd", "RetentionError",
+           "library_path", "load_library", "abi_version", "last_error"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libretention.so")
+_lock = threading.Lock()
+_lib = None
+
+RET_F32 = 0
+RET_BF16 = 1
+RET_PHI_ELU1 = 1
+ERRORS = {
+    -1: "RET_ERR_NULL", -2: "RET_ERR_SHAPE", -3: "RET_ERR_DTYPE", -4: "RET_ERR_CHUNK",
+    -5: "RET_ERR_GAMMA", -6: "RET_ERR_PHI", -7: "RET_ERR_ALIGN", -8: "RET_ERR_ALIAS",
+    -10: "RET_ERR_HIP",
+}
+MAX_HEADS = 256
+
+
+class RetentionError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {message}")
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libretention.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is missing: build it with `python -m retention_chunkwise_amd._build` "
+                    "(or __graft_entry__.build()); there is no non-HIP fallback")
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, fp, i = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int
+            lib.retention_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp]
+            lib.retention_fwd.restype = i
+            lib.retention_decode_step.argtypes = [vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp]
+            lib.retention_decode_step.restype = i
+            lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp]
+            lib.linear_attn_fwd.restype = i
+            lib.retention_last_error.argtypes = []
+            lib.retention_last_error.restype = ctypes.c_char_p
+            lib.retention_abi_version.argtypes = []
+            lib.retention_abi_version.restype = i
+            _lib = lib
+        return _lib
+
+
+def abi_version() -> int:
+    return int(load_library().retention_abi_version())
+
+
+def last_error() -> str:
+    return load_library().retention_last_error().decode()
+
+
+def _raise(rc: int):
+    if rc != 0:
+        raise RetentionError(rc, last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return RET_F32
+    if t.dtype == torch.bfloat16:
+        return RET_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _check_dev(name: str, t: torch.Tensor, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+def _gamma_array(gamma, H: int):
+    g = np.ascontiguousarray(np.asarray(
+        gamma.detach().cpu().numpy() if isinstance(gamma, torch.Tensor) else gamma,
+        dtype=np.float32).reshape(-1))
+    if g.size == 1 and H > 1:
+        g = np.full(H, g[0], dtype=np.float32)
+    if g.size != H:
+        raise ValueError(f"gamma must have {H} entries (got {g.size})")
+    return (ctypes.c_float * H)(*g.tolist())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
+                  want_state: bool = True):
+    """Chunkwise causal retention from a zero initial state.
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv] (float32 or bfloat16, same dtype, on the
+    GPU); gamma: H decay values in (0, 1].  Returns (out, final_state) with
+    out [B,H,T,dv] in the input dtype and final_state [B,H,dk,dv] float32
+    (None if want_state is False and none was passed).
+    """
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, v.dtype)
+    if final_state is None and want_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+    g = _gamma_array(gamma, H)
+    rc = lib.retention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), out.data_ptr(),
+                           final_state.data_ptr() if final_state is not None else None,
+                           B, H, T, dk, dv, _dtype_code(q), _stream(q))
+    _raise(rc)
+    return out, final_state
+
+
+def retention_decode_step(q, k, v, gamma, state, out=None):
+    """One recurrent step S <- gamma S + k v^T, out = q S, state updated in place.
+
+    q, k: [N,H,dk]; v: [N,H,dv] (float32 or bfloat16); state: [N,H,dk,dv]
+    float32.  Returns out [N,H,dv] in the input dtype.
+    """
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("state", state, torch.float32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [N,H,dk] and v [N,H,dv]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if tuple(state.shape) != (N, H, dk, dv):
+        raise ValueError("state must be [N,H,dk,dv]")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, v.dtype)
+    g = _gamma_array(gamma, H)
+    rc = lib.retention_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, state.data_ptr(),
+                                   out.data_ptr(), N, H, dk, dv, _dtype_code(q), _stream(q))
+    _raise(rc)
+    return out
+
+
+def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None):
+    """Causal linear attention with phi = elu+1 and its normaliser.
+
+    q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv].
+    """
+    lib = load_library()
+    if phi not in ("elu1", RET_PHI_ELU1):
+        raise ValueError("phi must be 'elu1'")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, v.dtype)
+    rc = lib.linear_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), RET_PHI_ELU1, out.data_ptr(),
+                             B, H, T, dk, dv, _dtype_code(q), float(eps), _stream(q))
+    _raise(rc)
+    return out

@@ -1,0 +1,200 @@
+// capi.hip -- the extern "C" entry points of libretention (include/retention.h).
+//
+// Every argument is validated on the host before anything is enqueued, so a
+// rejected call has no side effect.  No entry point allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/retention.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return RET_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const char* name;
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(const Range& a, const Range& b) {
+    return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo;
+}
+
+Range range(const char* name, const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{name, lo, lo + bytes};
+}
+
+int dtype_size(int dtype) {
+    if (dtype == RET_F32) return 4;
+    if (dtype == RET_BF16) return 2;
+    return 0;
+}
+
+// product of non-negative factors; false on overflow of size_t
+bool mul_ok(size_t& acc, long long f) {
+    if (f < 0) return false;
+    if (f != 0 && acc > SIZE_MAX / static_cast<size_t>(f)) return false;
+    acc *= static_cast<size_t>(f);
+    return true;
+}
+
+int check_gamma(const float* gamma, int H, float* log2g) {
+    for (int h = 0; h < H; ++h) {
+        const float g = gamma[h];
+        if (!(g > 0.f && g <= 1.f))  // also rejects NaN
+            return fail(RET_ERR_GAMMA, "gamma[%d] = %g is outside (0, 1]", h, static_cast<double>(g));
+        if (log2g) log2g[h] = static_cast<float>(log2(static_cast<double>(g)));
+    }
+    return RET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* retention_last_error(void) { return g_err; }
+
+int retention_abi_version(void) { return RET_ABI_VERSION; }
+
+int retention_fwd(const void* q, const void* k, const void* v, const float* gamma, int chunk,
+                  void* out, float* final_state, int B, int H, int T, int dk, int dv, int dtype,
+                  void* stream) {
+    if (!gamma) return fail(RET_ERR_NULL, "retention_fwd: gamma must be non-NULL");
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "retention_fwd: unknown dtype %d", dtype);
+    if (chunk != 64 && chunk != 128)
+        return fail(RET_ERR_CHUNK, "retention_fwd: chunk must be 64 or 128 (got %d)", chunk);
+    if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
+        return fail(RET_ERR_SHAPE, "retention_fwd: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)",
+                    ret::kMaxHeads, B, H, T);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "retention_fwd: dk and dv must each be 64 or 128 (got %d, %d)", dk, dv);
+    size_t nqk = esz, nv = esz, ns = 4;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv) ||
+        !mul_ok(ns, B) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
+        return fail(RET_ERR_SHAPE, "retention_fwd: tensor sizes overflow");
+    if (nqk > 0 && (!q || !k || !v || !out))
+        return fail(RET_ERR_NULL, "retention_fwd: q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (final_state && !aligned16(final_state)))
+        return fail(RET_ERR_ALIGN, "retention_fwd: device pointers must be 16-byte aligned");
+    ret::WalkArgs a{};
+    int rc = check_gamma(gamma, H, a.log2g);
+    if (rc) return rc;
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
+    const Range ro = range("out", out, nv);
+    for (const Range& in : {rq, rk, rv})
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "retention_fwd: out overlaps %s", in.name);
+    if (final_state) {
+        const Range rs = range("final_state", final_state, ns);
+        for (const Range& in : {rq, rk, rv, ro})
+            if (overlap(rs, in)) return fail(RET_ERR_ALIAS, "retention_fwd: final_state overlaps %s", in.name);
+    }
+    if (B == 0) return ok();
+    const long long bh = static_cast<long long>(B) * H;
+    const int nt = ret::choose_walk_nt(bh, dv, 256);
+    a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = final_state;
+    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = 0.f;
+    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, chunk, dk, nt, false,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int retention_decode_step(const void* q, const void* k, const void* v, const float* gamma,
+                          float* state, void* out, int N, int H, int dk, int dv, int dtype,
+                          void* stream) {
+    if (!gamma) return fail(RET_ERR_NULL, "retention_decode_step: gamma must be non-NULL");
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "retention_decode_step: unknown dtype %d", dtype);
+    if (N < 0 || H < 1 || H > ret::kMaxHeads)
+        return fail(RET_ERR_SHAPE, "retention_decode_step: need N >= 0, 1 <= H <= %d (got N=%d H=%d)",
+                    ret::kMaxHeads, N, H);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "retention_decode_step: dk and dv must each be 64 or 128 (got %d, %d)", dk, dv);
+    size_t nqk = esz, nv = esz, ns = 4;
+    if (!mul_ok(nqk, N) || !mul_ok(nqk, H) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, N) || !mul_ok(nv, H) || !mul_ok(nv, dv) ||
+        !mul_ok(ns, N) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
+        return fail(RET_ERR_SHAPE, "retention_decode_step: tensor sizes overflow");
+    if (nqk > 0 && (!q || !k || !v || !state || !out))
+        return fail(RET_ERR_NULL, "retention_decode_step: q, k, v, state and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(out))
+        return fail(RET_ERR_ALIGN, "retention_decode_step: device pointers must be 16-byte aligned");
+    ret::DecodeArgs a{};
+    int rc = check_gamma(gamma, H, nullptr);
+    if (rc) return rc;
+    for (int h = 0; h < H; ++h) a.gamma[h] = gamma[h];
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
+    const Range rs = range("state", state, ns), ro = range("out", out, nv);
+    for (const Range& in : {rq, rk, rv}) {
+        if (overlap(rs, in)) return fail(RET_ERR_ALIAS, "retention_decode_step: state overlaps %s", in.name);
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "retention_decode_step: out overlaps %s", in.name);
+    }
+    if (overlap(ro, rs)) return fail(RET_ERR_ALIAS, "retention_decode_step: out overlaps state");
+    if (N == 0) return ok();
+    a.q = q; a.k = k; a.v = v; a.state = state; a.out = out; a.N = N; a.H = H;
+    const hipError_t e = ret::launch_decode(a, dtype == RET_BF16, dk, dv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(RET_ERR_HIP, "retention_decode_step: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int linear_attn_fwd(const void* q, const void* k, const void* v, int phi, void* out, int B, int H,
+                    int T, int dk, int dv, int dtype, float eps, void* stream) {
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "linear_attn_fwd: unknown dtype %d", dtype);
+    if (phi != RET_PHI_ELU1) return fail(RET_ERR_PHI, "linear_attn_fwd: unknown feature map %d", phi);
+    if (!(eps >= 0.f) || isinf(eps))
+        return fail(RET_ERR_SHAPE, "linear_attn_fwd: eps must be finite and >= 0");
+    if (B < 0 || T < 0 || H < 1)
+        return fail(RET_ERR_SHAPE, "linear_attn_fwd: need B >= 0, T >= 0, H >= 1 (got B=%d H=%d T=%d)", B, H, T);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "linear_attn_fwd: dk and dv must each be 64 or 128 (got %d, %d)", dk, dv);
+    size_t nqk = esz, nv = esz;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv))
+        return fail(RET_ERR_SHAPE, "linear_attn_fwd: tensor sizes overflow");
+    if (nqk > 0 && (!q || !k || !v || !out))
+        return fail(RET_ERR_NULL, "linear_attn_fwd: q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(RET_ERR_ALIGN, "linear_attn_fwd: device pointers must be 16-byte aligned");
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
+    const Range ro = range("out", out, nv);
+    for (const Range& in : {rq, rk, rv})
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "linear_attn_fwd: out overlaps %s", in.name);
+    if (B == 0) return ok();
+    ret::WalkArgs a{};
+    const long long bh = static_cast<long long>(B) * H;
+    const int nt = ret::choose_walk_nt(bh, dv, 256);
+    a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = nullptr;
+    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = eps;
+    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, 128, dk, nt, true,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(RET_ERR_HIP, "linear_attn_fwd: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host (CPU only: no call here reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import retention_chunkwise_amd as rc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "retention.h")
+
+
+def _lib():
+    if not os.path.exists(rc.library_path()):
+        pytest.skip("libretention.so not built (run __graft_entry__.build())")
+    return rc.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_three_entry_points():
+    names = _declared_functions()
+    for n in ("retention_fwd", "retention_decode_step", "linear_attn_fwd",
+              "retention_last_error", "retention_abi_version"):
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), f"libretention.so does not export {name}"
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define RET_ABI_VERSION (\d+)", text).group(1))
+    assert rc.abi_version() == ver if os.path.exists(rc.library_path()) else True
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((m.group(1), int(m.group(2))) for m in
+                  re.finditer(r"#define (RET_\w+) \(?(-?\d+)\)?", text))
+    assert consts["RET_F32"] == rc.RET_F32 and consts["RET_BF16"] == rc.RET_BF16
+    assert consts["RET_PHI_ELU1"] == rc.RET_PHI_ELU1
+    for code, name in rc.ERRORS.items():
+        assert consts[name] == code
+
+
+# ---------------------------------------------------------------- validation
+FAKE = 0x10000  # a 16-byte aligned address; never dereferenced: validation fails first
+
+
+def _gam(vals):
+    return (ctypes.c_float * len(vals))(*vals)
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9, 0.9]), chunk=64, out=FAKE * 4,
+             fs=None, B=1, H=2, T=16, dk=64, dv=64, dtype=rc.RET_F32)
+    a.update(kw)
+    return lib.retention_fwd(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["out"], a["fs"],
+                             a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(gamma=None), -1),
+    (dict(dtype=7), -3),
+    (dict(chunk=96), -4),
+    (dict(chunk=0), -4),
+    (dict(dk=96), -2),
+    (dict(dv=32), -2),
+    (dict(H=0), -2),
+    (dict(B=-1), -2),
+    (dict(T=-5), -2),
+    (dict(gamma=_gam([0.9, 1.5])), -5),
+    (dict(gamma=_gam([0.0, 0.5])), -5),
+    (dict(gamma=_gam([float("nan"), 0.5])), -5),
+    (dict(q=FAKE + 4), -7),
+    (dict(out=FAKE), -8),           # out aliases q
+    (dict(fs=FAKE * 4 + 64), -8),   # final_state overlaps out
+])
+def test_retention_fwd_rejects(kw, code):
+    lib = _lib()
+    assert _fwd(lib, **kw) == code
+    assert rc.last_error() != ""
+
+
+def test_retention_fwd_too_many_heads():
+    lib = _lib()
+    H = rc.MAX_HEADS + 1
+    assert _fwd(lib, H=H, gamma=_gam([0.9] * H)) == -2
+
+
+def test_empty_batch_is_accepted_without_device():
+    lib = _lib()
+    assert _fwd(lib, B=0, q=None, k=None, v=None, out=None) == 0
+    assert rc.last_error() == ""
+
+
+def _dec(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9]), state=FAKE * 4, out=FAKE * 64,
+             N=2, H=1, dk=64, dv=64, dtype=rc.RET_BF16)
+    a.update(kw)
+    return lib.retention_decode_step(a["q"], a["k"], a["v"], a["gamma"], a["state"], a["out"],
+                                     a["N"], a["H"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(state=None), -1),
+    (dict(dtype=3), -3),
+    (dict(dk=100), -2),
+    (dict(gamma=_gam([-0.1])), -5),
+    (dict(state=FAKE * 4 + 8), -7),
+    (dict(out=FAKE * 4 + 16), -8),   # out inside state
+    (dict(state=FAKE * 3), -8),      # state aliases v
+])
+def test_decode_rejects(kw, code):
+    lib = _lib()
+    assert _dec(lib, **kw) == code
+
+
+def _lin(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, phi=rc.RET_PHI_ELU1, out=FAKE * 4, B=1, H=1, T=8,
+             dk=64, dv=64, dtype=rc.RET_BF16, eps=1e-6)
+    a.update(kw)
+    return lib.linear_attn_fwd(a["q"], a["k"], a["v"], a["phi"], a["out"], a["B"], a["H"], a["T"],
+                               a["dk"], a["dv"], a["dtype"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(phi=0), -6),
+    (dict(phi=2), -6),
+    (dict(v=None), -1),
+    (dict(eps=-1.0), -2),
+    (dict(eps=float("inf")), -2),
+    (dict(dv=48), -2),
+    (dict(out=FAKE * 2), -8),
+])
+def test_linattn_rejects(kw, code):
+    lib = _lib()
+    assert _lin(lib, **kw) == code
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    if not os.path.exists(rc.library_path()):
+        pytest.skip("libretention.so not built")
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        rc.retention_fwd(q, q, q, [0.9])
