@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the chunkwise-retention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one chunkwise retention forward (out + final state) over the
+long-sequence workload: batch 1, 32 heads, T = 65,536, d_k = d_v = 128,
+bf16 in / fp32 accumulate, chunk 128, gamma_h = 1 - 2^(-5 - 4h/31).  Inputs
+are seeded synthetic tensors already resident in HBM when timing starts.  The
+JSON line also carries the other measured parts of the path: the recurrent
+decode step (256 sequences x 32 heads, 128 x 128 fp32 state, 1000 consecutive
+steps) and the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
+d = 64), each with its own roofline figures.
+
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("chunkwise retention fwd tokens/s + TFLOP/s (% MFMA peak); decode GB/s (% HBM)")
+PROFILES = os.path.join(ROOT, "profiles")
+WALK_SOURCES = ["retention_chunkwise_amd/csrc/walk.hip", "retention_chunkwise_amd/csrc/internal.h"]
+DECODE_SOURCES = ["retention_chunkwise_amd/csrc/decode.hip", "retention_chunkwise_amd/csrc/internal.h"]
+
+
+def sources_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str, paths) -> dict | None:
+    """HBM bytes per launch from committed rocprofv3 counter runs.
+
+    Returns None when no summary exists or when the kernel source changed
+    after the counters were taken.
+    """
+    p = os.path.join(PROFILES, f"hbm_traffic_{name}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_sha") != sources_sha(paths):
+        return None
+    return d
+
+
+def time_launches(fn, steps: int, warmup: int):
+    """Run fn warmup + steps times; return (avg ms per launch from HIP events,
+    wall ms per step).  Events are recorded on torch's current stream, which
+    is the stream the library launches on."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return ev0.elapsed_time(ev1) / steps, wall / steps
+
+
+def cpu_baseline_fwd(inp, w, target_s: float = 10.0):
+    """The fp64 oracle (recurrent form) on the host cores, on a prefix of every
+    head's sequence; the rate is scaled to tokens/s of the whole workload."""
+    import oracle
+
+    nthreads = min(os.cpu_count() or 1, 16)
+    cores = oracle.threads_used(nthreads)
+    q, k, v, g = inp["q"], inp["k"], inp["v"], inp["gamma"]
+    Ts = 256
+    while True:
+        t0 = time.perf_counter()
+        oracle.retention_recurrent(q[:, :, :Ts], k[:, :, :Ts], v[:, :, :Ts], g, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or Ts >= w.T:
+            break
+        Ts = min(w.T, max(Ts * 2, int(Ts * target_s / max(dt, 1e-3) * 0.9)))
+    rate = w.B * Ts / dt  # tokens/s (all heads processed for each token)
+    return {"value": rate, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"fp64 recurrent oracle, g++ -O2 + OpenMP over (b, h); first {Ts} of "
+                      f"{w.T} tokens of all {w.B * w.H} heads ({dt:.1f} s)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true",
+                    help="time only the headline forward")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run plain device copies of known size (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this library runs on a single GPU; multi-GPU runs are not part of this "
+              "build (see DESIGN.md for how the path would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import retention_chunkwise_amd as rc
+    from retention_chunkwise_amd import metrics as M
+    from retention_chunkwise_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    rc.load_library()
+
+    # ---------------- headline: chunkwise retention forward, long sequence
+    w = wl.WORKLOADS["ret_fwd_long_bf16"]
+    inp = wl.make_inputs(w, seed=0)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    out = torch.empty_like(v)
+    fs = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    gamma = inp["gamma"]
+
+    def fwd():
+        rc.retention_fwd(q, k, v, gamma, chunk=w.chunk, out=out, final_state=fs)
+
+    kern_ms, step_ms = time_launches(fwd, args.steps, args.warmup)
+    tokens = w.B * w.T
+    fl_dense = M.fwd_flops(w.B, w.H, w.T, w.dk, w.dv, w.chunk)
+    fl_causal = M.fwd_flops(w.B, w.H, w.T, w.dk, w.dv, w.chunk, causal=True)
+    by = M.fwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, final_state=True)
+    tflops = fl_dense / (step_ms * 1e-3) / 1e12
+    achieved_gbs = by / (kern_ms * 1e-3) / 1e9
+    traffic = measured_traffic("walk_kernel_ret_fwd_long_bf16", WALK_SOURCES)
+
+    res = {
+        "metric": METRIC,
+        "value": tokens / (step_ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": w.description, "B": w.B, "H": w.H,
+                   "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk, "seed": 0},
+        "tflops": tflops,
+        "tflops_causal_min": fl_causal / (step_ms * 1e-3) / 1e12,
+        "mfma_peak_frac": tflops / M.PEAK_TFLOPS["bf16"],
+        "hbm_gbs": achieved_gbs,
+        "roofline": {
+            "kernel": "walk_kernel<bf16, C=128, dk=128, 16-column slices>",
+            "bound": "hbm",
+            "achieved": achieved_gbs,
+            "peak": M.PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved_gbs / M.PEAK_HBM_GBS,
+            "traffic": (traffic["bytes_per_launch"] if traffic else None),
+            "algorithmic_bytes_per_launch": by,
+            "kernel_ms": kern_ms,
+        },
+        "pages_flop_comparison": {
+            "T": 65536, "d": 128,
+            "left_order_flops": M.attention_flops(65536, 128, 128, "left"),
+            "right_order_flops": M.attention_flops(65536, 128, 128, "right"),
+            "note": "analytic counts from the 'Linear attention' page; no hardware timing",
+        },
+    }
+
+    # ---------------- decode step and linear attention
+    if not args.no_components:
+        wd = wl.WORKLOADS["decode_bf16"]
+        di = wl.make_inputs(wd, seed=0)
+        dq, dk_, dv_ = (di[n].to(dev) for n in ("q", "k", "v"))
+        state = di["state"].to(dev)
+        dout = torch.empty_like(dv_)
+
+        def dstep():
+            rc.retention_decode_step(dq, dk_, dv_, di["gamma"], state, out=dout)
+
+        d_kern, d_wall = time_launches(dstep, args.decode_steps, 10)
+        d_bytes = M.decode_bytes(wd.B, wd.H, wd.dk, wd.dv, 2)
+        d_gbs = d_bytes / (d_kern * 1e-3) / 1e9
+        d_tr = measured_traffic("decode_kernel_decode_bf16", DECODE_SOURCES)
+        res["decode"] = {
+            "workload": wd.name, "steps_timed": args.decode_steps,
+            "us_per_step": d_kern * 1e3, "wall_us_per_step": d_wall * 1e3,
+            "tokens_per_s": wd.B / (d_wall * 1e-3),
+            "gbs": d_gbs, "hbm_frac": d_gbs / M.PEAK_HBM_GBS,
+            "tflops": M.decode_flops(wd.B, wd.H, wd.dk, wd.dv) / (d_kern * 1e-3) / 1e12,
+            "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": d_gbs / M.PEAK_HBM_GBS,
+                         "traffic": (d_tr["bytes_per_launch"] if d_tr else None)},
+        }
+        del dq, dk_, dv_, state, dout
+
+        wa = wl.WORKLOADS["linattn_elu1_bf16"]
+        li = wl.make_inputs(wa, seed=0)
+        lq, lk, lv = (li[n].to(dev) for n in ("q", "k", "v"))
+        lout = torch.empty_like(lv)
+
+        def lstep():
+            rc.linear_attn_fwd(lq, lk, lv, out=lout)
+
+        l_kern, l_wall = time_launches(lstep, args.steps, args.warmup)
+        l_fl = M.fwd_flops(wa.B, wa.H, wa.T, wa.dk, wa.dv, wa.chunk)
+        l_by = M.fwd_bytes(wa.B, wa.H, wa.T, wa.dk, wa.dv, 2, final_state=False)
+        l_gbs = l_by / (l_kern * 1e-3) / 1e9
+        res["linear_attn"] = {
+            "workload": wa.name, "ms_per_call": l_kern, "tokens_per_s": wa.B * wa.T / (l_wall * 1e-3),
+            "tflops": l_fl / (l_kern * 1e-3) / 1e12,
+            "mfma_peak_frac": l_fl / (l_kern * 1e-3) / 1e12 / M.PEAK_TFLOPS["bf16"],
+            "gbs": l_gbs, "hbm_frac": l_gbs / M.PEAK_HBM_GBS,
+        }
+        del lq, lk, lv, lout
+
+    if args.calibrate_copy:
+        # plain device-to-device copies of a known size, for scaling HBM counters
+        n = 1 << 28  # 1 GiB of fp32
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = n * 4
+        del src, dst
+
+    # ---------------- CPU baseline (the oracle on the host cores)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_fwd(inp, w)
+
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,7 +18,8 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libretention.so")
-SOURCES = ["capi.hip", "walk.hip", "decode.hip"]
+SOURCES = ["capi.hip", "walk.hip", "walk_ret_bf16.hip", "walk_ret_f32.hip", "walk_lin_bf16.hip",
+           "walk_lin_f32.hip", "decode.hip"]
 ARCH = "gfx950"
 
 

@@ -41,6 +41,10 @@ struct DecodeArgs {
 // Launchers (host).  They assume validated arguments and return a hipError_t.
 hipError_t launch_walk(const WalkArgs& a, bool bf16, int chunk, int dk, int nt,
                        bool linattn, hipStream_t stream);
+hipError_t launch_walk_ret_bf16(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
+hipError_t launch_walk_ret_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
+hipError_t launch_walk_lin_bf16(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
+hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
                          hipStream_t stream);
 

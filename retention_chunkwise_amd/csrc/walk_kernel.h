@@ -1,0 +1,619 @@
+// walk_kernel.h -- chunkwise causal retention / elu+1 linear attention on gfx950.
+//
+// What is computed ("RetNet", single-head definition O = (Q K^T (.) D) V,
+// D_nm = gamma^(n-m) for n >= m, and "Chunked Recurrent Representation";
+// "Efficient and Sparse Transformers" section 6, "Chunkwise form"):
+// the sequence is cut into chunks of C tokens.  With S the fp32 dk x dv state
+// before a chunk, local indices i, j in [0, c) and c <= C the chunk length,
+//   O_i   = sum_{j<=i} gamma^(i-j) (q_i . k_j) v_j  +  gamma^(i+1) q_i S
+//   S_new = gamma^c S + sum_j gamma^(c-1-j) k_j v_j^T
+// (obtained by unrolling S_t = gamma S_{t-1} + k_t v_t^T inside the chunk).
+// Linear attention ("Linear attention", box "Causal linear attention,
+// recurrent form") is the same walk with gamma = 1, phi = elu+1 applied to q
+// and k, and the normaliser z carried beside S:
+//   O_i = (intra_i + phi(q_i) S) / (rowsum_i + phi(q_i) . z + eps),
+//   z_new = z + sum_j phi(k_j).
+//
+// Mapping onto the chip.  One workgroup (4 waves, 256 threads) owns one
+// (batch, head) pair and one slice of 16*NT value columns, and walks every
+// chunk of the sequence in order, keeping its slice of S in registers (fp32).
+// Value columns of S and O are independent, so slices need no communication;
+// each slice recomputes Q K^T for its chunk.  Slices of one (b, h) are placed
+// on the same XCD so their shared Q / K reads hit that XCD's L2.
+//
+// Per chunk, wave W owns query tiles {W, C/16-1-W} (16 rows each; one tile
+// when C = 64), which balances the causal triangle across waves.  The wave
+// index is a template parameter, so every tile loop is unrolled at compile
+// time with no divergent branches.  All contractions run on MFMA (bf16:
+// v_mfma_f32_16x16x32_bf16, fp32: v_mfma_f32_16x16x4f32), fp32 accumulate:
+//   S^T_tile = K Q^T      A = K rows (LDS), B = Q rows (registers)
+//   P^T      = S^T (.) D  decay factors precomputed per lane, in registers
+//   O^T     += S_prev^T (xi Q)^T   A = state copy (LDS), B = Q (registers)
+//   O^T     += V^T P^T    A = V slice packed 4 tokens deep (LDS), B = P^T
+//   S^T      = gamma^c S^T + (zeta V)^T K
+// Computing the transposed products lets the output of the Q K^T MFMA feed the
+// P V MFMA directly from registers (each lane holds 4 consecutive keys of one
+// query), so P never goes through LDS.  The next chunk's K, V and Q are loaded
+// from HBM into registers while the current chunk computes.
+#pragma once
+
+#include <type_traits>
+
+#include "internal.h"
+
+namespace ret {
+namespace walk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float bf2f(unsigned short b) {
+    return __uint_as_float(static_cast<unsigned>(b) << 16);
+}
+
+__device__ __forceinline__ unsigned short f2bf(float f) {
+    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
+}
+
+// phi(x) = elu(x) + 1: x + 1 for x > 0, e^x otherwise.
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ bf16x8 cat_bf16(const u16x4& lo, const u16x4& hi) {
+    u16x8 r;
+    r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+    r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+__device__ __forceinline__ u16x4 cvt4_bf16(const f32x4& x) {
+    return __builtin_bit_cast(u16x4, __builtin_convertvector(x, bf16x4));
+}
+
+__device__ __forceinline__ float sum_over_groups(float x) {
+    // lanes l, l^16, l^32, l^48 hold the four 4-row groups of one column
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+template <bool BF16, int C, int DK, int NT, bool LIN>
+struct Cfg {
+    typedef typename std::conditional<BF16, unsigned short, float>::type E;
+    static constexpr int NI = C / 16;                 // 16-token tiles per chunk
+    static constexpr int NS = (NI == 8) ? 2 : 1;      // query tiles per wave
+    static constexpr int DVS = 16 * NT;               // value columns per workgroup
+    static constexpr int ESZ = BF16 ? 2 : 4;          // element bytes
+    static constexpr int EPV = 16 / ESZ;              // elements per 16-byte vector
+    static constexpr int KSTR = DK + EPV;             // row stride of K / state copy (16-B pad)
+    static constexpr int KT = DK / 16;                // 16-wide key tiles
+    static constexpr int SPW = NT * KT / 4;           // state tiles per wave
+    static constexpr int KU = C * DK * ESZ / 16 / kThreads;  // 16-B K units per thread
+    static constexpr int RU = DK * ESZ / 16;          // 16-B units per K row
+    static constexpr int VU = (C / 4) * (DVS / EPV);  // V staging units
+    static constexpr int VSTRIDE = kThreads / VU;     // one V unit every VSTRIDE threads
+    static constexpr int QU = DK * ESZ / 64;          // 16-B Q units per lane per tile
+    static constexpr int DEC = C + 32;                // decay table entries
+    static_assert(NI == 4 || NI == 8, "chunk must be 64 or 128");
+    static_assert(DK == 64 || DK == 128, "dk must be 64 or 128");
+    static_assert(NT * KT % 4 == 0, "state tiles must split over 4 waves");
+    static_assert(C * DK * ESZ / 16 % kThreads == 0, "K staging split");
+    static_assert(VU <= kThreads && kThreads % VU == 0, "V staging split");
+};
+
+template <bool BF16, int C, int DK, int NT, bool LIN>
+struct Smem {
+    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    using E = typename Cf::E;
+    alignas(16) E Ks[C * Cf::KSTR];            // K (or phi(K)) rows
+    alignas(16) E V4s[C * Cf::DVS];            // V slice, [j/4][n][4]
+    alignas(16) E V4z[C * Cf::DVS];            // zeta-scaled copy
+    alignas(16) E Sts[2][Cf::DVS * Cf::KSTR];  // S^T copy, [n][k], double-buffered
+    alignas(16) float dec[Cf::DEC];            // [16 + m] = gamma^m, [0..15] = 0
+    alignas(16) float zs[2][LIN ? DK : 4];     // normaliser z (linear attention)
+};
+
+template <bool BF16, int C, int DK, int NT, bool LIN, int W>
+__device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, NT, LIN>& sm,
+                                          const int bh, const int nbase, const float lg) {
+    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    using E = typename Cf::E;
+    constexpr int NI = Cf::NI, NS = Cf::NS, DVS = Cf::DVS, KSTR = Cf::KSTR, EPV = Cf::EPV;
+    constexpr int KT = Cf::KT, SPW = Cf::SPW, KU = Cf::KU, RU = Cf::RU, VSTRIDE = Cf::VSTRIDE;
+    constexpr int QU = Cf::QU;
+    constexpr int IT0 = W;                                // query tiles of this wave
+    constexpr int IT1 = (NS == 2) ? NI - 1 - W : W;
+    constexpr int ITMAX = IT1;                            // IT1 >= IT0
+
+    const int tid = threadIdx.x;
+    const int l = tid & 63, l16 = l & 15, g = l >> 4;
+    const int T = a.T, DV = a.dv;
+    const long long qk_base = static_cast<long long>(bh) * T * DK;
+    const long long v_base = static_cast<long long>(bh) * T * DV;
+    const E* __restrict__ qg = static_cast<const E*>(a.q) + qk_base;
+    const E* __restrict__ kg = static_cast<const E*>(a.k) + qk_base;
+    const E* __restrict__ vg = static_cast<const E*>(a.v) + v_base;
+    E* __restrict__ og = static_cast<E*>(a.out) + v_base;
+
+    auto its = [](int s) constexpr { return s == 0 ? IT0 : IT1; };
+
+    // decay factors of this lane for the tiles this wave owns:
+    // dfac[dt][r] = gamma^(16 dt + l16 - 4g - r) for a non-negative exponent, else 0
+    float dfac[ITMAX + 1][4];
+#pragma unroll
+    for (int dt = 0; dt <= ITMAX; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int e = 16 * dt + l16 - 4 * g - r;
+            dfac[dt][r] = (e < 0) ? 0.f : exp2f(static_cast<float>(e) * lg);
+        }
+    float xi[NS];  // gamma^(i+1) for this lane's query row in each owned tile
+#pragma unroll
+    for (int s = 0; s < NS; ++s) xi[s] = exp2f(static_cast<float>(its(s) * 16 + l16 + 1) * lg);
+
+    f32x4 sacc[SPW];
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint4 kpre[KU];
+    uint4 vpre[4];
+    uint4 qnext[NS][QU];
+    uint4 qcur[NS][QU];
+    const bool vthread = (tid % VSTRIDE) == 0;
+    const int vunit = tid / VSTRIDE;
+    const int vjq = vunit / (DVS / EPV), vcg = vunit % (DVS / EPV);
+
+    // Loads of one chunk into registers.  Rows past the end of the sequence
+    // read the last valid row (always in bounds); they are replaced by zeros
+    // when the registers are staged, after the loads have landed, so no
+    // instruction consumes a prefetched value in the iteration that issues it.
+    auto load_chunk = [&](int c) {
+        const int t0 = c * C;
+#pragma unroll
+        for (int m = 0; m < KU; ++m) {
+            const int u = tid + m * kThreads;
+            const int row = u / RU, col = u % RU;
+            const int t = t0 + row;
+            const int tt = t < T ? t : T - 1;
+            kpre[m] = *reinterpret_cast<const uint4*>(kg + static_cast<long long>(tt) * DK + col * EPV);
+        }
+        if (vthread) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = t0 + 4 * vjq + r;
+                const int tt = t < T ? t : T - 1;
+                vpre[r] = *reinterpret_cast<const uint4*>(vg + static_cast<long long>(tt) * DV + nbase + vcg * EPV);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int t = t0 + its(s) * 16 + l16;
+            const int tt = t < T ? t : T - 1;
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                // bf16: unit u covers k = 32u + 8g .. +7 ; fp32: k = (DK/4) g + 4u .. +3
+                const int k0 = BF16 ? (32 * u + 8 * g) : ((DK / 4) * g + 4 * u);
+                qnext[s][u] = *reinterpret_cast<const uint4*>(qg + static_cast<long long>(tt) * DK + k0);
+            }
+        }
+    };
+
+    auto apply_phi16 = [](uint4 x) -> uint4 {
+        if constexpr (BF16) {
+            u16x8 e = __builtin_bit_cast(u16x8, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = f2bf(phi_elu1(bf2f(e[i])));
+            return __builtin_bit_cast(uint4, e);
+        } else {
+            f32x4 e = __builtin_bit_cast(f32x4, x);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) e[i] = phi_elu1(e[i]);
+            return __builtin_bit_cast(uint4, e);
+        }
+    };
+
+    const int nch = (T + C - 1) / C;
+    if (nch > 0) load_chunk(0);
+
+    for (int c = 0; c < nch; ++c) {
+        const int t0 = c * C;
+        const int clen = (T - t0 < C) ? (T - t0) : C;
+        const int cur = c & 1, nxt = cur ^ 1;
+
+        __syncthreads();  // all reads of the previous chunk's LDS tiles are done
+        // ---- stage K rows
+#pragma unroll
+        for (int m = 0; m < KU; ++m) {
+            const int u = tid + m * kThreads;
+            const int row = u / RU, col = u % RU;
+            uint4 x = kpre[m];
+            if constexpr (LIN) x = apply_phi16(x);
+            if (row >= clen) x = uint4{0, 0, 0, 0};
+            *reinterpret_cast<uint4*>(&sm.Ks[row * KSTR + col * EPV]) = x;
+        }
+        // ---- stage the V slice, packed 4 tokens deep, plain and zeta-scaled
+        if (vthread) {
+            float zeta[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = 16 + clen - 1 - (4 * vjq + r);  // gamma^(c-1-j), 0 past the end
+                zeta[r] = sm.dec[e < 0 ? 0 : e];
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * vjq + r >= clen) vpre[r] = uint4{0, 0, 0, 0};
+            E* dst = &sm.V4s[(vjq * DVS + vcg * EPV) * 4];
+            E* dstz = &sm.V4z[(vjq * DVS + vcg * EPV) * 4];
+            if constexpr (BF16) {
+                u16x8 rows[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rows[r] = __builtin_bit_cast(u16x8, vpre[r]);
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {  // 4 columns (32 bytes) per half
+                    u16x8 o0, o1, z0, z1;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        o0[r] = rows[r][4 * p + 0];
+                        o0[4 + r] = rows[r][4 * p + 1];
+                        o1[r] = rows[r][4 * p + 2];
+                        o1[4 + r] = rows[r][4 * p + 3];
+                        z0[r] = f2bf(bf2f(rows[r][4 * p + 0]) * zeta[r]);
+                        z0[4 + r] = f2bf(bf2f(rows[r][4 * p + 1]) * zeta[r]);
+                        z1[r] = f2bf(bf2f(rows[r][4 * p + 2]) * zeta[r]);
+                        z1[4 + r] = f2bf(bf2f(rows[r][4 * p + 3]) * zeta[r]);
+                    }
+                    *reinterpret_cast<u16x8*>(dst + 16 * p) = o0;
+                    *reinterpret_cast<u16x8*>(dst + 16 * p + 8) = o1;
+                    *reinterpret_cast<u16x8*>(dstz + 16 * p) = z0;
+                    *reinterpret_cast<u16x8*>(dstz + 16 * p + 8) = z1;
+                }
+            } else {
+                f32x4 rows[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) rows[r] = __builtin_bit_cast(f32x4, vpre[r]);
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) {
+                    f32x4 o, z;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        o[r] = rows[r][cc];
+                        z[r] = rows[r][cc] * zeta[r];
+                    }
+                    *reinterpret_cast<f32x4*>(dst + 4 * cc) = o;
+                    *reinterpret_cast<f32x4*>(dstz + 4 * cc) = z;
+                }
+            }
+        }
+        // ---- this chunk's Q (feature-mapped for linear attention)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const bool qvalid = its(s) * 16 + l16 < clen;
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                uint4 x = qnext[s][u];
+                if constexpr (LIN) x = apply_phi16(x);
+                qcur[s][u] = qvalid ? x : uint4{0, 0, 0, 0};
+            }
+        }
+        __syncthreads();
+
+        if (c + 1 < nch) load_chunk(c + 1);
+
+        // ---------------- S^T tiles = K Q^T for key tiles jt <= query tile
+        f32x4 pacc[NS][NI];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int jt = 0; jt < NI; ++jt) pacc[s][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        if constexpr (BF16) {
+#pragma unroll
+            for (int ks = 0; ks < DK / 32; ++ks) {
+                bf16x8 ka[ITMAX + 1];
+#pragma unroll
+                for (int jt = 0; jt <= ITMAX; ++jt)
+                    ka[jt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Ks[(jt * 16 + l16) * KSTR + 32 * ks + 8 * g]));
+#pragma unroll
+                for (int jt = 0; jt <= ITMAX; ++jt)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+                        if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], as_bf16x8(qcur[s][ks]), pacc[s][jt]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                f32x4 ka[ITMAX + 1];
+#pragma unroll
+                for (int jt = 0; jt <= ITMAX; ++jt)
+                    ka[jt] = *reinterpret_cast<const f32x4*>(&sm.Ks[(jt * 16 + l16) * KSTR + (DK / 4) * g + 4 * u]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int jt = 0; jt <= ITMAX; ++jt)
+#pragma unroll
+                        for (int s = 0; s < NS; ++s)
+                            if (jt <= its(s)) {
+                                const f32x4 q4 = __builtin_bit_cast(f32x4, qcur[s][u]);
+                                pacc[s][jt] = mfma_f32(ka[jt][e], q4[e], pacc[s][jt]);
+                            }
+            }
+        }
+
+        // ---------------- decay mask: P^T[j][i] = S^T[j][i] * gamma^(i-j), 0 for j > i
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int jt = 0; jt <= ITMAX; ++jt)
+                if (jt <= its(s))
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) pacc[s][jt][r] *= dfac[its(s) - jt][r];
+
+        // bf16 copies of P^T, two key tiles per MFMA operand; row sums for the normaliser
+        float rsum[NS];
+        bf16x8 pb[NS][NI / 2];
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            rsum[s] = 0.f;
+            if constexpr (BF16) {
+#pragma unroll
+                for (int p = 0; p < NI / 2; ++p) {
+                    if (2 * p <= its(s)) {
+                        const u16x4 lo = cvt4_bf16(pacc[s][2 * p]);
+                        const u16x4 hi = (2 * p + 1 <= its(s)) ? cvt4_bf16(pacc[s][2 * p + 1]) : u16x4{0, 0, 0, 0};
+                        pb[s][p] = cat_bf16(lo, hi);
+                        if constexpr (LIN) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) rsum[s] += bf2f(lo[r]) + bf2f(hi[r]);
+                        }
+                    }
+                }
+            } else if constexpr (LIN) {
+#pragma unroll
+                for (int jt = 0; jt <= ITMAX; ++jt)
+                    if (jt <= its(s))
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rsum[s] += pacc[s][jt][r];
+            }
+        }
+
+        // ---------------- O^T = S_prev^T (xi Q)^T + V^T P^T
+        f32x4 oacc[NS][NT];
+        const E* st = sm.Sts[cur];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) oacc[s][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const E* srow = st + (nt * 16 + l16) * KSTR;
+            if constexpr (BF16) {
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(srow + 32 * ks + 8 * g));
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) oacc[s][nt] = mfma_bf16(av, as_bf16x8(qcur[s][ks]), oacc[s][nt]);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < QU; ++u) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(srow + (DK / 4) * g + 4 * u);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+#pragma unroll
+                        for (int s = 0; s < NS; ++s) {
+                            const f32x4 q4 = __builtin_bit_cast(f32x4, qcur[s][u]);
+                            oacc[s][nt] = mfma_f32(a4[e], q4[e], oacc[s][nt]);
+                        }
+                }
+            }
+            if constexpr (!LIN) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) oacc[s][nt] *= xi[s];
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int p = 0; 2 * p <= ITMAX; ++p) {
+                    const E* v0 = &sm.V4s[((8 * p + g) * DVS + nt * 16 + l16) * 4];
+                    const E* v1 = &sm.V4s[((8 * p + 4 + g) * DVS + nt * 16 + l16) * 4];
+                    const bf16x8 av = cat_bf16(*reinterpret_cast<const u16x4*>(v0),
+                                               *reinterpret_cast<const u16x4*>(v1));
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+                        if (2 * p <= its(s)) oacc[s][nt] = mfma_bf16(av, pb[s][p], oacc[s][nt]);
+                }
+            } else {
+#pragma unroll
+                for (int jt = 0; jt <= ITMAX; ++jt) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.V4s[((4 * jt + g) * DVS + nt * 16 + l16) * 4]);
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+                        if (jt <= its(s))
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) oacc[s][nt] = mfma_f32(a4[r], pacc[s][jt][r], oacc[s][nt]);
+                }
+            }
+        }
+
+        // ---------------- normalise (linear attention) and store O
+        float rden[NS];
+        if constexpr (LIN) {
+            const float* zc = sm.zs[cur];
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                float dq = 0.f;  // phi(q_i) . z over this lane's key slots
+#pragma unroll
+                for (int u = 0; u < QU; ++u) {
+                    if constexpr (BF16) {
+                        const u16x8 e = __builtin_bit_cast(u16x8, qcur[s][u]);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) dq += bf2f(e[i]) * zc[32 * u + 8 * g + i];
+                    } else {
+                        const f32x4 e = __builtin_bit_cast(f32x4, qcur[s][u]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dq += e[i] * zc[(DK / 4) * g + 4 * u + i];
+                    }
+                }
+                rden[s] = 1.f / (sum_over_groups(rsum[s] + dq) + a.eps);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int row = its(s) * 16 + l16;
+            if (row < clen) {
+                E* orow = og + static_cast<long long>(t0 + row) * DV + nbase + 4 * g;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    f32x4 o = oacc[s][nt];
+                    if constexpr (LIN) o *= rden[s];
+                    if constexpr (BF16) *reinterpret_cast<u16x4*>(orow + nt * 16) = cvt4_bf16(o);
+                    else *reinterpret_cast<f32x4*>(orow + nt * 16) = o;
+                }
+            }
+        }
+
+        // ---------------- state: S^T <- gamma^c S^T + (zeta V)^T K   (and z += sum phi(k))
+        const float gc = sm.dec[16 + clen];
+        E* stn = sm.Sts[nxt];
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = W + 4 * m;
+            const int nt = qt / KT, kt = qt % KT;
+            f32x4 acc = sacc[m] * gc;
+            float zsum = 0.f;
+            const int kcol = kt * 16 + l16;
+            if constexpr (BF16) {
+#pragma unroll
+                for (int js = 0; js < C / 32; ++js) {
+                    const E* v0 = &sm.V4z[((8 * js + g) * DVS + nt * 16 + l16) * 4];
+                    const E* v1 = &sm.V4z[((8 * js + 4 + g) * DVS + nt * 16 + l16) * 4];
+                    const bf16x8 av = cat_bf16(*reinterpret_cast<const u16x4*>(v0),
+                                               *reinterpret_cast<const u16x4*>(v1));
+                    u16x4 blo, bhi;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        blo[r] = sm.Ks[(js * 32 + 4 * g + r) * KSTR + kcol];
+                        bhi[r] = sm.Ks[(js * 32 + 16 + 4 * g + r) * KSTR + kcol];
+                    }
+                    acc = mfma_bf16(av, cat_bf16(blo, bhi), acc);
+                    if (LIN && nt == 0) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) zsum += bf2f(blo[r]) + bf2f(bhi[r]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int jt = 0; jt < NI; ++jt) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.V4z[((4 * jt + g) * DVS + nt * 16 + l16) * 4]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float b = sm.Ks[(jt * 16 + 4 * g + r) * KSTR + kcol];
+                        acc = mfma_f32(a4[r], b, acc);
+                        if (LIN && nt == 0) zsum += b;
+                    }
+                }
+            }
+            sacc[m] = acc;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (BF16) stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = f2bf(acc[r]);
+                else stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = acc[r];
+            }
+            if (LIN && nt == 0) {
+                zsum = sum_over_groups(zsum);
+                if (g == 0) sm.zs[nxt][kcol] = sm.zs[cur][kcol] + zsum;
+            }
+        }
+    }
+
+    // ---------------- final state [dk][dv] fp32
+    if (a.final_state) {
+        float* fs = a.final_state + static_cast<long long>(bh) * DK * DV;
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = W + 4 * m;
+            const int nt = qt / KT, kt = qt % KT;
+            *reinterpret_cast<f32x4*>(fs + static_cast<long long>(kt * 16 + l16) * DV + nbase + nt * 16 + 4 * g) = sacc[m];
+        }
+    }
+}
+
+template <bool BF16, int C, int DK, int NT, bool LIN>
+__global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
+    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    using E = typename Cf::E;
+    __shared__ Smem<BF16, C, DK, NT, LIN> sm;
+
+    // workgroup -> (b*H + h, value slice); slices of one (b, h) share an XCD
+    int L = blockIdx.x;
+    if (a.xcd_remap) {
+        const int per = gridDim.x >> 3;
+        L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    }
+    const int bh = L / a.nslices;
+    const int nbase = (L % a.nslices) * Cf::DVS;
+    const int h = bh % a.H;
+    const float lg = LIN ? 0.f : a.log2g[h];
+
+    const int tid = threadIdx.x;
+    for (int m = tid; m < Cf::DEC; m += kThreads)
+        sm.dec[m] = (m < 16) ? 0.f : exp2f(static_cast<float>(m - 16) * lg);
+    for (int m = tid; m < Cf::DVS * Cf::KSTR; m += kThreads) sm.Sts[0][m] = E(0);
+    if constexpr (LIN)
+        for (int m = tid; m < DK; m += kThreads) sm.zs[0][m] = 0.f;
+    // (the first barrier inside walk_body orders these writes before any read)
+
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    switch (wave) {
+        case 0: walk_body<BF16, C, DK, NT, LIN, 0>(a, sm, bh, nbase, lg); break;
+        case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, bh, nbase, lg); break;
+        case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, bh, nbase, lg); break;
+        default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, bh, nbase, lg); break;
+    }
+}
+
+template <bool BF16, int C, int DK, int NT, bool LIN>
+hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
+    const long long groups = static_cast<long long>(a.B) * a.H * a.nslices;
+    if (groups <= 0) return hipSuccess;
+    if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
+    WalkArgs args = a;
+    args.xcd_remap = (groups % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((walk_kernel<BF16, C, DK, NT, LIN>), dim3(static_cast<unsigned>(groups)),
+                       dim3(kThreads), 0, stream, args);
+    return hipGetLastError();
+}
+
+// Instantiates every (chunk, dk, NT) variant for one (dtype, operator) pair.
+template <bool BF16, bool LIN>
+hipError_t launch_variant(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream) {
+#define RET_WALK_CASE(C_, DK_, NT_) \
+    if (chunk == C_ && dk == DK_ && nt == NT_) return launch_t<BF16, C_, DK_, NT_, LIN>(a, stream);
+    RET_WALK_CASE(64, 64, 1)
+    RET_WALK_CASE(64, 64, 2)
+    RET_WALK_CASE(64, 128, 1)
+    RET_WALK_CASE(64, 128, 2)
+    RET_WALK_CASE(128, 64, 1)
+    RET_WALK_CASE(128, 64, 2)
+    RET_WALK_CASE(128, 128, 1)
+    RET_WALK_CASE(128, 128, 2)
+#undef RET_WALK_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace walk
+}  // namespace ret
