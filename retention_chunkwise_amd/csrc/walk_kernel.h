@@ -91,6 +91,43 @@ __device__ __forceinline__ float sum_over_groups(float x) {
     return x;
 }
 
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, let lane L address 8 bytes M[L][0..3]; lane i receives
+// {M[i/4 + 4m][i % 4] : m = 0..3}.  With lane L pointing at row r0 + L/4,
+// columns c0 + 4 (L % 4) of a row-major bf16 tile, lane i therefore gets rows
+// r0..r0+3 of column c0 + i: four consecutive tokens of one column, which is
+// the MFMA operand layout for a contraction over tokens.
+__device__ __forceinline__ u16x4 lds_tr4(const unsigned short* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(u16x4, r);
+}
+
+// Raw buffer access with hardware range checking: a resource covers exactly
+// the valid bytes of one chunk, so loads past its end return zeros and stores
+// past its end are dropped.  Offsets are 32-bit byte offsets.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    // word 3: 32-bit data format, the standard raw-buffer setting on gfx9-family parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+    return uint4{v[0], v[1], v[2], v[3]};
+}
+
+__device__ __forceinline__ void bstore8(__amdgpu_buffer_rsrc_t r, unsigned off, const u16x4& x) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, static_cast<int>(off), 0, 0);
+}
+
+__device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, unsigned off, const f32x4& x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, static_cast<int>(off), 0, 0);
+}
+
 template <bool BF16, int C, int DK, int NT, bool LIN>
 struct Cfg {
     typedef typename std::conditional<BF16, unsigned short, float>::type E;
@@ -99,32 +136,35 @@ struct Cfg {
     static constexpr int DVS = 16 * NT;               // value columns per workgroup
     static constexpr int ESZ = BF16 ? 2 : 4;          // element bytes
     static constexpr int EPV = 16 / ESZ;              // elements per 16-byte vector
-    static constexpr int KSTR = DK + EPV;             // row stride of K / state copy (16-B pad)
+    static constexpr int KSTR = DK + EPV;             // row stride of Q / K / state copy (16-B pad)
+    static constexpr int VSTR = DVS;                  // row stride of the V slice copies
     static constexpr int KT = DK / 16;                // 16-wide key tiles
     static constexpr int SPW = NT * KT / 4;           // state tiles per wave
-    static constexpr int KU = C * DK * ESZ / 16 / kThreads;  // 16-B K units per thread
-    static constexpr int RU = DK * ESZ / 16;          // 16-B units per K row
-    static constexpr int VU = (C / 4) * (DVS / EPV);  // V staging units
-    static constexpr int VSTRIDE = kThreads / VU;     // one V unit every VSTRIDE threads
+    static constexpr int KU = C * DK * ESZ / 16 / kThreads;  // 16-B units of a Q / K chunk per thread
+    static constexpr int RU = DK * ESZ / 16;          // 16-B units per Q / K row
+    static constexpr int VRU = DVS * ESZ / 16;        // 16-B units per V-slice row
+    static constexpr int VUT = C * VRU;               // V-slice units per chunk
+    static constexpr int VPT = (VUT + kThreads - 1) / kThreads;
+    static constexpr bool QLDS = BF16;                // bf16: Q staged in LDS; fp32: per wave in registers
     static constexpr int QU = DK * ESZ / 64;          // 16-B Q units per lane per tile
     static constexpr int DEC = C + 32;                // decay table entries
     static_assert(NI == 4 || NI == 8, "chunk must be 64 or 128");
     static_assert(DK == 64 || DK == 128, "dk must be 64 or 128");
     static_assert(NT * KT % 4 == 0, "state tiles must split over 4 waves");
-    static_assert(C * DK * ESZ / 16 % kThreads == 0, "K staging split");
-    static_assert(VU <= kThreads && kThreads % VU == 0, "V staging split");
+    static_assert(C * DK * ESZ / 16 % kThreads == 0, "Q/K staging split");
 };
 
 template <bool BF16, int C, int DK, int NT, bool LIN>
 struct Smem {
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
-    alignas(16) E Ks[C * Cf::KSTR];            // K (or phi(K)) rows
-    alignas(16) E V4s[C * Cf::DVS];            // V slice, [j/4][n][4]
-    alignas(16) E V4z[C * Cf::DVS];            // zeta-scaled copy
-    alignas(16) E Sts[2][Cf::DVS * Cf::KSTR];  // S^T copy, [n][k], double-buffered
-    alignas(16) float dec[Cf::DEC];            // [16 + m] = gamma^m, [0..15] = 0
-    alignas(16) float zs[2][LIN ? DK : 4];     // normaliser z (linear attention)
+    alignas(16) E Qs[Cf::QLDS ? C * Cf::KSTR : 8];   // Q (or phi(Q)) rows (bf16 only)
+    alignas(16) E Ks[C * Cf::KSTR];                  // K (or phi(K)) rows
+    alignas(16) E Vs[C * Cf::VSTR];                  // V slice, row-major
+    alignas(16) E Vz[C * Cf::VSTR];                  // zeta-scaled V slice
+    alignas(16) E Sts[2][Cf::DVS * Cf::KSTR];        // S^T copy, [n][k], double-buffered
+    alignas(16) float dec[Cf::DEC];                  // [16 + m] = gamma^m, [0..15] = 0
+    alignas(16) float zs[2][LIN ? DK : 4];           // normaliser z (linear attention)
 };
 
 template <bool BF16, int C, int DK, int NT, bool LIN, int W>
@@ -133,21 +173,22 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
     constexpr int NI = Cf::NI, NS = Cf::NS, DVS = Cf::DVS, KSTR = Cf::KSTR, EPV = Cf::EPV;
-    constexpr int KT = Cf::KT, SPW = Cf::SPW, KU = Cf::KU, RU = Cf::RU, VSTRIDE = Cf::VSTRIDE;
-    constexpr int QU = Cf::QU;
+    constexpr int VSTR = Cf::VSTR, KT = Cf::KT, SPW = Cf::SPW, KU = Cf::KU, RU = Cf::RU;
+    constexpr int VRU = Cf::VRU, VUT = Cf::VUT, VPT = Cf::VPT, QU = Cf::QU;
+    constexpr bool QLDS = Cf::QLDS;
     constexpr int IT0 = W;                                // query tiles of this wave
     constexpr int IT1 = (NS == 2) ? NI - 1 - W : W;
     constexpr int ITMAX = IT1;                            // IT1 >= IT0
 
     const int tid = threadIdx.x;
     const int l = tid & 63, l16 = l & 15, g = l >> 4;
+    const int lq = l16 >> 2, lr = l16 & 3;                // transpose-read lane roles
     const int T = a.T, DV = a.dv;
-    const long long qk_base = static_cast<long long>(bh) * T * DK;
-    const long long v_base = static_cast<long long>(bh) * T * DV;
-    const E* __restrict__ qg = static_cast<const E*>(a.q) + qk_base;
-    const E* __restrict__ kg = static_cast<const E*>(a.k) + qk_base;
-    const E* __restrict__ vg = static_cast<const E*>(a.v) + v_base;
-    E* __restrict__ og = static_cast<E*>(a.out) + v_base;
+    // this (b, h)'s rows; the V / O pointers already point at this slice's columns
+    const E* __restrict__ qh = static_cast<const E*>(a.q) + static_cast<long long>(bh) * T * DK;
+    const E* __restrict__ kh = static_cast<const E*>(a.k) + static_cast<long long>(bh) * T * DK;
+    const E* __restrict__ vh = static_cast<const E*>(a.v) + static_cast<long long>(bh) * T * DV + nbase;
+    E* __restrict__ oh = static_cast<E*>(a.out) + static_cast<long long>(bh) * T * DV + nbase;
 
     auto its = [](int s) constexpr { return s == 0 ? IT0 : IT1; };
 
@@ -170,44 +211,43 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     uint4 kpre[KU];
-    uint4 vpre[4];
-    uint4 qnext[NS][QU];
-    uint4 qcur[NS][QU];
-    const bool vthread = (tid % VSTRIDE) == 0;
-    const int vunit = tid / VSTRIDE;
-    const int vjq = vunit / (DVS / EPV), vcg = vunit % (DVS / EPV);
+    uint4 qpre[QLDS ? KU : 1];
+    uint4 vpre[VPT];
+    uint4 qnext[NS][QLDS ? 1 : QU];
+    uint4 qcur[NS][QLDS ? 1 : QU];
 
-    // Loads of one chunk into registers.  Rows past the end of the sequence
-    // read the last valid row (always in bounds); they are replaced by zeros
-    // when the registers are staged, after the loads have landed, so no
+    // Loads of one chunk into registers through range-checked buffer
+    // resources: rows past the end of the sequence read as zeros.  No
     // instruction consumes a prefetched value in the iteration that issues it.
     auto load_chunk = [&](int c) {
         const int t0 = c * C;
+        const int cl = (T - t0 < C) ? (T - t0) : C;
+        const auto rk = make_rsrc(kh + static_cast<long long>(t0) * DK, cl * DK * Cf::ESZ);
+        const auto rq = make_rsrc(qh + static_cast<long long>(t0) * DK, cl * DK * Cf::ESZ);
+        const auto rv = make_rsrc(vh + static_cast<long long>(t0) * DV, cl * DV * Cf::ESZ);
 #pragma unroll
         for (int m = 0; m < KU; ++m) {
             const int u = tid + m * kThreads;
             const int row = u / RU, col = u % RU;
-            const int t = t0 + row;
-            const int tt = t < T ? t : T - 1;
-            kpre[m] = *reinterpret_cast<const uint4*>(kg + static_cast<long long>(tt) * DK + col * EPV);
+            const unsigned off = static_cast<unsigned>((row * DK + col * EPV) * Cf::ESZ);
+            kpre[m] = bload16(rk, off);
+            if constexpr (QLDS) qpre[m] = bload16(rq, off);
         }
-        if (vthread) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = t0 + 4 * vjq + r;
-                const int tt = t < T ? t : T - 1;
-                vpre[r] = *reinterpret_cast<const uint4*>(vg + static_cast<long long>(tt) * DV + nbase + vcg * EPV);
+        for (int m = 0; m < VPT; ++m) {
+            const int u = tid + m * kThreads;
+            if (VUT % kThreads == 0 || u < VUT) {
+                const int row = u / VRU, col = u % VRU;
+                vpre[m] = bload16(rv, static_cast<unsigned>((row * DV + col * EPV) * Cf::ESZ));
             }
         }
+        if constexpr (!QLDS) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int t = t0 + its(s) * 16 + l16;
-            const int tt = t < T ? t : T - 1;
+            for (int s = 0; s < NS; ++s) {
+                const int row = its(s) * 16 + l16;
 #pragma unroll
-            for (int u = 0; u < QU; ++u) {
-                // bf16: unit u covers k = 32u + 8g .. +7 ; fp32: k = (DK/4) g + 4u .. +3
-                const int k0 = BF16 ? (32 * u + 8 * g) : ((DK / 4) * g + 4 * u);
-                qnext[s][u] = *reinterpret_cast<const uint4*>(qg + static_cast<long long>(tt) * DK + k0);
+                for (int u = 0; u < QU; ++u)  // k = (DK/4) g + 4u .. +3
+                    qnext[s][u] = bload16(rq, static_cast<unsigned>((row * DK + (DK / 4) * g + 4 * u) * Cf::ESZ));
             }
         }
     };
@@ -232,86 +272,93 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     for (int c = 0; c < nch; ++c) {
         const int t0 = c * C;
         const int clen = (T - t0 < C) ? (T - t0) : C;
+        const bool tail = clen < C;  // uniform: only the last chunk can be short
         const int cur = c & 1, nxt = cur ^ 1;
 
         __syncthreads();  // all reads of the previous chunk's LDS tiles are done
-        // ---- stage K rows
+        // ---- stage Q and K rows
 #pragma unroll
         for (int m = 0; m < KU; ++m) {
             const int u = tid + m * kThreads;
             const int row = u / RU, col = u % RU;
             uint4 x = kpre[m];
             if constexpr (LIN) x = apply_phi16(x);
-            if (row >= clen) x = uint4{0, 0, 0, 0};
             *reinterpret_cast<uint4*>(&sm.Ks[row * KSTR + col * EPV]) = x;
-        }
-        // ---- stage the V slice, packed 4 tokens deep, plain and zeta-scaled
-        if (vthread) {
-            float zeta[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = 16 + clen - 1 - (4 * vjq + r);  // gamma^(c-1-j), 0 past the end
-                zeta[r] = sm.dec[e < 0 ? 0 : e];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * vjq + r >= clen) vpre[r] = uint4{0, 0, 0, 0};
-            E* dst = &sm.V4s[(vjq * DVS + vcg * EPV) * 4];
-            E* dstz = &sm.V4z[(vjq * DVS + vcg * EPV) * 4];
-            if constexpr (BF16) {
-                u16x8 rows[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) rows[r] = __builtin_bit_cast(u16x8, vpre[r]);
-#pragma unroll
-                for (int p = 0; p < 2; ++p) {  // 4 columns (32 bytes) per half
-                    u16x8 o0, o1, z0, z1;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        o0[r] = rows[r][4 * p + 0];
-                        o0[4 + r] = rows[r][4 * p + 1];
-                        o1[r] = rows[r][4 * p + 2];
-                        o1[4 + r] = rows[r][4 * p + 3];
-                        z0[r] = f2bf(bf2f(rows[r][4 * p + 0]) * zeta[r]);
-                        z0[4 + r] = f2bf(bf2f(rows[r][4 * p + 1]) * zeta[r]);
-                        z1[r] = f2bf(bf2f(rows[r][4 * p + 2]) * zeta[r]);
-                        z1[4 + r] = f2bf(bf2f(rows[r][4 * p + 3]) * zeta[r]);
-                    }
-                    *reinterpret_cast<u16x8*>(dst + 16 * p) = o0;
-                    *reinterpret_cast<u16x8*>(dst + 16 * p + 8) = o1;
-                    *reinterpret_cast<u16x8*>(dstz + 16 * p) = z0;
-                    *reinterpret_cast<u16x8*>(dstz + 16 * p + 8) = z1;
-                }
-            } else {
-                f32x4 rows[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) rows[r] = __builtin_bit_cast(f32x4, vpre[r]);
-#pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
-                    f32x4 o, z;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        o[r] = rows[r][cc];
-                        z[r] = rows[r][cc] * zeta[r];
-                    }
-                    *reinterpret_cast<f32x4*>(dst + 4 * cc) = o;
-                    *reinterpret_cast<f32x4*>(dstz + 4 * cc) = z;
-                }
+            if constexpr (QLDS) {
+                uint4 y = qpre[m];
+                if constexpr (LIN) y = apply_phi16(y);
+                *reinterpret_cast<uint4*>(&sm.Qs[row * KSTR + col * EPV]) = y;
             }
         }
-        // ---- this chunk's Q (feature-mapped for linear attention)
+        // ---- stage the V slice, plain and zeta-scaled (zeta_j = gamma^(c-1-j))
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const bool qvalid = its(s) * 16 + l16 < clen;
+        for (int m = 0; m < VPT; ++m) {
+            const int u = tid + m * kThreads;
+            if (VUT % kThreads == 0 || u < VUT) {
+                const int row = u / VRU, col = u % VRU;
+                const int ez = 16 + clen - 1 - row;  // gamma^(c-1-j); 0 past the end
+                const float zeta = sm.dec[ez < 0 ? 0 : ez];
+                const uint4 x = vpre[m];
+                uint4 xz;
+                if constexpr (BF16) {
+                    const u16x8 e = __builtin_bit_cast(u16x8, x);
+                    u16x8 z;
 #pragma unroll
-            for (int u = 0; u < QU; ++u) {
-                uint4 x = qnext[s][u];
-                if constexpr (LIN) x = apply_phi16(x);
-                qcur[s][u] = qvalid ? x : uint4{0, 0, 0, 0};
+                    for (int i = 0; i < 8; ++i) z[i] = f2bf(bf2f(e[i]) * zeta);
+                    xz = __builtin_bit_cast(uint4, z);
+                } else {
+                    xz = __builtin_bit_cast(uint4, __builtin_bit_cast(f32x4, x) * zeta);
+                }
+                *reinterpret_cast<uint4*>(&sm.Vs[row * VSTR + col * EPV]) = x;
+                *reinterpret_cast<uint4*>(&sm.Vz[row * VSTR + col * EPV]) = xz;
+            }
+        }
+        // ---- this chunk's Q in registers (fp32 path)
+        if constexpr (!QLDS) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int u = 0; u < QU; ++u) {
+                    uint4 x = qnext[s][u];
+                    if constexpr (LIN) x = apply_phi16(x);
+                    qcur[s][u] = x;
+                }
+        }
+        // ---- linear attention, short last chunk: phi(0) = 1, so padded rows
+        // ---- (loaded as zeros) are zeroed again after the feature map
+        if (LIN && tail) {
+#pragma unroll
+            for (int m = 0; m < KU; ++m) {
+                const int u = tid + m * kThreads;
+                const int row = u / RU, col = u % RU;
+                if (row >= clen) {
+                    *reinterpret_cast<uint4*>(&sm.Ks[row * KSTR + col * EPV]) = uint4{0, 0, 0, 0};
+                    if constexpr (QLDS) *reinterpret_cast<uint4*>(&sm.Qs[row * KSTR + col * EPV]) = uint4{0, 0, 0, 0};
+                }
+            }
+            if constexpr (!QLDS) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s)
+                    if (its(s) * 16 + l16 >= clen)
+#pragma unroll
+                        for (int u = 0; u < QU; ++u) qcur[s][u] = uint4{0, 0, 0, 0};
             }
         }
         __syncthreads();
 
         if (c + 1 < nch) load_chunk(c + 1);
+
+        // ---------------- Q operands of this wave's query tiles
+        uint4 qb[NS][QU];
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int u = 0; u < QU; ++u) {
+                if constexpr (QLDS)
+                    qb[s][u] = *reinterpret_cast<const uint4*>(&sm.Qs[(its(s) * 16 + l16) * KSTR + 32 * u + 8 * g]);
+                else
+                    qb[s][u] = qcur[s][u];
+            }
 
         // ---------------- S^T tiles = K Q^T for key tiles jt <= query tile
         f32x4 pacc[NS][NI];
@@ -331,7 +378,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 for (int jt = 0; jt <= ITMAX; ++jt)
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
-                        if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], as_bf16x8(qcur[s][ks]), pacc[s][jt]);
+                        if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], as_bf16x8(qb[s][ks]), pacc[s][jt]);
             }
         } else {
 #pragma unroll
@@ -347,7 +394,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
                         for (int s = 0; s < NS; ++s)
                             if (jt <= its(s)) {
-                                const f32x4 q4 = __builtin_bit_cast(f32x4, qcur[s][u]);
+                                const f32x4 q4 = __builtin_bit_cast(f32x4, qb[s][u]);
                                 pacc[s][jt] = mfma_f32(ka[jt][e], q4[e], pacc[s][jt]);
                             }
             }
@@ -403,7 +450,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 for (int ks = 0; ks < DK / 32; ++ks) {
                     const bf16x8 av = as_bf16x8(*reinterpret_cast<const uint4*>(srow + 32 * ks + 8 * g));
 #pragma unroll
-                    for (int s = 0; s < NS; ++s) oacc[s][nt] = mfma_bf16(av, as_bf16x8(qcur[s][ks]), oacc[s][nt]);
+                    for (int s = 0; s < NS; ++s) oacc[s][nt] = mfma_bf16(av, as_bf16x8(qb[s][ks]), oacc[s][nt]);
                 }
             } else {
 #pragma unroll
@@ -413,7 +460,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                     for (int e = 0; e < 4; ++e)
 #pragma unroll
                         for (int s = 0; s < NS; ++s) {
-                            const f32x4 q4 = __builtin_bit_cast(f32x4, qcur[s][u]);
+                            const f32x4 q4 = __builtin_bit_cast(f32x4, qb[s][u]);
                             oacc[s][nt] = mfma_f32(a4[e], q4[e], oacc[s][nt]);
                         }
                 }
@@ -428,10 +475,9 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             if constexpr (BF16) {
 #pragma unroll
                 for (int p = 0; 2 * p <= ITMAX; ++p) {
-                    const E* v0 = &sm.V4s[((8 * p + g) * DVS + nt * 16 + l16) * 4];
-                    const E* v1 = &sm.V4s[((8 * p + 4 + g) * DVS + nt * 16 + l16) * 4];
-                    const bf16x8 av = cat_bf16(*reinterpret_cast<const u16x4*>(v0),
-                                               *reinterpret_cast<const u16x4*>(v1));
+                    // A = V^T: tokens 32p + 4g + {0..3} and 32p + 16 + 4g + {0..3} of column l16
+                    const E* v0 = &sm.Vs[(32 * p + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
+                    const bf16x8 av = cat_bf16(lds_tr4(v0), lds_tr4(v0 + 16 * VSTR));
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
                         if (2 * p <= its(s)) oacc[s][nt] = mfma_bf16(av, pb[s][p], oacc[s][nt]);
@@ -439,12 +485,13 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             } else {
 #pragma unroll
                 for (int jt = 0; jt <= ITMAX; ++jt) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.V4s[((4 * jt + g) * DVS + nt * 16 + l16) * 4]);
 #pragma unroll
-                    for (int s = 0; s < NS; ++s)
-                        if (jt <= its(s))
+                    for (int r = 0; r < 4; ++r) {
+                        const float av = sm.Vs[(jt * 16 + 4 * g + r) * VSTR + nt * 16 + l16];
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) oacc[s][nt] = mfma_f32(a4[r], pacc[s][jt][r], oacc[s][nt]);
+                        for (int s = 0; s < NS; ++s)
+                            if (jt <= its(s)) oacc[s][nt] = mfma_f32(av, pacc[s][jt][r], oacc[s][nt]);
+                    }
                 }
             }
         }
@@ -459,11 +506,11 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
                 for (int u = 0; u < QU; ++u) {
                     if constexpr (BF16) {
-                        const u16x8 e = __builtin_bit_cast(u16x8, qcur[s][u]);
+                        const u16x8 e = __builtin_bit_cast(u16x8, qb[s][u]);
 #pragma unroll
                         for (int i = 0; i < 8; ++i) dq += bf2f(e[i]) * zc[32 * u + 8 * g + i];
                     } else {
-                        const f32x4 e = __builtin_bit_cast(f32x4, qcur[s][u]);
+                        const f32x4 e = __builtin_bit_cast(f32x4, qb[s][u]);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dq += e[i] * zc[(DK / 4) * g + 4 * u + i];
                     }
@@ -471,17 +518,18 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 rden[s] = 1.f / (sum_over_groups(rsum[s] + dq) + a.eps);
             }
         }
+        {
+            const auto ro = make_rsrc(oh + static_cast<long long>(t0) * DV, clen * DV * Cf::ESZ);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const int row = its(s) * 16 + l16;
-            if (row < clen) {
-                E* orow = og + static_cast<long long>(t0 + row) * DV + nbase + 4 * g;
+            for (int s = 0; s < NS; ++s) {
+                const int row = its(s) * 16 + l16;  // rows past the end are dropped by the resource
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     f32x4 o = oacc[s][nt];
                     if constexpr (LIN) o *= rden[s];
-                    if constexpr (BF16) *reinterpret_cast<u16x4*>(orow + nt * 16) = cvt4_bf16(o);
-                    else *reinterpret_cast<f32x4*>(orow + nt * 16) = o;
+                    const unsigned off = static_cast<unsigned>((row * DV + nt * 16 + 4 * g) * Cf::ESZ);
+                    if constexpr (BF16) bstore8(ro, off, cvt4_bf16(o));
+                    else bstore16(ro, off, o);
                 }
             }
         }
@@ -499,16 +547,11 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             if constexpr (BF16) {
 #pragma unroll
                 for (int js = 0; js < C / 32; ++js) {
-                    const E* v0 = &sm.V4z[((8 * js + g) * DVS + nt * 16 + l16) * 4];
-                    const E* v1 = &sm.V4z[((8 * js + 4 + g) * DVS + nt * 16 + l16) * 4];
-                    const bf16x8 av = cat_bf16(*reinterpret_cast<const u16x4*>(v0),
-                                               *reinterpret_cast<const u16x4*>(v1));
-                    u16x4 blo, bhi;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        blo[r] = sm.Ks[(js * 32 + 4 * g + r) * KSTR + kcol];
-                        bhi[r] = sm.Ks[(js * 32 + 16 + 4 * g + r) * KSTR + kcol];
-                    }
+                    // A = (zeta V)^T, B = K: tokens 32js + 4g + {0..3}, 32js + 16 + 4g + {0..3}
+                    const E* v0 = &sm.Vz[(32 * js + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
+                    const E* k0 = &sm.Ks[(32 * js + 4 * g + lq) * KSTR + kt * 16 + 4 * lr];
+                    const bf16x8 av = cat_bf16(lds_tr4(v0), lds_tr4(v0 + 16 * VSTR));
+                    const u16x4 blo = lds_tr4(k0), bhi = lds_tr4(k0 + 16 * KSTR);
                     acc = mfma_bf16(av, cat_bf16(blo, bhi), acc);
                     if (LIN && nt == 0) {
 #pragma unroll
@@ -518,11 +561,11 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             } else {
 #pragma unroll
                 for (int jt = 0; jt < NI; ++jt) {
-                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sm.V4z[((4 * jt + g) * DVS + nt * 16 + l16) * 4]);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
+                        const float av = sm.Vz[(jt * 16 + 4 * g + r) * VSTR + nt * 16 + l16];
                         const float b = sm.Ks[(jt * 16 + 4 * g + r) * KSTR + kcol];
-                        acc = mfma_f32(a4[r], b, acc);
+                        acc = mfma_f32(av, b, acc);
                         if (LIN && nt == 0) zsum += b;
                     }
                 }
@@ -542,12 +585,12 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 
     // ---------------- final state [dk][dv] fp32
     if (a.final_state) {
-        float* fs = a.final_state + static_cast<long long>(bh) * DK * DV;
+        float* fs = a.final_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
             const int qt = W + 4 * m;
             const int nt = qt / KT, kt = qt % KT;
-            *reinterpret_cast<f32x4*>(fs + static_cast<long long>(kt * 16 + l16) * DV + nbase + nt * 16 + 4 * g) = sacc[m];
+            *reinterpret_cast<f32x4*>(fs + (kt * 16 + l16) * DV + nt * 16 + 4 * g) = sacc[m];
         }
     }
 }
