@@ -112,7 +112,7 @@ int retention_fwd(const void* q, const void* k, const void* v, const float* gamm
     }
     if (B == 0) return ok();
     const long long bh = static_cast<long long>(B) * H;
-    const int nt = ret::choose_walk_nt(bh, dv, 256);
+    const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, chunk, dk);
     a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = final_state;
     a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = 0.f;
     const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, chunk, dk, nt, false,
@@ -187,7 +187,7 @@ int linear_attn_fwd(const void* q, const void* k, const void* v, int phi, void* 
     if (B == 0) return ok();
     ret::WalkArgs a{};
     const long long bh = static_cast<long long>(B) * H;
-    const int nt = ret::choose_walk_nt(bh, dv, 256);
+    const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, 128, dk);
     a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = nullptr;
     a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = eps;
     const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, 128, dk, nt, true,

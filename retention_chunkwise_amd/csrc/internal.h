@@ -50,6 +50,6 @@ hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
 
 // Choice of value-slice width (in 16-column MFMA tiles) for the chunk walk:
 // the widest slice that still gives at least `target_groups` workgroups.
-int choose_walk_nt(long long bh, int dv, int target_groups);
+int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk, int dk);
 
 }  // namespace ret

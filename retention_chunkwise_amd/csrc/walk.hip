@@ -3,9 +3,11 @@
 
 namespace ret {
 
-int choose_walk_nt(long long bh, int dv, int target_groups) {
+int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk, int dk) {
     // widest value slice (fewer recomputed Q K^T tiles) that still yields
-    // enough workgroups to occupy every compute unit
+    // enough workgroups to occupy every compute unit; the bf16 variant with
+    // chunk 128, dk 128 and 32-column slices does not fit in LDS
+    if (bf16 && chunk == 128 && dk == 128) return 1;
     int best = 1;
     if (dv % 32 == 0 && bh * (dv / 32) >= target_groups) best = 2;
     return best;

@@ -128,6 +128,48 @@ __device__ __forceinline__ void bstore16(__amdgpu_buffer_rsrc_t r, unsigned off,
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, static_cast<int>(off), 0, 0);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Buffer resource words for the LDS-DMA loads (same layout as make_rsrc).
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
+    const unsigned long long p = reinterpret_cast<unsigned long long>(base);
+    u32x4 r;
+    r[0] = static_cast<unsigned>(p);
+    r[1] = static_cast<unsigned>(p >> 32) & 0xffffu;  // stride 0
+    r[2] = static_cast<unsigned>(bytes);
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// 16 bytes per lane from a range-checked buffer straight into LDS: lane l's
+// data lands at LDS byte `lds_addr` + 16 l (lds_addr must be wave-uniform).
+// Issued as inline asm on purpose: the compiler's own wait insertion treats
+// any LDS-DMA as possibly aliasing every later LDS read and would wait for the
+// prefetch right after issuing it.  The kernels wait for these loads
+// explicitly (wait_vmcnt) before the barrier that precedes any read.  M0 is
+// written here and nowhere else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const u32x4& rsrc, unsigned lds_addr, unsigned voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voff), "s"(rsrc)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <typename T>
+__device__ __forceinline__ unsigned lds_addr_of(const T* p) {
+    typedef __attribute__((address_space(3))) const T lds_t;
+    return static_cast<unsigned>(reinterpret_cast<unsigned long>((lds_t*)(p)));
+}
+
 template <bool BF16, int C, int DK, int NT, bool LIN>
 struct Cfg {
     typedef typename std::conditional<BF16, unsigned short, float>::type E;
@@ -136,55 +178,84 @@ struct Cfg {
     static constexpr int DVS = 16 * NT;               // value columns per workgroup
     static constexpr int ESZ = BF16 ? 2 : 4;          // element bytes
     static constexpr int EPV = 16 / ESZ;              // elements per 16-byte vector
-    static constexpr int KSTR = DK + EPV;             // row stride of Q / K / state copy (16-B pad)
+    static constexpr int KSTR = DK + EPV;             // padded row stride (fp32 K, state copy)
     static constexpr int VSTR = DVS;                  // row stride of the V slice copies
     static constexpr int KT = DK / 16;                // 16-wide key tiles
     static constexpr int SPW = NT * KT / 4;           // state tiles per wave
     static constexpr int KU = C * DK * ESZ / 16 / kThreads;  // 16-B units of a Q / K chunk per thread
-    static constexpr int RU = DK * ESZ / 16;          // 16-B units per Q / K row
+    static constexpr int RU = DK * ESZ / 16;          // 16-B units (slots) per Q / K row
+    static constexpr int RB = DK * ESZ;               // bytes per Q / K row
     static constexpr int VRU = DVS * ESZ / 16;        // 16-B units per V-slice row
     static constexpr int VUT = C * VRU;               // V-slice units per chunk
     static constexpr int VPT = (VUT + kThreads - 1) / kThreads;
-    static constexpr bool QLDS = BF16;                // bf16: Q staged in LDS; fp32: per wave in registers
+    // bf16: Q and K go HBM -> LDS by DMA into double-buffered, unpadded,
+    // slot-swizzled tiles; fp32: K staged through registers into padded rows,
+    // Q kept in registers by the wave that uses it.
+    static constexpr bool DMA = BF16;
     static constexpr int QU = DK * ESZ / 64;          // 16-B Q units per lane per tile
+    static constexpr int KI = C * DK * ESZ / 1024;    // 1-KB DMA instructions per Q / K chunk
+    static constexpr int VI = C * DVS * ESZ / 1024;   // 1-KB DMA instructions per V slice chunk
     static constexpr int DEC = C + 32;                // decay table entries
     static_assert(NI == 4 || NI == 8, "chunk must be 64 or 128");
     static_assert(DK == 64 || DK == 128, "dk must be 64 or 128");
     static_assert(NT * KT % 4 == 0, "state tiles must split over 4 waves");
     static_assert(C * DK * ESZ / 16 % kThreads == 0, "Q/K staging split");
+    static_assert(!DMA || RU == 8 || RU == 16, "swizzle assumes 8 or 16 slots per row");
 };
+
+// Byte offset of 16-byte slot `col16` of row `r` in a swizzled Q / K tile.
+// Rows are unpadded; slots are XOR-permuted so that 16 consecutive rows read
+// at one column hit 16 different bank groups.
+template <int RU>
+__device__ __forceinline__ int swz_off(int r, int col16) {
+    const int x = (RU == 16) ? (r & 15) : ((r >> 1) & 7);
+    return r * (RU * 16) + ((col16 ^ x) << 4);
+}
 
 template <bool BF16, int C, int DK, int NT, bool LIN>
 struct Smem {
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
-    alignas(16) E Qs[Cf::QLDS ? C * Cf::KSTR : 8];   // Q (or phi(Q)) rows (bf16 only)
-    alignas(16) E Ks[C * Cf::KSTR];                  // K (or phi(K)) rows
-    alignas(16) E Vs[C * Cf::VSTR];                  // V slice, row-major
-    alignas(16) E Vz[C * Cf::VSTR];                  // zeta-scaled V slice
-    alignas(16) E Sts[2][Cf::DVS * Cf::KSTR];        // S^T copy, [n][k], double-buffered
-    alignas(16) float dec[Cf::DEC];                  // [16 + m] = gamma^m, [0..15] = 0
-    alignas(16) float zs[2][LIN ? DK : 4];           // normaliser z (linear attention)
+    static constexpr bool DMA = Cf::DMA;
+    alignas(16) float dec[Cf::DEC];                   // [16 + m] = gamma^m, [0..15] = 0
+    alignas(16) float zs[2][LIN ? DK : 4];            // normaliser z (linear attention)
+    alignas(16) E Sts[2][Cf::DVS * Cf::KSTR];         // S^T copy, [n][k], double-buffered
+    alignas(16) E Vs[Cf::DMA ? 8 : C * Cf::VSTR];     // V slice, row-major (fp32 path)
+    alignas(16) E Vz[C * Cf::VSTR];                   // zeta-scaled V slice
+    alignas(16) E Ks[DMA ? 8 : C * Cf::KSTR];         // K rows, padded (fp32)
+};
+
+// The double-buffered Q / K chunk tiles of the DMA path.  Each buffer is its
+// own __shared__ array, so the compiler can tell that a DMA into one buffer
+// does not touch the other and need not wait for it before reading.
+template <typename E>
+struct QKTiles {
+    E* q[2];
+    E* k[2];
+    E* v[2];  // the V slice, row-major
 };
 
 template <bool BF16, int C, int DK, int NT, bool LIN, int W>
 __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, NT, LIN>& sm,
+                                          const QKTiles<typename Cfg<BF16, C, DK, NT, LIN>::E>& qk,
                                           const int bh, const int nbase, const float lg) {
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
-    constexpr int NI = Cf::NI, NS = Cf::NS, DVS = Cf::DVS, KSTR = Cf::KSTR, EPV = Cf::EPV;
+    constexpr int NI = Cf::NI, NS = Cf::NS, KSTR = Cf::KSTR, EPV = Cf::EPV;
     constexpr int VSTR = Cf::VSTR, KT = Cf::KT, SPW = Cf::SPW, KU = Cf::KU, RU = Cf::RU;
-    constexpr int VRU = Cf::VRU, VUT = Cf::VUT, VPT = Cf::VPT, QU = Cf::QU;
-    constexpr bool QLDS = Cf::QLDS;
+    constexpr int VRU = Cf::VRU, VUT = Cf::VUT, VPT = Cf::VPT, QU = Cf::QU, ESZ = Cf::ESZ;
+    constexpr bool DMA = Cf::DMA;
     constexpr int IT0 = W;                                // query tiles of this wave
     constexpr int IT1 = (NS == 2) ? NI - 1 - W : W;
     constexpr int ITMAX = IT1;                            // IT1 >= IT0
+    // vector-memory ops a thread issues after a chunk's Q/K (and V) loads:
+    // the V loads and the output stores of the chunk being computed
+    constexpr int STORES = NS * NT;
 
     const int tid = threadIdx.x;
     const int l = tid & 63, l16 = l & 15, g = l >> 4;
     const int lq = l16 >> 2, lr = l16 & 3;                // transpose-read lane roles
     const int T = a.T, DV = a.dv;
-    // this (b, h)'s rows; the V / O pointers already point at this slice's columns
     const E* __restrict__ qh = static_cast<const E*>(a.q) + static_cast<long long>(bh) * T * DK;
     const E* __restrict__ kh = static_cast<const E*>(a.k) + static_cast<long long>(bh) * T * DK;
     const E* __restrict__ vh = static_cast<const E*>(a.v) + static_cast<long long>(bh) * T * DV + nbase;
@@ -210,44 +281,83 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    uint4 kpre[KU];
-    uint4 qpre[QLDS ? KU : 1];
-    uint4 vpre[VPT];
-    uint4 qnext[NS][QLDS ? 1 : QU];
-    uint4 qcur[NS][QLDS ? 1 : QU];
+    // DMA path: 1-KB instruction i of a chunk is issued by wave i % 4 and fills
+    // LDS bytes [1024 i, +1024) of its tile; lane l's 16 bytes land at +16 l.
+    // The per-lane source offsets inside a chunk are loop invariant.
+    constexpr int KIW = DMA ? Cf::KI / 4 : 1;                        // Q/K instructions per wave
+    constexpr int VIW = DMA ? (Cf::VI > W ? (Cf::VI - W + 3) / 4 : 0) : 0;  // V instructions per wave
+    int goff[KIW];
+    int gvoff[VIW > 0 ? VIW : 1];
+    if constexpr (DMA) {
+#pragma unroll
+        for (int m = 0; m < KIW; ++m) {
+            const int b = (W + 4 * m) * 1024 + l * 16;
+            const int r = b / (RU * 16), slot = (b % (RU * 16)) >> 4;
+            const int x = (RU == 16) ? (r & 15) : ((r >> 1) & 7);
+            goff[m] = r * (RU * 16) + ((slot ^ x) << 4);
+        }
+#pragma unroll
+        for (int m = 0; m < VIW; ++m) {
+            const int b = (W + 4 * m) * 1024 + l * 16;
+            const int r = b / (VRU * 16), unit = (b % (VRU * 16)) >> 4;
+            gvoff[m] = r * DV * ESZ + unit * 16;
+        }
+    }
 
-    // Loads of one chunk into registers through range-checked buffer
-    // resources: rows past the end of the sequence read as zeros.  No
-    // instruction consumes a prefetched value in the iteration that issues it.
-    auto load_chunk = [&](int c) {
+    uint4 kpre[DMA ? 1 : KU];
+    uint4 vpre[DMA ? 1 : VPT];
+    uint4 qnext[NS][DMA ? 1 : QU];
+    uint4 qcur[NS][DMA ? 1 : QU];
+
+    // Issue the loads of chunk c (into LDS buffer `buf` on the DMA path) through
+    // range-checked buffer resources: rows past the end of the sequence read as
+    // zeros.  No instruction consumes these values in the step that issues them.
+    auto load_chunk = [&](int c, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const int t0 = c * C;
         const int cl = (T - t0 < C) ? (T - t0) : C;
-        const auto rk = make_rsrc(kh + static_cast<long long>(t0) * DK, cl * DK * Cf::ESZ);
-        const auto rq = make_rsrc(qh + static_cast<long long>(t0) * DK, cl * DK * Cf::ESZ);
-        const auto rv = make_rsrc(vh + static_cast<long long>(t0) * DV, cl * DV * Cf::ESZ);
+        const auto rk = make_rsrc(kh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
+        const auto rq = make_rsrc(qh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
+        const auto rv = make_rsrc(vh + static_cast<long long>(t0) * DV, cl * DV * ESZ);
+        if constexpr (DMA) {
+            const u32x4 wk = rsrc_words(kh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
+            const u32x4 wq = rsrc_words(qh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
+            const u32x4 wv = rsrc_words(vh + static_cast<long long>(t0) * DV, cl * DV * ESZ);
+            const unsigned kbase = __builtin_amdgcn_readfirstlane(lds_addr_of(qk.k[buf]));
+            const unsigned qbase = __builtin_amdgcn_readfirstlane(lds_addr_of(qk.q[buf]));
+            const unsigned vbase = __builtin_amdgcn_readfirstlane(lds_addr_of(qk.v[buf]));
 #pragma unroll
-        for (int m = 0; m < KU; ++m) {
-            const int u = tid + m * kThreads;
-            const int row = u / RU, col = u % RU;
-            const unsigned off = static_cast<unsigned>((row * DK + col * EPV) * Cf::ESZ);
-            kpre[m] = bload16(rk, off);
-            if constexpr (QLDS) qpre[m] = bload16(rq, off);
-        }
-#pragma unroll
-        for (int m = 0; m < VPT; ++m) {
-            const int u = tid + m * kThreads;
-            if (VUT % kThreads == 0 || u < VUT) {
-                const int row = u / VRU, col = u % VRU;
-                vpre[m] = bload16(rv, static_cast<unsigned>((row * DV + col * EPV) * Cf::ESZ));
+            for (int m = 0; m < KIW; ++m) {
+                const unsigned o = (W + 4 * m) * 1024;  // LDS bytes this instruction fills
+                dma16(wk, kbase + o, static_cast<unsigned>(goff[m]));
+                dma16(wq, qbase + o, static_cast<unsigned>(goff[m]));
             }
-        }
-        if constexpr (!QLDS) {
+#pragma unroll
+            for (int m = 0; m < VIW; ++m)
+                dma16(wv, vbase + (W + 4 * m) * 1024, static_cast<unsigned>(gvoff[m]));
+        } else {
+#pragma unroll
+            for (int m = 0; m < KU; ++m) {
+                const int u = tid + m * kThreads;
+                const int row = u / RU, col = u % RU;
+                kpre[m] = bload16(rk, static_cast<unsigned>((row * DK + col * EPV) * ESZ));
+            }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int row = its(s) * 16 + l16;
 #pragma unroll
                 for (int u = 0; u < QU; ++u)  // k = (DK/4) g + 4u .. +3
-                    qnext[s][u] = bload16(rq, static_cast<unsigned>((row * DK + (DK / 4) * g + 4 * u) * Cf::ESZ));
+                    qnext[s][u] = bload16(rq, static_cast<unsigned>((row * DK + (DK / 4) * g + 4 * u) * ESZ));
+            }
+        }
+        if constexpr (!DMA) {
+#pragma unroll
+            for (int m = 0; m < VPT; ++m) {
+                const int u = tid + m * kThreads;
+                if (VUT % kThreads == 0 || u < VUT) {
+                    const int row = u / VRU, col = u % VRU;
+                    vpre[m] = bload16(rv, static_cast<unsigned>((row * DV + col * EPV) * ESZ));
+                }
             }
         }
     };
@@ -266,31 +376,74 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         }
     };
 
-    const int nch = (T + C - 1) / C;
-    if (nch > 0) load_chunk(0);
+    // Operand reads of Q / K tiles (A or B operand of the Q K^T MFMA): row r,
+    // 16-byte unit u of the k-slots this lane owns.
+    auto k_unit = [&](auto bufc, int r, int u) -> uint4 {
+        constexpr int buf = decltype(bufc)::value;
+        if constexpr (DMA)
+            return *reinterpret_cast<const uint4*>(&qk.k[buf][swz_off<RU>(r, u) / ESZ]);
+        else
+            return *reinterpret_cast<const uint4*>(&sm.Ks[r * KSTR + u * EPV]);
+    };
 
-    for (int c = 0; c < nch; ++c) {
+    const int nch = (T + C - 1) / C;
+
+    // One chunk.  B is the LDS buffer holding this chunk's Q / K (DMA path)
+    // and the state-copy buffer the chunk reads; chunk c + 1 goes to 1 - B.
+    auto step = [&](int c, auto bufc) {
+        constexpr int B = decltype(bufc)::value;
+        constexpr int NB = 1 - B;
         const int t0 = c * C;
         const int clen = (T - t0 < C) ? (T - t0) : C;
         const bool tail = clen < C;  // uniform: only the last chunk can be short
-        const int cur = c & 1, nxt = cur ^ 1;
 
-        __syncthreads();  // all reads of the previous chunk's LDS tiles are done
-        // ---- stage Q and K rows
+        // This chunk's loads were issued one step ago, and the only vector-memory
+        // ops issued after them are the previous step's output stores (vector
+        // memory ops complete in issue order).  Before the first step nothing
+        // else is in flight, so wait for everything.
+        if (c == 0) wait_vmcnt<0>();
+        else wait_vmcnt<STORES>();
+        __syncthreads();  // loads landed everywhere; previous chunk's LDS reads done
+
+        // ---- stage: K rows (fp32), the V slice (plain and zeta-scaled), feature maps
+        if constexpr (!DMA) {
 #pragma unroll
-        for (int m = 0; m < KU; ++m) {
-            const int u = tid + m * kThreads;
-            const int row = u / RU, col = u % RU;
-            uint4 x = kpre[m];
-            if constexpr (LIN) x = apply_phi16(x);
-            *reinterpret_cast<uint4*>(&sm.Ks[row * KSTR + col * EPV]) = x;
-            if constexpr (QLDS) {
-                uint4 y = qpre[m];
-                if constexpr (LIN) y = apply_phi16(y);
-                *reinterpret_cast<uint4*>(&sm.Qs[row * KSTR + col * EPV]) = y;
+            for (int m = 0; m < KU; ++m) {
+                const int u = tid + m * kThreads;
+                const int row = u / RU, col = u % RU;
+                uint4 x = kpre[m];
+                if constexpr (LIN) x = apply_phi16(x);
+                if (LIN && tail && row >= clen) x = uint4{0, 0, 0, 0};
+                *reinterpret_cast<uint4*>(&sm.Ks[row * KSTR + col * EPV]) = x;
+            }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                const bool pad = LIN && tail && (its(s) * 16 + l16 >= clen);
+#pragma unroll
+                for (int u = 0; u < QU; ++u) {
+                    uint4 x = qnext[s][u];
+                    if constexpr (LIN) x = apply_phi16(x);
+                    qcur[s][u] = pad ? uint4{0, 0, 0, 0} : x;
+                }
+            }
+        } else if constexpr (LIN) {
+            // phi on this thread's DMA units of Q and K, in place; rows past the
+            // end (loaded as zeros) must stay zero, not phi(0) = 1
+#pragma unroll
+            for (int m = 0; m < KU; ++m) {
+                const int b = (W * KU + m) * 1024 + l * 16;
+                const int r = b / (RU * 16);
+                uint4* pk = reinterpret_cast<uint4*>(&qk.k[B][b / ESZ]);
+                uint4* pq = reinterpret_cast<uint4*>(&qk.q[B][b / ESZ]);
+                const unsigned keep = (tail && r >= clen) ? 0u : ~0u;  // bit mask, not a select
+                uint4 xk = apply_phi16(*pk);
+                uint4 xq = apply_phi16(*pq);
+                xk.x &= keep; xk.y &= keep; xk.z &= keep; xk.w &= keep;
+                xq.x &= keep; xq.y &= keep; xq.z &= keep; xq.w &= keep;
+                *pk = xk;
+                *pq = xq;
             }
         }
-        // ---- stage the V slice, plain and zeta-scaled (zeta_j = gamma^(c-1-j))
 #pragma unroll
         for (int m = 0; m < VPT; ++m) {
             const int u = tid + m * kThreads;
@@ -298,7 +451,9 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 const int row = u / VRU, col = u % VRU;
                 const int ez = 16 + clen - 1 - row;  // gamma^(c-1-j); 0 past the end
                 const float zeta = sm.dec[ez < 0 ? 0 : ez];
-                const uint4 x = vpre[m];
+                uint4 x;
+                if constexpr (DMA) x = *reinterpret_cast<const uint4*>(&qk.v[B][row * VSTR + col * EPV]);
+                else x = vpre[m];
                 uint4 xz;
                 if constexpr (BF16) {
                     const u16x8 e = __builtin_bit_cast(u16x8, x);
@@ -309,44 +464,13 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 } else {
                     xz = __builtin_bit_cast(uint4, __builtin_bit_cast(f32x4, x) * zeta);
                 }
-                *reinterpret_cast<uint4*>(&sm.Vs[row * VSTR + col * EPV]) = x;
+                if constexpr (!DMA) *reinterpret_cast<uint4*>(&sm.Vs[row * VSTR + col * EPV]) = x;
                 *reinterpret_cast<uint4*>(&sm.Vz[row * VSTR + col * EPV]) = xz;
-            }
-        }
-        // ---- this chunk's Q in registers (fp32 path)
-        if constexpr (!QLDS) {
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-                for (int u = 0; u < QU; ++u) {
-                    uint4 x = qnext[s][u];
-                    if constexpr (LIN) x = apply_phi16(x);
-                    qcur[s][u] = x;
-                }
-        }
-        // ---- linear attention, short last chunk: phi(0) = 1, so padded rows
-        // ---- (loaded as zeros) are zeroed again after the feature map
-        if (LIN && tail) {
-#pragma unroll
-            for (int m = 0; m < KU; ++m) {
-                const int u = tid + m * kThreads;
-                const int row = u / RU, col = u % RU;
-                if (row >= clen) {
-                    *reinterpret_cast<uint4*>(&sm.Ks[row * KSTR + col * EPV]) = uint4{0, 0, 0, 0};
-                    if constexpr (QLDS) *reinterpret_cast<uint4*>(&sm.Qs[row * KSTR + col * EPV]) = uint4{0, 0, 0, 0};
-                }
-            }
-            if constexpr (!QLDS) {
-#pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    if (its(s) * 16 + l16 >= clen)
-#pragma unroll
-                        for (int u = 0; u < QU; ++u) qcur[s][u] = uint4{0, 0, 0, 0};
             }
         }
         __syncthreads();
 
-        if (c + 1 < nch) load_chunk(c + 1);
+        if (c + 1 < nch) load_chunk(c + 1, std::integral_constant<int, NB>{});
 
         // ---------------- Q operands of this wave's query tiles
         uint4 qb[NS][QU];
@@ -354,8 +478,8 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int u = 0; u < QU; ++u) {
-                if constexpr (QLDS)
-                    qb[s][u] = *reinterpret_cast<const uint4*>(&sm.Qs[(its(s) * 16 + l16) * KSTR + 32 * u + 8 * g]);
+                if constexpr (DMA)
+                    qb[s][u] = *reinterpret_cast<const uint4*>(&qk.q[B][swz_off<RU>(its(s) * 16 + l16, 4 * u + g) / ESZ]);
                 else
                     qb[s][u] = qcur[s][u];
             }
@@ -372,8 +496,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             for (int ks = 0; ks < DK / 32; ++ks) {
                 bf16x8 ka[ITMAX + 1];
 #pragma unroll
-                for (int jt = 0; jt <= ITMAX; ++jt)
-                    ka[jt] = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.Ks[(jt * 16 + l16) * KSTR + 32 * ks + 8 * g]));
+                for (int jt = 0; jt <= ITMAX; ++jt) ka[jt] = as_bf16x8(k_unit(bufc, jt * 16 + l16, 4 * ks + g));
 #pragma unroll
                 for (int jt = 0; jt <= ITMAX; ++jt)
 #pragma unroll
@@ -439,7 +562,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 
         // ---------------- O^T = S_prev^T (xi Q)^T + V^T P^T
         f32x4 oacc[NS][NT];
-        const E* st = sm.Sts[cur];
+        const E* st = sm.Sts[B];
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -476,7 +599,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
                 for (int p = 0; 2 * p <= ITMAX; ++p) {
                     // A = V^T: tokens 32p + 4g + {0..3} and 32p + 16 + 4g + {0..3} of column l16
-                    const E* v0 = &sm.Vs[(32 * p + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
+                    const E* v0 = &qk.v[B][(32 * p + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
                     const bf16x8 av = cat_bf16(lds_tr4(v0), lds_tr4(v0 + 16 * VSTR));
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
@@ -499,7 +622,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         // ---------------- normalise (linear attention) and store O
         float rden[NS];
         if constexpr (LIN) {
-            const float* zc = sm.zs[cur];
+            const float* zc = sm.zs[B];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 float dq = 0.f;  // phi(q_i) . z over this lane's key slots
@@ -519,7 +642,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
         }
         {
-            const auto ro = make_rsrc(oh + static_cast<long long>(t0) * DV, clen * DV * Cf::ESZ);
+            const auto ro = make_rsrc(oh + static_cast<long long>(t0) * DV, clen * DV * ESZ);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
                 const int row = its(s) * 16 + l16;  // rows past the end are dropped by the resource
@@ -527,7 +650,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 for (int nt = 0; nt < NT; ++nt) {
                     f32x4 o = oacc[s][nt];
                     if constexpr (LIN) o *= rden[s];
-                    const unsigned off = static_cast<unsigned>((row * DV + nt * 16 + 4 * g) * Cf::ESZ);
+                    const unsigned off = static_cast<unsigned>((row * DV + nt * 16 + 4 * g) * ESZ);
                     if constexpr (BF16) bstore8(ro, off, cvt4_bf16(o));
                     else bstore16(ro, off, o);
                 }
@@ -536,7 +659,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 
         // ---------------- state: S^T <- gamma^c S^T + (zeta V)^T K   (and z += sum phi(k))
         const float gc = sm.dec[16 + clen];
-        E* stn = sm.Sts[nxt];
+        E* stn = sm.Sts[NB];
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
             const int qt = W + 4 * m;
@@ -549,9 +672,11 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 for (int js = 0; js < C / 32; ++js) {
                     // A = (zeta V)^T, B = K: tokens 32js + 4g + {0..3}, 32js + 16 + 4g + {0..3}
                     const E* v0 = &sm.Vz[(32 * js + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
-                    const E* k0 = &sm.Ks[(32 * js + 4 * g + lq) * KSTR + kt * 16 + 4 * lr];
                     const bf16x8 av = cat_bf16(lds_tr4(v0), lds_tr4(v0 + 16 * VSTR));
-                    const u16x4 blo = lds_tr4(k0), bhi = lds_tr4(k0 + 16 * KSTR);
+                    const int r0 = 32 * js + 4 * g + lq;
+                    const int c16 = 2 * kt + (lr >> 1), half = (lr & 1) * 8;
+                    const u16x4 blo = lds_tr4(&qk.k[B][(swz_off<RU>(r0, c16) + half) / ESZ]);
+                    const u16x4 bhi = lds_tr4(&qk.k[B][(swz_off<RU>(r0 + 16, c16) + half) / ESZ]);
                     acc = mfma_bf16(av, cat_bf16(blo, bhi), acc);
                     if (LIN && nt == 0) {
 #pragma unroll
@@ -578,9 +703,15 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
             if (LIN && nt == 0) {
                 zsum = sum_over_groups(zsum);
-                if (g == 0) sm.zs[nxt][kcol] = sm.zs[cur][kcol] + zsum;
+                if (g == 0) sm.zs[NB][kcol] = sm.zs[B][kcol] + zsum;
             }
         }
+    };
+
+    if (nch > 0) load_chunk(0, std::integral_constant<int, 0>{});
+    for (int c = 0; c < nch; c += 2) {
+        step(c, std::integral_constant<int, 0>{});
+        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>{});
     }
 
     // ---------------- final state [dk][dv] fp32
@@ -600,6 +731,15 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
     __shared__ Smem<BF16, C, DK, NT, LIN> sm;
+    constexpr int QKN = Cf::DMA ? C * DK : 8;
+    __shared__ __attribute__((aligned(16))) E sq0[QKN];
+    __shared__ __attribute__((aligned(16))) E sq1[QKN];
+    __shared__ __attribute__((aligned(16))) E sk0[QKN];
+    __shared__ __attribute__((aligned(16))) E sk1[QKN];
+    constexpr int VN = Cf::DMA ? C * Cf::VSTR : 8;
+    __shared__ __attribute__((aligned(16))) E sv0[VN];
+    __shared__ __attribute__((aligned(16))) E sv1[VN];
+    const QKTiles<E> qk{{sq0, sq1}, {sk0, sk1}, {sv0, sv1}};
 
     // workgroup -> (b*H + h, value slice); slices of one (b, h) share an XCD
     int L = blockIdx.x;
@@ -622,15 +762,28 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     switch (wave) {
-        case 0: walk_body<BF16, C, DK, NT, LIN, 0>(a, sm, bh, nbase, lg); break;
-        case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, bh, nbase, lg); break;
-        case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, bh, nbase, lg); break;
-        default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, bh, nbase, lg); break;
+        case 0: walk_body<BF16, C, DK, NT, LIN, 0>(a, sm, qk, bh, nbase, lg); break;
+        case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, qk, bh, nbase, lg); break;
+        case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, qk, bh, nbase, lg); break;
+        default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, qk, bh, nbase, lg); break;
     }
+}
+
+// LDS available to one workgroup on gfx950.
+constexpr size_t kLdsBytes = 160 * 1024;
+
+template <bool BF16, int C, int DK, int NT, bool LIN>
+constexpr bool fits() {
+    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    return sizeof(Smem<BF16, C, DK, NT, LIN>) + 4 * sizeof(typename Cf::E) * (Cf::DMA ? C * DK : 8) +
+               2 * sizeof(typename Cf::E) * (Cf::DMA ? C * Cf::VSTR : 8) <= kLdsBytes;
 }
 
 template <bool BF16, int C, int DK, int NT, bool LIN>
 hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
+    if constexpr (!fits<BF16, C, DK, NT, LIN>()) {
+        return hipErrorInvalidConfiguration;
+    } else {
     const long long groups = static_cast<long long>(a.B) * a.H * a.nslices;
     if (groups <= 0) return hipSuccess;
     if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -639,6 +792,7 @@ hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((walk_kernel<BF16, C, DK, NT, LIN>), dim3(static_cast<unsigned>(groups)),
                        dim3(kThreads), 0, stream, args);
     return hipGetLastError();
+    }
 }
 
 // Instantiates every (chunk, dk, NT) variant for one (dtype, operator) pair.
