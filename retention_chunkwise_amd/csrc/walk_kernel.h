@@ -523,6 +523,59 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
         }
 
+        // ---------------- state: S^T <- gamma^c S^T + (zeta V)^T K   (and z += sum phi(k))
+        // Independent of the Q K^T tiles, so it is issued here, where its MFMAs
+        // overlap the decay arithmetic below.  The per-tile accumulation chains
+        // are interleaved (token blocks outer, tiles inner).
+        f32x4 snew[SPW];
+        float zsum[SPW];
+        {
+            const float gc = sm.dec[16 + clen];
+#pragma unroll
+            for (int m = 0; m < SPW; ++m) {
+                snew[m] = sacc[m] * gc;
+                zsum[m] = 0.f;
+            }
+            if constexpr (BF16) {
+#pragma unroll
+                for (int js = 0; js < C / 32; ++js) {
+#pragma unroll
+                    for (int m = 0; m < SPW; ++m) {
+                        const int qt = W + 4 * m;
+                        const int nt = qt / KT, kt = qt % KT;
+                        // A = (zeta V)^T, B = K: tokens 32js + 4g + {0..3}, 32js + 16 + 4g + {0..3}
+                        const E* v0 = &sm.Vz[(32 * js + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
+                        const bf16x8 av = cat_bf16(lds_tr4(v0), lds_tr4(v0 + 16 * VSTR));
+                        const int r0 = 32 * js + 4 * g + lq;
+                        const int c16 = 2 * kt + (lr >> 1), half = (lr & 1) * 8;
+                        const u16x4 blo = lds_tr4(&qk.k[B][(swz_off<RU>(r0, c16) + half) / ESZ]);
+                        const u16x4 bhi = lds_tr4(&qk.k[B][(swz_off<RU>(r0 + 16, c16) + half) / ESZ]);
+                        snew[m] = mfma_bf16(av, cat_bf16(blo, bhi), snew[m]);
+                        if (LIN && nt == 0) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) zsum[m] += bf2f(blo[r]) + bf2f(bhi[r]);
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int jt = 0; jt < NI; ++jt) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+                        for (int m = 0; m < SPW; ++m) {
+                            const int qt = W + 4 * m;
+                            const int nt = qt / KT, kt = qt % KT;
+                            const float av = sm.Vz[(jt * 16 + 4 * g + r) * VSTR + nt * 16 + l16];
+                            const float b = sm.Ks[(jt * 16 + 4 * g + r) * KSTR + kt * 16 + l16];
+                            snew[m] = mfma_f32(av, b, snew[m]);
+                            if (LIN && nt == 0) zsum[m] += b;
+                        }
+                    }
+                }
+            }
+        }
+
         // ---------------- decay mask: P^T[j][i] = S^T[j][i] * gamma^(i-j), 0 for j > i
 #pragma unroll
         for (int s = 0; s < NS; ++s)
@@ -657,53 +710,24 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
         }
 
-        // ---------------- state: S^T <- gamma^c S^T + (zeta V)^T K   (and z += sum phi(k))
-        const float gc = sm.dec[16 + clen];
-        E* stn = sm.Sts[NB];
+        // ---------------- commit the new state: fp32 master in registers, operand copy in LDS
+        {
+            E* stn = sm.Sts[NB];
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m;
-            const int nt = qt / KT, kt = qt % KT;
-            f32x4 acc = sacc[m] * gc;
-            float zsum = 0.f;
-            const int kcol = kt * 16 + l16;
-            if constexpr (BF16) {
+            for (int m = 0; m < SPW; ++m) {
+                const int qt = W + 4 * m;
+                const int nt = qt / KT, kt = qt % KT;
+                const int kcol = kt * 16 + l16;
+                sacc[m] = snew[m];
 #pragma unroll
-                for (int js = 0; js < C / 32; ++js) {
-                    // A = (zeta V)^T, B = K: tokens 32js + 4g + {0..3}, 32js + 16 + 4g + {0..3}
-                    const E* v0 = &sm.Vz[(32 * js + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
-                    const bf16x8 av = cat_bf16(lds_tr4(v0), lds_tr4(v0 + 16 * VSTR));
-                    const int r0 = 32 * js + 4 * g + lq;
-                    const int c16 = 2 * kt + (lr >> 1), half = (lr & 1) * 8;
-                    const u16x4 blo = lds_tr4(&qk.k[B][(swz_off<RU>(r0, c16) + half) / ESZ]);
-                    const u16x4 bhi = lds_tr4(&qk.k[B][(swz_off<RU>(r0 + 16, c16) + half) / ESZ]);
-                    acc = mfma_bf16(av, cat_bf16(blo, bhi), acc);
-                    if (LIN && nt == 0) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) zsum += bf2f(blo[r]) + bf2f(bhi[r]);
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (BF16) stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = f2bf(snew[m][r]);
+                    else stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = snew[m][r];
                 }
-            } else {
-#pragma unroll
-                for (int jt = 0; jt < NI; ++jt) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float av = sm.Vz[(jt * 16 + 4 * g + r) * VSTR + nt * 16 + l16];
-                        const float b = sm.Ks[(jt * 16 + 4 * g + r) * KSTR + kcol];
-                        acc = mfma_f32(av, b, acc);
-                        if (LIN && nt == 0) zsum += b;
-                    }
+                if (LIN && nt == 0) {
+                    const float zt = sum_over_groups(zsum[m]);
+                    if (g == 0) sm.zs[NB][kcol] = sm.zs[B][kcol] + zt;
                 }
-            }
-            sacc[m] = acc;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (BF16) stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = f2bf(acc[r]);
-                else stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = acc[r];
-            }
-            if (LIN && nt == 0) {
-                zsum = sum_over_groups(zsum);
-                if (g == 0) sm.zs[NB][kcol] = sm.zs[B][kcol] + zsum;
             }
         }
     };
