@@ -28,7 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = ("chunkwise retention fwd tokens/s + TFLOP/s (% MFMA peak); decode GB/s (% HBM)")
 PROFILES = os.path.join(ROOT, "profiles")
-WALK_SOURCES = ["retention_chunkwise_amd/csrc/walk.hip", "retention_chunkwise_amd/csrc/internal.h"]
+WALK_SOURCES = ["retention_chunkwise_amd/csrc/walk_kernel.h", "retention_chunkwise_amd/csrc/internal.h"]
 DECODE_SOURCES = ["retention_chunkwise_amd/csrc/decode.hip", "retention_chunkwise_amd/csrc/internal.h"]
 
 
@@ -114,8 +114,9 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this library runs on a single GPU; multi-GPU runs are not part of this "
-              "build (see DESIGN.md for how the path would shard)", file=sys.stderr)
+        print("bench.py: this library runs on a single GPU; runs on several GPUs are not "
+              "supported (batch and heads shard with no communication, a split sequence needs one "
+              "state scan across GPUs)", file=sys.stderr)
         sys.exit(2)
 
     import torch
