@@ -1,11 +1,18 @@
 // capi.hip -- the extern "C" entry points of libretention (include/retention.h).
 //
 // Every argument is validated on the host before anything is enqueued, so a
-// rejected call has no side effect.  No entry point allocates device memory.
+// rejected call has no side effect.  The only device memory the library
+// allocates is the segment-state workspace of the segment-split forward,
+// taken stream-ordered from a library-owned pool and released on the same
+// stream when the call's kernels finish.
 #include <math.h>
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "../../include/retention.h"
 #include "internal.h"
@@ -67,6 +74,62 @@ int check_gamma(const float* gamma, int H, float* log2g) {
     return RET_OK;
 }
 
+// ---- forward path selection
+//
+// RET_FWD_PATH = "slice" | "segment" forces a forward path (any other value
+// or unset: automatic); RET_FWD_SEGMENTS = n forces the segment count of the
+// segment path.  Both exist for tests and tuning; they never change results
+// beyond rounding.
+enum class FwdPath { kSlice, kSegment };
+
+int env_int(const char* name) {
+    const char* s = getenv(name);
+    return s ? atoi(s) : 0;
+}
+
+FwdPath choose_fwd_path(int dtype) {
+    const char* s = getenv("RET_FWD_PATH");
+    const bool seg_ok = dtype == RET_BF16;
+    if (s && !strcmp(s, "slice")) return FwdPath::kSlice;
+    if (s && !strcmp(s, "segment") && seg_ok) return FwdPath::kSegment;
+    return seg_ok ? FwdPath::kSegment : FwdPath::kSlice;
+}
+
+// ---- workspace: one stream-ordered memory pool per device, created on first
+// use and kept until the process ends.  Freed blocks stay in the pool
+// (release threshold: unlimited) so repeated calls do not reach the driver.
+constexpr int kMaxDevices = 64;
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[kMaxDevices] = {};
+
+hipError_t device_pool(hipMemPool_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (!g_pools[dev]) {
+        hipMemPoolProps props;
+        memset(&props, 0, sizeof(props));
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return e;
+        uint64_t keep = UINT64_MAX;
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return e;
+        }
+        g_pools[dev] = pool;
+    }
+    *out = g_pools[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -112,11 +175,51 @@ int retention_fwd(const void* q, const void* k, const void* v, const float* gamm
     }
     if (B == 0) return ok();
     const long long bh = static_cast<long long>(B) * H;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (choose_fwd_path(dtype) == FwdPath::kSegment) {
+        ret::SegArgs sa{};
+        const int nch = (T + chunk - 1) / chunk;
+        int cps = 1;
+        const int forced = env_int("RET_FWD_SEGMENTS");
+        if (forced > 0) {
+            const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
+            cps = (nch > 0) ? (nch + g - 1) / g : 1;
+            sa.G = (nch > 0) ? (nch + cps - 1) / cps : 1;
+        } else {
+            sa.G = ret::choose_segments(bh, nch, 256, 4, 16, &cps);
+        }
+        sa.cps = cps;
+        sa.q = q; sa.k = k; sa.v = v; sa.out = out; sa.final_state = final_state;
+        sa.B = B; sa.H = H; sa.T = T;
+        memcpy(sa.log2g, a.log2g, sizeof(sa.log2g));
+        size_t ws_bytes = 4;
+        if (sa.G > 1 && (!mul_ok(ws_bytes, bh) || !mul_ok(ws_bytes, sa.G - 1) || !mul_ok(ws_bytes, dk) ||
+                         !mul_ok(ws_bytes, dv)))
+            return fail(RET_ERR_SHAPE, "retention_fwd: workspace size overflows");
+        void* ws = nullptr;
+        hipMemPool_t pool = nullptr;
+        if (sa.G > 1) {
+            hipError_t e = device_pool(&pool);
+            if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, st);
+            if (e != hipSuccess)
+                return fail(RET_ERR_HIP, "retention_fwd: workspace allocation of %zu bytes failed: %s", ws_bytes,
+                            hipGetErrorString(e));
+        }
+        sa.ws = static_cast<float*>(ws);
+        const hipError_t e = ret::launch_seg(sa, chunk, dk, dv, st);
+        if (ws) {
+            const hipError_t ef = hipFreeAsync(ws, st);
+            if (e == hipSuccess && ef != hipSuccess)
+                return fail(RET_ERR_HIP, "retention_fwd: workspace release failed: %s", hipGetErrorString(ef));
+        }
+        if (e != hipSuccess)
+            return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
+        return ok();
+    }
     const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, chunk, dk);
     a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = final_state;
     a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = 0.f;
-    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, chunk, dk, nt, false,
-                                          static_cast<hipStream_t>(stream));
+    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, chunk, dk, nt, false, st);
     if (e != hipSuccess)
         return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
     return ok();

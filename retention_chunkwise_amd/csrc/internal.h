@@ -38,6 +38,21 @@ struct DecodeArgs {
     float gamma[kMaxHeads];
 };
 
+// Arguments of the segment-split forward (retention, bf16): seg_state_kernel
+// then seg_walk_kernel.
+struct SegArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* final_state;  // may be null
+    float* ws;           // [B*H][G-1][dk*dv] fp32 segment states; unused when G == 1
+    int B, H, T;
+    int G;               // segments per (b, h); every segment but the last is full
+    int cps;             // chunks per segment
+    float log2g[kMaxHeads];
+};
+
 // Launchers (host).  They assume validated arguments and return a hipError_t.
 hipError_t launch_walk(const WalkArgs& a, bool bf16, int chunk, int dk, int nt,
                        bool linattn, hipStream_t stream);
@@ -47,6 +62,15 @@ hipError_t launch_walk_lin_bf16(const WalkArgs& a, int chunk, int dk, int nt, hi
 hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
                          hipStream_t stream);
+
+hipError_t launch_seg(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
+
+// Segment count for the segment-split forward: enough (b, h, segment)
+// workgroups to occupy the chip, at least `min_cps` chunks per segment.
+// Returns G; *cps receives the chunks per segment (G = ceil(nch / cps)).
+int choose_segments(long long bh, int nch, int target_groups, int min_cps, int max_g, int* cps);
 
 // Choice of value-slice width (in 16-column MFMA tiles) for the chunk walk:
 // the widest slice that still gives at least `target_groups` workgroups.

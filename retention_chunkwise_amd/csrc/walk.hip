@@ -1,4 +1,5 @@
-// walk.hip -- dispatch of the chunk-walk kernel variants (see walk_kernel.h).
+// walk.hip -- dispatch of the chunk-walk kernel variants (walk_kernel.h) and of
+// the segment-split forward (seg_kernel.h).
 #include "internal.h"
 
 namespace ret {
@@ -21,6 +22,25 @@ hipError_t launch_walk(const WalkArgs& a, bool bf16, int chunk, int dk, int nt, 
     }
     return linattn ? launch_walk_lin_f32(a, chunk, dk, nt, stream)
                    : launch_walk_ret_f32(a, chunk, dk, nt, stream);
+}
+
+hipError_t launch_seg(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream) {
+    if (chunk == 64) return launch_seg_c64(a, dk, dv, stream);
+    if (chunk == 128) return launch_seg_c128(a, dk, dv, stream);
+    return hipErrorInvalidValue;
+}
+
+int choose_segments(long long bh, int nch, int target_groups, int min_cps, int max_g, int* cps) {
+    long long g = (bh > 0) ? (target_groups + bh - 1) / bh : 1;
+    const long long by_len = (min_cps > 0) ? nch / min_cps : nch;
+    if (g > by_len) g = by_len;
+    if (g > max_g) g = max_g;
+    if (g < 1) g = 1;
+    int c = static_cast<int>((nch + g - 1) / g);
+    if (c < 1) c = 1;
+    *cps = c;
+    const int G = (nch + c - 1) / c;
+    return G < 1 ? 1 : G;
 }
 
 }  // namespace ret

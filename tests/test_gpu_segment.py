@@ -1,0 +1,99 @@
+"""Segment-split forward (bf16) against the fp64 oracle (needs a gfx950 GPU).
+
+The segment path cuts every (b, h) sequence into G segments: one kernel sums
+each full segment's decayed k v^T contributions, the walk kernel starts each
+segment from the decayed sum of the earlier ones.  These cases force the path
+and the segment count through the library's RET_FWD_PATH / RET_FWD_SEGMENTS
+knobs and compare out and the final state with the oracle in full: one and
+several segments, segment counts that do not divide the chunk count, ragged
+last chunks, chunk 64 and 128, every (dk, dv) pair, small and unit decays.
+Tolerance: relative Frobenius error 2e-2 (bf16 inputs, fp32 accumulation).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import retention_chunkwise_amd as rc
+from retention_chunkwise_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _inputs(seed, **over):
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(dtype="bf16", **over)
+    return w, wl.make_inputs(w, seed)
+
+
+def _run(inp, chunk, monkeypatch, path="segment", segments=None):
+    monkeypatch.setenv("RET_FWD_PATH", path)
+    if segments is None:
+        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
+    else:
+        monkeypatch.setenv("RET_FWD_SEGMENTS", str(segments))
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    print(f"[segment] chunk={chunk} path={path} G={segments} shape={tuple(q.shape)} dv={v.shape[-1]}",
+          flush=True)
+    out, fs = rc.retention_fwd(q, k, v, inp["gamma"], chunk=chunk)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), fs.cpu().numpy()
+
+
+def _check(tag, out, fs, inp):
+    ref, ref_s = oracle.retention_recurrent(inp["q"], inp["k"], inp["v"], inp["gamma"], nthreads=8)
+    e_o, e_s = oracle.rel_frobenius(out, ref), oracle.rel_frobenius(fs, ref_s)
+    print(f"[parity] {tag}: out {e_o:.3e} state {e_s:.3e} (tol {TOL:.0e})", flush=True)
+    assert e_o <= TOL and e_s <= TOL, tag
+    assert np.isfinite(out).all() and np.isfinite(fs).all()
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, 1), (1000, 3), (1333, 4), (700, 16)])
+def test_segment_small_full(chunk, dk, dv, T, G, monkeypatch):
+    w, inp = _inputs(seed=11, B=2, H=2, T=T, dk=dk, dv=dv, chunk=chunk, scale=1.0 / np.sqrt(dk))
+    out, fs = _run(inp, chunk, monkeypatch, segments=G)
+    _check(f"segment C={chunk} dk={dk} dv={dv} T={T} G={G}", out, fs, inp)
+
+
+@pytest.mark.parametrize("T", [1, 37, 128, 129, 255, 256, 257])
+def test_segment_short_and_ragged(T, monkeypatch):
+    w, inp = _inputs(seed=12, B=1, H=3, T=T, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
+    out, fs = _run(inp, 128, monkeypatch, segments=2)
+    _check(f"segment short T={T}", out, fs, inp)
+
+
+def test_segment_zero_length(monkeypatch):
+    w, inp = _inputs(seed=13, B=1, H=2, T=0, dk=128, dv=128, chunk=128)
+    out, fs = _run(inp, 128, monkeypatch, segments=4)
+    assert out.size == 0 and np.all(fs == 0.0)
+
+
+@pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
+def test_segment_gamma_extremes(gval, monkeypatch):
+    w, inp = _inputs(seed=14, B=1, H=2, T=900, dk=64, dv=64, chunk=64, scale=1.0 / 8)
+    inp["gamma"] = np.full(w.H, gval, dtype=np.float32)
+    out, fs = _run(inp, 64, monkeypatch, segments=5)
+    _check(f"segment gamma={gval}", out, fs, inp)
+
+
+def test_segment_matches_slice_path_and_is_deterministic(monkeypatch):
+    w, inp = _inputs(seed=15, B=1, H=4, T=2000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
+    o_seg, s_seg = _run(inp, 128, monkeypatch, segments=6)
+    o_seg2, s_seg2 = _run(inp, 128, monkeypatch, segments=6)
+    assert np.array_equal(o_seg, o_seg2) and np.array_equal(s_seg, s_seg2), "run-to-run results differ"
+    o_sl, s_sl = _run(inp, 128, monkeypatch, path="slice")
+    _check("segment G=6", o_seg, s_seg, inp)
+    _check("slice", o_sl, s_sl, inp)
+    e = oracle.rel_frobenius(o_seg, o_sl)
+    print(f"[parity] segment vs slice out {e:.3e}", flush=True)
+    assert e <= TOL
+
+
+def test_segment_auto_choice(monkeypatch):
+    # automatic segment count (several segments for 2 heads x 24 chunks)
+    w, inp = _inputs(seed=16, B=1, H=2, T=3000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
+    out, fs = _run(inp, 128, monkeypatch, segments=None)
+    _check("segment auto", out, fs, inp)
