@@ -98,6 +98,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, then s_barrier.  Unlike __syncthreads() it does not wait for
+// outstanding vector-memory operations (prefetch loads, output stores), which
+// the kernels order themselves with wait_vmcnt.  The asm's memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Buffer resource words for the LDS-DMA loads (same layout as make_rsrc).
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
     const unsigned long long p = reinterpret_cast<unsigned long long>(base);
@@ -132,19 +139,21 @@ __device__ __forceinline__ unsigned lds_addr_of(const T* p) {
     return static_cast<unsigned>(reinterpret_cast<unsigned long>((lds_t*)(p)));
 }
 
-// 16-byte unit swizzle of unpadded row-major bf16 tiles whose rows hold RU
-// units (RU = 8 or 16).  Returns the XOR mask applied to the unit index of
-// row r.  Two read patterns are conflict-free under it: 16 consecutive rows at
-// one unit (MFMA operand rows), and 4 consecutive rows (starting at a multiple
-// of 4) at two adjacent units (transpose reads over tokens).
+// 16-byte unit swizzle of unpadded row-major bf16 tiles whose rows hold RU =
+// 8 or 16 units (128 or 256 bytes).  The unit index of row r is XORed with
+//   r & 15            (RU = 16)
+//   (r >> 1) & 7      (RU = 8)
+// Measured on gfx950 (64 four-byte banks): with it, 16-byte operand reads of
+// 16 consecutive rows at one unit run at the speed of a contiguous read, and
+// 8-byte transpose reads of 4 consecutive rows at two adjacent units run as
+// fast as any swizzle tried (those reads are not bank-limited).
 template <int RU>
 __device__ __forceinline__ int swz_mask(int r) {
     static_assert(RU == 8 || RU == 16, "8 or 16 units per row");
-    if constexpr (RU == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-    else return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    return (RU == 16) ? (r & 15) : ((r >> 1) & 7);
 }
 
-// Byte offset of logical unit u of row r in a tile laid out with swz_mask.
+// Byte offset of logical unit u of row r in a tile with RU units per row.
 template <int RU>
 __device__ __forceinline__ int swz_byte(int r, int u) {
     return r * (RU * 16) + ((u ^ swz_mask<RU>(r)) << 4);

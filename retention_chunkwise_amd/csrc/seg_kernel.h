@@ -22,12 +22,17 @@
 //                     in registers and writes O; the last segment also writes
 //                     the final state.
 // Every workgroup covers the full value width, so Q K^T is computed once per
-// chunk, and each workgroup streams its own slice of the sequence.
+// chunk (per half of the value width), and each workgroup streams its own
+// slice of the sequence.
 //
-// Per chunk, wave W (of 4) owns query tiles {W, C/16-1-W} (16 rows each, one
-// tile when C = 64) and dk tiles {W*DK/64 ...} of the state with every value
-// tile.  All products run on v_mfma_f32_16x16x32_bf16, transposed so that the
-// Q K^T accumulators feed the P V product from registers:
+// Waves.  A workgroup has 8 waves (two per SIMD).  Wave w = P + 4 h owns
+// query tiles {P, C/16-1-P} (16 rows each; one tile when C = 64), which
+// balances the causal triangle, and value half h; its state tiles are dk
+// tiles {P*DK/64, ...} x the value tiles of half h.  P is a template
+// parameter (four code variants, each unrolled over its exact causal tile
+// set); h only shifts addresses.  All products run on
+// v_mfma_f32_16x16x32_bf16, transposed so that the Q K^T accumulators feed the
+// P V product from registers:
 //   S^T   = K Q^T            A: K rows (LDS)           B: Q rows (registers)
 //   P^T   = S^T (.) D        decay factors per lane
 //   O^T   = xi (.) S_prev^T Q^T + V^T P^T
@@ -35,8 +40,9 @@
 //   S     = gamma^c S + (zeta (.) K)^T V
 //                            A: K^T (LDS transpose reads, scaled by zeta)
 //                            B: the V^T registers of the output product
-// K and V go HBM -> LDS by DMA into double-buffered swizzled tiles, one chunk
-// ahead; Q goes HBM -> registers directly in operand layout, one chunk ahead.
+// K and V go HBM -> LDS by DMA into double-buffered swizzled tiles and Q goes
+// HBM -> registers of the wave that uses it, all issued one chunk ahead.  LDS
+// addresses are a per-lane offset computed once plus an immediate.
 #pragma once
 
 #include <type_traits>
@@ -49,7 +55,7 @@ namespace seg {
 
 using namespace ::ret::kc;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 template <int C, int DK, int DV>
 struct SCfg {
@@ -59,21 +65,23 @@ struct SCfg {
     static constexpr int NKT = DK / 16;            // dk tiles of the state
     static constexpr int NVT = DV / 16;            // dv tiles of the state
     static constexpr int SKT = NKT / 4;            // dk tiles per wave
+    static constexpr int NVH = NVT / 2;            // dv tiles per wave (one value half)
     static constexpr int KRU = DK / 8;             // 16-byte units per K (and state copy) row
     static constexpr int VRU = DV / 8;             // 16-byte units per V row
-    static constexpr int KIW = C * DK * 2 / 1024 / 4;  // 1-KB DMA instructions per wave, K
-    static constexpr int VIW = C * DV * 2 / 1024 / 4;  // same for V
+    static constexpr int KIW = C * DK * 2 / 1024 / 8;  // 1-KB DMA instructions per wave, K
+    static constexpr int VIW = C * DV * 2 / 1024 / 8;  // same for V
     static constexpr int QF = DK / 32;             // Q operand blocks per query tile
     static constexpr int STATE = DK * DV;          // floats per state
     static_assert(NI == 4 || NI == 8, "chunk must be 64 or 128");
     static_assert(NKT == 4 || NKT == 8, "dk must be 64 or 128");
     static_assert(NVT == 4 || NVT == 8, "dv must be 64 or 128");
+    static_assert(KIW >= 1 && VIW >= 1, "every wave issues DMA");
 };
 
 // Workspace layout of one segment state: tile (m, n) of S (dk tile m, dv
 // tile n) occupies 256 floats, lane l's four values S[16m + 4(l/16) + r]
-// [16n + l%16] (r = 0..3) at 4 l.  Both kernels use the same ownership, so
-// the state moves with one 16-byte load or store per lane and tile.
+// [16n + l%16] (r = 0..3) at 4 l, so the state moves with one 16-byte access
+// per lane and tile.
 __device__ __forceinline__ int ws_tile_off(int m, int n, int nvt, int lane) {
     return ((m * nvt + n) << 8) + (lane << 2);
 }
@@ -83,89 +91,131 @@ __device__ __forceinline__ int ws_tile_off(int m, int n, int nvt, int lane) {
 struct STiles {
     unsigned short* k[2];
     unsigned short* v[2];
-    unsigned short* s;  // bf16 copy of S^T, [dv][dk], swizzled (walk kernel)
+    unsigned short* s;     // bf16 copy of S^T, [dv][dk], swizzled (walk kernel)
 };
 
-// Per-lane byte offsets, within a chunk, of the 16-byte units that DMA
-// instruction (W + 4 m) places at LDS byte 1024 (W + 4 m) + 16 l of a
-// swizzled tile with RU units per row and `rowbytes` bytes per global row.
-template <int RU, int N, int W>
-__device__ __forceinline__ void dma_offsets(unsigned (&off)[N], int rowbytes, int l) {
+// Per-lane pieces of the swizzled LDS addresses (see swz_mask).  With RB the
+// row bytes of a tile and R0 % 16 == 0:
+//  - operand rows (16 bytes at row R0 + l%16, unit 4 ks + g):
+//      R0 RB + opr[ks]
+//  - transpose reads (rows R0 + 4g .. +3, value/key tile t):
+//      R0 RB + tr + ((t << 5) ^ z16)
+struct LaneOff {
+    int opr[4];
+    int tr;
+    int z16;
+};
+
+template <int RU>
+__device__ __forceinline__ LaneOff lane_offsets(int l) {
+    constexpr int RB = RU * 16;
+    const int l16 = l & 15, g = l >> 4, lq = l16 >> 2, lr = l16 & 3;
+    LaneOff o;
 #pragma unroll
-    for (int m = 0; m < N; ++m) {
-        const int b = (W + 4 * m) * 1024 + l * 16;
-        const int r = b / (RU * 16), su = (b % (RU * 16)) >> 4;
-        off[m] = static_cast<unsigned>(r * rowbytes + ((su ^ swz_mask<RU>(r)) << 4));
-    }
+    for (int ks = 0; ks < 4; ++ks) o.opr[ks] = l16 * RB + (((4 * ks + g) ^ swz_mask<RU>(l16)) << 4);
+    const int y = 4 * g + lq;
+    o.tr = y * RB + (lr & 1) * 8;
+    o.z16 = (swz_mask<RU>(y) ^ (lr >> 1)) << 4;
+    return o;
 }
 
-// Transpose read of an operand over tokens from a swizzled bf16 tile: this
-// lane receives rows r0 .. r0+3 (r0 = the 16-lane group's base row) of
-// column 16 t + l%16, as four consecutive k-slots.
-template <int RU>
-__device__ __forceinline__ u16x4 tr_rows(const unsigned short* tile, int r0, int t, int lq, int lr) {
-    const char* base = reinterpret_cast<const char*>(tile);
-    return lds_tr4(reinterpret_cast<const unsigned short*>(
-        base + swz_byte<RU>(r0 + lq, 2 * t + (lr >> 1)) + (lr & 1) * 8));
+__device__ __forceinline__ u16x4 tr_at(const unsigned short* tile, int byte) {
+    return lds_tr4(reinterpret_cast<const unsigned short*>(reinterpret_cast<const char*>(tile) + byte));
 }
 
+__device__ __forceinline__ bf16x8 b128_at(const unsigned short* tile, int byte) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + byte));
+}
+
+// Operand of 32 tokens (rows R0 .. R0+31) of tile column block t: two
+// transpose reads; k-slots 8g + e hold rows R0 + slot_key(g, e).
 template <int RU>
-__device__ __forceinline__ bf16x8 row_unit(const unsigned short* tile, int r, int u) {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
-        reinterpret_cast<const char*>(tile) + swz_byte<RU>(r, u)));
+__device__ __forceinline__ bf16x8 tr_block(const unsigned short* tile, int R0, int xt, const LaneOff& lo) {
+    constexpr int RB = RU * 16;
+    return cat_bf16(tr_at(tile, R0 * RB + lo.tr + xt), tr_at(tile, (R0 + 16) * RB + lo.tr + xt));
 }
 
 // The 8 keys of this lane's k-slots in a 32-token block: 4g + e for e < 4,
 // 16 + 4g + (e - 4) otherwise (the layout of two stacked MFMA output tiles).
 __device__ __forceinline__ int slot_key(int g, int e) { return (e < 4) ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
-// A-operand of the state update: K^T rows 16 m .. 16 m + 15 (dk), keys of
-// block js, each key scaled by z(js, e).
-template <int RU, typename ZF>
-__device__ __forceinline__ bf16x8 kt_scaled(const unsigned short* kb, int m, int js, int g, int lq, int lr,
-                                            ZF zf) {
-    const u16x4 lo = tr_rows<RU>(kb, 32 * js + 4 * g, m, lq, lr);
-    const u16x4 hi = tr_rows<RU>(kb, 32 * js + 16 + 4 * g, m, lq, lr);
-    f32x4 a, b;
+// K^T operand (dk tile t, token block js) with each key scaled by z[e].
+template <int RU>
+__device__ __forceinline__ bf16x8 kt_scaled(const unsigned short* kb, int js, int xt, const LaneOff& lo,
+                                            const float (&z)[8]) {
+    constexpr int RB = RU * 16;
+    const u16x4 a = tr_at(kb, 32 * js * RB + lo.tr + xt);
+    const u16x4 b = tr_at(kb, (32 * js + 16) * RB + lo.tr + xt);
+    f32x4 x, y;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        a[e] = bf2f(lo[e]) * zf(js, e);
-        b[e] = bf2f(hi[e]) * zf(js, e + 4);
+        x[e] = bf2f(a[e]) * z[e];
+        y[e] = bf2f(b[e]) * z[e + 4];
     }
-    return cat_bf16(cvt4_bf16(a), cvt4_bf16(b));
+    return cat_bf16(cvt4_bf16(x), cvt4_bf16(y));
+}
+
+// 2^x on the transcendental unit (v_exp_f32, about 1 ulp; results below the
+// normal range flush to zero, which is harmless for decay factors).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Hides a value from loop-invariant code motion: re-issued in every chunk
+// step, it keeps the compiler from hoisting LDS addresses (which then fold
+// into the instructions' immediate offsets) and decay products out of the
+// chunk loop, where each would hold a register for the whole walk.
+__device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void opaque(float& x) { asm volatile("" : "+v"(x)); }
+template <int NOPR>
+__device__ __forceinline__ void opaque(LaneOff& o) {
+#pragma unroll
+    for (int i = 0; i < NOPR; ++i) opaque(o.opr[i]);
+    opaque(o.tr);
+    opaque(o.z16);
+}
+
+// Uniform value moved to a scalar register.
+__device__ __forceinline__ float uni(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// Byte offset, within a chunk, of the 16-byte unit that lane l of DMA
+// instruction w (LDS bytes [1024 w, +1024)) places at LDS byte 1024 w + 16 l
+// of a swizzled tile with RU units per row.  Instruction w + 8 m reads the
+// same offset + 8192 m (the swizzle mask depends on row bits that do not
+// change between them).
+template <int RU>
+__device__ __forceinline__ unsigned dma_offset(int w, int l) {
+    const int b = w * 1024 + l * 16;
+    const int r = b / (RU * 16), su = (b % (RU * 16)) >> 4;
+    return static_cast<unsigned>(r * (RU * 16) + ((su ^ swz_mask<RU>(r)) << 4));
 }
 
 // ---------------------------------------------------------------------------
 // seg_state_kernel: dS_j for one (b, h) and segment j < G - 1.
 
-template <int C, int DK, int DV, int W>
-__device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
+template <int C, int DK, int DV>
+__device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg, int w) {
     using Cf = SCfg<C, DK, DV>;
-    constexpr int NB = Cf::NB, NVT = Cf::NVT, SKT = Cf::SKT, KRU = Cf::KRU, VRU = Cf::VRU;
+    constexpr int NB = Cf::NB, NVT = Cf::NVT, NVH = Cf::NVH, SKT = Cf::SKT, KRU = Cf::KRU, VRU = Cf::VRU;
     constexpr int KIW = Cf::KIW, VIW = Cf::VIW;
-    const int tid = threadIdx.x;
-    const int l = tid & 63, l16 = l & 15, g = l >> 4, lq = l16 >> 2, lr = l16 & 3;
-    (void)l16;
+    const int l = threadIdx.x & 63, g = l >> 4;
+    const int p = w & 3, h = w >> 2;
     const int T = a.T;
     const unsigned short* kh = static_cast<const unsigned short*>(a.k) + static_cast<long long>(bh) * T * DK;
     const unsigned short* vh = static_cast<const unsigned short*>(a.v) + static_cast<long long>(bh) * T * DV;
+    const LaneOff lk0 = lane_offsets<KRU>(l), lv0 = lane_offsets<VRU>(l);
 
-    float zb[8];  // gamma^(31 - key) for this lane's k-slots
+    float zb0[8];  // gamma^(31 - key) for this lane's k-slots
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zb[e] = exp2f(static_cast<float>(31 - slot_key(g, e)) * lg);
-    float bj[NB];  // gamma^(32 (NB - 1 - js))
-#pragma unroll
-    for (int js = 0; js < NB; ++js) bj[js] = exp2f(static_cast<float>(32 * (NB - 1 - js)) * lg);
+    for (int e = 0; e < 8; ++e) zb0[e] = ex2(static_cast<float>(31 - slot_key(g, e)) * lg);
 
-    unsigned koff[KIW], voff[VIW];
-    dma_offsets<KRU, KIW, W>(koff, DK * 2, l);
-    dma_offsets<VRU, VIW, W>(voff, DV * 2, l);
+    const unsigned koff = dma_offset<KRU>(w, l), voff = dma_offset<VRU>(w, l);
 
-    f32x4 acc[SKT][NVT];
+    f32x4 acc[SKT][NVH];
 #pragma unroll
     for (int mi = 0; mi < SKT; ++mi)
 #pragma unroll
-        for (int n = 0; n < NVT; ++n) acc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ni = 0; ni < NVH; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int c_first = seg * a.cps, c_last = c_first + a.cps - 1;  // all chunks full
 
@@ -177,9 +227,9 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
         const unsigned kbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.k[buf]));
         const unsigned vbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.v[buf]));
 #pragma unroll
-        for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (W + 4 * m) * 1024, koff[m]);
+        for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (w + 8 * m) * 1024, koff + 8192u * m);
 #pragma unroll
-        for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (W + 4 * m) * 1024, voff[m]);
+        for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (w + 8 * m) * 1024, voff + 8192u * m);
     };
 
     // chunks in reverse order (the walk kernel then finds the segment's first
@@ -187,30 +237,41 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
     auto step = [&](int c, auto bufc) {
         constexpr int B = decltype(bufc)::value;
         wait_vmcnt<0>();
-        __syncthreads();
+        lds_barrier();
         if (c > c_first) load_chunk(c - 1, std::integral_constant<int, 1 - B>{});
+        LaneOff lk = lk0, lv = lv0;
+        opaque<0>(lk);
+        opaque<0>(lv);
+        float zb[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            zb[e] = zb0[e];
+            opaque(zb[e]);
+        }
         // gamma^(C (c_last - c)): decay from the end of chunk c to the end of the segment
-        const float wc = exp2f(static_cast<float>(C) * static_cast<float>(c_last - c) * lg);
+        const float wc = uni(ex2(static_cast<float>(C) * static_cast<float>(c_last - c) * lg));
         const unsigned short* kb = tl.k[B];
         const unsigned short* vb = tl.v[B];
         bf16x8 kz[SKT][NB];
 #pragma unroll
-        for (int mi = 0; mi < SKT; ++mi)
+        for (int js = 0; js < NB; ++js) {
+            const float bj = uni(ex2(static_cast<float>(32 * (NB - 1 - js)) * lg)) * wc;
+            float z[8];
 #pragma unroll
-            for (int js = 0; js < NB; ++js)
-                kz[mi][js] = kt_scaled<KRU>(kb, SKT * W + mi, js, g, lq, lr,
-                                            [&](int j, int e) { return zb[e] * bj[j] * wc; });
+            for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj;
 #pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-            bf16x8 vf[NB];
+            for (int mi = 0; mi < SKT; ++mi)
+                kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * p + mi) << 5) ^ lk.z16, lk, z);
+        }
 #pragma unroll
-            for (int js = 0; js < NB; ++js)
-                vf[js] = cat_bf16(tr_rows<VRU>(vb, 32 * js + 4 * g, n, lq, lr),
-                                  tr_rows<VRU>(vb, 32 * js + 16 + 4 * g, n, lq, lr));
+        for (int ni = 0; ni < NVH; ++ni) {
+            const int xt = ((NVH * h + ni) << 5) ^ lv.z16;
 #pragma unroll
-            for (int js = 0; js < NB; ++js)
+            for (int js = 0; js < NB; ++js) {
+                const bf16x8 vf = tr_block<VRU>(vb, 32 * js, xt, lv);
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi) acc[mi][n] = mfma_bf16(kz[mi][js], vf[js], acc[mi][n]);
+                for (int mi = 0; mi < SKT; ++mi) acc[mi][ni] = mfma_bf16(kz[mi][js], vf, acc[mi][ni]);
+            }
         }
     };
 
@@ -224,124 +285,165 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
 #pragma unroll
     for (int mi = 0; mi < SKT; ++mi)
 #pragma unroll
-        for (int n = 0; n < NVT; ++n)
-            *reinterpret_cast<f32x4*>(wsj + ws_tile_off(SKT * W + mi, n, NVT, l)) = acc[mi][n];
+        for (int ni = 0; ni < NVH; ++ni)
+            *reinterpret_cast<f32x4*>(wsj + ws_tile_off(SKT * p + mi, NVH * h + ni, NVT, l)) = acc[mi][ni];
 }
 
 // ---------------------------------------------------------------------------
 // seg_walk_kernel: outputs of one (b, h, segment g).
+//
+// Roles.  Waves 0-3 ("O-waves", P = wave) compute the outputs of query tiles
+// {P, C/16-1-P} over the full value width; waves 4-7 ("S-waves", P = wave-4)
+// carry dk tiles {P*DK/64, ...} x every value tile of the state.  Waves P and
+// P + 4 share a SIMD, so the MFMA-heavy output products of one overlap the
+// vector work of the other.  Both roles pass the same two barriers per step.
+//
+// Value-column order of the output products.  O-wave MFMA tiles pair up: row
+// 4q + j (q, j < 4) of tile 2a + b holds value column 32a + 8q + 4b + j, so a
+// lane's accumulators of the two tiles of a pair are 8 consecutive columns of
+// one query row (one 16-byte store).  The bf16 state copy stores its rows in
+// the same order: row 16 n + i holds the value column of row i of tile n.
 
-template <int C, int DK, int DV, int W>
+// 16-byte output store, marked non-temporal (the output is written once and
+// not read back by this kernel).
+__device__ __forceinline__ void bstore16_nt(__amdgpu_buffer_rsrc_t r, unsigned off, const bf16x8& x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, static_cast<int>(off), 0, 2);
+}
+
+// State-copy row of value column dv.
+__device__ __forceinline__ int perm_row(int dv) {
+    return (dv & ~31) | (((dv >> 2) & 1) << 4) | (((dv >> 3) & 3) << 2) | (dv & 3);
+}
+
+template <int C, int DK, int DV, int P, bool OW>
 __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
     using Cf = SCfg<C, DK, DV>;
     constexpr int NI = Cf::NI, NS = Cf::NS, NB = Cf::NB, NVT = Cf::NVT, SKT = Cf::SKT;
     constexpr int KRU = Cf::KRU, VRU = Cf::VRU, QF = Cf::QF, KIW = Cf::KIW, VIW = Cf::VIW;
-    constexpr int IT0 = W;
-    constexpr int IT1 = (NS == 2) ? NI - 1 - W : W;
+    constexpr int KRB = KRU * 16, VRB = VRU * 16;
+    constexpr int NPAIR = NVT / 2;
+    constexpr int IT0 = P;
+    constexpr int IT1 = (NS == 2) ? NI - 1 - P : P;
     constexpr int ITMAX = IT1;
-    // vector-memory ops a thread issues after a chunk's loads: the output stores
-    constexpr int STORES = NS * NVT;
+    // vector-memory ops a thread issues after a chunk's loads: its output stores
+    constexpr int STORES = OW ? NS * NPAIR : 0;
     auto its = [](int s) constexpr { return s == 0 ? IT0 : IT1; };
 
-    const int tid = threadIdx.x;
-    const int l = tid & 63, l16 = l & 15, g = l >> 4, lq = l16 >> 2, lr = l16 & 3;
+    const int w = P + (OW ? 0 : 4);
+    const int l = threadIdx.x & 63, l16 = l & 15, g = l >> 4, lq = l16 >> 2, lr = l16 & 3;
     const int T = a.T;
     const unsigned short* qh = static_cast<const unsigned short*>(a.q) + static_cast<long long>(bh) * T * DK;
     const unsigned short* kh = static_cast<const unsigned short*>(a.k) + static_cast<long long>(bh) * T * DK;
     const unsigned short* vh = static_cast<const unsigned short*>(a.v) + static_cast<long long>(bh) * T * DV;
     unsigned short* oh = static_cast<unsigned short*>(a.out) + static_cast<long long>(bh) * T * DV;
+    const LaneOff lk0 = lane_offsets<KRU>(l), lv0 = lane_offsets<VRU>(l);
+    // O-wave transpose reads of V in the permuted column order: lane L reads
+    // row R0 + 4g + L/4, unit 4a + L%4, half b:  R0 RB + rowo + (uo ^ (a << 6)) + 8 b
+    const int rowo0 = (4 * g + lq) * VRB;
+    const int uo0 = (lr ^ swz_mask<VRU>(4 * g + lq)) << 4;
 
     const int nch = (T + C - 1) / C;
     const int c_begin = seg * a.cps;
     const int c_end = (c_begin + a.cps < nch) ? c_begin + a.cps : nch;
 
-    // ---- per-lane decay constants
+    // ---- decay constants
     // P^T element (key 16 jt + 4g + r, query 16 it + l16) has decay
     // gamma^(16 d + l16 - 4g - r), d = it - jt: f0 for d = 0 (0 above the
     // diagonal), gd[d] * f1 for d >= 1 (both exponents non-negative).
-    float f0[4], f1[4];
+    float f0[4], f1_0[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int e = l16 - 4 * g - r;
-        f0[r] = (e < 0) ? 0.f : exp2f(static_cast<float>(e) * lg);
-        f1[r] = exp2f(static_cast<float>(16 + e) * lg);
+        f0[r] = (e < 0) ? 0.f : ex2(static_cast<float>(e) * lg);
+        f1_0[r] = ex2(static_cast<float>(16 + e) * lg);
     }
     float gd[ITMAX + 1];
     gd[0] = 1.f;
 #pragma unroll
-    for (int d = 1; d <= ITMAX; ++d) gd[d] = exp2f(static_cast<float>(16 * (d - 1)) * lg);
+    for (int d = 1; d <= ITMAX; ++d) gd[d] = uni(ex2(static_cast<float>(16 * (d - 1)) * lg));
     float xi[NS];  // gamma^(i+1) for this lane's query in each owned tile
 #pragma unroll
-    for (int s = 0; s < NS; ++s) xi[s] = exp2f(static_cast<float>(16 * its(s) + l16 + 1) * lg);
-    float zb[8];  // gamma^(31 - key) for this lane's k-slots; zeta = zb * bj for a full chunk
+    for (int s = 0; s < NS; ++s) xi[s] = ex2(static_cast<float>(16 * its(s) + l16 + 1) * lg);
+    float zb0[8];  // gamma^(31 - key) for this lane's k-slots; zeta = zb * bj for a full chunk
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zb[e] = exp2f(static_cast<float>(31 - slot_key(g, e)) * lg);
+    for (int e = 0; e < 8; ++e) zb0[e] = ex2(static_cast<float>(31 - slot_key(g, e)) * lg);
     float bj[NB];
 #pragma unroll
-    for (int js = 0; js < NB; ++js) bj[js] = exp2f(static_cast<float>(32 * (NB - 1 - js)) * lg);
-    const float gC = exp2f(static_cast<float>(C) * lg);
+    for (int js = 0; js < NB; ++js) bj[js] = uni(ex2(static_cast<float>(32 * (NB - 1 - js)) * lg));
+    const float gC = uni(ex2(static_cast<float>(C) * lg));
 
-    // ---- state entering the segment
-    f32x4 sacc[SKT][NVT];
+    // ---- S-waves: state entering the segment
+    f32x4 sacc[OW ? 1 : SKT][OW ? 1 : NVT];
+    if constexpr (!OW) {
 #pragma unroll
-    for (int mi = 0; mi < SKT; ++mi)
+        for (int mi = 0; mi < SKT; ++mi)
 #pragma unroll
-        for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (seg > 0) {
-        const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * Cf::STATE;
-        const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
-        for (int j = 0; j < seg; ++j) {
-            const float w = exp2f(lseg * static_cast<float>(seg - 1 - j));
-            const float* wj = wsb + static_cast<long long>(j) * Cf::STATE;
+            for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (seg > 0) {
+            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * Cf::STATE;
+            const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
+            for (int j = 0; j < seg; ++j) {
+                const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j)));
+                const float* sj = wsb + static_cast<long long>(j) * Cf::STATE;
 #pragma unroll
-            for (int mi = 0; mi < SKT; ++mi)
+                for (int mi = 0; mi < SKT; ++mi)
 #pragma unroll
-                for (int n = 0; n < NVT; ++n)
-                    sacc[mi][n] += w * *reinterpret_cast<const f32x4*>(wj + ws_tile_off(SKT * W + mi, n, NVT, l));
+                    for (int n = 0; n < NVT; ++n)
+                        sacc[mi][n] += wj * *reinterpret_cast<const f32x4*>(sj + ws_tile_off(SKT * P + mi, n, NVT, l));
+            }
         }
     }
 
     // bf16 copy of S^T in LDS: this lane's S[16m + 4g + r][16n + l16], r = 0..3,
-    // are 4 consecutive dk of row dv = 16n + l16
+    // are 4 consecutive dk of value column 16n + l16
     auto write_state_copy = [&]() {
-        char* sb = reinterpret_cast<char*>(tl.s);
+        if constexpr (!OW) {
+            char* sb = reinterpret_cast<char*>(tl.s);
 #pragma unroll
-        for (int mi = 0; mi < SKT; ++mi) {
-            const int m = SKT * W + mi;
+            for (int mi = 0; mi < SKT; ++mi) {
+                const int m = SKT * P + mi;
 #pragma unroll
-            for (int n = 0; n < NVT; ++n)
-                *reinterpret_cast<u16x4*>(sb + swz_byte<KRU>(16 * n + l16, 2 * m + (g >> 1)) + (g & 1) * 8) =
-                    cvt4_bf16(sacc[mi][n]);
+                for (int n = 0; n < NVT; ++n)
+                    *reinterpret_cast<u16x4*>(sb + swz_byte<KRU>(perm_row(16 * n + l16), 2 * m + (g >> 1)) +
+                                              (g & 1) * 8) = cvt4_bf16(sacc[mi][n]);
+            }
         }
     };
 
-    unsigned koff[KIW], voff[VIW];
-    dma_offsets<KRU, KIW, W>(koff, DK * 2, l);
-    dma_offsets<VRU, VIW, W>(voff, DV * 2, l);
-
-    uint4 qf[2][NS][QF];  // Q operands, double-buffered in registers
+    const unsigned koff = dma_offset<KRU>(w, l), voff = dma_offset<VRU>(w, l);
 
     // Issue the loads of chunk c through range-checked resources (rows past
-    // the end of the sequence read as zeros).  Nothing consumes them in the
-    // step that issues them.
+    // the end of the sequence read as zeros).
+    auto chunk_len = [&](int c) {
+        const long long t0 = static_cast<long long>(c) * C;
+        return (T - t0 < C) ? static_cast<int>(T - t0) : C;
+    };
+    bf16x8 qf[OW ? 2 : 1][NS][QF];  // O-waves: Q operands, double-buffered in registers
+    // Issued unconditionally (a chunk past the segment gets a zero-length
+    // range, which moves no data): a conditional load would make the
+    // compiler's own waits assume the path without it and stall on the
+    // loads just issued.
     auto load_chunk = [&](int c, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
         const long long t0 = static_cast<long long>(c) * C;
-        const int cl = (T - t0 < C) ? static_cast<int>(T - t0) : C;
+        const int cl = (c < c_end) ? chunk_len(c) : 0;
         const u32x4 wk = rsrc_words(kh + t0 * DK, cl * DK * 2);
         const u32x4 wv = rsrc_words(vh + t0 * DV, cl * DV * 2);
         const unsigned kbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.k[buf]));
         const unsigned vbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.v[buf]));
 #pragma unroll
-        for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (W + 4 * m) * 1024, koff[m]);
+        for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (w + 8 * m) * 1024, koff + 8192u * m);
 #pragma unroll
-        for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (W + 4 * m) * 1024, voff[m]);
-        const auto rq = make_rsrc(qh + t0 * DK, cl * DK * 2);
+        for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (w + 8 * m) * 1024, voff + 8192u * m);
+        if constexpr (OW) {
+            const auto rq = make_rsrc(qh + t0 * DK, cl * DK * 2);
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
-            for (int ks = 0; ks < QF; ++ks)
-                qf[buf][s][ks] = bload16(rq, static_cast<unsigned>(((16 * its(s) + l16) * DK + 32 * ks + 8 * g) * 2));
+                for (int ks = 0; ks < QF; ++ks)
+                    qf[buf][s][ks] = __builtin_bit_cast(
+                        bf16x8, bload16(rq, static_cast<unsigned>(((16 * its(s) + l16) * DK + 32 * ks + 8 * g) * 2)));
+        }
     };
 
     auto step = [&](int c, auto bufc) {
@@ -350,141 +452,171 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
         const int clen = (T - t0 < C) ? static_cast<int>(T - t0) : C;
         const bool tail = clen < C;  // uniform; only the last chunk of the sequence
 
-        // This chunk's loads were issued one step ago; the only vector-memory
-        // ops issued after them are the previous step's output stores, and
-        // vector-memory ops complete in issue order.
+        // This chunk's loads were issued during the previous step; the only
+        // vector-memory ops issued after them are the previous step's output
+        // stores, and vector-memory ops complete in issue order.
         if (c == c_begin) wait_vmcnt<0>();
         else wait_vmcnt<STORES>();
-        __syncthreads();  // chunk in LDS everywhere, state copy written
-        if (c + 1 < c_end) load_chunk(c + 1, std::integral_constant<int, 1 - B>{});
+        lds_barrier();  // chunk in LDS everywhere, state copy written
+        load_chunk(c + 1, std::integral_constant<int, 1 - B>{});
 
         const unsigned short* kb = tl.k[B];
         const unsigned short* vb = tl.v[B];
 
-        // ---- S^T tiles = K Q^T for key tiles jt <= query tile
-        f32x4 pacc[NS][NI];
+        if constexpr (OW) {
+            LaneOff lk = lk0;
+            opaque<QF>(lk);
+            float f1[4];
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
+            for (int r = 0; r < 4; ++r) {
+                f1[r] = f1_0[r];
+                opaque(f1[r]);
+            }
+            // ---- S^T tiles = K Q^T for key tiles jt <= query tile
+            f32x4 pacc[NS][NI];
 #pragma unroll
-            for (int jt = 0; jt < NI; ++jt) pacc[s][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int ks = 0; ks < QF; ++ks) {
-            bf16x8 ka[ITMAX + 1];
-#pragma unroll
-            for (int jt = 0; jt <= ITMAX; ++jt) ka[jt] = row_unit<KRU>(kb, 16 * jt + l16, 4 * ks + g);
-#pragma unroll
-            for (int jt = 0; jt <= ITMAX; ++jt)
-#pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    if (jt <= its(s))
-                        pacc[s][jt] = mfma_bf16(ka[jt], __builtin_bit_cast(bf16x8, qf[B][s][ks]), pacc[s][jt]);
-        }
-
-        // ---- zeta-scaled K^T operands of the state update
-        bf16x8 kz[SKT][NB];
-        if (!tail) {
-#pragma unroll
-            for (int mi = 0; mi < SKT; ++mi)
-#pragma unroll
-                for (int js = 0; js < NB; ++js)
-                    kz[mi][js] = kt_scaled<KRU>(kb, SKT * W + mi, js, g, lq, lr,
-                                                [&](int j, int e) { return zb[e] * bj[j]; });
-        } else {
-            // gamma^(clen - 1 - key) for keys inside the chunk, 0 past its end
-#pragma unroll
-            for (int mi = 0; mi < SKT; ++mi)
-#pragma unroll
-                for (int js = 0; js < NB; ++js)
-                    kz[mi][js] = kt_scaled<KRU>(kb, SKT * W + mi, js, g, lq, lr, [&](int j, int e) {
-                        const int ex = clen - 1 - 32 * j - slot_key(g, e);
-                        return (ex < 0) ? 0.f : exp2f(static_cast<float>(ex) * lg);
-                    });
-        }
-
-        // ---- decay mask, bf16 P^T operands (two key tiles per operand)
-        bf16x8 pb[NS][NB];
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int js = 0; js < NB; ++js)
-                if (2 * js <= its(s)) {
-                    f32x4 lo = pacc[s][2 * js], hi = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const int d0 = its(s) - 2 * js;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) lo[r] *= (d0 == 0) ? f0[r] : gd[d0] * f1[r];
-                    if (2 * js + 1 <= its(s)) {
-                        hi = pacc[s][2 * js + 1];
-                        const int d1 = d0 - 1;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) hi[r] *= (d1 == 0) ? f0[r] : gd[d1] * f1[r];
-                    }
-                    pb[s][js] = cat_bf16(cvt4_bf16(lo), cvt4_bf16(hi));
-                }
-
-        // ---- state decay for this chunk
-        const float gc = tail ? exp2f(static_cast<float>(clen) * lg) : gC;
-#pragma unroll
-        for (int mi = 0; mi < SKT; ++mi)
-#pragma unroll
-            for (int n = 0; n < NVT; ++n) sacc[mi][n] *= gc;
-
-        // ---- per value tile: O^T tiles, stores, state update
-        const auto ro = make_rsrc(oh + t0 * DV, clen * DV * 2);
-#pragma unroll
-        for (int n = 0; n < NVT; ++n) {
-            bf16x8 vf[NB];
-#pragma unroll
-            for (int js = 0; js < NB; ++js)
-                vf[js] = cat_bf16(tr_rows<VRU>(vb, 32 * js + 4 * g, n, lq, lr),
-                                  tr_rows<VRU>(vb, 32 * js + 16 + 4 * g, n, lq, lr));
-            f32x4 oacc[NS];
-#pragma unroll
-            for (int s = 0; s < NS; ++s) oacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int jt = 0; jt < NI; ++jt) pacc[s][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < QF; ++ks) {
-                const bf16x8 sf = row_unit<KRU>(tl.s, 16 * n + l16, 4 * ks + g);
+                bf16x8 ka[ITMAX + 1];
 #pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    oacc[s] = mfma_bf16(sf, __builtin_bit_cast(bf16x8, qf[B][s][ks]), oacc[s]);
+                for (int jt = 0; jt <= ITMAX; ++jt) ka[jt] = b128_at(kb, 16 * jt * KRB + lk.opr[ks]);
+#pragma unroll
+                for (int jt = 0; jt <= ITMAX; ++jt)
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+                        if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], qf[B][s][ks], pacc[s][jt]);
             }
-#pragma unroll
-            for (int s = 0; s < NS; ++s) oacc[s] *= xi[s];
-#pragma unroll
-            for (int js = 0; js < NB; ++js)
-#pragma unroll
-                for (int s = 0; s < NS; ++s)
-                    if (2 * js <= its(s)) oacc[s] = mfma_bf16(vf[js], pb[s][js], oacc[s]);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const int row = 16 * its(s) + l16;  // rows past the end are dropped by the resource
-                bstore8(ro, static_cast<unsigned>((row * DV + 16 * n + 4 * g) * 2), cvt4_bf16(oacc[s]));
-            }
-#pragma unroll
-            for (int js = 0; js < NB; ++js)
-#pragma unroll
-                for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] = mfma_bf16(kz[mi][js], vf[js], sacc[mi][n]);
-        }
 
-        __syncthreads();  // every wave is done reading the old state copy
-        write_state_copy();
+            // ---- decay mask, bf16 P^T operands (two key tiles per operand)
+            bf16x8 pb[NS][NB];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int js = 0; js < NB; ++js)
+                    if (2 * js <= its(s)) {
+                        f32x4 lo = pacc[s][2 * js], hi = f32x4{0.f, 0.f, 0.f, 0.f};
+                        const int d0 = its(s) - 2 * js;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) lo[r] *= (d0 == 0) ? f0[r] : gd[d0] * f1[r];
+                        if (2 * js + 1 <= its(s)) {
+                            hi = pacc[s][2 * js + 1];
+                            const int d1 = d0 - 1;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) hi[r] *= (d1 == 0) ? f0[r] : gd[d1] * f1[r];
+                        }
+                        pb[s][js] = cat_bf16(cvt4_bf16(lo), cvt4_bf16(hi));
+                    }
+
+            // ---- O^T = xi S_prev^T Q^T + V^T P^T per value-tile pair; 16-byte stores
+            int rowo = rowo0, uo = uo0;
+            opaque(rowo);
+            opaque(uo);
+            const auto ro = make_rsrc(oh + t0 * DV, clen * DV * 2);
+#pragma unroll
+            for (int pa = 0; pa < NPAIR; ++pa) {
+                const int uoa = uo ^ (pa << 6);
+                f32x4 oacc[NS][2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    const int n = 2 * pa + b;
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) oacc[s][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < QF; ++ks) {
+                        const bf16x8 sf = b128_at(tl.s, 16 * n * KRB + lk.opr[ks]);
+#pragma unroll
+                        for (int s = 0; s < NS; ++s) oacc[s][b] = mfma_bf16(sf, qf[B][s][ks], oacc[s][b]);
+                    }
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) oacc[s][b] *= xi[s];
+#pragma unroll
+                    for (int js = 0; 2 * js <= ITMAX; ++js) {
+                        const bf16x8 vf = cat_bf16(tr_at(vb, 32 * js * VRB + rowo + uoa + 8 * b),
+                                                   tr_at(vb, (32 * js + 16) * VRB + rowo + uoa + 8 * b));
+#pragma unroll
+                        for (int s = 0; s < NS; ++s)
+                            if (2 * js <= its(s)) oacc[s][b] = mfma_bf16(vf, pb[s][js], oacc[s][b]);
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    const int row = 16 * its(s) + l16;  // rows past the end are dropped by the resource
+                    bstore16_nt(ro, static_cast<unsigned>((row * DV + 32 * pa + 8 * g) * 2),
+                                cat_bf16(cvt4_bf16(oacc[s][0]), cvt4_bf16(oacc[s][1])));
+                }
+            }
+            lds_barrier();  // every O-wave is done reading the old state copy
+        } else {
+            LaneOff lk = lk0, lv = lv0;
+            opaque<0>(lk);
+            opaque<0>(lv);
+            float zb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                zb[e] = zb0[e];
+                opaque(zb[e]);
+            }
+            // ---- zeta-scaled K^T operands of the state update
+            bf16x8 kz[SKT][NB];
+#pragma unroll
+            for (int js = 0; js < NB; ++js) {
+                float z[8];
+                if (!tail) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj[js];
+                } else {
+                    // gamma^(clen - 1 - key) for keys inside the chunk, 0 past its end
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int ex = clen - 1 - 32 * js - slot_key(g, e);
+                        z[e] = (ex < 0) ? 0.f : ex2(static_cast<float>(ex) * lg);
+                    }
+                }
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi)
+                    kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * P + mi) << 5) ^ lk.z16, lk, z);
+            }
+
+            // ---- S = gamma^c S + (zeta K)^T V
+            const float gc = tail ? uni(ex2(static_cast<float>(clen) * lg)) : gC;
+#pragma unroll
+            for (int n = 0; n < NVT; ++n) {
+                const int xt = (n << 5) ^ lv.z16;
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] *= gc;
+#pragma unroll
+                for (int js = 0; js < NB; ++js) {
+                    const bf16x8 vf = tr_block<VRU>(vb, 32 * js, xt, lv);
+#pragma unroll
+                    for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] = mfma_bf16(kz[mi][js], vf, sacc[mi][n]);
+                }
+            }
+            lds_barrier();  // every O-wave is done reading the old state copy
+            write_state_copy();
+        }
     };
 
-    if (c_begin < c_end) load_chunk(c_begin, std::integral_constant<int, 0>{});
+    load_chunk(c_begin, std::integral_constant<int, 0>{});
     write_state_copy();  // ordered before the first read by the first step's barrier
     for (int c = c_begin; c < c_end; c += 2) {
         step(c, std::integral_constant<int, 0>{});
         if (c + 1 < c_end) step(c + 1, std::integral_constant<int, 1>{});
     }
 
-    if (a.final_state && seg == a.G - 1) {
-        float* fs = a.final_state + static_cast<long long>(bh) * DK * DV;
+    if constexpr (!OW) {
+        if (a.final_state && seg == a.G - 1) {
+            float* fs = a.final_state + static_cast<long long>(bh) * DK * DV;
 #pragma unroll
-        for (int mi = 0; mi < SKT; ++mi) {
-            const int m = SKT * W + mi;
+            for (int mi = 0; mi < SKT; ++mi) {
+                const int m = SKT * P + mi;
 #pragma unroll
-            for (int n = 0; n < NVT; ++n)
+                for (int n = 0; n < NVT; ++n)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) fs[(16 * m + 4 * g + r) * DV + 16 * n + l16] = sacc[mi][n][r];
+                    for (int r = 0; r < 4; ++r) fs[(16 * m + 4 * g + r) * DV + 16 * n + l16] = sacc[mi][n][r];
+            }
         }
     }
 }
@@ -500,12 +632,7 @@ __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a)
     const int bh = blockIdx.x / segs, seg = blockIdx.x % segs;
     const float lg = a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    switch (wave) {
-        case 0: state_body<C, DK, DV, 0>(a, tl, bh, seg, lg); break;
-        case 1: state_body<C, DK, DV, 1>(a, tl, bh, seg, lg); break;
-        case 2: state_body<C, DK, DV, 2>(a, tl, bh, seg, lg); break;
-        default: state_body<C, DK, DV, 3>(a, tl, bh, seg, lg); break;
-    }
+    state_body<C, DK, DV>(a, tl, bh, seg, lg, wave);
 }
 
 template <int C, int DK, int DV>
@@ -520,10 +647,14 @@ __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) 
     const float lg = a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: walk_body<C, DK, DV, 0>(a, tl, bh, seg, lg); break;
-        case 1: walk_body<C, DK, DV, 1>(a, tl, bh, seg, lg); break;
-        case 2: walk_body<C, DK, DV, 2>(a, tl, bh, seg, lg); break;
-        default: walk_body<C, DK, DV, 3>(a, tl, bh, seg, lg); break;
+        case 0: walk_body<C, DK, DV, 0, true>(a, tl, bh, seg, lg); break;
+        case 1: walk_body<C, DK, DV, 1, true>(a, tl, bh, seg, lg); break;
+        case 2: walk_body<C, DK, DV, 2, true>(a, tl, bh, seg, lg); break;
+        case 3: walk_body<C, DK, DV, 3, true>(a, tl, bh, seg, lg); break;
+        case 4: walk_body<C, DK, DV, 0, false>(a, tl, bh, seg, lg); break;
+        case 5: walk_body<C, DK, DV, 1, false>(a, tl, bh, seg, lg); break;
+        case 6: walk_body<C, DK, DV, 2, false>(a, tl, bh, seg, lg); break;
+        default: walk_body<C, DK, DV, 3, false>(a, tl, bh, seg, lg); break;
     }
 }
 
