@@ -130,6 +130,47 @@ hipError_t device_pool(hipMemPool_t* out) {
     return hipSuccess;
 }
 
+// Segment-split forward (bf16): segment count, workspace from the pool, the
+// two kernels, workspace released on the same stream.
+hipError_t launch_segment_path(const void* q, const void* k, const void* v, void* out, float* final_state,
+                               const float* log2g, float eps, int B, int H, int T, int chunk, int dk, int dv,
+                               bool linattn, hipStream_t st) {
+    const long long bh = static_cast<long long>(B) * H;
+    ret::SegArgs sa{};
+    const int nch = (T + chunk - 1) / chunk;
+    int cps = 1;
+    const int forced = env_int("RET_FWD_SEGMENTS");
+    if (forced > 0) {
+        const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
+        cps = (nch > 0) ? (nch + g - 1) / g : 1;
+        sa.G = (nch > 0) ? (nch + cps - 1) / cps : 1;
+    } else {
+        sa.G = ret::choose_segments(bh, nch, 256, 4, 16, &cps);
+    }
+    sa.cps = cps;
+    sa.q = q; sa.k = k; sa.v = v; sa.out = out; sa.final_state = final_state;
+    sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
+    if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
+    size_t ws_bytes = 4;
+    const long long slot = static_cast<long long>(dk) * dv + (linattn ? dk : 0);
+    if (sa.G > 1 && (!mul_ok(ws_bytes, bh) || !mul_ok(ws_bytes, sa.G - 1) || !mul_ok(ws_bytes, slot)))
+        return hipErrorInvalidValue;
+    void* ws = nullptr;
+    if (sa.G > 1) {
+        hipMemPool_t pool = nullptr;
+        hipError_t e = device_pool(&pool);
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, st);
+        if (e != hipSuccess) return e;
+    }
+    sa.ws = static_cast<float*>(ws);
+    const hipError_t e = ret::launch_seg(sa, chunk, dk, dv, linattn, st);
+    if (ws) {
+        const hipError_t ef = hipFreeAsync(ws, st);
+        if (e == hipSuccess && ef != hipSuccess) return ef;
+    }
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,43 +218,9 @@ int retention_fwd(const void* q, const void* k, const void* v, const float* gamm
     const long long bh = static_cast<long long>(B) * H;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (choose_fwd_path(dtype) == FwdPath::kSegment) {
-        ret::SegArgs sa{};
-        const int nch = (T + chunk - 1) / chunk;
-        int cps = 1;
-        const int forced = env_int("RET_FWD_SEGMENTS");
-        if (forced > 0) {
-            const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
-            cps = (nch > 0) ? (nch + g - 1) / g : 1;
-            sa.G = (nch > 0) ? (nch + cps - 1) / cps : 1;
-        } else {
-            sa.G = ret::choose_segments(bh, nch, 256, 4, 16, &cps);
-        }
-        sa.cps = cps;
-        sa.q = q; sa.k = k; sa.v = v; sa.out = out; sa.final_state = final_state;
-        sa.B = B; sa.H = H; sa.T = T;
-        memcpy(sa.log2g, a.log2g, sizeof(sa.log2g));
-        size_t ws_bytes = 4;
-        if (sa.G > 1 && (!mul_ok(ws_bytes, bh) || !mul_ok(ws_bytes, sa.G - 1) || !mul_ok(ws_bytes, dk) ||
-                         !mul_ok(ws_bytes, dv)))
-            return fail(RET_ERR_SHAPE, "retention_fwd: workspace size overflows");
-        void* ws = nullptr;
-        hipMemPool_t pool = nullptr;
-        if (sa.G > 1) {
-            hipError_t e = device_pool(&pool);
-            if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, st);
-            if (e != hipSuccess)
-                return fail(RET_ERR_HIP, "retention_fwd: workspace allocation of %zu bytes failed: %s", ws_bytes,
-                            hipGetErrorString(e));
-        }
-        sa.ws = static_cast<float*>(ws);
-        const hipError_t e = ret::launch_seg(sa, chunk, dk, dv, st);
-        if (ws) {
-            const hipError_t ef = hipFreeAsync(ws, st);
-            if (e == hipSuccess && ef != hipSuccess)
-                return fail(RET_ERR_HIP, "retention_fwd: workspace release failed: %s", hipGetErrorString(ef));
-        }
-        if (e != hipSuccess)
-            return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
+        const hipError_t e = launch_segment_path(q, k, v, out, final_state, a.log2g, 0.f, B, H, T, chunk, dk, dv,
+                                                 false, st);
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "retention_fwd: %s", hipGetErrorString(e));
         return ok();
     }
     const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, chunk, dk);
@@ -288,6 +295,13 @@ int linear_attn_fwd(const void* q, const void* k, const void* v, int phi, void* 
     for (const Range& in : {rq, rk, rv})
         if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "linear_attn_fwd: out overlaps %s", in.name);
     if (B == 0) return ok();
+    if (choose_fwd_path(dtype) == FwdPath::kSegment) {
+        // 64-token chunks when dk = 128 (the 128-token variant would spill registers)
+        const hipError_t e = launch_segment_path(q, k, v, out, nullptr, nullptr, eps, B, H, T, dk == 128 ? 64 : 128,
+                                                 dk, dv, true, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "linear_attn_fwd: %s", hipGetErrorString(e));
+        return ok();
+    }
     ret::WalkArgs a{};
     const long long bh = static_cast<long long>(B) * H;
     const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, 128, dk);

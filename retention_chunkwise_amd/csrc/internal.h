@@ -38,18 +38,19 @@ struct DecodeArgs {
     float gamma[kMaxHeads];
 };
 
-// Arguments of the segment-split forward (retention, bf16): seg_state_kernel
-// then seg_walk_kernel.
+// Arguments of the segment-split forward (bf16; retention, or linear
+// attention with the elu+1 feature map): seg_state_kernel then seg_walk_kernel.
 struct SegArgs {
     const void* q;
     const void* k;
     const void* v;
     void* out;
     float* final_state;  // may be null
-    float* ws;           // [B*H][G-1][dk*dv] fp32 segment states; unused when G == 1
+    float* ws;           // [B*H][G-1][dk*dv (+ dk)] fp32 segment states (and normalisers); unused when G == 1
     int B, H, T;
     int G;               // segments per (b, h); every segment but the last is full
     int cps;             // chunks per segment
+    float eps;           // linear attention only
     float log2g[kMaxHeads];
 };
 
@@ -63,9 +64,11 @@ hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hip
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
                          hipStream_t stream);
 
-hipError_t launch_seg(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg(const SegArgs& a, int chunk, int dk, int dv, bool linattn, hipStream_t stream);
 hipError_t launch_seg_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg_lin_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg_lin_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
 
 // Segment count for the segment-split forward: enough (b, h, segment)
 // workgroups to occupy the chip, at least `min_cps` chunks per segment.

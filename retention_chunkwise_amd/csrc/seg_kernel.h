@@ -57,7 +57,7 @@ using namespace ::ret::kc;
 
 constexpr int kThreads = 512;
 
-template <int C, int DK, int DV>
+template <int C, int DK, int DV, bool LIN = false>
 struct SCfg {
     static constexpr int NI = C / 16;              // 16-token tiles per chunk
     static constexpr int NS = (NI == 8) ? 2 : 1;   // query tiles per wave
@@ -72,6 +72,7 @@ struct SCfg {
     static constexpr int VIW = C * DV * 2 / 1024 / 8;  // same for V
     static constexpr int QF = DK / 32;             // Q operand blocks per query tile
     static constexpr int STATE = DK * DV;          // floats per state
+    static constexpr int WS = STATE + (LIN ? DK : 0);  // floats per workspace slot (state, normaliser)
     static_assert(NI == 4 || NI == 8, "chunk must be 64 or 128");
     static_assert(NKT == 4 || NKT == 8, "dk must be 64 or 128");
     static_assert(NVT == 4 || NVT == 8, "dv must be 64 or 128");
@@ -92,6 +93,7 @@ struct STiles {
     unsigned short* k[2];
     unsigned short* v[2];
     unsigned short* s;     // bf16 copy of S^T, [dv][dk], swizzled (walk kernel)
+    float* z;              // normaliser z, [dk] fp32 (walk kernel, linear attention)
 };
 
 // Per-lane pieces of the swizzled LDS addresses (see swz_mask).  With RB the
@@ -173,6 +175,31 @@ __device__ __forceinline__ void opaque(LaneOff& o) {
     opaque(o.z16);
 }
 
+// phi(x) = elu(x) + 1 = x + 1 for x > 0, e^x otherwise ("Linear attention",
+// the elu+1 feature map), with e^x as 2^(x log2 e) on v_exp_f32.
+__device__ __forceinline__ float phi_e1(float x) { return x > 0.f ? x + 1.f : ex2(x * 1.4426950408889634f); }
+
+// phi applied to 8 bf16 values, rounded back to bf16.
+__device__ __forceinline__ bf16x8 phi8(const bf16x8& x) {
+    const u16x8 e = __builtin_bit_cast(u16x8, x);
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = phi_e1(bf2f(e[i]));
+        b[i] = phi_e1(bf2f(e[i + 4]));
+    }
+    return cat_bf16(cvt4_bf16(a), cvt4_bf16(b));
+}
+
+// Sum of 8 bf16 values in fp32.
+__device__ __forceinline__ float sum8(const bf16x8& x) {
+    const u16x8 e = __builtin_bit_cast(u16x8, x);
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += bf2f(e[i]);
+    return t;
+}
+
 // Uniform value moved to a scalar register.
 __device__ __forceinline__ float uni(float x) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
@@ -193,9 +220,9 @@ __device__ __forceinline__ unsigned dma_offset(int w, int l) {
 // ---------------------------------------------------------------------------
 // seg_state_kernel: dS_j for one (b, h) and segment j < G - 1.
 
-template <int C, int DK, int DV>
+template <int C, int DK, int DV, bool LIN>
 __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg, int w) {
-    using Cf = SCfg<C, DK, DV>;
+    using Cf = SCfg<C, DK, DV, LIN>;
     constexpr int NB = Cf::NB, NVT = Cf::NVT, NVH = Cf::NVH, SKT = Cf::SKT, KRU = Cf::KRU, VRU = Cf::VRU;
     constexpr int KIW = Cf::KIW, VIW = Cf::VIW;
     const int l = threadIdx.x & 63, g = l >> 4;
@@ -212,10 +239,13 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
     const unsigned koff = dma_offset<KRU>(w, l), voff = dma_offset<VRU>(w, l);
 
     f32x4 acc[SKT][NVH];
+    float zsum[SKT];  // linear attention: partial column sums of phi(K)
 #pragma unroll
-    for (int mi = 0; mi < SKT; ++mi)
+    for (int mi = 0; mi < SKT; ++mi) {
+        zsum[mi] = 0.f;
 #pragma unroll
         for (int ni = 0; ni < NVH; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     const int c_first = seg * a.cps, c_last = c_first + a.cps - 1;  // all chunks full
 
@@ -255,13 +285,22 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
         bf16x8 kz[SKT][NB];
 #pragma unroll
         for (int js = 0; js < NB; ++js) {
-            const float bj = uni(ex2(static_cast<float>(32 * (NB - 1 - js)) * lg)) * wc;
-            float z[8];
+            if constexpr (LIN) {
+                // phi(k)^T operands and their column sums (the normaliser)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj;
+                for (int mi = 0; mi < SKT; ++mi) {
+                    kz[mi][js] = phi8(tr_block<KRU>(kb, 32 * js, ((SKT * p + mi) << 5) ^ lk.z16, lk));
+                    zsum[mi] += sum8(kz[mi][js]);
+                }
+            } else {
+                const float bj = uni(ex2(static_cast<float>(32 * (NB - 1 - js)) * lg)) * wc;
+                float z[8];
 #pragma unroll
-            for (int mi = 0; mi < SKT; ++mi)
-                kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * p + mi) << 5) ^ lk.z16, lk, z);
+                for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj;
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi)
+                    kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * p + mi) << 5) ^ lk.z16, lk, z);
+            }
         }
 #pragma unroll
         for (int ni = 0; ni < NVH; ++ni) {
@@ -281,12 +320,18 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
         if (c - 1 >= c_first) step(c - 1, std::integral_constant<int, 1>{});
     }
 
-    float* wsj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * Cf::STATE;
+    float* wsj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * Cf::WS;
 #pragma unroll
-    for (int mi = 0; mi < SKT; ++mi)
+    for (int mi = 0; mi < SKT; ++mi) {
 #pragma unroll
         for (int ni = 0; ni < NVH; ++ni)
             *reinterpret_cast<f32x4*>(wsj + ws_tile_off(SKT * p + mi, NVH * h + ni, NVT, l)) = acc[mi][ni];
+        if constexpr (LIN) {
+            // lanes l, l^16, l^32, l^48 hold the four key groups of column 16m + l%16
+            const float zt = sum_over_groups(zsum[mi]);
+            if (h == 0 && g == 0) wsj[Cf::STATE + 16 * (SKT * p + mi) + (l & 15)] = zt;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -315,9 +360,9 @@ __device__ __forceinline__ int perm_row(int dv) {
     return (dv & ~31) | (((dv >> 2) & 1) << 4) | (((dv >> 3) & 3) << 2) | (dv & 3);
 }
 
-template <int C, int DK, int DV, int P, bool OW>
+template <int C, int DK, int DV, bool LIN, int P, bool OW>
 __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
-    using Cf = SCfg<C, DK, DV>;
+    using Cf = SCfg<C, DK, DV, LIN>;
     constexpr int NI = Cf::NI, NS = Cf::NS, NB = Cf::NB, NVT = Cf::NVT, SKT = Cf::SKT;
     constexpr int KRU = Cf::KRU, VRU = Cf::VRU, QF = Cf::QF, KIW = Cf::KIW, VIW = Cf::VIW;
     constexpr int KRB = KRU * 16, VRB = VRU * 16;
@@ -372,24 +417,29 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
     for (int js = 0; js < NB; ++js) bj[js] = uni(ex2(static_cast<float>(32 * (NB - 1 - js)) * lg));
     const float gC = uni(ex2(static_cast<float>(C) * lg));
 
-    // ---- S-waves: state entering the segment
+    // ---- S-waves: state (and, for linear attention, normaliser) entering the segment
     f32x4 sacc[OW ? 1 : SKT][OW ? 1 : NVT];
+    float zacc[SKT];  // z[16m + l16] of this wave's dk tiles (linear attention)
     if constexpr (!OW) {
 #pragma unroll
-        for (int mi = 0; mi < SKT; ++mi)
+        for (int mi = 0; mi < SKT; ++mi) {
+            zacc[mi] = 0.f;
 #pragma unroll
             for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if (seg > 0) {
-            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * Cf::STATE;
+            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * Cf::WS;
             const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
             for (int j = 0; j < seg; ++j) {
                 const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j)));
-                const float* sj = wsb + static_cast<long long>(j) * Cf::STATE;
+                const float* sj = wsb + static_cast<long long>(j) * Cf::WS;
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi)
+                for (int mi = 0; mi < SKT; ++mi) {
 #pragma unroll
                     for (int n = 0; n < NVT; ++n)
                         sacc[mi][n] += wj * *reinterpret_cast<const f32x4*>(sj + ws_tile_off(SKT * P + mi, n, NVT, l));
+                    if constexpr (LIN) zacc[mi] += sj[Cf::STATE + 16 * (SKT * P + mi) + l16];
+                }
             }
         }
     }
@@ -406,6 +456,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 for (int n = 0; n < NVT; ++n)
                     *reinterpret_cast<u16x4*>(sb + swz_byte<KRU>(perm_row(16 * n + l16), 2 * m + (g >> 1)) +
                                               (g & 1) * 8) = cvt4_bf16(sacc[mi][n]);
+                if (LIN && g == 0) tl.z[16 * m + l16] = zacc[mi];
             }
         }
     };
@@ -463,6 +514,21 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
         const unsigned short* kb = tl.k[B];
         const unsigned short* vb = tl.v[B];
 
+        if constexpr (LIN) {
+            // phi on the K chunk, in place; rows past the end (loaded as zeros)
+            // stay zero rather than phi(0) = 1
+            constexpr int UPT = C * DK / 8 / kThreads;  // 16-byte units per thread
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                const int u = threadIdx.x + kThreads * i;
+                if (u / KRU < clen) {
+                    bf16x8* pk = reinterpret_cast<bf16x8*>(tl.k[B] + 8 * u);
+                    *pk = phi8(*pk);
+                }
+            }
+            lds_barrier();
+        }
+
         if constexpr (OW) {
             LaneOff lk = lk0;
             opaque<QF>(lk);
@@ -472,6 +538,13 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 f1[r] = f1_0[r];
                 opaque(f1[r]);
             }
+            // ---- Q operands (phi(q) for linear attention)
+            bf16x8 qp[NS][QF];
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+                for (int ks = 0; ks < QF; ++ks) qp[s][ks] = LIN ? phi8(qf[B][s][ks]) : qf[B][s][ks];
+
             // ---- S^T tiles = K Q^T for key tiles jt <= query tile
             f32x4 pacc[NS][NI];
 #pragma unroll
@@ -487,7 +560,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 for (int jt = 0; jt <= ITMAX; ++jt)
 #pragma unroll
                     for (int s = 0; s < NS; ++s)
-                        if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], qf[B][s][ks], pacc[s][jt]);
+                        if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], qp[s][ks], pacc[s][jt]);
             }
 
             // ---- decay mask, bf16 P^T operands (two key tiles per operand)
@@ -510,6 +583,27 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                         pb[s][js] = cat_bf16(cvt4_bf16(lo), cvt4_bf16(hi));
                     }
 
+            // ---- linear attention: 1 / (row sum of P + phi(q) . z_prev + eps) per query
+            float rden[NS];
+            if constexpr (LIN) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int js = 0; js < NB; ++js)
+                        if (2 * js <= its(s)) t += sum8(pb[s][js]);  // the bf16 weights the numerator uses
+#pragma unroll
+                    for (int ks = 0; ks < QF; ++ks) {
+                        const u16x8 e = __builtin_bit_cast(u16x8, qp[s][ks]);
+                        const f32x4 z0 = *reinterpret_cast<const f32x4*>(tl.z + 32 * ks + 8 * g);
+                        const f32x4 z1 = *reinterpret_cast<const f32x4*>(tl.z + 32 * ks + 8 * g + 4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) t += bf2f(e[i]) * z0[i] + bf2f(e[i + 4]) * z1[i];
+                    }
+                    rden[s] = 1.f / (sum_over_groups(t) + a.eps);
+                }
+            }
+
             // ---- O^T = xi S_prev^T Q^T + V^T P^T per value-tile pair; 16-byte stores
             int rowo = rowo0, uo = uo0;
             opaque(rowo);
@@ -528,10 +622,12 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                     for (int ks = 0; ks < QF; ++ks) {
                         const bf16x8 sf = b128_at(tl.s, 16 * n * KRB + lk.opr[ks]);
 #pragma unroll
-                        for (int s = 0; s < NS; ++s) oacc[s][b] = mfma_bf16(sf, qf[B][s][ks], oacc[s][b]);
+                        for (int s = 0; s < NS; ++s) oacc[s][b] = mfma_bf16(sf, qp[s][ks], oacc[s][b]);
                     }
+                    if constexpr (!LIN) {
 #pragma unroll
-                    for (int s = 0; s < NS; ++s) oacc[s][b] *= xi[s];
+                        for (int s = 0; s < NS; ++s) oacc[s][b] *= xi[s];
+                    }
 #pragma unroll
                     for (int js = 0; 2 * js <= ITMAX; ++js) {
                         const bf16x8 vf = cat_bf16(tr_at(vb, 32 * js * VRB + rowo + uoa + 8 * b),
@@ -543,6 +639,10 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 }
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
+                    if constexpr (LIN) {
+                        oacc[s][0] *= rden[s];
+                        oacc[s][1] *= rden[s];
+                    }
                     const int row = 16 * its(s) + l16;  // rows past the end are dropped by the resource
                     bstore16_nt(ro, static_cast<unsigned>((row * DV + 32 * pa + 8 * g) * 2),
                                 cat_bf16(cvt4_bf16(oacc[s][0]), cvt4_bf16(oacc[s][1])));
@@ -559,40 +659,59 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 zb[e] = zb0[e];
                 opaque(zb[e]);
             }
-            // ---- zeta-scaled K^T operands of the state update
+            // ---- zeta-scaled K^T operands of the state update (phi(k)^T, unscaled,
+            // for linear attention, with their column sums)
             bf16x8 kz[SKT][NB];
+            float zsum[SKT];
+#pragma unroll
+            for (int mi = 0; mi < SKT; ++mi) zsum[mi] = 0.f;
 #pragma unroll
             for (int js = 0; js < NB; ++js) {
-                float z[8];
-                if (!tail) {
+                if constexpr (LIN) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj[js];
-                } else {
-                    // gamma^(clen - 1 - key) for keys inside the chunk, 0 past its end
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int ex = clen - 1 - 32 * js - slot_key(g, e);
-                        z[e] = (ex < 0) ? 0.f : ex2(static_cast<float>(ex) * lg);
+                    for (int mi = 0; mi < SKT; ++mi) {
+                        kz[mi][js] = tr_block<KRU>(kb, 32 * js, ((SKT * P + mi) << 5) ^ lk.z16, lk);
+                        zsum[mi] += sum8(kz[mi][js]);
                     }
-                }
+                } else {
+                    float z[8];
+                    if (!tail) {
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi)
-                    kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * P + mi) << 5) ^ lk.z16, lk, z);
+                        for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj[js];
+                    } else {
+                        // gamma^(clen - 1 - key) for keys inside the chunk, 0 past its end
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int ex = clen - 1 - 32 * js - slot_key(g, e);
+                            z[e] = (ex < 0) ? 0.f : ex2(static_cast<float>(ex) * lg);
+                        }
+                    }
+#pragma unroll
+                    for (int mi = 0; mi < SKT; ++mi)
+                        kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * P + mi) << 5) ^ lk.z16, lk, z);
+                }
             }
 
-            // ---- S = gamma^c S + (zeta K)^T V
+            // ---- S = gamma^c S + (zeta K)^T V   (z += sum phi(k) for linear attention)
             const float gc = tail ? uni(ex2(static_cast<float>(clen) * lg)) : gC;
 #pragma unroll
             for (int n = 0; n < NVT; ++n) {
                 const int xt = (n << 5) ^ lv.z16;
+                if constexpr (!LIN) {
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] *= gc;
+                    for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] *= gc;
+                }
 #pragma unroll
                 for (int js = 0; js < NB; ++js) {
                     const bf16x8 vf = tr_block<VRU>(vb, 32 * js, xt, lv);
 #pragma unroll
                     for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] = mfma_bf16(kz[mi][js], vf, sacc[mi][n]);
                 }
+            }
+            if constexpr (LIN) {
+                // lanes l, l^16, l^32, l^48 hold the four key groups of column 16m + l%16
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi) zacc[mi] += sum_over_groups(zsum[mi]);
             }
             lds_barrier();  // every O-wave is done reading the old state copy
             write_state_copy();
@@ -621,65 +740,87 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
     }
 }
 
-template <int C, int DK, int DV>
+template <int C, int DK, int DV, bool LIN>
 __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned short k0[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short k1[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short v0[C * DV];
     __shared__ __attribute__((aligned(16))) unsigned short v1[C * DV];
-    const STiles tl{{k0, k1}, {v0, v1}, nullptr};
+    const STiles tl{{k0, k1}, {v0, v1}, nullptr, nullptr};
     const int segs = a.G - 1;
     const int bh = blockIdx.x / segs, seg = blockIdx.x % segs;
-    const float lg = a.log2g[bh % a.H];
+    const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    state_body<C, DK, DV>(a, tl, bh, seg, lg, wave);
+    state_body<C, DK, DV, LIN>(a, tl, bh, seg, lg, wave);
 }
 
-template <int C, int DK, int DV>
+template <int C, int DK, int DV, bool LIN>
 __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned short k0[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short k1[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short v0[C * DV];
     __shared__ __attribute__((aligned(16))) unsigned short v1[C * DV];
     __shared__ __attribute__((aligned(16))) unsigned short st[DV * DK];
-    const STiles tl{{k0, k1}, {v0, v1}, st};
+    float* zp = nullptr;
+    if constexpr (LIN) {
+        __shared__ __attribute__((aligned(16))) float zs[DK];  // only linear attention carries z
+        zp = zs;
+    }
+    const STiles tl{{k0, k1}, {v0, v1}, st, zp};
     const int bh = blockIdx.x / a.G, seg = blockIdx.x % a.G;
-    const float lg = a.log2g[bh % a.H];
+    const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: walk_body<C, DK, DV, 0, true>(a, tl, bh, seg, lg); break;
-        case 1: walk_body<C, DK, DV, 1, true>(a, tl, bh, seg, lg); break;
-        case 2: walk_body<C, DK, DV, 2, true>(a, tl, bh, seg, lg); break;
-        case 3: walk_body<C, DK, DV, 3, true>(a, tl, bh, seg, lg); break;
-        case 4: walk_body<C, DK, DV, 0, false>(a, tl, bh, seg, lg); break;
-        case 5: walk_body<C, DK, DV, 1, false>(a, tl, bh, seg, lg); break;
-        case 6: walk_body<C, DK, DV, 2, false>(a, tl, bh, seg, lg); break;
-        default: walk_body<C, DK, DV, 3, false>(a, tl, bh, seg, lg); break;
+        case 0: walk_body<C, DK, DV, LIN, 0, true>(a, tl, bh, seg, lg); break;
+        case 1: walk_body<C, DK, DV, LIN, 1, true>(a, tl, bh, seg, lg); break;
+        case 2: walk_body<C, DK, DV, LIN, 2, true>(a, tl, bh, seg, lg); break;
+        case 3: walk_body<C, DK, DV, LIN, 3, true>(a, tl, bh, seg, lg); break;
+        case 4: walk_body<C, DK, DV, LIN, 0, false>(a, tl, bh, seg, lg); break;
+        case 5: walk_body<C, DK, DV, LIN, 1, false>(a, tl, bh, seg, lg); break;
+        case 6: walk_body<C, DK, DV, LIN, 2, false>(a, tl, bh, seg, lg); break;
+        default: walk_body<C, DK, DV, LIN, 3, false>(a, tl, bh, seg, lg); break;
     }
 }
 
-template <int C, int DK, int DV>
+// LDS available to one workgroup on gfx950, and what the walk kernel takes.
+constexpr int kLdsBytes = 160 * 1024;
+template <int C, int DK, int DV, bool LIN>
+constexpr bool walk_fits() {
+    return 2 * C * DK * 2 + 2 * C * DV * 2 + DV * DK * 2 + (LIN ? DK * 4 : 0) <= kLdsBytes;
+}
+// Variants that are built: they fit in LDS, and linear attention with dk = 128
+// runs with 64-token chunks (at 128 its walk kernel would spill registers).
+template <int C, int DK, int DV, bool LIN>
+constexpr bool walk_supported() {
+    return walk_fits<C, DK, DV, LIN>() && !(LIN && C == 128 && DK == 128);
+}
+
+template <int C, int DK, int DV, bool LIN>
 hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
+    if constexpr (!walk_supported<C, DK, DV, LIN>()) {
+        return hipErrorInvalidConfiguration;
+    } else {
     const long long bh = static_cast<long long>(a.B) * a.H;
     if (bh <= 0) return hipSuccess;
     if (bh * a.G > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.G > 1) {
-        hipLaunchKernelGGL((seg_state_kernel<C, DK, DV>), dim3(static_cast<unsigned>(bh * (a.G - 1))),
+        hipLaunchKernelGGL((seg_state_kernel<C, DK, DV, LIN>), dim3(static_cast<unsigned>(bh * (a.G - 1))),
                            dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, LIN>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
+    }
 }
 
-template <int C>
+template <int C, bool LIN>
 hipError_t launch_chunk(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    if (dk == 64 && dv == 64) return launch_t<C, 64, 64>(a, stream);
-    if (dk == 64 && dv == 128) return launch_t<C, 64, 128>(a, stream);
-    if (dk == 128 && dv == 64) return launch_t<C, 128, 64>(a, stream);
-    if (dk == 128 && dv == 128) return launch_t<C, 128, 128>(a, stream);
+    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, LIN>(a, stream);
+    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, LIN>(a, stream);
+    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, LIN>(a, stream);
+    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, LIN>(a, stream);
     return hipErrorInvalidValue;
 }
 

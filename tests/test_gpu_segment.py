@@ -97,3 +97,55 @@ def test_segment_auto_choice(monkeypatch):
     w, inp = _inputs(seed=16, B=1, H=2, T=3000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
     out, fs = _run(inp, 128, monkeypatch, segments=None)
     _check("segment auto", out, fs, inp)
+
+
+# ------------------------------------------------------------- elu+1 linear attention
+def _run_lin(inp, monkeypatch, path="segment", segments=None):
+    monkeypatch.setenv("RET_FWD_PATH", path)
+    if segments is None:
+        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
+    else:
+        monkeypatch.setenv("RET_FWD_SEGMENTS", str(segments))
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    print(f"[segment] linattn path={path} G={segments} shape={tuple(q.shape)} dv={v.shape[-1]}", flush=True)
+    out = rc.linear_attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _check_lin(tag, out, inp):
+    ref, _, _ = oracle.linattn_recurrent(inp["q"], inp["k"], inp["v"], nthreads=8)
+    e = oracle.rel_frobenius(out, ref)
+    print(f"[parity] {tag}: out {e:.3e} (tol {TOL:.0e})", flush=True)
+    assert e <= TOL and np.isfinite(out).all(), tag
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, 1), (1333, 3), (2000, 8)])
+def test_segment_linattn_full(dk, dv, T, G, monkeypatch):
+    w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=2, T=T, dk=dk, dv=dv)
+    inp = wl.make_inputs(w, 21)
+    out = _run_lin(inp, monkeypatch, segments=G)
+    _check_lin(f"linattn segment dk={dk} dv={dv} T={T} G={G}", out, inp)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 300])
+def test_segment_linattn_short_and_ragged(T, monkeypatch):
+    w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=1, H=3, T=T)
+    inp = wl.make_inputs(w, 22)
+    out = _run_lin(inp, monkeypatch, segments=2)
+    _check_lin(f"linattn segment short T={T}", out, inp)
+
+
+def test_segment_linattn_matches_slice_path(monkeypatch):
+    w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=4, T=1500)
+    inp = wl.make_inputs(w, 23)
+    o_seg = _run_lin(inp, monkeypatch, segments=5)
+    o_seg2 = _run_lin(inp, monkeypatch, segments=5)
+    assert np.array_equal(o_seg, o_seg2), "run-to-run results differ"
+    o_sl = _run_lin(inp, monkeypatch, path="slice")
+    _check_lin("linattn segment G=5", o_seg, inp)
+    _check_lin("linattn slice", o_sl, inp)
+    e = oracle.rel_frobenius(o_seg, o_sl)
+    print(f"[parity] linattn segment vs slice {e:.3e}", flush=True)
+    assert e <= TOL
