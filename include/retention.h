@@ -19,14 +19,25 @@
  *  - stream is a hipStream_t (passed as void*); NULL means the default
  *    stream.  Calls are asynchronous: they enqueue kernels on the stream and
  *    return.  Results are visible after the stream is synchronised.
- *  - Ownership: the caller allocates and owns every buffer.  The library
- *    allocates no device memory and keeps no pointer after the call returns.
+ *  - Ownership: the caller allocates and owns every tensor buffer; the
+ *    library keeps no pointer to them after the call returns.  The only
+ *    device memory the library allocates is the segment-state workspace of
+ *    the bf16 forward paths (retention_fwd, linear_attn_fwd): G-1 fp32 states
+ *    per (b, h) when a sequence is split into G segments, at most
+ *    B*H*15*(dk*dv + dk)*4 bytes.  It is taken stream-ordered from a
+ *    library-owned memory pool (one per device, created on first use, kept
+ *    until the process ends) and released on the same stream after the
+ *    call's kernels, so calls on different streams never share it.
  *  - Errors: the return value is RET_OK (0) or a negative RET_ERR_* code.
  *    Argument errors are detected on the host before anything is enqueued, so
  *    a failed call has no effect.  RET_ERR_HIP reports a failed launch.  A
  *    human-readable message for the last error of the calling thread is
  *    returned by retention_last_error().  Inputs are never modified (except
  *    state in retention_decode_step, which is updated in place).
+ *  - Tuning and testing knobs, read from the environment at every call:
+ *    RET_FWD_PATH = "slice" | "segment" forces the forward path (segment
+ *    needs bf16; anything else means automatic), RET_FWD_SEGMENTS = n forces
+ *    the segment count.  Neither changes results beyond rounding.
  *
  * Sources (page title, then passage):
  *   "RetNet" (bembew.net): the single-head definition O = (Q K^T (.) D) V with
@@ -66,7 +77,7 @@ extern "C" {
 #define RET_ERR_PHI (-6)       /* unknown feature map */
 #define RET_ERR_ALIGN (-7)     /* a device pointer is not 16-byte aligned */
 #define RET_ERR_ALIAS (-8)     /* an output overlaps an input or another output */
-#define RET_ERR_HIP (-10)      /* the HIP runtime rejected a launch */
+#define RET_ERR_HIP (-10)      /* a launch or the workspace allocation failed */
 
 /*
  * retention_fwd -- causal retention over whole sequences, chunkwise form,
@@ -78,8 +89,10 @@ extern "C" {
  * "Efficient and Sparse Transformers", section 6, "Chunkwise form".)  Inside a
  * chunk of `chunk` tokens the masked, decayed Q K^T V is computed in parallel;
  * across chunks a fp32 dk x dv state per (b, h) is carried with
- * S <- gamma^c S + (K (.) zeta)^T V.  The result does not depend on `chunk`
- * beyond rounding.
+ * S <- gamma^c S + (K (.) zeta)^T V.  bf16 inputs split each sequence into
+ * segments whose entering states are decayed sums of the earlier segments'
+ * contributions (the recurrence is linear); fp32 inputs walk whole sequences.
+ * The result does not depend on `chunk` or on the split beyond rounding.
  *
  *   q, k, v      device, [B][H][T][dk|dv], dtype
  *   gamma        host, H floats in (0, 1]
@@ -114,7 +127,7 @@ int retention_decode_step(const void *q, const void *k, const void *v,
 
 /*
  * linear_attn_fwd -- causal linear attention with a positive feature map and
- * its normaliser, chunkwise (internal chunk 128):
+ * its normaliser, chunkwise (internal chunk 128; 64 for bf16 with dk = 128):
  *
  *   S_t = S_{t-1} + phi(k_t) v_t^T,  z_t = z_{t-1} + phi(k_t),
  *   out_t = S_t^T phi(q_t) / (z_t^T phi(q_t) + eps)
