@@ -50,6 +50,7 @@ struct SegArgs {
     int B, H, T;
     int G;               // segments per (b, h); every segment but the last is full
     int cps;             // chunks per segment
+    int scps;            // state-kernel blocks per segment (set by the launcher)
     float eps;           // linear attention only
     float log2g[kMaxHeads];
 };

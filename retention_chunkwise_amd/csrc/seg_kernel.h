@@ -220,11 +220,18 @@ __device__ __forceinline__ unsigned dma_offset(int w, int l) {
 // ---------------------------------------------------------------------------
 // seg_state_kernel: dS_j for one (b, h) and segment j < G - 1.
 
-template <int C, int DK, int DV, bool LIN>
-__device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg, int w) {
+// The segment contribution does not depend on how the segment is blocked, so
+// this kernel walks 64-token blocks (C here is the block length) through a
+// ring of NBUF LDS buffers, prefetching NBUF-1 blocks ahead.  Blocks run last
+// to first (the walk kernel then finds each segment's first chunks most
+// recently read).
+template <int C, int DK, int DV, bool LIN, int NBUF>
+__device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kring, unsigned short* vring, int bh,
+                                           int seg, float lg, int w) {
     using Cf = SCfg<C, DK, DV, LIN>;
     constexpr int NB = Cf::NB, NVT = Cf::NVT, NVH = Cf::NVH, SKT = Cf::SKT, KRU = Cf::KRU, VRU = Cf::VRU;
     constexpr int KIW = Cf::KIW, VIW = Cf::VIW;
+    constexpr int OPS = KIW + VIW;  // DMA instructions a thread issues per block
     const int l = threadIdx.x & 63, g = l >> 4;
     const int p = w & 3, h = w >> 2;
     const int T = a.T;
@@ -247,28 +254,34 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
         for (int ni = 0; ni < NVH; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int c_first = seg * a.cps, c_last = c_first + a.cps - 1;  // all chunks full
+    const int nblk = a.scps;                      // blocks per segment, all full
+    const long long t_seg = static_cast<long long>(seg) * nblk * C;
+    const unsigned kring0 = __builtin_amdgcn_readfirstlane(lds_addr_of(kring));
+    const unsigned vring0 = __builtin_amdgcn_readfirstlane(lds_addr_of(vring));
 
-    auto load_chunk = [&](int c, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        const long long t0 = static_cast<long long>(c) * C;
-        const u32x4 wk = rsrc_words(kh + t0 * DK, C * DK * 2);
-        const u32x4 wv = rsrc_words(vh + t0 * DV, C * DV * 2);
-        const unsigned kbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.k[buf]));
-        const unsigned vbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.v[buf]));
+    // Block i of the walk is segment block nblk-1-i.  Issued for every i (a
+    // block past the segment start gets a zero-length range, which moves no
+    // data), so each step issues the same number of DMA instructions.
+    auto load_block = [&](int i) {
+        const int bi = nblk - 1 - i;
+        const long long t0 = t_seg + static_cast<long long>(bi) * C;
+        const int bytes = (bi >= 0) ? C : 0;
+        const u32x4 wk = rsrc_words(kh + t0 * DK, bytes * DK * 2);
+        const u32x4 wv = rsrc_words(vh + t0 * DV, bytes * DV * 2);
+        const int buf = i % NBUF;
+        const unsigned kbase = kring0 + buf * (C * DK * 2), vbase = vring0 + buf * (C * DV * 2);
 #pragma unroll
         for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (w + 8 * m) * 1024, koff + 8192u * m);
 #pragma unroll
         for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (w + 8 * m) * 1024, voff + 8192u * m);
     };
 
-    // chunks in reverse order (the walk kernel then finds the segment's first
-    // chunks most recently read)
-    auto step = [&](int c, auto bufc) {
-        constexpr int B = decltype(bufc)::value;
-        wait_vmcnt<0>();
-        lds_barrier();
-        if (c > c_first) load_chunk(c - 1, std::integral_constant<int, 1 - B>{});
+    for (int i = 0; i < NBUF - 1; ++i) load_block(i);
+    for (int i = 0; i < nblk; ++i) {
+        // blocks i+1 .. i+NBUF-2 may still be in flight; block i has landed
+        wait_vmcnt<(NBUF - 2) * OPS>();
+        lds_barrier();  // block i in LDS everywhere; block i-1's buffer is free
+        load_block(i + NBUF - 1);
         LaneOff lk = lk0, lv = lv0;
         opaque<0>(lk);
         opaque<0>(lv);
@@ -278,10 +291,11 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
             zb[e] = zb0[e];
             opaque(zb[e]);
         }
-        // gamma^(C (c_last - c)): decay from the end of chunk c to the end of the segment
-        const float wc = uni(ex2(static_cast<float>(C) * static_cast<float>(c_last - c) * lg));
-        const unsigned short* kb = tl.k[B];
-        const unsigned short* vb = tl.v[B];
+        // gamma^(C i): decay from the end of this block to the end of the segment
+        const float wc = uni(ex2(static_cast<float>(C) * static_cast<float>(i) * lg));
+        const int buf = i % NBUF;
+        const unsigned short* kb = kring + buf * (C * DK);
+        const unsigned short* vb = vring + buf * (C * DV);
         bf16x8 kz[SKT][NB];
 #pragma unroll
         for (int js = 0; js < NB; ++js) {
@@ -312,13 +326,8 @@ __device__ __forceinline__ void state_body(const SegArgs& a, const STiles& tl, i
                 for (int mi = 0; mi < SKT; ++mi) acc[mi][ni] = mfma_bf16(kz[mi][js], vf, acc[mi][ni]);
             }
         }
-    };
-
-    load_chunk(c_last, std::integral_constant<int, 0>{});
-    for (int c = c_last; c >= c_first; c -= 2) {
-        step(c, std::integral_constant<int, 0>{});
-        if (c - 1 >= c_first) step(c - 1, std::integral_constant<int, 1>{});
     }
+    wait_vmcnt<0>();  // drain the zero-length tail loads before the workgroup ends
 
     float* wsj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * Cf::WS;
 #pragma unroll
@@ -742,18 +751,19 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
     }
 }
 
-template <int C, int DK, int DV, bool LIN>
+// State kernel blocking: 64-token blocks, 4-deep ring.
+constexpr int kStateBlock = 64;
+constexpr int kStateRing = 4;
+
+template <int DK, int DV, bool LIN>
 __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned short k0[C * DK];
-    __shared__ __attribute__((aligned(16))) unsigned short k1[C * DK];
-    __shared__ __attribute__((aligned(16))) unsigned short v0[C * DV];
-    __shared__ __attribute__((aligned(16))) unsigned short v1[C * DV];
-    const STiles tl{{k0, k1}, {v0, v1}, nullptr, nullptr};
+    __shared__ __attribute__((aligned(16))) unsigned short kring[kStateRing * kStateBlock * DK];
+    __shared__ __attribute__((aligned(16))) unsigned short vring[kStateRing * kStateBlock * DV];
     const int segs = a.G - 1;
     const int bh = blockIdx.x / segs, seg = blockIdx.x % segs;
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    state_body<C, DK, DV, LIN>(a, tl, bh, seg, lg, wave);
+    state_body<kStateBlock, DK, DV, LIN, kStateRing>(a, kring, vring, bh, seg, lg, wave);
 }
 
 template <int C, int DK, int DV, bool LIN>
@@ -806,8 +816,10 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     if (bh <= 0) return hipSuccess;
     if (bh * a.G > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.G > 1) {
-        hipLaunchKernelGGL((seg_state_kernel<C, DK, DV, LIN>), dim3(static_cast<unsigned>(bh * (a.G - 1))),
-                           dim3(kThreads), 0, stream, a);
+        SegArgs sa = a;
+        sa.scps = a.cps * (C / kStateBlock);
+        hipLaunchKernelGGL((seg_state_kernel<DK, DV, LIN>), dim3(static_cast<unsigned>(bh * (a.G - 1))),
+                           dim3(kThreads), 0, stream, sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
