@@ -22,9 +22,9 @@
  *  - Ownership: the caller allocates and owns every tensor buffer; the
  *    library keeps no pointer to them after the call returns.  The only
  *    device memory the library allocates is the segment-state workspace of
- *    the bf16 forward paths (retention_fwd, linear_attn_fwd): G-1 fp32 states
- *    per (b, h) when a sequence is split into G segments, at most
- *    B*H*15*(dk*dv + dk)*4 bytes.  It is taken stream-ordered from a
+ *    the bf16 forward paths (retention_fwd, linear_attn_fwd): up to 16 fp32
+ *    partial states per (b, h) when a sequence is split into segments, at
+ *    most B*H*16*(dk*dv + dk)*4 bytes.  It is taken stream-ordered from a
  *    library-owned memory pool (one per device, created on first use, kept
  *    until the process ends) and released on the same stream after the
  *    call's kernels, so calls on different streams never share it.

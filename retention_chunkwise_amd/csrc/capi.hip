@@ -148,12 +148,24 @@ hipError_t launch_segment_path(const void* q, const void* k, const void* v, void
         sa.G = ret::choose_segments(bh, nch, 256, 4, 16, &cps);
     }
     sa.cps = cps;
+    // state-kernel workgroups per segment: enough to occupy the chip, dividing
+    // the segment's 64-token blocks evenly, at most 16 workspace slots per
+    // (b, h) (the walk sums up to that many states on entry)
+    const int sblocks = cps * (chunk / 64);
+    const long long sgroups = bh * (sa.G - 1);
+    int pieces = (sgroups > 0 && sgroups < 256) ? static_cast<int>(256 / sgroups) : 1;
+    if (sa.G > 1 && pieces > 16 / (sa.G - 1)) pieces = 16 / (sa.G - 1);
+    if (pieces > sblocks) pieces = sblocks;
+    if (pieces < 1) pieces = 1;
+    while (pieces > 1 && sblocks % pieces != 0) --pieces;
+    sa.pieces = pieces;
     sa.q = q; sa.k = k; sa.v = v; sa.out = out; sa.final_state = final_state;
     sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
     if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
     size_t ws_bytes = 4;
     const long long slot = static_cast<long long>(dk) * dv + (linattn ? dk : 0);
-    if (sa.G > 1 && (!mul_ok(ws_bytes, bh) || !mul_ok(ws_bytes, sa.G - 1) || !mul_ok(ws_bytes, slot)))
+    if (sa.G > 1 && (!mul_ok(ws_bytes, bh) || !mul_ok(ws_bytes, sa.G - 1) || !mul_ok(ws_bytes, sa.pieces) ||
+                     !mul_ok(ws_bytes, slot)))
         return hipErrorInvalidValue;
     void* ws = nullptr;
     if (sa.G > 1) {

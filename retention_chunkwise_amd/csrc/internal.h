@@ -46,11 +46,13 @@ struct SegArgs {
     const void* v;
     void* out;
     float* final_state;  // may be null
-    float* ws;           // [B*H][G-1][dk*dv (+ dk)] fp32 segment states (and normalisers); unused when G == 1
+    float* ws;           // [B*H][G-1][pieces][dk*dv (+ dk)] fp32 segment states (and normalisers);
+                         // unused when G == 1
     int B, H, T;
     int G;               // segments per (b, h); every segment but the last is full
     int cps;             // chunks per segment
     int scps;            // state-kernel blocks per segment (set by the launcher)
+    int pieces;          // state-kernel workgroups per segment (divides scps)
     float eps;           // linear attention only
     float log2g[kMaxHeads];
 };

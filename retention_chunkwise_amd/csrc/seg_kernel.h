@@ -227,7 +227,7 @@ __device__ __forceinline__ unsigned dma_offset(int w, int l) {
 // recently read).
 template <int C, int DK, int DV, bool LIN, int NBUF>
 __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kring, unsigned short* vring, int bh,
-                                           int seg, float lg, int w) {
+                                           int seg, int piece, float lg, int w) {
     using Cf = SCfg<C, DK, DV, LIN>;
     constexpr int NB = Cf::NB, NVT = Cf::NVT, NVH = Cf::NVH, SKT = Cf::SKT, KRU = Cf::KRU, VRU = Cf::VRU;
     constexpr int KIW = Cf::KIW, VIW = Cf::VIW;
@@ -254,8 +254,9 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
         for (int ni = 0; ni < NVH; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int nblk = a.scps;                      // blocks per segment, all full
-    const long long t_seg = static_cast<long long>(seg) * nblk * C;
+    // this workgroup sums piece `piece` of segment `seg`: blocks [piece nblk, +nblk)
+    const int nblk = a.scps / a.pieces;           // blocks per piece, all full
+    const long long t_seg = (static_cast<long long>(seg) * a.scps + static_cast<long long>(piece) * nblk) * C;
     const unsigned kring0 = __builtin_amdgcn_readfirstlane(lds_addr_of(kring));
     const unsigned vring0 = __builtin_amdgcn_readfirstlane(lds_addr_of(vring));
 
@@ -291,7 +292,7 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
             zb[e] = zb0[e];
             opaque(zb[e]);
         }
-        // gamma^(C i): decay from the end of this block to the end of the segment
+        // gamma^(C i): decay from the end of this block to the end of the piece
         const float wc = uni(ex2(static_cast<float>(C) * static_cast<float>(i) * lg));
         const int buf = i % NBUF;
         const unsigned short* kb = kring + buf * (C * DK);
@@ -329,7 +330,7 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
     }
     wait_vmcnt<0>();  // drain the zero-length tail loads before the workgroup ends
 
-    float* wsj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * Cf::WS;
+    float* wsj = a.ws + ((static_cast<long long>(bh) * (a.G - 1) + seg) * a.pieces + piece) * Cf::WS;
 #pragma unroll
     for (int mi = 0; mi < SKT; ++mi) {
 #pragma unroll
@@ -439,11 +440,15 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (seg > 0) {
-            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * Cf::WS;
+            // piece p of segment j is decayed by gamma^(L (seg-1-j) + Lp (pieces-1-p))
+            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * a.pieces * Cf::WS;
             const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
-            for (int j = 0; j < seg; ++j) {
-                const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j)));
-                const float* sj = wsb + static_cast<long long>(j) * Cf::WS;
+            const float lpiece = lseg / static_cast<float>(a.pieces);
+            for (int jp = 0; jp < seg * a.pieces; ++jp) {
+                const int j = jp / a.pieces, pc = jp % a.pieces;
+                const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
+                                         lpiece * static_cast<float>(a.pieces - 1 - pc)));
+                const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
 #pragma unroll
                 for (int mi = 0; mi < SKT; ++mi) {
 #pragma unroll
@@ -759,11 +764,11 @@ template <int DK, int DV, bool LIN>
 __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned short kring[kStateRing * kStateBlock * DK];
     __shared__ __attribute__((aligned(16))) unsigned short vring[kStateRing * kStateBlock * DV];
-    const int segs = a.G - 1;
-    const int bh = blockIdx.x / segs, seg = blockIdx.x % segs;
+    const int slots = (a.G - 1) * a.pieces;
+    const int bh = blockIdx.x / slots, slot = blockIdx.x % slots;
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    state_body<kStateBlock, DK, DV, LIN, kStateRing>(a, kring, vring, bh, seg, lg, wave);
+    state_body<kStateBlock, DK, DV, LIN, kStateRing>(a, kring, vring, bh, slot / a.pieces, slot % a.pieces, lg, wave);
 }
 
 template <int C, int DK, int DV, bool LIN>
@@ -818,7 +823,7 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     if (a.G > 1) {
         SegArgs sa = a;
         sa.scps = a.cps * (C / kStateBlock);
-        hipLaunchKernelGGL((seg_state_kernel<DK, DV, LIN>), dim3(static_cast<unsigned>(bh * (a.G - 1))),
+        hipLaunchKernelGGL((seg_state_kernel<DK, DV, LIN>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
                            dim3(kThreads), 0, stream, sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
