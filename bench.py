@@ -137,9 +137,11 @@ def main():
     out = torch.empty_like(v)
     fs = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     gamma = inp["gamma"]
+    ws_n = rc.retention_fwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, q.dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
     def fwd():
-        rc.retention_fwd(q, k, v, gamma, chunk=w.chunk, out=out, final_state=fs)
+        rc.retention_fwd(q, k, v, gamma, chunk=w.chunk, out=out, final_state=fs, workspace=ws)
 
     kern_ms, step_ms = time_launches(fwd, args.steps, args.warmup)
     tokens = w.B * w.T
@@ -221,9 +223,11 @@ def main():
         li = wl.make_inputs(wa, seed=0)
         lq, lk, lv = (li[n].to(dev) for n in ("q", "k", "v"))
         lout = torch.empty_like(lv)
+        lws = torch.empty(max(rc.linear_attn_workspace_bytes(wa.B, wa.H, wa.T, wa.dk, wa.dv, lq.dtype), 1),
+                          dtype=torch.uint8, device=dev)
 
         def lstep():
-            rc.linear_attn_fwd(lq, lk, lv, out=lout)
+            rc.linear_attn_fwd(lq, lk, lv, out=lout, workspace=lws)
 
         l_kern, l_wall = time_launches(lstep, args.steps, args.warmup)
         l_fl = M.fwd_flops(wa.B, wa.H, wa.T, wa.dk, wa.dv, wa.chunk)
@@ -235,7 +239,7 @@ def main():
             "mfma_peak_frac": l_fl / (l_kern * 1e-3) / 1e12 / M.PEAK_TFLOPS["bf16"],
             "gbs": l_gbs, "hbm_frac": l_gbs / M.PEAK_HBM_GBS,
         }
-        del lq, lk, lv, lout
+        del lq, lk, lv, lout, lws
 
     if args.calibrate_copy:
         # plain device-to-device copies of a known size, for scaling HBM counters

@@ -19,15 +19,16 @@
  *  - stream is a hipStream_t (passed as void*); NULL means the default
  *    stream.  Calls are asynchronous: they enqueue kernels on the stream and
  *    return.  Results are visible after the stream is synchronised.
- *  - Ownership: the caller allocates and owns every tensor buffer; the
- *    library keeps no pointer to them after the call returns.  The only
- *    device memory the library allocates is the segment-state workspace of
- *    the bf16 forward paths (retention_fwd, linear_attn_fwd): up to 16 fp32
- *    partial states per (b, h) when a sequence is split into segments, at
- *    most B*H*16*(dk*dv + dk)*4 bytes.  It is taken stream-ordered from a
- *    library-owned memory pool (one per device, created on first use, kept
- *    until the process ends) and released on the same stream after the
- *    call's kernels, so calls on different streams never share it.
+ *  - Ownership: the caller allocates and owns every buffer, workspace
+ *    included; the library allocates no device memory and keeps no pointer
+ *    after the call returns.  The bf16 forward paths (retention_fwd,
+ *    linear_attn_fwd) split each sequence into segments and need a device
+ *    workspace for the partial segment states: ask
+ *    retention_fwd_workspace_bytes / linear_attn_workspace_bytes for its size
+ *    (0 when none is needed), pass a 16-byte aligned buffer of at least that
+ *    many bytes that overlaps no tensor of the call.  Its contents on entry
+ *    are irrelevant; calls that share a workspace must not overlap in time
+ *    (the same stream, or synchronised streams).
  *  - Errors: the return value is RET_OK (0) or a negative RET_ERR_* code.
  *    Argument errors are detected on the host before anything is enqueued, so
  *    a failed call has no effect.  RET_ERR_HIP reports a failed launch.  A
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 1
+#define RET_ABI_VERSION 2
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -77,6 +78,7 @@ extern "C" {
 #define RET_ERR_PHI (-6)       /* unknown feature map */
 #define RET_ERR_ALIGN (-7)     /* a device pointer is not 16-byte aligned */
 #define RET_ERR_ALIAS (-8)     /* an output overlaps an input or another output */
+#define RET_ERR_WORKSPACE (-9) /* workspace NULL or smaller than the call needs */
 #define RET_ERR_HIP (-10)      /* a launch or the workspace allocation failed */
 
 /*
@@ -102,10 +104,18 @@ extern "C" {
  *                (written); may be NULL.  T = 0 writes zeros.
  *   dk, dv       each 64 or 128; dv must be a multiple of 16
  *   T            >= 0, any value (a short last chunk is handled exactly)
+ *   workspace    device scratch of ws_bytes bytes (see Ownership); may be
+ *                NULL when retention_fwd_workspace_bytes returns 0
  */
 int retention_fwd(const void *q, const void *k, const void *v, const float *gamma,
                   int chunk, void *out, float *final_state, int B, int H, int T,
-                  int dk, int dv, int dtype, void *stream);
+                  int dk, int dv, int dtype, void *workspace, size_t ws_bytes,
+                  void *stream);
+
+/* Workspace bytes retention_fwd needs for these arguments (0: none, or the
+ * arguments are invalid and the call will say why).  Host only. */
+size_t retention_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                     int dtype);
 
 /*
  * retention_decode_step -- one recurrent step for N sequences x H heads,
@@ -135,14 +145,20 @@ int retention_decode_step(const void *q, const void *k, const void *v,
  * ("Linear attention", box "Causal linear attention, recurrent form", and
  * theorem "Recurrent and parallel forms agree".)  Zero initial S and z.
  *
- *   q, k, v  device, [B][H][T][dk|dv], dtype     out  device, [B][H][T][dv]
- *   phi      RET_PHI_ELU1
- *   eps      >= 0 (the pages use 1e-6)
- *   dk, dv   each 64 or 128; T >= 0
+ *   q, k, v    device, [B][H][T][dk|dv], dtype     out  device, [B][H][T][dv]
+ *   phi        RET_PHI_ELU1
+ *   eps        >= 0 (the pages use 1e-6)
+ *   dk, dv     each 64 or 128; T >= 0
+ *   workspace  device scratch of ws_bytes bytes (see Ownership); may be NULL
+ *              when linear_attn_workspace_bytes returns 0
  */
 int linear_attn_fwd(const void *q, const void *k, const void *v, int phi, void *out,
                     int B, int H, int T, int dk, int dv, int dtype, float eps,
-                    void *stream);
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes linear_attn_fwd needs for these arguments (0: none, or the
+ * arguments are invalid).  Host only. */
+size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none).  The pointer stays valid until the next call on that thread. */

@@ -13,6 +13,12 @@ Functions
 retention_fwd(q, k, v, gamma, chunk=64)        -> (out, final_state)
 retention_decode_step(q, k, v, gamma, state)   -> out      (state updated in place)
 linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
+retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
+linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
+
+The two forwards take an optional ``workspace=`` uint8 tensor for the
+segment states of the bf16 paths; without one, the binding takes it from
+PyTorch's allocator for the call.
 """
 from __future__ import annotations
 
@@ -23,7 +29,8 @@ import threading
 import numpy as np
 import torch
 
-__all__ = ["retention_fwd", "retention_decode_step", "linear_attn_fwd", "RetentionError",
+__all__ = ["retention_fwd", "retention_decode_step", "linear_attn_fwd", "retention_fwd_workspace_bytes",
+           "linear_attn_workspace_bytes", "RetentionError",
            "library_path", "load_library", "abi_version", "last_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +44,7 @@ RET_PHI_ELU1 = 1
 ERRORS = {
     -1: "RET_ERR_NULL", -2: "RET_ERR_SHAPE", -3: "RET_ERR_DTYPE", -4: "RET_ERR_CHUNK",
     -5: "RET_ERR_GAMMA", -6: "RET_ERR_PHI", -7: "RET_ERR_ALIGN", -8: "RET_ERR_ALIAS",
-    -10: "RET_ERR_HIP",
+    -9: "RET_ERR_WORKSPACE", -10: "RET_ERR_HIP",
 }
 MAX_HEADS = 256
 
@@ -62,12 +69,16 @@ def load_library():
                     f"{_LIB_PATH} is missing: build it with `python -m retention_chunkwise_amd._build` "
                     "(or __graft_entry__.build()); there is no non-HIP fallback")
             lib = ctypes.CDLL(_LIB_PATH)
-            vp, fp, i = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int
-            lib.retention_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp]
+            vp, fp, i, sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.c_size_t
+            lib.retention_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp, sz, vp]
             lib.retention_fwd.restype = i
+            lib.retention_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+            lib.retention_fwd_workspace_bytes.restype = sz
+            lib.linear_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            lib.linear_attn_workspace_bytes.restype = sz
             lib.retention_decode_step.argtypes = [vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp]
             lib.retention_decode_step.restype = i
-            lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp]
+            lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
             lib.linear_attn_fwd.restype = i
             lib.retention_last_error.argtypes = []
             lib.retention_last_error.restype = ctypes.c_char_p
@@ -124,14 +135,42 @@ def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _workspace(nbytes: int, device, given=None):
+    """Scratch for the segment-split paths: the caller's uint8 tensor when one
+    is given (the library checks its size), else one from PyTorch's allocator
+    on the current stream (returned to that stream's pool after the call is
+    enqueued)."""
+    if given is not None:
+        _check_dev("workspace", given, torch.uint8)
+        return given, given.numel()
+    if nbytes <= 0:
+        return None, 0
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device), int(nbytes)
+
+
+def retention_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                                  dtype=torch.bfloat16) -> int:
+    """Bytes of device workspace retention_fwd needs for these sizes (0: none)."""
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), code))
+
+
+def linear_attn_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype=torch.bfloat16) -> int:
+    """Bytes of device workspace linear_attn_fwd needs for these sizes (0: none)."""
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().linear_attn_workspace_bytes(B, H, T, dk, dv, code))
+
+
 def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
-                  want_state: bool = True):
+                  want_state: bool = True, workspace=None):
     """Chunkwise causal retention from a zero initial state.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv] (float32 or bfloat16, same dtype, on the
     GPU); gamma: H decay values in (0, 1].  Returns (out, final_state) with
     out [B,H,T,dv] in the input dtype and final_state [B,H,dk,dv] float32
-    (None if want_state is False and none was passed).
+    (None if want_state is False and none was passed).  workspace: optional
+    uint8 GPU tensor of at least retention_fwd_workspace_bytes(...) bytes;
+    one is allocated per call when it is omitted.
     """
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -148,9 +187,12 @@ def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
     if final_state is not None:
         _check_dev("final_state", final_state, torch.float32)
     g = _gamma_array(gamma, H)
+    dt = _dtype_code(q)
+    ws, nws = _workspace(lib.retention_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), dt), q.device,
+                         workspace)
     rc = lib.retention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), out.data_ptr(),
                            final_state.data_ptr() if final_state is not None else None,
-                           B, H, T, dk, dv, _dtype_code(q), _stream(q))
+                           B, H, T, dk, dv, dt, ws.data_ptr() if ws is not None else None, nws, _stream(q))
     _raise(rc)
     return out, final_state
 
@@ -181,10 +223,12 @@ def retention_decode_step(q, k, v, gamma, state, out=None):
     return out
 
 
-def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None):
+def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None, workspace=None):
     """Causal linear attention with phi = elu+1 and its normaliser.
 
-    q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv].
+    q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv].  workspace:
+    optional uint8 GPU tensor of at least linear_attn_workspace_bytes(...)
+    bytes; one is allocated per call when it is omitted.
     """
     lib = load_library()
     if phi not in ("elu1", RET_PHI_ELU1):
@@ -198,7 +242,10 @@ def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None):
     if out is None:
         out = torch.empty_like(v)
     _check_dev("out", out, v.dtype)
+    dt = _dtype_code(q)
+    ws, nws = _workspace(lib.linear_attn_workspace_bytes(B, H, T, dk, dv, dt), q.device, workspace)
     rc = lib.linear_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), RET_PHI_ELU1, out.data_ptr(),
-                             B, H, T, dk, dv, _dtype_code(q), float(eps), _stream(q))
+                             B, H, T, dk, dv, dt, float(eps), ws.data_ptr() if ws is not None else None, nws,
+                             _stream(q))
     _raise(rc)
     return out

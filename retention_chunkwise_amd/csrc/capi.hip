@@ -1,10 +1,8 @@
 // capi.hip -- the extern "C" entry points of libretention (include/retention.h).
 //
 // Every argument is validated on the host before anything is enqueued, so a
-// rejected call has no side effect.  The only device memory the library
-// allocates is the segment-state workspace of the segment-split forward,
-// taken stream-ordered from a library-owned pool and released on the same
-// stream when the call's kernels finish.
+// rejected call has no side effect.  The library allocates no device memory:
+// the segment-split forward paths take their workspace from the caller.
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
@@ -12,7 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <mutex>
+#include <initializer_list>
 
 #include "../../include/retention.h"
 #include "internal.h"
@@ -95,93 +93,77 @@ FwdPath choose_fwd_path(int dtype) {
     return seg_ok ? FwdPath::kSegment : FwdPath::kSlice;
 }
 
-// ---- workspace: one stream-ordered memory pool per device, created on first
-// use and kept until the process ends.  Freed blocks stay in the pool
-// (release threshold: unlimited) so repeated calls do not reach the driver.
-constexpr int kMaxDevices = 64;
-std::mutex g_pool_mu;
-hipMemPool_t g_pools[kMaxDevices] = {};
+// Segment plan of the bf16 forward paths: segment count G, chunks per
+// segment, state-kernel workgroups per segment, and the workspace they need
+// ((G - 1) * pieces partial states per (b, h); none when G == 1).
+struct SegPlan {
+    int G = 1, cps = 1, pieces = 1;
+    size_t ws_bytes = 0;
+};
 
-hipError_t device_pool(hipMemPool_t* out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(g_pool_mu);
-    if (!g_pools[dev]) {
-        hipMemPoolProps props;
-        memset(&props, 0, sizeof(props));
-        props.allocType = hipMemAllocationTypePinned;
-        props.handleTypes = hipMemHandleTypeNone;
-        props.location.type = hipMemLocationTypeDevice;
-        props.location.id = dev;
-        hipMemPool_t pool = nullptr;
-        e = hipMemPoolCreate(&pool, &props);
-        if (e != hipSuccess) return e;
-        uint64_t keep = UINT64_MAX;
-        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-        if (e != hipSuccess) {
-            (void)hipMemPoolDestroy(pool);
-            return e;
-        }
-        g_pools[dev] = pool;
-    }
-    *out = g_pools[dev];
-    return hipSuccess;
-}
-
-// Segment-split forward (bf16): segment count, workspace from the pool, the
-// two kernels, workspace released on the same stream.
-hipError_t launch_segment_path(const void* q, const void* k, const void* v, void* out, float* final_state,
-                               const float* log2g, float eps, int B, int H, int T, int chunk, int dk, int dv,
-                               bool linattn, hipStream_t st) {
-    const long long bh = static_cast<long long>(B) * H;
-    ret::SegArgs sa{};
+bool plan_segments(long long bh, int T, int chunk, int dk, int dv, bool linattn, SegPlan* p) {
     const int nch = (T + chunk - 1) / chunk;
-    int cps = 1;
     const int forced = env_int("RET_FWD_SEGMENTS");
     if (forced > 0) {
         const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
-        cps = (nch > 0) ? (nch + g - 1) / g : 1;
-        sa.G = (nch > 0) ? (nch + cps - 1) / cps : 1;
+        p->cps = (nch > 0) ? (nch + g - 1) / g : 1;
+        p->G = (nch > 0) ? (nch + p->cps - 1) / p->cps : 1;
     } else {
-        sa.G = ret::choose_segments(bh, nch, 256, 4, 16, &cps);
+        p->G = ret::choose_segments(bh, nch, 256, 4, 16, &p->cps);
     }
-    sa.cps = cps;
-    // state-kernel workgroups per segment: enough to occupy the chip, dividing
-    // the segment's 64-token blocks evenly, at most 16 workspace slots per
-    // (b, h) (the walk sums up to that many states on entry)
-    const int sblocks = cps * (chunk / 64);
-    const long long sgroups = bh * (sa.G - 1);
+    // state-kernel workgroups per segment: enough to occupy the chip in one
+    // round, dividing the segment's 64-token blocks evenly, at most 16 partial
+    // states per (b, h) (the walk sums up to that many states on entry)
+    const int sblocks = p->cps * (chunk / 64);
+    const long long sgroups = bh * (p->G - 1);
     int pieces = (sgroups > 0 && sgroups < 256) ? static_cast<int>(256 / sgroups) : 1;
-    if (sa.G > 1 && pieces > 16 / (sa.G - 1)) pieces = 16 / (sa.G - 1);
+    if (p->G > 1 && pieces > 16 / (p->G - 1)) pieces = 16 / (p->G - 1);
     if (pieces > sblocks) pieces = sblocks;
     if (pieces < 1) pieces = 1;
     while (pieces > 1 && sblocks % pieces != 0) --pieces;
-    sa.pieces = pieces;
+    p->pieces = pieces;
+    p->ws_bytes = 0;
+    if (p->G > 1) {
+        size_t n = 4;
+        const long long slot = static_cast<long long>(dk) * dv + (linattn ? dk : 0);
+        if (!mul_ok(n, bh) || !mul_ok(n, p->G - 1) || !mul_ok(n, p->pieces) || !mul_ok(n, slot)) return false;
+        p->ws_bytes = n;
+    }
+    return true;
+}
+
+// Checks the caller's workspace against a plan (before anything is enqueued).
+int check_workspace(const char* fn, const SegPlan& p, const void* workspace, size_t ws_bytes,
+                    std::initializer_list<Range> others) {
+    if (p.ws_bytes == 0) return RET_OK;
+    if (!workspace || ws_bytes < p.ws_bytes)
+        return fail(RET_ERR_WORKSPACE, "%s: needs a workspace of %zu bytes (got %zu%s)", fn, p.ws_bytes, ws_bytes,
+                    workspace ? "" : ", NULL");
+    if (!aligned16(workspace)) return fail(RET_ERR_ALIGN, "%s: workspace must be 16-byte aligned", fn);
+    const Range rw = range("workspace", workspace, p.ws_bytes);
+    for (const Range& o : others)
+        if (overlap(rw, o)) return fail(RET_ERR_ALIAS, "%s: workspace overlaps %s", fn, o.name);
+    return RET_OK;
+}
+
+// Launches the segment-split forward (bf16) with a checked plan and workspace.
+hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
+                               float* final_state, void* workspace, const float* log2g, float eps, int B, int H,
+                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st) {
+    ret::SegArgs sa{};
+    sa.G = plan.G;
+    sa.cps = plan.cps;
+    sa.pieces = plan.pieces;
     sa.q = q; sa.k = k; sa.v = v; sa.out = out; sa.final_state = final_state;
+    sa.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
     sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
     if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
-    size_t ws_bytes = 4;
-    const long long slot = static_cast<long long>(dk) * dv + (linattn ? dk : 0);
-    if (sa.G > 1 && (!mul_ok(ws_bytes, bh) || !mul_ok(ws_bytes, sa.G - 1) || !mul_ok(ws_bytes, sa.pieces) ||
-                     !mul_ok(ws_bytes, slot)))
-        return hipErrorInvalidValue;
-    void* ws = nullptr;
-    if (sa.G > 1) {
-        hipMemPool_t pool = nullptr;
-        hipError_t e = device_pool(&pool);
-        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, ws_bytes, pool, st);
-        if (e != hipSuccess) return e;
-    }
-    sa.ws = static_cast<float*>(ws);
-    const hipError_t e = ret::launch_seg(sa, chunk, dk, dv, linattn, st);
-    if (ws) {
-        const hipError_t ef = hipFreeAsync(ws, st);
-        if (e == hipSuccess && ef != hipSuccess) return ef;
-    }
-    return e;
+    return ret::launch_seg(sa, chunk, dk, dv, linattn, st);
 }
+
+// Internal chunk of the bf16 linear-attention path: 64 when dk = 128 (the
+// 128-token variant would spill registers), else 128.
+int linattn_chunk(int dk) { return dk == 128 ? 64 : 128; }
 
 }  // namespace
 
@@ -189,11 +171,30 @@ extern "C" {
 
 const char* retention_last_error(void) { return g_err; }
 
+size_t retention_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+    if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
+        (dv != 64 && dv != 128) || !dtype_size(dtype))
+        return 0;
+    if (choose_fwd_path(dtype) != FwdPath::kSegment) return 0;
+    SegPlan plan;
+    if (!plan_segments(static_cast<long long>(B) * H, T, chunk, dk, dv, false, &plan)) return 0;
+    return plan.ws_bytes;
+}
+
+size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+    if (B <= 0 || H < 1 || T < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || !dtype_size(dtype))
+        return 0;
+    if (choose_fwd_path(dtype) != FwdPath::kSegment) return 0;
+    SegPlan plan;
+    if (!plan_segments(static_cast<long long>(B) * H, T, linattn_chunk(dk), dk, dv, true, &plan)) return 0;
+    return plan.ws_bytes;
+}
+
 int retention_abi_version(void) { return RET_ABI_VERSION; }
 
 int retention_fwd(const void* q, const void* k, const void* v, const float* gamma, int chunk,
                   void* out, float* final_state, int B, int H, int T, int dk, int dv, int dtype,
-                  void* stream) {
+                  void* workspace, size_t ws_bytes, void* stream) {
     if (!gamma) return fail(RET_ERR_NULL, "retention_fwd: gamma must be non-NULL");
     const int esz = dtype_size(dtype);
     if (!esz) return fail(RET_ERR_DTYPE, "retention_fwd: unknown dtype %d", dtype);
@@ -230,9 +231,16 @@ int retention_fwd(const void* q, const void* k, const void* v, const float* gamm
     const long long bh = static_cast<long long>(B) * H;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (choose_fwd_path(dtype) == FwdPath::kSegment) {
-        const hipError_t e = launch_segment_path(q, k, v, out, final_state, a.log2g, 0.f, B, H, T, chunk, dk, dv,
-                                                 false, st);
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "retention_fwd: %s", hipGetErrorString(e));
+        SegPlan plan;
+        if (!plan_segments(bh, T, chunk, dk, dv, false, &plan))
+            return fail(RET_ERR_SHAPE, "retention_fwd: workspace size overflows");
+        const Range none{"", 0, 0};
+        rc = check_workspace("retention_fwd", plan, workspace, ws_bytes,
+                             {rq, rk, rv, ro, final_state ? range("final_state", final_state, ns) : none});
+        if (rc) return rc;
+        const hipError_t e = launch_segment_path(plan, q, k, v, out, final_state, workspace, a.log2g, 0.f, B, H, T,
+                                                 chunk, dk, dv, false, st);
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
         return ok();
     }
     const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, chunk, dk);
@@ -284,7 +292,8 @@ int retention_decode_step(const void* q, const void* k, const void* v, const flo
 }
 
 int linear_attn_fwd(const void* q, const void* k, const void* v, int phi, void* out, int B, int H,
-                    int T, int dk, int dv, int dtype, float eps, void* stream) {
+                    int T, int dk, int dv, int dtype, float eps, void* workspace, size_t ws_bytes,
+                    void* stream) {
     const int esz = dtype_size(dtype);
     if (!esz) return fail(RET_ERR_DTYPE, "linear_attn_fwd: unknown dtype %d", dtype);
     if (phi != RET_PHI_ELU1) return fail(RET_ERR_PHI, "linear_attn_fwd: unknown feature map %d", phi);
@@ -308,10 +317,15 @@ int linear_attn_fwd(const void* q, const void* k, const void* v, int phi, void* 
         if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "linear_attn_fwd: out overlaps %s", in.name);
     if (B == 0) return ok();
     if (choose_fwd_path(dtype) == FwdPath::kSegment) {
-        // 64-token chunks when dk = 128 (the 128-token variant would spill registers)
-        const hipError_t e = launch_segment_path(q, k, v, out, nullptr, nullptr, eps, B, H, T, dk == 128 ? 64 : 128,
-                                                 dk, dv, true, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "linear_attn_fwd: %s", hipGetErrorString(e));
+        const long long bhs = static_cast<long long>(B) * H;
+        SegPlan plan;
+        if (!plan_segments(bhs, T, linattn_chunk(dk), dk, dv, true, &plan))
+            return fail(RET_ERR_SHAPE, "linear_attn_fwd: workspace size overflows");
+        const int rcw = check_workspace("linear_attn_fwd", plan, workspace, ws_bytes, {rq, rk, rv, ro});
+        if (rcw) return rcw;
+        const hipError_t e = launch_segment_path(plan, q, k, v, out, nullptr, workspace, nullptr, eps, B, H, T,
+                                                 linattn_chunk(dk), dk, dv, true, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "linear_attn_fwd: launch failed: %s", hipGetErrorString(e));
         return ok();
     }
     ret::WalkArgs a{};

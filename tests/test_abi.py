@@ -63,10 +63,10 @@ def _gam(vals):
 
 def _fwd(lib, **kw):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9, 0.9]), chunk=64, out=FAKE * 4,
-             fs=None, B=1, H=2, T=16, dk=64, dv=64, dtype=rc.RET_F32)
+             fs=None, B=1, H=2, T=16, dk=64, dv=64, dtype=rc.RET_F32, ws=None, nws=0)
     a.update(kw)
     return lib.retention_fwd(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["out"], a["fs"],
-                             a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], None)
+                             a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["ws"], a["nws"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -129,10 +129,10 @@ def test_decode_rejects(kw, code):
 
 def _lin(lib, **kw):
     a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, phi=rc.RET_PHI_ELU1, out=FAKE * 4, B=1, H=1, T=8,
-             dk=64, dv=64, dtype=rc.RET_BF16, eps=1e-6)
+             dk=64, dv=64, dtype=rc.RET_BF16, eps=1e-6, ws=None, nws=0)
     a.update(kw)
     return lib.linear_attn_fwd(a["q"], a["k"], a["v"], a["phi"], a["out"], a["B"], a["H"], a["T"],
-                               a["dk"], a["dv"], a["dtype"], a["eps"], None)
+                               a["dk"], a["dv"], a["dtype"], a["eps"], a["ws"], a["nws"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -156,3 +156,34 @@ def test_binding_fails_loudly_without_gpu_tensors():
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         rc.retention_fwd(q, q, q, [0.9])
+
+
+# ---------------------------------------------------------------- workspace
+def test_workspace_sizes():
+    lib = _lib()
+    # fp32 walks whole sequences: no workspace
+    assert lib.retention_fwd_workspace_bytes(1, 2, 4096, 64, 64, 64, rc.RET_F32) == 0
+    # one chunk: one segment, no workspace
+    assert lib.retention_fwd_workspace_bytes(1, 2, 100, 128, 128, 128, rc.RET_BF16) == 0
+    # long bf16 sequences are split: (G - 1) * pieces fp32 states per (b, h)
+    n = lib.retention_fwd_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    assert n > 0 and n % (128 * 128 * 4 * 32) == 0
+    m = lib.linear_attn_workspace_bytes(8, 16, 8192, 64, 64, rc.RET_BF16)
+    assert m > 0 and m % ((64 * 64 + 64) * 4 * 128) == 0
+    # invalid arguments report 0 (the call itself reports the error)
+    assert lib.retention_fwd_workspace_bytes(1, 2, 4096, 96, 64, 64, rc.RET_BF16) == 0
+
+
+def test_workspace_is_required_and_checked():
+    lib = _lib()
+    kw = dict(dtype=rc.RET_BF16, T=65536, dk=128, dv=128, chunk=128, gamma=_gam([0.9, 0.9]),
+              q=FAKE, k=FAKE * 1024, v=FAKE * 2048, out=FAKE * 4096)
+    need = lib.retention_fwd_workspace_bytes(1, 2, 65536, 128, 128, 128, rc.RET_BF16)
+    assert need > 0
+    assert _fwd(lib, **kw) == -9                                   # none given
+    assert _fwd(lib, ws=FAKE * 8192, nws=need - 16, **kw) == -9    # too small
+    assert _fwd(lib, ws=FAKE * 8192 + 8, nws=need, **kw) == -7     # misaligned
+    assert _fwd(lib, ws=FAKE * 1024, nws=need, **kw) == -8         # overlaps k
+    lneed = lib.linear_attn_workspace_bytes(1, 1, 65536, 64, 64, rc.RET_BF16)
+    assert lneed > 0
+    assert _lin(lib, T=65536, q=FAKE, k=FAKE * 1024, v=FAKE * 2048, out=FAKE * 4096) == -9

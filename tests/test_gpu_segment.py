@@ -149,3 +149,34 @@ def test_segment_linattn_matches_slice_path(monkeypatch):
     e = oracle.rel_frobenius(o_seg, o_sl)
     print(f"[parity] linattn segment vs slice {e:.3e}", flush=True)
     assert e <= TOL
+
+
+# ------------------------------------------------------------- caller workspace
+def test_caller_workspace_contents_do_not_matter(monkeypatch):
+    """A caller-owned workspace filled with garbage gives the same bits as a
+    fresh one; a workspace one byte short is refused."""
+    monkeypatch.delenv("RET_FWD_PATH", raising=False)
+    monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
+    w, inp = _inputs(seed=17, B=1, H=4, T=4000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    need = rc.retention_fwd_workspace_bytes(1, 4, 4000, 128, 128, 128, torch.bfloat16)
+    print(f"[segment] caller workspace {need} bytes", flush=True)
+    assert need > 0
+    o1, s1 = rc.retention_fwd(q, k, v, inp["gamma"], chunk=128)
+    ws = torch.full((need + 4096,), 0x7F, dtype=torch.uint8, device="cuda")
+    o2, s2 = rc.retention_fwd(q, k, v, inp["gamma"], chunk=128, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    with pytest.raises(RuntimeError, match="RET_ERR_WORKSPACE"):
+        rc.retention_fwd(q, k, v, inp["gamma"], chunk=128, workspace=ws[: need - 1])
+
+    wa = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=1, H=4, T=4000)
+    li = wl.make_inputs(wa, 24)
+    lq, lk, lv = (li[n].cuda() for n in ("q", "k", "v"))
+    lneed = rc.linear_attn_workspace_bytes(1, 4, 4000, wa.dk, wa.dv, torch.bfloat16)
+    assert lneed > 0
+    l1 = rc.linear_attn_fwd(lq, lk, lv)
+    lws = torch.full((lneed,), 0xFF, dtype=torch.uint8, device="cuda")
+    l2 = rc.linear_attn_fwd(lq, lk, lv, workspace=lws)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2)
