@@ -94,7 +94,9 @@ def _bind(lib):
     lib.oracle_decode_steps.argtypes = [_D, _D, _D, _D, _D, _D, _l, _l, _l, _l, _l,
                                         ctypes.c_int]
     lib.oracle_linattn_recurrent.argtypes = [_D, _D, _D, ctypes.c_double, _l, _l, _l,
-                                             _l, _l, _D, _D, _D, ctypes.c_int]
+                                             _l, _l, _D, _D, _D, _D, _D, ctypes.c_int]
+    lib.oracle_linattn_decode_steps.argtypes = [_D, _D, _D, ctypes.c_double, _D, _D, _D,
+                                                _l, _l, _l, _l, _l, ctypes.c_int]
     lib.oracle_linattn_parallel.argtypes = [_D, _D, _D, ctypes.c_double, _l, _l, _l,
                                             _l, _l, _D]
     lib.oracle_linattn_rows.argtypes = [_D, _D, _D, ctypes.c_double, _l, _l, _l, _l, _l,
@@ -103,6 +105,7 @@ def _bind(lib):
     for name in ("oracle_retention_recurrent", "oracle_retention_parallel",
                  "oracle_retention_rows", "oracle_retention_chunkwise",
                  "oracle_decode_steps", "oracle_linattn_recurrent",
+                 "oracle_linattn_decode_steps",
                  "oracle_linattn_parallel", "oracle_linattn_rows",
                  "oracle_threads_used"):
         getattr(lib, name).restype = ctypes.c_int
@@ -218,8 +221,11 @@ def decode_steps(q, k, v, gamma, state, nsteps: int = 1, nthreads: int = 1):
     return out, S
 
 
-def linattn_recurrent(q, k, v, eps: float = ELU1_EPS, nthreads: int = 1):
-    """Causal linear attention, phi = elu+1 with normaliser, recurrent form.
+def linattn_recurrent(q, k, v, eps: float = ELU1_EPS, init_S=None, init_z=None,
+                      nthreads: int = 1):
+    """Causal linear attention, phi = elu+1 with normaliser, recurrent form
+    ("Linear attention" page, recurrent-form box), from (init_S, init_z)
+    (zero when None).
 
     Returns (out [B,H,T,dv], S [B,H,dk,dv], z [B,H,dk]).
     """
@@ -228,9 +234,48 @@ def linattn_recurrent(q, k, v, eps: float = ELU1_EPS, nthreads: int = 1):
     out = np.zeros((B, H, T, dv))
     S = np.zeros((B, H, dk, dv))
     z = np.zeros((B, H, dk))
+    iS = iz = None
+    if init_S is not None:
+        iS = _f64(init_S)
+        if iS.shape != (B, H, dk, dv):
+            raise ValueError("init_S must be [B,H,dk,dv]")
+    if init_z is not None:
+        iz = _f64(init_z)
+        if iz.shape != (B, H, dk):
+            raise ValueError("init_z must be [B,H,dk]")
     _check(load().oracle_linattn_recurrent(_p(q), _p(k), _p(v), float(eps), B, H, T, dk,
-                                           dv, _p(out), _p(S), _p(z), int(nthreads)),
+                                           dv, _p(iS) if iS is not None else None,
+                                           _p(iz) if iz is not None else None,
+                                           _p(out), _p(S), _p(z), int(nthreads)),
            "oracle_linattn_recurrent")
+    return out, S, z
+
+
+def linattn_decode_steps(q, k, v, S, z, eps: float = ELU1_EPS, nsteps: int = 1,
+                         nthreads: int = 1):
+    """nsteps decode steps of causal linear attention with the same token
+    ("Linear attention" page, the decode-step exercise).
+
+    q, k: [N,H,dk]; v: [N,H,dv]; S: [N,H,dk,dv]; z: [N,H,dk].  Returns
+    (out [N,H,dv] of the last step, S_new, z_new); the inputs are not
+    modified.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    S = _f64(S).copy()
+    z = _f64(z).copy()
+    if q.ndim != 3:
+        raise ValueError("q must be [N,H,dk]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if k.shape != q.shape or v.shape[:2] != (N, H):
+        raise ValueError("shape mismatch between q, k, v")
+    if S.shape != (N, H, dk, dv) or z.shape != (N, H, dk):
+        raise ValueError("S must be [N,H,dk,dv] and z [N,H,dk]")
+    out = np.zeros((N, H, dv))
+    _check(load().oracle_linattn_decode_steps(_p(q), _p(k), _p(v), float(eps), _p(S), _p(z),
+                                              _p(out), N, H, dk, dv, int(nsteps),
+                                              int(nthreads)),
+           "oracle_linattn_decode_steps")
     return out, S, z
 
 

@@ -310,10 +310,15 @@ static double phi_elu1(double x)
  *        with a small eps added to the denominator (the interview task adds
  *        it "as written"; each token is included in its own sum).
  *   [ESF] Code 12.5.1 and [LRR] Code 13.3.2 run the same loop.
- * final_S [B][H][dk][dv] and final_z [B][H][dk] may be NULL.
+ * The loop starts from (S, z) = (init_S, init_z), the state and normaliser
+ * after earlier tokens ([LA] "Interview: causal linear attention, recurrent
+ * and parallel, plus the decode step" hands exactly that pair from one call
+ * to the next); NULL means zero.  final_S [B][H][dk][dv] and final_z
+ * [B][H][dk] may be NULL.
  */
 int oracle_linattn_recurrent(const double *q, const double *k, const double *v,
                              double eps, long B, long H, long T, long dk, long dv,
+                             const double *init_S, const double *init_z,
                              double *out, double *final_S, double *final_z,
                              int nthreads)
 {
@@ -331,6 +336,10 @@ int oracle_linattn_recurrent(const double *q, const double *k, const double *v,
             free(S); free(z); free(pq); free(pk);
             continue;
         }
+        if (init_S)
+            memcpy(S, init_S + bh * dk * dv, (size_t)(dk * dv) * sizeof(double));
+        if (init_z)
+            memcpy(z, init_z + bh * dk, (size_t)dk * sizeof(double));
         for (long t = 0; t < T; ++t) {
             const double *qt = q + (bh * T + t) * dk;
             const double *kt = k + (bh * T + t) * dk;
@@ -361,6 +370,64 @@ int oracle_linattn_recurrent(const double *q, const double *k, const double *v,
         if (final_z)
             memcpy(final_z + bh * dk, z, (size_t)dk * sizeof(double));
         free(S); free(z); free(pq); free(pk);
+    }
+    return err;
+}
+
+/*
+ * One decode step of causal linear attention for N sequences x H heads, in
+ * place on (S, z).
+ *   [LA] "Interview: causal linear attention, recurrent and parallel, plus
+ *        the decode step": the step takes the state S (d_phi x d_v) and the
+ *        normaliser z (d_phi) after t-1 tokens and one token's q, k, v; it
+ *        adds phi(k) v^T to S and phi(k) to z, then reads
+ *        o = S^T phi(q) / (z^T phi(q) + eps) from the updated pair.
+ * q, k: [N][H][dk], v, out: [N][H][dv], S: [N][H][dk][dv], z: [N][H][dk].
+ * The step is applied nsteps times with the same token; out holds the last
+ * read-out.  (The page's function returns new arrays; the Python wrapper
+ * copies S and z first, so its inputs are left unchanged.)
+ */
+int oracle_linattn_decode_steps(const double *q, const double *k, const double *v,
+                                double eps, double *S, double *z, double *out,
+                                long N, long H, long dk, long dv, long nsteps,
+                                int nthreads)
+{
+    if (!q || !k || !v || !S || !z || !out || N < 0 || H <= 0 || dk <= 0 ||
+        dv <= 0 || nsteps < 1)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for num_threads(oracle_threads(nthreads)) schedule(dynamic, 1)
+    for (long nh = 0; nh < N * H; ++nh) {
+        const double *qn = q + nh * dk, *kn = k + nh * dk, *vn = v + nh * dv;
+        double *Sn = S + nh * dk * dv, *zn = z + nh * dk, *o = out + nh * dv;
+        double *fq = (double *)malloc((size_t)dk * sizeof(double));
+        double *fk = (double *)malloc((size_t)dk * sizeof(double));
+        if (!fq || !fk) {
+            err = ORACLE_ERR_NOMEM;
+            free(fq); free(fk);
+            continue;
+        }
+        for (long i = 0; i < dk; ++i) {
+            fq[i] = phi_elu1(qn[i]);
+            fk[i] = phi_elu1(kn[i]);
+        }
+        for (long s = 0; s < nsteps; ++s) {
+            for (long i = 0; i < dk; ++i) {
+                for (long j = 0; j < dv; ++j)
+                    Sn[i * dv + j] += fk[i] * vn[j];
+                zn[i] += fk[i];
+            }
+            double den = eps;
+            for (long i = 0; i < dk; ++i)
+                den += zn[i] * fq[i];
+            for (long j = 0; j < dv; ++j) {
+                double num = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    num += Sn[i * dv + j] * fq[i];
+                o[j] = num / den;
+            }
+        }
+        free(fq); free(fk);
     }
     return err;
 }

@@ -356,6 +356,123 @@ def pin_prefill_decode_handoff():
     _close(Stail, Sfull, 1e-12, "final state from initial state")
 
 
+# ---------------------------------------------------------------- NEXT-1: initial state, phi decode
+def pin_linattn_decode_hand_example():
+    """The three-token elu+1 example, one decode step per token.
+
+    "Linear attention", the decode-step exercise: from S = 0, z = 0 each step
+    adds phi(k) v^T and phi(k), then reads o = S^T phi(q) / (z^T phi(q) + eps).
+    Stepping the printed tokens must reproduce the printed S_t, z_t and o_t
+    (eps = 0), and with eps = 1 the printed numerators over (denominator + 1).
+    The wrapper must leave its input arrays unchanged.
+    """
+    g = _golden("linattn_hand_example.json")
+    q = np.array(g["q"], float)
+    k = np.array(g["k"], float)
+    v = np.array(g["v"], float)
+    num = np.array(g["numerator"], float)
+    den = np.array(g["denominator"], float)
+    for eps in (0.0, 1.0):
+        S = np.zeros((1, 1, 2, 2))
+        z = np.zeros((1, 1, 2))
+        for t in range(3):
+            o, S, z = oracle.linattn_decode_steps(q[t][None, None], k[t][None, None],
+                                                  v[t][None, None], S, z, eps=eps)
+            _close(S[0, 0], g["S"][t], 1e-15, f"decode S_{t + 1}")
+            _close(z[0, 0], g["z"][t], 1e-15, f"decode z_{t + 1}")
+            expect = g["o"][t] if eps == 0.0 else num[t] / (den[t] + 1.0)
+            _close(o[0, 0], expect, 1e-15, f"decode o_{t + 1} (eps={eps})")
+    # the wrapper copies: the caller's arrays keep their values
+    S0 = np.ones((1, 1, 2, 2))
+    z0 = np.ones((1, 1, 2))
+    oracle.linattn_decode_steps(q[0][None, None], k[0][None, None], v[0][None, None], S0, z0)
+    assert np.all(S0 == 1.0) and np.all(z0 == 1.0), "decode modified its inputs"
+
+
+def pin_linattn_decode_repeated_token():
+    """n steps with the same token: S_n = S_0 + n phi(k) v^T, z_n = z_0 + n phi(k).
+
+    The read-out after n steps is then S_n^T phi(q) / (z_n^T phi(q) + eps).
+    With q = k = 0 every feature is phi(0) = 1 (hand example: phi(0) = 1), so
+    the closed form needs no feature map: z_n = z_0 + n, o = (1^T S_n) /
+    (1^T z_n + eps).
+    """
+    rng = np.random.default_rng(5)
+    N, H, dk, dv = 2, 3, 4, 5
+    v = rng.standard_normal((N, H, dv))
+    S0 = rng.standard_normal((N, H, dk, dv)) * 0.3
+    z0 = rng.uniform(0.5, 2.0, (N, H, dk))
+    zero = np.zeros((N, H, dk))
+    for n in (1, 3, 40):
+        o, S, z = oracle.linattn_decode_steps(zero, zero, v, S0, z0, eps=1e-3, nsteps=n)
+        S_exp = S0 + n * v[:, :, None, :]
+        z_exp = z0 + n
+        _close(S, S_exp, 1e-13, f"phi decode state after {n} steps")
+        _close(z, z_exp, 1e-13, f"phi decode normaliser after {n} steps")
+        o_exp = S_exp.sum(axis=2) / (z_exp.sum(axis=2) + 1e-3)[..., None]
+        _close(o, o_exp, 1e-13, f"phi decode read-out after {n} steps")
+
+
+def pin_linattn_prefill_decode_handoff():
+    """Linear attention from an initial (S, z) = the tail of one longer run.
+
+    fwd(T) then n decode steps reproduces the last n rows of fwd(T + n);
+    fwd of the tail from fwd(T)'s (S, z) reproduces the same rows and the same
+    final pair.  On the hand example, token 1 as prefill and tokens 2, 3 from
+    its (S_1, z_1) give the printed o_2, o_3 ("Linear attention", hand example
+    and the decode-step exercise).
+    """
+    rng = np.random.default_rng(18)
+    B, H, T, n, dk, dv = 2, 2, 25, 4, 5, 3
+    q, k, v = (_rand(rng, (B, H, T + n, dk)), _rand(rng, (B, H, T + n, dk)),
+               _rand(rng, (B, H, T + n, dv)))
+    full, Sf, zf = oracle.linattn_recurrent(q, k, v)
+    _, S, z = oracle.linattn_recurrent(q[:, :, :T], k[:, :, :T], v[:, :, :T])
+    tail, St, zt = oracle.linattn_recurrent(q[:, :, T:], k[:, :, T:], v[:, :, T:],
+                                            init_S=S, init_z=z)
+    _close(tail, full[:, :, T:], 1e-12, "linattn fwd from initial (S, z)")
+    _close(St, Sf, 1e-12, "linattn final S from initial state")
+    _close(zt, zf, 1e-12, "linattn final z from initial state")
+    for s in range(n):
+        o, S, z = oracle.linattn_decode_steps(q[:, :, T + s], k[:, :, T + s], v[:, :, T + s], S, z)
+        _close(o, full[:, :, T + s], 1e-12, f"linattn decode step {s}")
+    _close(S, Sf, 1e-12, "linattn S after handoff")
+    _close(z, zf, 1e-12, "linattn z after handoff")
+    g = _golden("linattn_hand_example.json")
+    hq = np.array(g["q"], float)[None, None]
+    hk = np.array(g["k"], float)[None, None]
+    hv = np.array(g["v"], float)[None, None]
+    S1 = np.array(g["S"][0], float)[None, None]
+    z1 = np.array(g["z"][0], float)[None, None]
+    o23, S3, z3 = oracle.linattn_recurrent(hq[:, :, 1:], hk[:, :, 1:], hv[:, :, 1:], eps=0.0,
+                                           init_S=S1, init_z=z1)
+    _close(o23[0, 0], g["o"][1:], 1e-15, "hand example o_2, o_3 from (S_1, z_1)")
+    _close(S3[0, 0], g["S"][2], 1e-15, "hand example S_3 from (S_1, z_1)")
+    _close(z3[0, 0], g["z"][2], 1e-15, "hand example z_3 from (S_1, z_1)")
+
+
+def pin_retention_initial_state_decays():
+    """With zero keys only the initial state speaks: o_t = g^(t+1) q_t S_0.
+
+    The recurrence S_t = g S_(t-1) + k_t v_t^T ("RetNet", "Recurrent
+    Representation") with k = 0 leaves S_t = g^(t+1) S_0 after token t
+    (0-based), so the read-out is the initial state decayed t + 1 times and
+    the final state is g^T S_0.
+    """
+    rng = np.random.default_rng(19)
+    B, H, T, dk, dv = 1, 3, 70, 4, 6
+    gam = np.array([0.5, 0.93, 1.0])
+    q = _rand(rng, (B, H, T, dk))
+    k = np.zeros((B, H, T, dk))
+    v = _rand(rng, (B, H, T, dv))
+    S0 = _rand(rng, (B, H, dk, dv))
+    out, fs = oracle.retention_recurrent(q, k, v, gam, init_state=S0)
+    for h in range(H):
+        pw = gam[h] ** np.arange(1, T + 1)
+        _close(out[0, h], pw[:, None] * (q[0, h] @ S0[0, h]), 1e-13, f"init-state read-out h={h}")
+        _close(fs[0, h], gam[h] ** T * S0[0, h], 1e-13, f"init-state final h={h}")
+
+
 # ---------------------------------------------------------------- P-10
 def pin_metric_calculator():
     """The pages' analytic counts.
@@ -401,5 +518,9 @@ ALL_PINS = [
     pin_chunk_invariance,
     pin_single_key_and_constant_values,
     pin_prefill_decode_handoff,
+    pin_linattn_decode_hand_example,
+    pin_linattn_decode_repeated_token,
+    pin_linattn_prefill_decode_handoff,
+    pin_retention_initial_state_decays,
     pin_metric_calculator,
 ]

@@ -79,6 +79,27 @@ MUTANTS = [
     ("linattn_parallel_drops_eps",
      "ot[j] /= (rowsum + eps);",
      "ot[j] /= rowsum;"),
+    ("linattn_ignores_initial_state",
+     "        if (init_S)\n",
+     "        if (0 && init_S)\n"),
+    ("linattn_ignores_initial_normaliser",
+     "        if (init_z)\n",
+     "        if (0 && init_z)\n"),
+    ("linattn_decode_reads_before_write",
+     "num += Sn[i * dv + j] * fq[i];",
+     "num += (Sn[i * dv + j] - fk[i] * vn[j]) * fq[i];"),
+    ("linattn_decode_z_not_accumulated",
+     "zn[i] += fk[i];",
+     "zn[i] = fk[i];"),
+    ("linattn_decode_drops_eps",
+     "double den = eps;",
+     "double den = 0.0;"),
+    ("linattn_decode_raw_query",
+     "fq[i] = phi_elu1(qn[i]);",
+     "fq[i] = qn[i];"),
+    ("linattn_decode_transposed_outer_product",
+     "Sn[i * dv + j] += fk[i] * vn[j];",
+     "Sn[i * dv + j] += fk[j % dk] * vn[i % dv];"),
     ("linattn_rows_doubles_eps",
      "o[j] /= (rowsum + eps);",
      "o[j] /= (rowsum + 2.0 * eps);"),
