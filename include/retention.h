@@ -34,7 +34,7 @@
  *    a failed call has no effect.  RET_ERR_HIP reports a failed launch.  A
  *    human-readable message for the last error of the calling thread is
  *    returned by retention_last_error().  Inputs are never modified (except
- *    state in retention_decode_step, which is updated in place).
+ *    the state of the two decode steps, which is updated in place).
  *  - Tuning and testing knobs, read from the environment at every call:
  *    RET_FWD_PATH = "slice" | "segment" forces the forward path (segment
  *    needs bf16; anything else means automatic), RET_FWD_SEGMENTS = n forces
@@ -48,7 +48,10 @@
  *   "Efficient and Sparse Transformers" (temporalbook 12.5), section 6: the
  *       parallel, recurrent and chunkwise forms; gamma = 1 as linear attention.
  *   "Linear attention" (zerotofrontier 21.2): box "Causal linear attention,
- *       recurrent form" (S, z, eps) and the decode-step interface.
+ *       recurrent form" (S, z, eps); the coding exercise "Causal linear
+ *       attention, recurrent and parallel, plus the decode step" (one decode
+ *       step on (S, z)); section "Decoding, training, and what each costs"
+ *       (prefill, then decode from the prefill's state).
  */
 #ifndef RETENTION_H
 #define RETENTION_H
@@ -59,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 2
+#define RET_ABI_VERSION 3
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -79,7 +82,7 @@ extern "C" {
 #define RET_ERR_ALIGN (-7)     /* a device pointer is not 16-byte aligned */
 #define RET_ERR_ALIAS (-8)     /* an output overlaps an input or another output */
 #define RET_ERR_WORKSPACE (-9) /* workspace NULL or smaller than the call needs */
-#define RET_ERR_HIP (-10)      /* a launch or the workspace allocation failed */
+#define RET_ERR_HIP (-10)      /* a kernel launch failed */
 
 /*
  * retention_fwd -- causal retention over whole sequences, chunkwise form,
@@ -113,9 +116,32 @@ int retention_fwd(const void *q, const void *k, const void *v, const float *gamm
                   void *stream);
 
 /* Workspace bytes retention_fwd needs for these arguments (0: none, or the
- * arguments are invalid and the call will say why).  Host only. */
+ * arguments are invalid and the call will say why).  Host only.  The same
+ * size serves retention_fwd_from_state. */
 size_t retention_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                      int dtype);
+
+/*
+ * retention_fwd_from_state -- retention_fwd continued from a given state S0
+ * (the state after earlier tokens, e.g. a previous call's final_state):
+ *
+ *   out[b,h,t,:] = gamma^(t+1) q_t S0 + sum_{s<=t} gamma^(t-s) (q_t . k_s) v_s
+ *   final_state  = gamma^T S0 + sum_s gamma^(T-1-s) k_s v_s^T
+ *
+ * i.e. the recurrence of "RetNet", "Recurrent Representation", started from S0
+ * instead of zero; running a sequence in pieces, each from the previous
+ * piece's final state, gives the result of one call over the whole sequence.
+ *
+ *   initial_state  device, [B][H][dk][dv] fp32, read only; may be NULL (zero).
+ *                  It may alias q, k or v but not out or final_state.
+ *   other arguments as retention_fwd; T = 0 copies initial_state to
+ *   final_state.
+ */
+int retention_fwd_from_state(const void *q, const void *k, const void *v,
+                             const float *gamma, int chunk, const float *initial_state,
+                             void *out, float *final_state, int B, int H, int T, int dk,
+                             int dv, int dtype, void *workspace, size_t ws_bytes,
+                             void *stream);
 
 /*
  * retention_decode_step -- one recurrent step for N sequences x H heads,
@@ -157,8 +183,51 @@ int linear_attn_fwd(const void *q, const void *k, const void *v, int phi, void *
                     void *workspace, size_t ws_bytes, void *stream);
 
 /* Workspace bytes linear_attn_fwd needs for these arguments (0: none, or the
- * arguments are invalid).  Host only. */
+ * arguments are invalid).  Host only.  The same size serves
+ * linear_attn_fwd_from_state. */
 size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
+
+/*
+ * linear_attn_fwd_from_state -- linear_attn_fwd started from (S0, z0), the
+ * state and normaliser after earlier tokens, and optionally returning the pair
+ * after the last token, so a prefill can hand its (S, z) to
+ * linear_attn_decode_step ("Linear attention", the decode-step exercise and
+ * section "Decoding, training, and what each costs").
+ *
+ *   initial_S  device, [B][H][dk][dv] fp32, read only; NULL means zero
+ *   initial_z  device, [B][H][dk] fp32, read only; NULL means zero
+ *   final_S    device, [B][H][dk][dv] fp32 (written); may be NULL
+ *   final_z    device, [B][H][dk] fp32 (written); may be NULL
+ *   The initial pair may alias q, k or v; no output may overlap an input or
+ *   another output.  Other arguments as linear_attn_fwd; T = 0 copies the
+ *   initial pair to the final one.
+ */
+int linear_attn_fwd_from_state(const void *q, const void *k, const void *v, int phi,
+                               const float *initial_S, const float *initial_z, void *out,
+                               float *final_S, float *final_z, int B, int H, int T,
+                               int dk, int dv, int dtype, float eps, void *workspace,
+                               size_t ws_bytes, void *stream);
+
+/*
+ * linear_attn_decode_step -- one decode step of causal linear attention for
+ * N sequences x H heads, updating (S, z) in place, then reading the output
+ * from the updated pair:
+ *
+ *   S <- S + phi(k) v^T,  z <- z + phi(k),  out = S^T phi(q) / (z^T phi(q) + eps)
+ *
+ * ("Linear attention", the coding exercise "Causal linear attention, recurrent
+ * and parallel, plus the decode step": the token is included in its own sum.
+ * The exercise returns new arrays; this call works in place, like
+ * retention_decode_step, and a caller that needs the old pair copies it.)
+ *
+ *   q, k    device, [N][H][dk], dtype       v, out  device, [N][H][dv], dtype
+ *   S       device, [N][H][dk][dv] fp32, read and written in place
+ *   z       device, [N][H][dk] fp32, read and written in place
+ *   phi     RET_PHI_ELU1;  eps >= 0 (the pages use 1e-6);  dk, dv each 64 or 128
+ */
+int linear_attn_decode_step(const void *q, const void *k, const void *v, int phi,
+                            float *S, float *z, void *out, int N, int H, int dk, int dv,
+                            int dtype, float eps, void *stream);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none).  The pointer stays valid until the next call on that thread. */

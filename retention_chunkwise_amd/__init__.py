@@ -10,9 +10,11 @@ call raises.
 
 Functions
 ---------
-retention_fwd(q, k, v, gamma, chunk=64)        -> (out, final_state)
+retention_fwd(q, k, v, gamma, chunk=64, initial_state=None) -> (out, final_state)
 retention_decode_step(q, k, v, gamma, state)   -> out      (state updated in place)
 linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
+linear_attn_fwd(..., initial_state=(S, z), return_state=True) -> (out, S, z)
+linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
 linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
 
@@ -29,7 +31,8 @@ import threading
 import numpy as np
 import torch
 
-__all__ = ["retention_fwd", "retention_decode_step", "linear_attn_fwd", "retention_fwd_workspace_bytes",
+__all__ = ["retention_fwd", "retention_decode_step", "linear_attn_fwd", "linear_attn_decode_step",
+           "retention_fwd_workspace_bytes",
            "linear_attn_workspace_bytes", "RetentionError",
            "library_path", "load_library", "abi_version", "last_error"]
 
@@ -79,6 +82,13 @@ def load_library():
             lib.retention_decode_step.argtypes = [vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp]
             lib.retention_decode_step.restype = i
             lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
+            lib.retention_fwd_from_state.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+            lib.retention_fwd_from_state.restype = i
+            lib.linear_attn_fwd_from_state.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                                       ctypes.c_float, vp, sz, vp]
+            lib.linear_attn_fwd_from_state.restype = i
+            lib.linear_attn_decode_step.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp]
+            lib.linear_attn_decode_step.restype = i
             lib.linear_attn_fwd.restype = i
             lib.retention_last_error.argtypes = []
             lib.retention_last_error.restype = ctypes.c_char_p
@@ -161,16 +171,23 @@ def linear_attn_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype=
     return int(load_library().linear_attn_workspace_bytes(B, H, T, dk, dv, code))
 
 
+def _ptr(t):
+    return t.data_ptr() if t is not None else None
+
+
 def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
-                  want_state: bool = True, workspace=None):
-    """Chunkwise causal retention from a zero initial state.
+                  want_state: bool = True, workspace=None, initial_state=None):
+    """Chunkwise causal retention, from a zero state or from initial_state.
 
     q, k: [B,H,T,dk]; v: [B,H,T,dv] (float32 or bfloat16, same dtype, on the
     GPU); gamma: H decay values in (0, 1].  Returns (out, final_state) with
     out [B,H,T,dv] in the input dtype and final_state [B,H,dk,dv] float32
-    (None if want_state is False and none was passed).  workspace: optional
-    uint8 GPU tensor of at least retention_fwd_workspace_bytes(...) bytes;
-    one is allocated per call when it is omitted.
+    (None if want_state is False and none was passed).  initial_state:
+    optional [B,H,dk,dv] float32 state after earlier tokens (e.g. a previous
+    call's final_state; it must not be the final_state buffer of this call).
+    workspace: optional uint8 GPU tensor of at least
+    retention_fwd_workspace_bytes(...) bytes; one is allocated per call when it
+    is omitted.
     """
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -186,13 +203,21 @@ def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _check_dev("final_state", final_state, torch.float32)
+    if initial_state is not None:
+        _check_dev("initial_state", initial_state, torch.float32)
+        if tuple(initial_state.shape) != (B, H, dk, dv):
+            raise ValueError("initial_state must be [B,H,dk,dv]")
     g = _gamma_array(gamma, H)
     dt = _dtype_code(q)
     ws, nws = _workspace(lib.retention_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), dt), q.device,
                          workspace)
-    rc = lib.retention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), out.data_ptr(),
-                           final_state.data_ptr() if final_state is not None else None,
-                           B, H, T, dk, dv, dt, ws.data_ptr() if ws is not None else None, nws, _stream(q))
+    if initial_state is None:
+        rc = lib.retention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), out.data_ptr(),
+                               _ptr(final_state), B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
+    else:
+        rc = lib.retention_fwd_from_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk),
+                                          initial_state.data_ptr(), out.data_ptr(), _ptr(final_state),
+                                          B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return out, final_state
 
@@ -223,12 +248,17 @@ def retention_decode_step(q, k, v, gamma, state, out=None):
     return out
 
 
-def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None, workspace=None):
+def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None, workspace=None,
+                    initial_state=None, return_state: bool = False, final_state=None):
     """Causal linear attention with phi = elu+1 and its normaliser.
 
-    q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv].  workspace:
-    optional uint8 GPU tensor of at least linear_attn_workspace_bytes(...)
-    bytes; one is allocated per call when it is omitted.
+    q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv], or
+    (out, S, z) when return_state is True or final_state = (S, z) buffers are
+    passed (S [B,H,dk,dv], z [B,H,dk], float32).  initial_state: optional
+    (S0, z0) pair after earlier tokens (either may be None for zero).
+    workspace: optional uint8 GPU tensor of at least
+    linear_attn_workspace_bytes(...) bytes; one is allocated per call when it
+    is omitted.
     """
     lib = load_library()
     if phi not in ("elu1", RET_PHI_ELU1):
@@ -244,8 +274,60 @@ def linear_attn_fwd(q, k, v, phi: str = "elu1", eps: float = 1e-6, out=None, wor
     _check_dev("out", out, v.dtype)
     dt = _dtype_code(q)
     ws, nws = _workspace(lib.linear_attn_workspace_bytes(B, H, T, dk, dv, dt), q.device, workspace)
-    rc = lib.linear_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), RET_PHI_ELU1, out.data_ptr(),
-                             B, H, T, dk, dv, dt, float(eps), ws.data_ptr() if ws is not None else None, nws,
-                             _stream(q))
+    S0 = z0 = None
+    if initial_state is not None:
+        S0, z0 = initial_state
+    fS = fz = None
+    if final_state is not None:
+        fS, fz = final_state
+    elif return_state:
+        fS = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        fz = torch.empty((B, H, dk), dtype=torch.float32, device=q.device)
+    for name, t, shp in (("initial S", S0, (B, H, dk, dv)), ("initial z", z0, (B, H, dk)),
+                         ("final S", fS, (B, H, dk, dv)), ("final z", fz, (B, H, dk))):
+        if t is not None:
+            _check_dev(name, t, torch.float32)
+            if tuple(t.shape) != shp:
+                raise ValueError(f"{name} must be {list(shp)}")
+    if S0 is None and z0 is None and fS is None and fz is None:
+        rc = lib.linear_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), RET_PHI_ELU1, out.data_ptr(),
+                                 B, H, T, dk, dv, dt, float(eps), _ptr(ws), nws, _stream(q))
+        _raise(rc)
+        return out
+    rc = lib.linear_attn_fwd_from_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), RET_PHI_ELU1, _ptr(S0),
+                                        _ptr(z0), out.data_ptr(), _ptr(fS), _ptr(fz), B, H, T, dk, dv, dt,
+                                        float(eps), _ptr(ws), nws, _stream(q))
+    _raise(rc)
+    if fS is None and fz is None:
+        return out
+    return out, fS, fz
+
+
+def linear_attn_decode_step(q, k, v, S, z, eps: float = 1e-6, out=None, phi: str = "elu1"):
+    """One decode step of causal linear attention (phi = elu+1), in place:
+    S <- S + phi(k) v^T, z <- z + phi(k), out = S^T phi(q) / (z^T phi(q) + eps).
+
+    q, k: [N,H,dk]; v: [N,H,dv] (float32 or bfloat16); S: [N,H,dk,dv] and
+    z: [N,H,dk] float32.  Returns out [N,H,dv] in the input dtype.
+    """
+    lib = load_library()
+    if phi not in ("elu1", RET_PHI_ELU1):
+        raise ValueError("phi must be 'elu1'")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("S", S, torch.float32)
+    _check_dev("z", z, torch.float32)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [N,H,dk] and v [N,H,dv]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    if tuple(S.shape) != (N, H, dk, dv) or tuple(z.shape) != (N, H, dk):
+        raise ValueError("S must be [N,H,dk,dv] and z [N,H,dk]")
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, v.dtype)
+    rc = lib.linear_attn_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), RET_PHI_ELU1, S.data_ptr(),
+                                     z.data_ptr(), out.data_ptr(), N, H, dk, dv, _dtype_code(q), float(eps),
+                                     _stream(q))
     _raise(rc)
     return out

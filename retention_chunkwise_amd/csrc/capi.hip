@@ -62,11 +62,11 @@ bool mul_ok(size_t& acc, long long f) {
     return true;
 }
 
-int check_gamma(const float* gamma, int H, float* log2g) {
+int check_gamma(const char* fn, const float* gamma, int H, float* log2g) {
     for (int h = 0; h < H; ++h) {
         const float g = gamma[h];
         if (!(g > 0.f && g <= 1.f))  // also rejects NaN
-            return fail(RET_ERR_GAMMA, "gamma[%d] = %g is outside (0, 1]", h, static_cast<double>(g));
+            return fail(RET_ERR_GAMMA, "%s: gamma[%d] = %g is outside (0, 1]", fn, h, static_cast<double>(g));
         if (log2g) log2g[h] = static_cast<float>(log2(static_cast<double>(g)));
     }
     return RET_OK;
@@ -146,15 +146,26 @@ int check_workspace(const char* fn, const SegPlan& p, const void* workspace, siz
     return RET_OK;
 }
 
+// State pointers of a forward call: entering token 0 and after the last token
+// (each may be null; the normalisers are linear attention only).
+struct FwdState {
+    const float* init_state = nullptr;
+    const float* init_z = nullptr;
+    float* final_state = nullptr;
+    float* final_z = nullptr;
+};
+
 // Launches the segment-split forward (bf16) with a checked plan and workspace.
 hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
-                               float* final_state, void* workspace, const float* log2g, float eps, int B, int H,
+                               const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
                                int T, int chunk, int dk, int dv, bool linattn, hipStream_t st) {
     ret::SegArgs sa{};
     sa.G = plan.G;
     sa.cps = plan.cps;
     sa.pieces = plan.pieces;
-    sa.q = q; sa.k = k; sa.v = v; sa.out = out; sa.final_state = final_state;
+    sa.q = q; sa.k = k; sa.v = v; sa.out = out;
+    sa.final_state = fst.final_state; sa.init_state = fst.init_state;
+    sa.init_z = fst.init_z; sa.final_z = fst.final_z;
     sa.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
     sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
     if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
@@ -192,151 +203,246 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
 
 int retention_abi_version(void) { return RET_ABI_VERSION; }
 
-int retention_fwd(const void* q, const void* k, const void* v, const float* gamma, int chunk,
-                  void* out, float* final_state, int B, int H, int T, int dk, int dv, int dtype,
-                  void* workspace, size_t ws_bytes, void* stream) {
-    if (!gamma) return fail(RET_ERR_NULL, "retention_fwd: gamma must be non-NULL");
+}  // extern "C"
+
+namespace {
+
+// Checks an optional fp32 state tensor of `bytes` bytes: 16-byte aligned and
+// overlapping none of `others`.
+int check_state_arg(const char* fn, const char* name, const void* p, size_t bytes, std::initializer_list<Range> others) {
+    if (!p) return RET_OK;
+    if (!aligned16(p)) return fail(RET_ERR_ALIGN, "%s: %s must be 16-byte aligned", fn, name);
+    const Range r = range(name, p, bytes);
+    for (const Range& o : others)
+        if (overlap(r, o)) return fail(RET_ERR_ALIAS, "%s: %s overlaps %s", fn, name, o.name);
+    return RET_OK;
+}
+
+// Shared by retention_fwd and retention_fwd_from_state.
+int ret_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const float* gamma, int chunk,
+                 const float* initial_state, void* out, float* final_state, int B, int H, int T, int dk, int dv,
+                 int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
     const int esz = dtype_size(dtype);
-    if (!esz) return fail(RET_ERR_DTYPE, "retention_fwd: unknown dtype %d", dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
     if (chunk != 64 && chunk != 128)
-        return fail(RET_ERR_CHUNK, "retention_fwd: chunk must be 64 or 128 (got %d)", chunk);
+        return fail(RET_ERR_CHUNK, "%s: chunk must be 64 or 128 (got %d)", fn, chunk);
     if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
-        return fail(RET_ERR_SHAPE, "retention_fwd: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)",
+        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)", fn,
                     ret::kMaxHeads, B, H, T);
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
-        return fail(RET_ERR_SHAPE, "retention_fwd: dk and dv must each be 64 or 128 (got %d, %d)", dk, dv);
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
     size_t nqk = esz, nv = esz, ns = 4;
     if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
         !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv) ||
         !mul_ok(ns, B) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
-        return fail(RET_ERR_SHAPE, "retention_fwd: tensor sizes overflow");
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
     if (nqk > 0 && (!q || !k || !v || !out))
-        return fail(RET_ERR_NULL, "retention_fwd: q, k, v and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        (final_state && !aligned16(final_state)))
-        return fail(RET_ERR_ALIGN, "retention_fwd: device pointers must be 16-byte aligned");
+        return fail(RET_ERR_NULL, "%s: q, k, v and out must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     ret::WalkArgs a{};
-    int rc = check_gamma(gamma, H, a.log2g);
+    int rc = check_gamma(fn, gamma, H, a.log2g);
     if (rc) return rc;
     const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
     const Range ro = range("out", out, nv);
+    const Range none{"", 0, 0};
     for (const Range& in : {rq, rk, rv})
-        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "retention_fwd: out overlaps %s", in.name);
-    if (final_state) {
-        const Range rs = range("final_state", final_state, ns);
-        for (const Range& in : {rq, rk, rv, ro})
-            if (overlap(rs, in)) return fail(RET_ERR_ALIAS, "retention_fwd: final_state overlaps %s", in.name);
-    }
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
+    const Range ri = initial_state ? range("initial_state", initial_state, ns) : none;
+    if ((rc = check_state_arg(fn, "final_state", final_state, ns, {rq, rk, rv, ro, ri}))) return rc;
+    if ((rc = check_state_arg(fn, "initial_state", initial_state, ns, {ro}))) return rc;
     if (B == 0) return ok();
     const long long bh = static_cast<long long>(B) * H;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    FwdState fst;
+    fst.init_state = initial_state;
+    fst.final_state = final_state;
     if (choose_fwd_path(dtype) == FwdPath::kSegment) {
         SegPlan plan;
         if (!plan_segments(bh, T, chunk, dk, dv, false, &plan))
-            return fail(RET_ERR_SHAPE, "retention_fwd: workspace size overflows");
-        const Range none{"", 0, 0};
-        rc = check_workspace("retention_fwd", plan, workspace, ws_bytes,
-                             {rq, rk, rv, ro, final_state ? range("final_state", final_state, ns) : none});
+            return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+        rc = check_workspace(fn, plan, workspace, ws_bytes,
+                             {rq, rk, rv, ro, final_state ? range("final_state", final_state, ns) : none, ri});
         if (rc) return rc;
-        const hipError_t e = launch_segment_path(plan, q, k, v, out, final_state, workspace, a.log2g, 0.f, B, H, T,
+        const hipError_t e = launch_segment_path(plan, q, k, v, out, fst, workspace, a.log2g, 0.f, B, H, T,
                                                  chunk, dk, dv, false, st);
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
         return ok();
     }
     const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, chunk, dk);
-    a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = final_state;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = final_state; a.init_state = initial_state;
     a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = 0.f;
     const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, chunk, dk, nt, false, st);
-    if (e != hipSuccess)
-        return fail(RET_ERR_HIP, "retention_fwd: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
+}
+
+// Shared by linear_attn_fwd and linear_attn_fwd_from_state.
+int lin_fwd_impl(const char* fn, const void* q, const void* k, const void* v, int phi, const float* initial_S,
+                 const float* initial_z, void* out, float* final_S, float* final_z, int B, int H, int T, int dk,
+                 int dv, int dtype, float eps, void* workspace, size_t ws_bytes, void* stream) {
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (phi != RET_PHI_ELU1) return fail(RET_ERR_PHI, "%s: unknown feature map %d", fn, phi);
+    if (!(eps >= 0.f) || isinf(eps)) return fail(RET_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
+    if (B < 0 || T < 0 || H < 1)
+        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, H >= 1 (got B=%d H=%d T=%d)", fn, B, H, T);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
+    size_t nqk = esz, nv = esz, ns = 4, nz = 4;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv) ||
+        !mul_ok(ns, B) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv) ||
+        !mul_ok(nz, B) || !mul_ok(nz, H) || !mul_ok(nz, dk))
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
+    if (nqk > 0 && (!q || !k || !v || !out))
+        return fail(RET_ERR_NULL, "%s: q, k, v and out must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
+    const Range ro = range("out", out, nv);
+    const Range none{"", 0, 0};
+    for (const Range& in : {rq, rk, rv})
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
+    const Range riS = initial_S ? range("initial_S", initial_S, ns) : none;
+    const Range riz = initial_z ? range("initial_z", initial_z, nz) : none;
+    const Range rfS = final_S ? range("final_S", final_S, ns) : none;
+    int rc;
+    if ((rc = check_state_arg(fn, "final_S", final_S, ns, {rq, rk, rv, ro, riS, riz}))) return rc;
+    if ((rc = check_state_arg(fn, "final_z", final_z, nz, {rq, rk, rv, ro, riS, riz, rfS}))) return rc;
+    if ((rc = check_state_arg(fn, "initial_S", initial_S, ns, {ro}))) return rc;
+    if ((rc = check_state_arg(fn, "initial_z", initial_z, nz, {ro}))) return rc;
+    if (B == 0) return ok();
+    const long long bh = static_cast<long long>(B) * H;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    FwdState fst;
+    fst.init_state = initial_S;
+    fst.init_z = initial_z;
+    fst.final_state = final_S;
+    fst.final_z = final_z;
+    if (choose_fwd_path(dtype) == FwdPath::kSegment) {
+        SegPlan plan;
+        if (!plan_segments(bh, T, linattn_chunk(dk), dk, dv, true, &plan))
+            return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+        const Range rfz = final_z ? range("final_z", final_z, nz) : none;
+        rc = check_workspace(fn, plan, workspace, ws_bytes, {rq, rk, rv, ro, riS, riz, rfS, rfz});
+        if (rc) return rc;
+        const hipError_t e = launch_segment_path(plan, q, k, v, out, fst, workspace, nullptr, eps, B, H, T,
+                                                 linattn_chunk(dk), dk, dv, true, st);
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    }
+    ret::WalkArgs a{};
+    const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, 128, dk);
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.final_state = final_S; a.init_state = initial_S; a.init_z = initial_z; a.final_z = final_z;
+    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = eps;
+    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, 128, dk, nt, true, st);
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
+// Shared argument checks of the two decode steps.  z is the normaliser of the
+// linear-attention step (null for retention).
+int decode_checks(const char* fn, const void* q, const void* k, const void* v, const float* state, const float* z,
+                  bool lin, const void* out, int N, int H, int dk, int dv, int dtype) {
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    const int hmax = lin ? 0x7fffffff : ret::kMaxHeads;
+    if (N < 0 || H < 1 || H > hmax)
+        return fail(RET_ERR_SHAPE, "%s: need N >= 0, 1 <= H <= %d (got N=%d H=%d)", fn, hmax, N, H);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
+    size_t nqk = esz, nv = esz, ns = 4, nz = 4;
+    if (!mul_ok(nqk, N) || !mul_ok(nqk, H) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, N) || !mul_ok(nv, H) || !mul_ok(nv, dv) ||
+        !mul_ok(ns, N) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv) ||
+        !mul_ok(nz, N) || !mul_ok(nz, H) || !mul_ok(nz, dk))
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
+    if (nqk > 0 && (!q || !k || !v || !state || !out || (lin && !z)))
+        return fail(RET_ERR_NULL, lin ? "%s: q, k, v, S, z and out must be non-NULL"
+                                      : "%s: q, k, v, state and out must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(out) ||
+        (lin && !aligned16(z)))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    const char* sname = lin ? "S" : "state";
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
+    const Range rs = range(sname, state, ns), ro = range("out", out, nv);
+    const Range rz = lin ? range("z", z, nz) : Range{"", 0, 0};
+    for (const Range& in : {rq, rk, rv}) {
+        if (overlap(rs, in)) return fail(RET_ERR_ALIAS, "%s: %s overlaps %s", fn, sname, in.name);
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
+        if (overlap(rz, in)) return fail(RET_ERR_ALIAS, "%s: z overlaps %s", fn, in.name);
+    }
+    if (overlap(ro, rs)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, sname);
+    if (overlap(rz, rs)) return fail(RET_ERR_ALIAS, "%s: z overlaps S", fn);
+    if (overlap(rz, ro)) return fail(RET_ERR_ALIAS, "%s: z overlaps out", fn);
+    return RET_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int retention_fwd(const void* q, const void* k, const void* v, const float* gamma, int chunk,
+                  void* out, float* final_state, int B, int H, int T, int dk, int dv, int dtype,
+                  void* workspace, size_t ws_bytes, void* stream) {
+    return ret_fwd_impl("retention_fwd", q, k, v, gamma, chunk, nullptr, out, final_state, B, H, T, dk, dv, dtype,
+                        workspace, ws_bytes, stream);
+}
+
+int retention_fwd_from_state(const void* q, const void* k, const void* v, const float* gamma, int chunk,
+                             const float* initial_state, void* out, float* final_state, int B, int H, int T,
+                             int dk, int dv, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    return ret_fwd_impl("retention_fwd_from_state", q, k, v, gamma, chunk, initial_state, out, final_state, B, H,
+                        T, dk, dv, dtype, workspace, ws_bytes, stream);
 }
 
 int retention_decode_step(const void* q, const void* k, const void* v, const float* gamma,
                           float* state, void* out, int N, int H, int dk, int dv, int dtype,
                           void* stream) {
-    if (!gamma) return fail(RET_ERR_NULL, "retention_decode_step: gamma must be non-NULL");
-    const int esz = dtype_size(dtype);
-    if (!esz) return fail(RET_ERR_DTYPE, "retention_decode_step: unknown dtype %d", dtype);
-    if (N < 0 || H < 1 || H > ret::kMaxHeads)
-        return fail(RET_ERR_SHAPE, "retention_decode_step: need N >= 0, 1 <= H <= %d (got N=%d H=%d)",
-                    ret::kMaxHeads, N, H);
-    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
-        return fail(RET_ERR_SHAPE, "retention_decode_step: dk and dv must each be 64 or 128 (got %d, %d)", dk, dv);
-    size_t nqk = esz, nv = esz, ns = 4;
-    if (!mul_ok(nqk, N) || !mul_ok(nqk, H) || !mul_ok(nqk, dk) ||
-        !mul_ok(nv, N) || !mul_ok(nv, H) || !mul_ok(nv, dv) ||
-        !mul_ok(ns, N) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
-        return fail(RET_ERR_SHAPE, "retention_decode_step: tensor sizes overflow");
-    if (nqk > 0 && (!q || !k || !v || !state || !out))
-        return fail(RET_ERR_NULL, "retention_decode_step: q, k, v, state and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(state) || !aligned16(out))
-        return fail(RET_ERR_ALIGN, "retention_decode_step: device pointers must be 16-byte aligned");
-    ret::DecodeArgs a{};
-    int rc = check_gamma(gamma, H, nullptr);
+    const char* fn = "retention_decode_step";
+    if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
+    int rc = decode_checks(fn, q, k, v, state, nullptr, false, out, N, H, dk, dv, dtype);
     if (rc) return rc;
+    ret::DecodeArgs a{};
+    if ((rc = check_gamma(fn, gamma, H, nullptr))) return rc;
     for (int h = 0; h < H; ++h) a.gamma[h] = gamma[h];
-    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
-    const Range rs = range("state", state, ns), ro = range("out", out, nv);
-    for (const Range& in : {rq, rk, rv}) {
-        if (overlap(rs, in)) return fail(RET_ERR_ALIAS, "retention_decode_step: state overlaps %s", in.name);
-        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "retention_decode_step: out overlaps %s", in.name);
-    }
-    if (overlap(ro, rs)) return fail(RET_ERR_ALIAS, "retention_decode_step: out overlaps state");
     if (N == 0) return ok();
     a.q = q; a.k = k; a.v = v; a.state = state; a.out = out; a.N = N; a.H = H;
     const hipError_t e = ret::launch_decode(a, dtype == RET_BF16, dk, dv, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(RET_ERR_HIP, "retention_decode_step: launch failed: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
 
 int linear_attn_fwd(const void* q, const void* k, const void* v, int phi, void* out, int B, int H,
                     int T, int dk, int dv, int dtype, float eps, void* workspace, size_t ws_bytes,
                     void* stream) {
-    const int esz = dtype_size(dtype);
-    if (!esz) return fail(RET_ERR_DTYPE, "linear_attn_fwd: unknown dtype %d", dtype);
-    if (phi != RET_PHI_ELU1) return fail(RET_ERR_PHI, "linear_attn_fwd: unknown feature map %d", phi);
-    if (!(eps >= 0.f) || isinf(eps))
-        return fail(RET_ERR_SHAPE, "linear_attn_fwd: eps must be finite and >= 0");
-    if (B < 0 || T < 0 || H < 1)
-        return fail(RET_ERR_SHAPE, "linear_attn_fwd: need B >= 0, T >= 0, H >= 1 (got B=%d H=%d T=%d)", B, H, T);
-    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
-        return fail(RET_ERR_SHAPE, "linear_attn_fwd: dk and dv must each be 64 or 128 (got %d, %d)", dk, dv);
-    size_t nqk = esz, nv = esz;
-    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
-        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv))
-        return fail(RET_ERR_SHAPE, "linear_attn_fwd: tensor sizes overflow");
-    if (nqk > 0 && (!q || !k || !v || !out))
-        return fail(RET_ERR_NULL, "linear_attn_fwd: q, k, v and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-        return fail(RET_ERR_ALIGN, "linear_attn_fwd: device pointers must be 16-byte aligned");
-    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
-    const Range ro = range("out", out, nv);
-    for (const Range& in : {rq, rk, rv})
-        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "linear_attn_fwd: out overlaps %s", in.name);
-    if (B == 0) return ok();
-    if (choose_fwd_path(dtype) == FwdPath::kSegment) {
-        const long long bhs = static_cast<long long>(B) * H;
-        SegPlan plan;
-        if (!plan_segments(bhs, T, linattn_chunk(dk), dk, dv, true, &plan))
-            return fail(RET_ERR_SHAPE, "linear_attn_fwd: workspace size overflows");
-        const int rcw = check_workspace("linear_attn_fwd", plan, workspace, ws_bytes, {rq, rk, rv, ro});
-        if (rcw) return rcw;
-        const hipError_t e = launch_segment_path(plan, q, k, v, out, nullptr, workspace, nullptr, eps, B, H, T,
-                                                 linattn_chunk(dk), dk, dv, true, static_cast<hipStream_t>(stream));
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "linear_attn_fwd: launch failed: %s", hipGetErrorString(e));
-        return ok();
-    }
-    ret::WalkArgs a{};
-    const long long bh = static_cast<long long>(B) * H;
-    const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, 128, dk);
-    a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = nullptr;
-    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = eps;
-    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, 128, dk, nt, true,
-                                          static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(RET_ERR_HIP, "linear_attn_fwd: launch failed: %s", hipGetErrorString(e));
+    return lin_fwd_impl("linear_attn_fwd", q, k, v, phi, nullptr, nullptr, out, nullptr, nullptr, B, H, T, dk, dv,
+                        dtype, eps, workspace, ws_bytes, stream);
+}
+
+int linear_attn_fwd_from_state(const void* q, const void* k, const void* v, int phi, const float* initial_S,
+                               const float* initial_z, void* out, float* final_S, float* final_z, int B, int H,
+                               int T, int dk, int dv, int dtype, float eps, void* workspace, size_t ws_bytes,
+                               void* stream) {
+    return lin_fwd_impl("linear_attn_fwd_from_state", q, k, v, phi, initial_S, initial_z, out, final_S, final_z,
+                        B, H, T, dk, dv, dtype, eps, workspace, ws_bytes, stream);
+}
+
+int linear_attn_decode_step(const void* q, const void* k, const void* v, int phi, float* S, float* z, void* out,
+                            int N, int H, int dk, int dv, int dtype, float eps, void* stream) {
+    const char* fn = "linear_attn_decode_step";
+    if (phi != RET_PHI_ELU1) return fail(RET_ERR_PHI, "%s: unknown feature map %d", fn, phi);
+    if (!(eps >= 0.f) || isinf(eps)) return fail(RET_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
+    const int rc = decode_checks(fn, q, k, v, S, z, true, out, N, H, dk, dv, dtype);
+    if (rc) return rc;
+    if (N == 0) return ok();
+    ret::DecodeArgs a{};
+    a.q = q; a.k = k; a.v = v; a.state = S; a.z = z; a.out = out; a.N = N; a.H = H; a.eps = eps;
+    const hipError_t e = ret::launch_decode_lin(a, dtype == RET_BF16, dk, dv, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
 

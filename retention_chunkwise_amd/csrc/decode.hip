@@ -1,9 +1,15 @@
-// decode.hip -- recurrent retention decode step on gfx950.
+// decode.hip -- recurrent decode steps on gfx950.
 //
-// For every (sequence, head): S <- gamma S + k v^T, then o = q S, reading the
-// output from the updated state ("RetNet", "Recurrent Representation";
-// "Efficient and Sparse Transformers", section 6, recurrent form and its
-// minimal recurrent step).  S is fp32, dk x dv, updated in place.
+// Retention, for every (sequence, head): S <- gamma S + k v^T, then o = q S,
+// reading the output from the updated state ("RetNet", "Recurrent
+// Representation"; "Efficient and Sparse Transformers", section 6, recurrent
+// form and its minimal recurrent step).  S is fp32, dk x dv, updated in place.
+//
+// Linear attention with phi = elu+1 ("Linear attention", the decode-step
+// exercise): S <- S + phi(k) v^T, z <- z + phi(k), then
+// o = S^T phi(q) / (z^T phi(q) + eps) from the updated pair; S and z are fp32
+// and updated in place.  The same kernel runs it with gamma = 1, phi applied
+// to q and k as they are staged, and the denominator reduced by wave 0.
 //
 // The step is bound by HBM: each state element is read once and written once
 // and takes two FMAs.  One workgroup streams one state tile.  Thread t owns
@@ -32,7 +38,10 @@ __device__ __forceinline__ float load_elem(const void* p, long long i) {
     }
 }
 
-template <bool BF16, int DK, int DV>
+// elu(x) + 1: x + 1 for x > 0, e^x otherwise
+__device__ __forceinline__ float phi_elu1(float x) { return x > 0.f ? x + 1.f : expf(x); }
+
+template <bool BF16, int DK, int DV, bool LIN>
 __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
     constexpr int CG = DV / 4;          // 16-byte column groups per row
     constexpr int RP = kThreads / CG;   // row phases
@@ -43,10 +52,11 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
     __shared__ float ks[DK];
     __shared__ float vs[DV];
     __shared__ __attribute__((aligned(16))) float red[RP][DV];
+    __shared__ float den_s;  // linear attention: z^T phi(q) + eps
 
     const int tid = threadIdx.x;
     const long long nh = blockIdx.x;
-    const float gam = a.gamma[nh % a.H];
+    const float gam = LIN ? 1.f : a.gamma[nh % a.H];
     const int cg = tid % CG, rp = tid / CG;
     float* S = a.state + nh * DK * DV;
 
@@ -57,12 +67,43 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
         const int row = rp + m * RP;
         sv[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV + 4 * cg));
     }
+    constexpr int ZPT = LIN ? DK / 64 : 1;  // normaliser entries per wave-0 lane
+    float zr[ZPT];
+    if constexpr (LIN) {
+        if (tid < 64) {
+#pragma unroll
+            for (int u = 0; u < ZPT; ++u) zr[u] = a.z[nh * DK + tid + 64 * u];
+        }
+    }
     for (int i = tid; i < 2 * DK + DV; i += kThreads) {
-        if (i < DK) qs[i] = load_elem<BF16>(a.q, nh * DK + i);
-        else if (i < 2 * DK) ks[i - DK] = load_elem<BF16>(a.k, nh * DK + (i - DK));
-        else vs[i - 2 * DK] = load_elem<BF16>(a.v, nh * DV + (i - 2 * DK));
+        if (i < DK) {
+            const float x = load_elem<BF16>(a.q, nh * DK + i);
+            qs[i] = LIN ? phi_elu1(x) : x;
+        } else if (i < 2 * DK) {
+            const float x = load_elem<BF16>(a.k, nh * DK + (i - DK));
+            ks[i - DK] = LIN ? phi_elu1(x) : x;
+        } else {
+            vs[i - 2 * DK] = load_elem<BF16>(a.v, nh * DV + (i - 2 * DK));
+        }
     }
     __syncthreads();
+
+    if constexpr (LIN) {
+        // z <- z + phi(k); denominator z^T phi(q) + eps, reduced across wave 0
+        if (tid < 64) {
+            float part = 0.f;
+#pragma unroll
+            for (int u = 0; u < ZPT; ++u) {
+                const int i = tid + 64 * u;
+                const float zn = zr[u] + ks[i];
+                a.z[nh * DK + i] = zn;
+                part = fmaf(zn, qs[i], part);
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+            if (tid == 0) den_s = part + a.eps;
+        }
+    }
 
     const f32x4 vv = *reinterpret_cast<const f32x4*>(&vs[4 * cg]);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -83,6 +124,7 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
         float o = 0.f;
 #pragma unroll
         for (int r = 0; r < RP; ++r) o += red[r][n];
+        if constexpr (LIN) o /= den_s;
         if constexpr (BF16) {
             static_cast<unsigned short*>(a.out)[nh * DV + n] =
                 __builtin_bit_cast(unsigned short, static_cast<__bf16>(o));
@@ -92,29 +134,33 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(const DecodeArgs a) {
     }
 }
 
-template <bool BF16, int DK, int DV>
+template <bool BF16, int DK, int DV, bool LIN>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     const long long groups = static_cast<long long>(a.N) * a.H;
     if (groups <= 0) return hipSuccess;
     if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_kernel<BF16, DK, DV>), dim3(static_cast<unsigned>(groups)),
+    hipLaunchKernelGGL((decode_kernel<BF16, DK, DV, LIN>), dim3(static_cast<unsigned>(groups)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 
-template <bool BF16>
+template <bool BF16, bool LIN>
 hipError_t launch_b(const DecodeArgs& a, int dk, int dv, hipStream_t stream) {
-    if (dk == 64 && dv == 64) return launch_t<BF16, 64, 64>(a, stream);
-    if (dk == 64 && dv == 128) return launch_t<BF16, 64, 128>(a, stream);
-    if (dk == 128 && dv == 64) return launch_t<BF16, 128, 64>(a, stream);
-    if (dk == 128 && dv == 128) return launch_t<BF16, 128, 128>(a, stream);
+    if (dk == 64 && dv == 64) return launch_t<BF16, 64, 64, LIN>(a, stream);
+    if (dk == 64 && dv == 128) return launch_t<BF16, 64, 128, LIN>(a, stream);
+    if (dk == 128 && dv == 64) return launch_t<BF16, 128, 64, LIN>(a, stream);
+    if (dk == 128 && dv == 128) return launch_t<BF16, 128, 128, LIN>(a, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t stream) {
-    return bf16 ? launch_b<true>(a, dk, dv, stream) : launch_b<false>(a, dk, dv, stream);
+    return bf16 ? launch_b<true, false>(a, dk, dv, stream) : launch_b<false, false>(a, dk, dv, stream);
+}
+
+hipError_t launch_decode_lin(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t stream) {
+    return bf16 ? launch_b<true, true>(a, dk, dv, stream) : launch_b<false, true>(a, dk, dv, stream);
 }
 
 }  // namespace ret

@@ -18,7 +18,10 @@ struct WalkArgs {
     const void* k;
     const void* v;
     void* out;
-    float* final_state;  // may be null
+    float* final_state;        // may be null
+    const float* init_state;   // [B][H][dk][dv] state before token 0; null: zero
+    const float* init_z;       // [B][H][dk] normaliser before token 0 (linear attention); null: zero
+    float* final_z;            // [B][H][dk] normaliser after the last token (linear attention); may be null
     int B, H, T;
     int dv;              // full value width (the kernel handles one slice of it)
     int nslices;         // dv / (16 * NT)
@@ -27,15 +30,18 @@ struct WalkArgs {
     float log2g[kMaxHeads];
 };
 
-// Arguments of the recurrent decode-step kernel.
+// Arguments of the recurrent decode-step kernel (retention, or linear
+// attention with the elu+1 feature map and its normaliser z).
 struct DecodeArgs {
     const void* q;
     const void* k;
     const void* v;
     float* state;
+    float* z;     // [N][H][dk], linear attention only
     void* out;
     int N, H;
-    float gamma[kMaxHeads];
+    float eps;    // linear attention only
+    float gamma[kMaxHeads];  // retention only
 };
 
 // Arguments of the segment-split forward (bf16; retention, or linear
@@ -45,7 +51,10 @@ struct SegArgs {
     const void* k;
     const void* v;
     void* out;
-    float* final_state;  // may be null
+    float* final_state;        // may be null
+    const float* init_state;   // [B][H][dk][dv] state before token 0; null: zero
+    const float* init_z;       // [B][H][dk] normaliser before token 0 (linear attention); null: zero
+    float* final_z;            // [B][H][dk] normaliser after the last token (linear attention); may be null
     float* ws;           // [B*H][G-1][pieces][dk*dv (+ dk)] fp32 segment states (and normalisers);
                          // unused when G == 1
     int B, H, T;
@@ -66,6 +75,7 @@ hipError_t launch_walk_lin_bf16(const WalkArgs& a, int chunk, int dk, int nt, hi
 hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
                          hipStream_t stream);
+hipError_t launch_decode_lin(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t stream);
 
 hipError_t launch_seg(const SegArgs& a, int chunk, int dk, int dv, bool linattn, hipStream_t stream);
 hipError_t launch_seg_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);

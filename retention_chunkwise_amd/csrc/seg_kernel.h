@@ -458,6 +458,26 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 }
             }
         }
+        if (a.init_state) {
+            // the state before token 0, decayed over the seg * L tokens before this segment
+            const float w0 = uni(ex2(static_cast<float>(a.cps) * static_cast<float>(C) * lg * static_cast<float>(seg)));
+            const float* si = a.init_state + static_cast<long long>(bh) * DK * DV;
+#pragma unroll
+            for (int mi = 0; mi < SKT; ++mi) {
+                const int m = SKT * P + mi;
+#pragma unroll
+                for (int n = 0; n < NVT; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[mi][n][r] += w0 * si[(16 * m + 4 * g + r) * DV + 16 * n + l16];
+            }
+        }
+        if constexpr (LIN) {
+            if (a.init_z) {
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi)
+                    zacc[mi] += a.init_z[static_cast<long long>(bh) * DK + 16 * (SKT * P + mi) + l16];
+            }
+        }
     }
 
     // bf16 copy of S^T in LDS: this lane's S[16m + 4g + r][16n + l16], r = 0..3,
@@ -751,6 +771,13 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 for (int n = 0; n < NVT; ++n)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) fs[(16 * m + 4 * g + r) * DV + 16 * n + l16] = sacc[mi][n][r];
+            }
+        }
+        if constexpr (LIN) {
+            if (a.final_z && seg == a.G - 1 && g == 0) {
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi)
+                    a.final_z[static_cast<long long>(bh) * DK + 16 * (SKT * P + mi) + l16] = zacc[mi];
             }
         }
     }

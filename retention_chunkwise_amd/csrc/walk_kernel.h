@@ -155,9 +155,18 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
     for (int s = 0; s < NS; ++s) xi[s] = exp2f(static_cast<float>(its(s) * 16 + l16 + 1) * lg);
 
-    f32x4 sacc[SPW];
+    f32x4 sacc[SPW];  // S[16 kt + l16][nbase + 16 nt + 4g + r] of this wave's tiles
 #pragma unroll
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (a.init_state) {
+        const float* si = a.init_state + static_cast<long long>(bh) * DK * DV + nbase;
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = W + 4 * m;
+            const int nt = qt / KT, kt = qt % KT;
+            sacc[m] = *reinterpret_cast<const f32x4*>(si + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
+        }
+    }
 
     // DMA path: 1-KB instruction i of a chunk is issued by wave i % 4 and fills
     // LDS bytes [1024 i, +1024) of its tile; lane l's 16 bytes land at +16 l.
@@ -657,9 +666,17 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
     const int tid = threadIdx.x;
     for (int m = tid; m < Cf::DEC; m += kThreads)
         sm.dec[m] = (m < 16) ? 0.f : exp2f(static_cast<float>(m - 16) * lg);
-    for (int m = tid; m < Cf::DVS * Cf::KSTR; m += kThreads) sm.Sts[0][m] = E(0);
+    // operand copy of the state entering token 0: Sts[j][i] = S[i][nbase + j]
+    const float* si = a.init_state ? a.init_state + static_cast<long long>(bh) * DK * a.dv + nbase : nullptr;
+    for (int m = tid; m < Cf::DVS * Cf::KSTR; m += kThreads) {
+        const int j = m / Cf::KSTR, i = m % Cf::KSTR;
+        const float x = (si && i < DK) ? si[static_cast<long long>(i) * a.dv + j] : 0.f;
+        if constexpr (BF16) sm.Sts[0][m] = f2bf(x);
+        else sm.Sts[0][m] = x;
+    }
     if constexpr (LIN)
-        for (int m = tid; m < DK; m += kThreads) sm.zs[0][m] = 0.f;
+        for (int m = tid; m < DK; m += kThreads)
+            sm.zs[0][m] = a.init_z ? a.init_z[static_cast<long long>(bh) * DK + m] : 0.f;
     // (the first barrier inside walk_body orders these writes before any read)
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -668,6 +685,15 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
         case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, qk, bh, nbase, lg); break;
         case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, qk, bh, nbase, lg); break;
         default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, qk, bh, nbase, lg); break;
+    }
+    if constexpr (LIN) {
+        // the normaliser after the last chunk sits in zs[nch % 2]; every slice
+        // of a (b, h) holds the same z, slice 0 writes it
+        if (a.final_z && nbase == 0) {
+            __syncthreads();
+            const int nch = (a.T + C - 1) / C;
+            for (int m = tid; m < DK; m += kThreads) a.final_z[static_cast<long long>(bh) * DK + m] = sm.zs[nch & 1][m];
+        }
     }
 }
 

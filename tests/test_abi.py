@@ -187,3 +187,86 @@ def test_workspace_is_required_and_checked():
     lneed = lib.linear_attn_workspace_bytes(1, 1, 65536, 64, 64, rc.RET_BF16)
     assert lneed > 0
     assert _lin(lib, T=65536, q=FAKE, k=FAKE * 1024, v=FAKE * 2048, out=FAKE * 4096) == -9
+
+
+# ---------------------------------------------------------------- initial state, phi decode
+def _fwd_s(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9, 0.9]), chunk=64, init=FAKE * 5,
+             out=FAKE * 4, fs=FAKE * 6, B=1, H=2, T=16, dk=64, dv=64, dtype=rc.RET_F32, ws=None, nws=0)
+    a.update(kw)
+    return lib.retention_fwd_from_state(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["init"], a["out"],
+                                        a["fs"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["ws"],
+                                        a["nws"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(init=FAKE * 5 + 8), -7),       # misaligned initial state
+    (dict(init=FAKE * 6), -8),           # initial state is the final state buffer
+    (dict(init=FAKE * 4), -8),           # initial state overlaps out
+    (dict(dk=96), -2),
+    (dict(gamma=_gam([0.9, 1.5])), -5),
+])
+def test_retention_fwd_from_state_rejects(kw, code):
+    lib = _lib()
+    assert _fwd_s(lib, **kw) == code
+    assert "retention_fwd_from_state" in lib.retention_last_error().decode()
+
+
+def test_retention_fwd_from_state_accepts_shared_input_and_empty_batch():
+    lib = _lib()
+    # an initial state may alias an input (read only); B = 0 enqueues nothing
+    assert _fwd_s(lib, B=0, init=FAKE) == 0
+
+
+def _lin_s(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, phi=rc.RET_PHI_ELU1, iS=FAKE * 5, iz=FAKE * 7, out=FAKE * 4,
+             fS=FAKE * 6, fz=FAKE * 8, B=1, H=1, T=8, dk=64, dv=64, dtype=rc.RET_F32, eps=1e-6, ws=None, nws=0)
+    a.update(kw)
+    return lib.linear_attn_fwd_from_state(a["q"], a["k"], a["v"], a["phi"], a["iS"], a["iz"], a["out"], a["fS"],
+                                          a["fz"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["eps"],
+                                          a["ws"], a["nws"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(iz=FAKE * 7 + 4), -7),
+    (dict(fz=FAKE * 6), -8),            # final z inside final S
+    (dict(fS=FAKE * 5), -8),            # final S is the initial S
+    (dict(fz=FAKE * 7), -8),            # final z is the initial z
+    (dict(phi=3), -6),
+    (dict(eps=-1.0), -2),
+])
+def test_linattn_fwd_from_state_rejects(kw, code):
+    lib = _lib()
+    assert _lin_s(lib, **kw) == code
+    assert "linear_attn_fwd_from_state" in lib.retention_last_error().decode()
+
+
+def _ldec(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, phi=rc.RET_PHI_ELU1, S=FAKE * 4, z=FAKE * 5, out=FAKE * 6,
+             N=2, H=3, dk=64, dv=64, dtype=rc.RET_BF16, eps=1e-6)
+    a.update(kw)
+    return lib.linear_attn_decode_step(a["q"], a["k"], a["v"], a["phi"], a["S"], a["z"], a["out"], a["N"],
+                                       a["H"], a["dk"], a["dv"], a["dtype"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(z=None), -1),
+    (dict(S=None), -1),
+    (dict(z=FAKE * 5 + 4), -7),
+    (dict(z=FAKE * 4), -8),             # z inside S
+    (dict(out=FAKE * 5), -8),           # out overlaps z
+    (dict(S=FAKE), -8),                 # S overlaps q
+    (dict(phi=0), -6),
+    (dict(dk=32), -2),
+    (dict(dtype=7), -3),
+    (dict(eps=float("inf")), -2),
+])
+def test_linattn_decode_rejects(kw, code):
+    lib = _lib()
+    assert _ldec(lib, **kw) == code
+    assert "linear_attn_decode_step" in lib.retention_last_error().decode()
+
+
+def test_linattn_decode_empty_is_accepted():
+    lib = _lib()
+    assert _ldec(lib, N=0) == 0
