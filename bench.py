@@ -9,8 +9,9 @@ bf16 in / fp32 accumulate, chunk 128, gamma_h = 1 - 2^(-5 - 4h/31).  Inputs
 are seeded synthetic tensors already resident in HBM when timing starts.  The
 JSON line also carries the other measured parts of the path: the recurrent
 decode step (256 sequences x 32 heads, 128 x 128 fp32 state, 1000 consecutive
-steps) and the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
-d = 64), each with its own roofline figures.
+steps), the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
+d = 64) and the elu+1 decode step on the decode shapes, each with its own
+roofline figures.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -217,7 +218,30 @@ def main():
                          "frac": d_gbs / M.PEAK_HBM_GBS,
                          "traffic": (d_tr["bytes_per_launch"] if d_tr else None)},
         }
-        del dq, dk_, dv_, state, dout
+
+        # the elu+1 decode step on the same shapes: (S, z) from about 100 earlier tokens
+        g = torch.Generator().manual_seed(0)
+        lz = (100.0 + 10.0 * torch.rand((wd.B, wd.H, wd.dk), generator=g)).to(dev)
+        lS = (torch.randn((wd.B, wd.H, wd.dk, wd.dv), generator=g) * 10.0).to(dev)
+
+        def lstep_dec():
+            rc.linear_attn_decode_step(dq, dk_, dv_, lS, lz, out=dout)
+
+        ld_kern, ld_wall = time_launches(lstep_dec, args.decode_steps, 10)
+        ld_bytes = M.linattn_decode_bytes(wd.B, wd.H, wd.dk, wd.dv, 2)
+        ld_gbs = ld_bytes / (ld_kern * 1e-3) / 1e9
+        ld_tr = measured_traffic("linattn_decode_kernel_decode_bf16", DECODE_SOURCES)
+        res["linear_attn_decode"] = {
+            "workload": "linattn elu+1 decode, 256 sequences x 32 heads, 128 x 128 fp32 state + normaliser, "
+                        "bf16 tokens", "steps_timed": args.decode_steps,
+            "us_per_step": ld_kern * 1e3, "wall_us_per_step": ld_wall * 1e3,
+            "tokens_per_s": wd.B / (ld_wall * 1e-3),
+            "gbs": ld_gbs, "hbm_frac": ld_gbs / M.PEAK_HBM_GBS,
+            "roofline": {"bound": "hbm", "achieved": ld_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": ld_gbs / M.PEAK_HBM_GBS,
+                         "traffic": (ld_tr["bytes_per_launch"] if ld_tr else None)},
+        }
+        del dq, dk_, dv_, state, dout, lS, lz
 
         wa = wl.WORKLOADS["linattn_elu1_bf16"]
         li = wl.make_inputs(wa, seed=0)
@@ -233,11 +257,16 @@ def main():
         l_fl = M.fwd_flops(wa.B, wa.H, wa.T, wa.dk, wa.dv, wa.chunk)
         l_by = M.fwd_bytes(wa.B, wa.H, wa.T, wa.dk, wa.dv, 2, final_state=False)
         l_gbs = l_by / (l_kern * 1e-3) / 1e9
+        l_tr = measured_traffic("linattn_linattn_elu1_bf16", FWD_SOURCES)
         res["linear_attn"] = {
             "workload": wa.name, "ms_per_call": l_kern, "tokens_per_s": wa.B * wa.T / (l_wall * 1e-3),
             "tflops": l_fl / (l_kern * 1e-3) / 1e12,
             "mfma_peak_frac": l_fl / (l_kern * 1e-3) / 1e12 / M.PEAK_TFLOPS["bf16"],
             "gbs": l_gbs, "hbm_frac": l_gbs / M.PEAK_HBM_GBS,
+            "roofline": {"kernel": "linear_attn_fwd: seg_state_kernel + seg_walk_kernel<C=128, dk=64, dv=64, LIN>",
+                         "bound": "hbm", "achieved": l_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": l_gbs / M.PEAK_HBM_GBS,
+                         "traffic": (l_tr["bytes_per_launch"] if l_tr else None)},
         }
         del lq, lk, lv, lout, lws
 

@@ -88,5 +88,10 @@ def decode_bytes(N, H, dk, dv, elem_bytes: int) -> int:
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * elem_bytes + dv * elem_bytes)
 
 
+def linattn_decode_bytes(N, H, dk, dv, elem_bytes: int) -> int:
+    """The retention decode bytes plus the fp32 normaliser z read and written."""
+    return decode_bytes(N, H, dk, dv, elem_bytes) + N * H * 2 * dk * 4
+
+
 def decode_flops(N, H, dk, dv) -> int:
     return N * H * decode_flops_per_head(dk, dv)
