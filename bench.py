@@ -270,6 +270,31 @@ def main():
         }
         del lq, lk, lv, lout, lws
 
+    # ---------------- fp32 forward with final state, [4, 8, 2048, 64], chunk 64
+    if not args.no_components:
+        wf = wl.WORKLOADS["ret_fwd_mh_f32"]
+        fi = wl.make_inputs(wf, seed=0)
+        fq, fk, fv = (fi[n].to(dev) for n in ("q", "k", "v"))
+        fout = torch.empty_like(fv)
+        ffs = torch.empty((wf.B, wf.H, wf.dk, wf.dv), dtype=torch.float32, device=dev)
+
+        def f32step():
+            rc.retention_fwd(fq, fk, fv, fi["gamma"], chunk=wf.chunk, out=fout, final_state=ffs)
+
+        f_kern, f_wall = time_launches(f32step, max(args.steps, 200), args.warmup)
+        f_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, wf.chunk)
+        f_by = M.fwd_bytes(wf.B, wf.H, wf.T, wf.dk, wf.dv, 4, final_state=True)
+        f_tf = f_fl / (f_kern * 1e-3) / 1e12
+        res["fwd_f32"] = {
+            "workload": wf.name, "ms_per_call": f_kern, "wall_ms_per_call": f_wall,
+            "tokens_per_s": wf.B * wf.T / (f_kern * 1e-3),
+            "tflops": f_tf, "gbs": f_by / (f_kern * 1e-3) / 1e9,
+            "roofline": {"kernel": "retention_fwd fp32: walk_kernel<fp32, C=64, dk=64>", "bound": "mfma",
+                         "achieved": f_tf, "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                         "frac": f_tf / M.PEAK_TFLOPS["f32"], "traffic": None},
+        }
+        del fq, fk, fv, fout, ffs
+
     if args.calibrate_copy:
         # plain device-to-device copies of a known size, for scaling HBM counters
         n = 1 << 28  # 1 GiB of fp32

@@ -93,24 +93,64 @@ FwdPath choose_fwd_path(int dtype) {
     return seg_ok ? FwdPath::kSegment : FwdPath::kSlice;
 }
 
-// Segment plan of the bf16 forward paths: segment count G, chunks per
-// segment, state-kernel workgroups per segment, and the workspace they need
-// ((G - 1) * pieces partial states per (b, h); none when G == 1).
+// Plan of a forward call: the path, the segment count G, chunks per segment,
+// state-kernel workgroups per segment (segment path), the value-slice width
+// (value-slice path), and the workspace they need: (G - 1) * pieces partial
+// states per (b, h), none when G == 1.
 struct SegPlan {
-    int G = 1, cps = 1, pieces = 1;
+    FwdPath path = FwdPath::kSegment;
+    int chunk = 64;
+    int G = 1, cps = 1, pieces = 1, nt = 1;
     size_t ws_bytes = 0;
 };
 
-bool plan_segments(long long bh, int T, int chunk, int dk, int dv, bool linattn, SegPlan* p) {
-    const int nch = (T + chunk - 1) / chunk;
+// Segment count forced by RET_FWD_SEGMENTS (0: not forced).
+bool forced_segments(int nch, SegPlan* p) {
     const int forced = env_int("RET_FWD_SEGMENTS");
-    if (forced > 0) {
-        const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
-        p->cps = (nch > 0) ? (nch + g - 1) / g : 1;
-        p->G = (nch > 0) ? (nch + p->cps - 1) / p->cps : 1;
-    } else {
-        p->G = ret::choose_segments(bh, nch, 256, 4, 16, &p->cps);
+    if (forced <= 0) return false;
+    const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
+    p->cps = (nch > 0) ? (nch + g - 1) / g : 1;
+    p->G = (nch > 0) ? (nch + p->cps - 1) / p->cps : 1;
+    return true;
+}
+
+bool set_ws_bytes(long long bh, int dk, int dv, bool linattn, SegPlan* p) {
+    p->ws_bytes = 0;
+    if (p->G > 1) {
+        size_t n = 4;
+        const long long slot = static_cast<long long>(dk) * dv + (linattn ? dk : 0);
+        if (!mul_ok(n, bh) || !mul_ok(n, p->G - 1) || !mul_ok(n, p->pieces) || !mul_ok(n, slot)) return false;
+        p->ws_bytes = n;
     }
+    return true;
+}
+
+// Value-slice path: fp32 walks segments with the widest value slice that
+// fits in LDS (Q K^T computed once per segment chunk, the segments give the
+// parallelism); a bf16 walk on this path (only when forced) keeps whole
+// sequences and narrow slices unless a segment count is forced too.
+bool plan_slices(long long bh, int T, int chunk, int dk, int dv, bool linattn, bool bf16, SegPlan* p) {
+    p->path = FwdPath::kSlice;
+    p->chunk = chunk;
+    p->pieces = 1;
+    const int nch = (T + chunk - 1) / chunk;
+    const bool forced = forced_segments(nch, p);
+    if (!bf16 || forced) {
+        p->nt = ret::choose_walk_nt_wide(dv, bf16, chunk, dk, linattn);
+        if (!forced) p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, 256, 2, 16, &p->cps);
+    } else {
+        p->nt = ret::choose_walk_nt(bh, dv, 256, bf16, chunk, dk);
+        p->G = 1;
+        p->cps = nch > 0 ? nch : 1;
+    }
+    return set_ws_bytes(bh, dk, dv, linattn, p);
+}
+
+bool plan_segments(long long bh, int T, int chunk, int dk, int dv, bool linattn, SegPlan* p) {
+    p->path = FwdPath::kSegment;
+    p->chunk = chunk;
+    const int nch = (T + chunk - 1) / chunk;
+    if (!forced_segments(nch, p)) p->G = ret::choose_segments(bh, nch, 256, 4, 16, &p->cps);
     // state-kernel workgroups per segment: enough to occupy the chip in one
     // round, dividing the segment's 64-token blocks evenly, at most 16 partial
     // states per (b, h) (the walk sums up to that many states on entry)
@@ -122,14 +162,24 @@ bool plan_segments(long long bh, int T, int chunk, int dk, int dv, bool linattn,
     if (pieces < 1) pieces = 1;
     while (pieces > 1 && sblocks % pieces != 0) --pieces;
     p->pieces = pieces;
-    p->ws_bytes = 0;
-    if (p->G > 1) {
-        size_t n = 4;
-        const long long slot = static_cast<long long>(dk) * dv + (linattn ? dk : 0);
-        if (!mul_ok(n, bh) || !mul_ok(n, p->G - 1) || !mul_ok(n, p->pieces) || !mul_ok(n, slot)) return false;
-        p->ws_bytes = n;
-    }
-    return true;
+    return set_ws_bytes(bh, dk, dv, linattn, p);
+}
+
+// Internal chunk of the linear-attention forward: bf16 segments use 128
+// tokens (64 when dk = 128, where 128 would spill registers); the fp32 walk
+// uses 64 (wider value slices fit in LDS); a forced bf16 slice walk 128.
+int linattn_chunk(int dk, FwdPath path, bool bf16) {
+    if (path == FwdPath::kSegment) return dk == 128 ? 64 : 128;
+    return bf16 ? 128 : 64;
+}
+
+// The plan a forward call with these arguments will use.
+bool plan_fwd(long long bh, int T, int chunk, int dk, int dv, bool linattn, int dtype, SegPlan* p) {
+    const FwdPath path = choose_fwd_path(dtype);
+    const bool bf16 = dtype == RET_BF16;
+    if (linattn) chunk = linattn_chunk(dk, path, bf16);
+    if (path == FwdPath::kSegment) return plan_segments(bh, T, chunk, dk, dv, linattn, p);
+    return plan_slices(bh, T, chunk, dk, dv, linattn, bf16, p);
 }
 
 // Checks the caller's workspace against a plan (before anything is enqueued).
@@ -172,9 +222,21 @@ hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k
     return ret::launch_seg(sa, chunk, dk, dv, linattn, st);
 }
 
-// Internal chunk of the bf16 linear-attention path: 64 when dk = 128 (the
-// 128-token variant would spill registers), else 128.
-int linattn_chunk(int dk) { return dk == 128 ? 64 : 128; }
+// Launches the value-slice walk (and its segment-state kernel) with a checked
+// plan and workspace.
+hipError_t launch_slice_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
+                             const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
+                             int T, int dk, int dv, bool bf16, bool linattn, hipStream_t st) {
+    ret::WalkArgs a{};
+    a.q = q; a.k = k; a.v = v; a.out = out;
+    a.final_state = fst.final_state; a.init_state = fst.init_state;
+    a.init_z = fst.init_z; a.final_z = fst.final_z;
+    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * plan.nt); a.eps = eps;
+    a.G = plan.G; a.cps = plan.cps;
+    a.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+    if (log2g) memcpy(a.log2g, log2g, sizeof(a.log2g));
+    return ret::launch_walk(a, bf16, plan.chunk, dk, plan.nt, linattn, st);
+}
 
 }  // namespace
 
@@ -186,18 +248,16 @@ size_t retention_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
     if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
         (dv != 64 && dv != 128) || !dtype_size(dtype))
         return 0;
-    if (choose_fwd_path(dtype) != FwdPath::kSegment) return 0;
     SegPlan plan;
-    if (!plan_segments(static_cast<long long>(B) * H, T, chunk, dk, dv, false, &plan)) return 0;
+    if (!plan_fwd(static_cast<long long>(B) * H, T, chunk, dk, dv, false, dtype, &plan)) return 0;
     return plan.ws_bytes;
 }
 
 size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
     if (B <= 0 || H < 1 || T < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || !dtype_size(dtype))
         return 0;
-    if (choose_fwd_path(dtype) != FwdPath::kSegment) return 0;
     SegPlan plan;
-    if (!plan_segments(static_cast<long long>(B) * H, T, linattn_chunk(dk), dk, dv, true, &plan)) return 0;
+    if (!plan_fwd(static_cast<long long>(B) * H, T, 64, dk, dv, true, dtype, &plan)) return 0;
     return plan.ws_bytes;
 }
 
@@ -258,22 +318,17 @@ int ret_fwd_impl(const char* fn, const void* q, const void* k, const void* v, co
     FwdState fst;
     fst.init_state = initial_state;
     fst.final_state = final_state;
-    if (choose_fwd_path(dtype) == FwdPath::kSegment) {
-        SegPlan plan;
-        if (!plan_segments(bh, T, chunk, dk, dv, false, &plan))
-            return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
-        rc = check_workspace(fn, plan, workspace, ws_bytes,
-                             {rq, rk, rv, ro, final_state ? range("final_state", final_state, ns) : none, ri});
-        if (rc) return rc;
-        const hipError_t e = launch_segment_path(plan, q, k, v, out, fst, workspace, a.log2g, 0.f, B, H, T,
-                                                 chunk, dk, dv, false, st);
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-        return ok();
-    }
-    const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, chunk, dk);
-    a.q = q; a.k = k; a.v = v; a.out = out; a.final_state = final_state; a.init_state = initial_state;
-    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = 0.f;
-    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, chunk, dk, nt, false, st);
+    SegPlan plan;
+    if (!plan_fwd(bh, T, chunk, dk, dv, false, dtype, &plan))
+        return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    rc = check_workspace(fn, plan, workspace, ws_bytes,
+                         {rq, rk, rv, ro, final_state ? range("final_state", final_state, ns) : none, ri});
+    if (rc) return rc;
+    const hipError_t e =
+        plan.path == FwdPath::kSegment
+            ? launch_segment_path(plan, q, k, v, out, fst, workspace, a.log2g, 0.f, B, H, T, chunk, dk, dv, false, st)
+            : launch_slice_path(plan, q, k, v, out, fst, workspace, a.log2g, 0.f, B, H, T, dk, dv,
+                                dtype == RET_BF16, false, st);
     if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }
@@ -321,24 +376,17 @@ int lin_fwd_impl(const char* fn, const void* q, const void* k, const void* v, in
     fst.init_z = initial_z;
     fst.final_state = final_S;
     fst.final_z = final_z;
-    if (choose_fwd_path(dtype) == FwdPath::kSegment) {
-        SegPlan plan;
-        if (!plan_segments(bh, T, linattn_chunk(dk), dk, dv, true, &plan))
-            return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
-        const Range rfz = final_z ? range("final_z", final_z, nz) : none;
-        rc = check_workspace(fn, plan, workspace, ws_bytes, {rq, rk, rv, ro, riS, riz, rfS, rfz});
-        if (rc) return rc;
-        const hipError_t e = launch_segment_path(plan, q, k, v, out, fst, workspace, nullptr, eps, B, H, T,
-                                                 linattn_chunk(dk), dk, dv, true, st);
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-        return ok();
-    }
-    ret::WalkArgs a{};
-    const int nt = ret::choose_walk_nt(bh, dv, 256, dtype == RET_BF16, 128, dk);
-    a.q = q; a.k = k; a.v = v; a.out = out;
-    a.final_state = final_S; a.init_state = initial_S; a.init_z = initial_z; a.final_z = final_z;
-    a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * nt); a.eps = eps;
-    const hipError_t e = ret::launch_walk(a, dtype == RET_BF16, 128, dk, nt, true, st);
+    SegPlan plan;
+    if (!plan_fwd(bh, T, 64, dk, dv, true, dtype, &plan)) return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    const Range rfz = final_z ? range("final_z", final_z, nz) : none;
+    rc = check_workspace(fn, plan, workspace, ws_bytes, {rq, rk, rv, ro, riS, riz, rfS, rfz});
+    if (rc) return rc;
+    const hipError_t e =
+        plan.path == FwdPath::kSegment
+            ? launch_segment_path(plan, q, k, v, out, fst, workspace, nullptr, eps, B, H, T, plan.chunk, dk, dv,
+                                  true, st)
+            : launch_slice_path(plan, q, k, v, out, fst, workspace, nullptr, eps, B, H, T, dk, dv,
+                                dtype == RET_BF16, true, st);
     if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }

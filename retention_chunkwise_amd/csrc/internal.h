@@ -26,6 +26,10 @@ struct WalkArgs {
     int dv;              // full value width (the kernel handles one slice of it)
     int nslices;         // dv / (16 * NT)
     int xcd_remap;       // 1: spread (b, h) groups so their slices share an XCD
+    int G;               // segments per (b, h) (1: walk whole sequences); all but the last are full
+    int cps;             // chunks per segment
+    int seg_len;         // tokens per full segment (set by the launcher: cps * chunk)
+    float* ws;           // [B*H][G-1][dk*dv (+ dk)] fp32 segment states, row-major; unused when G == 1
     float eps;           // linear attention only
     float log2g[kMaxHeads];
 };
@@ -91,5 +95,14 @@ int choose_segments(long long bh, int nch, int target_groups, int min_cps, int m
 // Choice of value-slice width (in 16-column MFMA tiles) for the chunk walk:
 // the widest slice that still gives at least `target_groups` workgroups.
 int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk, int dk);
+
+// Widest value slice of the segmented walk whose workgroup fits in LDS (the
+// fewest recomputed Q K^T tiles); the segments provide the parallelism.
+int choose_walk_nt_wide(int dv, bool bf16, int chunk, int dk, bool linattn);
+bool walk_variant_fits(bool bf16, bool linattn, int chunk, int dk, int nt);
+bool walk_fits_ret_bf16(int chunk, int dk, int nt);
+bool walk_fits_ret_f32(int chunk, int dk, int nt);
+bool walk_fits_lin_bf16(int chunk, int dk, int nt);
+bool walk_fits_lin_f32(int chunk, int dk, int nt);
 
 }  // namespace ret

@@ -14,6 +14,19 @@ int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk
     return best;
 }
 
+bool walk_variant_fits(bool bf16, bool linattn, int chunk, int dk, int nt) {
+    if (bf16) return linattn ? walk_fits_lin_bf16(chunk, dk, nt) : walk_fits_ret_bf16(chunk, dk, nt);
+    return linattn ? walk_fits_lin_f32(chunk, dk, nt) : walk_fits_ret_f32(chunk, dk, nt);
+}
+
+int choose_walk_nt_wide(int dv, bool bf16, int chunk, int dk, bool linattn) {
+    // the fp32 128-token walk with dk = 128 runs out of registers beyond one tile per slice
+    if (!bf16 && chunk == 128 && dk == 128) return 1;
+    for (int nt = dv / 16; nt > 1; nt /= 2)
+        if (walk_variant_fits(bf16, linattn, chunk, dk, nt)) return nt;
+    return 1;
+}
+
 hipError_t launch_walk(const WalkArgs& a, bool bf16, int chunk, int dk, int nt, bool linattn,
                        hipStream_t stream) {
     if (bf16) {

@@ -15,11 +15,16 @@
 //   z_new = z + sum_j phi(k_j).
 //
 // Mapping onto the chip.  One workgroup (4 waves, 256 threads) owns one
-// (batch, head) pair and one slice of 16*NT value columns, and walks every
-// chunk of the sequence in order, keeping its slice of S in registers (fp32).
-// Value columns of S and O are independent, so slices need no communication;
-// each slice recomputes Q K^T for its chunk.  Slices of one (b, h) are placed
-// on the same XCD so their shared Q / K reads hit that XCD's L2.
+// (batch, head) pair, one segment of G consecutive runs of whole chunks and
+// one slice of 16*NT value columns, and walks the chunks of its segment in
+// order, keeping its slice of S in registers (fp32).  Value columns of S and
+// O are independent, so slices need no communication; each slice recomputes
+// Q K^T for its chunk.  Slices of one (b, h, segment) are placed on the same
+// XCD so their shared Q / K reads hit that XCD's L2.  The recurrence is
+// linear, so the state entering segment g is
+//   S_in(g) = gamma^(g L) S_0 + sum_{j<g} gamma^(L (g-1-j)) dS_j,
+// with L the segment length and dS_j = sum_{t in segment j}
+// gamma^(end_j - 1 - t) k_t v_t^T computed beforehand by slice_state_kernel.
 //
 // Per chunk, wave W owns query tiles {W, C/16-1-W} (16 rows each; one tile
 // when C = 64), which balances the causal triangle across waves.  The wave
@@ -116,7 +121,7 @@ struct QKTiles {
 template <bool BF16, int C, int DK, int NT, bool LIN, int W>
 __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, NT, LIN>& sm,
                                           const QKTiles<typename Cfg<BF16, C, DK, NT, LIN>::E>& qk,
-                                          const int bh, const int nbase, const float lg) {
+                                          const int bh, const int nbase, const int seg, const float lg) {
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
     constexpr int NI = Cf::NI, NS = Cf::NS, KSTR = Cf::KSTR, EPV = Cf::EPV;
@@ -155,16 +160,48 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
     for (int s = 0; s < NS; ++s) xi[s] = exp2f(static_cast<float>(its(s) * 16 + l16 + 1) * lg);
 
-    f32x4 sacc[SPW];  // S[16 kt + l16][nbase + 16 nt + 4g + r] of this wave's tiles
+    // ---- state entering the segment: S[16 kt + l16][nbase + 16 nt + 4g + r] of this wave's tiles
+    f32x4 sacc[SPW];
 #pragma unroll
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float lseg = static_cast<float>(a.seg_len) * lg;  // log2 of gamma^L
+    if (seg > 0) {
+        constexpr int ZW = LIN ? DK : 0;  // normaliser floats after each state slot
+        const long long slot = static_cast<long long>(DK) * DV + ZW;
+        const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + nbase;
+        for (int j = 0; j < seg; ++j) {
+            const float wj = exp2f(lseg * static_cast<float>(seg - 1 - j));
+#pragma unroll
+            for (int m = 0; m < SPW; ++m) {
+                const int qt = W + 4 * m;
+                const int nt = qt / KT, kt = qt % KT;
+                sacc[m] += wj * *reinterpret_cast<const f32x4*>(wsb + j * slot + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
+            }
+        }
+    }
     if (a.init_state) {
+        const float w0 = exp2f(lseg * static_cast<float>(seg));
         const float* si = a.init_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
             const int qt = W + 4 * m;
             const int nt = qt / KT, kt = qt % KT;
-            sacc[m] = *reinterpret_cast<const f32x4*>(si + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
+            sacc[m] += w0 * *reinterpret_cast<const f32x4*>(si + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
+        }
+    }
+    {
+        // operand copy for the first chunk: Sts[0][j][i] = S[i][nbase + j] (the
+        // first barrier of the first step orders these writes before any read)
+        E* st0 = sm.Sts[0];
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = W + 4 * m;
+            const int nt = qt / KT, kt = qt % KT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (BF16) st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16] = f2bf(sacc[m][r]);
+                else st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16] = sacc[m][r];
+            }
         }
     }
 
@@ -274,6 +311,8 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     };
 
     const int nch = (T + C - 1) / C;
+    const int c_begin = seg * a.cps;
+    const int c_end = (c_begin + a.cps < nch) ? c_begin + a.cps : nch;
 
     // One chunk.  B is the LDS buffer holding this chunk's Q / K (DMA path)
     // and the state-copy buffer the chunk reads; chunk c + 1 goes to 1 - B.
@@ -288,7 +327,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         // ops issued after them are the previous step's output stores (vector
         // memory ops complete in issue order).  Before the first step nothing
         // else is in flight, so wait for everything.
-        if (c == 0) wait_vmcnt<0>();
+        if (c == c_begin) wait_vmcnt<0>();
         else wait_vmcnt<STORES>();
         __syncthreads();  // loads landed everywhere; previous chunk's LDS reads done
 
@@ -357,7 +396,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         }
         __syncthreads();
 
-        if (c + 1 < nch) load_chunk(c + 1, std::integral_constant<int, NB>{});
+        if (c + 1 < c_end) load_chunk(c + 1, std::integral_constant<int, NB>{});
 
         // ---------------- Q operands of this wave's query tiles
         uint4 qb[NS][QU];
@@ -619,14 +658,14 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         }
     };
 
-    if (nch > 0) load_chunk(0, std::integral_constant<int, 0>{});
-    for (int c = 0; c < nch; c += 2) {
+    if (c_begin < c_end) load_chunk(c_begin, std::integral_constant<int, 0>{});
+    for (int c = c_begin; c < c_end; c += 2) {
         step(c, std::integral_constant<int, 0>{});
-        if (c + 1 < nch) step(c + 1, std::integral_constant<int, 1>{});
+        if (c + 1 < c_end) step(c + 1, std::integral_constant<int, 1>{});
     }
 
-    // ---------------- final state [dk][dv] fp32
-    if (a.final_state) {
+    // ---------------- final state [dk][dv] fp32 (the last segment ends the sequence)
+    if (a.final_state && seg == a.G - 1) {
         float* fs = a.final_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
@@ -652,13 +691,15 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
     __shared__ __attribute__((aligned(16))) E sv1[VN];
     const QKTiles<E> qk{{sq0, sq1}, {sk0, sk1}, {sv0, sv1}};
 
-    // workgroup -> (b*H + h, value slice); slices of one (b, h) share an XCD
+    // workgroup -> ((b*H + h) * G + segment, value slice); the slices of one
+    // (b, h, segment) share an XCD
     int L = blockIdx.x;
     if (a.xcd_remap) {
         const int per = gridDim.x >> 3;
         L = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     }
-    const int bh = L / a.nslices;
+    const int bhs = L / a.nslices;
+    const int bh = bhs / a.G, seg = bhs % a.G;
     const int nbase = (L % a.nslices) * Cf::DVS;
     const int h = bh % a.H;
     const float lg = LIN ? 0.f : a.log2g[h];
@@ -666,33 +707,110 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
     const int tid = threadIdx.x;
     for (int m = tid; m < Cf::DEC; m += kThreads)
         sm.dec[m] = (m < 16) ? 0.f : exp2f(static_cast<float>(m - 16) * lg);
-    // operand copy of the state entering token 0: Sts[j][i] = S[i][nbase + j]
-    const float* si = a.init_state ? a.init_state + static_cast<long long>(bh) * DK * a.dv + nbase : nullptr;
-    for (int m = tid; m < Cf::DVS * Cf::KSTR; m += kThreads) {
-        const int j = m / Cf::KSTR, i = m % Cf::KSTR;
-        const float x = (si && i < DK) ? si[static_cast<long long>(i) * a.dv + j] : 0.f;
-        if constexpr (BF16) sm.Sts[0][m] = f2bf(x);
-        else sm.Sts[0][m] = x;
+    if constexpr (LIN) {
+        // normaliser entering the segment: z_0 + the earlier segments' sums (gamma = 1)
+        const long long slot = static_cast<long long>(DK) * a.dv + DK;
+        const float* zw = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + static_cast<long long>(DK) * a.dv;
+        for (int m = tid; m < DK; m += kThreads) {
+            float z = a.init_z ? a.init_z[static_cast<long long>(bh) * DK + m] : 0.f;
+            for (int j = 0; j < seg; ++j) z += zw[j * slot + m];
+            sm.zs[0][m] = z;
+        }
     }
-    if constexpr (LIN)
-        for (int m = tid; m < DK; m += kThreads)
-            sm.zs[0][m] = a.init_z ? a.init_z[static_cast<long long>(bh) * DK + m] : 0.f;
-    // (the first barrier inside walk_body orders these writes before any read)
+    // (the first barrier inside walk_body orders these writes, and the state
+    // copy walk_body writes, before any read)
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     switch (wave) {
-        case 0: walk_body<BF16, C, DK, NT, LIN, 0>(a, sm, qk, bh, nbase, lg); break;
-        case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, qk, bh, nbase, lg); break;
-        case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, qk, bh, nbase, lg); break;
-        default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, qk, bh, nbase, lg); break;
+        case 0: walk_body<BF16, C, DK, NT, LIN, 0>(a, sm, qk, bh, nbase, seg, lg); break;
+        case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, qk, bh, nbase, seg, lg); break;
+        case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, qk, bh, nbase, seg, lg); break;
+        default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, qk, bh, nbase, seg, lg); break;
     }
     if constexpr (LIN) {
-        // the normaliser after the last chunk sits in zs[nch % 2]; every slice
-        // of a (b, h) holds the same z, slice 0 writes it
-        if (a.final_z && nbase == 0) {
+        // the normaliser after the segment's last chunk sits in zs[chunks % 2];
+        // every slice holds the same z, slice 0 of the last segment writes it
+        if (a.final_z && nbase == 0 && seg == a.G - 1) {
             __syncthreads();
             const int nch = (a.T + C - 1) / C;
-            for (int m = tid; m < DK; m += kThreads) a.final_z[static_cast<long long>(bh) * DK + m] = sm.zs[nch & 1][m];
+            const int c_begin = seg * a.cps;
+            const int n = (c_begin < nch) ? nch - c_begin : 0;
+            for (int m = tid; m < DK; m += kThreads) a.final_z[static_cast<long long>(bh) * DK + m] = sm.zs[n & 1][m];
+        }
+    }
+}
+
+// Segment contributions for the segmented walk.  Workgroup (b*H + h, j), for
+// each full segment j < G - 1, writes
+//   dS_j = sum_{t in segment j} gamma^(end_j - 1 - t) k_t v_t^T
+// row-major [dk][dv] to workspace slot (b*H + h, j); for linear attention k_t
+// is phi(k_t), gamma = 1, and z_j = sum phi(k_t) follows the state.  Wave w
+// owns key-feature tiles {w, w + 4} and every value tile; each fp32 MFMA
+// (16x16x4) contracts over 4 consecutive tokens: A = zeta K^T, B = V, both
+// read straight from HBM / L2 (one 4- or 2-byte element per lane per tile).
+template <bool BF16, int DK, int DV, bool LIN>
+__global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a) {
+    using E = typename std::conditional<BF16, unsigned short, float>::type;
+    constexpr int KT = DK / 16, NV = DV / 16, MW = (KT + 3) / 4, U = 4;  // U: token quads per batch
+    const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, g = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh = blockIdx.x / (a.G - 1), seg = blockIdx.x % (a.G - 1);
+    const float lg = LIN ? 0.f : a.log2g[bh % a.H];
+    const long long t0 = static_cast<long long>(seg) * a.seg_len;
+    const E* kh = static_cast<const E*>(a.k) + (static_cast<long long>(bh) * a.T + t0) * DK;
+    const E* vh = static_cast<const E*>(a.v) + (static_cast<long long>(bh) * a.T + t0) * DV;
+    auto ld = [](const E* p) -> float {
+        if constexpr (BF16) return bf2f(*p);
+        else return *p;
+    };
+
+    f32x4 acc[MW][NV];
+    float zs[MW];
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi) {
+        zs[mi] = 0.f;
+#pragma unroll
+        for (int n = 0; n < NV; ++n) acc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // every full segment is a whole number of chunks, so seg_len % (4 U) == 0
+    for (int tb = 0; tb < a.seg_len; tb += 4 * U) {
+        float ka[U][MW], vb[U][NV];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + 4 * u + g;  // token of this lane's contraction slot
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+                ka[u][mi] = (w + 4 * mi < KT) ? ld(kh + static_cast<long long>(t) * DK + 16 * (w + 4 * mi) + l16) : 0.f;
+#pragma unroll
+            for (int n = 0; n < NV; ++n) vb[u][n] = ld(vh + static_cast<long long>(t) * DV + 16 * n + l16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + 4 * u + g;
+            const float zeta = LIN ? 1.f : exp2f(static_cast<float>(a.seg_len - 1 - t) * lg);
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi) {
+                const float x = LIN ? phi_elu1(ka[u][mi]) : ka[u][mi] * zeta;
+                if constexpr (LIN) zs[mi] += x;
+#pragma unroll
+                for (int n = 0; n < NV; ++n) acc[mi][n] = mfma_f32(x, vb[u][n], acc[mi][n]);
+            }
+        }
+    }
+    const long long slot = static_cast<long long>(DK) * DV + (LIN ? DK : 0);
+    float* out = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * slot;
+#pragma unroll
+    for (int mi = 0; mi < MW; ++mi) {
+        const int m = w + 4 * mi;
+        if (m < KT) {
+#pragma unroll
+            for (int n = 0; n < NV; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) out[(16 * m + 4 * g + r) * DV + 16 * n + l16] = acc[mi][n][r];
+            if constexpr (LIN) {
+                const float z = sum_over_groups(zs[mi]);
+                if (g == 0) out[DK * DV + 16 * m + l16] = z;
+            }
         }
     }
 }
@@ -712,11 +830,23 @@ hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
     if constexpr (!fits<BF16, C, DK, NT, LIN>()) {
         return hipErrorInvalidConfiguration;
     } else {
-    const long long groups = static_cast<long long>(a.B) * a.H * a.nslices;
+    const long long groups = static_cast<long long>(a.B) * a.H * a.nslices * a.G;
     if (groups <= 0) return hipSuccess;
     if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
     WalkArgs args = a;
     args.xcd_remap = (groups % 8 == 0) ? 1 : 0;
+    args.seg_len = a.cps * C;
+    if (a.G > 1) {
+        const long long sgroups = static_cast<long long>(a.B) * a.H * (a.G - 1);
+        const int dv = a.dv;
+#define RET_SLICE_STATE(DV_)                                                                             \
+        if (dv == DV_) hipLaunchKernelGGL((slice_state_kernel<BF16, DK, DV_, LIN>),                      \
+                                          dim3(static_cast<unsigned>(sgroups)), dim3(kThreads), 0, stream, args);
+        RET_SLICE_STATE(64)
+        RET_SLICE_STATE(128)
+#undef RET_SLICE_STATE
+        if (dv != 64 && dv != 128) return hipErrorInvalidValue;
+    }
     hipLaunchKernelGGL((walk_kernel<BF16, C, DK, NT, LIN>), dim3(static_cast<unsigned>(groups)),
                        dim3(kThreads), 0, stream, args);
     return hipGetLastError();
@@ -736,8 +866,41 @@ hipError_t launch_variant(const WalkArgs& a, int chunk, int dk, int nt, hipStrea
     RET_WALK_CASE(128, 64, 2)
     RET_WALK_CASE(128, 128, 1)
     RET_WALK_CASE(128, 128, 2)
+    if constexpr (!BF16) {
+        RET_WALK_CASE(64, 64, 4)
+        RET_WALK_CASE(64, 64, 8)
+        RET_WALK_CASE(64, 128, 4)
+        RET_WALK_CASE(64, 128, 8)
+        RET_WALK_CASE(128, 64, 4)
+        RET_WALK_CASE(128, 128, 4)
+    }
 #undef RET_WALK_CASE
     return hipErrorInvalidValue;
+}
+
+// Whether the (chunk, dk, NT) variant fits in LDS (and is instantiated).
+template <bool BF16, bool LIN>
+bool variant_fits(int chunk, int dk, int nt) {
+#define RET_WALK_FITS(C_, DK_, NT_) \
+    if (chunk == C_ && dk == DK_ && nt == NT_) return fits<BF16, C_, DK_, NT_, LIN>();
+    RET_WALK_FITS(64, 64, 1)
+    RET_WALK_FITS(64, 64, 2)
+    RET_WALK_FITS(64, 128, 1)
+    RET_WALK_FITS(64, 128, 2)
+    RET_WALK_FITS(128, 64, 1)
+    RET_WALK_FITS(128, 64, 2)
+    RET_WALK_FITS(128, 128, 1)
+    RET_WALK_FITS(128, 128, 2)
+    if constexpr (!BF16) {
+        RET_WALK_FITS(64, 64, 4)
+        RET_WALK_FITS(64, 64, 8)
+        RET_WALK_FITS(64, 128, 4)
+        RET_WALK_FITS(64, 128, 8)
+        RET_WALK_FITS(128, 64, 4)
+        RET_WALK_FITS(128, 128, 4)
+    }
+#undef RET_WALK_FITS
+    return false;
 }
 
 }  // namespace walk

@@ -7,4 +7,6 @@ hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hip
     return walk::launch_variant<false, true>(a, chunk, dk, nt, stream);
 }
 
+bool walk_fits_lin_f32(int chunk, int dk, int nt) { return walk::variant_fits<false, true>(chunk, dk, nt); }
+
 }  // namespace ret

@@ -161,8 +161,9 @@ def test_binding_fails_loudly_without_gpu_tensors():
 # ---------------------------------------------------------------- workspace
 def test_workspace_sizes():
     lib = _lib()
-    # fp32 walks whole sequences: no workspace
-    assert lib.retention_fwd_workspace_bytes(1, 2, 4096, 64, 64, 64, rc.RET_F32) == 0
+    # fp32 walks segments too: (G - 1) states per (b, h), no pieces
+    n32 = lib.retention_fwd_workspace_bytes(1, 2, 4096, 64, 64, 64, rc.RET_F32)
+    assert n32 > 0 and n32 % (64 * 64 * 4 * 2) == 0
     # one chunk: one segment, no workspace
     assert lib.retention_fwd_workspace_bytes(1, 2, 100, 128, 128, 128, rc.RET_BF16) == 0
     # long bf16 sequences are split: (G - 1) * pieces fp32 states per (b, h)

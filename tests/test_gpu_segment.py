@@ -23,7 +23,7 @@ TOL = 2e-2
 
 
 def _inputs(seed, **over):
-    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(dtype="bf16", **over)
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(**{"dtype": "bf16", **over})
     return w, wl.make_inputs(w, seed)
 
 
@@ -180,3 +180,44 @@ def test_caller_workspace_contents_do_not_matter(monkeypatch):
     l2 = rc.linear_attn_fwd(lq, lk, lv, workspace=lws)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------- segmented value-slice walk
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, 2), (1333, 5), (700, 16)])
+def test_slice_segments_full(dtype, chunk, dk, dv, T, G, monkeypatch):
+    """The value-slice walk split into G segments (fp32 picks G by itself;
+    bf16 only when forced), against the oracle in full."""
+    w, inp = _inputs(seed=18, B=2, H=2, T=T, dk=dk, dv=dv, chunk=chunk, scale=1.0 / np.sqrt(dk), dtype=dtype)
+    out, fs = _run(inp, chunk, monkeypatch, path="slice", segments=G)
+    tol = 1e-4 if dtype == "f32" else TOL
+    ref, ref_s = oracle.retention_recurrent(inp["q"], inp["k"], inp["v"], inp["gamma"], nthreads=8)
+    e_o, e_s = oracle.rel_frobenius(out, ref), oracle.rel_frobenius(fs, ref_s)
+    print(f"[parity] slice {dtype} C={chunk} dk={dk} dv={dv} T={T} G={G}: out {e_o:.3e} state {e_s:.3e}", flush=True)
+    assert e_o <= tol and e_s <= tol
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, 3), (300, 16)])
+def test_slice_segments_linattn(dtype, dk, dv, T, G, monkeypatch):
+    w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype)
+    inp = wl.make_inputs(w, 25)
+    out = _run_lin(inp, monkeypatch, path="slice", segments=G)
+    ref, _, _ = oracle.linattn_recurrent(inp["q"], inp["k"], inp["v"], nthreads=8)
+    e = oracle.rel_frobenius(out, ref)
+    tol = 1e-4 if dtype == "f32" else TOL
+    print(f"[parity] slice linattn {dtype} dk={dk} dv={dv} T={T} G={G}: {e:.3e}", flush=True)
+    assert e <= tol and np.isfinite(out).all()
+
+
+def test_f32_auto_segments_match_one_segment(monkeypatch):
+    """fp32 automatic segments against the forced single-segment walk."""
+    w, inp = _inputs(seed=19, B=4, H=8, T=2048, dk=64, dv=64, chunk=64, scale=1.0 / 8, dtype="f32")
+    o_auto, s_auto = _run(inp, 64, monkeypatch, path="slice", segments=None)
+    o_one, s_one = _run(inp, 64, monkeypatch, path="slice", segments=1)
+    e_o, e_s = oracle.rel_frobenius(o_auto, o_one), oracle.rel_frobenius(s_auto, s_one)
+    print(f"[parity] f32 auto vs one segment: out {e_o:.3e} state {e_s:.3e}", flush=True)
+    assert e_o <= 1e-5 and e_s <= 1e-5
