@@ -75,9 +75,10 @@ int check_gamma(const char* fn, const float* gamma, int H, float* log2g) {
 // ---- forward path selection
 //
 // RET_FWD_PATH = "slice" | "segment" forces a forward path (any other value
-// or unset: automatic); RET_FWD_SEGMENTS = n forces the segment count of the
-// segment path.  Both exist for tests and tuning; they never change results
-// beyond rounding.
+// or unset: automatic); RET_FWD_SEGMENTS = n forces the segment count;
+// RET_WALK_NT = n narrows the value slices of the slice path to n 16-column
+// tiles.  They exist for tests and tuning and never change results beyond
+// rounding.
 enum class FwdPath { kSlice, kSegment };
 
 int env_int(const char* name) {
@@ -137,6 +138,9 @@ bool plan_slices(long long bh, int T, int chunk, int dk, int dv, bool linattn, b
     const bool forced = forced_segments(nch, p);
     if (!bf16 || forced) {
         p->nt = ret::choose_walk_nt_wide(dv, bf16, chunk, dk, linattn);
+        const int want = env_int("RET_WALK_NT");  // tuning: a narrower slice, if that variant fits
+        if (want > 0 && want < p->nt && (dv / 16) % want == 0 && ret::walk_variant_fits(bf16, linattn, chunk, dk, want))
+            p->nt = want;
         if (!forced) p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, 256, 2, 16, &p->cps);
     } else {
         p->nt = ret::choose_walk_nt(bh, dv, 256, bf16, chunk, dk);

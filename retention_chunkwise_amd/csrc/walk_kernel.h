@@ -64,7 +64,7 @@ struct Cfg {
     static constexpr int KSTR = DK + EPV;             // padded row stride (fp32 K, state copy)
     static constexpr int VSTR = DVS;                  // row stride of the V slice copies
     static constexpr int KT = DK / 16;                // 16-wide key tiles
-    static constexpr int SPW = NT * KT / 4;           // state tiles per wave
+    static constexpr int NTILE = NT * KT;             // 16x16 state tiles of a slice
     static constexpr int KU = C * DK * ESZ / 16 / kThreads;  // 16-B units of a Q / K chunk per thread
     static constexpr int RU = DK * ESZ / 16;          // 16-B units (slots) per Q / K row
     static constexpr int RB = DK * ESZ;               // bytes per Q / K row
@@ -84,6 +84,38 @@ struct Cfg {
     static_assert(NT * KT % 4 == 0, "state tiles must split over 4 waves");
     static_assert(C * DK * ESZ / 16 % kThreads == 0, "Q/K staging split");
     static_assert(!DMA || RU == 8 || RU == 16, "swizzle assumes 8 or 16 slots per row");
+};
+
+// Split of the NT * KT state tiles over the 4 waves.  Wave W's query tiles
+// cost it (tiles of Q K^T) + (tiles of P V) + (inter-chunk tiles); with
+// 64-token chunks wave W owns query tile W alone, so that work grows with W,
+// and the state tiles (C contraction steps each) go greedily to the least
+// loaded wave until the loads even out (7/5/3/1 tiles for dk = dv = 64).
+// Each wave's tiles are a contiguous run in (value tile, key tile) order.
+template <int C, int DK, int NT>
+struct StateSplit {
+    static constexpr int NI = C / 16, KT = DK / 16;
+    static constexpr int qtiles(int w) { return (NI == 8) ? (w + 1) + (NI - w) : (w + 1); }  // key tiles seen
+    static constexpr int load(int w) {
+        return qtiles(w) * DK + NT * qtiles(w) * 16 + ((NI == 8) ? 2 : 1) * NT * DK;
+    }
+    static constexpr int count(int w) {
+        int ld[4] = {load(0), load(1), load(2), load(3)};
+        int cnt[4] = {0, 0, 0, 0};
+        for (int t = 0; t < NT * KT; ++t) {
+            int b = 0;
+            for (int i = 1; i < 4; ++i)
+                if (ld[i] < ld[b]) b = i;
+            ld[b] += C;
+            ++cnt[b];
+        }
+        return cnt[w];
+    }
+    static constexpr int start(int w) {
+        int s = 0;
+        for (int i = 0; i < w; ++i) s += count(i);
+        return s;
+    }
 };
 
 // Byte offset of 16-byte slot `col16` of row `r` in a swizzled Q / K tile.
@@ -125,7 +157,11 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     using Cf = Cfg<BF16, C, DK, NT, LIN>;
     using E = typename Cf::E;
     constexpr int NI = Cf::NI, NS = Cf::NS, KSTR = Cf::KSTR, EPV = Cf::EPV;
-    constexpr int VSTR = Cf::VSTR, KT = Cf::KT, SPW = Cf::SPW, KU = Cf::KU, RU = Cf::RU;
+    constexpr int VSTR = Cf::VSTR, KT = Cf::KT, KU = Cf::KU, RU = Cf::RU;
+    constexpr int SPW = StateSplit<C, DK, NT>::count(W);  // state tiles of this wave
+    constexpr int TS = StateSplit<C, DK, NT>::start(W);   // its first tile
+    static_assert(StateSplit<C, DK, NT>::start(3) + StateSplit<C, DK, NT>::count(3) == Cf::NTILE,
+                  "every state tile has one owner");
     constexpr int VRU = Cf::VRU, VUT = Cf::VUT, VPT = Cf::VPT, QU = Cf::QU, ESZ = Cf::ESZ;
     constexpr bool DMA = Cf::DMA;
     constexpr int IT0 = W;                                // query tiles of this wave
@@ -161,7 +197,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     for (int s = 0; s < NS; ++s) xi[s] = exp2f(static_cast<float>(its(s) * 16 + l16 + 1) * lg);
 
     // ---- state entering the segment: S[16 kt + l16][nbase + 16 nt + 4g + r] of this wave's tiles
-    f32x4 sacc[SPW];
+    f32x4 sacc[SPW > 0 ? SPW : 1];
 #pragma unroll
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float lseg = static_cast<float>(a.seg_len) * lg;  // log2 of gamma^L
@@ -173,7 +209,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             const float wj = exp2f(lseg * static_cast<float>(seg - 1 - j));
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
-                const int qt = W + 4 * m;
+                const int qt = TS + m;
                 const int nt = qt / KT, kt = qt % KT;
                 sacc[m] += wj * *reinterpret_cast<const f32x4*>(wsb + j * slot + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
             }
@@ -184,7 +220,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         const float* si = a.init_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m;
+            const int qt = TS + m;
             const int nt = qt / KT, kt = qt % KT;
             sacc[m] += w0 * *reinterpret_cast<const f32x4*>(si + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
         }
@@ -195,7 +231,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         E* st0 = sm.Sts[0];
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m;
+            const int qt = TS + m;
             const int nt = qt / KT, kt = qt % KT;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -453,8 +489,8 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         // Independent of the Q K^T tiles, so it is issued here, where its MFMAs
         // overlap the decay arithmetic below.  The per-tile accumulation chains
         // are interleaved (token blocks outer, tiles inner).
-        f32x4 snew[SPW];
-        float zsum[SPW];
+        f32x4 snew[SPW > 0 ? SPW : 1];
+        float zsum[SPW > 0 ? SPW : 1];
         {
             const float gc = sm.dec[16 + clen];
 #pragma unroll
@@ -467,7 +503,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                 for (int js = 0; js < C / 32; ++js) {
 #pragma unroll
                     for (int m = 0; m < SPW; ++m) {
-                        const int qt = W + 4 * m;
+                        const int qt = TS + m;
                         const int nt = qt / KT, kt = qt % KT;
                         // A = (zeta V)^T, B = K: tokens 32js + 4g + {0..3}, 32js + 16 + 4g + {0..3}
                         const E* v0 = &sm.Vz[(32 * js + 4 * g + lq) * VSTR + nt * 16 + 4 * lr];
@@ -490,7 +526,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                     for (int r = 0; r < 4; ++r) {
 #pragma unroll
                         for (int m = 0; m < SPW; ++m) {
-                            const int qt = W + 4 * m;
+                            const int qt = TS + m;
                             const int nt = qt / KT, kt = qt % KT;
                             const float av = sm.Vz[(jt * 16 + 4 * g + r) * VSTR + nt * 16 + l16];
                             const float b = sm.Ks[(jt * 16 + 4 * g + r) * KSTR + kt * 16 + l16];
@@ -641,7 +677,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             E* stn = sm.Sts[NB];
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
-                const int qt = W + 4 * m;
+                const int qt = TS + m;
                 const int nt = qt / KT, kt = qt % KT;
                 const int kcol = kt * 16 + l16;
                 sacc[m] = snew[m];
@@ -669,7 +705,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         float* fs = a.final_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m;
+            const int qt = TS + m;
             const int nt = qt / KT, kt = qt % KT;
             *reinterpret_cast<f32x4*>(fs + (kt * 16 + l16) * DV + nt * 16 + 4 * g) = sacc[m];
         }
@@ -751,17 +787,43 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
 template <bool BF16, int DK, int DV, bool LIN>
 __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a) {
     using E = typename std::conditional<BF16, unsigned short, float>::type;
-    constexpr int KT = DK / 16, NV = DV / 16, MW = (KT + 3) / 4, U = 4;  // U: token quads per batch
+    constexpr int KT = DK / 16, NV = DV / 16, MW = KT / 4, ESZ = sizeof(E);
+    static_assert(KT % 4 == 0, "every wave owns KT / 4 key-feature tiles");
+    // token quads per batch (64 or 32 tokens); the next batch's loads stay in flight
+    constexpr int U = (MW + NV <= 5) ? 16 : 8;
     const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, g = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int bh = blockIdx.x / (a.G - 1), seg = blockIdx.x % (a.G - 1);
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const long long t0 = static_cast<long long>(seg) * a.seg_len;
-    const E* kh = static_cast<const E*>(a.k) + (static_cast<long long>(bh) * a.T + t0) * DK;
-    const E* vh = static_cast<const E*>(a.v) + (static_cast<long long>(bh) * a.T + t0) * DV;
-    auto ld = [](const E* p) -> float {
-        if constexpr (BF16) return bf2f(*p);
-        else return *p;
+    // range-checked resources over exactly this segment: the prefetch past its
+    // last batch reads zeros, so every load is unconditional
+    const auto rk = make_rsrc(static_cast<const E*>(a.k) + (static_cast<long long>(bh) * a.T + t0) * DK,
+                              a.seg_len * DK * ESZ);
+    const auto rv = make_rsrc(static_cast<const E*>(a.v) + (static_cast<long long>(bh) * a.T + t0) * DV,
+                              a.seg_len * DV * ESZ);
+    auto ld = [](__amdgpu_buffer_rsrc_t r, int elem) -> float {
+        if constexpr (BF16) {
+            const unsigned short b = __builtin_amdgcn_raw_buffer_load_b16(r, elem * 2, 0, 0);
+            return __uint_as_float(static_cast<unsigned>(b) << 16);
+        } else {
+            return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, elem * 4, 0, 0));
+        }
+    };
+    // this lane's elements of the 64-token batch starting at token tb:
+    // token tb + 4u + g, key features 16 (w + 4 mi) + l16, value features 16 n + l16
+    float ka[2][U][MW], vb[2][U][NV];
+    auto load = [&](int tb, auto bufc) {
+        constexpr int b = decltype(bufc)::value;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + 4 * u + g;
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+                ka[b][u][mi] = ld(rk, t * DK + 16 * (w + 4 * mi) + l16);
+#pragma unroll
+            for (int n = 0; n < NV; ++n) vb[b][u][n] = ld(rv, t * DV + 16 * n + l16);
+        }
     };
 
     f32x4 acc[MW][NV];
@@ -772,45 +834,48 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
 #pragma unroll
         for (int n = 0; n < NV; ++n) acc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // every full segment is a whole number of chunks, so seg_len % (4 U) == 0
-    for (int tb = 0; tb < a.seg_len; tb += 4 * U) {
-        float ka[U][MW], vb[U][NV];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int t = tb + 4 * u + g;  // token of this lane's contraction slot
-#pragma unroll
-            for (int mi = 0; mi < MW; ++mi)
-                ka[u][mi] = (w + 4 * mi < KT) ? ld(kh + static_cast<long long>(t) * DK + 16 * (w + 4 * mi) + l16) : 0.f;
-#pragma unroll
-            for (int n = 0; n < NV; ++n) vb[u][n] = ld(vh + static_cast<long long>(t) * DV + 16 * n + l16);
-        }
+    // A batch past the segment (at most one, when the batch count is odd) holds
+    // zeros and gets zero weights: it adds nothing, phi(0) included.
+    auto compute = [&](int tb, auto bufc) {
+        constexpr int b = decltype(bufc)::value;
+        const bool valid = tb < a.seg_len;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = tb + 4 * u + g;
-            const float zeta = LIN ? 1.f : exp2f(static_cast<float>(a.seg_len - 1 - t) * lg);
+            const float zeta = valid ? (LIN ? 1.f : exp2f(static_cast<float>(a.seg_len - 1 - t) * lg)) : 0.f;
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi) {
-                const float x = LIN ? phi_elu1(ka[u][mi]) : ka[u][mi] * zeta;
+                const float x = (LIN ? phi_elu1(ka[b][u][mi]) : ka[b][u][mi]) * zeta;
                 if constexpr (LIN) zs[mi] += x;
 #pragma unroll
-                for (int n = 0; n < NV; ++n) acc[mi][n] = mfma_f32(x, vb[u][n], acc[mi][n]);
+                for (int n = 0; n < NV; ++n) acc[mi][n] = mfma_f32(x, vb[b][u][n], acc[mi][n]);
             }
         }
+    };
+    // every full segment is a whole number of 64-token chunks, so of batches
+    // (the empty asm statements keep the scheduler from sinking a prefetch
+    // below the MFMAs it is meant to overlap)
+    load(0, std::integral_constant<int, 0>{});
+    for (int tb = 0; tb < a.seg_len; tb += 8 * U) {
+        load(tb + 4 * U, std::integral_constant<int, 1>{});
+        asm volatile("" ::: "memory");
+        compute(tb, std::integral_constant<int, 0>{});
+        load(tb + 8 * U, std::integral_constant<int, 0>{});
+        asm volatile("" ::: "memory");
+        compute(tb + 4 * U, std::integral_constant<int, 1>{});
     }
     const long long slot = static_cast<long long>(DK) * DV + (LIN ? DK : 0);
     float* out = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * slot;
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi) {
         const int m = w + 4 * mi;
-        if (m < KT) {
 #pragma unroll
-            for (int n = 0; n < NV; ++n)
+        for (int n = 0; n < NV; ++n)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) out[(16 * m + 4 * g + r) * DV + 16 * n + l16] = acc[mi][n][r];
-            if constexpr (LIN) {
-                const float z = sum_over_groups(zs[mi]);
-                if (g == 0) out[DK * DV + 16 * m + l16] = z;
-            }
+            for (int r = 0; r < 4; ++r) out[(16 * m + 4 * g + r) * DV + 16 * n + l16] = acc[mi][n][r];
+        if constexpr (LIN) {
+            const float z = sum_over_groups(zs[mi]);
+            if (g == 0) out[DK * DV + 16 * m + l16] = z;
         }
     }
 }
