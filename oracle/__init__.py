@@ -101,11 +101,13 @@ def _bind(lib):
                                             _l, _l, _D]
     lib.oracle_linattn_rows.argtypes = [_D, _D, _D, ctypes.c_double, _l, _l, _l, _l, _l,
                                         _L, _l, _D, ctypes.c_int]
+    lib.oracle_retention_bwd.argtypes = [_D, _D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _D,
+                                         ctypes.c_int]
     lib.oracle_threads_used.argtypes = [ctypes.c_int]
     for name in ("oracle_retention_recurrent", "oracle_retention_parallel",
                  "oracle_retention_rows", "oracle_retention_chunkwise",
                  "oracle_decode_steps", "oracle_linattn_recurrent",
-                 "oracle_linattn_decode_steps",
+                 "oracle_linattn_decode_steps", "oracle_retention_bwd",
                  "oracle_linattn_parallel", "oracle_linattn_rows",
                  "oracle_threads_used"):
         getattr(lib, name).restype = ctypes.c_int
@@ -219,6 +221,25 @@ def decode_steps(q, k, v, gamma, state, nsteps: int = 1, nthreads: int = 1):
                                       dk, dv, int(nsteps), int(nthreads)),
            "oracle_decode_steps")
     return out, S
+
+
+def retention_bwd(q, k, v, gamma, dout, nthreads: int = 1):
+    """Gradients (dq, dk, dv) of retention from a zero state, given dout,
+    as cumulative sums forward (queries) and backward (keys, values) in time
+    ("Linear attention" page, "Decoding, training, and what each costs")."""
+    q, k, v, g, do = _f64(q), _f64(k), _f64(v), _f64(gamma).reshape(-1), _f64(dout)
+    B, H, T, dk, dv = _shape4(q, k, v)
+    if do.shape != (B, H, T, dv):
+        raise ValueError("dout must be [B,H,T,dv]")
+    if g.shape != (H,):
+        raise ValueError("gamma must have H entries")
+    dq = np.zeros((B, H, T, dk))
+    dkk = np.zeros((B, H, T, dk))
+    dvv = np.zeros((B, H, T, dv))
+    _check(load().oracle_retention_bwd(_p(q), _p(k), _p(v), _p(g), _p(do), B, H, T, dk, dv,
+                                       _p(dq), _p(dkk), _p(dvv), int(nthreads)),
+           "oracle_retention_bwd")
+    return dq, dkk, dvv
 
 
 def linattn_recurrent(q, k, v, eps: float = ELU1_EPS, init_S=None, init_z=None,

@@ -290,6 +290,80 @@ int oracle_decode_steps(const double *q, const double *k, const double *v,
 }
 
 /*
+ * Gradient of retention (zero initial state) with respect to q, k and v, given
+ * dout = dL/dout for a scalar loss L.
+ *   [LA] section "Decoding, training, and what each costs": the gradients of
+ *        the causal recurrence are cumulative sums as well, running forward in
+ *        time for the queries and backward in time for the keys and values,
+ *        so no per-token state is stored.
+ * For the retention recurrence S_t = gamma S_{t-1} + k_t v_t^T, o_t = q_t S_t
+ * ([RetNet] "Recurrent Representation") these sums are
+ *   dq_t = S_t do_t                          (S_t: the forward state after token t)
+ *   U_t  = gamma U_{t+1} + q_t do_t^T,  U_T = 0   (dk x dv, backward in time)
+ *   dk_t = U_t v_t,   dv_t = U_t^T k_t
+ * dq, dk: [B][H][T][dk], dv: [B][H][T][dv].
+ */
+int oracle_retention_bwd(const double *q, const double *k, const double *v,
+                         const double *gamma, const double *dout, long B, long H,
+                         long T, long dk, long dv, double *dq, double *dkk,
+                         double *dvv, int nthreads)
+{
+    if (!q || !k || !v || !gamma || !dout || !dq || !dkk || !dvv || B < 0 || H <= 0 ||
+        T < 0 || dk <= 0 || dv <= 0)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for num_threads(oracle_threads(nthreads)) schedule(dynamic, 1)
+    for (long bh = 0; bh < B * H; ++bh) {
+        const double g = gamma[bh % H];
+        double *Sf = (double *)calloc((size_t)(dk * dv), sizeof(double));
+        double *U = (double *)calloc((size_t)(dk * dv), sizeof(double));
+        if (!Sf || !U) {
+            err = ORACLE_ERR_NOMEM;
+            free(Sf); free(U);
+            continue;
+        }
+        /* forward in time: the query gradients */
+        for (long t = 0; t < T; ++t) {
+            const double *kt = k + (bh * T + t) * dk, *vt = v + (bh * T + t) * dv;
+            const double *dot = dout + (bh * T + t) * dv;
+            double *dqt = dq + (bh * T + t) * dk;
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    Sf[i * dv + j] = g * Sf[i * dv + j] + kt[i] * vt[j];
+            for (long i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < dv; ++j)
+                    acc += Sf[i * dv + j] * dot[j];
+                dqt[i] = acc;
+            }
+        }
+        /* backward in time: the key and value gradients */
+        for (long t = T - 1; t >= 0; --t) {
+            const double *qt = q + (bh * T + t) * dk, *kt = k + (bh * T + t) * dk;
+            const double *vt = v + (bh * T + t) * dv, *dot = dout + (bh * T + t) * dv;
+            double *dkt = dkk + (bh * T + t) * dk, *dvt = dvv + (bh * T + t) * dv;
+            for (long i = 0; i < dk; ++i)
+                for (long j = 0; j < dv; ++j)
+                    U[i * dv + j] = g * U[i * dv + j] + qt[i] * dot[j];
+            for (long i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (long j = 0; j < dv; ++j)
+                    acc += U[i * dv + j] * vt[j];
+                dkt[i] = acc;
+            }
+            for (long j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    acc += U[i * dv + j] * kt[i];
+                dvt[j] = acc;
+            }
+        }
+        free(Sf); free(U);
+    }
+    return err;
+}
+
+/*
  * Feature map phi(x) = elu(x) + 1, entrywise.
  *   [LA] "Linear attention by hand on three tokens": elu(x) = x for x > 0 and
  *        e^x - 1 otherwise, so phi(x) = x + 1 for x >= 0 and e^x for x < 0.

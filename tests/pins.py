@@ -473,6 +473,80 @@ def pin_retention_initial_state_decays():
         _close(fs[0, h], gam[h] ** T * S0[0, h], 1e-13, f"init-state final h={h}")
 
 
+# ---------------------------------------------------------------- NEXT-2: gradients
+def _loss(q, k, v, gam, do):
+    out, _ = oracle.retention_recurrent(q, k, v, gam)
+    return float(np.sum(out * do))
+
+
+def pin_bwd_finite_differences():
+    """The oracle's gradients against central differences of the forward.
+
+    L = sum(out * dout) with out from the recurrent forward (pinned above);
+    each entry of q, k, v is moved by +-h and the difference quotient must
+    match dL/dx within the O(h^2) truncation error (the loss is quadratic in
+    each input, so the central difference is exact up to rounding).
+    """
+    rng = np.random.default_rng(20)
+    B, H, T, dk, dv = 1, 2, 7, 3, 4
+    gam = np.array([0.8, 0.97])
+    q, k, v = _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dv))
+    do = _rand(rng, (B, H, T, dv))
+    dq, dk_, dv_ = oracle.retention_bwd(q, k, v, gam, do)
+    h = 1e-4
+    for name, x, grad in (("q", q, dq), ("k", k, dk_), ("v", v, dv_)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], gam, do)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], gam, do)
+            num[idx] = (lp - lm) / (2 * h)
+        _close(grad, num, 1e-8, f"d{name} vs central differences")
+
+
+def pin_bwd_parallel_closed_form():
+    """Gradients of the parallel form O = (Q K^T (.) D) V, written with numpy:
+    dQ = ((dO V^T) (.) D) K,  dK = ((dO V^T) (.) D)^T Q,  dV = ((Q K^T) (.) D)^T dO,
+    with D built from non-negative powers only ("RetNet", single-head
+    definition), on d_k != d_v and a ragged length."""
+    rng = np.random.default_rng(21)
+    B, H, T, dk, dv = 2, 2, 41, 5, 3
+    gam = np.array([0.9, 1.0])
+    q, k, v = _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dv))
+    do = _rand(rng, (B, H, T, dv))
+    dq, dk_, dv_ = oracle.retention_bwd(q, k, v, gam, do)
+    n = np.arange(T)
+    for h in range(H):
+        e = n[:, None] - n[None, :]
+        D = np.where(e >= 0, gam[h] ** np.maximum(e, 0), 0.0)
+        for b in range(B):
+            Q, K, V, dO = q[b, h], k[b, h], v[b, h], do[b, h]
+            dP = (dO @ V.T) * D
+            _close(dq[b, h], dP @ K, 1e-11, f"dQ closed form b={b} h={h}")
+            _close(dk_[b, h], dP.T @ Q, 1e-11, f"dK closed form b={b} h={h}")
+            _close(dv_[b, h], ((Q @ K.T) * D).T @ dO, 1e-11, f"dV closed form b={b} h={h}")
+
+
+def pin_bwd_as_forwards():
+    """The gradients are retention forwards of permuted inputs: dq is the
+    causal forward of (dout, v, k); dk and dv are causal forwards of (v, dout,
+    q) and (k, q, dout) run on the time-reversed sequence."""
+    rng = np.random.default_rng(22)
+    B, H, T, dk, dv = 1, 3, 33, 4, 6
+    gam = np.array([0.7, 0.95, 1.0])
+    q, k, v = _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dv))
+    do = _rand(rng, (B, H, T, dv))
+    dq, dk_, dv_ = oracle.retention_bwd(q, k, v, gam, do)
+    f = lambda x: x[:, :, ::-1].copy()
+    _close(dq, oracle.retention_recurrent(do, v, k, gam)[0], 1e-12, "dq as a forward")
+    _close(dk_, f(oracle.retention_recurrent(f(v), f(do), f(q), gam)[0]), 1e-12, "dk as a reversed forward")
+    _close(dv_, f(oracle.retention_recurrent(f(k), f(q), f(do), gam)[0]), 1e-12, "dv as a reversed forward")
+
+
 # ---------------------------------------------------------------- P-10
 def pin_metric_calculator():
     """The pages' analytic counts.
@@ -522,5 +596,8 @@ ALL_PINS = [
     pin_linattn_decode_repeated_token,
     pin_linattn_prefill_decode_handoff,
     pin_retention_initial_state_decays,
+    pin_bwd_finite_differences,
+    pin_bwd_parallel_closed_form,
+    pin_bwd_as_forwards,
     pin_metric_calculator,
 ]

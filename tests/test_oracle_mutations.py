@@ -100,6 +100,21 @@ MUTANTS = [
     ("linattn_decode_transposed_outer_product",
      "Sn[i * dv + j] += fk[i] * vn[j];",
      "Sn[i * dv + j] += fk[j % dk] * vn[i % dv];"),
+    ("bwd_reverse_state_drops_gamma",
+     "U[i * dv + j] = g * U[i * dv + j] + qt[i] * dot[j];",
+     "U[i * dv + j] = U[i * dv + j] + qt[i] * dot[j];"),
+    ("bwd_reverse_state_excludes_own_token",
+     "acc += U[i * dv + j] * vt[j];",
+     "acc += (U[i * dv + j] - qt[i] * dot[j]) * vt[j];"),
+    ("bwd_dv_reads_transposed_state",
+     "acc += U[i * dv + j] * kt[i];",
+     "acc += U[(i * dv + j) % (dk * dv)] * kt[(i + 1) % dk];"),
+    ("bwd_dq_uses_state_before_token",
+     "acc += Sf[i * dv + j] * dot[j];",
+     "acc += (Sf[i * dv + j] - kt[i] * vt[j]) * dot[j];"),
+    ("bwd_forward_state_drops_gamma",
+     "Sf[i * dv + j] = g * Sf[i * dv + j] + kt[i] * vt[j];",
+     "Sf[i * dv + j] = Sf[i * dv + j] + kt[i] * vt[j];"),
     ("linattn_rows_doubles_eps",
      "o[j] /= (rowsum + eps);",
      "o[j] /= (rowsum + 2.0 * eps);"),
