@@ -10,7 +10,8 @@ are seeded synthetic tensors already resident in HBM when timing starts.  The
 JSON line also carries the other measured parts of the path: the recurrent
 decode step (256 sequences x 32 heads, 128 x 128 fp32 state, 1000 consecutive
 steps), the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
-d = 64) and the elu+1 decode step on the decode shapes, each with its own
+d = 64), the elu+1 decode step on the decode shapes, the backward pass of the
+long forward and the fp32 [4, 8, 2048, 64] forward, each with its own
 roofline figures.
 
 Only one GPU is used; --gpus above 1 exits with a message.
@@ -192,6 +193,30 @@ def main():
             "note": "analytic counts from the 'Linear attention' page; no hardware timing",
         },
     }
+
+    # ---------------- backward (dq, dk, dv) on the same workload
+    if not args.no_components:
+        g = torch.Generator().manual_seed(1)
+        dout = torch.randn((w.B, w.H, w.T, w.dv), generator=g).to(torch.bfloat16).to(dev)
+        gq, gk, gv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(max(rc.retention_bwd_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk, q.dtype), 1),
+                          dtype=torch.uint8, device=dev)
+
+        def bstep():
+            rc.retention_bwd(q, k, v, gamma, dout, chunk=w.chunk, dq=gq, dk=gk, dv=gv, workspace=bws)
+
+        b_kern, b_wall = time_launches(bstep, max(args.steps // 2, 5), args.warmup)
+        b_by = M.bwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
+        b_gbs = b_by / (b_kern * 1e-3) / 1e9
+        res["backward"] = {
+            "workload": w.name + " backward (dq, dk, dv given dout)", "ms_per_call": b_kern,
+            "tokens_per_s": tokens / (b_wall * 1e-3), "ratio_to_forward": b_kern / kern_ms,
+            "tflops": 3 * fl_dense / (b_kern * 1e-3) / 1e12,
+            "roofline": {"kernel": "retention_bwd: three segment walks (dq forward; dk, dv time-reversed)",
+                         "bound": "hbm", "achieved": b_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": b_gbs / M.PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": b_by},
+        }
+        del dout, gq, gk, gv, bws
 
     # ---------------- decode step and linear attention
     if not args.no_components:

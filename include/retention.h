@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 3
+#define RET_ABI_VERSION 4
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -142,6 +142,34 @@ int retention_fwd_from_state(const void *q, const void *k, const void *v,
                              void *out, float *final_state, int B, int H, int T, int dk,
                              int dv, int dtype, void *workspace, size_t ws_bytes,
                              void *stream);
+
+/*
+ * retention_bwd -- gradients of retention_fwd (zero initial state) with
+ * respect to q, k and v, given dout = dL/dout for a scalar loss L:
+ *
+ *   dq_t = S_t dout_t,          S_t = sum_{s<=t} gamma^(t-s) k_s v_s^T
+ *   dk_s = U_s v_s,  dv_s = U_s^T k_s,   U_s = sum_{t>=s} gamma^(t-s) q_t dout_t^T
+ *
+ * ("Linear attention", section "Decoding, training, and what each costs": the
+ * gradients of the causal recurrence are cumulative sums too, forward in time
+ * for the queries and backward in time for the keys and values; "RetNet",
+ * single-head definition, for the operator being differentiated.)  Computed
+ * as three chunkwise walks: dq is the forward of (dout, v, k), dk and dv are
+ * forwards of (v, dout, q) and (k, q, dout) over the time-reversed sequence.
+ *
+ *   q, k, v, dout  device, [B][H][T][dk|dv], dtype, read only
+ *   dq, dk, dv     device, [B][H][T][dk|dk|dv], dtype (written); none may
+ *                  overlap an input or another gradient
+ *   gamma, chunk, B, H, T, dk, dv, dtype: as retention_fwd
+ *   workspace      device scratch of retention_bwd_workspace_bytes(...) bytes
+ */
+int retention_bwd(const void *q, const void *k, const void *v, const float *gamma, int chunk,
+                  const void *dout, void *dq, void *dk, void *dv, int B, int H, int T,
+                  int d_k, int d_v, int dtype, void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes retention_bwd needs for these arguments (0: none, or the
+ * arguments are invalid).  Host only. */
+size_t retention_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
 
 /*
  * retention_decode_step -- one recurrent step for N sequences x H heads,

@@ -15,6 +15,8 @@ retention_decode_step(q, k, v, gamma, state)   -> out      (state updated in pla
 linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
 linear_attn_fwd(..., initial_state=(S, z), return_state=True) -> (out, S, z)
 linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place)
+retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv)
+retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.autograd)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
 linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
 
@@ -31,7 +33,8 @@ import threading
 import numpy as np
 import torch
 
-__all__ = ["retention_fwd", "retention_decode_step", "linear_attn_fwd", "linear_attn_decode_step",
+__all__ = ["retention_fwd", "retention_bwd", "retention", "retention_decode_step", "linear_attn_fwd",
+           "linear_attn_decode_step", "retention_bwd_workspace_bytes",
            "retention_fwd_workspace_bytes",
            "linear_attn_workspace_bytes", "RetentionError",
            "library_path", "load_library", "abi_version", "last_error"]
@@ -89,6 +92,10 @@ def load_library():
             lib.linear_attn_fwd_from_state.restype = i
             lib.linear_attn_decode_step.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp]
             lib.linear_attn_decode_step.restype = i
+            lib.retention_bwd.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+            lib.retention_bwd.restype = i
+            lib.retention_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+            lib.retention_bwd_workspace_bytes.restype = sz
             lib.linear_attn_fwd.restype = i
             lib.retention_last_error.argtypes = []
             lib.retention_last_error.restype = ctypes.c_char_p
@@ -165,6 +172,13 @@ def retention_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chun
     return int(load_library().retention_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), code))
 
 
+def retention_bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                                  dtype=torch.bfloat16) -> int:
+    """Bytes of device workspace retention_bwd needs for these sizes (0: none)."""
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_bwd_workspace_bytes(B, H, T, dk, dv, int(chunk), code))
+
+
 def linear_attn_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype=torch.bfloat16) -> int:
     """Bytes of device workspace linear_attn_fwd needs for these sizes (0: none)."""
     code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
@@ -220,6 +234,57 @@ def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
                                           B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return out, final_state
+
+
+def retention_bwd(q, k, v, gamma, dout, chunk: int = 64, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dq, dk, dv) of retention_fwd (zero initial state) given
+    dout = dL/dout; all tensors [B,H,T,*] in one dtype on the GPU."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3] or dout.shape != v.shape:
+        raise ValueError("q, k must be [B,H,T,dk] and v, dout [B,H,T,dv]")
+    B, H, T, d_k = q.shape
+    d_v = v.shape[3]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_dev(n, t, q.dtype)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of its input")
+    g = _gamma_array(gamma, H)
+    dt = _dtype_code(q)
+    ws, nws = _workspace(lib.retention_bwd_workspace_bytes(B, H, T, d_k, d_v, int(chunk), dt), q.device, workspace)
+    rc = lib.retention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), dout.data_ptr(), dq.data_ptr(),
+                           dk.data_ptr(), dv.data_ptr(), B, H, T, d_k, d_v, dt, _ptr(ws), nws, _stream(q))
+    _raise(rc)
+    return dq, dk, dv
+
+
+class _Retention(torch.autograd.Function):
+    """Autograd glue: forward is retention_fwd, backward is retention_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, gamma, chunk):
+        out, _ = retention_fwd(q, k, v, gamma, chunk=chunk, want_state=False)
+        ctx.save_for_backward(q, k, v)
+        ctx.gamma, ctx.chunk = gamma, chunk
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v = ctx.saved_tensors
+        dq, dk, dv = retention_bwd(q, k, v, ctx.gamma, dout.contiguous(), chunk=ctx.chunk)
+        return dq, dk, dv, None, None
+
+
+def retention(q, k, v, gamma, chunk: int = 64):
+    """Differentiable chunkwise retention (zero initial state): out [B,H,T,dv].
+
+    gamma is a host list / array of H decays (not differentiated)."""
+    g = gamma.detach().cpu().tolist() if isinstance(gamma, torch.Tensor) else gamma
+    return _Retention.apply(q, k, v, g, int(chunk))
 
 
 def retention_decode_step(q, k, v, gamma, state, out=None):

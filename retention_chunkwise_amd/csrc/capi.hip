@@ -212,7 +212,7 @@ struct FwdState {
 // Launches the segment-split forward (bf16) with a checked plan and workspace.
 hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
                                const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
-                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st) {
+                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st, bool reverse = false) {
     ret::SegArgs sa{};
     sa.G = plan.G;
     sa.cps = plan.cps;
@@ -223,15 +223,36 @@ hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k
     sa.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
     sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
     if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
+    if (reverse) return ret::launch_seg_rev(sa, chunk, dk, dv, st);
     return ret::launch_seg(sa, chunk, dk, dv, linattn, st);
+}
+
+// Plan of one walk of the backward pass: bf16 always takes the segment path
+// (its kernels have a time-reversed variant), fp32 the value-slice path.
+bool plan_bwd_walk(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan* p) {
+    if (dtype == RET_BF16) return plan_segments(bh, T, chunk, dk, dv, false, p);
+    return plan_slices(bh, T, chunk, dk, dv, false, false, p);
+}
+
+// The three walks of the backward pass: dq = fwd(dout, v, k) with widths
+// (dv, dk), dk = reversed fwd(v, dout, q) with widths (dv, dk), dv = reversed
+// fwd(k, q, dout) with widths (dk, dv).  They run one after another on one
+// stream and share the workspace, which must hold the largest plan.
+bool plan_bwd(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan plans[3], size_t* ws_max) {
+    if (!plan_bwd_walk(bh, T, chunk, dv, dk, dtype, &plans[0])) return false;
+    plans[1] = plans[0];
+    if (!plan_bwd_walk(bh, T, chunk, dk, dv, dtype, &plans[2])) return false;
+    *ws_max = plans[0].ws_bytes > plans[2].ws_bytes ? plans[0].ws_bytes : plans[2].ws_bytes;
+    return true;
 }
 
 // Launches the value-slice walk (and its segment-state kernel) with a checked
 // plan and workspace.
 hipError_t launch_slice_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
                              const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
-                             int T, int dk, int dv, bool bf16, bool linattn, hipStream_t st) {
+                             int T, int dk, int dv, bool bf16, bool linattn, hipStream_t st, bool reverse = false) {
     ret::WalkArgs a{};
+    a.reverse = reverse ? 1 : 0;
     a.q = q; a.k = k; a.v = v; a.out = out;
     a.final_state = fst.final_state; a.init_state = fst.init_state;
     a.init_z = fst.init_z; a.final_z = fst.final_z;
@@ -263,6 +284,16 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
     SegPlan plan;
     if (!plan_fwd(static_cast<long long>(B) * H, T, 64, dk, dv, true, dtype, &plan)) return 0;
     return plan.ws_bytes;
+}
+
+size_t retention_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+    if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
+        (dv != 64 && dv != 128) || !dtype_size(dtype))
+        return 0;
+    SegPlan plans[3];
+    size_t n = 0;
+    if (!plan_bwd(static_cast<long long>(B) * H, T, chunk, dk, dv, dtype, plans, &n)) return 0;
+    return n;
 }
 
 int retention_abi_version(void) { return RET_ABI_VERSION; }
@@ -449,6 +480,73 @@ int retention_fwd_from_state(const void* q, const void* k, const void* v, const 
                              int dk, int dv, int dtype, void* workspace, size_t ws_bytes, void* stream) {
     return ret_fwd_impl("retention_fwd_from_state", q, k, v, gamma, chunk, initial_state, out, final_state, B, H,
                         T, dk, dv, dtype, workspace, ws_bytes, stream);
+}
+
+int retention_bwd(const void* q, const void* k, const void* v, const float* gamma, int chunk, const void* dout,
+                  void* dq, void* dk, void* dv, int B, int H, int T, int d_k, int d_v, int dtype, void* workspace,
+                  size_t ws_bytes, void* stream) {
+    const char* fn = "retention_bwd";
+    if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (chunk != 64 && chunk != 128) return fail(RET_ERR_CHUNK, "%s: chunk must be 64 or 128 (got %d)", fn, chunk);
+    if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
+        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)", fn, ret::kMaxHeads, B,
+                    H, T);
+    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128))
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, d_k, d_v);
+    size_t nqk = esz, nv = esz;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, d_k) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, d_v))
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
+    if (nqk > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
+        return fail(RET_ERR_NULL, "%s: q, k, v, dout, dq, dk and dv must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    float log2g[ret::kMaxHeads] = {};
+    int rc = check_gamma(fn, gamma, H, log2g);
+    if (rc) return rc;
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv), rdo = range("dout", dout, nv);
+    const Range rdq = range("dq", dq, nqk), rdk = range("dk", dk, nqk), rdv = range("dv", dv, nv);
+    for (const Range& o : {rdq, rdk, rdv}) {
+        for (const Range& in : {rq, rk, rv, rdo})
+            if (overlap(o, in)) return fail(RET_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, in.name);
+    }
+    if (overlap(rdq, rdk) || overlap(rdq, rdv) || overlap(rdk, rdv))
+        return fail(RET_ERR_ALIAS, "%s: the gradient outputs overlap", fn);
+    if (B == 0) return ok();
+    const long long bh = static_cast<long long>(B) * H;
+    SegPlan plans[3];
+    size_t need = 0;
+    if (!plan_bwd(bh, T, chunk, d_k, d_v, dtype, plans, &need))
+        return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    SegPlan wplan;
+    wplan.ws_bytes = need;
+    rc = check_workspace(fn, wplan, workspace, ws_bytes, {rq, rk, rv, rdo, rdq, rdk, rdv});
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FwdState none;
+    // (query input, key input, value input, output, key width, value width, reversed)
+    struct Walk {
+        const void *a, *b, *c;
+        void* o;
+        int wk, wv;
+        bool rev;
+    };
+    const Walk walks[3] = {{dout, v, k, dq, d_v, d_k, false}, {v, dout, q, dk, d_v, d_k, true},
+                           {k, q, dout, dv, d_k, d_v, true}};
+    for (int i = 0; i < 3; ++i) {
+        const Walk& w = walks[i];
+        const hipError_t e =
+            plans[i].path == FwdPath::kSegment
+                ? launch_segment_path(plans[i], w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, chunk, w.wk,
+                                      w.wv, false, st, w.rev)
+                : launch_slice_path(plans[i], w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, w.wk, w.wv,
+                                    false, false, st, w.rev);
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    }
+    return ok();
 }
 
 int retention_decode_step(const void* q, const void* k, const void* v, const float* gamma,

@@ -26,6 +26,7 @@ struct WalkArgs {
     int dv;              // full value width (the kernel handles one slice of it)
     int nslices;         // dv / (16 * NT)
     int xcd_remap;       // 1: spread (b, h) groups so their slices share an XCD
+    int reverse;         // 1: walk the time-reversed sequence (token t at row T - 1 - t); fp32 only
     int G;               // segments per (b, h) (1: walk whole sequences); all but the last are full
     int cps;             // chunks per segment
     int seg_len;         // tokens per full segment (set by the launcher: cps * chunk)
@@ -86,6 +87,10 @@ hipError_t launch_seg_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_lin_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_lin_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
+// Time-reversed retention walk (token t read from and written to row T - 1 - t).
+hipError_t launch_seg_rev(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg_rev_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
+hipError_t launch_seg_rev_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
 
 // Segment count for the segment-split forward: enough (b, h, segment)
 // workgroups to occupy the chip, at least `min_cps` chunks per segment.

@@ -217,6 +217,18 @@ __device__ __forceinline__ unsigned dma_offset(int w, int l) {
     return static_cast<unsigned>(r * (RU * 16) + ((su ^ swz_mask<RU>(r)) << 4));
 }
 
+// The same unit read in time-reversed order: the chunk's row r lives at memory
+// row n - 1 - r of a chunk of n rows, so the offset is (n - 1) * row bytes plus
+// this per-lane part (unit offset minus r row bytes; instruction w + 8 m adds
+// -8192 m).  Rows past a short chunk come out negative, which the buffer's range
+// check turns into zeros.
+template <int RU>
+__device__ __forceinline__ int dma_offset_rev(int w, int l) {
+    const int b = w * 1024 + l * 16;
+    const int r = b / (RU * 16), su = (b % (RU * 16)) >> 4;
+    return ((su ^ swz_mask<RU>(r)) << 4) - r * (RU * 16);
+}
+
 // ---------------------------------------------------------------------------
 // seg_state_kernel: dS_j for one (b, h) and segment j < G - 1.
 
@@ -225,7 +237,7 @@ __device__ __forceinline__ unsigned dma_offset(int w, int l) {
 // ring of NBUF LDS buffers, prefetching NBUF-1 blocks ahead.  Blocks run last
 // to first (the walk kernel then finds each segment's first chunks most
 // recently read).
-template <int C, int DK, int DV, bool LIN, int NBUF>
+template <int C, int DK, int DV, bool LIN, int NBUF, bool REV>
 __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kring, unsigned short* vring, int bh,
                                            int seg, int piece, float lg, int w) {
     using Cf = SCfg<C, DK, DV, LIN>;
@@ -244,6 +256,7 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
     for (int e = 0; e < 8; ++e) zb0[e] = ex2(static_cast<float>(31 - slot_key(g, e)) * lg);
 
     const unsigned koff = dma_offset<KRU>(w, l), voff = dma_offset<VRU>(w, l);
+    const int koffr = dma_offset_rev<KRU>(w, l), voffr = dma_offset_rev<VRU>(w, l);
 
     f32x4 acc[SKT][NVH];
     float zsum[SKT];  // linear attention: partial column sums of phi(K)
@@ -267,14 +280,20 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
         const int bi = nblk - 1 - i;
         const long long t0 = t_seg + static_cast<long long>(bi) * C;
         const int bytes = (bi >= 0) ? C : 0;
-        const u32x4 wk = rsrc_words(kh + t0 * DK, bytes * DK * 2);
-        const u32x4 wv = rsrc_words(vh + t0 * DV, bytes * DV * 2);
+        // memory row of the block's first row (reversed: its rows run backwards from T - 1 - t0)
+        const long long mrow = REV ? (bytes ? T - t0 - C : 0) : t0;
+        const u32x4 wk = rsrc_words(kh + mrow * DK, bytes * DK * 2);
+        const u32x4 wv = rsrc_words(vh + mrow * DV, bytes * DV * 2);
         const int buf = i % NBUF;
         const unsigned kbase = kring0 + buf * (C * DK * 2), vbase = vring0 + buf * (C * DV * 2);
 #pragma unroll
-        for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (w + 8 * m) * 1024, koff + 8192u * m);
+        for (int m = 0; m < KIW; ++m)
+            dma16(wk, kbase + (w + 8 * m) * 1024,
+                  REV ? static_cast<unsigned>((C - 1) * DK * 2 + koffr - 8192 * m) : koff + 8192u * m);
 #pragma unroll
-        for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (w + 8 * m) * 1024, voff + 8192u * m);
+        for (int m = 0; m < VIW; ++m)
+            dma16(wv, vbase + (w + 8 * m) * 1024,
+                  REV ? static_cast<unsigned>((C - 1) * DV * 2 + voffr - 8192 * m) : voff + 8192u * m);
     };
 
     for (int i = 0; i < NBUF - 1; ++i) load_block(i);
@@ -372,7 +391,7 @@ __device__ __forceinline__ int perm_row(int dv) {
     return (dv & ~31) | (((dv >> 2) & 1) << 4) | (((dv >> 3) & 3) << 2) | (dv & 3);
 }
 
-template <int C, int DK, int DV, bool LIN, int P, bool OW>
+template <int C, int DK, int DV, bool LIN, int P, bool OW, bool REV>
 __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
     using Cf = SCfg<C, DK, DV, LIN>;
     constexpr int NI = Cf::NI, NS = Cf::NS, NB = Cf::NB, NVT = Cf::NVT, SKT = Cf::SKT;
@@ -498,6 +517,12 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
     };
 
     const unsigned koff = dma_offset<KRU>(w, l), voff = dma_offset<VRU>(w, l);
+    const int koffr = dma_offset_rev<KRU>(w, l), voffr = dma_offset_rev<VRU>(w, l);
+    // Time-reversed walks (REV) read and write chunk row r at memory row
+    // T - 1 - (t0 + r): the chunk's memory rows start at T - t0 - clen and run
+    // backwards.
+    auto mem_row0 = [&](long long t0, int cl) -> long long { return REV ? (cl ? T - t0 - cl : 0) : t0; };
+    auto row_in = [&](int r, int cl) -> int { return REV ? cl - 1 - r : r; };
 
     // Issue the loads of chunk c through range-checked resources (rows past
     // the end of the sequence read as zeros).
@@ -514,22 +539,27 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
         constexpr int buf = decltype(bufc)::value;
         const long long t0 = static_cast<long long>(c) * C;
         const int cl = (c < c_end) ? chunk_len(c) : 0;
-        const u32x4 wk = rsrc_words(kh + t0 * DK, cl * DK * 2);
-        const u32x4 wv = rsrc_words(vh + t0 * DV, cl * DV * 2);
+        const long long mrow = mem_row0(t0, cl);
+        const u32x4 wk = rsrc_words(kh + mrow * DK, cl * DK * 2);
+        const u32x4 wv = rsrc_words(vh + mrow * DV, cl * DV * 2);
         const unsigned kbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.k[buf]));
         const unsigned vbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.v[buf]));
 #pragma unroll
-        for (int m = 0; m < KIW; ++m) dma16(wk, kbase + (w + 8 * m) * 1024, koff + 8192u * m);
+        for (int m = 0; m < KIW; ++m)
+            dma16(wk, kbase + (w + 8 * m) * 1024,
+                  REV ? static_cast<unsigned>((cl - 1) * DK * 2 + koffr - 8192 * m) : koff + 8192u * m);
 #pragma unroll
-        for (int m = 0; m < VIW; ++m) dma16(wv, vbase + (w + 8 * m) * 1024, voff + 8192u * m);
+        for (int m = 0; m < VIW; ++m)
+            dma16(wv, vbase + (w + 8 * m) * 1024,
+                  REV ? static_cast<unsigned>((cl - 1) * DV * 2 + voffr - 8192 * m) : voff + 8192u * m);
         if constexpr (OW) {
-            const auto rq = make_rsrc(qh + t0 * DK, cl * DK * 2);
+            const auto rq = make_rsrc(qh + mrow * DK, cl * DK * 2);
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int ks = 0; ks < QF; ++ks)
                     qf[buf][s][ks] = __builtin_bit_cast(
-                        bf16x8, bload16(rq, static_cast<unsigned>(((16 * its(s) + l16) * DK + 32 * ks + 8 * g) * 2)));
+                        bf16x8, bload16(rq, static_cast<unsigned>(((row_in(16 * its(s) + l16, cl)) * DK + 32 * ks + 8 * g) * 2)));
         }
     };
 
@@ -644,7 +674,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             int rowo = rowo0, uo = uo0;
             opaque(rowo);
             opaque(uo);
-            const auto ro = make_rsrc(oh + t0 * DV, clen * DV * 2);
+            const auto ro = make_rsrc(oh + mem_row0(t0, clen) * DV, clen * DV * 2);
 #pragma unroll
             for (int pa = 0; pa < NPAIR; ++pa) {
                 const int uoa = uo ^ (pa << 6);
@@ -679,7 +709,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                         oacc[s][0] *= rden[s];
                         oacc[s][1] *= rden[s];
                     }
-                    const int row = 16 * its(s) + l16;  // rows past the end are dropped by the resource
+                    const int row = row_in(16 * its(s) + l16, clen);  // rows past the end are dropped by the resource
                     bstore16_bf(ro, static_cast<unsigned>((row * DV + 32 * pa + 8 * g) * 2),
                                 cat_bf16(cvt4_bf16(oacc[s][0]), cvt4_bf16(oacc[s][1])));
                 }
@@ -787,7 +817,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 constexpr int kStateBlock = 64;
 constexpr int kStateRing = 4;
 
-template <int DK, int DV, bool LIN>
+template <int DK, int DV, bool LIN, bool REV>
 __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned short kring[kStateRing * kStateBlock * DK];
     __shared__ __attribute__((aligned(16))) unsigned short vring[kStateRing * kStateBlock * DV];
@@ -795,10 +825,11 @@ __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a)
     const int bh = blockIdx.x / slots, slot = blockIdx.x % slots;
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    state_body<kStateBlock, DK, DV, LIN, kStateRing>(a, kring, vring, bh, slot / a.pieces, slot % a.pieces, lg, wave);
+    state_body<kStateBlock, DK, DV, LIN, kStateRing, REV>(a, kring, vring, bh, slot / a.pieces, slot % a.pieces, lg,
+                                                          wave);
 }
 
-template <int C, int DK, int DV, bool LIN>
+template <int C, int DK, int DV, bool LIN, bool REV>
 __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned short k0[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short k1[C * DK];
@@ -815,14 +846,14 @@ __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) 
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: walk_body<C, DK, DV, LIN, 0, true>(a, tl, bh, seg, lg); break;
-        case 1: walk_body<C, DK, DV, LIN, 1, true>(a, tl, bh, seg, lg); break;
-        case 2: walk_body<C, DK, DV, LIN, 2, true>(a, tl, bh, seg, lg); break;
-        case 3: walk_body<C, DK, DV, LIN, 3, true>(a, tl, bh, seg, lg); break;
-        case 4: walk_body<C, DK, DV, LIN, 0, false>(a, tl, bh, seg, lg); break;
-        case 5: walk_body<C, DK, DV, LIN, 1, false>(a, tl, bh, seg, lg); break;
-        case 6: walk_body<C, DK, DV, LIN, 2, false>(a, tl, bh, seg, lg); break;
-        default: walk_body<C, DK, DV, LIN, 3, false>(a, tl, bh, seg, lg); break;
+        case 0: walk_body<C, DK, DV, LIN, 0, true, REV>(a, tl, bh, seg, lg); break;
+        case 1: walk_body<C, DK, DV, LIN, 1, true, REV>(a, tl, bh, seg, lg); break;
+        case 2: walk_body<C, DK, DV, LIN, 2, true, REV>(a, tl, bh, seg, lg); break;
+        case 3: walk_body<C, DK, DV, LIN, 3, true, REV>(a, tl, bh, seg, lg); break;
+        case 4: walk_body<C, DK, DV, LIN, 0, false, REV>(a, tl, bh, seg, lg); break;
+        case 5: walk_body<C, DK, DV, LIN, 1, false, REV>(a, tl, bh, seg, lg); break;
+        case 6: walk_body<C, DK, DV, LIN, 2, false, REV>(a, tl, bh, seg, lg); break;
+        default: walk_body<C, DK, DV, LIN, 3, false, REV>(a, tl, bh, seg, lg); break;
     }
 }
 
@@ -839,7 +870,7 @@ constexpr bool walk_supported() {
     return walk_fits<C, DK, DV, LIN>() && !(LIN && C == 128 && DK == 128);
 }
 
-template <int C, int DK, int DV, bool LIN>
+template <int C, int DK, int DV, bool LIN, bool REV>
 hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     if constexpr (!walk_supported<C, DK, DV, LIN>()) {
         return hipErrorInvalidConfiguration;
@@ -850,23 +881,26 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     if (a.G > 1) {
         SegArgs sa = a;
         sa.scps = a.cps * (C / kStateBlock);
-        hipLaunchKernelGGL((seg_state_kernel<DK, DV, LIN>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
+        hipLaunchKernelGGL((seg_state_kernel<DK, DV, LIN, REV>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
                            dim3(kThreads), 0, stream, sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, LIN>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, LIN, REV>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
     }
 }
 
-template <int C, bool LIN>
+// REV: the walk runs over the time-reversed sequence (token t read from and
+// written to row T - 1 - t); the gradients of keys and values are such walks.
+template <int C, bool LIN, bool REV = false>
 hipError_t launch_chunk(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, LIN>(a, stream);
-    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, LIN>(a, stream);
-    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, LIN>(a, stream);
-    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, LIN>(a, stream);
+    static_assert(!(LIN && REV), "time-reversed walks are retention only");
+    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, LIN, REV>(a, stream);
+    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, LIN, REV>(a, stream);
+    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, LIN, REV>(a, stream);
+    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, LIN, REV>(a, stream);
     return hipErrorInvalidValue;
 }
 

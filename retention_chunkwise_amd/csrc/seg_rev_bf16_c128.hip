@@ -1,0 +1,11 @@
+// seg_rev_bf16_c128.hip -- time-reversed segment-split retention walk, bf16,
+// chunk 128 (the key and value gradients of the backward pass).
+#include "seg_kernel.h"
+
+namespace ret {
+
+hipError_t launch_seg_rev_c128(const SegArgs& a, int dk, int dv, hipStream_t stream) {
+    return seg::launch_chunk<128, false, true>(a, dk, dv, stream);
+}
+
+}  // namespace ret

@@ -269,6 +269,13 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     uint4 qnext[NS][DMA ? 1 : QU];
     uint4 qcur[NS][DMA ? 1 : QU];
 
+    // Time-reversed walks (fp32 only) read and write chunk row r of a chunk of
+    // cl rows starting at token t0 at memory row T - 1 - (t0 + r): the chunk's
+    // memory rows start at T - t0 - cl and run backwards.
+    const bool rev = !DMA && a.reverse;
+    auto mem_row0 = [&](int t0, int cl) -> long long { return rev ? T - t0 - cl : t0; };
+    auto row_in = [&](int r, int cl) -> int { return rev ? cl - 1 - r : r; };
+
     // Issue the loads of chunk c (into LDS buffer `buf` on the DMA path) through
     // range-checked buffer resources: rows past the end of the sequence read as
     // zeros.  No instruction consumes these values in the step that issues them.
@@ -276,9 +283,10 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         constexpr int buf = decltype(bufc)::value;
         const int t0 = c * C;
         const int cl = (T - t0 < C) ? (T - t0) : C;
-        const auto rk = make_rsrc(kh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
-        const auto rq = make_rsrc(qh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
-        const auto rv = make_rsrc(vh + static_cast<long long>(t0) * DV, cl * DV * ESZ);
+        const long long mrow = mem_row0(t0, cl);
+        const auto rk = make_rsrc(kh + mrow * DK, cl * DK * ESZ);
+        const auto rq = make_rsrc(qh + mrow * DK, cl * DK * ESZ);
+        const auto rv = make_rsrc(vh + mrow * DV, cl * DV * ESZ);
         if constexpr (DMA) {
             const u32x4 wk = rsrc_words(kh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
             const u32x4 wq = rsrc_words(qh + static_cast<long long>(t0) * DK, cl * DK * ESZ);
@@ -299,12 +307,12 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
             for (int m = 0; m < KU; ++m) {
                 const int u = tid + m * kThreads;
-                const int row = u / RU, col = u % RU;
+                const int row = row_in(u / RU, cl), col = u % RU;
                 kpre[m] = bload16(rk, static_cast<unsigned>((row * DK + col * EPV) * ESZ));
             }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const int row = its(s) * 16 + l16;
+                const int row = row_in(its(s) * 16 + l16, cl);
 #pragma unroll
                 for (int u = 0; u < QU; ++u)  // k = (DK/4) g + 4u .. +3
                     qnext[s][u] = bload16(rq, static_cast<unsigned>((row * DK + (DK / 4) * g + 4 * u) * ESZ));
@@ -315,7 +323,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             for (int m = 0; m < VPT; ++m) {
                 const int u = tid + m * kThreads;
                 if (VUT % kThreads == 0 || u < VUT) {
-                    const int row = u / VRU, col = u % VRU;
+                    const int row = row_in(u / VRU, cl), col = u % VRU;
                     vpre[m] = bload16(rv, static_cast<unsigned>((row * DV + col * EPV) * ESZ));
                 }
             }
@@ -657,10 +665,10 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
         }
         {
-            const auto ro = make_rsrc(oh + static_cast<long long>(t0) * DV, clen * DV * ESZ);
+            const auto ro = make_rsrc(oh + mem_row0(t0, clen) * DV, clen * DV * ESZ);
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const int row = its(s) * 16 + l16;  // rows past the end are dropped by the resource
+                const int row = row_in(its(s) * 16 + l16, clen);  // rows past the end are dropped by the resource
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     f32x4 o = oacc[s][nt];
@@ -797,10 +805,13 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const long long t0 = static_cast<long long>(seg) * a.seg_len;
     // range-checked resources over exactly this segment: the prefetch past its
-    // last batch reads zeros, so every load is unconditional
-    const auto rk = make_rsrc(static_cast<const E*>(a.k) + (static_cast<long long>(bh) * a.T + t0) * DK,
+    // last batch reads zeros, so every load is unconditional.  A time-reversed
+    // walk reads segment token t at row T - 1 - (t0 + t).
+    const bool rev = a.reverse != 0;
+    const long long mrow = rev ? a.T - t0 - a.seg_len : t0;
+    const auto rk = make_rsrc(static_cast<const E*>(a.k) + (static_cast<long long>(bh) * a.T + mrow) * DK,
                               a.seg_len * DK * ESZ);
-    const auto rv = make_rsrc(static_cast<const E*>(a.v) + (static_cast<long long>(bh) * a.T + t0) * DV,
+    const auto rv = make_rsrc(static_cast<const E*>(a.v) + (static_cast<long long>(bh) * a.T + mrow) * DV,
                               a.seg_len * DV * ESZ);
     auto ld = [](__amdgpu_buffer_rsrc_t r, int elem) -> float {
         if constexpr (BF16) {
@@ -818,11 +829,12 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int t = tb + 4 * u + g;
+            const int tr = rev ? a.seg_len - 1 - t : t;  // memory row within the segment
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi)
-                ka[b][u][mi] = ld(rk, t * DK + 16 * (w + 4 * mi) + l16);
+                ka[b][u][mi] = ld(rk, tr * DK + 16 * (w + 4 * mi) + l16);
 #pragma unroll
-            for (int n = 0; n < NV; ++n) vb[b][u][n] = ld(rv, t * DV + 16 * n + l16);
+            for (int n = 0; n < NV; ++n) vb[b][u][n] = ld(rv, tr * DV + 16 * n + l16);
         }
     };
 

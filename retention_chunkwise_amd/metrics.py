@@ -88,6 +88,11 @@ def decode_bytes(N, H, dk, dv, elem_bytes: int) -> int:
     return N * H * (2 * dk * dv * 4 + (2 * dk + dv) * elem_bytes + dv * elem_bytes)
 
 
+def bwd_bytes(B, H, T, dk, dv, elem_bytes: int) -> int:
+    """q, k, v and dout read once, dq, dk and dv written once."""
+    return B * H * T * (3 * dk + 2 * dv + dk + dv) * elem_bytes
+
+
 def linattn_decode_bytes(N, H, dk, dv, elem_bytes: int) -> int:
     """The retention decode bytes plus the fp32 normaliser z read and written."""
     return decode_bytes(N, H, dk, dv, elem_bytes) + N * H * 2 * dk * 4

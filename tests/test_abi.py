@@ -271,3 +271,43 @@ def test_linattn_decode_rejects(kw, code):
 def test_linattn_decode_empty_is_accepted():
     lib = _lib()
     assert _ldec(lib, N=0) == 0
+
+
+# ---------------------------------------------------------------- backward
+def _bwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9, 0.9]), chunk=64, do=FAKE * 4, dq=FAKE * 5,
+             dk=FAKE * 6, dv=FAKE * 7, B=1, H=2, T=16, d_k=64, d_v=64, dtype=rc.RET_F32, ws=None, nws=0)
+    a.update(kw)
+    return lib.retention_bwd(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["do"], a["dq"], a["dk"], a["dv"],
+                             a["B"], a["H"], a["T"], a["d_k"], a["d_v"], a["dtype"], a["ws"], a["nws"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), -1),
+    (dict(dv=None), -1),
+    (dict(gamma=None), -1),
+    (dict(dtype=5), -3),
+    (dict(chunk=32), -4),
+    (dict(gamma=_gam([0.9, 0.0])), -5),
+    (dict(d_v=96), -2),
+    (dict(dq=FAKE * 5 + 4), -7),
+    (dict(dq=FAKE), -8),                 # dq is q
+    (dict(dv=FAKE * 4), -8),             # dv overlaps dout
+    (dict(dk=FAKE * 5), -8),             # dk is dq
+    (dict(T=65536, dtype=rc.RET_BF16, d_k=128, d_v=128, chunk=128, q=FAKE, k=FAKE * 1024, v=FAKE * 2048,
+          do=FAKE * 3072, dq=FAKE * 4096, dk=FAKE * 5120, dv=FAKE * 6144), -9),   # no workspace
+])
+def test_retention_bwd_rejects(kw, code):
+    lib = _lib()
+    assert _bwd(lib, **kw) == code
+    assert "retention_bwd" in lib.retention_last_error().decode()
+
+
+def test_retention_bwd_workspace_and_empty_batch():
+    lib = _lib()
+    n = lib.retention_bwd_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    assert n > 0 and n == lib.retention_fwd_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    # dq walks with widths (dv, dk), dv with (dk, dv): the larger plan sets the size
+    n2 = lib.retention_bwd_workspace_bytes(1, 4, 4096, 64, 128, 64, rc.RET_F32)
+    assert n2 >= lib.retention_fwd_workspace_bytes(1, 4, 4096, 64, 128, 64, rc.RET_F32)
+    assert _bwd(lib, B=0) == 0

@@ -1,0 +1,138 @@
+"""Retention gradients (retention_bwd) against the fp64 oracle (needs a gfx950 GPU).
+
+retention_bwd returns dq, dk, dv of retention_fwd from a zero state, given
+dout.  The library computes them as three chunkwise walks (dq forward in
+time, dk and dv over the time-reversed sequence); the oracle computes them as
+cumulative sums forward and backward in time.  Cases: bf16 (segment path,
+several forced segment counts) and fp32 (value-slice path), chunks 64 and
+128, every (dk, dv) pair, ragged and short lengths, unit and small decays, the
+full long-sequence shape on two heads, and the autograd wrapper.
+Tolerances: relative Frobenius error 1e-4 (fp32), 2e-2 (bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import retention_chunkwise_amd as rc
+from retention_chunkwise_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _inputs(seed, dtype, B, H, T, dk, dv, chunk=64):
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, chunk=chunk, dtype=dtype,
+                                              scale=1.0 / np.sqrt(dk))
+    inp = wl.make_inputs(w, seed)
+    g = torch.Generator().manual_seed(seed + 500)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp["do"] = torch.randn((B, H, T, dv), generator=g).to(tdt)
+    return w, inp
+
+
+def _segments(monkeypatch, G):
+    monkeypatch.delenv("RET_FWD_PATH", raising=False)
+    if G is None:
+        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
+    else:
+        monkeypatch.setenv("RET_FWD_SEGMENTS", str(G))
+
+
+def _check(tag, got, ref, tol):
+    for name, x, r in zip(("dq", "dk", "dv"), got, ref):
+        e = oracle.rel_frobenius(x, r)
+        print(f"[parity] {tag} {name}: rel_fro={e:.3e} (tol {tol:.0e})", flush=True)
+        assert e <= tol and np.all(np.isfinite(x)), f"{tag} {name}"
+
+
+def _run(inp, chunk):
+    q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
+    dq, dk, dv = rc.retention_bwd(q, k, v, inp["gamma"], do, chunk=chunk)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy() for t in (dq, dk, dv)]
+
+
+@pytest.mark.parametrize("dtype,G", [("f32", None), ("f32", 3), ("bf16", None), ("bf16", 1), ("bf16", 5)])
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 1000), (64, 128, 129), (128, 64, 700)])
+def test_bwd_small_full(dtype, G, chunk, dk, dv, T, monkeypatch):
+    w, inp = _inputs(51, dtype, 2, 3, T, dk, dv, chunk)
+    _segments(monkeypatch, G)
+    print(f"[bwd] {dtype} G={G} C={chunk} dk={dk} dv={dv} T={T}", flush=True)
+    got = _run(inp, chunk)
+    ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"], nthreads=8)
+    _check(f"bwd {dtype} G={G} C={chunk} dk={dk} dv={dv} T={T}", got, ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 5, 64, 65, 127, 128, 129])
+def test_bwd_short_and_ragged(dtype, T, monkeypatch):
+    w, inp = _inputs(52, dtype, 1, 2, T, 64, 64)
+    _segments(monkeypatch, 2)
+    got = _run(inp, 64)
+    ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"])
+    _check(f"bwd short {dtype} T={T}", got, ref, TOL[dtype])
+
+
+def test_bwd_zero_length_and_empty_batch():
+    q = torch.zeros((1, 2, 0, 64), device="cuda", dtype=torch.bfloat16)
+    dq, dk, dv = rc.retention_bwd(q, q, q, [0.9, 0.9], q)
+    assert dq.shape == (1, 2, 0, 64) and dk.shape == dq.shape and dv.shape == dq.shape
+    e = torch.zeros((0, 2, 16, 64), device="cuda")
+    dq, dk, dv = rc.retention_bwd(e, e, e, [0.9, 0.9], e)
+    assert dq.shape == e.shape
+
+
+@pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
+def test_bwd_gamma_extremes(gval, monkeypatch):
+    w, inp = _inputs(53, "bf16", 1, 2, 900, 64, 64)
+    inp["gamma"] = np.full(2, gval, dtype=np.float32)
+    _segments(monkeypatch, 4)
+    got = _run(inp, 64)
+    ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"])
+    _check(f"bwd gamma={gval}", got, ref, TOL["bf16"])
+
+
+def test_bwd_long_sequence_two_heads(monkeypatch):
+    """The [1, 32, 65536, 128] bf16 shape; the oracle checks heads 0 and 31 in full."""
+    _segments(monkeypatch, None)
+    w = wl.WORKLOADS["ret_fwd_long_bf16"]
+    inp = wl.make_inputs(w, 0)
+    g = torch.Generator().manual_seed(54)
+    do = torch.randn((w.B, w.H, w.T, w.dv), generator=g).to(torch.bfloat16)
+    q, k, v, dod = inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), do.cuda()
+    print("[bwd] long [1,32,65536,128] bf16", flush=True)
+    dq, dk, dv = rc.retention_bwd(q, k, v, inp["gamma"], dod, chunk=w.chunk)
+    torch.cuda.synchronize()
+    for h in (0, w.H - 1):
+        sl = (slice(None), slice(h, h + 1))
+        ref = oracle.retention_bwd(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["gamma"][h:h + 1], do[sl],
+                                   nthreads=2)
+        got = [t[sl].float().cpu().numpy() for t in (dq, dk, dv)]
+        _check(f"bwd long head {h}", got, ref, TOL["bf16"])
+
+
+def test_autograd_wrapper_matches_oracle(monkeypatch):
+    _segments(monkeypatch, None)
+    w, inp = _inputs(55, "f32", 2, 2, 300, 64, 128)
+    q, k, v = (inp[n].cuda().requires_grad_(True) for n in ("q", "k", "v"))
+    out = rc.retention(q, k, v, inp["gamma"], chunk=64)
+    (out * inp["do"].cuda()).sum().backward()
+    torch.cuda.synchronize()
+    ref_out, _ = oracle.retention_recurrent(inp["q"], inp["k"], inp["v"], inp["gamma"])
+    e = oracle.rel_frobenius(out.detach().cpu().numpy(), ref_out)
+    print(f"[parity] autograd forward: {e:.3e}", flush=True)
+    assert e <= TOL["f32"]
+    ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"])
+    _check("autograd", [t.grad.cpu().numpy() for t in (q, k, v)], ref, TOL["f32"])
+
+
+def test_bwd_deterministic(monkeypatch):
+    _segments(monkeypatch, None)
+    w, inp = _inputs(56, "bf16", 1, 4, 2000, 128, 128, 128)
+    a = _run(inp, 128)
+    b = _run(inp, 128)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y), "run-to-run gradients differ"
