@@ -208,13 +208,15 @@ def main():
         b_kern, b_wall = time_launches(bstep, max(args.steps // 2, 5), args.warmup)
         b_by = M.bwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
         b_gbs = b_by / (b_kern * 1e-3) / 1e9
+        b_tr = measured_traffic("bwd_ret_fwd_long_bf16", FWD_SOURCES)
         res["backward"] = {
             "workload": w.name + " backward (dq, dk, dv given dout)", "ms_per_call": b_kern,
             "tokens_per_s": tokens / (b_wall * 1e-3), "ratio_to_forward": b_kern / kern_ms,
             "tflops": 3 * fl_dense / (b_kern * 1e-3) / 1e12,
             "roofline": {"kernel": "retention_bwd: three segment walks (dq forward; dk, dv time-reversed)",
                          "bound": "hbm", "achieved": b_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": b_gbs / M.PEAK_HBM_GBS, "traffic": None, "algorithmic_bytes_per_launch": b_by},
+                         "frac": b_gbs / M.PEAK_HBM_GBS, "traffic": (b_tr["bytes_per_launch"] if b_tr else None),
+                         "algorithmic_bytes_per_launch": b_by},
         }
         del dout, gq, gk, gv, bws
 
