@@ -103,11 +103,14 @@ def _bind(lib):
                                         _L, _l, _D, ctypes.c_int]
     lib.oracle_retention_bwd.argtypes = [_D, _D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, _D,
                                          ctypes.c_int]
+    lib.oracle_retention_normalized.argtypes = [_D, _D, _D, _D, _l, _l, _l, _l, _l, ctypes.c_int,
+                                                ctypes.c_double, _D, ctypes.c_int]
     lib.oracle_threads_used.argtypes = [ctypes.c_int]
     for name in ("oracle_retention_recurrent", "oracle_retention_parallel",
                  "oracle_retention_rows", "oracle_retention_chunkwise",
                  "oracle_decode_steps", "oracle_linattn_recurrent",
                  "oracle_linattn_decode_steps", "oracle_retention_bwd",
+                 "oracle_retention_normalized",
                  "oracle_linattn_parallel", "oracle_linattn_rows",
                  "oracle_threads_used"):
         getattr(lib, name).restype = ctypes.c_int
@@ -221,6 +224,25 @@ def decode_steps(q, k, v, gamma, state, nsteps: int = 1, nthreads: int = 1):
                                       dk, dv, int(nsteps), int(nthreads)),
            "oracle_decode_steps")
     return out, S
+
+
+GROUPNORM_EPS = 1e-5
+
+
+def retention_normalized(q, k, v, gamma, group: bool = False, eps: float = GROUPNORM_EPS, nthreads: int = 1):
+    """Retention divided by its decayed score row sum floored at 1 in size,
+    optionally followed by GroupNorm over each row ("Linear attention" page,
+    box "An LSTM whose cell is linear attention"; "RetNet", the layer's
+    optional GroupNorm).  Returns out [B,H,T,dv]."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(gamma).reshape(-1)
+    B, H, T, dk, dv = _shape4(q, k, v)
+    if g.shape != (H,):
+        raise ValueError("gamma must have H entries")
+    out = np.zeros((B, H, T, dv))
+    _check(load().oracle_retention_normalized(_p(q), _p(k), _p(v), _p(g), B, H, T, dk, dv,
+                                              1 if group else 0, float(eps), _p(out), int(nthreads)),
+           "oracle_retention_normalized")
+    return out
 
 
 def retention_bwd(q, k, v, gamma, dout, nthreads: int = 1):

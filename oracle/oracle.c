@@ -364,6 +364,77 @@ int oracle_retention_bwd(const double *q, const double *k, const double *v,
 }
 
 /*
+ * Retention with the row-sum floor and, optionally, GroupNorm.
+ *   [LA] box "An LSTM whose cell is linear attention": the matrix cell and
+ *        normaliser evolve as C_t = f C_{t-1} + i v_t k_t^T and
+ *        n_t = f n_{t-1} + i k_t, and the read-out divides C_t q_t by
+ *        max(|n_t^T q_t|, 1), a floor of 1 the page attributes to RetNet.
+ *        With f = gamma and i = 1 (C_t = S_t^T) this is the retention read-out
+ *        o_t = q_t S_t divided by its decayed row sum of scores
+ *        n_t^T q_t = sum_{s<=t} gamma^(t-s) q_t . k_s, floored at 1 in size;
+ *        the same page describes RetNet dividing each row of its scores by the
+ *        absolute value of their sum, clamped below at 1, with a normalisation
+ *        after it.
+ *   [RetNet] "Multi-Scale Retention and Network Architecture": the layer's
+ *        optional GroupNorm.  group != 0 replaces each output row (one head's
+ *        dv features) by (o - mean(o)) / sqrt(var(o) + eps), with the
+ *        population variance and no learned gain or bias.
+ */
+int oracle_retention_normalized(const double *q, const double *k, const double *v,
+                                const double *gamma, long B, long H, long T, long dk,
+                                long dv, int group, double eps, double *out, int nthreads)
+{
+    if (!q || !k || !v || !gamma || !out || B < 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for num_threads(oracle_threads(nthreads)) schedule(dynamic, 1)
+    for (long bh = 0; bh < B * H; ++bh) {
+        const double g = gamma[bh % H];
+        double *Sn = (double *)calloc((size_t)(dk * dv), sizeof(double));
+        double *n = (double *)calloc((size_t)dk, sizeof(double));
+        if (!Sn || !n) {
+            err = ORACLE_ERR_NOMEM;
+            free(Sn); free(n);
+            continue;
+        }
+        for (long t = 0; t < T; ++t) {
+            const double *qt = q + (bh * T + t) * dk, *kt = k + (bh * T + t) * dk;
+            const double *vt = v + (bh * T + t) * dv;
+            double *ot = out + (bh * T + t) * dv;
+            for (long i = 0; i < dk; ++i) {
+                for (long j = 0; j < dv; ++j)
+                    Sn[i * dv + j] = g * Sn[i * dv + j] + kt[i] * vt[j];
+                n[i] = g * n[i] + kt[i];
+            }
+            double r = 0.0;
+            for (long i = 0; i < dk; ++i)
+                r += n[i] * qt[i];
+            const double den = fabs(r) > 1.0 ? fabs(r) : 1.0;
+            for (long j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    acc += qt[i] * Sn[i * dv + j];
+                ot[j] = acc / den;
+            }
+            if (group) {
+                double mean = 0.0, var = 0.0;
+                for (long j = 0; j < dv; ++j)
+                    mean += ot[j];
+                mean /= (double)dv;
+                for (long j = 0; j < dv; ++j)
+                    var += (ot[j] - mean) * (ot[j] - mean);
+                var /= (double)dv;
+                const double rstd = 1.0 / sqrt(var + eps);
+                for (long j = 0; j < dv; ++j)
+                    ot[j] = (ot[j] - mean) * rstd;
+            }
+        }
+        free(Sn); free(n);
+    }
+    return err;
+}
+
+/*
  * Feature map phi(x) = elu(x) + 1, entrywise.
  *   [LA] "Linear attention by hand on three tokens": elu(x) = x for x > 0 and
  *        e^x - 1 otherwise, so phi(x) = x + 1 for x >= 0 and e^x for x < 0.

@@ -547,6 +547,70 @@ def pin_bwd_as_forwards():
     _close(dv_, f(oracle.retention_recurrent(f(k), f(q), f(do), gam)[0]), 1e-12, "dv as a reversed forward")
 
 
+# ---------------------------------------------------------------- NEXT-4: output normalisation
+def _parallel_floor(q, k, v, gam):
+    """numpy: (Q K^T (.) D) V divided by the row sums of Q K^T (.) D, floored at 1 in size."""
+    B, H, T = q.shape[:3]
+    out = np.zeros(q.shape[:3] + (v.shape[3],))
+    n = np.arange(T)
+    e = n[:, None] - n[None, :]
+    for h in range(H):
+        D = np.where(e >= 0, gam[h] ** np.maximum(e, 0), 0.0)
+        for b in range(B):
+            A = (q[b, h] @ k[b, h].T) * D
+            r = A.sum(axis=1)
+            out[b, h] = (A @ v[b, h]) / np.maximum(np.abs(r), 1.0)[:, None]
+    return out
+
+
+def pin_rowsum_floor_parallel():
+    """The floored read-out equals the parallel form divided by its own score
+    row sums (floor 1): the normaliser recurrence n_t = gamma n_{t-1} + k_t
+    ("Linear attention", box "An LSTM whose cell is linear attention", with
+    f = gamma, i = 1) must give exactly those row sums, sign included."""
+    rng = np.random.default_rng(23)
+    B, H, T, dk, dv = 2, 3, 45, 5, 4
+    gam = np.array([0.6, 0.95, 1.0])
+    q, k, v = 2.0 * _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dv))
+    _close(oracle.retention_normalized(q, k, v, gam), _parallel_floor(q, k, v, gam), 1e-12, "row-sum floor")
+
+
+def pin_rowsum_floor_inactive_for_small_scores():
+    """Scores whose row sums stay below 1 in size leave the output unchanged."""
+    rng = np.random.default_rng(24)
+    q, k, v = 1e-3 * _rand(rng, (1, 2, 30, 4)), _rand(rng, (1, 2, 30, 4)), _rand(rng, (1, 2, 30, 3))
+    gam = np.array([0.9, 0.5])
+    _close(oracle.retention_normalized(q, k, v, gam), oracle.retention_recurrent(q, k, v, gam)[0], 1e-15,
+           "floor inactive")
+
+
+def pin_rowsum_floor_scale_invariance():
+    """Once every row sum is at least 1 in size, scaling q leaves the output unchanged."""
+    rng = np.random.default_rng(25)
+    q, k, v = _rand(rng, (1, 2, 25, 4)), _rand(rng, (1, 2, 25, 4)), _rand(rng, (1, 2, 25, 3))
+    gam = np.array([0.8, 1.0])
+    big = oracle.retention_normalized(1e4 * q, k, v, gam)
+    bigger = oracle.retention_normalized(3e4 * q, k, v, gam)
+    _close(big, bigger, 1e-10, "scale invariance")
+
+
+def pin_groupnorm_rows():
+    """GroupNorm of the floored output: with eps = 0 every row has mean 0 and
+    mean square 1, and it is the textbook standardisation of the floored rows."""
+    rng = np.random.default_rng(26)
+    q, k, v = _rand(rng, (2, 2, 20, 6)), _rand(rng, (2, 2, 20, 6)), _rand(rng, (2, 2, 20, 8))
+    gam = np.array([0.9, 0.99])
+    g0 = oracle.retention_normalized(q, k, v, gam, group=True, eps=0.0)
+    _close(g0.mean(axis=-1), np.zeros(g0.shape[:3]), 1e-12, "row means")
+    _close((g0 ** 2).mean(axis=-1), np.ones(g0.shape[:3]), 1e-11, "row mean squares")
+    f = _parallel_floor(q, k, v, gam)
+    eps = 1e-3
+    mu = f.mean(axis=-1, keepdims=True)
+    var = ((f - mu) ** 2).mean(axis=-1, keepdims=True)
+    _close(oracle.retention_normalized(q, k, v, gam, group=True, eps=eps), (f - mu) / np.sqrt(var + eps), 1e-12,
+           "GroupNorm standardisation")
+
+
 # ---------------------------------------------------------------- P-10
 def pin_metric_calculator():
     """The pages' analytic counts.
@@ -599,5 +663,9 @@ ALL_PINS = [
     pin_bwd_finite_differences,
     pin_bwd_parallel_closed_form,
     pin_bwd_as_forwards,
+    pin_rowsum_floor_parallel,
+    pin_rowsum_floor_inactive_for_small_scores,
+    pin_rowsum_floor_scale_invariance,
+    pin_groupnorm_rows,
     pin_metric_calculator,
 ]

@@ -115,6 +115,21 @@ MUTANTS = [
     ("bwd_forward_state_drops_gamma",
      "Sf[i * dv + j] = g * Sf[i * dv + j] + kt[i] * vt[j];",
      "Sf[i * dv + j] = Sf[i * dv + j] + kt[i] * vt[j];"),
+    ("norm_floor_missing",
+     "const double den = fabs(r) > 1.0 ? fabs(r) : 1.0;",
+     "const double den = fabs(r) > 0.0 ? fabs(r) : 1.0;"),
+    ("norm_sign_kept",
+     "const double den = fabs(r) > 1.0 ? fabs(r) : 1.0;",
+     "const double den = fabs(r) > 1.0 ? r : 1.0;"),
+    ("norm_sum_not_decayed",
+     "n[i] = g * n[i] + kt[i];",
+     "n[i] = n[i] + kt[i];"),
+    ("norm_groupnorm_sample_variance",
+     "var /= (double)dv;",
+     "var /= (double)(dv - 1);"),
+    ("norm_groupnorm_eps_outside_sqrt",
+     "const double rstd = 1.0 / sqrt(var + eps);",
+     "const double rstd = 1.0 / (sqrt(var) + eps);"),
     ("linattn_rows_doubles_eps",
      "o[j] /= (rowsum + eps);",
      "o[j] /= (rowsum + 2.0 * eps);"),
