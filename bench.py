@@ -11,8 +11,8 @@ JSON line also carries the other measured parts of the path: the recurrent
 decode step (256 sequences x 32 heads, 128 x 128 fp32 state, 1000 consecutive
 steps), the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
 d = 64), the elu+1 decode step on the decode shapes, the backward pass of the
-long forward and the fp32 [4, 8, 2048, 64] forward, each with its own
-roofline figures.
+long forward, the long forward with the row-sum floor and GroupNorm fused,
+and the fp32 [4, 8, 2048, 64] forward, each with its own roofline figures.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -219,6 +219,27 @@ def main():
                          "algorithmic_bytes_per_launch": b_by},
         }
         del dout, gq, gk, gv, bws
+
+    # ---------------- the same forward with the row-sum floor and GroupNorm fused
+    if not args.no_components:
+        nout = torch.empty_like(v)
+        nws = torch.empty(max(rc.retention_fwd_normalized_workspace_bytes(w.B, w.H, w.T, w.dk, w.dv, w.chunk,
+                                                                          q.dtype), 1), dtype=torch.uint8, device=dev)
+
+        def nstep():
+            rc.retention_fwd_normalized(q, k, v, gamma, norm="group", chunk=w.chunk, out=nout, workspace=nws)
+
+        n_kern, n_wall = time_launches(nstep, max(args.steps // 2, 5), args.warmup)
+        n_by = M.fwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, final_state=False)
+        n_gbs = n_by / (n_kern * 1e-3) / 1e9
+        res["fwd_normalized"] = {
+            "workload": w.name + ", row-sum floor + GroupNorm fused (64-token chunks at d = 128)",
+            "ms_per_call": n_kern, "tokens_per_s": tokens / (n_wall * 1e-3), "ratio_to_forward": n_kern / kern_ms,
+            "roofline": {"kernel": "retention_fwd_normalized: seg_state_kernel + seg_walk_kernel<C=64, dk=128, dv=128, "
+                                   "GroupNorm>", "bound": "hbm", "achieved": n_gbs, "peak": M.PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": n_gbs / M.PEAK_HBM_GBS, "traffic": None},
+        }
+        del nout, nws
 
     # ---------------- decode step and linear attention
     if not args.no_components:

@@ -62,11 +62,15 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 4
+#define RET_ABI_VERSION 5
 
 /* element types of q, k, v, out */
 #define RET_F32 0
 #define RET_BF16 1
+
+/* output normalisations for retention_fwd_normalized */
+#define RET_NORM_ROWSUM 1 /* divide each row by its score row sum, floored at 1 in size */
+#define RET_NORM_GROUP 2  /* then GroupNorm over the row's dv features */
 
 /* feature maps for linear_attn_fwd */
 #define RET_PHI_ELU1 1 /* phi(x) = x + 1 for x > 0, e^x otherwise */
@@ -142,6 +146,39 @@ int retention_fwd_from_state(const void *q, const void *k, const void *v,
                              void *out, float *final_state, int B, int H, int T, int dk,
                              int dv, int dtype, void *workspace, size_t ws_bytes,
                              void *stream);
+
+/*
+ * retention_fwd_normalized -- retention_fwd (zero initial state) with the
+ * output normalisation of a RetNet layer fused into the chunk walk:
+ *
+ *   n_t   = gamma n_{t-1} + k_t             (decayed key sum, dk)
+ *   out_t = (q_t S_t) / max(|n_t . q_t|, 1)
+ *
+ * n_t . q_t is the row sum of the decayed scores, sum_{s<=t} gamma^(t-s)
+ * q_t . k_s ("Linear attention", box "An LSTM whose cell is linear
+ * attention", with forget gate gamma and input gate 1, and the remark that
+ * RetNet divides each score row by the absolute value of its sum clamped
+ * below at 1).  RET_NORM_GROUP then replaces each row by
+ * (out - mean(out)) / sqrt(var(out) + eps), population variance over the
+ * head's dv features, no learned gain or bias ("RetNet", the layer's
+ * optional GroupNorm).  Statistics are taken in fp32 before the single bf16
+ * rounding.
+ *
+ *   dtype    RET_BF16 only (RET_ERR_DTYPE otherwise)
+ *   norm     RET_NORM_ROWSUM or RET_NORM_GROUP (RET_ERR_SHAPE otherwise)
+ *   eps      GroupNorm epsilon, finite and >= 0 (1e-5 is usual)
+ *   workspace  retention_fwd_normalized_workspace_bytes(...) bytes
+ *   chunk    64 or 128; with dk = dv = 128 the walk uses 64 (LDS), same result
+ *   other arguments as retention_fwd (no final state)
+ */
+int retention_fwd_normalized(const void *q, const void *k, const void *v, const float *gamma,
+                             int chunk, int norm, float eps, void *out, int B, int H, int T,
+                             int dk, int dv, int dtype, void *workspace, size_t ws_bytes,
+                             void *stream);
+
+/* Workspace bytes retention_fwd_normalized needs (0: none or invalid).  Host only. */
+size_t retention_fwd_normalized_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
+                                                int dtype);
 
 /*
  * retention_bwd -- gradients of retention_fwd (zero initial state) with

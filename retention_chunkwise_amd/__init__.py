@@ -16,6 +16,7 @@ linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
 linear_attn_fwd(..., initial_state=(S, z), return_state=True) -> (out, S, z)
 linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place)
 retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv)
+retention_fwd_normalized(q, k, v, gamma, norm="group", eps=1e-5) -> out   (bf16)
 retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.autograd)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
 linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
@@ -34,7 +35,8 @@ import numpy as np
 import torch
 
 __all__ = ["retention_fwd", "retention_bwd", "retention", "retention_decode_step", "linear_attn_fwd",
-           "linear_attn_decode_step", "retention_bwd_workspace_bytes",
+           "linear_attn_decode_step", "retention_bwd_workspace_bytes", "retention_fwd_normalized",
+           "retention_fwd_normalized_workspace_bytes", "RET_NORM_ROWSUM", "RET_NORM_GROUP",
            "retention_fwd_workspace_bytes",
            "linear_attn_workspace_bytes", "RetentionError",
            "library_path", "load_library", "abi_version", "last_error"]
@@ -47,6 +49,8 @@ _lib = None
 RET_F32 = 0
 RET_BF16 = 1
 RET_PHI_ELU1 = 1
+RET_NORM_ROWSUM = 1
+RET_NORM_GROUP = 2
 ERRORS = {
     -1: "RET_ERR_NULL", -2: "RET_ERR_SHAPE", -3: "RET_ERR_DTYPE", -4: "RET_ERR_CHUNK",
     -5: "RET_ERR_GAMMA", -6: "RET_ERR_PHI", -7: "RET_ERR_ALIGN", -8: "RET_ERR_ALIAS",
@@ -94,6 +98,11 @@ def load_library():
             lib.linear_attn_decode_step.restype = i
             lib.retention_bwd.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
             lib.retention_bwd.restype = i
+            lib.retention_fwd_normalized.argtypes = [vp, vp, vp, fp, i, i, ctypes.c_float, vp, i, i, i, i, i, i, vp,
+                                                     sz, vp]
+            lib.retention_fwd_normalized.restype = i
+            lib.retention_fwd_normalized_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+            lib.retention_fwd_normalized_workspace_bytes.restype = sz
             lib.retention_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             lib.retention_bwd_workspace_bytes.restype = sz
             lib.linear_attn_fwd.restype = i
@@ -172,6 +181,13 @@ def retention_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chun
     return int(load_library().retention_fwd_workspace_bytes(B, H, T, dk, dv, int(chunk), code))
 
 
+def retention_fwd_normalized_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
+                                             dtype=torch.bfloat16) -> int:
+    """Bytes of device workspace retention_fwd_normalized needs (0: none)."""
+    code = RET_BF16 if dtype == torch.bfloat16 else RET_F32
+    return int(load_library().retention_fwd_normalized_workspace_bytes(B, H, T, dk, dv, int(chunk), code))
+
+
 def retention_bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, chunk: int = 64,
                                   dtype=torch.bfloat16) -> int:
     """Bytes of device workspace retention_bwd needs for these sizes (0: none)."""
@@ -234,6 +250,35 @@ def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
                                           B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return out, final_state
+
+
+def retention_fwd_normalized(q, k, v, gamma, norm: str = "group", eps: float = 1e-5, chunk: int = 64, out=None,
+                             workspace=None):
+    """Retention divided by its score row sum floored at 1 (norm="rowsum"),
+    then GroupNorm over each row (norm="group"), fused into the walk.
+
+    bf16 only.  q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv]."""
+    lib = load_library()
+    codes = {"rowsum": RET_NORM_ROWSUM, "group": RET_NORM_GROUP}
+    if norm not in codes:
+        raise ValueError("norm must be 'rowsum' or 'group'")
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, v.dtype)
+    g = _gamma_array(gamma, H)
+    dt = _dtype_code(q)
+    ws, nws = _workspace(lib.retention_fwd_normalized_workspace_bytes(B, H, T, dk, dv, int(chunk), dt), q.device,
+                         workspace)
+    rc = lib.retention_fwd_normalized(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), codes[norm],
+                                      float(eps), out.data_ptr(), B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
+    _raise(rc)
+    return out
 
 
 def retention_bwd(q, k, v, gamma, dout, chunk: int = 64, dq=None, dk=None, dv=None, workspace=None):

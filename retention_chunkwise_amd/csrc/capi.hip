@@ -286,6 +286,19 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
     return plan.ws_bytes;
 }
 
+// Chunk of the normalised walk: with dk = dv = 128 the 128-token walk and its
+// normaliser exceed the LDS, so it runs 64-token chunks (same result).
+int norm_chunk(int chunk, int dk, int dv) { return (chunk == 128 && dk == 128 && dv == 128) ? 64 : chunk; }
+
+size_t retention_fwd_normalized_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
+    if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
+        (dv != 64 && dv != 128) || dtype != RET_BF16)
+        return 0;
+    SegPlan plan;
+    if (!plan_segments(static_cast<long long>(B) * H, T, norm_chunk(chunk, dk, dv), dk, dv, true, &plan)) return 0;
+    return plan.ws_bytes;
+}
+
 size_t retention_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
     if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
         (dv != 64 && dv != 128) || !dtype_size(dtype))
@@ -480,6 +493,53 @@ int retention_fwd_from_state(const void* q, const void* k, const void* v, const 
                              int dk, int dv, int dtype, void* workspace, size_t ws_bytes, void* stream) {
     return ret_fwd_impl("retention_fwd_from_state", q, k, v, gamma, chunk, initial_state, out, final_state, B, H,
                         T, dk, dv, dtype, workspace, ws_bytes, stream);
+}
+
+int retention_fwd_normalized(const void* q, const void* k, const void* v, const float* gamma, int chunk, int norm,
+                             float eps, void* out, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                             size_t ws_bytes, void* stream) {
+    const char* fn = "retention_fwd_normalized";
+    if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
+    if (dtype != RET_BF16)
+        return fail(RET_ERR_DTYPE, "%s: bf16 only (dtype %d); the fused normalisation lives in the bf16 segment walk",
+                    fn, dtype);
+    if (norm != RET_NORM_ROWSUM && norm != RET_NORM_GROUP)
+        return fail(RET_ERR_SHAPE, "%s: norm must be RET_NORM_ROWSUM or RET_NORM_GROUP (got %d)", fn, norm);
+    if (!(eps >= 0.f) || isinf(eps)) return fail(RET_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
+    if (chunk != 64 && chunk != 128) return fail(RET_ERR_CHUNK, "%s: chunk must be 64 or 128 (got %d)", fn, chunk);
+    if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
+        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)", fn, ret::kMaxHeads, B,
+                    H, T);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
+    size_t nqk = 2, nv = 2;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv))
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
+    if (nqk > 0 && (!q || !k || !v || !out)) return fail(RET_ERR_NULL, "%s: q, k, v and out must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    float log2g[ret::kMaxHeads] = {};
+    int rc = check_gamma(fn, gamma, H, log2g);
+    if (rc) return rc;
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv), ro = range("out", out, nv);
+    for (const Range& in : {rq, rk, rv})
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
+    if (B == 0) return ok();
+    chunk = norm_chunk(chunk, dk, dv);
+    SegPlan plan;
+    if (!plan_segments(static_cast<long long>(B) * H, T, chunk, dk, dv, true, &plan))
+        return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if ((rc = check_workspace(fn, plan, workspace, ws_bytes, {rq, rk, rv, ro}))) return rc;
+    ret::SegArgs sa{};
+    sa.G = plan.G; sa.cps = plan.cps; sa.pieces = plan.pieces;
+    sa.q = q; sa.k = k; sa.v = v; sa.out = out;
+    sa.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+    sa.B = B; sa.H = H; sa.T = T; sa.gn_eps = eps;
+    memcpy(sa.log2g, log2g, sizeof(sa.log2g));
+    const hipError_t e = ret::launch_seg_norm(sa, chunk, dk, dv, norm == RET_NORM_GROUP, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
 }
 
 int retention_bwd(const void* q, const void* k, const void* v, const float* gamma, int chunk, const void* dout,

@@ -68,6 +68,7 @@ struct SegArgs {
     int scps;            // state-kernel blocks per segment (set by the launcher)
     int pieces;          // state-kernel workgroups per segment (divides scps)
     float eps;           // linear attention only
+    float gn_eps;        // GroupNorm epsilon (normalised retention with GroupNorm only)
     float log2g[kMaxHeads];
 };
 
@@ -87,6 +88,10 @@ hipError_t launch_seg_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_lin_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_lin_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
+// Retention with the row-sum floor, and GroupNorm when `group`.
+hipError_t launch_seg_norm(const SegArgs& a, int chunk, int dk, int dv, bool group, hipStream_t stream);
+hipError_t launch_seg_norm_c64(const SegArgs& a, int dk, int dv, bool group, hipStream_t stream);
+hipError_t launch_seg_norm_c128(const SegArgs& a, int dk, int dv, bool group, hipStream_t stream);
 // Time-reversed retention walk (token t read from and written to row T - 1 - t).
 hipError_t launch_seg_rev(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_rev_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);

@@ -57,7 +57,14 @@ using namespace ::ret::kc;
 
 constexpr int kThreads = 512;
 
-template <int C, int DK, int DV, bool LIN = false>
+// What a walk computes.  kModeRet: retention.  kModeLin: causal linear
+// attention, phi = elu+1 on q and k, gamma = 1, out / (row sum + eps).
+// kModeNorm: retention divided by its decayed score row sum floored at 1 in
+// size, the normaliser n = gamma^c n + sum zeta k carried beside the state.
+// kModeGroup: kModeNorm, then GroupNorm over each output row.
+constexpr int kModeRet = 0, kModeLin = 1, kModeNorm = 2, kModeGroup = 3;
+
+template <int C, int DK, int DV, int MODE = kModeRet>
 struct SCfg {
     static constexpr int NI = C / 16;              // 16-token tiles per chunk
     static constexpr int NS = (NI == 8) ? 2 : 1;   // query tiles per wave
@@ -72,7 +79,7 @@ struct SCfg {
     static constexpr int VIW = C * DV * 2 / 1024 / 8;  // same for V
     static constexpr int QF = DK / 32;             // Q operand blocks per query tile
     static constexpr int STATE = DK * DV;          // floats per state
-    static constexpr int WS = STATE + (LIN ? DK : 0);  // floats per workspace slot (state, normaliser)
+    static constexpr int WS = STATE + (MODE != kModeRet ? DK : 0);  // floats per slot (state, normaliser)
     static_assert(NI == 4 || NI == 8, "chunk must be 64 or 128");
     static_assert(NKT == 4 || NKT == 8, "dk must be 64 or 128");
     static_assert(NVT == 4 || NVT == 8, "dv must be 64 or 128");
@@ -237,10 +244,11 @@ __device__ __forceinline__ int dma_offset_rev(int w, int l) {
 // ring of NBUF LDS buffers, prefetching NBUF-1 blocks ahead.  Blocks run last
 // to first (the walk kernel then finds each segment's first chunks most
 // recently read).
-template <int C, int DK, int DV, bool LIN, int NBUF, bool REV>
+template <int C, int DK, int DV, int MODE, int NBUF, bool REV>
 __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kring, unsigned short* vring, int bh,
                                            int seg, int piece, float lg, int w) {
-    using Cf = SCfg<C, DK, DV, LIN>;
+    using Cf = SCfg<C, DK, DV, MODE>;
+    constexpr bool LIN = MODE == kModeLin, NRM = MODE >= kModeNorm, ZN = MODE != kModeRet;
     constexpr int NB = Cf::NB, NVT = Cf::NVT, NVH = Cf::NVH, SKT = Cf::SKT, KRU = Cf::KRU, VRU = Cf::VRU;
     constexpr int KIW = Cf::KIW, VIW = Cf::VIW;
     constexpr int OPS = KIW + VIW;  // DMA instructions a thread issues per block
@@ -332,8 +340,10 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
 #pragma unroll
                 for (int e = 0; e < 8; ++e) z[e] = zb[e] * bj;
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi)
+                for (int mi = 0; mi < SKT; ++mi) {
                     kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * p + mi) << 5) ^ lk.z16, lk, z);
+                    if constexpr (NRM) zsum[mi] += sum8(kz[mi][js]);  // decayed key sums (the normaliser)
+                }
             }
         }
 #pragma unroll
@@ -355,7 +365,7 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
 #pragma unroll
         for (int ni = 0; ni < NVH; ++ni)
             *reinterpret_cast<f32x4*>(wsj + ws_tile_off(SKT * p + mi, NVH * h + ni, NVT, l)) = acc[mi][ni];
-        if constexpr (LIN) {
+        if constexpr (ZN) {
             // lanes l, l^16, l^32, l^48 hold the four key groups of column 16m + l%16
             const float zt = sum_over_groups(zsum[mi]);
             if (h == 0 && g == 0) wsj[Cf::STATE + 16 * (SKT * p + mi) + (l & 15)] = zt;
@@ -391,9 +401,11 @@ __device__ __forceinline__ int perm_row(int dv) {
     return (dv & ~31) | (((dv >> 2) & 1) << 4) | (((dv >> 3) & 3) << 2) | (dv & 3);
 }
 
-template <int C, int DK, int DV, bool LIN, int P, bool OW, bool REV>
+template <int C, int DK, int DV, int MODE, int P, bool OW, bool REV>
 __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
-    using Cf = SCfg<C, DK, DV, LIN>;
+    using Cf = SCfg<C, DK, DV, MODE>;
+    constexpr bool LIN = MODE == kModeLin, NRM = MODE >= kModeNorm, GRP = MODE == kModeGroup;
+    constexpr bool ZN = MODE != kModeRet;  // a normaliser travels with the state
     constexpr int NI = Cf::NI, NS = Cf::NS, NB = Cf::NB, NVT = Cf::NVT, SKT = Cf::SKT;
     constexpr int KRU = Cf::KRU, VRU = Cf::VRU, QF = Cf::QF, KIW = Cf::KIW, VIW = Cf::VIW;
     constexpr int KRB = KRU * 16, VRB = VRU * 16;
@@ -473,7 +485,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 #pragma unroll
                     for (int n = 0; n < NVT; ++n)
                         sacc[mi][n] += wj * *reinterpret_cast<const f32x4*>(sj + ws_tile_off(SKT * P + mi, n, NVT, l));
-                    if constexpr (LIN) zacc[mi] += sj[Cf::STATE + 16 * (SKT * P + mi) + l16];
+                    if constexpr (ZN) zacc[mi] += wj * sj[Cf::STATE + 16 * (SKT * P + mi) + l16];
                 }
             }
         }
@@ -511,7 +523,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 for (int n = 0; n < NVT; ++n)
                     *reinterpret_cast<u16x4*>(sb + swz_byte<KRU>(perm_row(16 * n + l16), 2 * m + (g >> 1)) +
                                               (g & 1) * 8) = cvt4_bf16(sacc[mi][n]);
-                if (LIN && g == 0) tl.z[16 * m + l16] = zacc[mi];
+                if (ZN && g == 0) tl.z[16 * m + l16] = zacc[mi];
             }
         }
     };
@@ -649,24 +661,32 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                         pb[s][js] = cat_bf16(cvt4_bf16(lo), cvt4_bf16(hi));
                     }
 
-            // ---- linear attention: 1 / (row sum of P + phi(q) . z_prev + eps) per query
+            // ---- per-query divisors: the row sum of P (the bf16 weights the
+            // numerator uses) plus the earlier tokens' share, q . z_prev (decayed
+            // by xi for retention).  Linear attention: 1 / (sum + eps); the
+            // row-sum floor: 1 / max(|sum|, 1).
             float rden[NS];
-            if constexpr (LIN) {
+            if constexpr (ZN) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    float t = 0.f;
+                    float tp = 0.f, tz = 0.f;
 #pragma unroll
                     for (int js = 0; js < NB; ++js)
-                        if (2 * js <= its(s)) t += sum8(pb[s][js]);  // the bf16 weights the numerator uses
+                        if (2 * js <= its(s)) tp += sum8(pb[s][js]);
 #pragma unroll
                     for (int ks = 0; ks < QF; ++ks) {
                         const u16x8 e = __builtin_bit_cast(u16x8, qp[s][ks]);
                         const f32x4 z0 = *reinterpret_cast<const f32x4*>(tl.z + 32 * ks + 8 * g);
                         const f32x4 z1 = *reinterpret_cast<const f32x4*>(tl.z + 32 * ks + 8 * g + 4);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) t += bf2f(e[i]) * z0[i] + bf2f(e[i + 4]) * z1[i];
+                        for (int i = 0; i < 4; ++i) tz += bf2f(e[i]) * z0[i] + bf2f(e[i + 4]) * z1[i];
                     }
-                    rden[s] = 1.f / (sum_over_groups(t) + a.eps);
+                    if constexpr (LIN) {
+                        rden[s] = 1.f / (sum_over_groups(tp + tz) + a.eps);
+                    } else {
+                        const float r = sum_over_groups(tp + xi[s] * tz);
+                        rden[s] = 1.f / fmaxf(fabsf(r), 1.f);
+                    }
                 }
             }
 
@@ -675,10 +695,10 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             opaque(rowo);
             opaque(uo);
             const auto ro = make_rsrc(oh + mem_row0(t0, clen) * DV, clen * DV * 2);
-#pragma unroll
-            for (int pa = 0; pa < NPAIR; ++pa) {
+            // outputs of value-tile pair pa (columns 32 pa .. +31 in the permuted
+            // order) for this wave's query tiles, scaled by their divisors
+            auto pair_out = [&](int pa, f32x4 (&oacc)[NS][2]) {
                 const int uoa = uo ^ (pa << 6);
-                f32x4 oacc[NS][2];
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     const int n = 2 * pa + b;
@@ -703,15 +723,67 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                             if (2 * js <= its(s)) oacc[s][b] = mfma_bf16(vf, pb[s][js], oacc[s][b]);
                     }
                 }
+                if constexpr (ZN) {
 #pragma unroll
-                for (int s = 0; s < NS; ++s) {
-                    if constexpr (LIN) {
+                    for (int s = 0; s < NS; ++s) {
                         oacc[s][0] *= rden[s];
                         oacc[s][1] *= rden[s];
                     }
+                }
+            };
+            auto store_pair = [&](int pa, const f32x4 (&oacc)[NS][2]) {
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
                     const int row = row_in(16 * its(s) + l16, clen);  // rows past the end are dropped by the resource
                     bstore16_bf(ro, static_cast<unsigned>((row * DV + 32 * pa + 8 * g) * 2),
                                 cat_bf16(cvt4_bf16(oacc[s][0]), cvt4_bf16(oacc[s][1])));
+                }
+            };
+            if constexpr (GRP) {
+                // GroupNorm needs a whole row before any of it is stored, and the
+                // row does not fit in registers beside everything else: the first
+                // pass only sums each row (and its squares) over the value tiles,
+                // the second recomputes the products and stores standardised values.
+                float s1[NS], s2[NS];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) s1[s] = s2[s] = 0.f;
+#pragma unroll
+                for (int pa = 0; pa < NPAIR; ++pa) {
+                    f32x4 oacc[NS][2];
+                    pair_out(pa, oacc);
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                s1[s] += oacc[s][b][r];
+                                s2[s] += oacc[s][b][r] * oacc[s][b][r];
+                            }
+                }
+                float mu[NS], rstd[NS];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) {
+                    mu[s] = sum_over_groups(s1[s]) * (1.f / DV);
+                    const float var = fmaxf(sum_over_groups(s2[s]) * (1.f / DV) - mu[s] * mu[s], 0.f);
+                    rstd[s] = 1.f / sqrtf(var + a.gn_eps);
+                }
+#pragma unroll
+                for (int pa = 0; pa < NPAIR; ++pa) {
+                    f32x4 oacc[NS][2];
+                    pair_out(pa, oacc);
+#pragma unroll
+                    for (int s = 0; s < NS; ++s)
+#pragma unroll
+                        for (int b = 0; b < 2; ++b) oacc[s][b] = (oacc[s][b] - mu[s]) * rstd[s];
+                    store_pair(pa, oacc);
+                }
+            } else {
+#pragma unroll
+                for (int pa = 0; pa < NPAIR; ++pa) {
+                    f32x4 oacc[NS][2];
+                    pair_out(pa, oacc);
+                    store_pair(pa, oacc);
                 }
             }
             lds_barrier();  // every O-wave is done reading the old state copy
@@ -753,12 +825,15 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                         }
                     }
 #pragma unroll
-                    for (int mi = 0; mi < SKT; ++mi)
+                    for (int mi = 0; mi < SKT; ++mi) {
                         kz[mi][js] = kt_scaled<KRU>(kb, js, ((SKT * P + mi) << 5) ^ lk.z16, lk, z);
+                        if constexpr (NRM) zsum[mi] += sum8(kz[mi][js]);  // decayed key sums
+                    }
                 }
             }
 
-            // ---- S = gamma^c S + (zeta K)^T V   (z += sum phi(k) for linear attention)
+            // ---- S = gamma^c S + (zeta K)^T V   (z += sum phi(k) for linear attention,
+            // z = gamma^c z + sum zeta k for the row-sum floor)
             const float gc = tail ? uni(ex2(static_cast<float>(clen) * lg)) : gC;
 #pragma unroll
             for (int n = 0; n < NVT; ++n) {
@@ -774,10 +849,10 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                     for (int mi = 0; mi < SKT; ++mi) sacc[mi][n] = mfma_bf16(kz[mi][js], vf, sacc[mi][n]);
                 }
             }
-            if constexpr (LIN) {
+            if constexpr (ZN) {
                 // lanes l, l^16, l^32, l^48 hold the four key groups of column 16m + l%16
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi) zacc[mi] += sum_over_groups(zsum[mi]);
+                for (int mi = 0; mi < SKT; ++mi) zacc[mi] = (LIN ? 1.f : gc) * zacc[mi] + sum_over_groups(zsum[mi]);
             }
             lds_barrier();  // every O-wave is done reading the old state copy
             write_state_copy();
@@ -817,28 +892,30 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 constexpr int kStateBlock = 64;
 constexpr int kStateRing = 4;
 
-template <int DK, int DV, bool LIN, bool REV>
+template <int DK, int DV, int MODE, bool REV>
 __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a) {
+    constexpr bool LIN = MODE == kModeLin;
     __shared__ __attribute__((aligned(16))) unsigned short kring[kStateRing * kStateBlock * DK];
     __shared__ __attribute__((aligned(16))) unsigned short vring[kStateRing * kStateBlock * DV];
     const int slots = (a.G - 1) * a.pieces;
     const int bh = blockIdx.x / slots, slot = blockIdx.x % slots;
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    state_body<kStateBlock, DK, DV, LIN, kStateRing, REV>(a, kring, vring, bh, slot / a.pieces, slot % a.pieces, lg,
+    state_body<kStateBlock, DK, DV, MODE, kStateRing, REV>(a, kring, vring, bh, slot / a.pieces, slot % a.pieces, lg,
                                                           wave);
 }
 
-template <int C, int DK, int DV, bool LIN, bool REV>
+template <int C, int DK, int DV, int MODE, bool REV>
 __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) {
+    constexpr bool LIN = MODE == kModeLin;
     __shared__ __attribute__((aligned(16))) unsigned short k0[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short k1[C * DK];
     __shared__ __attribute__((aligned(16))) unsigned short v0[C * DV];
     __shared__ __attribute__((aligned(16))) unsigned short v1[C * DV];
     __shared__ __attribute__((aligned(16))) unsigned short st[DV * DK];
     float* zp = nullptr;
-    if constexpr (LIN) {
-        __shared__ __attribute__((aligned(16))) float zs[DK];  // only linear attention carries z
+    if constexpr (MODE != kModeRet) {
+        __shared__ __attribute__((aligned(16))) float zs[DK];  // only the normalised modes carry z
         zp = zs;
     }
     const STiles tl{{k0, k1}, {v0, v1}, st, zp};
@@ -846,33 +923,33 @@ __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) 
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: walk_body<C, DK, DV, LIN, 0, true, REV>(a, tl, bh, seg, lg); break;
-        case 1: walk_body<C, DK, DV, LIN, 1, true, REV>(a, tl, bh, seg, lg); break;
-        case 2: walk_body<C, DK, DV, LIN, 2, true, REV>(a, tl, bh, seg, lg); break;
-        case 3: walk_body<C, DK, DV, LIN, 3, true, REV>(a, tl, bh, seg, lg); break;
-        case 4: walk_body<C, DK, DV, LIN, 0, false, REV>(a, tl, bh, seg, lg); break;
-        case 5: walk_body<C, DK, DV, LIN, 1, false, REV>(a, tl, bh, seg, lg); break;
-        case 6: walk_body<C, DK, DV, LIN, 2, false, REV>(a, tl, bh, seg, lg); break;
-        default: walk_body<C, DK, DV, LIN, 3, false, REV>(a, tl, bh, seg, lg); break;
+        case 0: walk_body<C, DK, DV, MODE, 0, true, REV>(a, tl, bh, seg, lg); break;
+        case 1: walk_body<C, DK, DV, MODE, 1, true, REV>(a, tl, bh, seg, lg); break;
+        case 2: walk_body<C, DK, DV, MODE, 2, true, REV>(a, tl, bh, seg, lg); break;
+        case 3: walk_body<C, DK, DV, MODE, 3, true, REV>(a, tl, bh, seg, lg); break;
+        case 4: walk_body<C, DK, DV, MODE, 0, false, REV>(a, tl, bh, seg, lg); break;
+        case 5: walk_body<C, DK, DV, MODE, 1, false, REV>(a, tl, bh, seg, lg); break;
+        case 6: walk_body<C, DK, DV, MODE, 2, false, REV>(a, tl, bh, seg, lg); break;
+        default: walk_body<C, DK, DV, MODE, 3, false, REV>(a, tl, bh, seg, lg); break;
     }
 }
 
 // LDS available to one workgroup on gfx950, and what the walk kernel takes.
 constexpr int kLdsBytes = 160 * 1024;
-template <int C, int DK, int DV, bool LIN>
+template <int C, int DK, int DV, int MODE>
 constexpr bool walk_fits() {
-    return 2 * C * DK * 2 + 2 * C * DV * 2 + DV * DK * 2 + (LIN ? DK * 4 : 0) <= kLdsBytes;
+    return 2 * C * DK * 2 + 2 * C * DV * 2 + DV * DK * 2 + (MODE != kModeRet ? DK * 4 : 0) <= kLdsBytes;
 }
 // Variants that are built: they fit in LDS, and linear attention with dk = 128
 // runs with 64-token chunks (at 128 its walk kernel would spill registers).
-template <int C, int DK, int DV, bool LIN>
+template <int C, int DK, int DV, int MODE>
 constexpr bool walk_supported() {
-    return walk_fits<C, DK, DV, LIN>() && !(LIN && C == 128 && DK == 128);
+    return walk_fits<C, DK, DV, MODE>() && !(MODE == kModeLin && C == 128 && DK == 128);
 }
 
-template <int C, int DK, int DV, bool LIN, bool REV>
+template <int C, int DK, int DV, int MODE, bool REV>
 hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
-    if constexpr (!walk_supported<C, DK, DV, LIN>()) {
+    if constexpr (!walk_supported<C, DK, DV, MODE>()) {
         return hipErrorInvalidConfiguration;
     } else {
     const long long bh = static_cast<long long>(a.B) * a.H;
@@ -881,12 +958,14 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     if (a.G > 1) {
         SegArgs sa = a;
         sa.scps = a.cps * (C / kStateBlock);
-        hipLaunchKernelGGL((seg_state_kernel<DK, DV, LIN, REV>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
+        // the state kernel is the same for both normalised retention modes
+        constexpr int SMODE = (MODE == kModeGroup) ? kModeNorm : MODE;
+        hipLaunchKernelGGL((seg_state_kernel<DK, DV, SMODE, REV>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
                            dim3(kThreads), 0, stream, sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, LIN, REV>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, MODE, REV>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
     }
@@ -894,13 +973,13 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
 
 // REV: the walk runs over the time-reversed sequence (token t read from and
 // written to row T - 1 - t); the gradients of keys and values are such walks.
-template <int C, bool LIN, bool REV = false>
+template <int C, int MODE, bool REV = false>
 hipError_t launch_chunk(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    static_assert(!(LIN && REV), "time-reversed walks are retention only");
-    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, LIN, REV>(a, stream);
-    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, LIN, REV>(a, stream);
-    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, LIN, REV>(a, stream);
-    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, LIN, REV>(a, stream);
+    static_assert(!(MODE != kModeRet && REV), "time-reversed walks are retention only");
+    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, MODE, REV>(a, stream);
+    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, MODE, REV>(a, stream);
+    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, MODE, REV>(a, stream);
+    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, MODE, REV>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -4,7 +4,7 @@
 namespace ret {
 
 hipError_t launch_seg_lin_c64(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    return seg::launch_chunk<64, true>(a, dk, dv, stream);
+    return seg::launch_chunk<64, seg::kModeLin>(a, dk, dv, stream);
 }
 
 }  // namespace ret

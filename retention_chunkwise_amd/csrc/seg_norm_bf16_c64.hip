@@ -1,0 +1,12 @@
+// seg_norm_bf16_c64.hip -- segment-split retention with the row-sum floor
+// (and optionally GroupNorm) fused into the output, bf16, chunk 64.
+#include "seg_kernel.h"
+
+namespace ret {
+
+hipError_t launch_seg_norm_c64(const SegArgs& a, int dk, int dv, bool group, hipStream_t stream) {
+    return group ? seg::launch_chunk<64, seg::kModeGroup>(a, dk, dv, stream)
+                 : seg::launch_chunk<64, seg::kModeNorm>(a, dk, dv, stream);
+}
+
+}  // namespace ret

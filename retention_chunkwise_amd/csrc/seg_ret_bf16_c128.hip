@@ -4,7 +4,7 @@
 namespace ret {
 
 hipError_t launch_seg_c128(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    return seg::launch_chunk<128, false>(a, dk, dv, stream);
+    return seg::launch_chunk<128, seg::kModeRet>(a, dk, dv, stream);
 }
 
 }  // namespace ret

@@ -4,7 +4,7 @@
 namespace ret {
 
 hipError_t launch_seg_c64(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    return seg::launch_chunk<64, false>(a, dk, dv, stream);
+    return seg::launch_chunk<64, seg::kModeRet>(a, dk, dv, stream);
 }
 
 }  // namespace ret

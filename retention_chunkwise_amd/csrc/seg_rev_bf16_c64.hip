@@ -5,7 +5,7 @@
 namespace ret {
 
 hipError_t launch_seg_rev_c64(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    return seg::launch_chunk<64, false, true>(a, dk, dv, stream);
+    return seg::launch_chunk<64, seg::kModeRet, true>(a, dk, dv, stream);
 }
 
 }  // namespace ret

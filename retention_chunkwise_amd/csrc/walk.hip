@@ -37,6 +37,12 @@ hipError_t launch_walk(const WalkArgs& a, bool bf16, int chunk, int dk, int nt, 
                    : launch_walk_ret_f32(a, chunk, dk, nt, stream);
 }
 
+hipError_t launch_seg_norm(const SegArgs& a, int chunk, int dk, int dv, bool group, hipStream_t stream) {
+    if (chunk == 64) return launch_seg_norm_c64(a, dk, dv, group, stream);
+    if (chunk == 128) return launch_seg_norm_c128(a, dk, dv, group, stream);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_seg_rev(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream) {
     if (chunk == 64) return launch_seg_rev_c64(a, dk, dv, stream);
     if (chunk == 128) return launch_seg_rev_c128(a, dk, dv, stream);

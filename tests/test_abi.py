@@ -311,3 +311,38 @@ def test_retention_bwd_workspace_and_empty_batch():
     n2 = lib.retention_bwd_workspace_bytes(1, 4, 4096, 64, 128, 64, rc.RET_F32)
     assert n2 >= lib.retention_fwd_workspace_bytes(1, 4, 4096, 64, 128, 64, rc.RET_F32)
     assert _bwd(lib, B=0) == 0
+
+
+# ---------------------------------------------------------------- normalised forward
+def _nrm(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9, 0.9]), chunk=64, norm=rc.RET_NORM_GROUP, eps=1e-5,
+             out=FAKE * 4, B=1, H=2, T=16, dk=64, dv=64, dtype=rc.RET_BF16, ws=None, nws=0)
+    a.update(kw)
+    return lib.retention_fwd_normalized(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["norm"], a["eps"],
+                                        a["out"], a["B"], a["H"], a["T"], a["dk"], a["dv"], a["dtype"], a["ws"],
+                                        a["nws"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=rc.RET_F32), -3),       # bf16 only
+    (dict(norm=0), -2),
+    (dict(norm=3), -2),
+    (dict(eps=-1.0), -2),
+    (dict(chunk=96), -4),
+    (dict(gamma=_gam([0.9, 2.0])), -5),
+    (dict(out=FAKE * 2), -8),
+    (dict(v=FAKE * 3 + 2), -7),
+    (dict(T=65536, dk=128, dv=128, q=FAKE, k=FAKE * 1024, v=FAKE * 2048, out=FAKE * 4096), -9),
+])
+def test_retention_fwd_normalized_rejects(kw, code):
+    lib = _lib()
+    assert _nrm(lib, **kw) == code
+    assert "retention_fwd_normalized" in lib.retention_last_error().decode()
+
+
+def test_retention_fwd_normalized_workspace():
+    lib = _lib()
+    n = lib.retention_fwd_normalized_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    assert n > 0 and n % ((128 * 128 + 128) * 4) == 0
+    assert lib.retention_fwd_normalized_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_F32) == 0
+    assert _nrm(lib, B=0) == 0

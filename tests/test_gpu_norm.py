@@ -1,0 +1,100 @@
+"""Retention with the row-sum floor and GroupNorm fused into the walk
+(retention_fwd_normalized) against the fp64 oracle (needs a gfx950 GPU).
+
+The oracle follows the normaliser recurrence n_t = gamma n_{t-1} + k_t and
+divides each read-out by max(|n_t . q_t|, 1), then standardises each row for
+GroupNorm.  Cases: both normalisations, chunks 64 and 128, every (dk, dv)
+pair, several segment counts, ragged and short lengths, decays from 0.02 to 1,
+inputs scaled so that the floor is active for some rows and not for others,
+and the long bf16 shape on sampled heads.  Tolerance: relative Frobenius
+error 2e-2 (bf16 inputs, fp32 accumulation, one bf16 rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import retention_chunkwise_amd as rc
+from retention_chunkwise_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def _inputs(seed, B, H, T, dk, dv, qscale=1.0):
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", scale=1.0)
+    inp = wl.make_inputs(w, seed)
+    # q scaled so the score row sums straddle the floor of 1
+    inp["q"] = (inp["q"].float() * (qscale / np.sqrt(dk))).to(torch.bfloat16)
+    inp["k"] = (inp["k"].float() / np.sqrt(dk)).to(torch.bfloat16)
+    return w, inp
+
+
+def _run(inp, norm, chunk, monkeypatch, G=None, eps=1e-5):
+    monkeypatch.delenv("RET_FWD_PATH", raising=False)
+    if G is None:
+        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
+    else:
+        monkeypatch.setenv("RET_FWD_SEGMENTS", str(G))
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    out = rc.retention_fwd_normalized(q, k, v, inp["gamma"], norm=norm, eps=eps, chunk=chunk)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+def _check(tag, out, inp, norm, eps=1e-5):
+    ref = oracle.retention_normalized(inp["q"], inp["k"], inp["v"], inp["gamma"], group=(norm == "group"), eps=eps,
+                                      nthreads=8)
+    e = oracle.rel_frobenius(out, ref)
+    print(f"[parity] {tag}: rel_fro={e:.3e} (tol {TOL:.0e})", flush=True)
+    assert e <= TOL and np.isfinite(out).all(), tag
+
+
+@pytest.mark.parametrize("norm", ["rowsum", "group"])
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, None), (1333, 4), (300, 1)])
+def test_norm_small_full(norm, chunk, dk, dv, T, G, monkeypatch):
+    w, inp = _inputs(61, 2, 3, T, dk, dv, qscale=2.0)
+    out = _run(inp, norm, chunk, monkeypatch, G)
+    _check(f"norm {norm} C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, norm)
+
+
+@pytest.mark.parametrize("norm", ["rowsum", "group"])
+@pytest.mark.parametrize("T", [1, 5, 64, 65, 129])
+def test_norm_short_and_ragged(norm, T, monkeypatch):
+    w, inp = _inputs(62, 1, 2, T, 64, 64, qscale=3.0)
+    out = _run(inp, norm, 64, monkeypatch, 2)
+    _check(f"norm {norm} short T={T}", out, inp, norm)
+
+
+@pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
+@pytest.mark.parametrize("qscale", [0.05, 20.0])
+def test_norm_gamma_and_floor(gval, qscale, monkeypatch):
+    """Small q keeps every row sum under the floor (output = plain retention,
+    then GroupNorm); large q puts every row past it."""
+    w, inp = _inputs(63, 1, 2, 900, 64, 64, qscale=qscale)
+    inp["gamma"] = np.full(2, gval, dtype=np.float32)
+    for norm in ("rowsum", "group"):
+        out = _run(inp, norm, 64, monkeypatch, 3)
+        _check(f"norm {norm} gamma={gval} qscale={qscale}", out, inp, norm)
+
+
+def test_norm_group_eps(monkeypatch):
+    w, inp = _inputs(64, 1, 2, 500, 64, 64, qscale=2.0)
+    out = _run(inp, "group", 64, monkeypatch, None, eps=0.5)
+    _check("norm group eps=0.5", out, inp, "group", eps=0.5)
+
+
+def test_norm_long_sequence_sampled_heads(monkeypatch):
+    """[1, 32, 65536, 128] bf16: heads 0 and 31 against the oracle in full."""
+    w = wl.WORKLOADS["ret_fwd_long_bf16"]
+    inp = wl.make_inputs(w, 0)
+    out = _run(inp, "group", 128, monkeypatch, None)
+    for h in (0, w.H - 1):
+        ref = oracle.retention_normalized(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1],
+                                          inp["gamma"][h:h + 1], group=True, eps=1e-5)
+        e = oracle.rel_frobenius(out[:, h:h + 1], ref)
+        print(f"[parity] norm group long head {h}: rel_fro={e:.3e}", flush=True)
+        assert e <= TOL
