@@ -232,12 +232,14 @@ def main():
         n_kern, n_wall = time_launches(nstep, max(args.steps // 2, 5), args.warmup)
         n_by = M.fwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, final_state=False)
         n_gbs = n_by / (n_kern * 1e-3) / 1e9
+        n_tr = measured_traffic("fwd_normalized_ret_fwd_long_bf16", FWD_SOURCES)
         res["fwd_normalized"] = {
             "workload": w.name + ", row-sum floor + GroupNorm fused (64-token chunks at d = 128)",
             "ms_per_call": n_kern, "tokens_per_s": tokens / (n_wall * 1e-3), "ratio_to_forward": n_kern / kern_ms,
             "roofline": {"kernel": "retention_fwd_normalized: seg_state_kernel + seg_walk_kernel<C=64, dk=128, dv=128, "
                                    "GroupNorm>", "bound": "hbm", "achieved": n_gbs, "peak": M.PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": n_gbs / M.PEAK_HBM_GBS, "traffic": None},
+                         "unit": "GB/s", "frac": n_gbs / M.PEAK_HBM_GBS,
+                         "traffic": (n_tr["bytes_per_launch"] if n_tr else None)},
         }
         del nout, nws
 
