@@ -105,12 +105,13 @@ def _bind(lib):
                                          ctypes.c_int]
     lib.oracle_retention_normalized.argtypes = [_D, _D, _D, _D, _l, _l, _l, _l, _l, ctypes.c_int,
                                                 ctypes.c_double, _D, ctypes.c_int]
+    lib.oracle_gla_recurrent.argtypes = [_D, _D, _D, _D, _l, _l, _l, _l, _l, _D, _D, ctypes.c_int]
     lib.oracle_threads_used.argtypes = [ctypes.c_int]
     for name in ("oracle_retention_recurrent", "oracle_retention_parallel",
                  "oracle_retention_rows", "oracle_retention_chunkwise",
                  "oracle_decode_steps", "oracle_linattn_recurrent",
                  "oracle_linattn_decode_steps", "oracle_retention_bwd",
-                 "oracle_retention_normalized",
+                 "oracle_retention_normalized", "oracle_gla_recurrent",
                  "oracle_linattn_parallel", "oracle_linattn_rows",
                  "oracle_threads_used"):
         getattr(lib, name).restype = ctypes.c_int
@@ -224,6 +225,21 @@ def decode_steps(q, k, v, gamma, state, nsteps: int = 1, nthreads: int = 1):
                                       dk, dv, int(nsteps), int(nthreads)),
            "oracle_decode_steps")
     return out, S
+
+
+def gla_recurrent(q, k, v, log_gate, nthreads: int = 1):
+    """Gated linear attention with per-token, per-key-channel gates
+    exp(log_gate) ("Efficient and Sparse Transformers", section "Gated Linear
+    Attention"), recurrent form.  Returns (out [B,H,T,dv], final S [B,H,dk,dv])."""
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(log_gate)
+    B, H, T, dk, dv = _shape4(q, k, v)
+    if g.shape != (B, H, T, dk):
+        raise ValueError("log_gate must be [B,H,T,dk]")
+    out = np.zeros((B, H, T, dv))
+    fs = np.zeros((B, H, dk, dv))
+    _check(load().oracle_gla_recurrent(_p(q), _p(k), _p(v), _p(g), B, H, T, dk, dv, _p(out), _p(fs),
+                                       int(nthreads)), "oracle_gla_recurrent")
+    return out, fs
 
 
 GROUPNORM_EPS = 1e-5

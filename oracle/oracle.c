@@ -435,6 +435,55 @@ int oracle_retention_normalized(const double *q, const double *k, const double *
 }
 
 /*
+ * Gated linear attention with a per-token, per-key-channel gate, recurrent form.
+ *   [ESF] section "Gated Linear Attention: Toward Input-Dependent Forgetting":
+ *        the fixed decay of RetNet becomes a data-dependent gate G_t applied
+ *        element-wise to the state, S_t = G_t (.) S_{t-1} + k_t^T v_t, with
+ *        RetNet the case G_t = gamma 1 and plain linear attention G_t = 1; the
+ *        gate lets the model forget some channels and keep others.
+ * Here G_t[i][j] = alpha_t[i] (one gate per key channel, shared by the value
+ * columns), given as log-gates lg = log alpha in (-inf, 0]:
+ *   S_t[i][j] = exp(lg_t[i]) S_{t-1}[i][j] + k_t[i] v_t[j],   o_t = q_t S_t.
+ * lg: [B][H][T][dk].  final_state may be NULL.
+ */
+int oracle_gla_recurrent(const double *q, const double *k, const double *v,
+                         const double *lg, long B, long H, long T, long dk, long dv,
+                         double *out, double *final_state, int nthreads)
+{
+    if (!q || !k || !v || !lg || !out || B < 0 || H <= 0 || T < 0 || dk <= 0 || dv <= 0)
+        return ORACLE_ERR_ARG;
+    int err = ORACLE_OK;
+#pragma omp parallel for num_threads(oracle_threads(nthreads)) schedule(dynamic, 1)
+    for (long bh = 0; bh < B * H; ++bh) {
+        double *Sg = (double *)calloc((size_t)(dk * dv), sizeof(double));
+        if (!Sg) {
+            err = ORACLE_ERR_NOMEM;
+            continue;
+        }
+        for (long t = 0; t < T; ++t) {
+            const double *qt = q + (bh * T + t) * dk, *kt = k + (bh * T + t) * dk;
+            const double *vt = v + (bh * T + t) * dv, *gt = lg + (bh * T + t) * dk;
+            double *ot = out + (bh * T + t) * dv;
+            for (long i = 0; i < dk; ++i) {
+                const double a = exp(gt[i]);
+                for (long j = 0; j < dv; ++j)
+                    Sg[i * dv + j] = a * Sg[i * dv + j] + kt[i] * vt[j];
+            }
+            for (long j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (long i = 0; i < dk; ++i)
+                    acc += qt[i] * Sg[i * dv + j];
+                ot[j] = acc;
+            }
+        }
+        if (final_state)
+            memcpy(final_state + bh * dk * dv, Sg, (size_t)(dk * dv) * sizeof(double));
+        free(Sg);
+    }
+    return err;
+}
+
+/*
  * Feature map phi(x) = elu(x) + 1, entrywise.
  *   [LA] "Linear attention by hand on three tokens": elu(x) = x for x > 0 and
  *        e^x - 1 otherwise, so phi(x) = x + 1 for x >= 0 and e^x for x < 0.

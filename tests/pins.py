@@ -611,6 +611,62 @@ def pin_groupnorm_rows():
            "GroupNorm standardisation")
 
 
+# ---------------------------------------------------------------- NEXT-3: GLA gate
+def pin_gla_special_cases():
+    """A constant gate gamma is RetNet and a gate of 1 is plain linear
+    attention ("Efficient and Sparse Transformers", section "Gated Linear
+    Attention": G_t = gamma 1 and G_t = 1)."""
+    rng = np.random.default_rng(27)
+    B, H, T, dk, dv = 2, 3, 37, 5, 4
+    q, k, v = _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dv))
+    gam = np.array([0.9, 0.5, 1.0])
+    lg = np.broadcast_to(np.log(gam)[None, :, None, None], (B, H, T, dk)).copy()
+    o, S = oracle.gla_recurrent(q, k, v, lg)
+    ro, rS = oracle.retention_recurrent(q, k, v, gam)
+    _close(o, ro, 1e-12, "GLA constant gate = retention")
+    _close(S, rS, 1e-12, "GLA constant gate state")
+    o1, _ = oracle.gla_recurrent(q, k, v, np.zeros((B, H, T, dk)))
+    n = np.arange(T)
+    L = (n[:, None] >= n[None, :]).astype(float)
+    for b in range(B):
+        for h in range(H):
+            _close(o1[b, h], ((q[b, h] @ k[b, h].T) * L) @ v[b, h], 1e-11, "GLA unit gate = masked linear attention")
+
+
+def pin_gla_parallel_form():
+    """Brute force with per-channel cumulative log-gates:
+    o_i = sum_{j<=i} sum_c q_i[c] k_j[c] exp(sum_{s=j+1..i} lg_s[c]) v_j, on
+    random gates (d_k != d_v, ragged length)."""
+    rng = np.random.default_rng(28)
+    B, H, T, dk, dv = 1, 2, 29, 6, 3
+    q, k, v = _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dk)), _rand(rng, (B, H, T, dv))
+    lg = -rng.uniform(0.0, 1.5, (B, H, T, dk))
+    o, S = oracle.gla_recurrent(q, k, v, lg)
+    for h in range(H):
+        cum = np.cumsum(lg[0, h], axis=0)  # cum[i] = sum_{s<=i}
+        exp_ = np.zeros((T, T, dk))
+        for i in range(T):
+            for j in range(i + 1):
+                exp_[i, j] = np.exp(cum[i] - cum[j])
+        A = np.einsum("ic,jc,ijc->ij", q[0, h], k[0, h], exp_)
+        _close(o[0, h], A @ v[0, h], 1e-11, f"GLA parallel form h={h}")
+        Sref = np.einsum("jc,jv,jc->cv", k[0, h], v[0, h], np.exp(cum[-1][None, :] - cum))
+        _close(S[0, h], Sref, 1e-11, f"GLA final state h={h}")
+
+
+def pin_gla_channel_reset():
+    """A gate of 0 (a very negative log-gate) on every channel at token r
+    erases the past: the outputs from r on equal a run that starts at r."""
+    rng = np.random.default_rng(29)
+    T, r = 30, 11
+    q, k, v = _rand(rng, (1, 1, T, 4)), _rand(rng, (1, 1, T, 4)), _rand(rng, (1, 1, T, 5))
+    lg = -rng.uniform(0.0, 0.5, (1, 1, T, 4))
+    lg[0, 0, r] = -800.0
+    o, _ = oracle.gla_recurrent(q, k, v, lg)
+    o2, _ = oracle.gla_recurrent(q[:, :, r:], k[:, :, r:], v[:, :, r:], lg[:, :, r:])
+    _close(o[:, :, r:], o2, 1e-12, "GLA reset")
+
+
 # ---------------------------------------------------------------- P-10
 def pin_metric_calculator():
     """The pages' analytic counts.
@@ -667,5 +723,8 @@ ALL_PINS = [
     pin_rowsum_floor_inactive_for_small_scores,
     pin_rowsum_floor_scale_invariance,
     pin_groupnorm_rows,
+    pin_gla_special_cases,
+    pin_gla_parallel_form,
+    pin_gla_channel_reset,
     pin_metric_calculator,
 ]

@@ -130,6 +130,15 @@ MUTANTS = [
     ("norm_groupnorm_eps_outside_sqrt",
      "const double rstd = 1.0 / sqrt(var + eps);",
      "const double rstd = 1.0 / (sqrt(var) + eps);"),
+    ("gla_gate_on_value_axis",
+     "const double a = exp(gt[i]);\n                for (long j = 0; j < dv; ++j)\n                    Sg[i * dv + j] = a * Sg[i * dv + j] + kt[i] * vt[j];",
+     "for (long j = 0; j < dv; ++j)\n                    Sg[i * dv + j] = exp(gt[j % dk]) * Sg[i * dv + j] + kt[i] * vt[j];"),
+    ("gla_gate_applied_after_write",
+     "Sg[i * dv + j] = a * Sg[i * dv + j] + kt[i] * vt[j];",
+     "Sg[i * dv + j] = a * (Sg[i * dv + j] + kt[i] * vt[j]);"),
+    ("gla_gate_not_exponentiated",
+     "const double a = exp(gt[i]);",
+     "const double a = 1.0 + gt[i];"),
     ("linattn_rows_doubles_eps",
      "o[j] /= (rowsum + eps);",
      "o[j] /= (rowsum + 2.0 * eps);"),
