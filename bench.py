@@ -12,7 +12,8 @@ decode step (256 sequences x 32 heads, 128 x 128 fp32 state, 1000 consecutive
 steps), the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
 d = 64), the elu+1 decode step on the decode shapes, the backward pass of the
 long forward, the long forward with the row-sum floor and GroupNorm fused,
-and the fp32 [4, 8, 2048, 64] forward, each with its own roofline figures.
+the fp32 [4, 8, 2048, 64] forward and gated linear attention on that shape,
+each with its own roofline figures.
 
 Only one GPU is used; --gpus above 1 exits with a message.
 """
@@ -344,6 +345,31 @@ def main():
                          "frac": f_tf / M.PEAK_TFLOPS["f32"], "traffic": None},
         }
         del fq, fk, fv, fout, ffs
+
+    # ---------------- gated linear attention (per-token, per-key-channel gates), fp32, [4, 8, 2048, 64]
+    if not args.no_components:
+        wf = wl.WORKLOADS["ret_fwd_mh_f32"]
+        fi = wl.make_inputs(wf, seed=0)
+        g = torch.Generator().manual_seed(2)
+        glg = torch.nn.functional.logsigmoid(torch.randn((wf.B, wf.H, wf.T, wf.dk), generator=g) + 2.0).to(dev)
+        gq, gk, gv = (fi[n].to(dev) for n in ("q", "k", "v"))
+        gout = torch.empty_like(gv)
+        gfs = torch.empty((wf.B, wf.H, wf.dk, wf.dv), dtype=torch.float32, device=dev)
+
+        def glastep():
+            rc.gla_fwd(gq, gk, gv, glg, out=gout, final_state=gfs)
+
+        g_kern, g_wall = time_launches(glastep, max(args.steps, 100), args.warmup)
+        g_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, 64)
+        g_tf = g_fl / (g_kern * 1e-3) / 1e12
+        res["gla_f32"] = {
+            "workload": "gated linear attention, fp32 [4, 8, 2048, 64], log-gates logsigmoid(N(2, 1))",
+            "ms_per_call": g_kern, "tokens_per_s": wf.B * wf.T / (g_kern * 1e-3), "tflops": g_tf,
+            "roofline": {"kernel": "gla_fwd: gla_kernel<dk=64>", "bound": "mfma", "achieved": g_tf,
+                         "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": g_tf / M.PEAK_TFLOPS["f32"],
+                         "traffic": None},
+        }
+        del glg, gq, gk, gv, gout, gfs
 
     if args.calibrate_copy:
         # plain device-to-device copies of a known size, for scaling HBM counters

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 5
+#define RET_ABI_VERSION 6
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -293,6 +293,30 @@ int linear_attn_fwd_from_state(const void *q, const void *k, const void *v, int 
 int linear_attn_decode_step(const void *q, const void *k, const void *v, int phi,
                             float *S, float *z, void *out, int N, int H, int dk, int dv,
                             int dtype, float eps, void *stream);
+
+/*
+ * gla_fwd -- causal gated linear attention with one data-dependent gate per
+ * token and key channel, chunkwise (64-token chunks), from a zero state:
+ *
+ *   S_t[c][n] = exp(lg_t[c]) S_{t-1}[c][n] + k_t[c] v_t[n],   out_t = q_t S_t
+ *
+ * ("Efficient and Sparse Transformers", section "Gated Linear Attention:
+ * Toward Input-Dependent Forgetting": RetNet's fixed decay becomes a learned
+ * gate applied element-wise to the state; here the gate of key channel c,
+ * shared by the value columns.  lg = gamma for every channel is retention,
+ * lg = 0 plain linear attention.)  Inside a chunk the decays are
+ * exponentials of differences of running log-gate sums, all <= 0.
+ *
+ *   q, k, log_gate  device, [B][H][T][dk] fp32; log_gate finite and <= 0
+ *                   (accuracy assumes |log_gate| of order 1-10 per token;
+ *                   -inf is not accepted by the chunk form)
+ *   v, out          device, [B][H][T][dv] fp32
+ *   final_state     device, [B][H][dk][dv] fp32 (written); may be NULL
+ *   dtype           RET_F32 only (RET_ERR_DTYPE otherwise)
+ *   dk, dv          each 64 or 128
+ */
+int gla_fwd(const void *q, const void *k, const void *v, const float *log_gate, void *out,
+            float *final_state, int B, int H, int T, int dk, int dv, int dtype, void *stream);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none).  The pointer stays valid until the next call on that thread. */

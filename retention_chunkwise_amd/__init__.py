@@ -18,6 +18,7 @@ linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place
 retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv)
 retention_fwd_normalized(q, k, v, gamma, norm="group", eps=1e-5) -> out   (bf16)
 retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.autograd)
+gla_fwd(q, k, v, log_gate)                     -> (out, final_state)   (fp32)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
 linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
 
@@ -36,7 +37,7 @@ import torch
 
 __all__ = ["retention_fwd", "retention_bwd", "retention", "retention_decode_step", "linear_attn_fwd",
            "linear_attn_decode_step", "retention_bwd_workspace_bytes", "retention_fwd_normalized",
-           "retention_fwd_normalized_workspace_bytes", "RET_NORM_ROWSUM", "RET_NORM_GROUP",
+           "retention_fwd_normalized_workspace_bytes", "gla_fwd", "RET_NORM_ROWSUM", "RET_NORM_GROUP",
            "retention_fwd_workspace_bytes",
            "linear_attn_workspace_bytes", "RetentionError",
            "library_path", "load_library", "abi_version", "last_error"]
@@ -103,6 +104,8 @@ def load_library():
             lib.retention_fwd_normalized.restype = i
             lib.retention_fwd_normalized_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             lib.retention_fwd_normalized_workspace_bytes.restype = sz
+            lib.gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+            lib.gla_fwd.restype = i
             lib.retention_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             lib.retention_bwd_workspace_bytes.restype = sz
             lib.linear_attn_fwd.restype = i
@@ -279,6 +282,30 @@ def retention_fwd_normalized(q, k, v, gamma, norm: str = "group", eps: float = 1
                                       float(eps), out.data_ptr(), B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return out
+
+
+def gla_fwd(q, k, v, log_gate, out=None, final_state=None, want_state: bool = True):
+    """Gated linear attention with per-token, per-key-channel gates
+    exp(log_gate): q, k, log_gate [B,H,T,dk], v [B,H,T,dv], all float32 on the
+    GPU.  Returns (out [B,H,T,dv], final_state [B,H,dk,dv] or None)."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("log_gate", log_gate)):
+        _check_dev(n, t, torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or log_gate.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k, log_gate must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, torch.float32)
+    if final_state is None and want_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+    rc = lib.gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(), out.data_ptr(),
+                     _ptr(final_state), B, H, T, dk, dv, RET_F32, _stream(q))
+    _raise(rc)
+    return out, final_state
 
 
 def retention_bwd(q, k, v, gamma, dout, chunk: int = 64, dq=None, dk=None, dv=None, workspace=None):

@@ -641,6 +641,41 @@ int linear_attn_fwd_from_state(const void* q, const void* k, const void* v, int 
                         B, H, T, dk, dv, dtype, eps, workspace, ws_bytes, stream);
 }
 
+int gla_fwd(const void* q, const void* k, const void* v, const float* log_gate, void* out, float* final_state, int B,
+            int H, int T, int dk, int dv, int dtype, void* stream) {
+    const char* fn = "gla_fwd";
+    if (dtype != RET_F32) return fail(RET_ERR_DTYPE, "%s: fp32 only (dtype %d)", fn, dtype);
+    if (B < 0 || T < 0 || H < 1)
+        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, H >= 1 (got B=%d H=%d T=%d)", fn, B, H, T);
+    if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
+    size_t nqk = 4, nv = 4, ns = 4;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv) ||
+        !mul_ok(ns, B) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
+    if (nqk > 0 && (!q || !k || !v || !log_gate || !out))
+        return fail(RET_ERR_NULL, "%s: q, k, v, log_gate and out must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_gate) || !aligned16(out))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
+    const Range rg = range("log_gate", log_gate, nqk), ro = range("out", out, nv);
+    for (const Range& in : {rq, rk, rv, rg})
+        if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
+    int rc;
+    if ((rc = check_state_arg(fn, "final_state", final_state, ns, {rq, rk, rv, rg, ro}))) return rc;
+    if (B == 0) return ok();
+    ret::GlaArgs a{};
+    a.q = static_cast<const float*>(q); a.k = static_cast<const float*>(k); a.v = static_cast<const float*>(v);
+    a.lg = log_gate; a.out = static_cast<float*>(out); a.final_state = final_state;
+    a.B = B; a.H = H; a.T = T; a.dv = dv;
+    const int nt = ret::gla_choose_nt(static_cast<long long>(B) * H, dv);
+    a.nslices = dv / (16 * nt);
+    const hipError_t e = ret::launch_gla(a, dk, nt, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+}
+
 int linear_attn_decode_step(const void* q, const void* k, const void* v, int phi, float* S, float* z, void* out,
                             int N, int H, int dk, int dv, int dtype, float eps, void* stream) {
     const char* fn = "linear_attn_decode_step";

@@ -72,6 +72,19 @@ struct SegArgs {
     float log2g[kMaxHeads];
 };
 
+// Arguments of the gated linear attention walk (fp32).
+struct GlaArgs {
+    const float* q;
+    const float* k;
+    const float* v;
+    const float* lg;     // [B][H][T][dk] log-gates (finite, <= 0)
+    float* out;
+    float* final_state;  // may be null
+    int B, H, T;
+    int dv;
+    int nslices;         // dv / (16 * NT)
+};
+
 // Launchers (host).  They assume validated arguments and return a hipError_t.
 hipError_t launch_walk(const WalkArgs& a, bool bf16, int chunk, int dk, int nt,
                        bool linattn, hipStream_t stream);
@@ -105,6 +118,10 @@ int choose_segments(long long bh, int nch, int target_groups, int min_cps, int m
 // Choice of value-slice width (in 16-column MFMA tiles) for the chunk walk:
 // the widest slice that still gives at least `target_groups` workgroups.
 int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk, int dk);
+
+// Gated linear attention: value-slice width (in 16-column tiles) and launcher.
+int gla_choose_nt(long long bh, int dv);
+hipError_t launch_gla(const GlaArgs& a, int dk, int nt, hipStream_t stream);
 
 // Widest value slice of the segmented walk whose workgroup fits in LDS (the
 // fewest recomputed Q K^T tiles); the segments provide the parallelism.

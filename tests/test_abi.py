@@ -346,3 +346,30 @@ def test_retention_fwd_normalized_workspace():
     assert n > 0 and n % ((128 * 128 + 128) * 4) == 0
     assert lib.retention_fwd_normalized_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_F32) == 0
     assert _nrm(lib, B=0) == 0
+
+
+# ---------------------------------------------------------------- gated linear attention
+def _gla(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, lg=FAKE * 4, out=FAKE * 5, fs=None, B=1, H=2, T=16, dk=64, dv=64,
+             dtype=rc.RET_F32)
+    a.update(kw)
+    return lib.gla_fwd(a["q"], a["k"], a["v"], a["lg"], a["out"], a["fs"], a["B"], a["H"], a["T"], a["dk"],
+                       a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=rc.RET_BF16), -3),
+    (dict(lg=None), -1),
+    (dict(dk=32), -2),
+    (dict(lg=FAKE * 4 + 4), -7),
+    (dict(out=FAKE * 4), -8),            # out is the gate tensor
+    (dict(fs=FAKE * 5), -8),             # final state overlaps out
+])
+def test_gla_rejects(kw, code):
+    lib = _lib()
+    assert _gla(lib, **kw) == code
+    assert "gla_fwd" in lib.retention_last_error().decode()
+
+
+def test_gla_empty_batch():
+    assert _gla(_lib(), B=0) == 0

@@ -1,0 +1,96 @@
+"""Gated linear attention (gla_fwd, per-token per-key-channel gates) against
+the fp64 oracle (needs a gfx950 GPU).
+
+The oracle runs S_t = diag(exp(lg_t)) S_{t-1} + k_t^T v_t token by token; the
+kernel walks 64-token chunks with exponentials of running log-gate sums.
+Gates are log-sigmoids of Gaussian logits, from slow forgetting (gate about
+0.95) to fast (about 0.1), plus isolated near-resets; every (dk, dv) pair,
+ragged lengths, both slice widths, the final state, and the two special cases
+the pages name (a constant gate is retention, a unit gate linear attention).
+Tolerance: relative Frobenius error 1e-4 (fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import retention_chunkwise_amd as rc
+from retention_chunkwise_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _inputs(seed, B, H, T, dk, dv, mu):
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, dtype="f32", scale=1.0 / np.sqrt(dk))
+    inp = wl.make_inputs(w, seed)
+    g = torch.Generator().manual_seed(seed + 900)
+    inp["lg"] = torch.nn.functional.logsigmoid(torch.randn((B, H, T, dk), generator=g) + mu).float()
+    return w, inp
+
+
+def _run(inp):
+    q, k, v, lg = (inp[n].cuda() for n in ("q", "k", "v", "lg"))
+    out, fs = rc.gla_fwd(q, k, v, lg)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), fs.cpu().numpy()
+
+
+def _check(tag, out, fs, inp):
+    ref, ref_s = oracle.gla_recurrent(inp["q"], inp["k"], inp["v"], inp["lg"], nthreads=8)
+    e_o, e_s = oracle.rel_frobenius(out, ref), oracle.rel_frobenius(fs, ref_s)
+    print(f"[parity] {tag}: out {e_o:.3e} state {e_s:.3e} (tol {TOL:.0e})", flush=True)
+    assert e_o <= TOL and e_s <= TOL and np.isfinite(out).all(), tag
+
+
+@pytest.mark.parametrize("mu", [3.0, 0.0, -2.0])
+@pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 300), (64, 128, 129), (128, 64, 200)])
+def test_gla_small_full(mu, dk, dv, T):
+    w, inp = _inputs(71, 2, 3, T, dk, dv, mu)
+    out, fs = _run(inp)
+    _check(f"gla mu={mu} dk={dk} dv={dv} T={T}", out, fs, inp)
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 129])
+def test_gla_short_and_ragged(T):
+    w, inp = _inputs(72, 1, 2, T, 64, 64, 1.0)
+    out, fs = _run(inp)
+    _check(f"gla short T={T}", out, fs, inp)
+
+
+def test_gla_near_reset():
+    """Isolated gates of e^-20 on all channels: the state is nearly erased there."""
+    w, inp = _inputs(73, 1, 2, 400, 64, 64, 2.0)
+    inp["lg"][:, :, 100] = -20.0
+    inp["lg"][:, 1, 257] = -20.0
+    out, fs = _run(inp)
+    _check("gla near reset", out, fs, inp)
+
+
+def test_gla_wide_slices():
+    """Enough (b, h) pairs for 64-column slices (the other slice width)."""
+    w, inp = _inputs(74, 4, 64, 140, 64, 64, 1.0)
+    out, fs = _run(inp)
+    _check("gla 256 heads", out, fs, inp)
+
+
+def test_gla_special_cases_match_retention():
+    w, inp = _inputs(75, 2, 3, 500, 64, 64, 0.0)
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    gam = np.array([0.9, 0.99, 1.0], dtype=np.float32)
+    lg = torch.from_numpy(np.log(gam)).view(1, 3, 1, 1).expand(2, 3, 500, 64).contiguous().cuda()
+    og, sg = rc.gla_fwd(q, k, v, lg)
+    orr, sr = rc.retention_fwd(q, k, v, gam, chunk=64)
+    torch.cuda.synchronize()
+    e_o = oracle.rel_frobenius(og.cpu().numpy(), orr.cpu().numpy())
+    e_s = oracle.rel_frobenius(sg.cpu().numpy(), sr.cpu().numpy())
+    print(f"[parity] gla constant gate vs retention_fwd: out {e_o:.3e} state {e_s:.3e}", flush=True)
+    assert e_o <= TOL and e_s <= TOL
+
+
+def test_gla_empty_and_zero_length():
+    q = torch.zeros((1, 2, 0, 64), device="cuda")
+    out, fs = rc.gla_fwd(q, q, q, q)
+    torch.cuda.synchronize()
+    assert out.shape == (1, 2, 0, 64) and torch.all(fs == 0)
