@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 6
+#define RET_ABI_VERSION 7
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -314,9 +314,15 @@ int linear_attn_decode_step(const void *q, const void *k, const void *v, int phi
  *   final_state     device, [B][H][dk][dv] fp32 (written); may be NULL
  *   dtype           RET_F32 only (RET_ERR_DTYPE otherwise)
  *   dk, dv          each 64 or 128
+ *   workspace       gla_fwd_workspace_bytes(...) bytes: per segment but the
+ *                   last, its state contribution and per-channel gate totals
  */
 int gla_fwd(const void *q, const void *k, const void *v, const float *log_gate, void *out,
-            float *final_state, int B, int H, int T, int dk, int dv, int dtype, void *stream);
+            float *final_state, int B, int H, int T, int dk, int dv, int dtype,
+            void *workspace, size_t ws_bytes, void *stream);
+
+/* Workspace bytes gla_fwd needs (0: none or invalid).  Host only. */
+size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none).  The pointer stays valid until the next call on that thread. */

@@ -104,7 +104,9 @@ def load_library():
             lib.retention_fwd_normalized.restype = i
             lib.retention_fwd_normalized_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             lib.retention_fwd_normalized_workspace_bytes.restype = sz
-            lib.gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp]
+            lib.gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+            lib.gla_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+            lib.gla_fwd_workspace_bytes.restype = sz
             lib.gla_fwd.restype = i
             lib.retention_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
             lib.retention_bwd_workspace_bytes.restype = sz
@@ -284,7 +286,7 @@ def retention_fwd_normalized(q, k, v, gamma, norm: str = "group", eps: float = 1
     return out
 
 
-def gla_fwd(q, k, v, log_gate, out=None, final_state=None, want_state: bool = True):
+def gla_fwd(q, k, v, log_gate, out=None, final_state=None, want_state: bool = True, workspace=None):
     """Gated linear attention with per-token, per-key-channel gates
     exp(log_gate): q, k, log_gate [B,H,T,dk], v [B,H,T,dv], all float32 on the
     GPU.  Returns (out [B,H,T,dv], final_state [B,H,dk,dv] or None)."""
@@ -302,8 +304,9 @@ def gla_fwd(q, k, v, log_gate, out=None, final_state=None, want_state: bool = Tr
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _check_dev("final_state", final_state, torch.float32)
+    ws, nws = _workspace(lib.gla_fwd_workspace_bytes(B, H, T, dk, dv, RET_F32), q.device, workspace)
     rc = lib.gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(), out.data_ptr(),
-                     _ptr(final_state), B, H, T, dk, dv, RET_F32, _stream(q))
+                     _ptr(final_state), B, H, T, dk, dv, RET_F32, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return out, final_state
 

@@ -286,9 +286,27 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
     return plan.ws_bytes;
 }
 
+// Plan of the gated linear attention walk: 64-token chunks, the widest value
+// slice, and enough segments to occupy the chip (at least 2 chunks each).
+bool plan_gla(long long bh, int T, int dk, int dv, SegPlan* p) {
+    p->chunk = 64;
+    p->pieces = 1;
+    p->nt = ret::gla_choose_nt(bh, dv);
+    const int nch = (T + 63) / 64;
+    if (!forced_segments(nch, p)) p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, 256, 2, 16, &p->cps);
+    return set_ws_bytes(bh, dk, dv, true, p);
+}
+
 // Chunk of the normalised walk: with dk = dv = 128 the 128-token walk and its
 // normaliser exceed the LDS, so it runs 64-token chunks (same result).
 int norm_chunk(int chunk, int dk, int dv) { return (chunk == 128 && dk == 128 && dv == 128) ? 64 : chunk; }
+
+size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
+    if (B <= 0 || H < 1 || T < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || dtype != RET_F32) return 0;
+    SegPlan plan;
+    if (!plan_gla(static_cast<long long>(B) * H, T, dk, dv, &plan)) return 0;
+    return plan.ws_bytes;
+}
 
 size_t retention_fwd_normalized_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
     if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
@@ -642,7 +660,7 @@ int linear_attn_fwd_from_state(const void* q, const void* k, const void* v, int 
 }
 
 int gla_fwd(const void* q, const void* k, const void* v, const float* log_gate, void* out, float* final_state, int B,
-            int H, int T, int dk, int dv, int dtype, void* stream) {
+            int H, int T, int dk, int dv, int dtype, void* workspace, size_t ws_bytes, void* stream) {
     const char* fn = "gla_fwd";
     if (dtype != RET_F32) return fail(RET_ERR_DTYPE, "%s: fp32 only (dtype %d)", fn, dtype);
     if (B < 0 || T < 0 || H < 1)
@@ -665,12 +683,19 @@ int gla_fwd(const void* q, const void* k, const void* v, const float* log_gate, 
     int rc;
     if ((rc = check_state_arg(fn, "final_state", final_state, ns, {rq, rk, rv, rg, ro}))) return rc;
     if (B == 0) return ok();
+    SegPlan plan;
+    if (!plan_gla(static_cast<long long>(B) * H, T, dk, dv, &plan)) return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if ((rc = check_workspace(fn, plan, workspace, ws_bytes,
+                              {rq, rk, rv, rg, ro, final_state ? range("final_state", final_state, ns) : Range{"", 0, 0}})))
+        return rc;
     ret::GlaArgs a{};
     a.q = static_cast<const float*>(q); a.k = static_cast<const float*>(k); a.v = static_cast<const float*>(v);
     a.lg = log_gate; a.out = static_cast<float*>(out); a.final_state = final_state;
     a.B = B; a.H = H; a.T = T; a.dv = dv;
-    const int nt = ret::gla_choose_nt(static_cast<long long>(B) * H, dv);
+    const int nt = plan.nt;
     a.nslices = dv / (16 * nt);
+    a.G = plan.G; a.cps = plan.cps;
+    a.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
     const hipError_t e = ret::launch_gla(a, dk, nt, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();

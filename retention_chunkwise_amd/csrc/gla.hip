@@ -18,14 +18,28 @@
 //    exponent per term;
 //  - the inter-chunk and state products scale Q by e^{b_i} and K by
 //    e^{b_last - b_j}.
-// A gate of 0 (lg = -inf) closes a channel exactly.
+// Fast path.  One pre-scaled key array serves every product:
+// K^[j][c] = k_j[c] e^{b_{e_J}[c] - b_j[c]} (<= |k|).  Scores of key tile J
+// <= I take Q operands q_i e^{b_i - b_{e_I}} (>= 1 in size, bounded by
+// e^{span of one tile}) times e^{b_{e_I} - b_{e_J}} (<= 1); the diagonal tile
+// is that product masked.  The state update takes K^ times e^{b_last -
+// b_{e_J}} (<= 1).  It is used when every channel's log-gate sum over the
+// chunk stays above -80, so that no factor can overflow; a chunk with
+// stronger gates takes the exact path above (diagonal tiles summed term by
+// term, every exponent formed on the spot).
 //
-// Mapping.  One workgroup (4 waves) per (b, h, slice of 16 NT value columns)
-// walks all chunks of 64 tokens; wave W owns query tile W and state tiles
-// {W, W + 4, ...} of the slice.  The chunk's q, k, cumulative gates and the
-// value slice are staged in LDS (padded fp32 rows); S^T is copied to LDS for
-// the next chunk's inter-chunk product.  This first version walks whole
-// sequences (no segment split) and does not overlap loads with compute.
+// Segments.  Each (b, h) sequence is cut into G segments of whole chunks.  A
+// state-only pass (SO) walks every segment but the last and writes its
+// contribution dS_j (the state it would end with from zero) and its per-channel
+// log-gate total L_j; the walk of segment g then starts from
+//   S_in(g) = sum_{j<g} diag(exp(L_{j+1} + ... + L_{g-1})) dS_j,
+// all exponents <= 0.
+//
+// Mapping.  One workgroup (4 waves) per (b, h, segment, slice of 16 NT value
+// columns) walks the segment's chunks of 64 tokens; wave W owns query tile W
+// and state tiles {W, W + 4, ...} of the slice.  The chunk's q, k, cumulative
+// gates and the value slice are staged in LDS (padded fp32 rows); S^T is
+// copied to LDS for the next chunk's inter-chunk product.
 #include "internal.h"
 #include "kcommon.h"
 
@@ -56,13 +70,14 @@ struct Smem {
     alignas(16) float b[C * Cf::KSTR];     // log-gates, then their running sums over the chunk
     alignas(16) float v[C * Cf::VSTR];
     alignas(16) float st[Cf::DVS * Cf::KSTR];  // S^T copy: st[n][c] = S[c][nbase + n]
+    int unsafe;                                // this chunk's gates are too strong for the fast path
 };
 
 template <int DK, int NT>
 constexpr bool fits() { return sizeof(Smem<DK, NT>) <= 160 * 1024; }
 
-template <int DK, int NT, int W>
-__device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh, int nbase) {
+template <int DK, int NT, int W, bool SO>
+__device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh, int seg, int nbase) {
     using Cf = Cfg<DK, NT>;
     constexpr int KSTR = Cf::KSTR, VSTR = Cf::VSTR, KT = Cf::KT, SPW = Cf::SPW, DVS = Cf::DVS;
     const int T = a.T, DV = a.dv;
@@ -77,45 +92,168 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     f32x4 sacc[SPW];  // S[16 kt + l16][nbase + 16 nt + 4g + r], tile W + 4m = (nt, kt)
 #pragma unroll
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const long long slot = static_cast<long long>(DK) * DV + DK;  // workspace floats per (b, h, segment)
+    if (!SO && seg > 0) {
+        // S_in = sum_{j<seg} diag(exp(L_{j+1} + ... + L_{seg-1})) dS_j
+        const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot;
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT, ch = 16 * kt + l16;
+            float dsum = 0.f;
+            for (int j = seg - 1; j >= 0; --j) {
+                const float* sj = wsb + j * slot;
+                sacc[m] += __expf(dsum) * *reinterpret_cast<const f32x4*>(sj + ch * DV + nbase + 16 * nt + 4 * g);
+                dsum += sj[DK * DV + ch];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {  // state copy for the first chunk (ordered by the loop's first barrier)
+        const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sm.st[(16 * nt + 4 * g + r) * KSTR + 16 * kt + l16] = sacc[m][r];
+    }
+    float ltot = 0.f;  // state-only pass: this thread's channel's log-gate total over the segment
 
     const int nch = (T + C - 1) / C;
-    for (int c = 0; c < nch; ++c) {
+    const int c_begin = seg * a.cps;
+    const int c_end = (c_begin + a.cps < nch) ? c_begin + a.cps : nch;
+    for (int c = c_begin; c < c_end; ++c) {
         const long long t0 = static_cast<long long>(c) * C;
         const int clen = (T - t0 < C) ? static_cast<int>(T - t0) : C;
         __syncthreads();  // the previous chunk's reads of q, k, b, v are done
+        if (tid == 0) sm.unsafe = 0;
 
-        // ---- stage the chunk (rows past the end: zeros, gate 1)
-        for (int u = tid; u < C * DK / 4; u += kThreads) {
-            const int r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
-            f32x4 xq = {0.f, 0.f, 0.f, 0.f}, xk = xq, xg = xq;
-            if (r < clen) {
-                const long long o = (t0 + r) * DK + c4;
-                xq = *reinterpret_cast<const f32x4*>(qh + o);
-                xk = *reinterpret_cast<const f32x4*>(kh + o);
-                xg = *reinterpret_cast<const f32x4*>(gh + o);
+        // ---- stage the chunk (rows past the end: zeros, gate 1).  All of a
+        // thread's loads are issued before any LDS store; a row past the end
+        // reads row 0 of the chunk (always valid) and is zeroed afterwards.
+        {
+            constexpr int NU = C * DK / 4 / kThreads, NV = (C * DVS / 4 + kThreads - 1) / kThreads;
+            static_assert(NU * kThreads * 4 == C * DK, "q/k/gate staging split");
+            f32x4 xq[NU], xk[NU], xg[NU], xv[NV];
+#pragma unroll
+            for (int m = 0; m < NU; ++m) {
+                const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
+                const long long o = (t0 + (r < clen ? r : 0)) * DK + c4;
+                if constexpr (!SO) xq[m] = *reinterpret_cast<const f32x4*>(qh + o);
+                xk[m] = *reinterpret_cast<const f32x4*>(kh + o);
+                xg[m] = *reinterpret_cast<const f32x4*>(gh + o);
             }
-            *reinterpret_cast<f32x4*>(&sm.q[r * KSTR + c4]) = xq;
-            *reinterpret_cast<f32x4*>(&sm.k[r * KSTR + c4]) = xk;
-            *reinterpret_cast<f32x4*>(&sm.b[r * KSTR + c4]) = xg;
-        }
-        for (int u = tid; u < C * DVS / 4; u += kThreads) {
-            const int r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
-            f32x4 xv = {0.f, 0.f, 0.f, 0.f};
-            if (r < clen) xv = *reinterpret_cast<const f32x4*>(vh + (t0 + r) * DV + c4);
-            *reinterpret_cast<f32x4*>(&sm.v[r * VSTR + c4]) = xv;
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
+                if (u < C * DVS / 4) xv[m] = *reinterpret_cast<const f32x4*>(vh + (t0 + (r < clen ? r : 0)) * DV + c4);
+            }
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < NU; ++m) {
+                const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
+                const bool in = r < clen;
+                if constexpr (!SO) *reinterpret_cast<f32x4*>(&sm.q[r * KSTR + c4]) = in ? xq[m] : zero;
+                *reinterpret_cast<f32x4*>(&sm.k[r * KSTR + c4]) = in ? xk[m] : zero;
+                *reinterpret_cast<f32x4*>(&sm.b[r * KSTR + c4]) = in ? xg[m] : zero;
+            }
+#pragma unroll
+            for (int m = 0; m < NV; ++m) {
+                const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
+                if (u < C * DVS / 4) *reinterpret_cast<f32x4*>(&sm.v[r * VSTR + c4]) = (r < clen) ? xv[m] : zero;
+            }
         }
         __syncthreads();
-        // ---- running sums of the log-gates down each key channel
+        // ---- running sums of the log-gates down each key channel: the column
+        // is read into registers first (independent loads), summed there and
+        // written back
         if (tid < DK) {
-            float acc = 0.f;
-            for (int r = 0; r < C; ++r) {
-                acc += sm.b[r * KSTR + tid];
-                sm.b[r * KSTR + tid] = acc;
-            }
+            float col[C];
+#pragma unroll
+            for (int r = 0; r < C; ++r) col[r] = sm.b[r * KSTR + tid];
+#pragma unroll
+            for (int r = 1; r < C; ++r) col[r] += col[r - 1];
+#pragma unroll
+            for (int r = 0; r < C; ++r) sm.b[r * KSTR + tid] = col[r];
+            if (!(col[C - 1] >= -80.f)) sm.unsafe = 1;  // every thread that writes writes 1
+            ltot += col[C - 1];
         }
         __syncthreads();
 
         const int qi = 16 * I + l16;  // this lane's query row
+        const int last = clen - 1;
+        if (!sm.unsafe) {
+            // ---- fast path (see the header): Q factors in registers, K^ in place of k
+            constexpr int NQ = DK / 4;
+            const int eI = 16 * I + 15;
+            float qd[NQ], qx[NQ];  // q_i e^{b_i - b_{e_I}} and q_i e^{b_i} for channels 4s + g
+#pragma unroll
+            for (int s = 0; s < (SO ? 0 : NQ); ++s) {
+                const int ch = 4 * s + g;
+                const float qv = sm.q[qi * KSTR + ch], bq = sm.b[qi * KSTR + ch];
+                qd[s] = qv * __expf(bq - sm.b[eI * KSTR + ch]);
+                qx[s] = qv * __expf(bq);
+            }
+            for (int u = tid; u < C * DK; u += kThreads) {  // each element rewritten by its own thread
+                const int j = u / DK, ch = u % DK;
+                const int eJ = (j | 15);
+                sm.k[j * KSTR + ch] *= __expf(sm.b[eJ * KSTR + ch] - sm.b[j * KSTR + ch]);
+            }
+            __syncthreads();
+
+            f32x4 pacc[I + 1];
+#pragma unroll
+            for (int J = 0; J <= (SO ? -1 : I); ++J) {
+                pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+                const int eJ = 16 * J + 15, kj = 16 * J + l16;
+#pragma unroll 4
+                for (int s = 0; s < NQ; ++s) {
+                    const int ch = 4 * s + g;
+                    const float f = (J == I) ? 1.f : __expf(sm.b[eI * KSTR + ch] - sm.b[eJ * KSTR + ch]);
+                    pacc[J] = mfma_f32(sm.k[kj * KSTR + ch], qd[s] * f, pacc[J]);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)  // causal mask of the diagonal tile
+                if (16 * I + 4 * g + r > qi) pacc[I][r] = 0.f;
+
+#pragma unroll
+            for (int nt = 0; nt < (SO ? 0 : NT); ++nt) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+                for (int s = 0; s < NQ; ++s) o = mfma_f32(sm.st[(16 * nt + l16) * KSTR + 4 * s + g], qx[s], o);
+#pragma unroll
+                for (int J = 0; J <= I; ++J)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        o = mfma_f32(sm.v[(16 * J + 4 * g + r) * VSTR + 16 * nt + l16], pacc[J][r], o);
+                if (qi < clen) *reinterpret_cast<f32x4*>(oh + (t0 + qi) * DV + 16 * nt + 4 * g) = o;
+            }
+
+#pragma unroll
+            for (int m = 0; m < SPW; ++m) {
+                const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
+                const int ch = 16 * kt + l16;
+                const float bl = sm.b[last * KSTR + ch];
+                sacc[m] *= __expf(bl);
+#pragma unroll
+                for (int J = 0; J < C / 16; ++J) {
+                    const float f = __expf(bl - sm.b[(16 * J + 15) * KSTR + ch]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * J + 4 * g + r;
+                        sacc[m] = mfma_f32(sm.v[j * VSTR + 16 * nt + l16], sm.k[j * KSTR + ch] * f, sacc[m]);
+                    }
+                }
+            }
+            __syncthreads();  // every wave is done reading the old state copy
+#pragma unroll
+            for (int m = 0; m < SPW; ++m) {
+                const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sm.st[(16 * nt + 4 * g + r) * KSTR + 16 * kt + l16] = sacc[m][r];
+            }
+            continue;
+        }
+
+        // ---- exact path for chunks with strong gates
+        if constexpr (!SO) {
         // ---- scores S^T[j][i] for key tiles J <= I: lane holds keys 16J + 4g + r of query qi
         f32x4 pacc[I + 1];
 #pragma unroll
@@ -166,9 +304,9 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                     o = mfma_f32(sm.v[(16 * J + 4 * g + r) * VSTR + 16 * nt + l16], pacc[J][r], o);
             if (qi < clen) *reinterpret_cast<f32x4*>(oh + (t0 + qi) * DV + 16 * nt + 4 * g) = o;
         }
+        }  // !SO
 
         // ---- S = diag(e^{b_last}) S + sum_j diag(e^{b_last - b_j}) k_j v_j^T
-        const int last = clen - 1;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
             const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
@@ -193,7 +331,18 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         }
     }
 
-    if (a.final_state) {
+    if constexpr (SO) {
+        // this segment's contribution (its end state from zero) and log-gate totals
+        float* out = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * slot;
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
+            *reinterpret_cast<f32x4*>(out + (16 * kt + l16) * DV + nbase + 16 * nt + 4 * g) = sacc[m];
+        }
+        if (nbase == 0 && tid < DK) out[DK * DV + tid] = ltot;
+        return;
+    }
+    if (a.final_state && seg == a.G - 1) {
         float* fs = a.final_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
@@ -203,19 +352,20 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     }
 }
 
-template <int DK, int NT>
+// SO: the state-only pass over segments 0 .. G-2.
+template <int DK, int NT, bool SO>
 __global__ void __launch_bounds__(kThreads, 1) gla_kernel(const GlaArgs a) {
     __shared__ Smem<DK, NT> sm;
-    const int bh = blockIdx.x / a.nslices;
+    const int nseg = SO ? a.G - 1 : a.G;
+    const int bhs = blockIdx.x / a.nslices;
+    const int bh = bhs / nseg, seg = bhs % nseg;
     const int nbase = (blockIdx.x % a.nslices) * Cfg<DK, NT>::DVS;
-    for (int m = threadIdx.x; m < Cfg<DK, NT>::DVS * Cfg<DK, NT>::KSTR; m += kThreads) sm.st[m] = 0.f;
-    // (the first barrier of the chunk loop orders this before any read)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: body<DK, NT, 0>(a, sm, bh, nbase); break;
-        case 1: body<DK, NT, 1>(a, sm, bh, nbase); break;
-        case 2: body<DK, NT, 2>(a, sm, bh, nbase); break;
-        default: body<DK, NT, 3>(a, sm, bh, nbase); break;
+        case 0: body<DK, NT, 0, SO>(a, sm, bh, seg, nbase); break;
+        case 1: body<DK, NT, 1, SO>(a, sm, bh, seg, nbase); break;
+        case 2: body<DK, NT, 2, SO>(a, sm, bh, seg, nbase); break;
+        default: body<DK, NT, 3, SO>(a, sm, bh, seg, nbase); break;
     }
 }
 
@@ -224,10 +374,18 @@ hipError_t launch_t(const GlaArgs& a, hipStream_t stream) {
     if constexpr (!fits<DK, NT>()) {
         return hipErrorInvalidConfiguration;
     } else {
-        const long long groups = static_cast<long long>(a.B) * a.H * a.nslices;
+        const long long groups = static_cast<long long>(a.B) * a.H * a.nslices * a.G;
         if (groups <= 0) return hipSuccess;
         if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
-        hipLaunchKernelGGL((gla_kernel<DK, NT>), dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, stream, a);
+        if (a.G > 1) {
+            const long long sgroups = static_cast<long long>(a.B) * a.H * a.nslices * (a.G - 1);
+            hipLaunchKernelGGL((gla_kernel<DK, NT, true>), dim3(static_cast<unsigned>(sgroups)), dim3(kThreads), 0,
+                               stream, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((gla_kernel<DK, NT, false>), dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, stream,
+                           a);
         return hipGetLastError();
     }
 }
@@ -236,10 +394,9 @@ hipError_t launch_t(const GlaArgs& a, hipStream_t stream) {
 }  // namespace gla
 
 int gla_choose_nt(long long bh, int dv) {
-    // wide slices (fewer recomputed scores) while there are enough workgroups
-    if (dv % 64 == 0 && bh * (dv / 64) >= 256) return 4;
-    if (dv % 32 == 0 && bh * (dv / 32) >= 256) return 2;
-    return 1;
+    // the widest slice that fits (the segments supply the parallelism); 64 columns at most
+    (void)bh;
+    return dv >= 64 ? 4 : dv / 16;
 }
 
 hipError_t launch_gla(const GlaArgs& a, int dk, int nt, hipStream_t stream) {

@@ -83,6 +83,9 @@ struct GlaArgs {
     int B, H, T;
     int dv;
     int nslices;         // dv / (16 * NT)
+    int G;               // segments per (b, h); all but the last are full
+    int cps;             // chunks (64 tokens) per segment
+    float* ws;           // [B*H][G-1][dk*dv + dk] segment states and log-gate totals; unused when G == 1
 };
 
 // Launchers (host).  They assume validated arguments and return a hipError_t.

@@ -354,7 +354,7 @@ def _gla(lib, **kw):
              dtype=rc.RET_F32)
     a.update(kw)
     return lib.gla_fwd(a["q"], a["k"], a["v"], a["lg"], a["out"], a["fs"], a["B"], a["H"], a["T"], a["dk"],
-                       a["dv"], a["dtype"], None)
+                       a["dv"], a["dtype"], a.get("ws"), a.get("nws", 0), None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -373,3 +373,11 @@ def test_gla_rejects(kw, code):
 
 def test_gla_empty_batch():
     assert _gla(_lib(), B=0) == 0
+
+
+def test_gla_workspace():
+    lib = _lib()
+    n = lib.gla_fwd_workspace_bytes(4, 8, 2048, 64, 64, rc.RET_F32)
+    assert n > 0 and n % ((64 * 64 + 64) * 4 * 32) == 0
+    big = 1 << 28  # 256 MiB apart: no overlap between the fake tensors
+    assert _gla(lib, B=4, H=8, T=2048, q=big, k=2 * big, v=3 * big, lg=4 * big, out=5 * big) == -9

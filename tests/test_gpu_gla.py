@@ -89,8 +89,29 @@ def test_gla_special_cases_match_retention():
     assert e_o <= TOL and e_s <= TOL
 
 
+@pytest.mark.parametrize("G", [1, 3, 7])
+def test_gla_forced_segments(G, monkeypatch):
+    monkeypatch.setenv("RET_FWD_SEGMENTS", str(G))
+    w, inp = _inputs(78, 2, 2, 1000, 128, 64, 1.0)
+    inp["lg"][:, :, 300:364] = -3.0  # one chunk's worth of strong gates inside a segment
+    out, fs = _run(inp)
+    _check(f"gla G={G}", out, fs, inp)
+
+
 def test_gla_empty_and_zero_length():
     q = torch.zeros((1, 2, 0, 64), device="cuda")
     out, fs = rc.gla_fwd(q, q, q, q)
     torch.cuda.synchronize()
     assert out.shape == (1, 2, 0, 64) and torch.all(fs == 0)
+
+
+def test_gla_mixed_gate_strength():
+    """Strong gates (chunk sums below -80, the exact path) and weak ones (the
+    fast path) alternating in one sequence."""
+    w, inp = _inputs(76, 2, 2, 640, 64, 128, 2.0)
+    g = torch.Generator().manual_seed(77)
+    strong = torch.nn.functional.logsigmoid(torch.randn((2, 2, 640, 64), generator=g) - 2.5)
+    for c0 in range(0, 640, 128):
+        inp["lg"][:, :, c0:c0 + 64] = strong[:, :, c0:c0 + 64]
+    out, fs = _run(inp)
+    _check("gla mixed gate strength", out, fs, inp)
