@@ -38,7 +38,9 @@
  *  - Tuning and testing knobs, read from the environment at every call:
  *    RET_FWD_PATH = "slice" | "segment" forces the forward path (segment
  *    needs bf16; anything else means automatic), RET_FWD_SEGMENTS = n forces
- *    the segment count.  Neither changes results beyond rounding.
+ *    the segment count, RET_WALK_NT = n narrows the value slices of the slice
+ *    path, RET_LIN_CHUNK = 64 | 128 sets the linear-attention chunk.  None
+ *    changes results beyond rounding.
  *
  * Sources (page title, then passage):
  *   "RetNet" (bembew.net): the single-head definition O = (Q K^T (.) D) V with

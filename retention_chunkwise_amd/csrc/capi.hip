@@ -173,7 +173,11 @@ bool plan_segments(long long bh, int T, int chunk, int dk, int dv, bool linattn,
 // tokens (64 when dk = 128, where 128 would spill registers); the fp32 walk
 // uses 64 (wider value slices fit in LDS); a forced bf16 slice walk 128.
 int linattn_chunk(int dk, FwdPath path, bool bf16) {
-    if (path == FwdPath::kSegment) return dk == 128 ? 64 : 128;
+    if (path == FwdPath::kSegment) {
+        const int want = env_int("RET_LIN_CHUNK");  // tuning: 64 or 128 (128 only with dk = 64)
+        if (want == 64 || (want == 128 && dk == 64)) return want;
+        return dk == 128 ? 64 : 128;
+    }
     return bf16 ? 128 : 64;
 }
 
