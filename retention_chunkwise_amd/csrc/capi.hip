@@ -216,7 +216,8 @@ struct FwdState {
 // Launches the segment-split forward (bf16) with a checked plan and workspace.
 hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
                                const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
-                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st, bool reverse = false) {
+                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st, bool reverse = false,
+                               bool ws_transposed = false) {
     ret::SegArgs sa{};
     sa.G = plan.G;
     sa.cps = plan.cps;
@@ -226,6 +227,7 @@ hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k
     sa.init_z = fst.init_z; sa.final_z = fst.final_z;
     sa.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
     sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
+    sa.ws_tr = ws_transposed ? 1 : 0;
     if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
     if (reverse) return ret::launch_seg_rev(sa, chunk, dk, dv, st);
     return ret::launch_seg(sa, chunk, dk, dv, linattn, st);
@@ -241,7 +243,8 @@ bool plan_bwd_walk(long long bh, int T, int chunk, int dk, int dv, int dtype, Se
 // The three walks of the backward pass: dq = fwd(dout, v, k) with widths
 // (dv, dk), dk = reversed fwd(v, dout, q) with widths (dv, dk), dv = reversed
 // fwd(k, q, dout) with widths (dk, dv).  They run one after another on one
-// stream and share the workspace, which must hold the largest plan.
+// stream (dv, dk, dq) and share the workspace, which must hold the largest
+// plan.
 bool plan_bwd(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan plans[3], size_t* ws_max) {
     if (!plan_bwd_walk(bh, T, chunk, dv, dk, dtype, &plans[0])) return false;
     plans[1] = plans[0];
@@ -616,15 +619,23 @@ int retention_bwd(const void* q, const void* k, const void* v, const float* gamm
         int wk, wv;
         bool rev;
     };
-    const Walk walks[3] = {{dout, v, k, dq, d_v, d_k, false}, {v, dout, q, dk, d_v, d_k, true},
-                           {k, q, dout, dv, d_k, d_v, true}};
+    // dv first: its segment states sum q_s dout_s^T, the transpose of what the dk walk needs
+    // (dout_s q_s^T over the same reversed segments), so on the segment path the dk walk reads
+    // them transposed instead of running its own state pass
+    const Walk walks[3] = {{k, q, dout, dv, d_k, d_v, true}, {v, dout, q, dk, d_v, d_k, true},
+                           {dout, v, k, dq, d_v, d_k, false}};
+    const SegPlan* wplans[3] = {&plans[2], &plans[1], &plans[0]};
+    const bool share = plans[1].path == FwdPath::kSegment && plans[2].path == FwdPath::kSegment &&
+                       plans[1].G == plans[2].G && plans[1].cps == plans[2].cps &&
+                       plans[1].pieces == plans[2].pieces;
     for (int i = 0; i < 3; ++i) {
         const Walk& w = walks[i];
+        const SegPlan& pl = *wplans[i];
         const hipError_t e =
-            plans[i].path == FwdPath::kSegment
-                ? launch_segment_path(plans[i], w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, chunk, w.wk,
-                                      w.wv, false, st, w.rev)
-                : launch_slice_path(plans[i], w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, w.wk, w.wv,
+            pl.path == FwdPath::kSegment
+                ? launch_segment_path(pl, w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, chunk, w.wk,
+                                      w.wv, false, st, w.rev, i == 1 && share)
+                : launch_slice_path(pl, w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, w.wk, w.wv,
                                     false, false, st, w.rev);
         if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
