@@ -70,7 +70,7 @@ struct Smem {
     alignas(16) float b[C * Cf::KSTR];     // log-gates, then their running sums over the chunk
     alignas(16) float v[C * Cf::VSTR];
     alignas(16) float st[Cf::DVS * Cf::KSTR];  // S^T copy: st[n][c] = S[c][nbase + n]
-    int unsafe;                                // this chunk's gates are too strong for the fast path
+    int unsafe[4];                             // per wave: this chunk's gates are too strong for the fast path
 };
 
 template <int DK, int NT>
@@ -113,72 +113,143 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
 #pragma unroll
         for (int r = 0; r < 4; ++r) sm.st[(16 * nt + 4 * g + r) * KSTR + 16 * kt + l16] = sacc[m][r];
     }
-    float ltot = 0.f;  // state-only pass: this thread's channel's log-gate total over the segment
+    // Staging.  q and the value slice load as 16-byte rows; keys and log-gates
+    // in a column layout: lane (c16, rq) of wave W holds key channels
+    // 16 W + c16 + 64 u (u < DK / 64) of rows 16 rq .. 16 rq + 15, i.e. one
+    // 16-token tile per channel, so the running gate sums, the tile totals and
+    // the pre-scaled keys K^ come out of registers.  The next chunk's loads
+    // are issued before the current chunk's products.
+    constexpr int NU = C * DK / 4 / kThreads;
+    constexpr int NV = (C * DVS / 4 + kThreads - 1) / kThreads;
+    constexpr int CPW = DK / 64;
+    static_assert(NU * kThreads * 4 == C * DK, "q staging split");
+    const int c16 = l & 15, rq = l >> 4;
+    f32x4 pq[SO ? 1 : NU], pv[NV];
+    float pk[CPW][16], pg[CPW][16];
+    float ltot[CPW];  // state-only pass: log-gate totals of this lane's channels over the segment
+#pragma unroll
+    for (int u = 0; u < CPW; ++u) ltot[u] = 0.f;
 
     const int nch = (T + C - 1) / C;
     const int c_begin = seg * a.cps;
     const int c_end = (c_begin + a.cps < nch) ? c_begin + a.cps : nch;
+    auto chunk_len = [&](int c) {
+        const long long t0 = static_cast<long long>(c) * C;
+        return (T - t0 < C) ? static_cast<int>(T - t0) : C;
+    };
+    // rows past the end read row 0 of the chunk (always valid); they are zeroed when stored
+    auto load_qv = [&](int c) {
+        const long long t0 = static_cast<long long>(c) * C;
+        const int clen = chunk_len(c);
+        if constexpr (!SO) {
+#pragma unroll
+            for (int m = 0; m < NU; ++m) {
+                const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
+                pq[m] = *reinterpret_cast<const f32x4*>(qh + (t0 + (r < clen ? r : 0)) * DK + c4);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NV; ++m) {
+            const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
+            if (u < C * DVS / 4) pv[m] = *reinterpret_cast<const f32x4*>(vh + (t0 + (r < clen ? r : 0)) * DV + c4);
+        }
+    };
+    auto load_kg = [&](int c) {
+        const long long t0 = static_cast<long long>(c) * C;
+        const int clen = chunk_len(c);
+#pragma unroll
+        for (int u = 0; u < CPW; ++u) {
+            const int ch = 16 * W + c16 + 64 * u;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = 16 * rq + i;
+                const long long o = (t0 + (r < clen ? r : 0)) * DK + ch;
+                pk[u][i] = kh[o];
+                pg[u][i] = gh[o];
+            }
+        }
+    };
+    // With dk = 128 the registers do not hold the next chunk's keys and gates
+    // beside the products, so each chunk loads its own at the top of its step.
+    constexpr bool KG_EARLY = DK == 64;
+    if (c_begin < c_end) {
+        load_qv(c_begin);
+        if constexpr (KG_EARLY) load_kg(c_begin);
+    }
+
     for (int c = c_begin; c < c_end; ++c) {
         const long long t0 = static_cast<long long>(c) * C;
-        const int clen = (T - t0 < C) ? static_cast<int>(T - t0) : C;
-        __syncthreads();  // the previous chunk's reads of q, k, b, v are done
-        if (tid == 0) sm.unsafe = 0;
+        const int clen = chunk_len(c);
+        if constexpr (!KG_EARLY) load_kg(c);
+        __syncthreads();  // the previous chunk's reads of q, k, b, v and the flags are done
 
-        // ---- stage the chunk (rows past the end: zeros, gate 1).  All of a
-        // thread's loads are issued before any LDS store; a row past the end
-        // reads row 0 of the chunk (always valid) and is zeroed afterwards.
+        // ---- store the chunk (rows past the end: zeros, log-gate 0)
         {
-            constexpr int NU = C * DK / 4 / kThreads, NV = (C * DVS / 4 + kThreads - 1) / kThreads;
-            static_assert(NU * kThreads * 4 == C * DK, "q/k/gate staging split");
-            f32x4 xq[NU], xk[NU], xg[NU], xv[NV];
-#pragma unroll
-            for (int m = 0; m < NU; ++m) {
-                const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
-                const long long o = (t0 + (r < clen ? r : 0)) * DK + c4;
-                if constexpr (!SO) xq[m] = *reinterpret_cast<const f32x4*>(qh + o);
-                xk[m] = *reinterpret_cast<const f32x4*>(kh + o);
-                xg[m] = *reinterpret_cast<const f32x4*>(gh + o);
-            }
-#pragma unroll
-            for (int m = 0; m < NV; ++m) {
-                const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
-                if (u < C * DVS / 4) xv[m] = *reinterpret_cast<const f32x4*>(vh + (t0 + (r < clen ? r : 0)) * DV + c4);
-            }
             const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (!SO) {
 #pragma unroll
-            for (int m = 0; m < NU; ++m) {
-                const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
-                const bool in = r < clen;
-                if constexpr (!SO) *reinterpret_cast<f32x4*>(&sm.q[r * KSTR + c4]) = in ? xq[m] : zero;
-                *reinterpret_cast<f32x4*>(&sm.k[r * KSTR + c4]) = in ? xk[m] : zero;
-                *reinterpret_cast<f32x4*>(&sm.b[r * KSTR + c4]) = in ? xg[m] : zero;
+                for (int m = 0; m < NU; ++m) {
+                    const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
+                    *reinterpret_cast<f32x4*>(&sm.q[r * KSTR + c4]) = (r < clen) ? pq[m] : zero;
+                }
             }
 #pragma unroll
             for (int m = 0; m < NV; ++m) {
                 const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
-                if (u < C * DVS / 4) *reinterpret_cast<f32x4*>(&sm.v[r * VSTR + c4]) = (r < clen) ? xv[m] : zero;
+                if (u < C * DVS / 4) *reinterpret_cast<f32x4*>(&sm.v[r * VSTR + c4]) = (r < clen) ? pv[m] : zero;
             }
+            int bad = 0;
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) {
+                const int ch = 16 * W + c16 + 64 * u;
+                float cum[16];
+                float run = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    run += (16 * rq + i < clen) ? pg[u][i] : 0.f;
+                    cum[i] = run;
+                }
+                // tile totals of the four row quarters of this channel (lanes c16 + 16 q)
+                const float t0s = __shfl(run, c16), t1s = __shfl(run, c16 + 16);
+                const float t2s = __shfl(run, c16 + 32), t3s = __shfl(run, c16 + 48);
+                const float off = (rq > 0 ? t0s : 0.f) + (rq > 1 ? t1s : 0.f) + (rq > 2 ? t2s : 0.f);
+                const float tot = t0s + t1s + t2s + t3s;
+                if (!(tot >= -80.f)) bad = 1;
+                ltot[u] += tot;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = 16 * rq + i;
+                    sm.b[r * KSTR + ch] = off + cum[i];
+                    // K^ = k e^{b_{e_J} - b_j}: the tile's total minus the running sum
+                    sm.k[r * KSTR + ch] = ((r < clen) ? pk[u][i] : 0.f) * __expf(run - cum[i]);
+                }
+            }
+            const bool wbad = __any(bad);
+            if (l == 0) sm.unsafe[W] = wbad ? 1 : 0;
         }
         __syncthreads();
-        // ---- running sums of the log-gates down each key channel: the column
-        // is read into registers first (independent loads), summed there and
-        // written back
-        if (tid < DK) {
-            float col[C];
+        const bool unsafe = (sm.unsafe[0] | sm.unsafe[1] | sm.unsafe[2] | sm.unsafe[3]) != 0;
+        if (unsafe) {
+            // the exact path works from the raw keys
 #pragma unroll
-            for (int r = 0; r < C; ++r) col[r] = sm.b[r * KSTR + tid];
+            for (int u = 0; u < CPW; ++u) {
+                const int ch = 16 * W + c16 + 64 * u;
 #pragma unroll
-            for (int r = 1; r < C; ++r) col[r] += col[r - 1];
-#pragma unroll
-            for (int r = 0; r < C; ++r) sm.b[r * KSTR + tid] = col[r];
-            if (!(col[C - 1] >= -80.f)) sm.unsafe = 1;  // every thread that writes writes 1
-            ltot += col[C - 1];
+                for (int i = 0; i < 16; ++i) {
+                    const int r = 16 * rq + i;
+                    sm.k[r * KSTR + ch] = (r < clen) ? pk[u][i] : 0.f;
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
+        if (c + 1 < c_end) {
+            load_qv(c + 1);
+            if constexpr (KG_EARLY) load_kg(c + 1);
+        }
 
         const int qi = 16 * I + l16;  // this lane's query row
         const int last = clen - 1;
-        if (!sm.unsafe) {
+        if (!unsafe) {
             // ---- fast path (see the header): Q factors in registers, K^ in place of k
             constexpr int NQ = DK / 4;
             const int eI = 16 * I + 15;
@@ -190,12 +261,6 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 qd[s] = qv * __expf(bq - sm.b[eI * KSTR + ch]);
                 qx[s] = qv * __expf(bq);
             }
-            for (int u = tid; u < C * DK; u += kThreads) {  // each element rewritten by its own thread
-                const int j = u / DK, ch = u % DK;
-                const int eJ = (j | 15);
-                sm.k[j * KSTR + ch] *= __expf(sm.b[eJ * KSTR + ch] - sm.b[j * KSTR + ch]);
-            }
-            __syncthreads();
 
             f32x4 pacc[I + 1];
 #pragma unroll
@@ -339,7 +404,10 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
             *reinterpret_cast<f32x4*>(out + (16 * kt + l16) * DV + nbase + 16 * nt + 4 * g) = sacc[m];
         }
-        if (nbase == 0 && tid < DK) out[DK * DV + tid] = ltot;
+        if (nbase == 0 && rq == 0) {
+#pragma unroll
+            for (int u = 0; u < CPW; ++u) out[DK * DV + 16 * W + c16 + 64 * u] = ltot[u];
+        }
         return;
     }
     if (a.final_state && seg == a.G - 1) {
