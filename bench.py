@@ -35,6 +35,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 FWD_SOURCES = ["retention_chunkwise_amd/csrc/seg_kernel.h", "retention_chunkwise_amd/csrc/kcommon.h",
                "retention_chunkwise_amd/csrc/internal.h"]
 DECODE_SOURCES = ["retention_chunkwise_amd/csrc/decode.hip", "retention_chunkwise_amd/csrc/internal.h"]
+F32_SOURCES = ["retention_chunkwise_amd/csrc/walk_kernel.h", "retention_chunkwise_amd/csrc/kcommon.h",
+               "retention_chunkwise_amd/csrc/internal.h"]
+GLA_SOURCES = ["retention_chunkwise_amd/csrc/gla.hip", "retention_chunkwise_amd/csrc/kcommon.h",
+               "retention_chunkwise_amd/csrc/internal.h"]
 
 
 def sources_sha(paths) -> str:
@@ -336,13 +340,16 @@ def main():
         f_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, wf.chunk)
         f_by = M.fwd_bytes(wf.B, wf.H, wf.T, wf.dk, wf.dv, 4, final_state=True)
         f_tf = f_fl / (f_kern * 1e-3) / 1e12
+        f_tr = measured_traffic("fwd_f32_ret_fwd_mh_f32", F32_SOURCES)
         res["fwd_f32"] = {
             "workload": wf.name, "ms_per_call": f_kern, "wall_ms_per_call": f_wall,
             "tokens_per_s": wf.B * wf.T / (f_kern * 1e-3),
             "tflops": f_tf, "gbs": f_by / (f_kern * 1e-3) / 1e9,
             "roofline": {"kernel": "retention_fwd fp32: walk_kernel<fp32, C=64, dk=64>", "bound": "mfma",
                          "achieved": f_tf, "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                         "frac": f_tf / M.PEAK_TFLOPS["f32"], "traffic": None},
+                         "frac": f_tf / M.PEAK_TFLOPS["f32"],
+                         "traffic": (f_tr["bytes_per_launch"] if f_tr else None),
+                         "algorithmic_bytes_per_launch": f_by},
         }
         del fq, fk, fv, fout, ffs
 
@@ -362,12 +369,16 @@ def main():
         g_kern, g_wall = time_launches(glastep, max(args.steps, 100), args.warmup)
         g_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, 64)
         g_tf = g_fl / (g_kern * 1e-3) / 1e12
+        g_tr = measured_traffic("gla_gla_mh_f32", GLA_SOURCES)
+        g_by = M.fwd_bytes(wf.B, wf.H, wf.T, wf.dk, wf.dv, 4, final_state=True) + wf.B * wf.H * wf.T * wf.dk * 4
         res["gla_f32"] = {
             "workload": "gated linear attention, fp32 [4, 8, 2048, 64], log-gates logsigmoid(N(2, 1))",
             "ms_per_call": g_kern, "tokens_per_s": wf.B * wf.T / (g_kern * 1e-3), "tflops": g_tf,
             "roofline": {"kernel": "gla_fwd: gla_kernel<dk=64>", "bound": "mfma", "achieved": g_tf,
                          "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": g_tf / M.PEAK_TFLOPS["f32"],
-                         "traffic": None},
+                         "traffic": (g_tr["bytes_per_launch"] if g_tr else None),
+                         # q, k, v, log-gates read, out and final state written
+                         "algorithmic_bytes_per_launch": g_by},
         }
         del glg, gq, gk, gv, gout, gfs
 

@@ -1,0 +1,196 @@
+"""Summaries of rocprofv3 runs of bench.py, written under profiles/.
+
+    python -m retention_chunkwise_amd.profsum stats STATS_CSV BENCH_LOG
+        kernel durations (rocprofv3 --kernel-trace --stats) next to bench.py's
+        own HIP-event figures -> profiles/kernel_stats_bench_workloads.md
+    python -m retention_chunkwise_amd.profsum traffic FETCH_CSV WRITE_CSV
+        HBM bytes per call of each bench workload from two counter runs
+        (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) -> profiles/hbm_traffic_*.json
+
+Counter scaling: each counter is divided by what it reads, per byte, for the
+plain 1 GiB device copies that `bench.py --calibrate-copy` runs in the same
+process (FETCH_SIZE and WRITE_SIZE are KiB per dispatch).  A summary records
+the hash of the kernel sources it was taken with; bench.py reports no traffic
+once those sources change.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 30
+
+STATS_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
+             "-d $REPO/gpurun_out/prof_stats -o stats -- python3 $REPO/bench.py --steps 20 --warmup 3 "
+             "--decode-steps 200 --no-cpu-baseline")
+PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
+           "-d $REPO/gpurun_out/pmc_{tag} -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+           "--decode-steps 20 --no-cpu-baseline --calibrate-copy")
+
+SEG = "::seg_"
+# One call of each bench workload: (part of the kernel name, dispatches per call).
+# The dq walk of the backward is an ordinary forward walk with the same
+# shapes as the long forward, so both share those two kernels' averages.
+WORKLOADS = {
+    "fwd_ret_fwd_long_bf16": {
+        "what": "retention_fwd, [1, 32, 65536, 128] bf16, chunk 128",
+        "kernels": [(SEG + "state_kernel<128, 128, 0, false>", 1),
+                    (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
+        "algorithmic": 2149580800, "sources": "FWD_SOURCES"},
+    "bwd_ret_fwd_long_bf16": {
+        "what": "retention_bwd on the long workload: dv walk (reversed, with the state pass), dk walk "
+                "(reversed, reading the dv walk's segment states), dq walk (forward)",
+        "kernels": [(SEG + "state_kernel<128, 128, 0, true>", 1),
+                    (SEG + "walk_kernel<128, 128, 128, 0, true>", 2),
+                    (SEG + "state_kernel<128, 128, 0, false>", 1),
+                    (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
+        "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
+    "fwd_normalized_ret_fwd_long_bf16": {
+        "what": "retention_fwd_normalized (row-sum floor + GroupNorm) on the long workload",
+        "kernels": [(SEG + "state_kernel<128, 128, 2, false>", 1),
+                    (SEG + "walk_kernel<64, 128, 128, 3, false>", 1)],
+        "algorithmic": 2147483648, "sources": "FWD_SOURCES"},
+    "linattn_linattn_elu1_bf16": {
+        "what": "linear_attn_fwd, elu+1, [8, 16, 8192, 64] bf16",
+        "kernels": [(SEG + "state_kernel<64, 64, 1, false>", 1),
+                    (SEG + "walk_kernel<128, 64, 64, 1, false>", 1)],
+        "algorithmic": 536870912, "sources": "FWD_SOURCES"},
+    "decode_kernel_decode_bf16": {
+        "what": "retention_decode_step, 256 x 32 heads, 128 x 128 fp32 state",
+        "kernels": [("::decode_kernel<true, 128, 128, false>", 1)],
+        "algorithmic": 1082130432, "sources": "DECODE_SOURCES"},
+    "linattn_decode_kernel_decode_bf16": {
+        "what": "linear_attn_decode_step, 256 x 32 heads, 128 x 128 fp32 state + normaliser",
+        "kernels": [("::decode_kernel<true, 128, 128, true>", 1)],
+        "algorithmic": 1082130432 + 2 * 256 * 32 * 128 * 4, "sources": "DECODE_SOURCES"},
+    "fwd_f32_ret_fwd_mh_f32": {
+        "what": "retention_fwd fp32 [4, 8, 2048, 64], chunk 64, final state",
+        "kernels": [("::slice_state_kernel<false, 64, 64, false>", 1),
+                    ("walk::walk_kernel<false, 64, 64, 4, false>", 1)],
+        "algorithmic": 4 * 8 * 2048 * 64 * 4 * 4 + 4 * 8 * 64 * 64 * 4, "sources": "F32_SOURCES"},
+    "gla_gla_mh_f32": {
+        "what": "gla_fwd fp32 [4, 8, 2048, 64], final state",
+        "kernels": [("::gla_kernel<64, 4, true>", 1),
+                    ("::gla_kernel<64, 4, false>", 1)],
+        "algorithmic": 4 * 8 * 2048 * 64 * 4 * 5 + 4 * 8 * 64 * 64 * 4, "sources": "GLA_SOURCES"},
+}
+
+
+def _bench():
+    sys.path.insert(0, ROOT)
+    import bench  # noqa: E402  (for the source lists and their hash)
+
+    return bench
+
+
+def _strip_args(name: str) -> str:
+    """Kernel name without its parameter list (the last parenthesised part)."""
+    return name[:name.rfind("(")] if name.endswith(")") else name
+
+
+def _per_dispatch(path: str) -> dict[str, list[float]]:
+    """Counter value per dispatch, grouped by kernel name (signature dropped)."""
+    per = collections.defaultdict(float)
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            per[d] += float(r["Counter_Value"])
+            names[d] = _strip_args(r["Kernel_Name"])
+    out = collections.defaultdict(list)
+    for d in sorted(per):
+        out[names[d]].append(per[d])
+    return out
+
+
+def _find(groups: dict[str, list[float]], key: str) -> list[float]:
+    hits = [v for k, v in groups.items() if key in k]
+    if len(hits) != 1:
+        raise SystemExit(f"profsum: expected one kernel whose name contains {key!r}, found {len(hits)}")
+    return hits[0]
+
+
+def traffic(fetch_csv: str, write_csv: str) -> None:
+    b = _bench()
+    fetch, write = _per_dispatch(fetch_csv), _per_dispatch(write_csv)
+    cf, cw = _find(fetch, COPY_KERNEL), _find(write, COPY_KERNEL)
+    cf_kib, cw_kib = sum(cf) / len(cf), sum(cw) / len(cw)
+    fscale, wscale = COPY_BYTES / (cf_kib * 1024), COPY_BYTES / (cw_kib * 1024)
+    for name, spec in WORKLOADS.items():
+        srcs = getattr(b, spec["sources"])
+        ks, fb, wb = [], 0.0, 0.0
+        for prefix, per_call in spec["kernels"]:
+            fv, wv = _find(fetch, prefix), _find(write, prefix)
+            fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+            ks.append({"kernel": prefix, "per_call": per_call, "dispatches_fetch": len(fv),
+                       "dispatches_write": len(wv), "fetch_kib_raw": fk, "write_kib_raw": wk,
+                       "fetch_bytes": fk * 1024 * fscale, "write_bytes": wk * 1024 * wscale})
+            fb += per_call * fk * 1024 * fscale
+            wb += per_call * wk * 1024 * wscale
+        d = {"workload": spec["what"], "kernels": ks, "source_sha": b.sources_sha(srcs), "sources": srcs,
+             "fetch_scale": fscale, "write_scale": wscale, "fetch_bytes": fb, "write_bytes": wb,
+             "bytes_per_launch": fb + wb, "algorithmic_bytes_per_launch": spec["algorithmic"],
+             "traffic_over_algorithmic": (fb + wb) / spec["algorithmic"],
+             "calibration": (f"plain 1 GiB device copy ({COPY_KERNEL}): FETCH_SIZE read {cf_kib:.1f} KiB, "
+                             f"WRITE_SIZE {cw_kib:.1f} KiB"),
+             "commands": [PMC_CMD.format(ctr="FETCH_SIZE", tag="fetch"),
+                          PMC_CMD.format(ctr="WRITE_SIZE", tag="write")]}
+        with open(os.path.join(PROFILES, f"hbm_traffic_{name}.json"), "w") as f:
+            json.dump(d, f, indent=1)
+            f.write("\n")
+        print(f"{name}: {(fb + wb) / 1e9:.3f} GB per call ({(fb + wb) / spec['algorithmic']:.2f}x algorithmic)")
+
+
+BENCH_LINES = [("retention forward (long bf16, state + walk kernels)", ("roofline", "kernel_ms"), 1e6, "ns per call"),
+               ("backward (dq, dk, dv) of the long forward", ("backward", "ms_per_call"), 1e6, "ns per call"),
+               ("forward with row-sum floor + GroupNorm (long bf16)", ("fwd_normalized", "ms_per_call"), 1e6,
+                "ns per call"),
+               ("decode step", ("decode", "us_per_step"), 1e3, "ns per step"),
+               ("elu+1 decode step", ("linear_attn_decode", "us_per_step"), 1e3, "ns per step"),
+               ("linear attention [8, 16, 8192, 64] bf16", ("linear_attn", "ms_per_call"), 1e6, "ns per call"),
+               ("fp32 forward [4, 8, 2048, 64]", ("fwd_f32", "ms_per_call"), 1e6, "ns per call"),
+               ("gated linear attention fp32 [4, 8, 2048, 64]", ("gla_f32", "ms_per_call"), 1e6, "ns per call")]
+
+
+def stats(stats_csv: str, bench_log: str) -> None:
+    b = _bench()
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            n = r["Name"]
+            if n.startswith("void ret::"):
+                rows.append((_strip_args(n).replace("void ret::", ""), int(r["Calls"]), float(r["AverageNs"]),
+                             float(r["MinNs"]), float(r["MaxNs"]), float(r["TotalDurationNs"])))
+    rows.sort(key=lambda x: -x[5])
+    line = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")][-1]
+    res = json.loads(line)
+    out = ["# Kernel durations — bench workloads on one MI355X", "",
+           "Command (repository root as $REPO):", "", "    " + STATS_CMD, "",
+           "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for n, c, a, mn, mx, _ in rows:
+        out.append(f"| `{n}` | {c} | {a:,.0f} | {mn:,.0f} | {mx:,.0f} |")
+    out += ["", "bench.py's own HIP-event figures in the same run:", ""]
+    for label, (k1, k2), mul, unit in BENCH_LINES:
+        if k1 in res and k2 in res[k1]:
+            out.append(f"- {label}: {res[k1][k2] * mul:,.0f} {unit}")
+    out += ["", "Source hashes: segment kernels " + b.sources_sha(b.FWD_SOURCES) + ", decode "
+            + b.sources_sha(b.DECODE_SOURCES) + ", fp32 walk " + b.sources_sha(b.F32_SOURCES) + ", GLA "
+            + b.sources_sha(b.GLA_SOURCES) + "."]
+    with open(os.path.join(PROFILES, "kernel_stats_bench_workloads.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+if __name__ == "__main__":
+    if len(sys.argv) == 4 and sys.argv[1] == "stats":
+        stats(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 4 and sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3])
+    else:
+        raise SystemExit(__doc__)
