@@ -382,6 +382,16 @@ def main():
         }
         del glg, gq, gk, gv, gout, gfs
 
+    # ---------------- context: a plain device copy of 1 GiB (read + write), the
+    # ceiling a kernel that streams each byte once in and once out can expect
+    if not args.no_components:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        c_ms, _ = time_launches(lambda: dst.copy_(src), 10, 2)
+        res["hbm_copy_gbs"] = 2 * n * 4 / (c_ms * 1e-3) / 1e9
+        del src, dst
+
     if args.calibrate_copy:
         # plain device-to-device copies of a known size, for scaling HBM counters
         n = 1 << 28  # 1 GiB of fp32
