@@ -11,7 +11,8 @@ JSON line also carries the other measured parts of the path: the recurrent
 decode step (256 sequences x 32 heads, 128 x 128 fp32 state, 1000 consecutive
 steps), the elu+1 linear-attention forward (batch 8, 16 heads, T = 8192,
 d = 64), the elu+1 decode step on the decode shapes, the backward pass of the
-long forward, the long forward with the row-sum floor and GroupNorm fused,
+long forward, the long forward with the row-sum floor and GroupNorm fused, the backward again
+given the forward's segment states (as a training step keeps them),
 the fp32 [4, 8, 2048, 64] forward and gated linear attention on that shape,
 each with its own roofline figures.
 
@@ -221,6 +222,23 @@ def main():
             "roofline": {"kernel": "retention_bwd: three segment walks (dq forward; dk, dv time-reversed)",
                          "bound": "hbm", "achieved": b_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": b_gbs / M.PEAK_HBM_GBS, "traffic": (b_tr["bytes_per_launch"] if b_tr else None),
+                         "algorithmic_bytes_per_launch": b_by},
+        }
+        # the same backward given the forward's segment states: a training step keeps the forward's
+        # workspace (`ws` holds the states of the forward timed above, same q, k, v, gamma and chunk)
+        def bstep_ff():
+            rc.retention_bwd(q, k, v, gamma, dout, chunk=w.chunk, dq=gq, dk=gk, dv=gv, workspace=bws,
+                             fwd_workspace=ws)
+
+        f_kern, f_wall = time_launches(bstep_ff, max(args.steps // 2, 5), args.warmup)
+        f_gbs = b_by / (f_kern * 1e-3) / 1e9
+        f_tr = measured_traffic("bwd_from_fwd_ret_fwd_long_bf16", FWD_SOURCES)
+        res["backward_from_fwd"] = {
+            "workload": w.name + " backward given the forward's segment states (retention_bwd_from_fwd)",
+            "ms_per_call": f_kern, "tokens_per_s": tokens / (f_wall * 1e-3), "ratio_to_forward": f_kern / kern_ms,
+            "roofline": {"kernel": "retention_bwd_from_fwd: dv walk + state pass, dk walk, dq walk (no state pass)",
+                         "bound": "hbm", "achieved": f_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": f_gbs / M.PEAK_HBM_GBS, "traffic": (f_tr["bytes_per_launch"] if f_tr else None),
                          "algorithmic_bytes_per_launch": b_by},
         }
         del dout, gq, gk, gv, bws

@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 7
+#define RET_ABI_VERSION 8
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -209,6 +209,38 @@ int retention_bwd(const void *q, const void *k, const void *v, const float *gamm
 /* Workspace bytes retention_bwd needs for these arguments (0: none, or the
  * arguments are invalid).  Host only. */
 size_t retention_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype);
+
+/*
+ * retention_bwd_from_fwd -- retention_bwd for a training step whose forward
+ * kept its workspace.  The query gradient dq_t = S_t dout_t walks the forward
+ * recurrence S_t = gamma S_{t-1} + v_t k_t^T with the roles of keys and values
+ * swapped; its per-segment state sums are the transposes of the ones the
+ * forward (S_t = gamma S_{t-1} + k_t v_t^T, "RetNet", recurrent
+ * representation) left in its workspace.  Reading those instead of summing
+ * them again saves one read of k and v over all but the last segment.
+ *
+ *   fwd_workspace  device, read only: the workspace of a retention_fwd or
+ *                  retention_fwd_from_state call that completed earlier in
+ *                  stream order, with the same k, v, gamma, chunk, B, H, T,
+ *                  dk, dv and dtype (the initial state does not matter), not
+ *                  written since; it may be NULL when that call needed none
+ *                  (retention_fwd_workspace_bytes(...) == 0).  The library
+ *                  cannot check that it holds those states: a different
+ *                  buffer gives wrong dq without an error.
+ *   fwd_ws_bytes   its size; at least retention_fwd_workspace_bytes(...)
+ *   everything else: as retention_bwd, including `workspace`, which must be a
+ *                  separate buffer of retention_bwd_workspace_bytes(...) bytes
+ *
+ * Errors: those of retention_bwd; RET_ERR_WORKSPACE when fwd_workspace is
+ * NULL or short although the forward needed one; RET_ERR_ALIGN when it is not
+ * 16-byte aligned; RET_ERR_ALIAS when it overlaps dq, dk, dv or `workspace`.
+ * If the tuning knobs changed the forward's segment plan between the calls,
+ * dq runs its own state pass (the result is unchanged).
+ */
+int retention_bwd_from_fwd(const void *q, const void *k, const void *v, const float *gamma, int chunk,
+                           const void *dout, const void *fwd_workspace, size_t fwd_ws_bytes, void *dq,
+                           void *dk, void *dv, int B, int H, int T, int d_k, int d_v, int dtype,
+                           void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * retention_decode_step -- one recurrent step for N sequences x H heads,

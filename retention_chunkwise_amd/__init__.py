@@ -15,7 +15,7 @@ retention_decode_step(q, k, v, gamma, state)   -> out      (state updated in pla
 linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
 linear_attn_fwd(..., initial_state=(S, z), return_state=True) -> (out, S, z)
 linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place)
-retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv)
+retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv); fwd_workspace= reuses a forward's states
 retention_fwd_normalized(q, k, v, gamma, norm="group", eps=1e-5) -> out   (bf16)
 retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.autograd)
 gla_fwd(q, k, v, log_gate)                     -> (out, final_state)   (fp32)
@@ -99,6 +99,9 @@ def load_library():
             lib.linear_attn_decode_step.restype = i
             lib.retention_bwd.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
             lib.retention_bwd.restype = i
+            lib.retention_bwd_from_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, vp,
+                                                   sz, vp]
+            lib.retention_bwd_from_fwd.restype = i
             lib.retention_fwd_normalized.argtypes = [vp, vp, vp, fp, i, i, ctypes.c_float, vp, i, i, i, i, i, i, vp,
                                                      sz, vp]
             lib.retention_fwd_normalized.restype = i
@@ -311,9 +314,15 @@ def gla_fwd(q, k, v, log_gate, out=None, final_state=None, want_state: bool = Tr
     return out, final_state
 
 
-def retention_bwd(q, k, v, gamma, dout, chunk: int = 64, dq=None, dk=None, dv=None, workspace=None):
+def retention_bwd(q, k, v, gamma, dout, chunk: int = 64, dq=None, dk=None, dv=None, workspace=None,
+                  fwd_workspace=None):
     """Gradients (dq, dk, dv) of retention_fwd (zero initial state) given
-    dout = dL/dout; all tensors [B,H,T,*] in one dtype on the GPU."""
+    dout = dL/dout; all tensors [B,H,T,*] in one dtype on the GPU.
+
+    fwd_workspace: optional uint8 GPU tensor that a retention_fwd call on the
+    same k, v, gamma and chunk was given as its workspace (and that nothing has
+    written since); dq then reuses the segment states it holds.  It must not be
+    the workspace of this call."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
         _check_dev(n, t, q.dtype)
@@ -331,26 +340,39 @@ def retention_bwd(q, k, v, gamma, dout, chunk: int = 64, dq=None, dk=None, dv=No
     g = _gamma_array(gamma, H)
     dt = _dtype_code(q)
     ws, nws = _workspace(lib.retention_bwd_workspace_bytes(B, H, T, d_k, d_v, int(chunk), dt), q.device, workspace)
-    rc = lib.retention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), dout.data_ptr(), dq.data_ptr(),
-                           dk.data_ptr(), dv.data_ptr(), B, H, T, d_k, d_v, dt, _ptr(ws), nws, _stream(q))
+    if fwd_workspace is None:
+        rc = lib.retention_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), dout.data_ptr(),
+                               dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, T, d_k, d_v, dt, _ptr(ws), nws,
+                               _stream(q))
+    else:
+        _check_dev("fwd_workspace", fwd_workspace, torch.uint8)
+        rc = lib.retention_bwd_from_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), dout.data_ptr(),
+                                        _ptr(fwd_workspace), fwd_workspace.numel(), dq.data_ptr(), dk.data_ptr(),
+                                        dv.data_ptr(), B, H, T, d_k, d_v, dt, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return dq, dk, dv
 
 
 class _Retention(torch.autograd.Function):
-    """Autograd glue: forward is retention_fwd, backward is retention_bwd."""
+    """Autograd glue: forward is retention_fwd, backward is retention_bwd_from_fwd
+    with the forward's workspace (its segment states), kept until backward."""
 
     @staticmethod
     def forward(ctx, q, k, v, gamma, chunk):
-        out, _ = retention_fwd(q, k, v, gamma, chunk=chunk, want_state=False)
+        B, H, T, d_k = q.shape
+        n = retention_fwd_workspace_bytes(B, H, T, d_k, v.shape[3], chunk, q.dtype)
+        fws = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+        out, _ = retention_fwd(q, k, v, gamma, chunk=chunk, want_state=False, workspace=fws)
         ctx.save_for_backward(q, k, v)
-        ctx.gamma, ctx.chunk = gamma, chunk
+        ctx.gamma, ctx.chunk, ctx.fws = gamma, chunk, fws
         return out
 
     @staticmethod
     def backward(ctx, dout):
         q, k, v = ctx.saved_tensors
-        dq, dk, dv = retention_bwd(q, k, v, ctx.gamma, dout.contiguous(), chunk=ctx.chunk)
+        # without a forward workspace (one segment, or the fp32 path) there are no states to share
+        dq, dk, dv = retention_bwd(q, k, v, ctx.gamma, dout.contiguous(), chunk=ctx.chunk, fwd_workspace=ctx.fws)
+        ctx.fws = None
         return dq, dk, dv, None, None
 
 

@@ -502,6 +502,105 @@ int decode_checks(const char* fn, const void* q, const void* k, const void* v, c
     return RET_OK;
 }
 
+// retention_bwd, and retention_bwd_from_fwd when fn_fwd_ws is set: the dq walk
+// then reads the forward's segment states instead of running its own state pass.
+int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const float* gamma, int chunk,
+             const void* dout, const void* fwd_ws, size_t fwd_ws_bytes, bool with_fwd, void* dq, void* dk, void* dv,
+             int B, int H, int T, int d_k, int d_v, int dtype, void* workspace, size_t ws_bytes, void* stream) {
+    if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
+    if (chunk != 64 && chunk != 128) return fail(RET_ERR_CHUNK, "%s: chunk must be 64 or 128 (got %d)", fn, chunk);
+    if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
+        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)", fn, ret::kMaxHeads, B,
+                    H, T);
+    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128))
+        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, d_k, d_v);
+    size_t nqk = esz, nv = esz;
+    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, d_k) ||
+        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, d_v))
+        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
+    if (nqk > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
+        return fail(RET_ERR_NULL, "%s: q, k, v, dout, dq, dk and dv must be non-NULL", fn);
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+        !aligned16(dv))
+        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
+    float log2g[ret::kMaxHeads] = {};
+    int rc = check_gamma(fn, gamma, H, log2g);
+    if (rc) return rc;
+    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv), rdo = range("dout", dout, nv);
+    const Range rdq = range("dq", dq, nqk), rdk = range("dk", dk, nqk), rdv = range("dv", dv, nv);
+    for (const Range& o : {rdq, rdk, rdv}) {
+        for (const Range& in : {rq, rk, rv, rdo})
+            if (overlap(o, in)) return fail(RET_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, in.name);
+    }
+    if (overlap(rdq, rdk) || overlap(rdq, rdv) || overlap(rdk, rdv))
+        return fail(RET_ERR_ALIAS, "%s: the gradient outputs overlap", fn);
+    if (B == 0) return ok();
+    const long long bh = static_cast<long long>(B) * H;
+    SegPlan plans[3];
+    size_t need = 0;
+    if (!plan_bwd(bh, T, chunk, d_k, d_v, dtype, plans, &need))
+        return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    SegPlan wplan;
+    wplan.ws_bytes = need;
+    rc = check_workspace(fn, wplan, workspace, ws_bytes, {rq, rk, rv, rdo, rdq, rdk, rdv});
+    if (rc) return rc;
+    // The forward's segment states, if it left any: Sum gamma^.. k v^T per segment, the transposes
+    // of the dq walk's (keys v, values k) over the same segments.
+    bool dq_shares = false;
+    if (with_fwd) {
+        SegPlan fplan;
+        if (!plan_fwd(bh, T, chunk, d_k, d_v, false, dtype, &fplan))
+            return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+        if (fplan.ws_bytes > 0) {
+            if (!fwd_ws || fwd_ws_bytes < fplan.ws_bytes)
+                return fail(RET_ERR_WORKSPACE, "%s: the forward's workspace must hold %zu bytes (got %zu%s)", fn,
+                            fplan.ws_bytes, fwd_ws_bytes, fwd_ws ? "" : ", NULL");
+            if (!aligned16(fwd_ws)) return fail(RET_ERR_ALIGN, "%s: fwd_workspace must be 16-byte aligned", fn);
+            const Range rf = range("fwd_workspace", fwd_ws, fplan.ws_bytes);
+            for (const Range& o : {rdq, rdk, rdv, range("workspace", workspace, need)})
+                if (overlap(rf, o)) return fail(RET_ERR_ALIAS, "%s: fwd_workspace overlaps %s", fn, o.name);
+            // the forward's plan must be the one the dq walk uses (it is, unless the tuning
+            // knobs changed between the calls; then the dq walk runs its own state pass)
+            dq_shares = fplan.path == FwdPath::kSegment && plans[0].path == FwdPath::kSegment &&
+                        fplan.G == plans[0].G && fplan.cps == plans[0].cps && fplan.pieces == plans[0].pieces;
+        }
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const FwdState none;
+    // (query input, key input, value input, output, key width, value width, reversed)
+    struct Walk {
+        const void *a, *b, *c;
+        void* o;
+        int wk, wv;
+        bool rev;
+    };
+    // dv first: its segment states sum q_s dout_s^T, the transpose of what the dk walk needs
+    // (dout_s q_s^T over the same reversed segments), so on the segment path the dk walk reads
+    // them transposed instead of running its own state pass
+    const Walk walks[3] = {{k, q, dout, dv, d_k, d_v, true}, {v, dout, q, dk, d_v, d_k, true},
+                           {dout, v, k, dq, d_v, d_k, false}};
+    const SegPlan* wplans[3] = {&plans[2], &plans[1], &plans[0]};
+    const bool share = plans[1].path == FwdPath::kSegment && plans[2].path == FwdPath::kSegment &&
+                       plans[1].G == plans[2].G && plans[1].cps == plans[2].cps &&
+                       plans[1].pieces == plans[2].pieces;
+    for (int i = 0; i < 3; ++i) {
+        const Walk& w = walks[i];
+        const SegPlan& pl = *wplans[i];
+        const bool tr = (i == 1 && share) || (i == 2 && dq_shares);
+        void* ws = (i == 2 && dq_shares) ? const_cast<void*>(fwd_ws) : workspace;  // only read when tr
+        const hipError_t e =
+            pl.path == FwdPath::kSegment
+                ? launch_segment_path(pl, w.a, w.b, w.c, w.o, none, ws, log2g, 0.f, B, H, T, chunk, w.wk,
+                                      w.wv, false, st, w.rev, tr)
+                : launch_slice_path(pl, w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, w.wk, w.wv,
+                                    false, false, st, w.rev);
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    }
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -570,76 +669,16 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
 int retention_bwd(const void* q, const void* k, const void* v, const float* gamma, int chunk, const void* dout,
                   void* dq, void* dk, void* dv, int B, int H, int T, int d_k, int d_v, int dtype, void* workspace,
                   size_t ws_bytes, void* stream) {
-    const char* fn = "retention_bwd";
-    if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
-    const int esz = dtype_size(dtype);
-    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
-    if (chunk != 64 && chunk != 128) return fail(RET_ERR_CHUNK, "%s: chunk must be 64 or 128 (got %d)", fn, chunk);
-    if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
-        return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)", fn, ret::kMaxHeads, B,
-                    H, T);
-    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128))
-        return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, d_k, d_v);
-    size_t nqk = esz, nv = esz;
-    if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, d_k) ||
-        !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, d_v))
-        return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
-    if (nqk > 0 && (!q || !k || !v || !dout || !dq || !dk || !dv))
-        return fail(RET_ERR_NULL, "%s: q, k, v, dout, dq, dk and dv must be non-NULL", fn);
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
-        !aligned16(dv))
-        return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
-    float log2g[ret::kMaxHeads] = {};
-    int rc = check_gamma(fn, gamma, H, log2g);
-    if (rc) return rc;
-    const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv), rdo = range("dout", dout, nv);
-    const Range rdq = range("dq", dq, nqk), rdk = range("dk", dk, nqk), rdv = range("dv", dv, nv);
-    for (const Range& o : {rdq, rdk, rdv}) {
-        for (const Range& in : {rq, rk, rv, rdo})
-            if (overlap(o, in)) return fail(RET_ERR_ALIAS, "%s: %s overlaps %s", fn, o.name, in.name);
-    }
-    if (overlap(rdq, rdk) || overlap(rdq, rdv) || overlap(rdk, rdv))
-        return fail(RET_ERR_ALIAS, "%s: the gradient outputs overlap", fn);
-    if (B == 0) return ok();
-    const long long bh = static_cast<long long>(B) * H;
-    SegPlan plans[3];
-    size_t need = 0;
-    if (!plan_bwd(bh, T, chunk, d_k, d_v, dtype, plans, &need))
-        return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
-    SegPlan wplan;
-    wplan.ws_bytes = need;
-    rc = check_workspace(fn, wplan, workspace, ws_bytes, {rq, rk, rv, rdo, rdq, rdk, rdv});
-    if (rc) return rc;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const FwdState none;
-    // (query input, key input, value input, output, key width, value width, reversed)
-    struct Walk {
-        const void *a, *b, *c;
-        void* o;
-        int wk, wv;
-        bool rev;
-    };
-    // dv first: its segment states sum q_s dout_s^T, the transpose of what the dk walk needs
-    // (dout_s q_s^T over the same reversed segments), so on the segment path the dk walk reads
-    // them transposed instead of running its own state pass
-    const Walk walks[3] = {{k, q, dout, dv, d_k, d_v, true}, {v, dout, q, dk, d_v, d_k, true},
-                           {dout, v, k, dq, d_v, d_k, false}};
-    const SegPlan* wplans[3] = {&plans[2], &plans[1], &plans[0]};
-    const bool share = plans[1].path == FwdPath::kSegment && plans[2].path == FwdPath::kSegment &&
-                       plans[1].G == plans[2].G && plans[1].cps == plans[2].cps &&
-                       plans[1].pieces == plans[2].pieces;
-    for (int i = 0; i < 3; ++i) {
-        const Walk& w = walks[i];
-        const SegPlan& pl = *wplans[i];
-        const hipError_t e =
-            pl.path == FwdPath::kSegment
-                ? launch_segment_path(pl, w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, chunk, w.wk,
-                                      w.wv, false, st, w.rev, i == 1 && share)
-                : launch_slice_path(pl, w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, w.wk, w.wv,
-                                    false, false, st, w.rev);
-        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-    }
-    return ok();
+    return bwd_impl("retention_bwd", q, k, v, gamma, chunk, dout, nullptr, 0, false, dq, dk, dv, B, H, T, d_k, d_v,
+                    dtype, workspace, ws_bytes, stream);
+}
+
+int retention_bwd_from_fwd(const void* q, const void* k, const void* v, const float* gamma, int chunk,
+                           const void* dout, const void* fwd_workspace, size_t fwd_ws_bytes, void* dq, void* dk,
+                           void* dv, int B, int H, int T, int d_k, int d_v, int dtype, void* workspace,
+                           size_t ws_bytes, void* stream) {
+    return bwd_impl("retention_bwd_from_fwd", q, k, v, gamma, chunk, dout, fwd_workspace, fwd_ws_bytes, true, dq, dk,
+                    dv, B, H, T, d_k, d_v, dtype, workspace, ws_bytes, stream);
 }
 
 int retention_decode_step(const void* q, const void* k, const void* v, const float* gamma,

@@ -69,9 +69,9 @@ struct SegArgs {
     int pieces;          // state-kernel workgroups per segment (divides scps)
     float eps;           // linear attention only
     float gn_eps;        // GroupNorm epsilon (normalised retention with GroupNorm only)
-    int ws_tr;           // time-reversed retention only: ws already holds the segment states of the
-                         // walk with key and value roles swapped (shape dv x dk, same segments); the
-                         // state pass is skipped and the walk reads them transposed
+    int ws_tr;           // retention only: ws already holds the segment states of a walk over the same
+                         // segments with key and value roles swapped (shape dv x dk); the state pass
+                         // is skipped and the walk reads them transposed (ws is then only read)
     float log2g[kMaxHeads];
 };
 

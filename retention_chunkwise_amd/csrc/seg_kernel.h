@@ -480,7 +480,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                 const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
                                          lpiece * static_cast<float>(a.pieces - 1 - pc)));
                 const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
-                if (REV && !ZN && a.ws_tr) {
+                if (!ZN && a.ws_tr) {
                     // S[16m + 4g + r][16n + l16] is element l16 % 4 of lane 16 (l16 / 4) + 4g + r in
                     // tile (n, m) of the transposed state
 #pragma unroll
@@ -970,7 +970,7 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     const long long bh = static_cast<long long>(a.B) * a.H;
     if (bh <= 0) return hipSuccess;
     if (bh * a.G > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (a.G > 1 && !(REV && a.ws_tr)) {
+    if (a.G > 1 && !a.ws_tr) {
         SegArgs sa = a;
         sa.scps = a.cps * (C / kStateBlock);
         // the state kernel is the same for both normalised retention modes

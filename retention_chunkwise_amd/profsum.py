@@ -51,6 +51,13 @@ WORKLOADS = {
                     (SEG + "state_kernel<128, 128, 0, false>", 1),
                     (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
         "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
+    "bwd_from_fwd_ret_fwd_long_bf16": {
+        "what": "retention_bwd_from_fwd on the long workload: as retention_bwd, but the dq walk reads the "
+                "forward's segment states and runs no state pass",
+        "kernels": [(SEG + "state_kernel<128, 128, 0, true>", 1),
+                    (SEG + "walk_kernel<128, 128, 128, 0, true>", 2),
+                    (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
+        "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
     "fwd_normalized_ret_fwd_long_bf16": {
         "what": "retention_fwd_normalized (row-sum floor + GroupNorm) on the long workload",
         "kernels": [(SEG + "state_kernel<128, 128, 2, false>", 1),
@@ -149,6 +156,8 @@ def traffic(fetch_csv: str, write_csv: str) -> None:
 
 BENCH_LINES = [("retention forward (long bf16, state + walk kernels)", ("roofline", "kernel_ms"), 1e6, "ns per call"),
                ("backward (dq, dk, dv) of the long forward", ("backward", "ms_per_call"), 1e6, "ns per call"),
+               ("backward given the forward's segment states", ("backward_from_fwd", "ms_per_call"), 1e6,
+                "ns per call"),
                ("forward with row-sum floor + GroupNorm (long bf16)", ("fwd_normalized", "ms_per_call"), 1e6,
                 "ns per call"),
                ("decode step", ("decode", "us_per_step"), 1e3, "ns per step"),

@@ -381,3 +381,33 @@ def test_gla_workspace():
     assert n > 0 and n % ((64 * 64 + 64) * 4 * 32) == 0
     big = 1 << 28  # 256 MiB apart: no overlap between the fake tensors
     assert _gla(lib, B=4, H=8, T=2048, q=big, k=2 * big, v=3 * big, lg=4 * big, out=5 * big) == -9
+
+
+# ------------------------------------------------- retention_bwd_from_fwd validation
+M64 = 0x4000000  # 64 MiB: buffers this far apart do not overlap at the sizes below
+
+
+def _bwd_ff(lib, **kw):
+    a = dict(q=M64, k=2 * M64, v=3 * M64, gamma=_gam([0.9, 0.9]), chunk=128, do=4 * M64, fws=None, nfws=0,
+             dq=5 * M64, dk=6 * M64, dv=7 * M64, B=1, H=2, T=65536, d_k=128, d_v=128, dtype=rc.RET_BF16,
+             ws=8 * M64, nws=0)
+    a.update(kw)
+    return lib.retention_bwd_from_fwd(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["do"], a["fws"], a["nfws"],
+                                      a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["T"], a["d_k"], a["d_v"],
+                                      a["dtype"], a["ws"], a["nws"], None)
+
+
+def test_bwd_from_fwd_checks_the_forward_workspace():
+    lib = _lib()
+    need_b = lib.retention_bwd_workspace_bytes(1, 2, 65536, 128, 128, 128, rc.RET_BF16)
+    need_f = lib.retention_fwd_workspace_bytes(1, 2, 65536, 128, 128, 128, rc.RET_BF16)
+    assert need_b > 0 and need_f > 0 and need_b < M64 and need_f < M64
+    kw = dict(nws=need_b)
+    assert _bwd_ff(lib, **kw) == -9                                          # forward needed one: NULL
+    assert _bwd_ff(lib, fws=9 * M64, nfws=need_f - 16, **kw) == -9           # too small
+    assert _bwd_ff(lib, fws=9 * M64 + 8, nfws=need_f, **kw) == -7            # misaligned
+    assert _bwd_ff(lib, fws=5 * M64, nfws=need_f, **kw) == -8                # overlaps dq
+    assert _bwd_ff(lib, fws=8 * M64, nfws=need_f, **kw) == -8                # is the backward's workspace
+    assert _bwd_ff(lib, fws=9 * M64, nfws=need_f, nws=need_b - 16) == -9     # the backward's own is short
+    assert _bwd_ff(lib, fws=9 * M64, nfws=need_f, dq=M64, **kw) == -8        # dq overlaps q, as retention_bwd
+    assert _bwd_ff(lib, B=0, fws=9 * M64, nfws=need_f, **kw) == 0            # empty batch: nothing to do
