@@ -66,6 +66,17 @@ def measured_traffic(name: str, paths) -> dict | None:
     return d
 
 
+def measured_mfma(name: str, paths) -> dict | None:
+    """Matrix-core counters of a workload from a committed rocprofv3 summary
+    (None when absent or taken with other kernel sources)."""
+    p = os.path.join(PROFILES, f"mfma_{name}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    return d if d.get("source_sha") == sources_sha(paths) else None
+
+
 def time_launches(fn, steps: int, warmup: int):
     """Run fn warmup + steps times; return (avg ms per launch from HIP events,
     wall ms per step).  Events are recorded on torch's current stream, which
@@ -159,6 +170,7 @@ def main():
     tflops = fl_dense / (step_ms * 1e-3) / 1e12
     achieved_gbs = by / (kern_ms * 1e-3) / 1e9
     traffic = measured_traffic("fwd_ret_fwd_long_bf16", FWD_SOURCES)
+    mfma = measured_mfma("fwd_ret_fwd_long_bf16", FWD_SOURCES)
 
     res = {
         "metric": METRIC,
@@ -191,6 +203,13 @@ def main():
             "traffic": (traffic["bytes_per_launch"] if traffic else None),
             "algorithmic_bytes_per_launch": by,
             "kernel_ms": kern_ms,
+            # matrix-core counters of the two kernels (rocprofv3 --pmc, committed summary): MFMA busy
+            # share of the SIMDs, and the FLOPs the matrix cores issued per call at this call's time
+            "mfma_counters": ({"walk_mfma_busy": mfma["walk"]["mfma_busy"],
+                               "state_mfma_busy": mfma["state"]["mfma_busy"],
+                               "issued_tflops": mfma["issued_bf16_flops_per_call"] / (kern_ms * 1e-3) / 1e12,
+                               "issued_peak_frac": mfma["issued_bf16_flops_per_call"] / (kern_ms * 1e-3) / 1e12
+                               / M.PEAK_TFLOPS["bf16"]} if mfma else None),
         },
         "pages_flop_comparison": {
             "T": 65536, "d": 128,

@@ -6,6 +6,9 @@
     python -m retention_chunkwise_amd.profsum traffic FETCH_CSV WRITE_CSV
         HBM bytes per call of each bench workload from two counter runs
         (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) -> profiles/hbm_traffic_*.json
+    python -m retention_chunkwise_amd.profsum mfma MFMA_CSV STATS_CSV
+        matrix-core counters per kernel (issued MFMA FLOPs, MFMA busy share)
+        with the kernel-trace durations -> profiles/mfma_bench_workloads.md
 
 Counter scaling: each counter is divided by what it reads, per byte, for the
 plain 1 GiB device copies that `bench.py --calibrate-copy` runs in the same
@@ -154,6 +157,100 @@ def traffic(fetch_csv: str, write_csv: str) -> None:
         print(f"{name}: {(fb + wb) / 1e9:.3f} GB per call ({(fb + wb) / spec['algorithmic']:.2f}x algorithmic)")
 
 
+MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"
+MFMA_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
+            "-d $REPO/gpurun_out/pmc_mfma -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+            "--decode-steps 20 --no-cpu-baseline")
+SIMDS = 256 * 4        # MI355X: 256 CUs, 4 SIMDs each
+XCDS = 8               # GRBM_GUI_ACTIVE arrives summed over the XCDs; one XCD's count is the busy time
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix-core peaks
+
+
+def _per_dispatch_counters(path: str):
+    """{dispatch: (kernel, {counter: value})}; every counter summed over the
+    rows of its dispatch."""
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            name, ctrs = out.setdefault(d, (_strip_args(r["Kernel_Name"]), {}))
+            c, v = r["Counter_Name"], float(r["Counter_Value"])
+            ctrs[c] = ctrs.get(c, 0.0) + v
+    return out
+
+
+def mfma(mfma_csv: str, stats_csv: str) -> None:
+    per = _per_dispatch_counters(mfma_csv)
+    dur = {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            dur[_strip_args(r["Name"])] = float(r["AverageNs"])
+    agg = collections.OrderedDict()
+    for d in sorted(per):
+        name, c = per[d]
+        if not name.startswith("void ret::"):
+            continue
+        a = agg.setdefault(name, collections.defaultdict(float))
+        a["n"] += 1
+        for k, v in c.items():
+            a[k] += v
+    out = ["# Matrix-core counters — bench workloads on one MI355X", "",
+           "Command (repository root as $REPO):", "", "    " + MFMA_CMD, "",
+           "Issued FLOPs are the MFMA operation counters times 512 (the counters count 512-FLOP units), "
+           "averaged per dispatch; they include the masked and zero-padded parts of tiles and the recomputed "
+           "products, so they exceed the algorithmic FLOPs. MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES summed over "
+           f"the {SIMDS} SIMDs divided by {SIMDS} x the busy cycles of one XCD (rocprofv3's MfmaUtil). "
+           f"GRBM_GUI_ACTIVE arrives summed over the {XCDS} XCDs: divided by {XCDS} it matches the kernel's duration "
+           "at a 2.0 GHz clock (372,078 cycles for the 185.8 µs state kernel). The issued rate "
+           "divides the issued FLOPs by the kernel's average duration from profiles/kernel_stats_bench_workloads.md "
+           "and compares it with the dense peak of its own dtype (bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s).", "",
+           "| kernel | dispatches | issued bf16 GFLOP | issued fp32 GFLOP | MFMA busy | avg µs | issued TFLOP/s | % of dtype peak |",
+           "|---|---|---|---|---|---|---|---|"]
+    for name, a in agg.items():
+        n = a["n"]
+        fb = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / n
+        ff = a.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512 / n
+        busy = a.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / n
+        act = a.get("GRBM_GUI_ACTIVE", 0.0) / n / XCDS
+        util = 100.0 * busy / (act * SIMDS) if act > 0 else float("nan")
+        us = dur.get(name, float("nan")) / 1e3
+        dt = "bf16" if fb >= ff else "f32"
+        fl = fb if dt == "bf16" else ff
+        rate = fl / (us * 1e-6) / 1e12 if us == us and us > 0 else float("nan")
+        out.append(f"| `{name.replace('void ret::', '')}` | {n:.0f} | {fb / 1e9:,.2f} | {ff / 1e9:,.2f} | "
+                   f"{util:.1f} % | {us:,.1f} | {rate:,.1f} ({dt}) | {100 * rate / PEAK_TFLOPS[dt]:.1f} % |")
+    from retention_chunkwise_amd import metrics as M
+
+    b = _bench()
+    f_dense = M.fwd_flops(1, 32, 65536, 128, 128, 128)
+    f_causal = M.fwd_flops(1, 32, 65536, 128, 128, 128, causal=True)
+    walk = agg.get("void ret::seg::seg_walk_kernel<128, 128, 128, 0, false>")
+    state = agg.get("void ret::seg::seg_state_kernel<128, 128, 0, false>")
+    if walk and state:
+        def one(a):
+            n = a["n"]
+            return {"issued_bf16_flops": a["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / n,
+                    "mfma_busy": a["SQ_VALU_MFMA_BUSY_CYCLES"] / n / (a["GRBM_GUI_ACTIVE"] / n / XCDS * SIMDS)}
+        w1, s1 = one(walk), one(state)
+        issued = w1["issued_bf16_flops"] + s1["issued_bf16_flops"]
+        out += ["", f"One long forward ([1, 32, 65536, 128] bf16, chunk 128) issues {issued / 1e9:.1f} GFLOP on the "
+                f"matrix cores: the walk {w1['issued_bf16_flops'] / 1e9:.1f} (causal tiles only) and the state kernel "
+                f"{s1['issued_bf16_flops'] / 1e9:.1f} (the segment sums, computed a second time by the segment "
+                f"decomposition). The algorithmic count is {f_dense / 1e9:.1f} GFLOP dense (F_dense, the headline "
+                f"figure) and {f_causal / 1e9:.1f} GFLOP causal minimum."]
+        d = {"workload": "retention_fwd, [1, 32, 65536, 128] bf16, chunk 128", "walk": w1, "state": s1,
+             "issued_bf16_flops_per_call": issued, "algorithmic_flops_dense": f_dense,
+             "algorithmic_flops_causal": f_causal, "source_sha": b.sources_sha(b.FWD_SOURCES),
+             "sources": b.FWD_SOURCES, "command": MFMA_CMD,
+             "note": "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x one XCD's GRBM_GUI_ACTIVE)"}
+        with open(os.path.join(PROFILES, "mfma_fwd_ret_fwd_long_bf16.json"), "w") as f:
+            json.dump(d, f, indent=1)
+            f.write("\n")
+    with open(os.path.join(PROFILES, "mfma_bench_workloads.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 BENCH_LINES = [("retention forward (long bf16, state + walk kernels)", ("roofline", "kernel_ms"), 1e6, "ns per call"),
                ("backward (dq, dk, dv) of the long forward", ("backward", "ms_per_call"), 1e6, "ns per call"),
                ("backward given the forward's segment states", ("backward_from_fwd", "ms_per_call"), 1e6,
@@ -201,5 +298,7 @@ if __name__ == "__main__":
         stats(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 4 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 4 and sys.argv[1] == "mfma":
+        mfma(sys.argv[2], sys.argv[3])
     else:
         raise SystemExit(__doc__)
