@@ -142,6 +142,14 @@ bool plan_slices(long long bh, int T, int chunk, int dk, int dv, bool linattn, b
         if (want > 0 && want < p->nt && (dv / 16) % want == 0 && ret::walk_variant_fits(bf16, linattn, chunk, dk, want))
             p->nt = want;
         if (!forced) p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, 256, 2, 16, &p->cps);
+        // the segment-state kernel addresses one segment's K and V with 32-bit byte offsets:
+        // very long sequences take more segments, until a segment's K and V each stay under 2 GiB
+        const long long row = static_cast<long long>(dk > dv ? dk : dv) * (bf16 ? 2 : 4);
+        while (p->G > 1 && static_cast<long long>(p->cps) * chunk * row >= (1LL << 31)) {
+            const int g = p->G + 1;
+            p->cps = (nch + g - 1) / g;
+            p->G = (nch + p->cps - 1) / p->cps;
+        }
     } else {
         p->nt = ret::choose_walk_nt(bh, dv, 256, bf16, chunk, dk);
         p->G = 1;

@@ -411,3 +411,22 @@ def test_bwd_from_fwd_checks_the_forward_workspace():
     assert _bwd_ff(lib, fws=9 * M64, nfws=need_f, nws=need_b - 16) == -9     # the backward's own is short
     assert _bwd_ff(lib, fws=9 * M64, nfws=need_f, dq=M64, **kw) == -8        # dq overlaps q, as retention_bwd
     assert _bwd_ff(lib, B=0, fws=9 * M64, nfws=need_f, **kw) == 0            # empty batch: nothing to do
+
+
+def test_very_long_fp32_segments_stay_under_2_gib():
+    """The fp32 segment-state kernel uses 32-bit offsets within a segment: a
+    64M-token head at d = 128 takes more segments so that each segment's K and
+    V stay under 2 GiB (the plan shows in the workspace: G - 1 state slots)."""
+    lib = _lib()
+    T, d, chunk = 1 << 26, 128, 64
+    n = lib.retention_fwd_workspace_bytes(1, 1, T, d, d, chunk, rc.RET_F32)
+    slots = n // (d * d * 4)
+    assert n == slots * d * d * 4 and slots >= 1
+    G = slots + 1
+    nch = T // chunk
+    cps = -(-nch // G)
+    assert -(-nch // cps) == G
+    assert cps * chunk * d * 4 < 2 ** 31
+    # a shorter head keeps the usual plan
+    m = lib.retention_fwd_workspace_bytes(1, 1, 1 << 20, d, d, chunk, rc.RET_F32)
+    assert 0 < m <= 15 * d * d * 4
