@@ -237,3 +237,37 @@ def test_linattn_constant_values_give_constant_outputs():
     v = u.expand(1, 2, 300, w.dv).contiguous()
     out = rc.linear_attn_fwd(_dev(inp["q"]), _dev(inp["k"]), _dev(v), eps=0.0).cpu().numpy()
     _report("constant values", oracle.rel_frobenius(out, v.numpy()), TOL["f32"])
+
+
+# ------------------------------------------------------------- the largest head count
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_max_heads_each_with_its_own_gamma(dtype):
+    """256 heads, the most one call takes, each with its own decay
+    1 - 2^(-5 - 4h/255): the forward (value-slice path for fp32, segment path
+    for bf16, ragged tail), decode steps from the forward's final state, and the
+    gradients.  A head reading another head's decay would fail here."""
+    H = 256
+    w, inp = _inputs("ret_fwd_long_bf16", seed=9, B=1, H=H, T=200, dk=64, dv=64, chunk=64, dtype=dtype)
+    assert len(set(inp["gamma"].tolist())) == H
+    out, fs = _run_fwd(inp, 64)
+    ref, ref_s = oracle.retention_recurrent(inp["q"], inp["k"], inp["v"], inp["gamma"], nthreads=8)
+    _report(f"256 heads {dtype} out", oracle.rel_frobenius(out, ref), TOL[dtype])
+    _report(f"256 heads {dtype} final_state", oracle.rel_frobenius(fs, ref_s), TOL[dtype])
+
+    wd, dinp = _inputs("decode_bf16", seed=10, B=1, H=H, dk=64, dv=64, dtype=dtype)
+    state = torch.from_numpy(fs).cuda()
+    q, k, v = (_dev(dinp[n]) for n in ("q", "k", "v"))
+    for _ in range(2):
+        o = rc.retention_decode_step(q, k, v, inp["gamma"], state)
+    torch.cuda.synchronize()
+    ref_o, ref_st = oracle.decode_steps(dinp["q"], dinp["k"], dinp["v"], inp["gamma"], fs, nsteps=2)
+    _report(f"256 heads {dtype} decode out", oracle.rel_frobenius(o.float().cpu().numpy(), ref_o), TOL[dtype])
+    _report(f"256 heads {dtype} decode state", oracle.rel_frobenius(state.cpu().numpy(), ref_st), 1e-4)
+
+    g = torch.Generator().manual_seed(11)
+    do = torch.randn((1, H, 200, 64), generator=g).to(wl.torch_dtype(dtype))
+    dq, dk, dv = rc.retention_bwd(*(_dev(inp[n]) for n in ("q", "k", "v")), inp["gamma"], do.cuda(), chunk=64)
+    torch.cuda.synchronize()
+    ref_g = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], do, nthreads=8)
+    for name, x, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref_g):
+        _report(f"256 heads {dtype} {name}", oracle.rel_frobenius(x.float().cpu().numpy(), r), TOL[dtype])
