@@ -411,7 +411,7 @@ def main():
         res["gla_f32"] = {
             "workload": "gated linear attention, fp32 [4, 8, 2048, 64], log-gates logsigmoid(N(2, 1))",
             "ms_per_call": g_kern, "tokens_per_s": wf.B * wf.T / (g_kern * 1e-3), "tflops": g_tf,
-            "roofline": {"kernel": "gla_fwd: gla_kernel<dk=64>", "bound": "mfma", "achieved": g_tf,
+            "roofline": {"kernel": "gla_fwd: gla_kernel<dk=64, 32-column slices>", "bound": "mfma", "achieved": g_tf,
                          "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": g_tf / M.PEAK_TFLOPS["f32"],
                          "traffic": (g_tr["bytes_per_launch"] if g_tr else None),
                          # q, k, v, log-gates read, out and final state written

@@ -306,9 +306,10 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
 bool plan_gla(long long bh, int T, int dk, int dv, SegPlan* p) {
     p->chunk = 64;
     p->pieces = 1;
-    p->nt = ret::gla_choose_nt(bh, dv);
+    p->nt = ret::gla_choose_nt(bh, dk, dv);
     const int nch = (T + 63) / 64;
-    if (!forced_segments(nch, p)) p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, 256, 2, 16, &p->cps);
+    if (!forced_segments(nch, p))
+        p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, ret::gla_target_groups(dk, p->nt), 2, 16, &p->cps);
     return set_ws_bytes(bh, dk, dv, true, p);
 }
 

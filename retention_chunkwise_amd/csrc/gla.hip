@@ -420,9 +420,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     }
 }
 
-// SO: the state-only pass over segments 0 .. G-2.
+// SO: the state-only pass over segments 0 .. G-2.  The 32-column slices at
+// dk = 64 are held to 256 registers (they need 254), so that two workgroups
+// share a CU and hide each other's latencies; the other variants use more.
+template <int DK, int NT>
+constexpr int gla_min_blocks() { return (DK == 64 && NT == 2) ? 2 : 1; }
+
 template <int DK, int NT, bool SO>
-__global__ void __launch_bounds__(kThreads, 1) gla_kernel(const GlaArgs a) {
+__global__ void __launch_bounds__(kThreads, (gla_min_blocks<DK, NT>())) gla_kernel(const GlaArgs a) {
     __shared__ Smem<DK, NT> sm;
     const int nseg = SO ? a.G - 1 : a.G;
     const int bhs = blockIdx.x / a.nslices;
@@ -461,11 +466,16 @@ hipError_t launch_t(const GlaArgs& a, hipStream_t stream) {
 }  // namespace
 }  // namespace gla
 
-int gla_choose_nt(long long bh, int dv) {
-    // the widest slice that fits (the segments supply the parallelism); 64 columns at most
+int gla_choose_nt(long long bh, int dk, int dv) {
+    // dk = dv = 64: 32-column slices, two workgroups per CU (measured on [4, 8, 2048, 64]: 65 us against
+    // 69 us for 64-column slices at one per CU, bit-identical results); otherwise the widest slice
+    // that fits, 64 columns at most (the segments supply the parallelism)
     (void)bh;
+    if (dk == 64 && dv == 64) return 2;
     return dv >= 64 ? 4 : dv / 16;
 }
+
+int gla_target_groups(int dk, int nt) { return (dk == 64 && nt == 2) ? 512 : 256; }
 
 hipError_t launch_gla(const GlaArgs& a, int dk, int nt, hipStream_t stream) {
     if (dk == 64 && nt == 1) return gla::launch_t<64, 1>(a, stream);

@@ -126,7 +126,9 @@ int choose_segments(long long bh, int nch, int target_groups, int min_cps, int m
 int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk, int dk);
 
 // Gated linear attention: value-slice width (in 16-column tiles) and launcher.
-int gla_choose_nt(long long bh, int dv);
+int gla_choose_nt(long long bh, int dk, int dv);
+// Workgroups the GLA walk aims for: two per CU where two fit.
+int gla_target_groups(int dk, int nt);
 hipError_t launch_gla(const GlaArgs& a, int dk, int nt, hipStream_t stream);
 
 // Widest value slice of the segmented walk whose workgroup fits in LDS (the

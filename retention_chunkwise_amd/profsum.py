@@ -86,8 +86,8 @@ WORKLOADS = {
         "algorithmic": 4 * 8 * 2048 * 64 * 4 * 4 + 4 * 8 * 64 * 64 * 4, "sources": "F32_SOURCES"},
     "gla_gla_mh_f32": {
         "what": "gla_fwd fp32 [4, 8, 2048, 64], final state",
-        "kernels": [("::gla_kernel<64, 4, true>", 1),
-                    ("::gla_kernel<64, 4, false>", 1)],
+        "kernels": [("::gla_kernel<64, 2, true>", 1),
+                    ("::gla_kernel<64, 2, false>", 1)],
         "algorithmic": 4 * 8 * 2048 * 64 * 4 * 5 + 4 * 8 * 64 * 64 * 4, "sources": "GLA_SOURCES"},
 }
 
