@@ -22,24 +22,24 @@
 //                     in registers and writes O; the last segment also writes
 //                     the final state.
 // Every workgroup covers the full value width, so Q K^T is computed once per
-// chunk (per half of the value width), and each workgroup streams its own
-// slice of the sequence.
+// chunk, and each workgroup streams its own slice of the sequence.
 //
-// Waves.  A workgroup has 8 waves (two per SIMD).  Wave w = P + 4 h owns
+// Waves.  A workgroup has 8 waves (two per SIMD) in two roles (see the
+// seg_walk_kernel notes below): waves 0-3 compute outputs, wave P owning
 // query tiles {P, C/16-1-P} (16 rows each; one tile when C = 64), which
-// balances the causal triangle, and value half h; its state tiles are dk
-// tiles {P*DK/64, ...} x the value tiles of half h.  P is a template
-// parameter (four code variants, each unrolled over its exact causal tile
-// set); h only shifts addresses.  All products run on
-// v_mfma_f32_16x16x32_bf16, transposed so that the Q K^T accumulators feed the
-// P V product from registers:
+// balances the causal triangle, over the whole value width; waves 4-7 carry
+// the fp32 state, wave 4 + P owning dk tiles {P*DK/64, ...} x every value
+// tile.  P is a template parameter (four code variants, each unrolled over its
+// exact causal tile set).  All products run on v_mfma_f32_16x16x32_bf16,
+// transposed so that the Q K^T accumulators feed the P V product from
+// registers:
 //   S^T   = K Q^T            A: K rows (LDS)           B: Q rows (registers)
 //   P^T   = S^T (.) D        decay factors per lane
 //   O^T   = xi (.) S_prev^T Q^T + V^T P^T
 //                            A: bf16 state copy / V^T (LDS transpose reads)
 //   S     = gamma^c S + (zeta (.) K)^T V
 //                            A: K^T (LDS transpose reads, scaled by zeta)
-//                            B: the V^T registers of the output product
+//                            B: V^T (LDS transpose reads)
 // K and V go HBM -> LDS by DMA into double-buffered swizzled tiles and Q goes
 // HBM -> registers of the wave that uses it, all issued one chunk ahead.  LDS
 // addresses are a per-lane offset computed once plus an immediate.
