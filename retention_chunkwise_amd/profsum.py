@@ -126,7 +126,7 @@ def _find(groups: dict[str, list[float]], key: str) -> list[float]:
     return hits[0]
 
 
-def traffic(fetch_csv: str, write_csv: str) -> None:
+def traffic(fetch_csv: str, write_csv: str, out_dir: str = PROFILES) -> None:
     b = _bench()
     fetch, write = _per_dispatch(fetch_csv), _per_dispatch(write_csv)
     cf, cw = _find(fetch, COPY_KERNEL), _find(write, COPY_KERNEL)
@@ -151,7 +151,7 @@ def traffic(fetch_csv: str, write_csv: str) -> None:
                              f"WRITE_SIZE {cw_kib:.1f} KiB"),
              "commands": [PMC_CMD.format(ctr="FETCH_SIZE", tag="fetch"),
                           PMC_CMD.format(ctr="WRITE_SIZE", tag="write")]}
-        with open(os.path.join(PROFILES, f"hbm_traffic_{name}.json"), "w") as f:
+        with open(os.path.join(out_dir, f"hbm_traffic_{name}.json"), "w") as f:
             json.dump(d, f, indent=1)
             f.write("\n")
         print(f"{name}: {(fb + wb) / 1e9:.3f} GB per call ({(fb + wb) / spec['algorithmic']:.2f}x algorithmic)")
@@ -179,7 +179,7 @@ def _per_dispatch_counters(path: str):
     return out
 
 
-def mfma(mfma_csv: str, stats_csv: str) -> None:
+def mfma(mfma_csv: str, stats_csv: str, out_dir: str = PROFILES) -> None:
     per = _per_dispatch_counters(mfma_csv)
     dur = {}
     with open(stats_csv) as f:
@@ -243,10 +243,10 @@ def mfma(mfma_csv: str, stats_csv: str) -> None:
              "algorithmic_flops_causal": f_causal, "source_sha": b.sources_sha(b.FWD_SOURCES),
              "sources": b.FWD_SOURCES, "command": MFMA_CMD,
              "note": "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x one XCD's GRBM_GUI_ACTIVE)"}
-        with open(os.path.join(PROFILES, "mfma_fwd_ret_fwd_long_bf16.json"), "w") as f:
+        with open(os.path.join(out_dir, "mfma_fwd_ret_fwd_long_bf16.json"), "w") as f:
             json.dump(d, f, indent=1)
             f.write("\n")
-    with open(os.path.join(PROFILES, "mfma_bench_workloads.md"), "w") as f:
+    with open(os.path.join(out_dir, "mfma_bench_workloads.md"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
@@ -264,7 +264,7 @@ BENCH_LINES = [("retention forward (long bf16, state + walk kernels)", ("rooflin
                ("gated linear attention fp32 [4, 8, 2048, 64]", ("gla_f32", "ms_per_call"), 1e6, "ns per call")]
 
 
-def stats(stats_csv: str, bench_log: str) -> None:
+def stats(stats_csv: str, bench_log: str, out_dir: str = PROFILES) -> None:
     b = _bench()
     rows = []
     with open(stats_csv) as f:
@@ -288,7 +288,7 @@ def stats(stats_csv: str, bench_log: str) -> None:
     out += ["", "Source hashes: segment kernels " + b.sources_sha(b.FWD_SOURCES) + ", decode "
             + b.sources_sha(b.DECODE_SOURCES) + ", fp32 walk " + b.sources_sha(b.F32_SOURCES) + ", GLA "
             + b.sources_sha(b.GLA_SOURCES) + "."]
-    with open(os.path.join(PROFILES, "kernel_stats_bench_workloads.md"), "w") as f:
+    with open(os.path.join(out_dir, "kernel_stats_bench_workloads.md"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
