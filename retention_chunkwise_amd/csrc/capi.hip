@@ -265,9 +265,11 @@ bool plan_bwd(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan
 // plan and workspace.
 hipError_t launch_slice_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
                              const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
-                             int T, int dk, int dv, bool bf16, bool linattn, hipStream_t st, bool reverse = false) {
+                             int T, int dk, int dv, bool bf16, bool linattn, hipStream_t st, bool reverse = false,
+                             bool ws_transposed = false) {
     ret::WalkArgs a{};
     a.reverse = reverse ? 1 : 0;
+    a.ws_tr = ws_transposed ? 1 : 0;
     a.q = q; a.k = k; a.v = v; a.out = out;
     a.final_state = fst.final_state; a.init_state = fst.init_state;
     a.init_z = fst.init_z; a.final_z = fst.final_z;
@@ -572,8 +574,9 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
                 if (overlap(rf, o)) return fail(RET_ERR_ALIAS, "%s: fwd_workspace overlaps %s", fn, o.name);
             // the forward's plan must be the one the dq walk uses (it is, unless the tuning
             // knobs changed between the calls; then the dq walk runs its own state pass)
-            dq_shares = fplan.path == FwdPath::kSegment && plans[0].path == FwdPath::kSegment &&
-                        fplan.G == plans[0].G && fplan.cps == plans[0].cps && fplan.pieces == plans[0].pieces;
+            dq_shares = fplan.path == plans[0].path && fplan.G == plans[0].G && fplan.cps == plans[0].cps &&
+                        fplan.chunk == plans[0].chunk &&
+                        (fplan.path == FwdPath::kSlice || fplan.pieces == plans[0].pieces);
         }
     }
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -591,9 +594,9 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
     const Walk walks[3] = {{k, q, dout, dv, d_k, d_v, true}, {v, dout, q, dk, d_v, d_k, true},
                            {dout, v, k, dq, d_v, d_k, false}};
     const SegPlan* wplans[3] = {&plans[2], &plans[1], &plans[0]};
-    const bool share = plans[1].path == FwdPath::kSegment && plans[2].path == FwdPath::kSegment &&
-                       plans[1].G == plans[2].G && plans[1].cps == plans[2].cps &&
-                       plans[1].pieces == plans[2].pieces;
+    const bool share = plans[1].path == plans[2].path && plans[1].G == plans[2].G && plans[1].cps == plans[2].cps &&
+                       plans[1].chunk == plans[2].chunk &&
+                       (plans[1].path == FwdPath::kSlice || plans[1].pieces == plans[2].pieces);
     for (int i = 0; i < 3; ++i) {
         const Walk& w = walks[i];
         const SegPlan& pl = *wplans[i];
@@ -603,8 +606,8 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
             pl.path == FwdPath::kSegment
                 ? launch_segment_path(pl, w.a, w.b, w.c, w.o, none, ws, log2g, 0.f, B, H, T, chunk, w.wk,
                                       w.wv, false, st, w.rev, tr)
-                : launch_slice_path(pl, w.a, w.b, w.c, w.o, none, workspace, log2g, 0.f, B, H, T, w.wk, w.wv,
-                                    false, false, st, w.rev);
+                : launch_slice_path(pl, w.a, w.b, w.c, w.o, none, ws, log2g, 0.f, B, H, T, w.wk, w.wv,
+                                    false, false, st, w.rev, tr);
         if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     }
     return ok();

@@ -31,6 +31,9 @@ struct WalkArgs {
     int cps;             // chunks per segment
     int seg_len;         // tokens per full segment (set by the launcher: cps * chunk)
     float* ws;           // [B*H][G-1][dk*dv (+ dk)] fp32 segment states, row-major; unused when G == 1
+    int ws_tr;           // retention only: ws already holds the segment states of a walk over the same
+                         // segments with key and value roles swapped (dv x dk, row-major); the state
+                         // pass is skipped and the walk reads them transposed (ws is then only read)
     float eps;           // linear attention only
     float log2g[kMaxHeads];
 };

@@ -207,6 +207,19 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
         const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + nbase;
         for (int j = 0; j < seg; ++j) {
             const float wj = exp2f(lseg * static_cast<float>(seg - 1 - j));
+            if (!LIN && a.ws_tr) {
+                // S[i][nbase + c] is element (nbase + c) * DK + i of the transposed (DV x DK) state
+                const float* sj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + j) * slot;
+#pragma unroll
+                for (int m = 0; m < SPW; ++m) {
+                    const int qt = TS + m;
+                    const int nt = qt / KT, kt = qt % KT;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sacc[m][r] += wj * sj[static_cast<long long>(nbase + nt * 16 + 4 * g + r) * DK + kt * 16 + l16];
+                }
+                continue;
+            }
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
                 const int qt = TS + m;
@@ -913,7 +926,7 @@ hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
     WalkArgs args = a;
     args.xcd_remap = (groups % 8 == 0) ? 1 : 0;
     args.seg_len = a.cps * C;
-    if (a.G > 1) {
+    if (a.G > 1 && !a.ws_tr) {
         const long long sgroups = static_cast<long long>(a.B) * a.H * (a.G - 1);
         const int dv = a.dv;
 #define RET_SLICE_STATE(DV_)                                                                             \

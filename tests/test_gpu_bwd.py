@@ -160,17 +160,17 @@ def _run_from_fwd(inp, chunk, zero_states=False):
     return [t.float().cpu().numpy() for t in (dq, dk, dv)], n
 
 
-@pytest.mark.parametrize("G", [None, 3, 5])
+@pytest.mark.parametrize("dtype,G", [("bf16", None), ("bf16", 3), ("bf16", 5), ("f32", None), ("f32", 3)])
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 1000), (64, 128, 129), (128, 64, 700)])
-def test_bwd_from_fwd_small_full(G, chunk, dk, dv, T, monkeypatch):
-    w, inp = _inputs(57, "bf16", 2, 3, T, dk, dv, chunk)
+def test_bwd_from_fwd_small_full(dtype, G, chunk, dk, dv, T, monkeypatch):
+    w, inp = _inputs(57, dtype, 2, 3, T, dk, dv, chunk)
     _segments(monkeypatch, G)
-    tag = f"bwd_from_fwd G={G} C={chunk} dk={dk} dv={dv} T={T}"
+    tag = f"bwd_from_fwd {dtype} G={G} C={chunk} dk={dk} dv={dv} T={T}"
     print(f"[bwd] {tag}", flush=True)
     got, _ = _run_from_fwd(inp, chunk)
     ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"], nthreads=8)
-    _check(tag, got, ref, TOL["bf16"])
+    _check(tag, got, ref, TOL[dtype])
     # dk and dv take the same walks as retention_bwd; dq differs only in rounding
     plain = _run(inp, chunk)
     assert np.array_equal(got[1], plain[1]) and np.array_equal(got[2], plain[2]), tag
@@ -179,11 +179,13 @@ def test_bwd_from_fwd_small_full(G, chunk, dk, dv, T, monkeypatch):
     assert e <= 1e-2
 
 
-def test_bwd_from_fwd_reads_the_given_states(monkeypatch):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_from_fwd_reads_the_given_states(dtype, monkeypatch):
     """With the forward's states zeroed, dq loses every earlier segment's share
-    and dk, dv are unchanged: the dq walk reads the buffer it is given."""
+    and dk, dv are unchanged: the dq walk reads the buffer it is given (segment
+    path for bf16, value-slice path for fp32)."""
     _segments(monkeypatch, 4)
-    w, inp = _inputs(58, "bf16", 1, 2, 1024, 64, 64, 64)
+    w, inp = _inputs(58, dtype, 1, 2, 1024, 64, 64, 64)
     good, n = _run_from_fwd(inp, 64)
     assert n > 0
     bad, _ = _run_from_fwd(inp, 64, zero_states=True)
