@@ -115,10 +115,17 @@ def cpu_baseline_fwd(inp, w, target_s: float = 10.0):
             break
         Ts = min(w.T, max(Ts * 2, int(Ts * target_s / max(dt, 1e-3) * 0.9)))
     rate = w.B * Ts / dt  # tokens/s (all heads processed for each token)
+    # the same oracle on one thread, on a prefix sized to about 3 s
+    T1 = max(256, min(w.T, int(Ts * (3.0 / max(dt * cores, 1e-3)))))
+    t0 = time.perf_counter()
+    oracle.retention_recurrent(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], g, nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": rate, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"fp64 recurrent oracle, g++ -O2 + OpenMP over (b, h); first {Ts} of "
                       f"{w.T} tokens of all {w.B * w.H} heads ({dt:.1f} s)",
-            "seconds": dt}
+            "seconds": dt,
+            "single_thread": {"value": w.B * T1 / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"first {T1} tokens of all {w.B * w.H} heads ({dt1:.1f} s)"}}
 
 
 def main():
