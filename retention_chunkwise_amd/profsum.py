@@ -10,6 +10,9 @@
         matrix-core counters per kernel (issued MFMA FLOPs, MFMA busy share)
         with the kernel-trace durations -> profiles/mfma_bench_workloads.md
 
+In the recorded commands $REPO is the repository root and $OUT the directory
+the run writes its CSVs to.
+
 Counter scaling: each counter is divided by what it reads, per byte, for the
 plain 1 GiB device copies that `bench.py --calibrate-copy` runs in the same
 process (FETCH_SIZE and WRITE_SIZE are KiB per dispatch).  A summary records
@@ -30,10 +33,10 @@ COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
 
 STATS_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv "
-             "-d $REPO/gpurun_out/prof_stats -o stats -- python3 $REPO/bench.py --steps 20 --warmup 3 "
+             "-d $OUT/prof_stats -o stats -- python3 $REPO/bench.py --steps 20 --warmup 3 "
              "--decode-steps 200 --no-cpu-baseline")
 PMC_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {ctr} --output-format csv "
-           "-d $REPO/gpurun_out/pmc_{tag} -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+           "-d $OUT/pmc_{tag} -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 "
            "--decode-steps 20 --no-cpu-baseline --calibrate-copy")
 
 SEG = "::seg_"
@@ -159,7 +162,7 @@ def traffic(fetch_csv: str, write_csv: str, out_dir: str = PROFILES) -> None:
 
 MFMA_COUNTERS = "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"
 MFMA_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + MFMA_COUNTERS + " --output-format csv "
-            "-d $REPO/gpurun_out/pmc_mfma -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 "
+            "-d $OUT/pmc_mfma -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 "
             "--decode-steps 20 --no-cpu-baseline")
 SIMDS = 256 * 4        # MI355X: 256 CUs, 4 SIMDs each
 XCDS = 8               # GRBM_GUI_ACTIVE arrives summed over the XCDs; one XCD's count is the busy time
@@ -195,7 +198,7 @@ def mfma(mfma_csv: str, stats_csv: str, out_dir: str = PROFILES) -> None:
         for k, v in c.items():
             a[k] += v
     out = ["# Matrix-core counters — bench workloads on one MI355X", "",
-           "Command (repository root as $REPO):", "", "    " + MFMA_CMD, "",
+           "Command ($REPO: repository root, $OUT: output directory):", "", "    " + MFMA_CMD, "",
            "Issued FLOPs are the MFMA operation counters times 512 (the counters count 512-FLOP units), "
            "averaged per dispatch; they include the masked and zero-padded parts of tiles and the recomputed "
            "products, so they exceed the algorithmic FLOPs. MFMA busy is SQ_VALU_MFMA_BUSY_CYCLES summed over "
@@ -277,7 +280,7 @@ def stats(stats_csv: str, bench_log: str, out_dir: str = PROFILES) -> None:
     line = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")][-1]
     res = json.loads(line)
     out = ["# Kernel durations — bench workloads on one MI355X", "",
-           "Command (repository root as $REPO):", "", "    " + STATS_CMD, "",
+           "Command ($REPO: repository root, $OUT: output directory):", "", "    " + STATS_CMD, "",
            "| kernel | calls | avg ns | min ns | max ns |", "|---|---|---|---|---|"]
     for n, c, a, mn, mx, _ in rows:
         out.append(f"| `{n}` | {c} | {a:,.0f} | {mn:,.0f} | {mx:,.0f} |")
