@@ -9,6 +9,9 @@
     python -m retention_chunkwise_amd.profsum mfma MFMA_CSV STATS_CSV
         matrix-core counters per kernel (issued MFMA FLOPs, MFMA busy share)
         with the kernel-trace durations -> profiles/mfma_bench_workloads.md
+    python -m retention_chunkwise_amd.profsum sq SQ_CSV
+        shader counters per kernel (instruction mix, LDS bank conflicts,
+        waits) -> profiles/sq_bench_workloads.md
 
 In the recorded commands $REPO is the repository root and $OUT the directory
 the run writes its CSVs to.
@@ -254,6 +257,48 @@ def mfma(mfma_csv: str, stats_csv: str, out_dir: str = PROFILES) -> None:
     print("\n".join(out))
 
 
+SQ_COUNTERS = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE "
+               "SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE")
+SQ_CMD = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc " + SQ_COUNTERS + " --output-format csv "
+          "-d $OUT/pmc_sq -o pmc -- python3 $REPO/bench.py --steps 3 --warmup 1 --decode-steps 20 --no-cpu-baseline")
+
+
+def sq(sq_csv: str, out_dir: str = PROFILES) -> None:
+    per = _per_dispatch_counters(sq_csv)
+    agg = collections.OrderedDict()
+    for d in sorted(per):
+        name, c = per[d]
+        if not name.startswith("void ret::"):
+            continue
+        a = agg.setdefault(name, collections.defaultdict(float))
+        a["n"] += 1
+        for k, v in c.items():
+            a[k] += v
+    out = ["# Shader counters — bench workloads on one MI355X", "",
+           "Command ($REPO: repository root, $OUT: output directory):", "", "    " + SQ_CMD, "",
+           "Per dispatch, averaged over the run's dispatches of each kernel. Instruction counts are per wave "
+           "(SQ_INSTS_* / SQ_WAVES). LDS conflict share: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE, the share of "
+           "LDS-indexing cycles lost to bank conflicts. Wait: SQ_WAIT_INST_ANY per wave, in units of "
+           "one XCD's active cycles (GRBM_GUI_ACTIVE / " + str(XCDS) + "), i.e. roughly how much of the kernel's time "
+           "an average wave spent waiting for any instruction's operands (memory or LDS); the counter samples "
+           "every fourth cycle on some parts, so read it as a relative figure between kernels.", "",
+           "| kernel | waves | VALU / wave | MFMA / wave | LDS / wave | LDS conflict share | wait / active |",
+           "|---|---|---|---|---|---|---|"]
+    for name, a in agg.items():
+        n = a["n"]
+        waves = a.get("SQ_WAVES", 0.0) / n
+        w = max(waves, 1.0)
+        valu, mfma_, lds = (a.get(k, 0.0) / n / w for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS"))
+        conf = a.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(a.get("SQ_LDS_IDX_ACTIVE", 0.0), 1.0)
+        act = a.get("GRBM_GUI_ACTIVE", 0.0) / n / XCDS
+        wait = a.get("SQ_WAIT_INST_ANY", 0.0) / n / w / act if act > 0 else float("nan")
+        out.append(f"| `{name.replace('void ret::', '')}` | {waves:,.0f} | {valu:,.0f} | {mfma_:,.0f} | {lds:,.0f} | "
+                   f"{100 * conf:.1f} % | {wait:.2f} |")
+    with open(os.path.join(out_dir, "sq_bench_workloads.md"), "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 BENCH_LINES = [("retention forward (long bf16, state + walk kernels)", ("roofline", "kernel_ms"), 1e6, "ns per call"),
                ("backward (dq, dk, dv) of the long forward", ("backward", "ms_per_call"), 1e6, "ns per call"),
                ("backward given the forward's segment states", ("backward_from_fwd", "ms_per_call"), 1e6,
@@ -303,5 +348,7 @@ if __name__ == "__main__":
         traffic(sys.argv[2], sys.argv[3])
     elif len(sys.argv) == 4 and sys.argv[1] == "mfma":
         mfma(sys.argv[2], sys.argv[3])
+    elif len(sys.argv) == 3 and sys.argv[1] == "sq":
+        sq(sys.argv[2])
     else:
         raise SystemExit(__doc__)
