@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 8
+#define RET_ABI_VERSION 9
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -163,14 +163,18 @@ int retention_fwd_from_state(const void *q, const void *k, const void *v,
  * below at 1).  RET_NORM_GROUP then replaces each row by
  * (out - mean(out)) / sqrt(var(out) + eps), population variance over the
  * head's dv features, no learned gain or bias ("RetNet", the layer's
- * optional GroupNorm).  Statistics are taken in fp32 before the single bf16
- * rounding.
+ * optional GroupNorm).  Statistics are taken in fp32 before the single
+ * rounding to the output dtype.
  *
- *   dtype    RET_BF16 only (RET_ERR_DTYPE otherwise)
+ *   dtype    RET_BF16 (segment walk) or RET_F32 (value-slice walk).  fp32
+ *            GroupNorm needs each output row in one workgroup: chunk 64 with
+ *            dv = 64 or with dk = 64, dv = 128; chunk 128 with dk = dv = 64.
+ *            Other fp32 shapes return RET_ERR_SHAPE with RET_NORM_GROUP
+ *            (RET_NORM_ROWSUM takes every shape)
  *   norm     RET_NORM_ROWSUM or RET_NORM_GROUP (RET_ERR_SHAPE otherwise)
  *   eps      GroupNorm epsilon, finite and >= 0 (1e-5 is usual)
  *   workspace  retention_fwd_normalized_workspace_bytes(...) bytes
- *   chunk    64 or 128; with dk = dv = 128 the walk uses 64 (LDS), same result
+ *   chunk    64 or 128; bf16 with dk = dv = 128 walks 64 (LDS), same result
  *   other arguments as retention_fwd (no final state)
  */
 int retention_fwd_normalized(const void *q, const void *k, const void *v, const float *gamma,

@@ -265,7 +265,9 @@ def retention_fwd_normalized(q, k, v, gamma, norm: str = "group", eps: float = 1
     """Retention divided by its score row sum floored at 1 (norm="rowsum"),
     then GroupNorm over each row (norm="group"), fused into the walk.
 
-    bf16 only.  q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv]."""
+    bf16 or float32 (float32 GroupNorm: chunk 64 with dv = 64 or dk = 64, dv = 128;
+    chunk 128 with dk = dv = 64).
+    q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv]."""
     lib = load_library()
     codes = {"rowsum": RET_NORM_ROWSUM, "group": RET_NORM_GROUP}
     if norm not in codes:

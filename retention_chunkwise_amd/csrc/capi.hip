@@ -280,6 +280,29 @@ hipError_t launch_slice_path(const SegPlan& plan, const void* q, const void* k, 
     return ret::launch_walk(a, bf16, plan.chunk, dk, plan.nt, linattn, st);
 }
 
+// Plan of the gated linear attention walk: 64-token chunks, the widest value
+// slice, and enough segments to occupy the chip (at least 2 chunks each).
+bool plan_gla(long long bh, int T, int dk, int dv, SegPlan* p) {
+    p->chunk = 64;
+    p->pieces = 1;
+    p->nt = ret::gla_choose_nt(bh, dk, dv);
+    const int nch = (T + 63) / 64;
+    if (!forced_segments(nch, p))
+        p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, ret::gla_target_groups(dk, p->nt), 2, 16, &p->cps);
+    return set_ws_bytes(bh, dk, dv, true, p);
+}
+
+// Chunk of the normalised walk: with dk = dv = 128 the 128-token walk and its
+// normaliser exceed the LDS, so it runs 64-token chunks (same result).
+int norm_chunk(int chunk, int dk, int dv) { return (chunk == 128 && dk == 128 && dv == 128) ? 64 : chunk; }
+
+// Plan of a normalised forward: the bf16 segment walk, or the fp32 value-slice
+// walk (a normaliser slot travels with each segment state on both).
+bool plan_norm(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan* p) {
+    if (dtype == RET_BF16) return plan_segments(bh, T, norm_chunk(chunk, dk, dv), dk, dv, true, p);
+    return plan_slices(bh, T, chunk, dk, dv, true, false, p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -303,21 +326,7 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
     return plan.ws_bytes;
 }
 
-// Plan of the gated linear attention walk: 64-token chunks, the widest value
-// slice, and enough segments to occupy the chip (at least 2 chunks each).
-bool plan_gla(long long bh, int T, int dk, int dv, SegPlan* p) {
-    p->chunk = 64;
-    p->pieces = 1;
-    p->nt = ret::gla_choose_nt(bh, dk, dv);
-    const int nch = (T + 63) / 64;
-    if (!forced_segments(nch, p))
-        p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, ret::gla_target_groups(dk, p->nt), 2, 16, &p->cps);
-    return set_ws_bytes(bh, dk, dv, true, p);
-}
 
-// Chunk of the normalised walk: with dk = dv = 128 the 128-token walk and its
-// normaliser exceed the LDS, so it runs 64-token chunks (same result).
-int norm_chunk(int chunk, int dk, int dv) { return (chunk == 128 && dk == 128 && dv == 128) ? 64 : chunk; }
 
 size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
     if (B <= 0 || H < 1 || T < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || dtype != RET_F32) return 0;
@@ -328,10 +337,10 @@ size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
 
 size_t retention_fwd_normalized_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk, int dtype) {
     if (B <= 0 || H < 1 || T < 0 || (chunk != 64 && chunk != 128) || (dk != 64 && dk != 128) ||
-        (dv != 64 && dv != 128) || dtype != RET_BF16)
+        (dv != 64 && dv != 128) || (dtype != RET_BF16 && dtype != RET_F32))
         return 0;
     SegPlan plan;
-    if (!plan_segments(static_cast<long long>(B) * H, T, norm_chunk(chunk, dk, dv), dk, dv, true, &plan)) return 0;
+    if (!plan_norm(static_cast<long long>(B) * H, T, chunk, dk, dv, dtype, &plan)) return 0;
     return plan.ws_bytes;
 }
 
@@ -636,9 +645,8 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
                              size_t ws_bytes, void* stream) {
     const char* fn = "retention_fwd_normalized";
     if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
-    if (dtype != RET_BF16)
-        return fail(RET_ERR_DTYPE, "%s: bf16 only (dtype %d); the fused normalisation lives in the bf16 segment walk",
-                    fn, dtype);
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
     if (norm != RET_NORM_ROWSUM && norm != RET_NORM_GROUP)
         return fail(RET_ERR_SHAPE, "%s: norm must be RET_NORM_ROWSUM or RET_NORM_GROUP (got %d)", fn, norm);
     if (!(eps >= 0.f) || isinf(eps)) return fail(RET_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
@@ -648,7 +656,7 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
                     H, T);
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
         return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
-    size_t nqk = 2, nv = 2;
+    size_t nqk = esz, nv = esz;
     if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
         !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv))
         return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
@@ -661,12 +669,30 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
     const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv), ro = range("out", out, nv);
     for (const Range& in : {rq, rk, rv})
         if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
-    if (B == 0) return ok();
-    chunk = norm_chunk(chunk, dk, dv);
     SegPlan plan;
-    if (!plan_segments(static_cast<long long>(B) * H, T, chunk, dk, dv, true, &plan))
+    if (!plan_norm(static_cast<long long>(B) * H, T, chunk, dk, dv, dtype, &plan))
         return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    // GroupNorm needs whole output rows in one workgroup; the fp32 walk splits wide
+    // value rows over workgroups when the widest slice does not fit
+    if (dtype == RET_F32 && norm == RET_NORM_GROUP && plan.nt * 16 != dv)
+        return fail(RET_ERR_SHAPE, "%s: fp32 GroupNorm needs a whole output row in one workgroup: chunk 64 with "
+                    "dv = 64 or dk = 64, dv = 128; chunk 128 with dk = dv = 64 (got dk=%d, dv=%d, chunk %d)", fn, dk,
+                    dv, chunk);
+    if (B == 0) return ok();
     if ((rc = check_workspace(fn, plan, workspace, ws_bytes, {rq, rk, rv, ro}))) return rc;
+    if (dtype == RET_F32) {
+        ret::WalkArgs a{};
+        a.q = q; a.k = k; a.v = v; a.out = out;
+        a.B = B; a.H = H; a.T = T; a.dv = dv; a.nslices = dv / (16 * plan.nt); a.gn_eps = eps;
+        a.G = plan.G; a.cps = plan.cps;
+        a.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
+        memcpy(a.log2g, log2g, sizeof(a.log2g));
+        const hipError_t e = ret::launch_walk_norm_f32(a, plan.chunk, dk, plan.nt, norm == RET_NORM_GROUP,
+                                                       static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+        return ok();
+    }
+    chunk = plan.chunk;
     ret::SegArgs sa{};
     sa.G = plan.G; sa.cps = plan.cps; sa.pieces = plan.pieces;
     sa.q = q; sa.k = k; sa.v = v; sa.out = out;

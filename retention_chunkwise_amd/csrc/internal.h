@@ -35,6 +35,7 @@ struct WalkArgs {
                          // segments with key and value roles swapped (dv x dk, row-major); the state
                          // pass is skipped and the walk reads them transposed (ws is then only read)
     float eps;           // linear attention only
+    float gn_eps;        // GroupNorm epsilon (normalised retention with GroupNorm only)
     float log2g[kMaxHeads];
 };
 
@@ -101,6 +102,8 @@ hipError_t launch_walk_ret_bf16(const WalkArgs& a, int chunk, int dk, int nt, hi
 hipError_t launch_walk_ret_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
 hipError_t launch_walk_lin_bf16(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
 hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
+// fp32 retention with the row-sum floor, and GroupNorm when `group` (value-slice walk).
+hipError_t launch_walk_norm_f32(const WalkArgs& a, int chunk, int dk, int nt, bool group, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
                          hipStream_t stream);
 hipError_t launch_decode_lin(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t stream);

@@ -53,7 +53,7 @@ namespace walk {
 constexpr int kThreads = 256;
 using namespace ::ret::kc;
 
-template <bool BF16, int C, int DK, int NT, bool LIN>
+template <bool BF16, int C, int DK, int NT, int MODE>
 struct Cfg {
     typedef typename std::conditional<BF16, unsigned short, float>::type E;
     static constexpr int NI = C / 16;                 // 16-token tiles per chunk
@@ -127,13 +127,13 @@ __device__ __forceinline__ int swz_off(int r, int col16) {
     return r * (RU * 16) + ((col16 ^ x) << 4);
 }
 
-template <bool BF16, int C, int DK, int NT, bool LIN>
+template <bool BF16, int C, int DK, int NT, int MODE>
 struct Smem {
-    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    using Cf = Cfg<BF16, C, DK, NT, MODE>;
     using E = typename Cf::E;
     static constexpr bool DMA = Cf::DMA;
     alignas(16) float dec[Cf::DEC];                   // [16 + m] = gamma^m, [0..15] = 0
-    alignas(16) float zs[2][LIN ? DK : 4];            // normaliser z (linear attention)
+    alignas(16) float zs[2][MODE != 0 ? DK : 4];      // normaliser z (linear attention, row-sum floor)
     alignas(16) E Sts[2][Cf::DVS * Cf::KSTR];         // S^T copy, [n][k], double-buffered
     alignas(16) E Vs[Cf::DMA ? 8 : C * Cf::VSTR];     // V slice, row-major (fp32 path)
     alignas(16) E Vz[C * Cf::VSTR];                   // zeta-scaled V slice
@@ -150,12 +150,16 @@ struct QKTiles {
     E* v[2];  // the V slice, row-major
 };
 
-template <bool BF16, int C, int DK, int NT, bool LIN, int W>
-__device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, NT, LIN>& sm,
-                                          const QKTiles<typename Cfg<BF16, C, DK, NT, LIN>::E>& qk,
+template <bool BF16, int C, int DK, int NT, int MODE, int W>
+__device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, NT, MODE>& sm,
+                                          const QKTiles<typename Cfg<BF16, C, DK, NT, MODE>::E>& qk,
                                           const int bh, const int nbase, const int seg, const float lg) {
-    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    using Cf = Cfg<BF16, C, DK, NT, MODE>;
     using E = typename Cf::E;
+    // MODE: 0 retention, 1 elu+1 linear attention, 2 retention with the row-sum
+    // floor, 3 the floor plus GroupNorm (the numbering of the segment kernels)
+    constexpr bool LIN = MODE == 1, ZN = MODE != 0, NRM = MODE >= 2, GRP = MODE == 3;
+    static_assert(!(BF16 && NRM), "the normalised value-slice walks are fp32 only");
     constexpr int NI = Cf::NI, NS = Cf::NS, KSTR = Cf::KSTR, EPV = Cf::EPV;
     constexpr int VSTR = Cf::VSTR, KT = Cf::KT, KU = Cf::KU, RU = Cf::RU;
     constexpr int SPW = StateSplit<C, DK, NT>::count(W);  // state tiles of this wave
@@ -202,12 +206,12 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float lseg = static_cast<float>(a.seg_len) * lg;  // log2 of gamma^L
     if (seg > 0) {
-        constexpr int ZW = LIN ? DK : 0;  // normaliser floats after each state slot
+        constexpr int ZW = ZN ? DK : 0;  // normaliser floats after each state slot
         const long long slot = static_cast<long long>(DK) * DV + ZW;
         const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + nbase;
         for (int j = 0; j < seg; ++j) {
             const float wj = exp2f(lseg * static_cast<float>(seg - 1 - j));
-            if (!LIN && a.ws_tr) {
+            if (!ZN && a.ws_tr) {
                 // S[i][nbase + c] is element (nbase + c) * DK + i of the transposed (DV x DK) state
                 const float* sj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + j) * slot;
 #pragma unroll
@@ -552,7 +556,15 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                             const float av = sm.Vz[(jt * 16 + 4 * g + r) * VSTR + nt * 16 + l16];
                             const float b = sm.Ks[(jt * 16 + 4 * g + r) * KSTR + kt * 16 + l16];
                             snew[m] = mfma_f32(av, b, snew[m]);
-                            if (LIN && nt == 0) zsum[m] += b;
+                            if (ZN && nt == 0) {
+                                if constexpr (NRM) {
+                                    // decayed key sums: zeta_j = gamma^(c-1-j), 0 past the end
+                                    const int ez = 16 + clen - 1 - (jt * 16 + 4 * g + r);
+                                    zsum[m] += b * sm.dec[ez < 0 ? 0 : ez];
+                                } else {
+                                    zsum[m] += b;
+                                }
+                            }
                         }
                     }
                 }
@@ -587,7 +599,7 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                         }
                     }
                 }
-            } else if constexpr (LIN) {
+            } else if constexpr (ZN) {
 #pragma unroll
                 for (int jt = 0; jt <= ITMAX; ++jt)
                     if (jt <= its(s))
@@ -655,9 +667,9 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
         }
 
-        // ---------------- normalise (linear attention) and store O
+        // ---------------- normalise (linear attention, row-sum floor) and store O
         float rden[NS];
-        if constexpr (LIN) {
+        if constexpr (ZN) {
             const float* zc = sm.zs[B];
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
@@ -674,7 +686,33 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                         for (int i = 0; i < 4; ++i) dq += e[i] * zc[(DK / 4) * g + 4 * u + i];
                     }
                 }
-                rden[s] = 1.f / (sum_over_groups(rsum[s] + dq) + a.eps);
+                if constexpr (LIN) {
+                    rden[s] = 1.f / (sum_over_groups(rsum[s] + dq) + a.eps);
+                } else {
+                    // retention: the earlier tokens' share is decayed by xi like the read-out
+                    rden[s] = 1.f / fmaxf(fabsf(sum_over_groups(rsum[s] + xi[s] * dq)), 1.f);
+                }
+            }
+        }
+        // GroupNorm over each output row (the slice holds whole rows): lanes
+        // l, l^16, l^32, l^48 hold the row's four column groups
+        float mu[NS], rstd[NS];
+        if constexpr (GRP) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const f32x4 o = oacc[s][nt] * rden[s];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        s1 += o[r];
+                        s2 += o[r] * o[r];
+                    }
+                }
+                mu[s] = sum_over_groups(s1) * (1.f / Cf::DVS);
+                const float var = fmaxf(sum_over_groups(s2) * (1.f / Cf::DVS) - mu[s] * mu[s], 0.f);
+                rstd[s] = 1.f / sqrtf(var + a.gn_eps);
             }
         }
         {
@@ -685,7 +723,8 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     f32x4 o = oacc[s][nt];
-                    if constexpr (LIN) o *= rden[s];
+                    if constexpr (ZN) o *= rden[s];
+                    if constexpr (GRP) o = (o - mu[s]) * rstd[s];
                     const unsigned off = static_cast<unsigned>((row * DV + nt * 16 + 4 * g) * ESZ);
                     if constexpr (BF16) bstore8(ro, off, cvt4_bf16(o));
                     else bstore16(ro, off, o);
@@ -707,9 +746,11 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
                     if constexpr (BF16) stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = f2bf(snew[m][r]);
                     else stn[(nt * 16 + 4 * g + r) * KSTR + kcol] = snew[m][r];
                 }
-                if (LIN && nt == 0) {
+                if (ZN && nt == 0) {
                     const float zt = sum_over_groups(zsum[m]);
-                    if (g == 0) sm.zs[NB][kcol] = sm.zs[B][kcol] + zt;
+                    // the row-sum floor's normaliser decays like the state: z = gamma^c z + sum zeta k
+                    const float zd = NRM ? sm.dec[16 + clen] : 1.f;
+                    if (g == 0) sm.zs[NB][kcol] = zd * sm.zs[B][kcol] + zt;
                 }
             }
         }
@@ -733,11 +774,12 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
     }
 }
 
-template <bool BF16, int C, int DK, int NT, bool LIN>
+template <bool BF16, int C, int DK, int NT, int MODE>
 __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
-    using Cf = Cfg<BF16, C, DK, NT, LIN>;
+    using Cf = Cfg<BF16, C, DK, NT, MODE>;
     using E = typename Cf::E;
-    __shared__ Smem<BF16, C, DK, NT, LIN> sm;
+    constexpr bool LIN = MODE == 1, ZN = MODE != 0;
+    __shared__ Smem<BF16, C, DK, NT, MODE> sm;
     constexpr int QKN = Cf::DMA ? C * DK : 8;
     __shared__ __attribute__((aligned(16))) E sq0[QKN];
     __shared__ __attribute__((aligned(16))) E sq1[QKN];
@@ -764,13 +806,15 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
     const int tid = threadIdx.x;
     for (int m = tid; m < Cf::DEC; m += kThreads)
         sm.dec[m] = (m < 16) ? 0.f : exp2f(static_cast<float>(m - 16) * lg);
-    if constexpr (LIN) {
-        // normaliser entering the segment: z_0 + the earlier segments' sums (gamma = 1)
+    if constexpr (ZN) {
+        // normaliser entering the segment: z_0 + the earlier segments' sums, each decayed
+        // over the segments after it like the state (gamma = 1 for linear attention)
         const long long slot = static_cast<long long>(DK) * a.dv + DK;
         const float* zw = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + static_cast<long long>(DK) * a.dv;
+        const float lseg = static_cast<float>(a.seg_len) * lg;
         for (int m = tid; m < DK; m += kThreads) {
-            float z = a.init_z ? a.init_z[static_cast<long long>(bh) * DK + m] : 0.f;
-            for (int j = 0; j < seg; ++j) z += zw[j * slot + m];
+            float z = (LIN && a.init_z) ? a.init_z[static_cast<long long>(bh) * DK + m] : 0.f;
+            for (int j = 0; j < seg; ++j) z += exp2f(lseg * static_cast<float>(seg - 1 - j)) * zw[j * slot + m];
             sm.zs[0][m] = z;
         }
     }
@@ -779,10 +823,10 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     switch (wave) {
-        case 0: walk_body<BF16, C, DK, NT, LIN, 0>(a, sm, qk, bh, nbase, seg, lg); break;
-        case 1: walk_body<BF16, C, DK, NT, LIN, 1>(a, sm, qk, bh, nbase, seg, lg); break;
-        case 2: walk_body<BF16, C, DK, NT, LIN, 2>(a, sm, qk, bh, nbase, seg, lg); break;
-        default: walk_body<BF16, C, DK, NT, LIN, 3>(a, sm, qk, bh, nbase, seg, lg); break;
+        case 0: walk_body<BF16, C, DK, NT, MODE, 0>(a, sm, qk, bh, nbase, seg, lg); break;
+        case 1: walk_body<BF16, C, DK, NT, MODE, 1>(a, sm, qk, bh, nbase, seg, lg); break;
+        case 2: walk_body<BF16, C, DK, NT, MODE, 2>(a, sm, qk, bh, nbase, seg, lg); break;
+        default: walk_body<BF16, C, DK, NT, MODE, 3>(a, sm, qk, bh, nbase, seg, lg); break;
     }
     if constexpr (LIN) {
         // the normaliser after the segment's last chunk sits in zs[chunks % 2];
@@ -805,9 +849,10 @@ __global__ void __launch_bounds__(kThreads, 1) walk_kernel(const WalkArgs a) {
 // owns key-feature tiles {w, w + 4} and every value tile; each fp32 MFMA
 // (16x16x4) contracts over 4 consecutive tokens: A = zeta K^T, B = V, both
 // read straight from HBM / L2 (one 4- or 2-byte element per lane per tile).
-template <bool BF16, int DK, int DV, bool LIN>
+template <bool BF16, int DK, int DV, int MODE>
 __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a) {
     using E = typename std::conditional<BF16, unsigned short, float>::type;
+    constexpr bool LIN = MODE == 1, ZN = MODE != 0;
     constexpr int KT = DK / 16, NV = DV / 16, MW = KT / 4, ESZ = sizeof(E);
     static_assert(KT % 4 == 0, "every wave owns KT / 4 key-feature tiles");
     // token quads per batch (64 or 32 tokens); the next batch's loads stay in flight
@@ -871,7 +916,7 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
 #pragma unroll
             for (int mi = 0; mi < MW; ++mi) {
                 const float x = (LIN ? phi_elu1(ka[b][u][mi]) : ka[b][u][mi]) * zeta;
-                if constexpr (LIN) zs[mi] += x;
+                if constexpr (ZN) zs[mi] += x;  // phi(k), or zeta k for the row-sum floor
 #pragma unroll
                 for (int n = 0; n < NV; ++n) acc[mi][n] = mfma_f32(x, vb[b][u][n], acc[mi][n]);
             }
@@ -889,7 +934,7 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
         asm volatile("" ::: "memory");
         compute(tb + 4 * U, std::integral_constant<int, 1>{});
     }
-    const long long slot = static_cast<long long>(DK) * DV + (LIN ? DK : 0);
+    const long long slot = static_cast<long long>(DK) * DV + (ZN ? DK : 0);
     float* out = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * slot;
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi) {
@@ -898,7 +943,7 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
         for (int n = 0; n < NV; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r) out[(16 * m + 4 * g + r) * DV + 16 * n + l16] = acc[mi][n][r];
-        if constexpr (LIN) {
+        if constexpr (ZN) {
             const float z = sum_over_groups(zs[mi]);
             if (g == 0) out[DK * DV + 16 * m + l16] = z;
         }
@@ -908,16 +953,16 @@ __global__ void __launch_bounds__(kThreads) slice_state_kernel(const WalkArgs a)
 // LDS available to one workgroup on gfx950.
 constexpr size_t kLdsBytes = 160 * 1024;
 
-template <bool BF16, int C, int DK, int NT, bool LIN>
+template <bool BF16, int C, int DK, int NT, int MODE>
 constexpr bool fits() {
-    using Cf = Cfg<BF16, C, DK, NT, LIN>;
-    return sizeof(Smem<BF16, C, DK, NT, LIN>) + 4 * sizeof(typename Cf::E) * (Cf::DMA ? C * DK : 8) +
+    using Cf = Cfg<BF16, C, DK, NT, MODE>;
+    return sizeof(Smem<BF16, C, DK, NT, MODE>) + 4 * sizeof(typename Cf::E) * (Cf::DMA ? C * DK : 8) +
                2 * sizeof(typename Cf::E) * (Cf::DMA ? C * Cf::VSTR : 8) <= kLdsBytes;
 }
 
-template <bool BF16, int C, int DK, int NT, bool LIN>
+template <bool BF16, int C, int DK, int NT, int MODE>
 hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
-    if constexpr (!fits<BF16, C, DK, NT, LIN>()) {
+    if constexpr (!fits<BF16, C, DK, NT, MODE>()) {
         return hipErrorInvalidConfiguration;
     } else {
     const long long groups = static_cast<long long>(a.B) * a.H * a.nslices * a.G;
@@ -930,24 +975,24 @@ hipError_t launch_t(const WalkArgs& a, hipStream_t stream) {
         const long long sgroups = static_cast<long long>(a.B) * a.H * (a.G - 1);
         const int dv = a.dv;
 #define RET_SLICE_STATE(DV_)                                                                             \
-        if (dv == DV_) hipLaunchKernelGGL((slice_state_kernel<BF16, DK, DV_, LIN>),                      \
+        if (dv == DV_) hipLaunchKernelGGL((slice_state_kernel<BF16, DK, DV_, MODE>),                      \
                                           dim3(static_cast<unsigned>(sgroups)), dim3(kThreads), 0, stream, args);
         RET_SLICE_STATE(64)
         RET_SLICE_STATE(128)
 #undef RET_SLICE_STATE
         if (dv != 64 && dv != 128) return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL((walk_kernel<BF16, C, DK, NT, LIN>), dim3(static_cast<unsigned>(groups)),
+    hipLaunchKernelGGL((walk_kernel<BF16, C, DK, NT, MODE>), dim3(static_cast<unsigned>(groups)),
                        dim3(kThreads), 0, stream, args);
     return hipGetLastError();
     }
 }
 
 // Instantiates every (chunk, dk, NT) variant for one (dtype, operator) pair.
-template <bool BF16, bool LIN>
+template <bool BF16, int MODE>
 hipError_t launch_variant(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream) {
 #define RET_WALK_CASE(C_, DK_, NT_) \
-    if (chunk == C_ && dk == DK_ && nt == NT_) return launch_t<BF16, C_, DK_, NT_, LIN>(a, stream);
+    if (chunk == C_ && dk == DK_ && nt == NT_) return launch_t<BF16, C_, DK_, NT_, MODE>(a, stream);
     RET_WALK_CASE(64, 64, 1)
     RET_WALK_CASE(64, 64, 2)
     RET_WALK_CASE(64, 128, 1)
@@ -969,10 +1014,10 @@ hipError_t launch_variant(const WalkArgs& a, int chunk, int dk, int nt, hipStrea
 }
 
 // Whether the (chunk, dk, NT) variant fits in LDS (and is instantiated).
-template <bool BF16, bool LIN>
+template <bool BF16, int MODE>
 bool variant_fits(int chunk, int dk, int nt) {
 #define RET_WALK_FITS(C_, DK_, NT_) \
-    if (chunk == C_ && dk == DK_ && nt == NT_) return fits<BF16, C_, DK_, NT_, LIN>();
+    if (chunk == C_ && dk == DK_ && nt == NT_) return fits<BF16, C_, DK_, NT_, MODE>();
     RET_WALK_FITS(64, 64, 1)
     RET_WALK_FITS(64, 64, 2)
     RET_WALK_FITS(64, 128, 1)

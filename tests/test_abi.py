@@ -324,7 +324,9 @@ def _nrm(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=rc.RET_F32), -3),       # bf16 only
+    (dict(dtype=7), -3),
+    # fp32 GroupNorm needs whole rows in one workgroup, which dk = dv = 128 does not give
+    (dict(dtype=rc.RET_F32, dk=128, dv=128), -2),
     (dict(norm=0), -2),
     (dict(norm=3), -2),
     (dict(eps=-1.0), -2),
@@ -344,8 +346,13 @@ def test_retention_fwd_normalized_workspace():
     lib = _lib()
     n = lib.retention_fwd_normalized_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_BF16)
     assert n > 0 and n % ((128 * 128 + 128) * 4) == 0
-    assert lib.retention_fwd_normalized_workspace_bytes(1, 32, 65536, 128, 128, 128, rc.RET_F32) == 0
+    # fp32: the value-slice walk's segment states, with a normaliser slot each
+    n32 = lib.retention_fwd_normalized_workspace_bytes(4, 8, 2048, 64, 64, 64, rc.RET_F32)
+    assert n32 > 0 and n32 % ((64 * 64 + 64) * 4 * 32) == 0
+    assert lib.retention_fwd_normalized_workspace_bytes(1, 32, 4096, 64, 64, 64, 7) == 0
     assert _nrm(lib, B=0) == 0
+    # the floor alone has no whole-row requirement
+    assert _nrm(lib, B=0, dtype=rc.RET_F32, dk=128, dv=128, norm=rc.RET_NORM_ROWSUM) == 0
 
 
 # ---------------------------------------------------------------- gated linear attention

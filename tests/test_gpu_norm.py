@@ -6,8 +6,9 @@ divides each read-out by max(|n_t . q_t|, 1), then standardises each row for
 GroupNorm.  Cases: both normalisations, chunks 64 and 128, every (dk, dv)
 pair, several segment counts, ragged and short lengths, decays from 0.02 to 1,
 inputs scaled so that the floor is active for some rows and not for others,
-and the long bf16 shape on sampled heads.  Tolerance: relative Frobenius
-error 2e-2 (bf16 inputs, fp32 accumulation, one bf16 rounding).
+and the long bf16 shape on sampled heads.  The fp32 value-slice walk is held
+to the same oracle on every shape it takes.  Tolerance: relative Frobenius
+error 2e-2 (bf16 inputs, fp32 accumulation, one bf16 rounding), 1e-4 (fp32).
 """
 import numpy as np
 import pytest
@@ -20,14 +21,16 @@ from retention_chunkwise_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
+TOL32 = 1e-4
 
 
-def _inputs(seed, B, H, T, dk, dv, qscale=1.0):
-    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, dtype="bf16", scale=1.0)
+def _inputs(seed, B, H, T, dk, dv, qscale=1.0, dtype="bf16"):
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, scale=1.0)
     inp = wl.make_inputs(w, seed)
+    tdt = wl.torch_dtype(dtype)
     # q scaled so the score row sums straddle the floor of 1
-    inp["q"] = (inp["q"].float() * (qscale / np.sqrt(dk))).to(torch.bfloat16)
-    inp["k"] = (inp["k"].float() / np.sqrt(dk)).to(torch.bfloat16)
+    inp["q"] = (inp["q"].float() * (qscale / np.sqrt(dk))).to(tdt)
+    inp["k"] = (inp["k"].float() / np.sqrt(dk)).to(tdt)
     return w, inp
 
 
@@ -43,12 +46,12 @@ def _run(inp, norm, chunk, monkeypatch, G=None, eps=1e-5):
     return out.float().cpu().numpy()
 
 
-def _check(tag, out, inp, norm, eps=1e-5):
+def _check(tag, out, inp, norm, eps=1e-5, tol=TOL):
     ref = oracle.retention_normalized(inp["q"], inp["k"], inp["v"], inp["gamma"], group=(norm == "group"), eps=eps,
                                       nthreads=8)
     e = oracle.rel_frobenius(out, ref)
-    print(f"[parity] {tag}: rel_fro={e:.3e} (tol {TOL:.0e})", flush=True)
-    assert e <= TOL and np.isfinite(out).all(), tag
+    print(f"[parity] {tag}: rel_fro={e:.3e} (tol {tol:.0e})", flush=True)
+    assert e <= tol and np.isfinite(out).all(), tag
 
 
 @pytest.mark.parametrize("norm", ["rowsum", "group"])
@@ -98,3 +101,49 @@ def test_norm_long_sequence_sampled_heads(monkeypatch):
         e = oracle.rel_frobenius(out[:, h:h + 1], ref)
         print(f"[parity] norm group long head {h}: rel_fro={e:.3e}", flush=True)
         assert e <= TOL
+
+
+# ---------------------------------------------------------------- fp32 (value-slice walk)
+F32_GROUP_SHAPES = [(64, 64, 64), (64, 64, 128), (64, 128, 64), (128, 64, 64)]  # (chunk, dk, dv)
+
+
+@pytest.mark.parametrize("chunk,dk,dv", F32_GROUP_SHAPES)
+@pytest.mark.parametrize("T,G", [(1000, None), (1333, 4), (300, 1)])
+def test_norm_f32_group(chunk, dk, dv, T, G, monkeypatch):
+    w, inp = _inputs(71, 2, 3, T, dk, dv, qscale=2.0, dtype="f32")
+    out = _run(inp, "group", chunk, monkeypatch, G)
+    _check(f"norm f32 group C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, "group", tol=TOL32)
+
+
+@pytest.mark.parametrize("chunk", [64, 128])
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, None), (1333, 4)])
+def test_norm_f32_rowsum(chunk, dk, dv, T, G, monkeypatch):
+    w, inp = _inputs(72, 2, 3, T, dk, dv, qscale=2.0, dtype="f32")
+    out = _run(inp, "rowsum", chunk, monkeypatch, G)
+    _check(f"norm f32 rowsum C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, "rowsum", tol=TOL32)
+
+
+@pytest.mark.parametrize("norm", ["rowsum", "group"])
+@pytest.mark.parametrize("T", [1, 5, 64, 65, 129])
+def test_norm_f32_short_and_ragged(norm, T, monkeypatch):
+    w, inp = _inputs(73, 1, 2, T, 64, 64, qscale=3.0, dtype="f32")
+    out = _run(inp, norm, 64, monkeypatch, 2)
+    _check(f"norm f32 {norm} short T={T}", out, inp, norm, tol=TOL32)
+
+
+@pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
+@pytest.mark.parametrize("qscale", [0.05, 20.0])
+def test_norm_f32_gamma_and_floor(gval, qscale, monkeypatch):
+    w, inp = _inputs(74, 1, 2, 900, 64, 64, qscale=qscale, dtype="f32")
+    inp["gamma"] = np.full(2, gval, dtype=np.float32)
+    for norm in ("rowsum", "group"):
+        out = _run(inp, norm, 64, monkeypatch, 3)
+        _check(f"norm f32 {norm} gamma={gval} qscale={qscale}", out, inp, norm, tol=TOL32)
+
+
+def test_norm_f32_group_needs_whole_rows(monkeypatch):
+    """fp32 GroupNorm at dk = dv = 128 splits rows over workgroups: refused."""
+    w, inp = _inputs(75, 1, 1, 200, 128, 128, dtype="f32")
+    with pytest.raises(RuntimeError, match="whole output row"):
+        _run(inp, "group", 64, monkeypatch, None)
