@@ -167,10 +167,10 @@ int retention_fwd_from_state(const void *q, const void *k, const void *v,
  * rounding to the output dtype.
  *
  *   dtype    RET_BF16 (segment walk) or RET_F32 (value-slice walk).  fp32
- *            GroupNorm needs each output row in one workgroup: chunk 64 with
- *            dv = 64 or with dk = 64, dv = 128; chunk 128 with dk = dv = 64.
- *            Other fp32 shapes return RET_ERR_SHAPE with RET_NORM_GROUP
- *            (RET_NORM_ROWSUM takes every shape)
+ *            GroupNorm is fused into the walk where one workgroup holds whole
+ *            output rows (chunk 64 with dv = 64 or dk = 64, dv = 128; chunk
+ *            128 with dk = dv = 64); elsewhere the walk applies the floor and
+ *            a second pass over `out` standardises each row in place
  *   norm     RET_NORM_ROWSUM or RET_NORM_GROUP (RET_ERR_SHAPE otherwise)
  *   eps      GroupNorm epsilon, finite and >= 0 (1e-5 is usual)
  *   workspace  retention_fwd_normalized_workspace_bytes(...) bytes

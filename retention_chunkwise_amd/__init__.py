@@ -16,7 +16,7 @@ linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
 linear_attn_fwd(..., initial_state=(S, z), return_state=True) -> (out, S, z)
 linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place)
 retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv); fwd_workspace= reuses a forward's states
-retention_fwd_normalized(q, k, v, gamma, norm="group", eps=1e-5) -> out   (bf16)
+retention_fwd_normalized(q, k, v, gamma, norm="group", eps=1e-5) -> out   (bf16 or fp32)
 retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.autograd)
 gla_fwd(q, k, v, log_gate)                     -> (out, final_state)   (fp32)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
@@ -265,8 +265,8 @@ def retention_fwd_normalized(q, k, v, gamma, norm: str = "group", eps: float = 1
     """Retention divided by its score row sum floored at 1 (norm="rowsum"),
     then GroupNorm over each row (norm="group"), fused into the walk.
 
-    bf16 or float32 (float32 GroupNorm: chunk 64 with dv = 64 or dk = 64, dv = 128;
-    chunk 128 with dk = dv = 64).
+    bf16 or float32 (float32 GroupNorm is fused where one workgroup holds whole rows,
+    else a second in-place pass over out).
     q, k: [B,H,T,dk]; v: [B,H,T,dv].  Returns out [B,H,T,dv]."""
     lib = load_library()
     codes = {"rowsum": RET_NORM_ROWSUM, "group": RET_NORM_GROUP}

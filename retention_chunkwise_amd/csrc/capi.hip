@@ -672,12 +672,6 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
     SegPlan plan;
     if (!plan_norm(static_cast<long long>(B) * H, T, chunk, dk, dv, dtype, &plan))
         return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
-    // GroupNorm needs whole output rows in one workgroup; the fp32 walk splits wide
-    // value rows over workgroups when the widest slice does not fit
-    if (dtype == RET_F32 && norm == RET_NORM_GROUP && plan.nt * 16 != dv)
-        return fail(RET_ERR_SHAPE, "%s: fp32 GroupNorm needs a whole output row in one workgroup: chunk 64 with "
-                    "dv = 64 or dk = 64, dv = 128; chunk 128 with dk = dv = 64 (got dk=%d, dv=%d, chunk %d)", fn, dk,
-                    dv, chunk);
     if (B == 0) return ok();
     if ((rc = check_workspace(fn, plan, workspace, ws_bytes, {rq, rk, rv, ro}))) return rc;
     if (dtype == RET_F32) {
@@ -687,8 +681,14 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
         a.G = plan.G; a.cps = plan.cps;
         a.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
         memcpy(a.log2g, log2g, sizeof(a.log2g));
-        const hipError_t e = ret::launch_walk_norm_f32(a, plan.chunk, dk, plan.nt, norm == RET_NORM_GROUP,
-                                                       static_cast<hipStream_t>(stream));
+        // GroupNorm is fused where one workgroup holds whole rows; where the walk splits a
+        // row over value slices it applies the floor, and a row pass standardises in place
+        const bool group = norm == RET_NORM_GROUP, fused = plan.nt * 16 == dv;
+        hipError_t e = ret::launch_walk_norm_f32(a, plan.chunk, dk, plan.nt, group && fused,
+                                                 static_cast<hipStream_t>(stream));
+        if (e == hipSuccess && group && !fused)
+            e = ret::launch_group_norm_rows_f32(static_cast<float*>(out), static_cast<long long>(B) * H * T, dv, eps,
+                                                static_cast<hipStream_t>(stream));
         if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
         return ok();
     }

@@ -104,6 +104,8 @@ hipError_t launch_walk_lin_bf16(const WalkArgs& a, int chunk, int dk, int nt, hi
 hipError_t launch_walk_lin_f32(const WalkArgs& a, int chunk, int dk, int nt, hipStream_t stream);
 // fp32 retention with the row-sum floor, and GroupNorm when `group` (value-slice walk).
 hipError_t launch_walk_norm_f32(const WalkArgs& a, int chunk, int dk, int nt, bool group, hipStream_t stream);
+// GroupNorm over each fp32 row of dv (64 or 128) values, in place.
+hipError_t launch_group_norm_rows_f32(float* out, long long rows, int dv, float eps, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, bool bf16, int dk, int dv,
                          hipStream_t stream);
 hipError_t launch_decode_lin(const DecodeArgs& a, bool bf16, int dk, int dv, hipStream_t stream);

@@ -142,8 +142,11 @@ def test_norm_f32_gamma_and_floor(gval, qscale, monkeypatch):
         _check(f"norm f32 {norm} gamma={gval} qscale={qscale}", out, inp, norm, tol=TOL32)
 
 
-def test_norm_f32_group_needs_whole_rows(monkeypatch):
-    """fp32 GroupNorm at dk = dv = 128 splits rows over workgroups: refused."""
-    w, inp = _inputs(75, 1, 1, 200, 128, 128, dtype="f32")
-    with pytest.raises(RuntimeError, match="whole output row"):
-        _run(inp, "group", 64, monkeypatch, None)
+@pytest.mark.parametrize("chunk,dk,dv", [(64, 128, 128), (128, 64, 128), (128, 128, 64), (128, 128, 128)])
+@pytest.mark.parametrize("T,G", [(1000, None), (700, 3)])
+def test_norm_f32_group_rows_over_slices(chunk, dk, dv, T, G, monkeypatch):
+    """Shapes whose rows span several value slices: the walk applies the floor
+    and a row pass standardises in place."""
+    w, inp = _inputs(75, 2, 3, T, dk, dv, qscale=2.0, dtype="f32")
+    out = _run(inp, "group", chunk, monkeypatch, G)
+    _check(f"norm f32 group (row pass) C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, "group", tol=TOL32)
