@@ -35,12 +35,10 @@
  *    human-readable message for the last error of the calling thread is
  *    returned by retention_last_error().  Inputs are never modified (except
  *    the state of the two decode steps, which is updated in place).
- *  - Tuning and testing knobs, read from the environment at every call:
- *    RET_FWD_PATH = "slice" | "segment" forces the forward path (segment
- *    needs bf16; anything else means automatic), RET_FWD_SEGMENTS = n forces
- *    the segment count, RET_WALK_NT = n narrows the value slices of the slice
- *    path, RET_LIN_CHUNK = 64 | 128 sets the linear-attention chunk.  None
- *    changes results beyond rounding.
+ *  - The execution plan of a call (which kernels, how many segments, slice
+ *    widths, internal chunk) is a function of its arguments only, unless the
+ *    calling thread has set a plan override (retention_set_plan_override),
+ *    a hook for tests and tuning.  No environment variable is read.
  *
  * Sources (page title, then passage):
  *   "RetNet" (bembew.net): the single-head definition O = (Q K^T (.) D) V with
@@ -64,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 9
+#define RET_ABI_VERSION 10
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -172,7 +170,9 @@ int retention_fwd_from_state(const void *q, const void *k, const void *v,
  *            128 with dk = dv = 64); elsewhere the walk applies the floor and
  *            a second pass over `out` standardises each row in place
  *   norm     RET_NORM_ROWSUM or RET_NORM_GROUP (RET_ERR_SHAPE otherwise)
- *   eps      GroupNorm epsilon, finite and >= 0 (1e-5 is usual)
+ *   eps      GroupNorm epsilon, finite and > 0 (1e-5 is usual); a row whose
+ *            values are all equal (zero queries) then comes out as zeros.
+ *            Ignored by RET_NORM_ROWSUM (any finite value >= 0)
  *   workspace  retention_fwd_normalized_workspace_bytes(...) bytes
  *   chunk    64 or 128; bf16 with dk = dv = 128 walks 64 (LDS), same result
  *   other arguments as retention_fwd (no final state)
@@ -238,7 +238,7 @@ size_t retention_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
  * Errors: those of retention_bwd; RET_ERR_WORKSPACE when fwd_workspace is
  * NULL or short although the forward needed one; RET_ERR_ALIGN when it is not
  * 16-byte aligned; RET_ERR_ALIAS when it overlaps dq, dk, dv or `workspace`.
- * If the tuning knobs changed the forward's segment plan between the calls,
+ * If a plan override changed the forward's segment plan between the calls,
  * dq runs its own state pass (the result is unchanged).
  */
 int retention_bwd_from_fwd(const void *q, const void *k, const void *v, const float *gamma, int chunk,
@@ -361,6 +361,35 @@ int gla_fwd(const void *q, const void *k, const void *v, const float *log_gate, 
 
 /* Workspace bytes gla_fwd needs (0: none or invalid).  Host only. */
 size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype);
+
+/* forward paths for retention_set_plan_override */
+#define RET_PATH_AUTO 0    /* the library's choice */
+#define RET_PATH_SLICE 1   /* value-slice walk (fp32's path; bf16 only when forced) */
+#define RET_PATH_SEGMENT 2 /* segment-split walk where the dtype has one (bf16) */
+
+/*
+ * retention_set_plan_override -- testing and tuning hook.  Fixes parts of the
+ * plan that every later call made from the CALLING HOST THREAD would
+ * otherwise choose from its arguments, until the next call of this function;
+ * other threads are unaffected.  retention_set_plan_override(0, 0, 0, 0)
+ * restores the automatic plan.  No override changes results beyond floating-
+ * point rounding order; an override a kernel cannot honour (a slice width
+ * whose variant does not fit, the segment path for fp32) is ignored.
+ *
+ *   fwd_path   RET_PATH_AUTO, RET_PATH_SLICE or RET_PATH_SEGMENT
+ *   segments   0 (automatic) or the segment count per (b, h) sequence
+ *              (capped at the number of chunks), for every chunked walk
+ *   walk_nt    0 (automatic) or a narrower value slice of the slice path, in
+ *              16-column tiles: 1, 2, 4 or 8
+ *   lin_chunk  0 (automatic), 64 or 128: the chunk of bf16 linear attention
+ *              on the segment path (128 needs dk = 64)
+ *
+ * The workspace-size helpers follow the same override, so a workspace sized
+ * under one override must be used under the same override.  Returns RET_OK,
+ * or RET_ERR_SHAPE / RET_ERR_CHUNK for an out-of-range value (the previous
+ * override then stays in place).  Host only; enqueues nothing.
+ */
+int retention_set_plan_override(int fwd_path, int segments, int walk_nt, int lin_chunk);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none).  The pointer stays valid until the next call on that thread. */

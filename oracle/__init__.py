@@ -360,12 +360,47 @@ def linattn_rows(q, k, v, rows, eps: float = ELU1_EPS, nthreads: int = 1):
     return out
 
 
-def rel_frobenius(x, ref) -> float:
-    """Relative Frobenius error ||x - ref||_F / ||ref||_F (float64)."""
+def frobenius_parts(x, ref) -> tuple[float, float]:
+    """(||x - ref||_F, ||ref||_F) in float64: the numerator and denominator of
+    the relative Frobenius error, kept apart so that the errors of pieces of a
+    tensor (head groups compared one after another) combine exactly."""
     x = _f64(x)
     ref = _f64(ref)
-    den = float(np.linalg.norm(ref.ravel()))
-    num = float(np.linalg.norm((x - ref).ravel()))
-    if den == 0.0:
-        return num
-    return num / den
+    if x.shape != ref.shape:
+        raise ValueError(f"shape mismatch: {x.shape} vs {ref.shape}")
+    return float(np.linalg.norm((x - ref).ravel())), float(np.linalg.norm(ref.ravel()))
+
+
+def _ratio(num: float, den: float) -> float:
+    # a zero reference has no relative error: the absolute one is reported, so
+    # only an x that is zero as well passes a small tolerance
+    return num / den if den > 0.0 else num
+
+
+def rel_frobenius(x, ref) -> float:
+    """Relative Frobenius error ||x - ref||_F / ||ref||_F (float64), measured
+    against the reference; ||x - ref||_F itself when ref is all zeros."""
+    return _ratio(*frobenius_parts(x, ref))
+
+
+def combine_rel_frobenius(parts) -> float:
+    """The relative Frobenius error of a whole tensor from the
+    frobenius_parts of disjoint pieces that cover it."""
+    num2 = sum(n * n for n, _ in parts)
+    den2 = sum(d * d for _, d in parts)
+    return _ratio(float(np.sqrt(num2)), float(np.sqrt(den2)))
+
+
+def rel_frobenius_per_slice(x, ref, lead: int = 2) -> np.ndarray:
+    """Relative Frobenius error of every slice over the first `lead` axes
+    (per (b, h) for [B, H, ...] tensors), as an array of that shape."""
+    x = _f64(x)
+    ref = _f64(ref)
+    if x.shape != ref.shape:
+        raise ValueError(f"shape mismatch: {x.shape} vs {ref.shape}")
+    shp = x.shape[:lead]
+    d = (x - ref).reshape(shp + (-1,))
+    r = ref.reshape(shp + (-1,))
+    num = np.sqrt(np.sum(d * d, axis=-1))
+    den = np.sqrt(np.sum(r * r, axis=-1))
+    return np.where(den > 0.0, num / np.where(den > 0.0, den, 1.0), num)

@@ -21,6 +21,8 @@ retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.aut
 gla_fwd(q, k, v, log_gate)                     -> (out, final_state)   (fp32)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
 linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
+set_plan_override(path=None, segments=None, walk_nt=None, lin_chunk=None)   (this thread's calls)
+plan_override(...)                             context manager around set_plan_override
 
 The two forwards take an optional ``workspace=`` uint8 tensor for the
 segment states of the bf16 paths; without one, the binding takes it from
@@ -28,6 +30,7 @@ PyTorch's allocator for the call.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -39,7 +42,7 @@ __all__ = ["retention_fwd", "retention_bwd", "retention", "retention_decode_step
            "linear_attn_decode_step", "retention_bwd_workspace_bytes", "retention_fwd_normalized",
            "retention_fwd_normalized_workspace_bytes", "gla_fwd", "RET_NORM_ROWSUM", "RET_NORM_GROUP",
            "retention_fwd_workspace_bytes",
-           "linear_attn_workspace_bytes", "RetentionError",
+           "linear_attn_workspace_bytes", "RetentionError", "set_plan_override", "plan_override",
            "library_path", "load_library", "abi_version", "last_error"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +55,7 @@ RET_BF16 = 1
 RET_PHI_ELU1 = 1
 RET_NORM_ROWSUM = 1
 RET_NORM_GROUP = 2
+RET_PATH = {None: 0, "auto": 0, "slice": 1, "segment": 2}
 ERRORS = {
     -1: "RET_ERR_NULL", -2: "RET_ERR_SHAPE", -3: "RET_ERR_DTYPE", -4: "RET_ERR_CHUNK",
     -5: "RET_ERR_GAMMA", -6: "RET_ERR_PHI", -7: "RET_ERR_ALIGN", -8: "RET_ERR_ALIAS",
@@ -118,6 +122,8 @@ def load_library():
             lib.retention_last_error.restype = ctypes.c_char_p
             lib.retention_abi_version.argtypes = []
             lib.retention_abi_version.restype = i
+            lib.retention_set_plan_override.argtypes = [i, i, i, i]
+            lib.retention_set_plan_override.restype = i
             _lib = lib
         return _lib
 
@@ -133,6 +139,30 @@ def last_error() -> str:
 def _raise(rc: int):
     if rc != 0:
         raise RetentionError(rc, last_error())
+
+
+def set_plan_override(path=None, segments=None, walk_nt=None, lin_chunk=None) -> None:
+    """Fix parts of the library's execution plan for later calls made from
+    the calling thread (retention_set_plan_override in the C ABI); with no
+    arguments the automatic plan is restored.  path: "slice" | "segment" |
+    None; segments: the segment count per sequence; walk_nt: value-slice width
+    of the slice path in 16-column tiles; lin_chunk: 64 | 128.  Results do
+    not change beyond rounding."""
+    if path not in RET_PATH:
+        raise ValueError(f"path must be one of {sorted(k for k in RET_PATH if k)} or None")
+    _raise(load_library().retention_set_plan_override(RET_PATH[path], int(segments or 0), int(walk_nt or 0),
+                                                      int(lin_chunk or 0)))
+
+
+@contextlib.contextmanager
+def plan_override(**kw):
+    """``with plan_override(segments=4): ...`` -- set_plan_override for the
+    block, then the automatic plan again."""
+    set_plan_override(**kw)
+    try:
+        yield
+    finally:
+        set_plan_override()
 
 
 def _dtype_code(t: torch.Tensor) -> int:

@@ -1,10 +1,13 @@
 """Build libretention.so (HIP, gfx950 only) in-tree.
 
-    python -m retention_chunkwise_amd._build
+    python -m retention_chunkwise_amd._build [-v] [--incremental]
 
 compiles every source under csrc/ with hipcc for --offload-arch=gfx950 and
 links them into retention_chunkwise_amd/libretention.so.  Packed fp32 vector
 instructions are disabled for all device code (-packed-fp32-ops).
+--incremental keeps the objects and hipcc's dependency files under _build/ at
+the repository root and recompiles only the sources whose object is older than
+the source or any header it includes.
 """
 from __future__ import annotations
 
@@ -38,21 +41,40 @@ def common_flags() -> list[str]:
             "-Wall", "-Wno-unused-function"]
 
 
-def build(verbose: bool = False) -> str:
+OBJ_CACHE = os.path.join(os.path.dirname(HERE), "_build")
+
+
+def _stale(obj: str, src: str) -> bool:
+    """True when obj is missing or older than src or a file its depfile lists."""
+    dep = obj[:-2] + ".d"
+    if not (os.path.exists(obj) and os.path.exists(dep)):
+        return True
+    t = os.path.getmtime(obj)
+    text = open(dep).read().replace("\\\n", " ")
+    files = text.split(":", 1)[1].split() if ":" in text else [src]
+    return any(not os.path.exists(f) or os.path.getmtime(f) > t for f in files + [src])
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="retbuild_") as tmp:
+        odir = OBJ_CACHE if incremental else tmp
+        os.makedirs(odir, exist_ok=True)
         objs = []
         cmds = []
         for src in SOURCES:
-            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            obj = os.path.join(odir, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
-            cmds.append([cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+            path = os.path.join(CSRC, src)
+            if incremental and not _stale(obj, path):
+                continue
+            cmds.append([cc, *common_flags(), "-MD", "-MF", obj[:-2] + ".d", "-c", path, "-o", obj])
 
         def run(cmd):
             r = subprocess.run(cmd, capture_output=True, text=True)
             return cmd, r
 
-        with concurrent.futures.ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, len(cmds))) as ex:
             for cmd, r in ex.map(run, cmds):
                 # hipcc's host pass warns that it does not know the packed-fp32
                 # feature flag; that line is expected and harmless.
@@ -73,4 +95,4 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))

@@ -74,23 +74,24 @@ int check_gamma(const char* fn, const float* gamma, int H, float* log2g) {
 
 // ---- forward path selection
 //
-// RET_FWD_PATH = "slice" | "segment" forces a forward path (any other value
-// or unset: automatic); RET_FWD_SEGMENTS = n forces the segment count;
-// RET_WALK_NT = n narrows the value slices of the slice path to n 16-column
-// tiles.  They exist for tests and tuning and never change results beyond
-// rounding.
+// The plan of a call (path, segment count, value-slice width, linear-attention
+// chunk) is a function of its arguments, unless the calling thread has set a
+// plan override (retention_set_plan_override), which tests and tuning sweeps
+// use to force both paths and many segment counts on the same inputs.  No
+// override changes results beyond rounding.
 enum class FwdPath { kSlice, kSegment };
 
-int env_int(const char* name) {
-    const char* s = getenv(name);
-    return s ? atoi(s) : 0;
-}
+struct PlanOverride {
+    int path = RET_PATH_AUTO;  // RET_PATH_*
+    int segments = 0;          // 0: automatic
+    int walk_nt = 0;           // 0: automatic; else a narrower value slice (16-column tiles), slice path
+    int lin_chunk = 0;         // 0: automatic; else 64 or 128, bf16 linear attention on the segment path
+};
+thread_local PlanOverride g_over;
 
 FwdPath choose_fwd_path(int dtype) {
-    const char* s = getenv("RET_FWD_PATH");
     const bool seg_ok = dtype == RET_BF16;
-    if (s && !strcmp(s, "slice")) return FwdPath::kSlice;
-    if (s && !strcmp(s, "segment") && seg_ok) return FwdPath::kSegment;
+    if (g_over.path == RET_PATH_SLICE) return FwdPath::kSlice;
     return seg_ok ? FwdPath::kSegment : FwdPath::kSlice;
 }
 
@@ -105,9 +106,9 @@ struct SegPlan {
     size_t ws_bytes = 0;
 };
 
-// Segment count forced by RET_FWD_SEGMENTS (0: not forced).
+// Segment count fixed by the plan override (false: not fixed).
 bool forced_segments(int nch, SegPlan* p) {
-    const int forced = env_int("RET_FWD_SEGMENTS");
+    const int forced = g_over.segments;
     if (forced <= 0) return false;
     const int g = (forced < nch) ? forced : (nch > 0 ? nch : 1);
     p->cps = (nch > 0) ? (nch + g - 1) / g : 1;
@@ -138,7 +139,7 @@ bool plan_slices(long long bh, int T, int chunk, int dk, int dv, bool linattn, b
     const bool forced = forced_segments(nch, p);
     if (!bf16 || forced) {
         p->nt = ret::choose_walk_nt_wide(dv, bf16, chunk, dk, linattn);
-        const int want = env_int("RET_WALK_NT");  // tuning: a narrower slice, if that variant fits
+        const int want = g_over.walk_nt;  // override: a narrower slice, if that variant fits
         if (want > 0 && want < p->nt && (dv / 16) % want == 0 && ret::walk_variant_fits(bf16, linattn, chunk, dk, want))
             p->nt = want;
         if (!forced) p->G = ret::choose_segments(bh * (dv / (16 * p->nt)), nch, 256, 2, 16, &p->cps);
@@ -182,7 +183,7 @@ bool plan_segments(long long bh, int T, int chunk, int dk, int dv, bool linattn,
 // uses 64 (wider value slices fit in LDS); a forced bf16 slice walk 128.
 int linattn_chunk(int dk, FwdPath path, bool bf16) {
     if (path == FwdPath::kSegment) {
-        const int want = env_int("RET_LIN_CHUNK");  // tuning: 64 or 128 (128 only with dk = 64)
+        const int want = g_over.lin_chunk;  // override: 64 or 128 (128 only with dk = 64)
         if (want == 64 || (want == 128 && dk == 64)) return want;
         return dk == 128 ? 64 : 128;
     }
@@ -355,6 +356,23 @@ size_t retention_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int ch
 }
 
 int retention_abi_version(void) { return RET_ABI_VERSION; }
+
+int retention_set_plan_override(int fwd_path, int segments, int walk_nt, int lin_chunk) {
+    const char* fn = "retention_set_plan_override";
+    if (fwd_path != RET_PATH_AUTO && fwd_path != RET_PATH_SLICE && fwd_path != RET_PATH_SEGMENT)
+        return fail(RET_ERR_SHAPE, "%s: unknown path %d", fn, fwd_path);
+    if (segments < 0 || segments > 65536)
+        return fail(RET_ERR_SHAPE, "%s: segments must be 0..65536 (got %d)", fn, segments);
+    if (walk_nt != 0 && walk_nt != 1 && walk_nt != 2 && walk_nt != 4 && walk_nt != 8)
+        return fail(RET_ERR_SHAPE, "%s: walk_nt must be 0, 1, 2, 4 or 8 (got %d)", fn, walk_nt);
+    if (lin_chunk != 0 && lin_chunk != 64 && lin_chunk != 128)
+        return fail(RET_ERR_CHUNK, "%s: lin_chunk must be 0, 64 or 128 (got %d)", fn, lin_chunk);
+    g_over.path = fwd_path;
+    g_over.segments = segments;
+    g_over.walk_nt = walk_nt;
+    g_over.lin_chunk = lin_chunk;
+    return ok();
+}
 
 }  // extern "C"
 
@@ -581,8 +599,8 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
             const Range rf = range("fwd_workspace", fwd_ws, fplan.ws_bytes);
             for (const Range& o : {rdq, rdk, rdv, range("workspace", workspace, need)})
                 if (overlap(rf, o)) return fail(RET_ERR_ALIAS, "%s: fwd_workspace overlaps %s", fn, o.name);
-            // the forward's plan must be the one the dq walk uses (it is, unless the tuning
-            // knobs changed between the calls; then the dq walk runs its own state pass)
+            // the forward's plan must be the one the dq walk uses (it is, unless a plan
+            // override changed between the calls; then the dq walk runs its own state pass)
             dq_shares = fplan.path == plans[0].path && fplan.G == plans[0].G && fplan.cps == plans[0].cps &&
                         fplan.chunk == plans[0].chunk &&
                         (fplan.path == FwdPath::kSlice || fplan.pieces == plans[0].pieces);
@@ -650,6 +668,9 @@ int retention_fwd_normalized(const void* q, const void* k, const void* v, const 
     if (norm != RET_NORM_ROWSUM && norm != RET_NORM_GROUP)
         return fail(RET_ERR_SHAPE, "%s: norm must be RET_NORM_ROWSUM or RET_NORM_GROUP (got %d)", fn, norm);
     if (!(eps >= 0.f) || isinf(eps)) return fail(RET_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
+    // a row of equal values (all-zero queries, say) has variance 0: GroupNorm needs eps > 0
+    if (norm == RET_NORM_GROUP && !(eps > 0.f))
+        return fail(RET_ERR_SHAPE, "%s: GroupNorm needs eps > 0 (got %g)", fn, static_cast<double>(eps));
     if (chunk != 64 && chunk != 128) return fail(RET_ERR_CHUNK, "%s: chunk must be 64 or 128 (got %d)", fn, chunk);
     if (B < 0 || T < 0 || H < 1 || H > ret::kMaxHeads)
         return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, 1 <= H <= %d (got B=%d H=%d T=%d)", fn, ret::kMaxHeads, B,

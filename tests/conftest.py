@@ -26,3 +26,15 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture
+def plan():
+    """Setter of the library's per-thread plan override (path, segment count,
+    slice width, linear-attention chunk); the automatic plan is restored when
+    the test ends."""
+    import retention_chunkwise_amd as rc
+
+    rc.set_plan_override()
+    yield rc.set_plan_override
+    rc.set_plan_override()

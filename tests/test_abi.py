@@ -328,6 +328,7 @@ def _nrm(lib, **kw):
     (dict(norm=0), -2),
     (dict(norm=3), -2),
     (dict(eps=-1.0), -2),
+    (dict(eps=0.0), -2),  # GroupNorm of a constant row needs eps > 0
     (dict(chunk=96), -4),
     (dict(gamma=_gam([0.9, 2.0])), -5),
     (dict(out=FAKE * 2), -8),
@@ -338,6 +339,13 @@ def test_retention_fwd_normalized_rejects(kw, code):
     lib = _lib()
     assert _nrm(lib, **kw) == code
     assert "retention_fwd_normalized" in lib.retention_last_error().decode()
+
+
+def test_retention_fwd_normalized_rowsum_takes_eps_zero():
+    lib = _lib()
+    # eps only enters GroupNorm; the floor alone accepts 0 (validation passes, then B = 0 is a no-op)
+    assert _nrm(lib, norm=rc.RET_NORM_ROWSUM, eps=0.0, B=0) == 0
+    assert _nrm(lib, norm=rc.RET_NORM_GROUP, eps=0.0, B=0) == -2
 
 
 def test_retention_fwd_normalized_workspace():
@@ -435,3 +443,70 @@ def test_very_long_fp32_segments_stay_under_2_gib():
     # a shorter head keeps the usual plan
     m = lib.retention_fwd_workspace_bytes(1, 1, 1 << 20, d, d, chunk, rc.RET_F32)
     assert 0 < m <= 15 * d * d * 4
+
+
+# ---------------------------------------------------------------- plan override
+def test_plan_override_constants_match_binding():
+    text = open(HEADER).read()
+    consts = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"#define (RET_PATH_\w+) (\d+)", text))
+    assert consts == {"RET_PATH_AUTO": rc.RET_PATH["auto"], "RET_PATH_SLICE": rc.RET_PATH["slice"],
+                      "RET_PATH_SEGMENT": rc.RET_PATH["segment"]}
+
+
+def test_plan_override_sets_the_workspace_plan_and_is_restored():
+    lib = _lib()
+    args = (1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    auto = lib.retention_fwd_workspace_bytes(*args)
+    slot = 128 * 128 * 4
+    assert auto > 0 and auto % (32 * slot) == 0
+    with rc.plan_override(segments=1):
+        assert lib.retention_fwd_workspace_bytes(*args) == 0  # one segment: no partial states
+    with rc.plan_override(segments=3):
+        n3 = lib.retention_fwd_workspace_bytes(*args)  # (G-1) x pieces slots per (b, h)
+        assert n3 > 0 and n3 % (32 * 2 * slot) == 0 and n3 != auto
+    with rc.plan_override(path="slice", segments=1):
+        assert lib.retention_fwd_workspace_bytes(*args) == 0
+    assert lib.retention_fwd_workspace_bytes(*args) == auto  # the context manager restored the automatic plan
+
+
+@pytest.mark.parametrize("kw,code", [(dict(path="diagonal"), None), (dict(segments=-1), -2),
+                                     (dict(walk_nt=3), -2), (dict(lin_chunk=32), -4)])
+def test_plan_override_rejects_bad_values_and_keeps_the_previous_one(kw, code):
+    lib = _lib()
+    args = (1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    auto = lib.retention_fwd_workspace_bytes(*args)
+    rc.set_plan_override(segments=1)
+    try:
+        if code is None:
+            with pytest.raises(ValueError):
+                rc.set_plan_override(**kw)
+        else:
+            with pytest.raises(rc.RetentionError) as ei:
+                rc.set_plan_override(**kw)
+            assert ei.value.code == code
+        assert lib.retention_fwd_workspace_bytes(*args) == 0  # still G = 1
+    finally:
+        rc.set_plan_override()
+    assert lib.retention_fwd_workspace_bytes(*args) == auto
+
+
+def test_plan_override_is_per_thread():
+    import threading
+
+    lib = _lib()
+    args = (1, 32, 65536, 128, 128, 128, rc.RET_BF16)
+    auto = lib.retention_fwd_workspace_bytes(*args)
+    seen = {}
+
+    def other():
+        seen["before"] = lib.retention_fwd_workspace_bytes(*args)
+        rc.set_plan_override(segments=3)
+        seen["after"] = lib.retention_fwd_workspace_bytes(*args)
+
+    with rc.plan_override(segments=1):
+        t = threading.Thread(target=other)
+        t.start()
+        t.join()
+        assert lib.retention_fwd_workspace_bytes(*args) == 0
+    assert seen["before"] == auto and seen["after"] not in (0, auto)
+    assert lib.retention_fwd_workspace_bytes(*args) == auto

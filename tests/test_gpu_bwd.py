@@ -18,6 +18,7 @@ import torch
 import oracle
 import retention_chunkwise_amd as rc
 from retention_chunkwise_amd import workloads as wl
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -34,19 +35,13 @@ def _inputs(seed, dtype, B, H, T, dk, dv, chunk=64):
     return w, inp
 
 
-def _segments(monkeypatch, G):
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
-    if G is None:
-        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
-    else:
-        monkeypatch.setenv("RET_FWD_SEGMENTS", str(G))
+def _segments(plan, G):
+    plan(segments=G)
 
 
 def _check(tag, got, ref, tol):
     for name, x, r in zip(("dq", "dk", "dv"), got, ref):
-        e = oracle.rel_frobenius(x, r)
-        print(f"[parity] {tag} {name}: rel_fro={e:.3e} (tol {tol:.0e})", flush=True)
-        assert e <= tol and np.all(np.isfinite(x)), f"{tag} {name}"
+        parity.check(f"{tag} {name}", x, r, tol)
 
 
 def _run(inp, chunk):
@@ -59,9 +54,9 @@ def _run(inp, chunk):
 @pytest.mark.parametrize("dtype,G", [("f32", None), ("f32", 3), ("bf16", None), ("bf16", 1), ("bf16", 5)])
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 1000), (64, 128, 129), (128, 64, 700)])
-def test_bwd_small_full(dtype, G, chunk, dk, dv, T, monkeypatch):
+def test_bwd_small_full(dtype, G, chunk, dk, dv, T, plan):
     w, inp = _inputs(51, dtype, 2, 3, T, dk, dv, chunk)
-    _segments(monkeypatch, G)
+    _segments(plan, G)
     print(f"[bwd] {dtype} G={G} C={chunk} dk={dk} dv={dv} T={T}", flush=True)
     got = _run(inp, chunk)
     ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"], nthreads=8)
@@ -70,9 +65,9 @@ def test_bwd_small_full(dtype, G, chunk, dk, dv, T, monkeypatch):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T", [1, 5, 64, 65, 127, 128, 129])
-def test_bwd_short_and_ragged(dtype, T, monkeypatch):
+def test_bwd_short_and_ragged(dtype, T, plan):
     w, inp = _inputs(52, dtype, 1, 2, T, 64, 64)
-    _segments(monkeypatch, 2)
+    _segments(plan, 2)
     got = _run(inp, 64)
     ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"])
     _check(f"bwd short {dtype} T={T}", got, ref, TOL[dtype])
@@ -88,18 +83,18 @@ def test_bwd_zero_length_and_empty_batch():
 
 
 @pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
-def test_bwd_gamma_extremes(gval, monkeypatch):
+def test_bwd_gamma_extremes(gval, plan):
     w, inp = _inputs(53, "bf16", 1, 2, 900, 64, 64)
     inp["gamma"] = np.full(2, gval, dtype=np.float32)
-    _segments(monkeypatch, 4)
+    _segments(plan, 4)
     got = _run(inp, 64)
     ref = oracle.retention_bwd(inp["q"], inp["k"], inp["v"], inp["gamma"], inp["do"])
     _check(f"bwd gamma={gval}", got, ref, TOL["bf16"])
 
 
-def test_bwd_long_sequence_two_heads(monkeypatch):
+def test_bwd_long_sequence_two_heads(plan):
     """The [1, 32, 65536, 128] bf16 shape; the oracle checks heads 0 and 31 in full."""
-    _segments(monkeypatch, None)
+    _segments(plan, None)
     w = wl.WORKLOADS["ret_fwd_long_bf16"]
     inp = wl.make_inputs(w, 0)
     g = torch.Generator().manual_seed(54)
@@ -116,8 +111,8 @@ def test_bwd_long_sequence_two_heads(monkeypatch):
         _check(f"bwd long head {h}", got, ref, TOL["bf16"])
 
 
-def test_autograd_wrapper_matches_oracle(monkeypatch):
-    _segments(monkeypatch, None)
+def test_autograd_wrapper_matches_oracle(plan):
+    _segments(plan, None)
     w, inp = _inputs(55, "f32", 2, 2, 300, 64, 128)
     q, k, v = (inp[n].cuda().requires_grad_(True) for n in ("q", "k", "v"))
     out = rc.retention(q, k, v, inp["gamma"], chunk=64)
@@ -131,8 +126,8 @@ def test_autograd_wrapper_matches_oracle(monkeypatch):
     _check("autograd", [t.grad.cpu().numpy() for t in (q, k, v)], ref, TOL["f32"])
 
 
-def test_bwd_deterministic(monkeypatch):
-    _segments(monkeypatch, None)
+def test_bwd_deterministic(plan):
+    _segments(plan, None)
     w, inp = _inputs(56, "bf16", 1, 4, 2000, 128, 128, 128)
     a = _run(inp, 128)
     b = _run(inp, 128)
@@ -163,9 +158,9 @@ def _run_from_fwd(inp, chunk, zero_states=False):
 @pytest.mark.parametrize("dtype,G", [("bf16", None), ("bf16", 3), ("bf16", 5), ("f32", None), ("f32", 3)])
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 1000), (64, 128, 129), (128, 64, 700)])
-def test_bwd_from_fwd_small_full(dtype, G, chunk, dk, dv, T, monkeypatch):
+def test_bwd_from_fwd_small_full(dtype, G, chunk, dk, dv, T, plan):
     w, inp = _inputs(57, dtype, 2, 3, T, dk, dv, chunk)
-    _segments(monkeypatch, G)
+    _segments(plan, G)
     tag = f"bwd_from_fwd {dtype} G={G} C={chunk} dk={dk} dv={dv} T={T}"
     print(f"[bwd] {tag}", flush=True)
     got, _ = _run_from_fwd(inp, chunk)
@@ -180,11 +175,11 @@ def test_bwd_from_fwd_small_full(dtype, G, chunk, dk, dv, T, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_bwd_from_fwd_reads_the_given_states(dtype, monkeypatch):
+def test_bwd_from_fwd_reads_the_given_states(dtype, plan):
     """With the forward's states zeroed, dq loses every earlier segment's share
     and dk, dv are unchanged: the dq walk reads the buffer it is given (segment
     path for bf16, value-slice path for fp32)."""
-    _segments(monkeypatch, 4)
+    _segments(plan, 4)
     w, inp = _inputs(58, dtype, 1, 2, 1024, 64, 64, 64)
     good, n = _run_from_fwd(inp, 64)
     assert n > 0
@@ -195,9 +190,9 @@ def test_bwd_from_fwd_reads_the_given_states(dtype, monkeypatch):
     assert oracle.rel_frobenius(bad[0], good[0].astype(np.float64)) > 0.05
 
 
-def test_bwd_from_fwd_without_forward_workspace(monkeypatch):
+def test_bwd_from_fwd_without_forward_workspace(plan):
     """A one-segment forward leaves no states: the call equals retention_bwd."""
-    _segments(monkeypatch, 1)
+    _segments(plan, 1)
     w, inp = _inputs(59, "bf16", 2, 2, 500, 128, 64, 128)
     q, k, v, do = (inp[n].cuda() for n in ("q", "k", "v", "do"))
     assert rc.retention_fwd_workspace_bytes(2, 2, 500, 128, 64, 128, q.dtype) == 0
@@ -215,9 +210,9 @@ def test_bwd_from_fwd_without_forward_workspace(monkeypatch):
         assert np.array_equal(x.float().cpu().numpy(), y)
 
 
-def test_bwd_from_fwd_long_sequence_two_heads(monkeypatch):
+def test_bwd_from_fwd_long_sequence_two_heads(plan):
     """The [1, 32, 65536, 128] bf16 shape as bench.py runs it; heads 0 and 31 in full."""
-    _segments(monkeypatch, None)
+    _segments(plan, None)
     w = wl.WORKLOADS["ret_fwd_long_bf16"]
     inp = wl.make_inputs(w, 0)
     g = torch.Generator().manual_seed(54)
@@ -237,9 +232,9 @@ def test_bwd_from_fwd_long_sequence_two_heads(monkeypatch):
         _check(f"bwd_from_fwd long head {h}", got, ref, TOL["bf16"])
 
 
-def test_autograd_wrapper_bf16_shares_states(monkeypatch):
+def test_autograd_wrapper_bf16_shares_states(plan):
     """bf16 through torch.autograd: the forward keeps its workspace for backward."""
-    _segments(monkeypatch, 3)
+    _segments(plan, 3)
     w, inp = _inputs(60, "bf16", 1, 2, 900, 64, 64, 64)
     q, k, v = (inp[n].cuda().requires_grad_(True) for n in ("q", "k", "v"))
     out = rc.retention(q, k, v, inp["gamma"], chunk=64)

@@ -16,6 +16,7 @@ import torch
 import oracle
 import retention_chunkwise_amd as rc
 from retention_chunkwise_amd import workloads as wl
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -39,9 +40,8 @@ def _run(inp):
 
 def _check(tag, out, fs, inp):
     ref, ref_s = oracle.gla_recurrent(inp["q"], inp["k"], inp["v"], inp["lg"], nthreads=8)
-    e_o, e_s = oracle.rel_frobenius(out, ref), oracle.rel_frobenius(fs, ref_s)
-    print(f"[parity] {tag}: out {e_o:.3e} state {e_s:.3e} (tol {TOL:.0e})", flush=True)
-    assert e_o <= TOL and e_s <= TOL and np.isfinite(out).all(), tag
+    parity.check(f"{tag} out", out, ref, TOL)
+    parity.check(f"{tag} state", fs, ref_s, TOL)
 
 
 @pytest.mark.parametrize("mu", [3.0, 0.0, -2.0])
@@ -90,8 +90,8 @@ def test_gla_special_cases_match_retention():
 
 
 @pytest.mark.parametrize("G", [1, 3, 7])
-def test_gla_forced_segments(G, monkeypatch):
-    monkeypatch.setenv("RET_FWD_SEGMENTS", str(G))
+def test_gla_forced_segments(G, plan):
+    plan(segments=G)
     w, inp = _inputs(78, 2, 2, 1000, 128, 64, 1.0)
     inp["lg"][:, :, 300:364] = -3.0  # one chunk's worth of strong gates inside a segment
     out, fs = _run(inp)

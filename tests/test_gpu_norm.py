@@ -17,6 +17,7 @@ import torch
 import oracle
 import retention_chunkwise_amd as rc
 from retention_chunkwise_amd import workloads as wl
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -34,12 +35,8 @@ def _inputs(seed, B, H, T, dk, dv, qscale=1.0, dtype="bf16"):
     return w, inp
 
 
-def _run(inp, norm, chunk, monkeypatch, G=None, eps=1e-5):
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
-    if G is None:
-        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
-    else:
-        monkeypatch.setenv("RET_FWD_SEGMENTS", str(G))
+def _run(inp, norm, chunk, plan, G=None, eps=1e-5):
+    plan(segments=G)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     out = rc.retention_fwd_normalized(q, k, v, inp["gamma"], norm=norm, eps=eps, chunk=chunk)
     torch.cuda.synchronize()
@@ -49,52 +46,50 @@ def _run(inp, norm, chunk, monkeypatch, G=None, eps=1e-5):
 def _check(tag, out, inp, norm, eps=1e-5, tol=TOL):
     ref = oracle.retention_normalized(inp["q"], inp["k"], inp["v"], inp["gamma"], group=(norm == "group"), eps=eps,
                                       nthreads=8)
-    e = oracle.rel_frobenius(out, ref)
-    print(f"[parity] {tag}: rel_fro={e:.3e} (tol {tol:.0e})", flush=True)
-    assert e <= tol and np.isfinite(out).all(), tag
+    parity.check(tag, out, ref, tol)
 
 
 @pytest.mark.parametrize("norm", ["rowsum", "group"])
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, None), (1333, 4), (300, 1)])
-def test_norm_small_full(norm, chunk, dk, dv, T, G, monkeypatch):
+def test_norm_small_full(norm, chunk, dk, dv, T, G, plan):
     w, inp = _inputs(61, 2, 3, T, dk, dv, qscale=2.0)
-    out = _run(inp, norm, chunk, monkeypatch, G)
+    out = _run(inp, norm, chunk, plan, G)
     _check(f"norm {norm} C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, norm)
 
 
 @pytest.mark.parametrize("norm", ["rowsum", "group"])
 @pytest.mark.parametrize("T", [1, 5, 64, 65, 129])
-def test_norm_short_and_ragged(norm, T, monkeypatch):
+def test_norm_short_and_ragged(norm, T, plan):
     w, inp = _inputs(62, 1, 2, T, 64, 64, qscale=3.0)
-    out = _run(inp, norm, 64, monkeypatch, 2)
+    out = _run(inp, norm, 64, plan, 2)
     _check(f"norm {norm} short T={T}", out, inp, norm)
 
 
 @pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
 @pytest.mark.parametrize("qscale", [0.05, 20.0])
-def test_norm_gamma_and_floor(gval, qscale, monkeypatch):
+def test_norm_gamma_and_floor(gval, qscale, plan):
     """Small q keeps every row sum under the floor (output = plain retention,
     then GroupNorm); large q puts every row past it."""
     w, inp = _inputs(63, 1, 2, 900, 64, 64, qscale=qscale)
     inp["gamma"] = np.full(2, gval, dtype=np.float32)
     for norm in ("rowsum", "group"):
-        out = _run(inp, norm, 64, monkeypatch, 3)
+        out = _run(inp, norm, 64, plan, 3)
         _check(f"norm {norm} gamma={gval} qscale={qscale}", out, inp, norm)
 
 
-def test_norm_group_eps(monkeypatch):
+def test_norm_group_eps(plan):
     w, inp = _inputs(64, 1, 2, 500, 64, 64, qscale=2.0)
-    out = _run(inp, "group", 64, monkeypatch, None, eps=0.5)
+    out = _run(inp, "group", 64, plan, None, eps=0.5)
     _check("norm group eps=0.5", out, inp, "group", eps=0.5)
 
 
-def test_norm_long_sequence_sampled_heads(monkeypatch):
+def test_norm_long_sequence_sampled_heads(plan):
     """[1, 32, 65536, 128] bf16: heads 0 and 31 against the oracle in full."""
     w = wl.WORKLOADS["ret_fwd_long_bf16"]
     inp = wl.make_inputs(w, 0)
-    out = _run(inp, "group", 128, monkeypatch, None)
+    out = _run(inp, "group", 128, plan, None)
     for h in (0, w.H - 1):
         ref = oracle.retention_normalized(inp["q"][:, h:h + 1], inp["k"][:, h:h + 1], inp["v"][:, h:h + 1],
                                           inp["gamma"][h:h + 1], group=True, eps=1e-5)
@@ -109,44 +104,44 @@ F32_GROUP_SHAPES = [(64, 64, 64), (64, 64, 128), (64, 128, 64), (128, 64, 64)]  
 
 @pytest.mark.parametrize("chunk,dk,dv", F32_GROUP_SHAPES)
 @pytest.mark.parametrize("T,G", [(1000, None), (1333, 4), (300, 1)])
-def test_norm_f32_group(chunk, dk, dv, T, G, monkeypatch):
+def test_norm_f32_group(chunk, dk, dv, T, G, plan):
     w, inp = _inputs(71, 2, 3, T, dk, dv, qscale=2.0, dtype="f32")
-    out = _run(inp, "group", chunk, monkeypatch, G)
+    out = _run(inp, "group", chunk, plan, G)
     _check(f"norm f32 group C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, "group", tol=TOL32)
 
 
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, None), (1333, 4)])
-def test_norm_f32_rowsum(chunk, dk, dv, T, G, monkeypatch):
+def test_norm_f32_rowsum(chunk, dk, dv, T, G, plan):
     w, inp = _inputs(72, 2, 3, T, dk, dv, qscale=2.0, dtype="f32")
-    out = _run(inp, "rowsum", chunk, monkeypatch, G)
+    out = _run(inp, "rowsum", chunk, plan, G)
     _check(f"norm f32 rowsum C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, "rowsum", tol=TOL32)
 
 
 @pytest.mark.parametrize("norm", ["rowsum", "group"])
 @pytest.mark.parametrize("T", [1, 5, 64, 65, 129])
-def test_norm_f32_short_and_ragged(norm, T, monkeypatch):
+def test_norm_f32_short_and_ragged(norm, T, plan):
     w, inp = _inputs(73, 1, 2, T, 64, 64, qscale=3.0, dtype="f32")
-    out = _run(inp, norm, 64, monkeypatch, 2)
+    out = _run(inp, norm, 64, plan, 2)
     _check(f"norm f32 {norm} short T={T}", out, inp, norm, tol=TOL32)
 
 
 @pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
 @pytest.mark.parametrize("qscale", [0.05, 20.0])
-def test_norm_f32_gamma_and_floor(gval, qscale, monkeypatch):
+def test_norm_f32_gamma_and_floor(gval, qscale, plan):
     w, inp = _inputs(74, 1, 2, 900, 64, 64, qscale=qscale, dtype="f32")
     inp["gamma"] = np.full(2, gval, dtype=np.float32)
     for norm in ("rowsum", "group"):
-        out = _run(inp, norm, 64, monkeypatch, 3)
+        out = _run(inp, norm, 64, plan, 3)
         _check(f"norm f32 {norm} gamma={gval} qscale={qscale}", out, inp, norm, tol=TOL32)
 
 
 @pytest.mark.parametrize("chunk,dk,dv", [(64, 128, 128), (128, 64, 128), (128, 128, 64), (128, 128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, None), (700, 3)])
-def test_norm_f32_group_rows_over_slices(chunk, dk, dv, T, G, monkeypatch):
+def test_norm_f32_group_rows_over_slices(chunk, dk, dv, T, G, plan):
     """Shapes whose rows span several value slices: the walk applies the floor
     and a row pass standardises in place."""
     w, inp = _inputs(75, 2, 3, T, dk, dv, qscale=2.0, dtype="f32")
-    out = _run(inp, "group", chunk, monkeypatch, G)
+    out = _run(inp, "group", chunk, plan, G)
     _check(f"norm f32 group (row pass) C={chunk} dk={dk} dv={dv} T={T} G={G}", out, inp, "group", tol=TOL32)

@@ -3,8 +3,8 @@
 The segment path cuts every (b, h) sequence into G segments: one kernel sums
 each full segment's decayed k v^T contributions, the walk kernel starts each
 segment from the decayed sum of the earlier ones.  These cases force the path
-and the segment count through the library's RET_FWD_PATH / RET_FWD_SEGMENTS
-knobs and compare out and the final state with the oracle in full: one and
+and the segment count through the library's plan override
+(retention_set_plan_override) and compare out and the final state with the oracle in full: one and
 several segments, segment counts that do not divide the chunk count, ragged
 last chunks, chunk 64 and 128, every (dk, dv) pair, small and unit decays.
 Tolerance: relative Frobenius error 2e-2 (bf16 inputs, fp32 accumulation).
@@ -16,6 +16,7 @@ import torch
 import oracle
 import retention_chunkwise_amd as rc
 from retention_chunkwise_amd import workloads as wl
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -27,12 +28,8 @@ def _inputs(seed, **over):
     return w, wl.make_inputs(w, seed)
 
 
-def _run(inp, chunk, monkeypatch, path="segment", segments=None):
-    monkeypatch.setenv("RET_FWD_PATH", path)
-    if segments is None:
-        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
-    else:
-        monkeypatch.setenv("RET_FWD_SEGMENTS", str(segments))
+def _run(inp, chunk, plan, path="segment", segments=None):
+    plan(path=path, segments=segments)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     print(f"[segment] chunk={chunk} path={path} G={segments} shape={tuple(q.shape)} dv={v.shape[-1]}",
           flush=True)
@@ -43,48 +40,46 @@ def _run(inp, chunk, monkeypatch, path="segment", segments=None):
 
 def _check(tag, out, fs, inp):
     ref, ref_s = oracle.retention_recurrent(inp["q"], inp["k"], inp["v"], inp["gamma"], nthreads=8)
-    e_o, e_s = oracle.rel_frobenius(out, ref), oracle.rel_frobenius(fs, ref_s)
-    print(f"[parity] {tag}: out {e_o:.3e} state {e_s:.3e} (tol {TOL:.0e})", flush=True)
-    assert e_o <= TOL and e_s <= TOL, tag
-    assert np.isfinite(out).all() and np.isfinite(fs).all()
+    parity.check(f"{tag} out", out, ref, TOL)
+    parity.check(f"{tag} state", fs, ref_s, TOL)
 
 
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, 1), (1000, 3), (1333, 4), (700, 16)])
-def test_segment_small_full(chunk, dk, dv, T, G, monkeypatch):
+def test_segment_small_full(chunk, dk, dv, T, G, plan):
     w, inp = _inputs(seed=11, B=2, H=2, T=T, dk=dk, dv=dv, chunk=chunk, scale=1.0 / np.sqrt(dk))
-    out, fs = _run(inp, chunk, monkeypatch, segments=G)
+    out, fs = _run(inp, chunk, plan, segments=G)
     _check(f"segment C={chunk} dk={dk} dv={dv} T={T} G={G}", out, fs, inp)
 
 
 @pytest.mark.parametrize("T", [1, 37, 128, 129, 255, 256, 257])
-def test_segment_short_and_ragged(T, monkeypatch):
+def test_segment_short_and_ragged(T, plan):
     w, inp = _inputs(seed=12, B=1, H=3, T=T, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
-    out, fs = _run(inp, 128, monkeypatch, segments=2)
+    out, fs = _run(inp, 128, plan, segments=2)
     _check(f"segment short T={T}", out, fs, inp)
 
 
-def test_segment_zero_length(monkeypatch):
+def test_segment_zero_length(plan):
     w, inp = _inputs(seed=13, B=1, H=2, T=0, dk=128, dv=128, chunk=128)
-    out, fs = _run(inp, 128, monkeypatch, segments=4)
+    out, fs = _run(inp, 128, plan, segments=4)
     assert out.size == 0 and np.all(fs == 0.0)
 
 
 @pytest.mark.parametrize("gval", [1.0, 0.5, 0.02])
-def test_segment_gamma_extremes(gval, monkeypatch):
+def test_segment_gamma_extremes(gval, plan):
     w, inp = _inputs(seed=14, B=1, H=2, T=900, dk=64, dv=64, chunk=64, scale=1.0 / 8)
     inp["gamma"] = np.full(w.H, gval, dtype=np.float32)
-    out, fs = _run(inp, 64, monkeypatch, segments=5)
+    out, fs = _run(inp, 64, plan, segments=5)
     _check(f"segment gamma={gval}", out, fs, inp)
 
 
-def test_segment_matches_slice_path_and_is_deterministic(monkeypatch):
+def test_segment_matches_slice_path_and_is_deterministic(plan):
     w, inp = _inputs(seed=15, B=1, H=4, T=2000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
-    o_seg, s_seg = _run(inp, 128, monkeypatch, segments=6)
-    o_seg2, s_seg2 = _run(inp, 128, monkeypatch, segments=6)
+    o_seg, s_seg = _run(inp, 128, plan, segments=6)
+    o_seg2, s_seg2 = _run(inp, 128, plan, segments=6)
     assert np.array_equal(o_seg, o_seg2) and np.array_equal(s_seg, s_seg2), "run-to-run results differ"
-    o_sl, s_sl = _run(inp, 128, monkeypatch, path="slice")
+    o_sl, s_sl = _run(inp, 128, plan, path="slice")
     _check("segment G=6", o_seg, s_seg, inp)
     _check("slice", o_sl, s_sl, inp)
     e = oracle.rel_frobenius(o_seg, o_sl)
@@ -92,20 +87,16 @@ def test_segment_matches_slice_path_and_is_deterministic(monkeypatch):
     assert e <= TOL
 
 
-def test_segment_auto_choice(monkeypatch):
+def test_segment_auto_choice(plan):
     # automatic segment count (several segments for 2 heads x 24 chunks)
     w, inp = _inputs(seed=16, B=1, H=2, T=3000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
-    out, fs = _run(inp, 128, monkeypatch, segments=None)
+    out, fs = _run(inp, 128, plan, segments=None)
     _check("segment auto", out, fs, inp)
 
 
 # ------------------------------------------------------------- elu+1 linear attention
-def _run_lin(inp, monkeypatch, path="segment", segments=None):
-    monkeypatch.setenv("RET_FWD_PATH", path)
-    if segments is None:
-        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
-    else:
-        monkeypatch.setenv("RET_FWD_SEGMENTS", str(segments))
+def _run_lin(inp, plan, path="segment", segments=None):
+    plan(path=path, segments=segments)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     print(f"[segment] linattn path={path} G={segments} shape={tuple(q.shape)} dv={v.shape[-1]}", flush=True)
     out = rc.linear_attn_fwd(q, k, v)
@@ -115,35 +106,33 @@ def _run_lin(inp, monkeypatch, path="segment", segments=None):
 
 def _check_lin(tag, out, inp):
     ref, _, _ = oracle.linattn_recurrent(inp["q"], inp["k"], inp["v"], nthreads=8)
-    e = oracle.rel_frobenius(out, ref)
-    print(f"[parity] {tag}: out {e:.3e} (tol {TOL:.0e})", flush=True)
-    assert e <= TOL and np.isfinite(out).all(), tag
+    parity.check(f"{tag} out", out, ref, TOL)
 
 
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, 1), (1333, 3), (2000, 8)])
-def test_segment_linattn_full(dk, dv, T, G, monkeypatch):
+def test_segment_linattn_full(dk, dv, T, G, plan):
     w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=2, T=T, dk=dk, dv=dv)
     inp = wl.make_inputs(w, 21)
-    out = _run_lin(inp, monkeypatch, segments=G)
+    out = _run_lin(inp, plan, segments=G)
     _check_lin(f"linattn segment dk={dk} dv={dv} T={T} G={G}", out, inp)
 
 
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 129, 300])
-def test_segment_linattn_short_and_ragged(T, monkeypatch):
+def test_segment_linattn_short_and_ragged(T, plan):
     w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=1, H=3, T=T)
     inp = wl.make_inputs(w, 22)
-    out = _run_lin(inp, monkeypatch, segments=2)
+    out = _run_lin(inp, plan, segments=2)
     _check_lin(f"linattn segment short T={T}", out, inp)
 
 
-def test_segment_linattn_matches_slice_path(monkeypatch):
+def test_segment_linattn_matches_slice_path(plan):
     w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=4, T=1500)
     inp = wl.make_inputs(w, 23)
-    o_seg = _run_lin(inp, monkeypatch, segments=5)
-    o_seg2 = _run_lin(inp, monkeypatch, segments=5)
+    o_seg = _run_lin(inp, plan, segments=5)
+    o_seg2 = _run_lin(inp, plan, segments=5)
     assert np.array_equal(o_seg, o_seg2), "run-to-run results differ"
-    o_sl = _run_lin(inp, monkeypatch, path="slice")
+    o_sl = _run_lin(inp, plan, path="slice")
     _check_lin("linattn segment G=5", o_seg, inp)
     _check_lin("linattn slice", o_sl, inp)
     e = oracle.rel_frobenius(o_seg, o_sl)
@@ -152,11 +141,9 @@ def test_segment_linattn_matches_slice_path(monkeypatch):
 
 
 # ------------------------------------------------------------- caller workspace
-def test_caller_workspace_contents_do_not_matter(monkeypatch):
+def test_caller_workspace_contents_do_not_matter(plan):
     """A caller-owned workspace filled with garbage gives the same bits as a
     fresh one; a workspace one byte short is refused."""
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
-    monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
     w, inp = _inputs(seed=17, B=1, H=4, T=4000, dk=128, dv=128, chunk=128, scale=1.0 / np.sqrt(128))
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     need = rc.retention_fwd_workspace_bytes(1, 4, 4000, 128, 128, 128, torch.bfloat16)
@@ -187,11 +174,11 @@ def test_caller_workspace_contents_do_not_matter(monkeypatch):
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, 2), (1333, 5), (700, 16)])
-def test_slice_segments_full(dtype, chunk, dk, dv, T, G, monkeypatch):
+def test_slice_segments_full(dtype, chunk, dk, dv, T, G, plan):
     """The value-slice walk split into G segments (fp32 picks G by itself;
     bf16 only when forced), against the oracle in full."""
     w, inp = _inputs(seed=18, B=2, H=2, T=T, dk=dk, dv=dv, chunk=chunk, scale=1.0 / np.sqrt(dk), dtype=dtype)
-    out, fs = _run(inp, chunk, monkeypatch, path="slice", segments=G)
+    out, fs = _run(inp, chunk, plan, path="slice", segments=G)
     tol = 1e-4 if dtype == "f32" else TOL
     ref, ref_s = oracle.retention_recurrent(inp["q"], inp["k"], inp["v"], inp["gamma"], nthreads=8)
     e_o, e_s = oracle.rel_frobenius(out, ref), oracle.rel_frobenius(fs, ref_s)
@@ -202,10 +189,10 @@ def test_slice_segments_full(dtype, chunk, dk, dv, T, G, monkeypatch):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("dk,dv", [(64, 64), (128, 128)])
 @pytest.mark.parametrize("T,G", [(1000, 3), (300, 16)])
-def test_slice_segments_linattn(dtype, dk, dv, T, G, monkeypatch):
+def test_slice_segments_linattn(dtype, dk, dv, T, G, plan):
     w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=2, T=T, dk=dk, dv=dv, dtype=dtype)
     inp = wl.make_inputs(w, 25)
-    out = _run_lin(inp, monkeypatch, path="slice", segments=G)
+    out = _run_lin(inp, plan, path="slice", segments=G)
     ref, _, _ = oracle.linattn_recurrent(inp["q"], inp["k"], inp["v"], nthreads=8)
     e = oracle.rel_frobenius(out, ref)
     tol = 1e-4 if dtype == "f32" else TOL
@@ -213,11 +200,11 @@ def test_slice_segments_linattn(dtype, dk, dv, T, G, monkeypatch):
     assert e <= tol and np.isfinite(out).all()
 
 
-def test_f32_auto_segments_match_one_segment(monkeypatch):
+def test_f32_auto_segments_match_one_segment(plan):
     """fp32 automatic segments against the forced single-segment walk."""
     w, inp = _inputs(seed=19, B=4, H=8, T=2048, dk=64, dv=64, chunk=64, scale=1.0 / 8, dtype="f32")
-    o_auto, s_auto = _run(inp, 64, monkeypatch, path="slice", segments=None)
-    o_one, s_one = _run(inp, 64, monkeypatch, path="slice", segments=1)
+    o_auto, s_auto = _run(inp, 64, plan, path="slice", segments=None)
+    o_one, s_one = _run(inp, 64, plan, path="slice", segments=1)
     e_o, e_s = oracle.rel_frobenius(o_auto, o_one), oracle.rel_frobenius(s_auto, s_one)
     print(f"[parity] f32 auto vs one segment: out {e_o:.3e} state {e_s:.3e}", flush=True)
     assert e_o <= 1e-5 and e_s <= 1e-5

@@ -18,24 +18,18 @@ import torch
 import oracle
 import retention_chunkwise_amd as rc
 from retention_chunkwise_amd import workloads as wl
+from tests import parity
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def _path(monkeypatch, path, segments):
-    monkeypatch.setenv("RET_FWD_PATH", path)
-    if segments is None:
-        monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
-    else:
-        monkeypatch.setenv("RET_FWD_SEGMENTS", str(segments))
+def _path(plan, path, segments):
+    plan(path=path, segments=segments)
 
 
-def _report(tag, got, ref, tol):
-    e = oracle.rel_frobenius(got, ref)
-    print(f"[parity] {tag}: rel_fro={e:.3e} (tol {tol:.0e})", flush=True)
-    assert e <= tol and np.all(np.isfinite(got)), tag
+_report = parity.check
 
 
 def _ret_inputs(seed, dtype, B, H, T, dk, dv, chunk):
@@ -55,9 +49,9 @@ PATHS = [("f32", "slice", None), ("bf16", "slice", None), ("bf16", "segment", 1)
 @pytest.mark.parametrize("dtype,path,G", PATHS)
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 1000), (64, 128, 129), (128, 64, 700)])
-def test_ret_fwd_from_state_full(dtype, path, G, chunk, dk, dv, T, monkeypatch):
+def test_ret_fwd_from_state_full(dtype, path, G, chunk, dk, dv, T, plan):
     w, inp = _ret_inputs(31, dtype, 2, 3, T, dk, dv, chunk)
-    _path(monkeypatch, path, G)
+    _path(plan, path, G)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     print(f"[state] retention {dtype} {path} G={G} C={chunk} dk={dk} dv={dv} T={T}", flush=True)
     out, fs = rc.retention_fwd(q, k, v, inp["gamma"], chunk=chunk, initial_state=inp["S0"].cuda())
@@ -70,9 +64,9 @@ def test_ret_fwd_from_state_full(dtype, path, G, chunk, dk, dv, T, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype,path,G", PATHS)
-def test_ret_fwd_from_state_zero_length_copies_state(dtype, path, G, monkeypatch):
+def test_ret_fwd_from_state_zero_length_copies_state(dtype, path, G, plan):
     w, inp = _ret_inputs(32, dtype, 1, 2, 0, 128, 64, 64)
-    _path(monkeypatch, path, G)
+    _path(plan, path, G)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     _, fs = rc.retention_fwd(q, k, v, inp["gamma"], chunk=64, initial_state=inp["S0"].cuda())
     torch.cuda.synchronize()
@@ -80,10 +74,10 @@ def test_ret_fwd_from_state_zero_length_copies_state(dtype, path, G, monkeypatch
 
 
 @pytest.mark.parametrize("gval", [1.0, 0.5])
-def test_ret_fwd_from_state_gamma_extremes(gval, monkeypatch):
+def test_ret_fwd_from_state_gamma_extremes(gval, plan):
     w, inp = _ret_inputs(33, "bf16", 1, 2, 1500, 64, 64, 64)
     inp["gamma"] = np.full(2, gval, dtype=np.float32)
-    _path(monkeypatch, "segment", 6)
+    _path(plan, "segment", 6)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     out, fs = rc.retention_fwd(q, k, v, inp["gamma"], chunk=64, initial_state=inp["S0"].cuda())
     torch.cuda.synchronize()
@@ -93,10 +87,8 @@ def test_ret_fwd_from_state_gamma_extremes(gval, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_ret_chunked_prefill_matches_one_call(dtype, monkeypatch):
+def test_ret_chunked_prefill_matches_one_call(dtype, plan):
     """A sequence run in pieces, each from the previous piece's final state."""
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
-    monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
     w, inp = _ret_inputs(34, dtype, 1, 4, 3000, 128, 128, 128)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     cuts = [0, 1000, 1777, 1800, 3000]
@@ -133,9 +125,9 @@ LIN_PATHS = [("f32", "slice", None), ("bf16", "slice", None), ("bf16", "segment"
 
 @pytest.mark.parametrize("dtype,path,G", LIN_PATHS)
 @pytest.mark.parametrize("dk,dv,T", [(64, 64, 300), (128, 64, 1000), (64, 128, 129), (128, 128, 700)])
-def test_linattn_from_state_full(dtype, path, G, dk, dv, T, monkeypatch):
+def test_linattn_from_state_full(dtype, path, G, dk, dv, T, plan):
     inp = _lin_inputs(41, dtype, 2, 2, T, dk, dv)
-    _path(monkeypatch, path, G)
+    _path(plan, path, G)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     print(f"[state] linattn {dtype} {path} G={G} dk={dk} dv={dv} T={T}", flush=True)
     out, S, z = rc.linear_attn_fwd(q, k, v, initial_state=(inp["S0"].cuda(), inp["z0"].cuda()),
@@ -150,9 +142,9 @@ def test_linattn_from_state_full(dtype, path, G, dk, dv, T, monkeypatch):
 
 
 @pytest.mark.parametrize("dtype,path,G", LIN_PATHS)
-def test_linattn_returns_state_from_zero(dtype, path, G, monkeypatch):
+def test_linattn_returns_state_from_zero(dtype, path, G, plan):
     inp = _lin_inputs(42, dtype, 1, 3, 500, 64, 64)
-    _path(monkeypatch, path, G)
+    _path(plan, path, G)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     out, S, z = rc.linear_attn_fwd(q, k, v, return_state=True)
     plain = rc.linear_attn_fwd(q, k, v)
@@ -164,9 +156,8 @@ def test_linattn_returns_state_from_zero(dtype, path, G, monkeypatch):
     assert torch.equal(out, plain), "returning the state changed the output"
 
 
-def test_linattn_from_state_zero_length_copies_state(monkeypatch):
+def test_linattn_from_state_zero_length_copies_state(plan):
     inp = _lin_inputs(43, "bf16", 1, 2, 0, 128, 64)
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
     q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
     _, S, z = rc.linear_attn_fwd(q, k, v, initial_state=(inp["S0"].cuda(), inp["z0"].cuda()), return_state=True)
     torch.cuda.synchronize()
@@ -189,8 +180,10 @@ def test_linattn_decode_small(dtype, dk, dv):
     _report(f"phi decode {dtype} {dk}x{dv} z", z.cpu().numpy(), rz, 1e-4)
 
 
-def test_linattn_decode_full_size_1000_steps_sampled():
-    """256 sequences x 32 heads, 128 x 128 state, 1000 steps of one token."""
+def test_linattn_decode_full_size_1000_steps_whole_tensor():
+    """256 sequences x 32 heads, 128 x 128 state, 1000 steps of one token:
+    every S, z and output after the last step against the oracle's 1000
+    steps, 8 heads (2048 pairs) at a time."""
     N, H, d, steps = 256, 32, 128, 1000
     g = torch.Generator().manual_seed(45)
     q, k, v = (torch.randn((N, H, d), generator=g) / np.sqrt(d)).to(torch.bfloat16), \
@@ -205,25 +198,26 @@ def test_linattn_decode_full_size_1000_steps_sampled():
         out = rc.linear_attn_decode_step(qd, kd, vd, S, z)
     torch.cuda.synchronize()
     st, zt, o = S.cpu().numpy(), z.cpu().numpy(), out.float().cpu().numpy()
-    rng = np.random.default_rng(3)
-    pairs = sorted({(int(rng.integers(N)), int(rng.integers(H))) for _ in range(12)} | {(0, 0), (N - 1, H - 1)})
-    for n, h in pairs:
-        sl = (slice(n, n + 1), slice(h, h + 1))
-        ro, rS, rz = oracle.linattn_decode_steps(q[sl], k[sl], v[sl], S0[sl], z0[sl], nsteps=steps)
-        e_s = oracle.rel_frobenius(st[sl], rS)
-        e_z = oracle.rel_frobenius(zt[sl], rz)
-        e_o = oracle.rel_frobenius(o[sl], ro)
-        print(f"[parity] phi decode 1000 steps seq {n} head {h}: S {e_s:.2e} z {e_z:.2e} out {e_o:.2e}",
-              flush=True)
-        assert e_s <= 1e-4 and e_z <= 1e-4 and e_o <= TOL["bf16"]
+    acc_s = parity.HeadGroups("phi decode 1000 steps S", 1e-4)
+    acc_z = parity.HeadGroups("phi decode 1000 steps z", 1e-4)
+    acc_o = parity.HeadGroups("phi decode 1000 steps out", TOL["bf16"])
+    for h0 in range(0, H, 8):
+        sl = (slice(None), slice(h0, h0 + 8))
+        ro, rS, rz = oracle.linattn_decode_steps(q[sl], k[sl], v[sl], S0[sl], z0[sl], nsteps=steps, nthreads=16)
+        per = acc_s.add(st[sl], rS, h0)
+        acc_z.add(zt[sl], rz, h0)
+        acc_o.add(o[sl], ro, h0)
+        print(f"[parity] phi decode heads {h0}..{h0 + 7}: worst S per head " +
+              " ".join(f"{e:.1e}" for e in per.max(axis=0)), flush=True)
+    acc_s.finish()
+    acc_z.finish()
+    acc_o.finish()
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_linattn_prefill_then_decode_handoff(dtype, monkeypatch):
+def test_linattn_prefill_then_decode_handoff(dtype, plan):
     """Prefill T0 tokens, then decode the rest one token at a time: the
     decoded outputs are the last rows of one forward over all tokens."""
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
-    monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
     w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=2, T=1300, dk=64, dv=64, dtype=dtype)
     inp = wl.make_inputs(w, 46)
     T0, n = 1290, 10
@@ -242,9 +236,7 @@ def test_linattn_prefill_then_decode_handoff(dtype, monkeypatch):
     _report(f"phi handoff {dtype} z", z.cpu().numpy(), rz, TOL[dtype])
 
 
-def test_linattn_chunked_prefill_matches_one_call(monkeypatch):
-    monkeypatch.delenv("RET_FWD_PATH", raising=False)
-    monkeypatch.delenv("RET_FWD_SEGMENTS", raising=False)
+def test_linattn_chunked_prefill_matches_one_call(plan):
     w = wl.WORKLOADS["linattn_elu1_bf16"].with_(B=2, H=4, T=3000)
     inp = wl.make_inputs(w, 47)
     q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
