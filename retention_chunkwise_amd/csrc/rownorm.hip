@@ -5,7 +5,9 @@
 // (x - mean) / sqrt(var + eps), population variance, no gain or bias: the
 // reading of the RetNet layer's optional GroupNorm with one group per head.
 // One wave per row, grid-stride; dv / 64 values per lane, reductions by
-// cross-lane shuffles.  Statistics in fp32, as in the fused walks.
+// cross-lane shuffles.  Statistics in fp32, as in the fused walks; the row is
+// in registers, so the variance takes two passes (mean, then squared
+// deviations), exact for rows whose mean is large against their spread.
 #include "internal.h"
 
 namespace ret {
@@ -22,21 +24,21 @@ __global__ void __launch_bounds__(kRowThreads) group_norm_rows_kernel(float* out
     for (long long r = wave; r < rows; r += waves) {
         float* row = out + r * DV;
         float x[PER];
-        float s1 = 0.f, s2 = 0.f;
+        float s1 = 0.f;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             x[i] = row[lane + 64 * i];
             s1 += x[i];
-            s2 += x[i] * x[i];
         }
 #pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) {
-            s1 += __shfl_xor(s1, o);
-            s2 += __shfl_xor(s2, o);
-        }
+        for (int o = 32; o >= 1; o >>= 1) s1 += __shfl_xor(s1, o);
         const float mu = s1 * (1.f / DV);
-        const float var = fmaxf(s2 * (1.f / DV) - mu * mu, 0.f);
-        const float rstd = 1.f / sqrtf(var + eps);
+        float s2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) s2 += (x[i] - mu) * (x[i] - mu);
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) s2 += __shfl_xor(s2, o);
+        const float rstd = 1.f / sqrtf(s2 * (1.f / DV) + eps);
 #pragma unroll
         for (int i = 0; i < PER; ++i) row[lane + 64 * i] = (x[i] - mu) * rstd;
     }

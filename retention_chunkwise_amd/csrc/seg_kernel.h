@@ -656,10 +656,13 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                         if (jt <= its(s)) pacc[s][jt] = mfma_bf16(ka[jt], qp[s][ks], pacc[s][jt]);
             }
 
-            // ---- decay mask, bf16 P^T operands (two key tiles per operand)
+            // ---- decay mask, bf16 P^T operands (two key tiles per operand);
+            // the row-sum floor sums the fp32 weights before their rounding
             bf16x8 pb[NS][NB];
+            float psum[NS];
 #pragma unroll
-            for (int s = 0; s < NS; ++s)
+            for (int s = 0; s < NS; ++s) {
+                psum[s] = 0.f;
 #pragma unroll
                 for (int js = 0; js < NB; ++js)
                     if (2 * js <= its(s)) {
@@ -673,21 +676,29 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 #pragma unroll
                             for (int r = 0; r < 4; ++r) hi[r] *= (d1 == 0) ? f0[r] : gd[d1] * f1[r];
                         }
+                        if constexpr (NRM) psum[s] += (lo[0] + lo[1]) + (lo[2] + lo[3]) + ((hi[0] + hi[1]) + (hi[2] + hi[3]));
                         pb[s][js] = cat_bf16(cvt4_bf16(lo), cvt4_bf16(hi));
                     }
+            }
 
-            // ---- per-query divisors: the row sum of P (the bf16 weights the
-            // numerator uses) plus the earlier tokens' share, q . z_prev (decayed
-            // by xi for retention).  Linear attention: 1 / (sum + eps); the
-            // row-sum floor: 1 / max(|sum|, 1).
+            // ---- per-query divisors: the row sum of P plus the earlier tokens'
+            // share, q . z_prev (decayed by xi for retention).  Linear attention:
+            // 1 / (sum + eps) with the bf16 weights the numerator uses (all
+            // positive, so the quotient stays a weighted mean of the values);
+            // the row-sum floor: 1 / max(|sum|, 1) with the fp32 weights (signed
+            // weights cancel, and their rounding errors must not).
             float rden[NS];
             if constexpr (ZN) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     float tp = 0.f, tz = 0.f;
+                    if constexpr (LIN) {
 #pragma unroll
-                    for (int js = 0; js < NB; ++js)
-                        if (2 * js <= its(s)) tp += sum8(pb[s][js]);
+                        for (int js = 0; js < NB; ++js)
+                            if (2 * js <= its(s)) tp += sum8(pb[s][js]);
+                    } else {
+                        tp = psum[s];
+                    }
 #pragma unroll
                     for (int ks = 0; ks < QF; ++ks) {
                         const u16x8 e = __builtin_bit_cast(u16x8, qp[s][ks]);
@@ -757,31 +768,51 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             if constexpr (GRP) {
                 // GroupNorm needs a whole row before any of it is stored, and the
                 // row does not fit in registers beside everything else: the first
-                // pass only sums each row (and its squares) over the value tiles,
-                // the second recomputes the products and stores standardised values.
-                float s1[NS], s2[NS];
-#pragma unroll
-                for (int s = 0; s < NS; ++s) s1[s] = s2[s] = 0.f;
+                // pass only gathers each row's statistics over the value tiles, the
+                // second recomputes the products and stores standardised values.
+                // Statistics: per pair of value tiles the lane's 8 values give a
+                // mean and a sum of squared deviations, merged into the running
+                // pair by Chan's pairwise update, then across the four lane groups
+                // the same way; no E[x^2] - mean^2 cancellation.
+                float mean[NS], m2[NS];
 #pragma unroll
                 for (int pa = 0; pa < NPAIR; ++pa) {
                     f32x4 oacc[NS][2];
                     pair_out(pa, oacc);
 #pragma unroll
-                    for (int s = 0; s < NS; ++s)
+                    for (int s = 0; s < NS; ++s) {
+                        const f32x4 t = oacc[s][0] + oacc[s][1];
+                        const float mb = ((t[0] + t[1]) + (t[2] + t[3])) * 0.125f;
+                        const f32x4 d0 = oacc[s][0] - mb, d1 = oacc[s][1] - mb;
+                        float qb = 0.f;
 #pragma unroll
-                        for (int b = 0; b < 2; ++b)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                s1[s] += oacc[s][b][r];
-                                s2[s] += oacc[s][b][r] * oacc[s][b][r];
-                            }
+                        for (int r = 0; r < 4; ++r) qb += d0[r] * d0[r] + d1[r] * d1[r];
+                        if (pa == 0) {
+                            mean[s] = mb;
+                            m2[s] = qb;
+                        } else {
+                            // counts 8 pa (running) and 8 (this pair)
+                            const float dl = mb - mean[s], wb = 1.f / static_cast<float>(pa + 1);
+                            mean[s] += dl * wb;
+                            m2[s] += qb + dl * dl * (8.f * static_cast<float>(pa) * wb);
+                        }
+                    }
                 }
                 float mu[NS], rstd[NS];
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    mu[s] = sum_over_groups(s1[s]) * (1.f / DV);
-                    const float var = fmaxf(sum_over_groups(s2[s]) * (1.f / DV) - mu[s] * mu[s], 0.f);
-                    rstd[s] = 1.f / sqrtf(var + a.gn_eps);
+                    // merge equal counts: n = 8 NPAIR per lane, then 16 NPAIR
+                    float m = mean[s], q2 = m2[s], n = 8.f * NPAIR;
+#pragma unroll
+                    for (int x = 16; x <= 32; x <<= 1) {
+                        const float mo = __shfl_xor(m, x), qo = __shfl_xor(q2, x);
+                        const float dl = mo - m;
+                        q2 += qo + dl * dl * (0.5f * n);
+                        m = 0.5f * (m + mo);
+                        n *= 2.f;
+                    }
+                    mu[s] = m;
+                    rstd[s] = 1.f / sqrtf(q2 * (1.f / DV) + a.gn_eps);
                 }
 #pragma unroll
                 for (int pa = 0; pa < NPAIR; ++pa) {

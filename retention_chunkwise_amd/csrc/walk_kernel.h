@@ -695,24 +695,29 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
             }
         }
         // GroupNorm over each output row (the slice holds whole rows): lanes
-        // l, l^16, l^32, l^48 hold the row's four column groups
+        // l, l^16, l^32, l^48 hold the row's four column groups.  The row is
+        // in registers, so the variance takes two passes (mean, then squared
+        // deviations), which stays exact for rows whose mean dwarfs their spread.
         float mu[NS], rstd[NS];
         if constexpr (GRP) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                float s1 = 0.f, s2 = 0.f;
+                float s1 = 0.f;
 #pragma unroll
                 for (int nt = 0; nt < NT; ++nt) {
                     const f32x4 o = oacc[s][nt] * rden[s];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        s1 += o[r];
-                        s2 += o[r] * o[r];
-                    }
+                    for (int r = 0; r < 4; ++r) s1 += o[r];
                 }
                 mu[s] = sum_over_groups(s1) * (1.f / Cf::DVS);
-                const float var = fmaxf(sum_over_groups(s2) * (1.f / Cf::DVS) - mu[s] * mu[s], 0.f);
-                rstd[s] = 1.f / sqrtf(var + a.gn_eps);
+                float s2 = 0.f;
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const f32x4 o = oacc[s][nt] * rden[s] - mu[s];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s2 += o[r] * o[r];
+                }
+                rstd[s] = 1.f / sqrtf(sum_over_groups(s2) * (1.f / Cf::DVS) + a.gn_eps);
             }
         }
         {
