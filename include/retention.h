@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define RET_ABI_VERSION 10
+#define RET_ABI_VERSION 11
 
 /* element types of q, k, v, out */
 #define RET_F32 0
@@ -124,6 +124,33 @@ int retention_fwd(const void *q, const void *k, const void *v, const float *gamm
  * size serves retention_fwd_from_state. */
 size_t retention_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int chunk,
                                      int dtype);
+
+/*
+ * retention_fwd_noalloc -- retention_fwd for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, hosts that forbid allocation.  Same arguments and results as
+ * retention_fwd (bit for bit: the same kernels and plan), without `workspace`
+ * and `ws_bytes`.  The partial segment states live in a device array of the
+ * library instead, RET_NOALLOC_MAX_WORKSPACE bytes on each GPU it runs on,
+ * held from the first call on that GPU until the process ends.  The call
+ * allocates nothing (no hipMalloc, no library allocation).
+ *
+ *   - Sizes whose segment states need more than RET_NOALLOC_MAX_WORKSPACE
+ *     bytes (retention_fwd_workspace_bytes(...) tells) return
+ *     RET_ERR_WORKSPACE; use retention_fwd with a workspace for those.  The
+ *     [1, 32, 65536, 128] bf16 forward needs 14.7 MB.
+ *   - Every call on one GPU shares the array: calls that overlap in time on
+ *     one GPU (several streams, several host threads) race and give wrong
+ *     outputs.  Calls ordered on one stream are safe.  Its contents between
+ *     calls do not matter (each call writes the states before reading them).
+ *   - The device is the one that runs `stream` (the current device for NULL).
+ *     Its first call on a device looks up the array's address there
+ *     (RET_ERR_HIP if that fails).
+ */
+#define RET_NOALLOC_MAX_WORKSPACE 33554432 /* bytes of segment states per GPU (32 MiB) */
+int retention_fwd_noalloc(const void *q, const void *k, const void *v, const float *gamma, int chunk,
+                          void *out, float *final_state, int B, int H, int T, int dk, int dv,
+                          int dtype, void *stream);
 
 /*
  * retention_fwd_from_state -- retention_fwd continued from a given state S0

@@ -11,6 +11,7 @@ call raises.
 Functions
 ---------
 retention_fwd(q, k, v, gamma, chunk=64, initial_state=None) -> (out, final_state)
+retention_fwd_noalloc(q, k, v, gamma, chunk=64) -> (out, final_state)   (no workspace: library device array)
 retention_decode_step(q, k, v, gamma, state)   -> out      (state updated in place)
 linear_attn_fwd(q, k, v, phi="elu1", eps=1e-6) -> out
 linear_attn_fwd(..., initial_state=(S, z), return_state=True) -> (out, S, z)
@@ -38,7 +39,7 @@ import threading
 import numpy as np
 import torch
 
-__all__ = ["retention_fwd", "retention_bwd", "retention", "retention_decode_step", "linear_attn_fwd",
+__all__ = ["retention_fwd", "retention_fwd_noalloc", "retention_bwd", "retention", "retention_decode_step", "linear_attn_fwd",
            "linear_attn_decode_step", "retention_bwd_workspace_bytes", "retention_fwd_normalized",
            "retention_fwd_normalized_workspace_bytes", "gla_fwd", "RET_NORM_ROWSUM", "RET_NORM_GROUP",
            "retention_fwd_workspace_bytes",
@@ -94,6 +95,8 @@ def load_library():
             lib.retention_decode_step.argtypes = [vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp]
             lib.retention_decode_step.restype = i
             lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
+            lib.retention_fwd_noalloc.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp]
+            lib.retention_fwd_noalloc.restype = i
             lib.retention_fwd_from_state.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
             lib.retention_fwd_from_state.restype = i
             lib.linear_attn_fwd_from_state.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i,
@@ -286,6 +289,32 @@ def retention_fwd(q, k, v, gamma, chunk: int = 64, out=None, final_state=None,
         rc = lib.retention_fwd_from_state(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk),
                                           initial_state.data_ptr(), out.data_ptr(), _ptr(final_state),
                                           B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
+    _raise(rc)
+    return out, final_state
+
+
+def retention_fwd_noalloc(q, k, v, gamma, chunk: int = 64, out=None, final_state=None, want_state: bool = True):
+    """retention_fwd without a workspace: the library keeps the segment states
+    in its own device array (RET_NOALLOC_MAX_WORKSPACE bytes per GPU), so the
+    C call allocates nothing.  Pass `out` (and `final_state`) to keep this
+    wrapper from allocating them.  Calls that overlap in time on one GPU race."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,T,dk] and v [B,H,T,dv]")
+    B, H, T, dk = q.shape
+    dv = v.shape[3]
+    if out is None:
+        out = torch.empty_like(v)
+    _check_dev("out", out, v.dtype)
+    if final_state is None and want_state:
+        final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _check_dev("final_state", final_state, torch.float32)
+    g = _gamma_array(gamma, H)
+    rc = lib.retention_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), g, int(chunk), out.data_ptr(),
+                                   _ptr(final_state), B, H, T, dk, dv, _dtype_code(q), _stream(q))
     _raise(rc)
     return out, final_state
 

@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/retention.h"
 #include "internal.h"
@@ -389,10 +390,55 @@ int check_state_arg(const char* fn, const char* name, const void* p, size_t byte
     return RET_OK;
 }
 
-// Shared by retention_fwd and retention_fwd_from_state.
+}  // namespace
+
+// ---- allocation-free forward: the segment states live in a device array of
+// the library, not in a caller workspace.  Each GPU the library runs on holds
+// its own copy from the first use until the process ends; every call on that
+// GPU shares it, so calls that overlap in time on one GPU race.  The segment
+// states are written before they are read, so nothing needs clearing between
+// calls.
+constexpr size_t kScratchBytes = static_cast<size_t>(RET_NOALLOC_MAX_WORKSPACE);
+static_assert(kScratchBytes == (size_t{32} << 20), "the header states 32 MiB");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the device that runs `stream` (looked up once
+// per device, with that device current).  The array's host-side name is a
+// stand-in, not a device address: kernels get this pointer instead.
+int scratch_for(const char* fn, hipStream_t stream, void** ptr) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: no device for the stream: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices) return fail(RET_ERR_HIP, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return fail(RET_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(RET_ERR_HIP, "%s: hipSetDevice(%d) failed: %s", fn, dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) static_cast<void>(hipSetDevice(cur));  // the address is known; restoring is best effort
+        if (e != hipSuccess || !p)
+            return fail(RET_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", fn, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return RET_OK;
+}
+
+// Shared by retention_fwd, retention_fwd_from_state and retention_fwd_noalloc
+// (use_scratch: the workspace is the library's device array, not the caller's).
 int ret_fwd_impl(const char* fn, const void* q, const void* k, const void* v, const float* gamma, int chunk,
                  const float* initial_state, void* out, float* final_state, int B, int H, int T, int dk, int dv,
-                 int dtype, void* workspace, size_t ws_bytes, void* stream) {
+                 int dtype, void* workspace, size_t ws_bytes, void* stream, bool use_scratch = false) {
     if (!gamma) return fail(RET_ERR_NULL, "%s: gamma must be non-NULL", fn);
     const int esz = dtype_size(dtype);
     if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
@@ -432,6 +478,15 @@ int ret_fwd_impl(const char* fn, const void* q, const void* k, const void* v, co
     SegPlan plan;
     if (!plan_fwd(bh, T, chunk, dk, dv, false, dtype, &plan))
         return fail(RET_ERR_SHAPE, "%s: workspace size overflows", fn);
+    if (use_scratch && plan.ws_bytes > 0) {
+        if (plan.ws_bytes > kScratchBytes)
+            return fail(RET_ERR_WORKSPACE,
+                        "%s: these sizes need %zu bytes of segment states, more than the library's %zu-byte device "
+                        "array; call retention_fwd with a workspace instead",
+                        fn, plan.ws_bytes, kScratchBytes);
+        if ((rc = scratch_for(fn, st, &workspace))) return rc;
+        ws_bytes = kScratchBytes;
+    }
     rc = check_workspace(fn, plan, workspace, ws_bytes,
                          {rq, rk, rv, ro, final_state ? range("final_state", final_state, ns) : none, ri});
     if (rc) return rc;
@@ -649,6 +704,12 @@ int retention_fwd(const void* q, const void* k, const void* v, const float* gamm
                   void* workspace, size_t ws_bytes, void* stream) {
     return ret_fwd_impl("retention_fwd", q, k, v, gamma, chunk, nullptr, out, final_state, B, H, T, dk, dv, dtype,
                         workspace, ws_bytes, stream);
+}
+
+int retention_fwd_noalloc(const void* q, const void* k, const void* v, const float* gamma, int chunk, void* out,
+                          float* final_state, int B, int H, int T, int dk, int dv, int dtype, void* stream) {
+    return ret_fwd_impl("retention_fwd_noalloc", q, k, v, gamma, chunk, nullptr, out, final_state, B, H, T, dk, dv,
+                        dtype, nullptr, 0, stream, true);
 }
 
 int retention_fwd_from_state(const void* q, const void* k, const void* v, const float* gamma, int chunk,

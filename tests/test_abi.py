@@ -510,3 +510,43 @@ def test_plan_override_is_per_thread():
         assert lib.retention_fwd_workspace_bytes(*args) == 0
     assert seen["before"] == auto and seen["after"] not in (0, auto)
     assert lib.retention_fwd_workspace_bytes(*args) == auto
+
+
+# ---------------------------------------------------------------- allocation-free forward
+def _noalloc(lib, **kw):
+    a = dict(q=FAKE, k=FAKE * 2, v=FAKE * 3, gamma=_gam([0.9, 0.9]), chunk=64, out=FAKE * 4, fs=FAKE * 6, B=1, H=2,
+             T=16, dk=64, dv=64, dtype=rc.RET_BF16)
+    a.update(kw)
+    return lib.retention_fwd_noalloc(a["q"], a["k"], a["v"], a["gamma"], a["chunk"], a["out"], a["fs"], a["B"],
+                                     a["H"], a["T"], a["dk"], a["dv"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), -3),
+    (dict(chunk=96), -4),
+    (dict(gamma=_gam([0.9, 2.0])), -5),
+    (dict(out=FAKE * 2), -8),
+    (dict(v=FAKE * 3 + 2), -7),
+    (dict(q=None), -1),
+])
+def test_retention_fwd_noalloc_rejects(kw, code):
+    lib = _lib()
+    assert _noalloc(lib, **kw) == code
+    assert "retention_fwd_noalloc" in lib.retention_last_error().decode()
+
+
+def test_retention_fwd_noalloc_limit_is_checked_before_any_device_call():
+    """Sizes whose segment states exceed the library's 32 MiB array are
+    refused on the host (this runs without a GPU); B = 0 is a no-op."""
+    lib = _lib()
+    text = open(HEADER).read()
+    limit = int(re.search(r"#define RET_NOALLOC_MAX_WORKSPACE (\d+)", text).group(1))
+    assert limit == 32 << 20
+    G = 1 << 30  # 1 GiB apart: the [1, 64, 65536, 128] bf16 tensors do not overlap
+    big = dict(q=G, k=2 * G, v=3 * G, out=4 * G, fs=5 * G, H=64, T=65536, dk=128, dv=128, chunk=128,
+               gamma=_gam([0.9] * 64))
+    with rc.plan_override(segments=16):
+        assert lib.retention_fwd_workspace_bytes(1, 64, 65536, 128, 128, 128, rc.RET_BF16) > limit
+        assert _noalloc(lib, **big) == -9
+        assert "retention_fwd with a workspace" in lib.retention_last_error().decode()
+    assert _noalloc(lib, B=0) == 0
