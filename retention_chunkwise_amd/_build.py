@@ -1,13 +1,17 @@
 """Build libretention.so (HIP, gfx950 only) in-tree.
 
-    python -m retention_chunkwise_amd._build [-v] [--incremental]
+    python -m retention_chunkwise_amd._build [-v] [--incremental] [--sanitize-host]
 
 compiles every source under csrc/ with hipcc for --offload-arch=gfx950 and
 links them into retention_chunkwise_amd/libretention.so.  Packed fp32 vector
 instructions are disabled for all device code (-packed-fp32-ops).
 --incremental keeps the objects and hipcc's dependency files under _build/ at
 the repository root and recompiles only the sources whose object is older than
-the source or any header it includes.
+the source or any header it includes.  --sanitize-host builds a separate copy,
+_build/asan/libretention.so, whose host code (argument validation, planning,
+launch set-up) runs under AddressSanitizer and UndefinedBehaviorSanitizer; the
+device code is compiled exactly as in the normal build.  Loading it needs the
+clang ASan runtime preloaded (asan_runtime() names it); the CPU tests do that.
 """
 from __future__ import annotations
 
@@ -41,6 +45,21 @@ def common_flags() -> list[str]:
             "-Wall", "-Wno-unused-function"]
 
 
+# host-only sanitizers: each -fsanitize= applies to the host pass alone
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SANITIZED_LIB = os.path.join(os.path.dirname(HERE), "_build", "asan", "libretention.so")
+
+
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime the sanitized build links to."""
+    out = subprocess.run([hipcc(), "--print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = out.stdout.strip()
+    if not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("clang ASan runtime not found")
+    return path
+
+
 OBJ_CACHE = os.path.join(os.path.dirname(HERE), "_build")
 
 
@@ -55,10 +74,14 @@ def _stale(obj: str, src: str) -> bool:
     return any(not os.path.exists(f) or os.path.getmtime(f) > t for f in files + [src])
 
 
-def build(verbose: bool = False, incremental: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False, sanitize_host: bool = False) -> str:
     cc = hipcc()
+    extra = SANITIZE_HOST if sanitize_host else []
+    lib = SANITIZED_LIB if sanitize_host else LIB
+    if sanitize_host:
+        incremental = True
     with tempfile.TemporaryDirectory(prefix="retbuild_") as tmp:
-        odir = OBJ_CACHE if incremental else tmp
+        odir = (os.path.dirname(SANITIZED_LIB) if sanitize_host else OBJ_CACHE) if incremental else tmp
         os.makedirs(odir, exist_ok=True)
         objs = []
         cmds = []
@@ -68,7 +91,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
             path = os.path.join(CSRC, src)
             if incremental and not _stale(obj, path):
                 continue
-            cmds.append([cc, *common_flags(), "-MD", "-MF", obj[:-2] + ".d", "-c", path, "-o", obj])
+            cmds.append([cc, *common_flags(), *extra, "-MD", "-MF", obj[:-2] + ".d", "-c", path, "-o", obj])
 
         def run(cmd):
             r = subprocess.run(cmd, capture_output=True, text=True)
@@ -84,15 +107,17 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
                     sys.stderr.write("\n".join(msgs) + ("\n" if msgs else ""))
                 if r.returncode != 0:
                     raise RuntimeError(f"hipcc failed: {' '.join(cmd)}")
-        out_tmp = LIB + ".tmp"
-        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
+        out_tmp = lib + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra,
+                *(["-Xarch_host", "-shared-libasan"] if sanitize_host else []), "-o", out_tmp, *objs]
         r = subprocess.run(link, capture_output=True, text=True)
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError("hipcc link failed")
-        os.replace(out_tmp, LIB)
-    return LIB
+        os.replace(out_tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv,
+                sanitize_host="--sanitize-host" in sys.argv))
