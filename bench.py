@@ -98,12 +98,33 @@ def time_launches(fn, steps: int, warmup: int):
     return ev0.elapsed_time(ev1) / steps, wall / steps
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline_fwd(inp, w, target_s: float = 10.0):
     """The fp64 oracle (recurrent form) on the host cores, on a prefix of every
     head's sequence; the rate is scaled to tokens/s of the whole workload."""
     import oracle
 
-    nthreads = min(os.cpu_count() or 1, 16)
+    nproc = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = nproc
+    # one GPU's share of a shared host is 16 cores; more threads would take
+    # cores from the other GPUs' processes
+    cap = 16
+    nthreads = min(avail, cap)
     cores = oracle.threads_used(nthreads)
     q, k, v, g = inp["q"], inp["k"], inp["v"], inp["gamma"]
     Ts = 256
@@ -124,6 +145,7 @@ def cpu_baseline_fwd(inp, w, target_s: float = 10.0):
             "sample": f"fp64 recurrent oracle, g++ -O2 + OpenMP over (b, h); first {Ts} of "
                       f"{w.T} tokens of all {w.B * w.H} heads ({dt:.1f} s)",
             "seconds": dt,
+            "nproc": nproc, "cpus_available": avail, "thread_cap": cap, "cpu_model": cpu_model(),
             "single_thread": {"value": w.B * T1 / dt1, "unit": "tokens/s", "cores": 1,
                               "sample": f"first {T1} tokens of all {w.B * w.H} heads ({dt1:.1f} s)"}}
 
@@ -397,34 +419,40 @@ def main():
         }
         del fq, fk, fv, fout, ffs
 
-    # ---------------- gated linear attention (per-token, per-key-channel gates), fp32, [4, 8, 2048, 64]
+    # ---------------- gated linear attention (per-token, per-key-channel gates), [4, 8, 2048, 64],
+    # q, k, v and out in fp32 and in bf16 (log-gates and arithmetic fp32)
     if not args.no_components:
         wf = wl.WORKLOADS["ret_fwd_mh_f32"]
         fi = wl.make_inputs(wf, seed=0)
         g = torch.Generator().manual_seed(2)
         glg = torch.nn.functional.logsigmoid(torch.randn((wf.B, wf.H, wf.T, wf.dk), generator=g) + 2.0).to(dev)
-        gq, gk, gv = (fi[n].to(dev) for n in ("q", "k", "v"))
-        gout = torch.empty_like(gv)
-        gfs = torch.empty((wf.B, wf.H, wf.dk, wf.dv), dtype=torch.float32, device=dev)
+        for tag, tdt, esz in (("f32", torch.float32, 4), ("bf16", torch.bfloat16, 2)):
+            gq, gk, gv = (fi[n].to(dev).to(tdt) for n in ("q", "k", "v"))
+            gout = torch.empty_like(gv)
+            gfs = torch.empty((wf.B, wf.H, wf.dk, wf.dv), dtype=torch.float32, device=dev)
 
-        def glastep():
-            rc.gla_fwd(gq, gk, gv, glg, out=gout, final_state=gfs)
+            def glastep():
+                rc.gla_fwd(gq, gk, gv, glg, out=gout, final_state=gfs)
 
-        g_kern, g_wall = time_launches(glastep, max(args.steps, 100), args.warmup)
-        g_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, 64)
-        g_tf = g_fl / (g_kern * 1e-3) / 1e12
-        g_tr = measured_traffic("gla_gla_mh_f32", GLA_SOURCES)
-        g_by = M.fwd_bytes(wf.B, wf.H, wf.T, wf.dk, wf.dv, 4, final_state=True) + wf.B * wf.H * wf.T * wf.dk * 4
-        res["gla_f32"] = {
-            "workload": "gated linear attention, fp32 [4, 8, 2048, 64], log-gates logsigmoid(N(2, 1))",
-            "ms_per_call": g_kern, "tokens_per_s": wf.B * wf.T / (g_kern * 1e-3), "tflops": g_tf,
-            "roofline": {"kernel": "gla_fwd: gla_kernel<dk=64, 32-column slices>", "bound": "mfma", "achieved": g_tf,
-                         "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": g_tf / M.PEAK_TFLOPS["f32"],
-                         "traffic": (g_tr["bytes_per_launch"] if g_tr else None),
-                         # q, k, v, log-gates read, out and final state written
-                         "algorithmic_bytes_per_launch": g_by},
-        }
-        del glg, gq, gk, gv, gout, gfs
+            g_kern, g_wall = time_launches(glastep, max(args.steps, 100), args.warmup)
+            g_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, 64)
+            g_tf = g_fl / (g_kern * 1e-3) / 1e12
+            g_tr = measured_traffic(f"gla_gla_mh_{tag}", GLA_SOURCES)
+            # q, k, v read and out written in the input type, fp32 log-gates read, fp32 final state written
+            g_by = M.fwd_bytes(wf.B, wf.H, wf.T, wf.dk, wf.dv, esz, final_state=True) + wf.B * wf.H * wf.T * wf.dk * 4
+            res[f"gla_{tag}"] = {
+                "workload": f"gated linear attention, {tag} q/k/v/out, fp32 log-gates logsigmoid(N(2, 1)), "
+                            "[4, 8, 2048, 64]",
+                "ms_per_call": g_kern, "wall_ms_per_call": g_wall,
+                "tokens_per_s": wf.B * wf.T / (g_kern * 1e-3), "tflops": g_tf,
+                "roofline": {"kernel": "gla_fwd: state-only pass + walk, gla_kernel<dk=64, 64-column slice>",
+                             "bound": "mfma", "achieved": g_tf, "peak": M.PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                             "frac": g_tf / M.PEAK_TFLOPS["f32"],
+                             "traffic": (g_tr["bytes_per_launch"] if g_tr else None),
+                             "algorithmic_bytes_per_launch": g_by},
+            }
+            del gq, gk, gv, gout, gfs
+        del glg
 
     # ---------------- context: a plain device copy of 1 GiB (read + write), the
     # ceiling a kernel that streams each byte once in and once out can expect

@@ -368,16 +368,22 @@ int linear_attn_decode_step(const void *q, const void *k, const void *v, int phi
  * ("Efficient and Sparse Transformers", section "Gated Linear Attention:
  * Toward Input-Dependent Forgetting": RetNet's fixed decay becomes a learned
  * gate applied element-wise to the state; here the gate of key channel c,
- * shared by the value columns.  lg = gamma for every channel is retention,
- * lg = 0 plain linear attention.)  Inside a chunk the decays are
- * exponentials of differences of running log-gate sums, all <= 0.
+ * shared by the value columns.  lg = log(gamma) for every channel is
+ * retention, lg = 0 plain linear attention.)  Inside a chunk the gates are
+ * folded into the operands, each scaled by exponentials of log-gate sums
+ * relative to its 16-token tile (every folded operand at most its raw
+ * magnitude); a chunk holding a 16-token tile whose gate sum falls below -80
+ * in some channel forms its scores term by term with exponents
+ * e^{b_i - b_j} <= 1.
  *
- *   q, k, log_gate  device, [B][H][T][dk] fp32; log_gate finite and <= 0
- *                   (accuracy assumes |log_gate| of order 1-10 per token;
- *                   -inf is not accepted by the chunk form)
- *   v, out          device, [B][H][T][dv] fp32
+ *   q, k            device, [B][H][T][dk], dtype
+ *   log_gate        device, [B][H][T][dk] fp32 whatever the dtype; finite
+ *                   and <= 0 (a value above 0, a gate above 1, is taken as
+ *                   0; NaN propagates; accuracy assumes |log_gate| of order
+ *                   1-10 per token; -inf is not accepted by the chunk form)
+ *   v, out          device, [B][H][T][dv], dtype
  *   final_state     device, [B][H][dk][dv] fp32 (written); may be NULL
- *   dtype           RET_F32 only (RET_ERR_DTYPE otherwise)
+ *   dtype           RET_F32 or RET_BF16 (q, k, v, out); fp32 arithmetic
  *   dk, dv          each 64 or 128
  *   workspace       gla_fwd_workspace_bytes(...) bytes: per segment but the
  *                   last, its state contribution and per-channel gate totals

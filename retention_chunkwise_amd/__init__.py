@@ -19,7 +19,7 @@ linear_attn_decode_step(q, k, v, S, z, eps=1e-6) -> out   (S, z updated in place
 retention_bwd(q, k, v, gamma, dout, chunk=64)  -> (dq, dk, dv); fwd_workspace= reuses a forward's states
 retention_fwd_normalized(q, k, v, gamma, norm="group", eps=1e-5) -> out   (bf16 or fp32)
 retention(q, k, v, gamma, chunk=64)            -> out, differentiable (torch.autograd)
-gla_fwd(q, k, v, log_gate)                     -> (out, final_state)   (fp32)
+gla_fwd(q, k, v, log_gate)                     -> (out, final_state)   (fp32 or bf16 q/k/v, fp32 gates)
 retention_fwd_workspace_bytes(B, H, T, dk, dv, chunk, dtype) -> int
 linear_attn_workspace_bytes(B, H, T, dk, dv, dtype)          -> int
 set_plan_override(path=None, segments=None, walk_nt=None, lin_chunk=None)   (this thread's calls)
@@ -352,25 +352,28 @@ def retention_fwd_normalized(q, k, v, gamma, norm: str = "group", eps: float = 1
 
 def gla_fwd(q, k, v, log_gate, out=None, final_state=None, want_state: bool = True, workspace=None):
     """Gated linear attention with per-token, per-key-channel gates
-    exp(log_gate): q, k, log_gate [B,H,T,dk], v [B,H,T,dv], all float32 on the
-    GPU.  Returns (out [B,H,T,dv], final_state [B,H,dk,dv] or None)."""
+    exp(log_gate): q, k [B,H,T,dk] and v [B,H,T,dv] in float32 or bfloat16
+    (one dtype), log_gate [B,H,T,dk] float32, on the GPU.  Returns
+    (out [B,H,T,dv] in the input dtype, final_state [B,H,dk,dv] float32 or None)."""
     lib = load_library()
-    for n, t in (("q", q), ("k", k), ("v", v), ("log_gate", log_gate)):
-        _check_dev(n, t, torch.float32)
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, q.dtype)
+    _check_dev("log_gate", log_gate, torch.float32)
     if q.dim() != 4 or k.shape != q.shape or log_gate.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
         raise ValueError("q, k, log_gate must be [B,H,T,dk] and v [B,H,T,dv]")
     B, H, T, dk = q.shape
     dv = v.shape[3]
     if out is None:
         out = torch.empty_like(v)
-    _check_dev("out", out, torch.float32)
+    _check_dev("out", out, v.dtype)
     if final_state is None and want_state:
         final_state = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _check_dev("final_state", final_state, torch.float32)
-    ws, nws = _workspace(lib.gla_fwd_workspace_bytes(B, H, T, dk, dv, RET_F32), q.device, workspace)
+    dt = _dtype_code(q)
+    ws, nws = _workspace(lib.gla_fwd_workspace_bytes(B, H, T, dk, dv, dt), q.device, workspace)
     rc = lib.gla_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), log_gate.data_ptr(), out.data_ptr(),
-                     _ptr(final_state), B, H, T, dk, dv, RET_F32, _ptr(ws), nws, _stream(q))
+                     _ptr(final_state), B, H, T, dk, dv, dt, _ptr(ws), nws, _stream(q))
     _raise(rc)
     return out, final_state
 

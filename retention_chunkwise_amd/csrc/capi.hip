@@ -331,7 +331,7 @@ size_t linear_attn_workspace_bytes(int B, int H, int T, int dk, int dv, int dtyp
 
 
 size_t gla_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int dtype) {
-    if (B <= 0 || H < 1 || T < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || dtype != RET_F32) return 0;
+    if (B <= 0 || H < 1 || T < 0 || (dk != 64 && dk != 128) || (dv != 64 && dv != 128) || !dtype_size(dtype)) return 0;
     SegPlan plan;
     if (!plan_gla(static_cast<long long>(B) * H, T, dk, dv, &plan)) return 0;
     return plan.ws_bytes;
@@ -836,13 +836,15 @@ int linear_attn_fwd_from_state(const void* q, const void* k, const void* v, int 
 int gla_fwd(const void* q, const void* k, const void* v, const float* log_gate, void* out, float* final_state, int B,
             int H, int T, int dk, int dv, int dtype, void* workspace, size_t ws_bytes, void* stream) {
     const char* fn = "gla_fwd";
-    if (dtype != RET_F32) return fail(RET_ERR_DTYPE, "%s: fp32 only (dtype %d)", fn, dtype);
+    const int esz = dtype_size(dtype);
+    if (!esz) return fail(RET_ERR_DTYPE, "%s: unknown dtype %d", fn, dtype);
     if (B < 0 || T < 0 || H < 1)
         return fail(RET_ERR_SHAPE, "%s: need B >= 0, T >= 0, H >= 1 (got B=%d H=%d T=%d)", fn, B, H, T);
     if ((dk != 64 && dk != 128) || (dv != 64 && dv != 128))
         return fail(RET_ERR_SHAPE, "%s: dk and dv must each be 64 or 128 (got %d, %d)", fn, dk, dv);
-    size_t nqk = 4, nv = 4, ns = 4;
+    size_t nqk = esz, ng = 4, nv = esz, ns = 4;
     if (!mul_ok(nqk, B) || !mul_ok(nqk, H) || !mul_ok(nqk, T) || !mul_ok(nqk, dk) ||
+        !mul_ok(ng, B) || !mul_ok(ng, H) || !mul_ok(ng, T) || !mul_ok(ng, dk) ||
         !mul_ok(nv, B) || !mul_ok(nv, H) || !mul_ok(nv, T) || !mul_ok(nv, dv) ||
         !mul_ok(ns, B) || !mul_ok(ns, H) || !mul_ok(ns, dk) || !mul_ok(ns, dv))
         return fail(RET_ERR_SHAPE, "%s: tensor sizes overflow", fn);
@@ -851,7 +853,7 @@ int gla_fwd(const void* q, const void* k, const void* v, const float* log_gate, 
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(log_gate) || !aligned16(out))
         return fail(RET_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
     const Range rq = range("q", q, nqk), rk = range("k", k, nqk), rv = range("v", v, nv);
-    const Range rg = range("log_gate", log_gate, nqk), ro = range("out", out, nv);
+    const Range rg = range("log_gate", log_gate, ng), ro = range("out", out, nv);
     for (const Range& in : {rq, rk, rv, rg})
         if (overlap(ro, in)) return fail(RET_ERR_ALIAS, "%s: out overlaps %s", fn, in.name);
     int rc;
@@ -863,14 +865,14 @@ int gla_fwd(const void* q, const void* k, const void* v, const float* log_gate, 
                               {rq, rk, rv, rg, ro, final_state ? range("final_state", final_state, ns) : Range{"", 0, 0}})))
         return rc;
     ret::GlaArgs a{};
-    a.q = static_cast<const float*>(q); a.k = static_cast<const float*>(k); a.v = static_cast<const float*>(v);
-    a.lg = log_gate; a.out = static_cast<float*>(out); a.final_state = final_state;
+    a.q = q; a.k = k; a.v = v;
+    a.lg = log_gate; a.out = out; a.final_state = final_state;
     a.B = B; a.H = H; a.T = T; a.dv = dv;
     const int nt = plan.nt;
     a.nslices = dv / (16 * nt);
     a.G = plan.G; a.cps = plan.cps;
     a.ws = plan.ws_bytes ? static_cast<float*>(workspace) : nullptr;
-    const hipError_t e = ret::launch_gla(a, dk, nt, static_cast<hipStream_t>(stream));
+    const hipError_t e = ret::launch_gla(a, dtype == RET_BF16, dk, nt, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     return ok();
 }

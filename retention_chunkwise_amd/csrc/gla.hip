@@ -1,5 +1,5 @@
 // gla.hip -- chunkwise gated linear attention (per-token, per-key-channel
-// gates), fp32, gfx950.
+// gates), fp32 arithmetic, fp32 or bf16 q/k/v/out, gfx950.
 //
 // What is computed ("Efficient and Sparse Transformers", section "Gated
 // Linear Attention: Toward Input-Dependent Forgetting": the fixed decay of
@@ -7,39 +7,61 @@
 // one gate per key channel, alpha_t = exp(lg_t)):
 //   S_t[c][n] = alpha_t[c] S_{t-1}[c][n] + k_t[c] v_t[n],   o_t = q_t S_t.
 // Chunk form.  With b_i[c] the log-gates summed over the chunk up to and
-// including its token i, and S the state before the chunk:
+// including its token i (non-increasing in i), b_L its value at the chunk's
+// last token, and S the state before the chunk:
 //   o_i   = sum_{j<=i} sum_c q_i[c] k_j[c] e^{b_i[c] - b_j[c]} v_j + sum_c q_i[c] e^{b_i[c]} S[c][:]
-//   S_new = diag(e^{b_last}) S + sum_j diag(e^{b_last - b_j}) k_j v_j^T
-// Every exponent used is <= 0, so nothing overflows:
-//  - key tile J before query tile I: with e_J the last token of tile J,
-//    e^{b_i - b_j} = e^{b_i - b_{e_J}} e^{b_{e_J} - b_j}, both factors <= 1,
-//    folded into the Q and K operands of an fp32 MFMA;
-//  - the diagonal tiles (i, j in one 16-token tile) are summed directly, one
-//    exponent per term;
-//  - the inter-chunk and state products scale Q by e^{b_i} and K by
-//    e^{b_last - b_j}.
-// Fast path.  One pre-scaled key array serves every product:
-// K^[j][c] = k_j[c] e^{b_{e_J}[c] - b_j[c]} (<= |k|).  Scores of key tile J
-// <= I take Q operands q_i e^{b_i - b_{e_I}} (>= 1 in size, bounded by
-// e^{span of one tile}) times e^{b_{e_I} - b_{e_J}} (<= 1); the diagonal tile
-// is that product masked.  The state update takes K^ times e^{b_last -
-// b_{e_J}} (<= 1).  It is used when every channel's log-gate sum over the
-// chunk stays above -80, so that no factor can overflow; a chunk with
-// stronger gates takes the exact path above (diagonal tiles summed term by
-// term, every exponent formed on the spot).
+//   S_new = diag(e^{b_L}) S + sum_j diag(e^{b_L - b_j}) k_j v_j^T
+//
+// Tile-relative factors.  The chunk's 64 tokens form four 16-token tiles.  For
+// token i of tile I let cum_i be the gate sum from the tile's start to i, t_I
+// the tile's total and B_I = t_0 + ... + t_I (B_{-1} = 0), so b_i = B_{I-1} +
+// cum_i.  Every operand is folded once per chunk and stays bounded:
+//   Q^ = q e^{cum_i}             (<= |q|)    queries, relative to their tile's start
+//   K^ = k e^{t_J - cum_j}       (<= |k|)    keys, relative to their tile's end
+//   K' = k e^{b_L - b_j}         (<= |k|)    keys for the state update
+// and the scores of query tile I against key tile J <= I are
+//   P^T = K^ (Q^ (.) F_IJ)^T,  F_IJ = e^{B_{I-1} - B_J} (<= 1) for J < I,
+//                              F_II = e^{-t_I}          (>= 1) on the diagonal,
+// with F_{I,I-1} = 1; the inter-chunk read takes Q^ (.) e^{B_{I-1}} (<= |q|).
+// Only F_II grows, as e^{-t_I}: it stays finite while every 16-token tile's
+// gate sum is above -80 in every channel.  A chunk with a stronger tile (a
+// gate below e^-5 per token on average over 16 tokens) forms its scores term
+// by term instead (exact path), one exponent e^{b_i - b_j} <= 1 per term.  The
+// masked upper triangle of the diagonal tile is discarded by a select.
 //
 // Segments.  Each (b, h) sequence is cut into G segments of whole chunks.  A
 // state-only pass (SO) walks every segment but the last and writes its
 // contribution dS_j (the state it would end with from zero) and its per-channel
-// log-gate total L_j; the walk of segment g then starts from
+// log-gate total L_j; the walk of segment g starts from
 //   S_in(g) = sum_{j<g} diag(exp(L_{j+1} + ... + L_{g-1})) dS_j,
 // all exponents <= 0.
 //
-// Mapping.  One workgroup (4 waves) per (b, h, segment, slice of 16 NT value
-// columns) walks the segment's chunks of 64 tokens; wave W owns query tile W
-// and state tiles {W, W + 4, ...} of the slice.  The chunk's q, k, cumulative
-// gates and the value slice are staged in LDS (padded fp32 rows); S^T is
-// copied to LDS for the next chunk's inter-chunk product.
+// Mapping.  One workgroup of 8 waves per (b, h, segment, 64-column value
+// slice) walks the segment's 64-token chunks, so Q K^T is formed once per
+// chunk for the whole slice (the only slice when dv = 64).
+//  - Folding: lane l of wave w covers tokens 4 (l % 16) .. + 3 (in tile
+//    (l % 16) / 4) of the 4 channels 16 (w % 4) + 4 (l / 16) .. + 3 (+ 64 for
+//    dk = 128), loaded as 16-byte (bf16: 8-byte) runs.  Waves 0-3 fold the
+//    queries (and stage the same 4 value columns of the slice over the same
+//    tokens), waves 4-7 the keys; both read the gates of their channels (the
+//    second read hits the cache).  Running sums: a sum over the lane's 4
+//    tokens, a DPP prefix scan over the 16 lanes of a row, and shuffles for
+//    the tile totals.  The next chunk's raw q or k, gates and values are
+//    loaded straight into registers (range-checked buffer loads: rows past
+//    the end read as zeros) while the current chunk is computed.
+//  - LDS layouts: Q^, K^ and the S^T copy row-major by token / value column
+//    with channels in order; K' and V transposed ([channel][key],
+//    [column][key]).  In every product a lane of group g contracts over a run
+//    of 4 consecutive channels or keys, so each MFMA operand pair comes from
+//    16-byte reads and the folded keys and values go in with 16-byte writes.
+//  - Products: waves 0-3 (O-waves) own query tile W: scores, then O^T = S^T
+//    Q~^T + V^T P^T over the slice.  Waves 4-7 (S-waves) own state tiles,
+//    split so that each SIMD (O-wave W and S-wave W + 4) issues the same
+//    number of MFMAs.  The state-only pass splits the state tiles over all 8.
+//  - Two barriers per chunk: after the folded operands are written, and after
+//    the products (then the S-waves refresh the LDS copy of S^T).  Whether the
+//    next chunk needs the exact path is voted on as soon as its gates arrive,
+//    one step ahead.
 #include "internal.h"
 #include "kcommon.h"
 
@@ -49,87 +71,259 @@ namespace {
 
 using namespace ::ret::kc;
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int C = 64;
+constexpr float kTileBound = -80.f;  // F_II = e^{-t_I} <= e^{80} = 5.5e34
 
 template <int DK, int NT>
 struct Cfg {
-    static constexpr int KSTR = DK + 4;    // padded row stride of q, k, gates
-    static constexpr int DVS = 16 * NT;    // value columns per workgroup
-    static constexpr int VSTR = DVS + 4;   // padded row stride of the value slice
-    static constexpr int KT = DK / 16;
-    static constexpr int SPW = NT * KT / 4;  // state tiles per wave
-    static_assert(NT * KT % 4 == 0, "state tiles split over 4 waves");
+    static constexpr int KT = DK / 16;              // channel tiles
+    static constexpr int DVS = 16 * NT;             // value columns per workgroup
+    static constexpr int QS = DK + 4;               // row stride (floats) of Q^, K^ and the S^T copy
+    static constexpr int CS = C + 4;                // row stride of the transposed K' and V
+    static constexpr int NTILE = KT * NT;           // 16 x 16 state tiles
+    static constexpr int CPT = DK / 64;             // channels folded per thread
+    static_assert(DVS == 64, "the O-side waves stage 64 value columns");
+    static_assert(NTILE % 8 == 0, "state tiles split over 8 waves in the state-only pass");
+};
+
+// Rows of the factor table (each DK floats, channels in order):
+//   0..3   F_II = e^{-t_I}
+//   4, 5   F_20, F_30 = e^{B_1 - B_0}, e^{B_2 - B_0}
+//   6      F_31 = e^{B_2 - B_1}
+//   7..9   E_I = e^{B_{I-1}} for I = 1..3 (inter-chunk read)
+constexpr int kFRows = 10;
+template <int I, int J>
+constexpr int frow() {
+    if constexpr (I == J) return I;
+    else if constexpr (I == 2 && J == 0) return 4;
+    else if constexpr (I == 3 && J == 0) return 5;
+    else return 6;  // (3, 1)
+}
+
+// Buffer sets of folded operands: two at dk = 64, so that the next chunk is
+// folded while the current one's products run; one at dk = 128 (LDS).
+template <int DK>
+constexpr int nbuf() { return DK == 64 ? 2 : 1; }
+
+template <int DK, int NT>
+struct OpBuf {
+    using Cf = Cfg<DK, NT>;
+    alignas(16) float qb[C * Cf::QS];        // Q^ [token][channel]; exact path: raw q
+    alignas(16) float kb[C * Cf::QS];        // K^ [key][channel]; exact path: raw k
+    alignas(16) float gt[DK * Cf::CS];       // K'^T [channel][key]; exact path: b^T
+    alignas(16) float vt[Cf::DVS * Cf::CS];  // V^T [column][key]
+    alignas(16) float fb[kFRows * DK];       // factor table
+    alignas(16) float bl[DK];                // e^{b_L} per channel
 };
 
 template <int DK, int NT>
 struct Smem {
     using Cf = Cfg<DK, NT>;
-    alignas(16) float q[C * Cf::KSTR];
-    alignas(16) float k[C * Cf::KSTR];
-    alignas(16) float b[C * Cf::KSTR];     // log-gates, then their running sums over the chunk
-    alignas(16) float v[C * Cf::VSTR];
-    alignas(16) float st[Cf::DVS * Cf::KSTR];  // S^T copy: st[n][c] = S[c][nbase + n]
-    int unsafe[4];                             // per wave: this chunk's gates are too strong for the fast path
+    OpBuf<DK, NT> op[nbuf<DK>()];
+    alignas(16) float sc[Cf::DVS * Cf::QS];  // S^T copy: sc[n][c] = S[c][nbase + n]
+    int flag[2][4];                          // [chunk parity][key wave]: a tile past the bound (exact path)
 };
 
 template <int DK, int NT>
 constexpr bool fits() { return sizeof(Smem<DK, NT>) <= 160 * 1024; }
+static_assert(sizeof(Smem<64, 4>) <= 160 * 1024 && sizeof(Smem<128, 4>) <= 160 * 1024, "LDS");
 
-template <int DK, int NT, int W, bool SO>
+// State tiles of each S-wave in the walk.  O-wave W issues (W+1) DK/4 score,
+// 4 NT (W+1) intra-chunk and NT DK/4 inter-chunk MFMAs per chunk; a state
+// tile costs 16 (64 keys / 4).  S-wave W + 4 takes the tiles that bring its
+// SIMD to the mean.
+struct Split {
+    int first[4];
+    int cnt[4];
+};
+
+template <int DK, int NT>
+constexpr Split make_split() {
+    constexpr int NTILE = (DK / 16) * NT;
+    int work[4] = {};
+    int total = 16 * NTILE;
+    for (int w = 0; w < 4; ++w) {
+        work[w] = (w + 1) * (DK / 4) + 4 * NT * (w + 1) + NT * (DK / 4);
+        total += work[w];
+    }
+    Split s{};
+    int sum = 0;
+    for (int w = 0; w < 4; ++w) {
+        int c = (total / 4 - work[w] + 8) / 16;
+        if (c < 0) c = 0;
+        s.cnt[w] = c;
+        sum += c;
+    }
+    while (sum != NTILE) {  // even out rounding: adjust the most / least loaded SIMD
+        int best = 0;
+        for (int w = 1; w < 4; ++w) {
+            const int lw = work[w] + 16 * s.cnt[w], lb = work[best] + 16 * s.cnt[best];
+            if (sum > NTILE ? (lw > lb && s.cnt[w] > 0) || s.cnt[best] == 0 : lw < lb) best = w;
+        }
+        s.cnt[best] += (sum > NTILE) ? -1 : 1;
+        sum += (sum > NTILE) ? -1 : 1;
+    }
+    int f = 0;
+    for (int w = 0; w < 4; ++w) {
+        s.first[w] = f;
+        f += s.cnt[w];
+    }
+    return s;
+}
+
+// 4 consecutive q, k or v elements: fp32 (16 bytes) or bf16 (8 bytes), kept
+// raw in registers until they are folded (widening them at load time would
+// make the compiler wait for the load there).
+template <bool BF>
+struct Quad;
+template <>
+struct Quad<false> {
+    u32x4 x;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        x = __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0);
+    }
+    __device__ __forceinline__ f32x4 f() const { return __builtin_bit_cast(f32x4, x); }
+};
+template <>
+struct Quad<true> {
+    u32x2 x;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        x = __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0);
+    }
+    __device__ __forceinline__ f32x4 f() const {
+        const u16x4 e = __builtin_bit_cast(u16x4, x);
+        return f32x4{bf2f(e[0]), bf2f(e[1]), bf2f(e[2]), bf2f(e[3])};
+    }
+};
+
+// Inclusive prefix sum over the 16 lanes of a DPP row (lanes shifted in from
+// outside the row read as zero).
+__device__ __forceinline__ float row_scan16(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
+    return x;
+}
+
+template <bool BF>
+__device__ __forceinline__ void store4(char* p, const f32x4& o) {
+    if constexpr (BF) *reinterpret_cast<u16x4*>(p) = cvt4_bf16(o);
+    else *reinterpret_cast<f32x4*>(p) = o;
+}
+
+__device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void sts4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+
+// e^x as 2^(x log2 e) on v_exp_f32 (about 1 ulp).  Results below the normal
+// range flush to zero: every factor here is a decay or a product with one,
+// and a factor under 1e-38 contributes nothing at fp32 precision.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+template <bool BF, int DK, int NT, int W8, bool SO>
 __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh, int seg, int nbase) {
     using Cf = Cfg<DK, NT>;
-    constexpr int KSTR = Cf::KSTR, VSTR = Cf::VSTR, KT = Cf::KT, SPW = Cf::SPW, DVS = Cf::DVS;
+    using Buf = OpBuf<DK, NT>;
+    constexpr int QS = Cf::QS, CS = Cf::CS, KT = Cf::KT, NTILE = Cf::NTILE;
+    constexpr int CPT = Cf::CPT, NQ = DK / 4, NB = nbuf<DK>();
+    constexpr int ESZ = BF ? 2 : 4;
+    constexpr bool QW = W8 < 4;         // folds queries and stages values (walk); stages values (state-only pass)
+    constexpr bool OW = !SO && QW;      // output wave: query tile W8
+    constexpr Split SP = make_split<DK, NT>();
+    constexpr int TF = SO ? W8 * (NTILE / 8) : (OW ? 0 : SP.first[W8 - 4]);
+    constexpr int TN = SO ? NTILE / 8 : (OW ? 0 : SP.cnt[W8 - 4]);
+    constexpr int W = W8 & 3;
+    constexpr bool FOLDX = !(SO && QW);  // waves that fold q or k (and load gates)
     const int T = a.T, DV = a.dv;
-    const int tid = threadIdx.x, l = tid & 63, l16 = l & 15, g = l >> 4;
-    const float* qh = a.q + static_cast<long long>(bh) * T * DK;
-    const float* kh = a.k + static_cast<long long>(bh) * T * DK;
+    const int l = threadIdx.x & 63, l16 = l & 15, g = l >> 4;
+    const char* xh = static_cast<const char*>(QW ? a.q : a.k) + static_cast<long long>(bh) * T * DK * ESZ;
     const float* gh = a.lg + static_cast<long long>(bh) * T * DK;
-    const float* vh = a.v + static_cast<long long>(bh) * T * DV + nbase;
-    float* oh = a.out + static_cast<long long>(bh) * T * DV + nbase;
-    constexpr int I = W;  // query tile
+    const char* vh = static_cast<const char*>(a.v) + (static_cast<long long>(bh) * T * DV + nbase) * ESZ;
+    char* oh = static_cast<char*>(a.out) + (static_cast<long long>(bh) * T * DV + nbase) * ESZ;
 
-    f32x4 sacc[SPW];  // S[16 kt + l16][nbase + 16 nt + 4g + r], tile W + 4m = (nt, kt)
+    // ---- state tiles of this wave: tile t = (m = t % KT channel tile, n = t / KT value tile);
+    // lane holds S[16 m + 4 g + r][nbase + 16 n + l16]
+    f32x4 sacc[TN > 0 ? TN : 1];
 #pragma unroll
-    for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < TN; ++t) sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const long long slot = static_cast<long long>(DK) * DV + DK;  // workspace floats per (b, h, segment)
-    if (!SO && seg > 0) {
-        // S_in = sum_{j<seg} diag(exp(L_{j+1} + ... + L_{seg-1})) dS_j
-        const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot;
+    // S^T copy: the lane's 4 values are 4 consecutive channels of value column 16 n + l16
+    auto write_state_copy = [&]() {
+        if constexpr (!SO && !OW) {
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT, ch = 16 * kt + l16;
-            float dsum = 0.f;
-            for (int j = seg - 1; j >= 0; --j) {
-                const float* sj = wsb + j * slot;
-                sacc[m] += __expf(dsum) * *reinterpret_cast<const f32x4*>(sj + ch * DV + nbase + 16 * nt + 4 * g);
-                dsum += sj[DK * DV + ch];
+            for (int t = 0; t < TN; ++t) {
+                const int m = (TF + t) % KT, n = (TF + t) / KT;
+                sts4(&sm.sc[(16 * n + l16) * QS + 16 * m + 4 * g], sacc[t]);
             }
         }
+    };
+    if constexpr (!SO && !OW) {
+        if (seg > 0) {
+            // S_in = sum_{j<seg} diag(exp(L_{j+1} + ... + L_{seg-1})) dS_j, newest segment first; the
+            // next slot's values are loaded while the current one is added
+            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot;
+            // tiles in groups of up to 4, so that two slots' values stay in registers
+            auto group = [&](auto t0c) {
+                constexpr int T0 = decltype(t0c)::value;
+                constexpr int NG = (TN - T0 < 4) ? TN - T0 : 4;
+                float cv[NG][4], cl[NG][4], dsum[NG][4];
+                auto ld = [&](int j, float (&v)[NG][4], float (&L)[NG][4]) {
+                    const float* sj = wsb + j * slot;
+#pragma unroll
+                    for (int t = 0; t < NG; ++t) {
+                        const int m = (TF + T0 + t) % KT, n = (TF + T0 + t) / KT;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            v[t][r] = sj[(16 * m + 4 * g + r) * DV + nbase + 16 * n + l16];
+                            L[t][r] = sj[DK * DV + 16 * m + 4 * g + r];
+                        }
+                    }
+                };
+#pragma unroll
+                for (int t = 0; t < NG; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dsum[t][r] = 0.f;
+                ld(seg - 1, cv, cl);
+                for (int j = seg - 1; j >= 0; --j) {
+                    float nv[NG][4], nl[NG][4];
+                    if (j > 0) ld(j - 1, nv, nl);
+#pragma unroll
+                    for (int t = 0; t < NG; ++t)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            sacc[T0 + t][r] += fexp(dsum[t][r]) * cv[t][r];
+                            dsum[t][r] += cl[t][r];
+                        }
+                    if (j > 0) {
+#pragma unroll
+                        for (int t = 0; t < NG; ++t)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                cv[t][r] = nv[t][r];
+                                cl[t][r] = nl[t][r];
+                            }
+                    }
+                }
+            };
+            if constexpr (TN > 0) group(std::integral_constant<int, 0>{});
+            if constexpr (TN > 4) group(std::integral_constant<int, 4>{});
+            if constexpr (TN > 8) group(std::integral_constant<int, 8>{});
+            if constexpr (TN > 12) group(std::integral_constant<int, 12>{});
+            static_assert(TN <= 16, "prologue groups");
+        }
+        write_state_copy();  // for the first chunk (ordered by the barriers before the loop)
     }
-#pragma unroll
-    for (int m = 0; m < SPW; ++m) {  // state copy for the first chunk (ordered by the loop's first barrier)
-        const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sm.st[(16 * nt + 4 * g + r) * KSTR + 16 * kt + l16] = sacc[m][r];
-    }
-    // Staging.  q and the value slice load as 16-byte rows; keys and log-gates
-    // in a column layout: lane (c16, rq) of wave W holds key channels
-    // 16 W + c16 + 64 u (u < DK / 64) of rows 16 rq .. 16 rq + 15, i.e. one
-    // 16-token tile per channel, so the running gate sums, the tile totals and
-    // the pre-scaled keys K^ come out of registers.  The next chunk's loads
-    // are issued before the current chunk's products.
-    constexpr int NU = C * DK / 4 / kThreads;
-    constexpr int NV = (C * DVS / 4 + kThreads - 1) / kThreads;
-    constexpr int CPW = DK / 64;
-    static_assert(NU * kThreads * 4 == C * DK, "q staging split");
-    const int c16 = l & 15, rq = l >> 4;
-    f32x4 pq[SO ? 1 : NU], pv[NV];
-    float pk[CPW][16], pg[CPW][16];
-    float ltot[CPW];  // state-only pass: log-gate totals of this lane's channels over the segment
-#pragma unroll
-    for (int u = 0; u < CPW; ++u) ltot[u] = 0.f;
 
+    // ---- raw chunk registers.  Lane l of wave W covers token group tg = l % 16
+    // (tokens 4 tg .. 4 tg + 3, tile TT = tg / 4) of channel group cg = l / 16:
+    // channels c0(u) = 16 W + 4 cg + 64 u .. + 3 (q on the O-side, k on the
+    // S-side, and the gates) and value columns 16 W + 4 cg .. + 3 (O-side).  A
+    // channel group's 16 token groups fill one DPP row, so running sums over
+    // the chunk are row scans.
+    const int tg = l & 15, cg = l >> 4, TT = tg >> 2;
+    Quad<BF> rx[CPT][4], rv[4];
+    f32x4 rgt[CPT][4];
     const int nch = (T + C - 1) / C;
     const int c_begin = seg * a.cps;
     const int c_end = (c_begin + a.cps < nch) ? c_begin + a.cps : nch;
@@ -137,262 +331,325 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         const long long t0 = static_cast<long long>(c) * C;
         return (T - t0 < C) ? static_cast<int>(T - t0) : C;
     };
-    // rows past the end read row 0 of the chunk (always valid); they are zeroed when stored
-    auto load_qv = [&](int c) {
+    // Issued for every step (a chunk past the segment gets a zero-length
+    // range and reads zeros), so the compiler's waits see one shape.
+    auto load_chunk = [&](int c) {
         const long long t0 = static_cast<long long>(c) * C;
-        const int clen = chunk_len(c);
-        if constexpr (!SO) {
+        const int cl = (c < c_end) ? chunk_len(c) : 0;
+        if constexpr (FOLDX) {
+            const auto rsx = make_rsrc(xh + t0 * DK * ESZ, cl * DK * ESZ);
+            const auto rsg = make_rsrc(gh + t0 * DK, cl * DK * 4);
 #pragma unroll
-            for (int m = 0; m < NU; ++m) {
-                const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
-                pq[m] = *reinterpret_cast<const f32x4*>(qh + (t0 + (r < clen ? r : 0)) * DK + c4);
-            }
+            for (int u = 0; u < CPT; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned e = static_cast<unsigned>((4 * tg + i) * DK + 16 * W + 4 * cg + 64 * u);
+                    rx[u][i].load(rsx, e * ESZ);
+                    rgt[u][i] = __builtin_bit_cast(f32x4, bload16(rsg, e * 4));
+                }
         }
+        if constexpr (QW) {
+            const auto rsv = make_rsrc(vh + t0 * DV * ESZ, cl * DV * ESZ);
 #pragma unroll
-        for (int m = 0; m < NV; ++m) {
-            const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
-            if (u < C * DVS / 4) pv[m] = *reinterpret_cast<const f32x4*>(vh + (t0 + (r < clen ? r : 0)) * DV + c4);
+            for (int i = 0; i < 4; ++i)
+                rv[i].load(rsv, static_cast<unsigned>(((4 * tg + i) * DV + 16 * W + 4 * cg) * ESZ));
         }
     };
-    auto load_kg = [&](int c) {
-        const long long t0 = static_cast<long long>(c) * C;
-        const int clen = chunk_len(c);
+    // Gate sums of this lane's 4 channels: b[i] at its tokens (gates above 0
+    // taken as 0, NaN kept) and the tile boundary sums B[0..3] (B[3] = b_L).
+    auto gate_sums = [&](int u, f32x4 (&b)[4], f32x4 (&B)[4]) {
+        f32x4 run = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < CPW; ++u) {
-            const int ch = 16 * W + c16 + 64 * u;
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = 16 * rq + i;
-                const long long o = (t0 + (r < clen ? r : 0)) * DK + ch;
-                pk[u][i] = kh[o];
-                pg[u][i] = gh[o];
+            for (int e = 0; e < 4; ++e) {
+                const float x = rgt[u][i][e];
+                run[e] += (x > 0.f) ? 0.f : x;
             }
+            b[i] = run;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float incl = row_scan16(run[e]);
+            const float ex = incl - run[e];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[i][e] += ex;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) B[j][e] = __shfl(incl, 16 * cg + 4 * j + 3);
         }
     };
-    // With dk = 128 the registers do not hold the next chunk's keys and gates
-    // beside the products, so each chunk loads its own at the top of its step.
-    constexpr bool KG_EARLY = DK == 64;
-    if (c_begin < c_end) {
-        load_qv(c_begin);
-        if constexpr (KG_EARLY) load_kg(c_begin);
-    }
-
-    for (int c = c_begin; c < c_end; ++c) {
-        const long long t0 = static_cast<long long>(c) * C;
-        const int clen = chunk_len(c);
-        if constexpr (!KG_EARLY) load_kg(c);
-        __syncthreads();  // the previous chunk's reads of q, k, b, v and the flags are done
-
-        // ---- store the chunk (rows past the end: zeros, log-gate 0)
-        {
-            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (!SO) {
+    // Exact-path vote for the chunk now in the registers (key waves only): a
+    // 16-token tile whose gate sum in some channel is below the bound, or NaN.
+    auto vote = [&](int c) {
+        if constexpr (!SO && !QW) {
+            bool bad = false;
 #pragma unroll
-                for (int m = 0; m < NU; ++m) {
-                    const int u = tid + m * kThreads, r = u / (DK / 4), c4 = 4 * (u % (DK / 4));
-                    *reinterpret_cast<f32x4*>(&sm.q[r * KSTR + c4]) = (r < clen) ? pq[m] : zero;
-                }
-            }
+            for (int u = 0; u < CPT; ++u) {
 #pragma unroll
-            for (int m = 0; m < NV; ++m) {
-                const int u = tid + m * kThreads, r = u / (DVS / 4), c4 = 4 * (u % (DVS / 4));
-                if (u < C * DVS / 4) *reinterpret_cast<f32x4*>(&sm.v[r * VSTR + c4]) = (r < clen) ? pv[m] : zero;
-            }
-            int bad = 0;
+                for (int e = 0; e < 4; ++e) {
+                    float run = 0.f;
 #pragma unroll
-            for (int u = 0; u < CPW; ++u) {
-                const int ch = 16 * W + c16 + 64 * u;
-                float cum[16];
-                float run = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    run += (16 * rq + i < clen) ? pg[u][i] : 0.f;
-                    cum[i] = run;
-                }
-                // tile totals of the four row quarters of this channel (lanes c16 + 16 q)
-                const float t0s = __shfl(run, c16), t1s = __shfl(run, c16 + 16);
-                const float t2s = __shfl(run, c16 + 32), t3s = __shfl(run, c16 + 48);
-                const float off = (rq > 0 ? t0s : 0.f) + (rq > 1 ? t1s : 0.f) + (rq > 2 ? t2s : 0.f);
-                const float tot = t0s + t1s + t2s + t3s;
-                if (!(tot >= -80.f)) bad = 1;
-                ltot[u] += tot;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 16 * rq + i;
-                    sm.b[r * KSTR + ch] = off + cum[i];
-                    // K^ = k e^{b_{e_J} - b_j}: the tile's total minus the running sum
-                    sm.k[r * KSTR + ch] = ((r < clen) ? pk[u][i] : 0.f) * __expf(run - cum[i]);
+                    for (int i = 0; i < 4; ++i) run += fminf(rgt[u][i][e], 0.f) + (rgt[u][i][e] - rgt[u][i][e]);
+                    // the tile's sum: this lane and the next three token groups
+                    float tile = run;
+                    tile += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, run), 0x101, 0xf, 0xf, true));
+                    tile += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, run), 0x102, 0xf, 0xf, true));
+                    tile += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, run), 0x103, 0xf, 0xf, true));
+                    bad = bad || ((tg & 3) == 0 && !(tile >= kTileBound));
                 }
             }
             const bool wbad = __any(bad);
-            if (l == 0) sm.unsafe[W] = wbad ? 1 : 0;
+            if (l == 0) sm.flag[c & 1][W] = wbad ? 1 : 0;
         }
-        __syncthreads();
-        const bool unsafe = (sm.unsafe[0] | sm.unsafe[1] | sm.unsafe[2] | sm.unsafe[3]) != 0;
-        if (unsafe) {
-            // the exact path works from the raw keys
-#pragma unroll
-            for (int u = 0; u < CPW; ++u) {
-                const int ch = 16 * W + c16 + 64 * u;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = 16 * rq + i;
-                    sm.k[r * KSTR + ch] = (r < clen) ? pk[u][i] : 0.f;
-                }
-            }
-            __syncthreads();
-        }
-        if (c + 1 < c_end) {
-            load_qv(c + 1);
-            if constexpr (KG_EARLY) load_kg(c + 1);
-        }
+    };
+    auto exact_of = [&](int c) {
+        return !SO && (sm.flag[c & 1][0] | sm.flag[c & 1][1] | sm.flag[c & 1][2] | sm.flag[c & 1][3]) != 0;
+    };
 
-        const int qi = 16 * I + l16;  // this lane's query row
-        const int last = clen - 1;
-        if (!unsafe) {
-            // ---- fast path (see the header): Q factors in registers, K^ in place of k
-            constexpr int NQ = DK / 4;
-            const int eI = 16 * I + 15;
-            float qd[NQ], qx[NQ];  // q_i e^{b_i - b_{e_I}} and q_i e^{b_i} for channels 4s + g
+    f32x4 ltot[CPT];  // state-only pass: log-gate totals of this lane's channels over the segment
 #pragma unroll
-            for (int s = 0; s < (SO ? 0 : NQ); ++s) {
-                const int ch = 4 * s + g;
-                const float qv = sm.q[qi * KSTR + ch], bq = sm.b[qi * KSTR + ch];
-                qd[s] = qv * __expf(bq - sm.b[eI * KSTR + ch]);
-                qx[s] = qv * __expf(bq);
-            }
+    for (int u = 0; u < CPT; ++u) ltot[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            f32x4 pacc[I + 1];
+    // ---- fold the chunk in the registers into a buffer set
+    auto fold = [&](Buf& bf, bool exact) {
+        if constexpr (FOLDX) {
 #pragma unroll
-            for (int J = 0; J <= (SO ? -1 : I); ++J) {
-                pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-                const int eJ = 16 * J + 15, kj = 16 * J + l16;
-#pragma unroll 4
-                for (int s = 0; s < NQ; ++s) {
-                    const int ch = 4 * s + g;
-                    const float f = (J == I) ? 1.f : __expf(sm.b[eI * KSTR + ch] - sm.b[eJ * KSTR + ch]);
-                    pacc[J] = mfma_f32(sm.k[kj * KSTR + ch], qd[s] * f, pacc[J]);
-                }
-            }
+            for (int u = 0; u < CPT; ++u) {
+                const int c0 = 16 * W + 4 * cg + 64 * u;
+                f32x4 b[4], B[4];
+                gate_sums(u, b, B);
+                // B[TT - 1] and B[TT] by selects (TT varies across lanes; no indexed registers)
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 boff = (TT == 0) ? zero : (TT == 1) ? B[0] : (TT == 2) ? B[1] : B[2];
+                const f32x4 tI = ((TT == 0) ? B[0] : (TT == 1) ? B[1] : (TT == 2) ? B[2] : B[3]) - boff;
+                const f32x4 bL = B[3];
+                if constexpr (QW) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)  // causal mask of the diagonal tile
-                if (16 * I + 4 * g + r > qi) pacc[I][r] = 0.f;
-
+                    for (int i = 0; i < 4; ++i) {
+                        const f32x4 x = rx[u][i].f();
+                        f32x4 y;
 #pragma unroll
-            for (int nt = 0; nt < (SO ? 0 : NT); ++nt) {
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-                for (int s = 0; s < NQ; ++s) o = mfma_f32(sm.st[(16 * nt + l16) * KSTR + 4 * s + g], qx[s], o);
+                        for (int e = 0; e < 4; ++e) y[e] = exact ? x[e] : x[e] * fexp(b[i][e] - boff[e]);
+                        sts4(&bf.qb[(4 * tg + i) * QS + c0], y);
+                    }
+                    if (TT > 0 && (tg & 3) == 0)
+                        sts4(&bf.fb[(6 + TT) * DK + c0], f32x4{fexp(boff[0]), fexp(boff[1]), fexp(boff[2]), fexp(boff[3])});
+                } else {
+                    f32x4 xk[4];
 #pragma unroll
-                for (int J = 0; J <= I; ++J)
+                    for (int i = 0; i < 4; ++i) xk[i] = rx[u][i].f();
+                    if (exact) {
+                        // raw k and b^T: the products form every factor on the spot
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        o = mfma_f32(sm.v[(16 * J + 4 * g + r) * VSTR + 16 * nt + l16], pacc[J][r], o);
-                if (qi < clen) *reinterpret_cast<f32x4*>(oh + (t0 + qi) * DV + 16 * nt + 4 * g) = o;
-            }
-
+                        for (int i = 0; i < 4; ++i) sts4(&bf.kb[(4 * tg + i) * QS + c0], xk[i]);
 #pragma unroll
-            for (int m = 0; m < SPW; ++m) {
-                const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-                const int ch = 16 * kt + l16;
-                const float bl = sm.b[last * KSTR + ch];
-                sacc[m] *= __expf(bl);
+                        for (int e = 0; e < 4; ++e)
+                            sts4(&bf.gt[(c0 + e) * CS + 4 * tg], f32x4{b[0][e], b[1][e], b[2][e], b[3][e]});
+                    } else {
+                        if constexpr (!SO) {
 #pragma unroll
-                for (int J = 0; J < C / 16; ++J) {
-                    const float f = __expf(bl - sm.b[(16 * J + 15) * KSTR + ch]);
+                            for (int i = 0; i < 4; ++i) {
+                                f32x4 y;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * J + 4 * g + r;
-                        sacc[m] = mfma_f32(sm.v[j * VSTR + 16 * nt + l16], sm.k[j * KSTR + ch] * f, sacc[m]);
+                                for (int e = 0; e < 4; ++e) y[e] = xk[i][e] * fexp(tI[e] - (b[i][e] - boff[e]));
+                                sts4(&bf.kb[(4 * tg + i) * QS + c0], y);
+                            }
+                        }
+                        // K' = k e^{b_L - b_j}, stored transposed
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sts4(&bf.gt[(c0 + e) * CS + 4 * tg],
+                                 f32x4{xk[0][e] * fexp(bL[e] - b[0][e]), xk[1][e] * fexp(bL[e] - b[1][e]),
+                                       xk[2][e] * fexp(bL[e] - b[2][e]), xk[3][e] * fexp(bL[e] - b[3][e])});
+                    }
+                    if ((tg & 3) == 0) {
+                        if constexpr (SO) {
+                            if (TT == 0) ltot[u] += bL;
+                        } else {
+                            if (!exact)
+                                sts4(&bf.fb[TT * DK + c0], f32x4{fexp(-tI[0]), fexp(-tI[1]), fexp(-tI[2]), fexp(-tI[3])});
+                            if (TT == 0) {
+                                const f32x4 d1 = B[1] - B[0], d2 = B[2] - B[0];
+                                sts4(&bf.fb[4 * DK + c0], f32x4{fexp(d1[0]), fexp(d1[1]), fexp(d1[2]), fexp(d1[3])});
+                                sts4(&bf.fb[5 * DK + c0], f32x4{fexp(d2[0]), fexp(d2[1]), fexp(d2[2]), fexp(d2[3])});
+                            } else if (TT == 1) {
+                                const f32x4 d3 = B[2] - B[1];
+                                sts4(&bf.fb[6 * DK + c0], f32x4{fexp(d3[0]), fexp(d3[1]), fexp(d3[2]), fexp(d3[3])});
+                            }
+                        }
+                        if (TT == 0) sts4(&bf.bl[c0], f32x4{fexp(bL[0]), fexp(bL[1]), fexp(bL[2]), fexp(bL[3])});
                     }
                 }
             }
-            __syncthreads();  // every wave is done reading the old state copy
-#pragma unroll
-            for (int m = 0; m < SPW; ++m) {
-                const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sm.st[(16 * nt + 4 * g + r) * KSTR + 16 * kt + l16] = sacc[m][r];
-            }
-            continue;
         }
+        if constexpr (QW) {
+            // values: columns 16 W + 4 cg + e of the slice, keys 4 tg .. 4 tg + 3, stored transposed
+            f32x4 xv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = rv[i].f();
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                sts4(&bf.vt[(16 * W + 4 * cg + e) * CS + 4 * tg], f32x4{xv[0][e], xv[1][e], xv[2][e], xv[3][e]});
+        }
+    };
 
-        // ---- exact path for chunks with strong gates
-        if constexpr (!SO) {
-        // ---- scores S^T[j][i] for key tiles J <= I: lane holds keys 16J + 4g + r of query qi
-        f32x4 pacc[I + 1];
+    // ---- products of a chunk from buffer set X
+    auto products = [&](const Buf& bf, long long t0, int clen, bool exact) {
+        if constexpr (OW) {
+            const int qrow = 16 * W + l16;
+            float qo[NQ];  // Q^ of query row qrow, channels NQ g + s (exact path: raw q)
 #pragma unroll
-        for (int J = 0; J < I; ++J) {
-            pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int eJ = 16 * J + 15, kj = 16 * J + l16;
-#pragma unroll 4
-            for (int s = 0; s < DK / 4; ++s) {
-                const int ch = 4 * s + g;
-                const float be = sm.b[eJ * KSTR + ch];
-                const float ka = sm.k[kj * KSTR + ch] * __expf(be - sm.b[kj * KSTR + ch]);
-                const float qb = sm.q[qi * KSTR + ch] * __expf(sm.b[qi * KSTR + ch] - be);
-                pacc[J] = mfma_f32(ka, qb, pacc[J]);
+            for (int s4 = 0; s4 < NQ / 4; ++s4) {
+                const f32x4 x = lds4(&bf.qb[qrow * QS + NQ * g + 4 * s4]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qo[4 * s4 + e] = x[e];
             }
-        }
-        {
-            // diagonal tile: one exponent per term, keys after the query masked
-            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            f32x4 pacc[W + 1];
+            if (!exact) {
+                // scores P^T[key 16 J + 4 g + r][query] = K^ (Q^ (.) F_WJ)^T
+                auto tile = [&](auto Jc) {
+                    constexpr int J = decltype(Jc)::value;
+                    pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 16 * I + 4 * g + r;
-                if (j <= qi) {
-                    float acc = 0.f;
-                    for (int ch = 0; ch < DK; ++ch)
-                        acc += sm.q[qi * KSTR + ch] * sm.k[j * KSTR + ch] *
-                               __expf(sm.b[qi * KSTR + ch] - sm.b[j * KSTR + ch]);
-                    d[r] = acc;
+                    for (int s4 = 0; s4 < NQ / 4; ++s4) {
+                        const f32x4 kx = lds4(&bf.kb[(16 * J + l16) * QS + NQ * g + 4 * s4]);
+                        f32x4 fx = {1.f, 1.f, 1.f, 1.f};
+                        if constexpr (J != W - 1) fx = lds4(&bf.fb[frow<W, J>() * DK + NQ * g + 4 * s4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) pacc[J] = mfma_f32(kx[e], qo[4 * s4 + e] * fx[e], pacc[J]);
+                    }
+                };
+                tile(std::integral_constant<int, 0>{});
+                if constexpr (W >= 1) tile(std::integral_constant<int, 1>{});
+                if constexpr (W >= 2) tile(std::integral_constant<int, 2>{});
+                if constexpr (W >= 3) tile(std::integral_constant<int, 3>{});
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pacc[W][r] = (4 * g + r > l16) ? 0.f : pacc[W][r];
+                if constexpr (W > 0) {  // the inter-chunk read takes Q^ (.) E_W
+#pragma unroll
+                    for (int s4 = 0; s4 < NQ / 4; ++s4) {
+                        const f32x4 ex = lds4(&bf.fb[(6 + W) * DK + NQ * g + 4 * s4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) qo[4 * s4 + e] *= ex[e];
+                    }
+                }
+            } else {
+                // exact path: scores term by term, e^{b_i - b_j} <= 1; then q e^{b_i} for the inter-chunk read
+#pragma unroll
+                for (int J = 0; J <= W; ++J)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * J + 4 * g + r;
+                        float acc = 0.f;
+                        if (j <= qrow) {
+                            for (int cc = 0; cc < DK; ++cc)
+                                acc += bf.qb[qrow * QS + cc] * bf.kb[j * QS + cc] *
+                                       fexp(bf.gt[cc * CS + qrow] - bf.gt[cc * CS + j]);
+                        }
+                        pacc[J][r] = acc;
+                    }
+#pragma unroll
+                for (int s = 0; s < NQ; ++s) qo[s] *= fexp(bf.gt[(NQ * g + s) * CS + qrow]);
+            }
+            // ---- O^T = S^T Q~^T + V^T P^T per 16-column value tile; rows past the end are not stored
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s4 = 0; s4 < NQ / 4; ++s4) {
+                    const f32x4 sx = lds4(&sm.sc[(16 * nt + l16) * QS + NQ * g + 4 * s4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o = mfma_f32(sx[e], qo[4 * s4 + e], o);
+                }
+#pragma unroll
+                for (int J = 0; J <= W; ++J) {
+                    const f32x4 vx = lds4(&bf.vt[(16 * nt + l16) * CS + 16 * J + 4 * g]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o = mfma_f32(vx[r], pacc[J][r], o);
+                }
+                if (qrow < clen) store4<BF>(oh + ((t0 + qrow) * DV + 16 * nt + 4 * g) * ESZ, o);
+            }
+        } else {
+            // ---- S = diag(e^{b_L}) S + K'^T V for this wave's tiles; lane group g contracts keys 16 g ..
+#pragma unroll
+            for (int t = 0; t < TN; ++t) {
+                const int m = (TF + t) % KT, n = (TF + t) / KT;
+                if (!exact) {
+                    sacc[t] *= lds4(&bf.bl[16 * m + 4 * g]);
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const f32x4 kx = lds4(&bf.gt[(16 * m + l16) * CS + 16 * g + 4 * s4]);
+                        const f32x4 vx = lds4(&bf.vt[(16 * n + l16) * CS + 16 * g + 4 * s4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sacc[t] = mfma_f32(kx[e], vx[e], sacc[t]);
+                    }
+                } else {
+                    // exact path: K' = k e^{b_L - b_j} and e^{b_L} from raw k and b^T
+                    const int ch = 16 * m + l16;
+                    const float bLc = bf.gt[ch * CS + C - 1];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) sacc[t][r] *= fexp(bf.gt[(16 * m + 4 * g + r) * CS + C - 1]);
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const f32x4 vx = lds4(&bf.vt[(16 * n + l16) * CS + 16 * g + 4 * s4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int key = 16 * g + 4 * s4 + e;
+                            const float kp = bf.kb[key * QS + ch] * fexp(bLc - bf.gt[ch * CS + key]);
+                            sacc[t] = mfma_f32(kp, vx[e], sacc[t]);
+                        }
+                    }
                 }
             }
-            pacc[I] = d;
         }
+    };
 
-        // ---- O^T = S_prev^T (Q e^{b})^T + V^T P^T, 16-byte stores of rows qi
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-            for (int s = 0; s < DK / 4; ++s) {
-                const int ch = 4 * s + g;
-                const float sa = sm.st[(16 * nt + l16) * KSTR + ch];
-                const float qb = sm.q[qi * KSTR + ch] * __expf(sm.b[qi * KSTR + ch]);
-                o = mfma_f32(sa, qb, o);
-            }
-#pragma unroll
-            for (int J = 0; J <= I; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    o = mfma_f32(sm.v[(16 * J + 4 * g + r) * VSTR + 16 * nt + l16], pacc[J][r], o);
-            if (qi < clen) *reinterpret_cast<f32x4*>(oh + (t0 + qi) * DV + 16 * nt + 4 * g) = o;
-        }
-        }  // !SO
+    // ---- the walk.  Chunk c uses buffer set (c - c_begin) % NB; its exact-path
+    // flag was voted when its gates arrived and is kept in a register.
+    if (c_begin < c_end) {
+        load_chunk(c_begin);
+        vote(c_begin);
+    }
+    lds_barrier();  // the first vote and the state copy
+    bool ex_cur = (c_begin < c_end) && exact_of(c_begin);
+    if (c_begin < c_end) {
+        fold(sm.op[0], ex_cur);
+        load_chunk(c_begin + 1);
+        if constexpr (NB == 2) vote(c_begin + 1);
+    }
+    lds_barrier();  // the first chunk's operands and the second chunk's vote
 
-        // ---- S = diag(e^{b_last}) S + sum_j diag(e^{b_last - b_j}) k_j v_j^T
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-            const int ch = 16 * kt + l16;
-            const float bl = sm.b[last * KSTR + ch];
-            sacc[m] *= __expf(bl);
-#pragma unroll
-            for (int J = 0; J < C / 16; ++J)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int j = 16 * J + 4 * g + r;
-                    const float kb = sm.k[j * KSTR + ch] * __expf(bl - sm.b[j * KSTR + ch]);
-                    sacc[m] = mfma_f32(sm.v[j * VSTR + 16 * nt + l16], kb, sacc[m]);
-                }
+    auto step = [&](int c, auto xc) {
+        constexpr int X = decltype(xc)::value;
+        const long long t0 = static_cast<long long>(c) * C;
+        const int clen = chunk_len(c);
+        if constexpr (NB == 2) {
+            // fold the next chunk into the other buffer set while this chunk's products run
+            const bool ex_next = (c + 1 < c_end) && exact_of(c + 1);
+            if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
+            load_chunk(c + 2);
+            products(sm.op[X], t0, clen, ex_cur);
+            vote(c + 2);       // the gates of chunk c + 2 have arrived by now
+            lds_barrier();     // operands of c + 1 written; every read of c's operands and of the state copy done
+            write_state_copy();
+            lds_barrier();
+            ex_cur = ex_next;
+        } else {
+            products(sm.op[0], t0, clen, ex_cur);
+            vote(c + 1);       // the gates of chunk c + 1 have arrived by now
+            lds_barrier();     // every read of c's operands and of the state copy done
+            write_state_copy();
+            const bool ex_next = (c + 1 < c_end) && exact_of(c + 1);
+            if (c + 1 < c_end) fold(sm.op[0], ex_next);
+            load_chunk(c + 2);
+            lds_barrier();
+            ex_cur = ex_next;
         }
-        __syncthreads();  // every wave is done reading the old state copy
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sm.st[(16 * nt + 4 * g + r) * KSTR + 16 * kt + l16] = sacc[m][r];
+    };
+    for (int c = c_begin; c < c_end; c += NB) {
+        step(c, std::integral_constant<int, 0>{});
+        if constexpr (NB == 2) {
+            if (c + 1 < c_end) step(c + 1, std::integral_constant<int, 1>{});
         }
     }
 
@@ -400,34 +657,32 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         // this segment's contribution (its end state from zero) and log-gate totals
         float* out = a.ws + (static_cast<long long>(bh) * (a.G - 1) + seg) * slot;
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-            *reinterpret_cast<f32x4*>(out + (16 * kt + l16) * DV + nbase + 16 * nt + 4 * g) = sacc[m];
-        }
-        if (nbase == 0 && rq == 0) {
+        for (int t = 0; t < TN; ++t) {
+            const int m = (TF + t) % KT, n = (TF + t) / KT;
 #pragma unroll
-            for (int u = 0; u < CPW; ++u) out[DK * DV + 16 * W + c16 + 64 * u] = ltot[u];
+            for (int r = 0; r < 4; ++r) out[(16 * m + 4 * g + r) * DV + nbase + 16 * n + l16] = sacc[t][r];
         }
-        return;
-    }
-    if (a.final_state && seg == a.G - 1) {
-        float* fs = a.final_state + static_cast<long long>(bh) * DK * DV + nbase;
+        if constexpr (!QW) {
+            if (nbase == 0 && tg == 0) {
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = W + 4 * m, nt = qt / KT, kt = qt % KT;
-            *reinterpret_cast<f32x4*>(fs + (16 * kt + l16) * DV + 16 * nt + 4 * g) = sacc[m];
+                for (int u = 0; u < CPT; ++u) *reinterpret_cast<f32x4*>(out + DK * DV + 16 * W + 4 * cg + 64 * u) = ltot[u];
+            }
+        }
+    } else if constexpr (!OW) {
+        if (a.final_state && seg == a.G - 1) {
+            float* fs = a.final_state + static_cast<long long>(bh) * DK * DV + nbase;
+#pragma unroll
+            for (int t = 0; t < TN; ++t) {
+                const int m = (TF + t) % KT, n = (TF + t) / KT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) fs[(16 * m + 4 * g + r) * DV + 16 * n + l16] = sacc[t][r];
+            }
         }
     }
 }
 
-// SO: the state-only pass over segments 0 .. G-2.  The 32-column slices at
-// dk = 64 are held to 256 registers (they need 254), so that two workgroups
-// share a CU and hide each other's latencies; the other variants use more.
-template <int DK, int NT>
-constexpr int gla_min_blocks() { return (DK == 64 && NT == 2) ? 2 : 1; }
-
-template <int DK, int NT, bool SO>
-__global__ void __launch_bounds__(kThreads, (gla_min_blocks<DK, NT>())) gla_kernel(const GlaArgs a) {
+template <bool BF, int DK, int NT, bool SO>
+__global__ void __launch_bounds__(kThreads, 1) gla_kernel(const GlaArgs a) {
     __shared__ Smem<DK, NT> sm;
     const int nseg = SO ? a.G - 1 : a.G;
     const int bhs = blockIdx.x / a.nslices;
@@ -435,55 +690,56 @@ __global__ void __launch_bounds__(kThreads, (gla_min_blocks<DK, NT>())) gla_kern
     const int nbase = (blockIdx.x % a.nslices) * Cfg<DK, NT>::DVS;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: body<DK, NT, 0, SO>(a, sm, bh, seg, nbase); break;
-        case 1: body<DK, NT, 1, SO>(a, sm, bh, seg, nbase); break;
-        case 2: body<DK, NT, 2, SO>(a, sm, bh, seg, nbase); break;
-        default: body<DK, NT, 3, SO>(a, sm, bh, seg, nbase); break;
+        case 0: body<BF, DK, NT, 0, SO>(a, sm, bh, seg, nbase); break;
+        case 1: body<BF, DK, NT, 1, SO>(a, sm, bh, seg, nbase); break;
+        case 2: body<BF, DK, NT, 2, SO>(a, sm, bh, seg, nbase); break;
+        case 3: body<BF, DK, NT, 3, SO>(a, sm, bh, seg, nbase); break;
+        case 4: body<BF, DK, NT, 4, SO>(a, sm, bh, seg, nbase); break;
+        case 5: body<BF, DK, NT, 5, SO>(a, sm, bh, seg, nbase); break;
+        case 6: body<BF, DK, NT, 6, SO>(a, sm, bh, seg, nbase); break;
+        default: body<BF, DK, NT, 7, SO>(a, sm, bh, seg, nbase); break;
     }
 }
 
-template <int DK, int NT>
+template <bool BF, int DK, int NT>
 hipError_t launch_t(const GlaArgs& a, hipStream_t stream) {
-    if constexpr (!fits<DK, NT>()) {
-        return hipErrorInvalidConfiguration;
-    } else {
-        const long long groups = static_cast<long long>(a.B) * a.H * a.nslices * a.G;
-        if (groups <= 0) return hipSuccess;
-        if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
-        if (a.G > 1) {
-            const long long sgroups = static_cast<long long>(a.B) * a.H * a.nslices * (a.G - 1);
-            hipLaunchKernelGGL((gla_kernel<DK, NT, true>), dim3(static_cast<unsigned>(sgroups)), dim3(kThreads), 0,
-                               stream, a);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        hipLaunchKernelGGL((gla_kernel<DK, NT, false>), dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, stream,
-                           a);
-        return hipGetLastError();
+    static_assert(fits<DK, NT>(), "LDS");
+    const long long groups = static_cast<long long>(a.B) * a.H * a.nslices * a.G;
+    if (groups <= 0) return hipSuccess;
+    if (groups > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.G > 1) {
+        const long long sgroups = static_cast<long long>(a.B) * a.H * a.nslices * (a.G - 1);
+        hipLaunchKernelGGL((gla_kernel<BF, DK, NT, true>), dim3(static_cast<unsigned>(sgroups)), dim3(kThreads), 0,
+                           stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
+    hipLaunchKernelGGL((gla_kernel<BF, DK, NT, false>), dim3(static_cast<unsigned>(groups)), dim3(kThreads), 0, stream,
+                       a);
+    return hipGetLastError();
 }
 
 }  // namespace
 }  // namespace gla
 
+// Value slices of 64 columns: the whole value width when dv = 64, two slices
+// (each forming Q K^T) when dv = 128.
 int gla_choose_nt(long long bh, int dk, int dv) {
-    // dk = dv = 64: 32-column slices, two workgroups per CU (measured on [4, 8, 2048, 64]: 65 us against
-    // 69 us for 64-column slices at one per CU, bit-identical results); otherwise the widest slice
-    // that fits, 64 columns at most (the segments supply the parallelism)
     (void)bh;
-    if (dk == 64 && dv == 64) return 2;
+    (void)dk;
     return dv >= 64 ? 4 : dv / 16;
 }
 
-int gla_target_groups(int dk, int nt) { return (dk == 64 && nt == 2) ? 512 : 256; }
+int gla_target_groups(int dk, int nt) {
+    (void)dk;
+    (void)nt;
+    return 256;  // one 8-wave workgroup per CU
+}
 
-hipError_t launch_gla(const GlaArgs& a, int dk, int nt, hipStream_t stream) {
-    if (dk == 64 && nt == 1) return gla::launch_t<64, 1>(a, stream);
-    if (dk == 64 && nt == 2) return gla::launch_t<64, 2>(a, stream);
-    if (dk == 64 && nt == 4) return gla::launch_t<64, 4>(a, stream);
-    if (dk == 128 && nt == 1) return gla::launch_t<128, 1>(a, stream);
-    if (dk == 128 && nt == 2) return gla::launch_t<128, 2>(a, stream);
-    if (dk == 128 && nt == 4) return gla::launch_t<128, 4>(a, stream);
+hipError_t launch_gla(const GlaArgs& a, bool bf16, int dk, int nt, hipStream_t stream) {
+    if (nt != 4) return hipErrorInvalidValue;
+    if (dk == 64) return bf16 ? gla::launch_t<true, 64, 4>(a, stream) : gla::launch_t<false, 64, 4>(a, stream);
+    if (dk == 128) return bf16 ? gla::launch_t<true, 128, 4>(a, stream) : gla::launch_t<false, 128, 4>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -79,13 +79,13 @@ struct SegArgs {
     float log2g[kMaxHeads];
 };
 
-// Arguments of the gated linear attention walk (fp32).
+// Arguments of the gated linear attention walk (q, k, v, out fp32 or bf16; log-gates fp32).
 struct GlaArgs {
-    const float* q;
-    const float* k;
-    const float* v;
-    const float* lg;     // [B][H][T][dk] log-gates (finite, <= 0)
-    float* out;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* lg;     // [B][H][T][dk] log-gates (finite, <= 0; values above 0 are taken as 0)
+    void* out;
     float* final_state;  // may be null
     int B, H, T;
     int dv;
@@ -137,7 +137,7 @@ int choose_walk_nt(long long bh, int dv, int target_groups, bool bf16, int chunk
 int gla_choose_nt(long long bh, int dk, int dv);
 // Workgroups the GLA walk aims for: two per CU where two fit.
 int gla_target_groups(int dk, int nt);
-hipError_t launch_gla(const GlaArgs& a, int dk, int nt, hipStream_t stream);
+hipError_t launch_gla(const GlaArgs& a, bool bf16, int dk, int nt, hipStream_t stream);
 
 // Widest value slice of the segmented walk whose workgroup fits in LDS (the
 // fewest recomputed Q K^T tiles); the segments provide the parallelism.

@@ -91,10 +91,15 @@ WORKLOADS = {
                     ("walk::walk_kernel<false, 64, 64, 4, 0>", 1)],
         "algorithmic": 4 * 8 * 2048 * 64 * 4 * 4 + 4 * 8 * 64 * 64 * 4, "sources": "F32_SOURCES"},
     "gla_gla_mh_f32": {
-        "what": "gla_fwd fp32 [4, 8, 2048, 64], final state",
-        "kernels": [("::gla_kernel<64, 2, true>", 1),
-                    ("::gla_kernel<64, 2, false>", 1)],
+        "what": "gla_fwd fp32 [4, 8, 2048, 64], final state (state-only pass + walk)",
+        "kernels": [("::gla_kernel<false, 64, 4, true>", 1),
+                    ("::gla_kernel<false, 64, 4, false>", 1)],
         "algorithmic": 4 * 8 * 2048 * 64 * 4 * 5 + 4 * 8 * 64 * 64 * 4, "sources": "GLA_SOURCES"},
+    "gla_gla_mh_bf16": {
+        "what": "gla_fwd bf16 q/k/v/out, fp32 log-gates, [4, 8, 2048, 64], final state",
+        "kernels": [("::gla_kernel<true, 64, 4, true>", 1),
+                    ("::gla_kernel<true, 64, 4, false>", 1)],
+        "algorithmic": 4 * 8 * 2048 * 64 * (4 * 2 + 4) + 4 * 8 * 64 * 64 * 4, "sources": "GLA_SOURCES"},
 }
 
 
@@ -252,6 +257,7 @@ def mfma(mfma_csv: str, stats_csv: str, out_dir: str = PROFILES) -> None:
         with open(os.path.join(out_dir, "mfma_fwd_ret_fwd_long_bf16.json"), "w") as f:
             json.dump(d, f, indent=1)
             f.write("\n")
+    out += ["", _source_hashes(b)]
     with open(os.path.join(out_dir, "mfma_bench_workloads.md"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -294,6 +300,7 @@ def sq(sq_csv: str, out_dir: str = PROFILES) -> None:
         wait = a.get("SQ_WAIT_INST_ANY", 0.0) / n / w / act if act > 0 else float("nan")
         out.append(f"| `{name.replace('void ret::', '')}` | {waves:,.0f} | {valu:,.0f} | {mfma_:,.0f} | {lds:,.0f} | "
                    f"{100 * conf:.1f} % | {wait:.2f} |")
+    out += ["", _source_hashes(_bench())]
     with open(os.path.join(out_dir, "sq_bench_workloads.md"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -309,7 +316,15 @@ BENCH_LINES = [("retention forward (long bf16, state + walk kernels)", ("rooflin
                ("elu+1 decode step", ("linear_attn_decode", "us_per_step"), 1e3, "ns per step"),
                ("linear attention [8, 16, 8192, 64] bf16", ("linear_attn", "ms_per_call"), 1e6, "ns per call"),
                ("fp32 forward [4, 8, 2048, 64]", ("fwd_f32", "ms_per_call"), 1e6, "ns per call"),
-               ("gated linear attention fp32 [4, 8, 2048, 64]", ("gla_f32", "ms_per_call"), 1e6, "ns per call")]
+               ("gated linear attention fp32 [4, 8, 2048, 64]", ("gla_f32", "ms_per_call"), 1e6, "ns per call"),
+               ("gated linear attention bf16 [4, 8, 2048, 64]", ("gla_bf16", "ms_per_call"), 1e6, "ns per call")]
+
+
+def _source_hashes(b) -> str:
+    """The hashes of the kernel sources a summary was taken with (bench.py's source lists)."""
+    return ("Source hashes: segment kernels " + b.sources_sha(b.FWD_SOURCES) + ", decode "
+            + b.sources_sha(b.DECODE_SOURCES) + ", fp32 walk " + b.sources_sha(b.F32_SOURCES) + ", GLA "
+            + b.sources_sha(b.GLA_SOURCES) + ".")
 
 
 def stats(stats_csv: str, bench_log: str, out_dir: str = PROFILES) -> None:
@@ -333,9 +348,7 @@ def stats(stats_csv: str, bench_log: str, out_dir: str = PROFILES) -> None:
     for label, (k1, k2), mul, unit in BENCH_LINES:
         if k1 in res and k2 in res[k1]:
             out.append(f"- {label}: {res[k1][k2] * mul:,.0f} {unit}")
-    out += ["", "Source hashes: segment kernels " + b.sources_sha(b.FWD_SOURCES) + ", decode "
-            + b.sources_sha(b.DECODE_SOURCES) + ", fp32 walk " + b.sources_sha(b.F32_SOURCES) + ", GLA "
-            + b.sources_sha(b.GLA_SOURCES) + "."]
+    out += ["", _source_hashes(b)]
     with open(os.path.join(out_dir, "kernel_stats_bench_workloads.md"), "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))

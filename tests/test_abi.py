@@ -371,7 +371,7 @@ def _gla(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=rc.RET_BF16), -3),
+    (dict(dtype=7), -3),
     (dict(lg=None), -1),
     (dict(dk=32), -2),
     (dict(lg=FAKE * 4 + 4), -7),
@@ -386,12 +386,23 @@ def test_gla_rejects(kw, code):
 
 def test_gla_empty_batch():
     assert _gla(_lib(), B=0) == 0
+    assert _gla(_lib(), B=0, dtype=rc.RET_BF16) == 0
+
+
+def test_gla_bf16_gates_stay_fp32():
+    """bf16 q, k, v and out, fp32 log-gates: an output that starts where a
+    bf16-sized gate tensor would end still overlaps the fp32 gates."""
+    lib = _lib()
+    nq16 = 2 * 16 * 64 * 2  # bytes of a [1, 2, 16, 64] bf16 tensor; the fp32 gates take twice that
+    assert _gla(lib, dtype=rc.RET_BF16, lg=FAKE * 4, out=FAKE * 4 + nq16) == -8
+    assert "log_gate" in lib.retention_last_error().decode()
 
 
 def test_gla_workspace():
     lib = _lib()
     n = lib.gla_fwd_workspace_bytes(4, 8, 2048, 64, 64, rc.RET_F32)
     assert n > 0 and n % ((64 * 64 + 64) * 4 * 32) == 0
+    assert lib.gla_fwd_workspace_bytes(4, 8, 2048, 64, 64, rc.RET_BF16) == n  # fp32 states either way
     big = 1 << 28  # 256 MiB apart: no overlap between the fake tensors
     assert _gla(lib, B=4, H=8, T=2048, q=big, k=2 * big, v=3 * big, lg=4 * big, out=5 * big) == -9
 

@@ -5,9 +5,11 @@ The oracle runs S_t = diag(exp(lg_t)) S_{t-1} + k_t^T v_t token by token; the
 kernel walks 64-token chunks with exponentials of running log-gate sums.
 Gates are log-sigmoids of Gaussian logits, from slow forgetting (gate about
 0.95) to fast (about 0.1), plus isolated near-resets; every (dk, dv) pair,
-ragged lengths, both slice widths, the final state, and the two special cases
-the pages name (a constant gate is retention, a unit gate linear attention).
-Tolerance: relative Frobenius error 1e-4 (fp32).
+ragged lengths, one and two value slices, the final state, and the two
+special cases the pages name (a constant gate is retention, a unit gate linear
+attention); bf16 q, k, v and out (fp32 gates and arithmetic) on the same
+cases; gates above 1 are taken as 1.
+Tolerance: relative Frobenius error 1e-4 (fp32), 2e-2 (bf16).
 """
 import numpy as np
 import pytest
@@ -21,10 +23,11 @@ from tests import parity
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
+TOLS = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def _inputs(seed, B, H, T, dk, dv, mu):
-    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, dtype="f32", scale=1.0 / np.sqrt(dk))
+def _inputs(seed, B, H, T, dk, dv, mu, dtype="f32"):
+    w = wl.WORKLOADS["ret_fwd_mh_f32"].with_(B=B, H=H, T=T, dk=dk, dv=dv, dtype=dtype, scale=1.0 / np.sqrt(dk))
     inp = wl.make_inputs(w, seed)
     g = torch.Generator().manual_seed(seed + 900)
     inp["lg"] = torch.nn.functional.logsigmoid(torch.randn((B, H, T, dk), generator=g) + mu).float()
@@ -35,13 +38,13 @@ def _run(inp):
     q, k, v, lg = (inp[n].cuda() for n in ("q", "k", "v", "lg"))
     out, fs = rc.gla_fwd(q, k, v, lg)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), fs.cpu().numpy()
+    return out.float().cpu().numpy(), fs.cpu().numpy()
 
 
-def _check(tag, out, fs, inp):
+def _check(tag, out, fs, inp, tol=TOL):
     ref, ref_s = oracle.gla_recurrent(inp["q"], inp["k"], inp["v"], inp["lg"], nthreads=8)
-    parity.check(f"{tag} out", out, ref, TOL)
-    parity.check(f"{tag} state", fs, ref_s, TOL)
+    parity.check(f"{tag} out", out, ref, tol)
+    parity.check(f"{tag} state", fs, ref_s, tol)
 
 
 @pytest.mark.parametrize("mu", [3.0, 0.0, -2.0])
@@ -115,3 +118,45 @@ def test_gla_mixed_gate_strength():
         inp["lg"][:, :, c0:c0 + 64] = strong[:, :, c0:c0 + 64]
     out, fs = _run(inp)
     _check("gla mixed gate strength", out, fs, inp)
+
+
+@pytest.mark.parametrize("mu", [3.0, -2.0])
+@pytest.mark.parametrize("dk,dv,T", [(64, 64, 333), (128, 128, 300), (64, 128, 129), (128, 64, 200)])
+def test_gla_bf16_small_full(mu, dk, dv, T):
+    """bf16 q, k, v and out with fp32 gates; the oracle reads the rounded inputs."""
+    w, inp = _inputs(81, 2, 3, T, dk, dv, mu, dtype="bf16")
+    out, fs = _run(inp)
+    _check(f"gla bf16 mu={mu} dk={dk} dv={dv} T={T}", out, fs, inp, tol=TOLS["bf16"])
+
+
+@pytest.mark.parametrize("G", [1, 3])
+def test_gla_bf16_segments_and_mixed_gates(G, plan):
+    plan(segments=G)
+    w, inp = _inputs(82, 2, 2, 700, 64, 64, 2.0, dtype="bf16")
+    g = torch.Generator().manual_seed(83)
+    strong = torch.nn.functional.logsigmoid(torch.randn((2, 2, 700, 64), generator=g) - 2.5)
+    inp["lg"][:, :, 128:192] = strong[:, :, 128:192]  # one chunk on the exact path
+    out, fs = _run(inp)
+    _check(f"gla bf16 G={G} mixed", out, fs, inp, tol=TOLS["bf16"])
+
+
+def test_gla_gates_above_one_are_taken_as_one():
+    """A log-gate above 0 (a gate above 1) is outside the model; the kernel
+    takes it as 0, so the result equals the oracle on the clamped gates."""
+    w, inp = _inputs(84, 1, 2, 300, 64, 64, 1.0)
+    lg = inp["lg"].clone()
+    lg[:, :, 50:60] = 0.7
+    lg[:, 1, 200, :7] = 3.0
+    q, k, v = (inp[n].cuda() for n in ("q", "k", "v"))
+    out, fs = rc.gla_fwd(q, k, v, lg.cuda())
+    torch.cuda.synchronize()
+    clamped = dict(inp, lg=torch.clamp(lg, max=0.0))
+    _check("gla gates above one", out.cpu().numpy(), fs.cpu().numpy(), clamped)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gla_bench_shape(dtype):
+    """[4, 8, 2048, 64] with log-sigmoid(N(2, 1)) gates, the benchmark's GLA workload, in full."""
+    w, inp = _inputs(85, 4, 8, 2048, 64, 64, 2.0, dtype=dtype)
+    out, fs = _run(inp)
+    _check(f"gla [4,8,2048,64] {dtype}", out, fs, inp, tol=TOLS[dtype])
