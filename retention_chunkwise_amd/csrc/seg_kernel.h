@@ -471,38 +471,63 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         if (seg > 0) {
-            // piece p of segment j is decayed by gamma^(L (seg-1-j) + Lp (pieces-1-p))
+            // piece p of segment j is decayed by gamma^(L (seg-1-j) + Lp (pieces-1-p)); the next
+            // slot's values are loaded while the current one is added
             const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * a.pieces * Cf::WS;
             const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
             const float lpiece = lseg / static_cast<float>(a.pieces);
-            for (int jp = 0; jp < seg * a.pieces; ++jp) {
-                const int j = jp / a.pieces, pc = jp % a.pieces;
-                const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
-                                         lpiece * static_cast<float>(a.pieces - 1 - pc)));
-                const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
-                if (!ZN && a.ws_tr) {
-                    // S[16m + 4g + r][16n + l16] is element l16 % 4 of lane 16 (l16 / 4) + 4g + r in
-                    // tile (n, m) of the transposed state
+            const bool tr = !ZN && a.ws_tr;
+            const int nslot = seg * a.pieces;
+            // value tiles in groups of NG, so that two slots' values of a group stay in registers
+            constexpr int NG = NVT < 4 ? NVT : 4;
+            auto group = [&](auto n0c) {
+                constexpr int N0 = decltype(n0c)::value;
+                constexpr bool ZG = ZN && N0 == 0;  // the normaliser travels with the first group
+                struct Slot {
+                    f32x4 s[SKT][NG];
+                    float z[SKT];
+                };
+                auto ld = [&](int jp, Slot& x) {
+                    const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
 #pragma unroll
                     for (int mi = 0; mi < SKT; ++mi) {
                         const int m = SKT * P + mi;
 #pragma unroll
-                        for (int n = 0; n < NVT; ++n)
+                        for (int nn = 0; nn < NG; ++nn) {
+                            const int n = N0 + nn;
+                            if (tr) {
+                                // S[16m + 4g + r][16n + l16] is element l16 % 4 of lane 16 (l16 / 4) + 4g + r
+                                // in tile (n, m) of the transposed state
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                sacc[mi][n][r] += wj * sj[((n * Cf::NKT + m) << 8) +
-                                                          ((16 * (l16 >> 2) + 4 * g + r) << 2) + (l16 & 3)];
+                                for (int r = 0; r < 4; ++r)
+                                    x.s[mi][nn][r] = sj[((n * Cf::NKT + m) << 8) +
+                                                        ((16 * (l16 >> 2) + 4 * g + r) << 2) + (l16 & 3)];
+                            } else {
+                                x.s[mi][nn] = *reinterpret_cast<const f32x4*>(sj + ws_tile_off(m, n, NVT, l));
+                            }
+                        }
+                        x.z[mi] = ZG ? sj[Cf::STATE + 16 * m + l16] : 0.f;
                     }
-                    continue;
-                }
+                };
+                Slot cur, nxt;
+                ld(0, cur);
+                for (int jp = 0; jp < nslot; ++jp) {
+                    if (jp + 1 < nslot) ld(jp + 1, nxt);
+                    const int j = jp / a.pieces, pc = jp % a.pieces;
+                    const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
+                                             lpiece * static_cast<float>(a.pieces - 1 - pc)));
 #pragma unroll
-                for (int mi = 0; mi < SKT; ++mi) {
+                    for (int mi = 0; mi < SKT; ++mi) {
 #pragma unroll
-                    for (int n = 0; n < NVT; ++n)
-                        sacc[mi][n] += wj * *reinterpret_cast<const f32x4*>(sj + ws_tile_off(SKT * P + mi, n, NVT, l));
-                    if constexpr (ZN) zacc[mi] += wj * sj[Cf::STATE + 16 * (SKT * P + mi) + l16];
+                        for (int nn = 0; nn < NG; ++nn) sacc[mi][N0 + nn] += wj * cur.s[mi][nn];
+                        if constexpr (ZG) zacc[mi] += wj * cur.z[mi];
+                    }
+                    if (jp + 1 < nslot) cur = nxt;
                 }
-            }
+            };
+            group(std::integral_constant<int, 0>{});
+            if constexpr (NVT > 4) group(std::integral_constant<int, 4>{});
+            static_assert(NVT <= 8, "prologue groups");
         }
         if (a.init_state) {
             // the state before token 0, decayed over the seg * L tokens before this segment
