@@ -615,6 +615,22 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
         }
     };
 
+    // phi on the K chunk in buffer b, in place; rows past the end (loaded as
+    // zeros) stay zero rather than phi(0) = 1
+    auto phi_pass = [&](int b, int cl) {
+        if constexpr (LIN) {
+            constexpr int UPT = C * DK / 8 / kThreads;  // 16-byte units per thread
+#pragma unroll
+            for (int i = 0; i < UPT; ++i) {
+                const int u = threadIdx.x + kThreads * i;
+                if (u / KRU < cl) {
+                    bf16x8* pk = reinterpret_cast<bf16x8*>(tl.k[b] + 8 * u);
+                    *pk = phi8(*pk);
+                }
+            }
+        }
+    };
+
     auto step = [&](int c, auto bufc) {
         constexpr int B = decltype(bufc)::value;
         const long long t0 = static_cast<long long>(c) * C;
@@ -623,29 +639,34 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 
         // This chunk's loads were issued during the previous step; the only
         // vector-memory ops issued after them are the previous step's output
-        // stores, and vector-memory ops complete in issue order.
-        if (c == c_begin) wait_vmcnt<0>();
-        else wait_vmcnt<STORES>();
-        lds_barrier();  // chunk in LDS everywhere, state copy written
+        // stores, and vector-memory ops complete in issue order.  Linear
+        // attention waits for them at the end of the previous step instead,
+        // to apply phi there (the first chunk: here).
+        if (c == c_begin) {
+            wait_vmcnt<0>();
+            if constexpr (LIN) {
+                lds_barrier();
+                phi_pass(B, clen);
+            }
+        } else if constexpr (!LIN) {
+            wait_vmcnt<STORES>();
+        }
+        lds_barrier();  // chunk in LDS everywhere (phi applied), state copy written
         load_chunk(c + 1, std::integral_constant<int, 1 - B>{});
 
         const unsigned short* kb = tl.k[B];
         const unsigned short* vb = tl.v[B];
-
-        if constexpr (LIN) {
-            // phi on the K chunk, in place; rows past the end (loaded as zeros)
-            // stay zero rather than phi(0) = 1
-            constexpr int UPT = C * DK / 8 / kThreads;  // 16-byte units per thread
-#pragma unroll
-            for (int i = 0; i < UPT; ++i) {
-                const int u = threadIdx.x + kThreads * i;
-                if (u / KRU < clen) {
-                    bf16x8* pk = reinterpret_cast<bf16x8*>(tl.k[B] + 8 * u);
-                    *pk = phi8(*pk);
-                }
+        // Linear attention: the end of this step waits for chunk c + 1's loads
+        // and applies phi to its K in place before the next step's barrier.
+        auto end_step = [&]() {
+            if constexpr (LIN) {
+                wait_vmcnt<STORES>();
+                lds_barrier();  // chunk c + 1 in LDS everywhere; chunk c's K read by every wave
+                if (c + 1 < c_end) phi_pass(1 - B, chunk_len(c + 1));
+            } else {
+                lds_barrier();
             }
-            lds_barrier();
-        }
+        };
 
         if constexpr (OW) {
             LaneOff lk = lk0;
@@ -717,10 +738,16 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
                     float tp = 0.f, tz = 0.f;
+                    f32x4 ones_acc = {0.f, 0.f, 0.f, 0.f};
                     if constexpr (LIN) {
+                        // row sums of the bf16 weights on the matrix core: a ones
+                        // operand against P^T leaves every key's weight summed in
+                        // each row of the tile (all four lane groups alike)
+                        const bf16x8 ones = __builtin_bit_cast(bf16x8, u16x8{0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80,
+                                                                             0x3f80, 0x3f80, 0x3f80});
 #pragma unroll
                         for (int js = 0; js < NB; ++js)
-                            if (2 * js <= its(s)) tp += sum8(pb[s][js]);
+                            if (2 * js <= its(s)) ones_acc = mfma_bf16(ones, pb[s][js], ones_acc);
                     } else {
                         tp = psum[s];
                     }
@@ -733,7 +760,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                         for (int i = 0; i < 4; ++i) tz += bf2f(e[i]) * z0[i] + bf2f(e[i + 4]) * z1[i];
                     }
                     if constexpr (LIN) {
-                        rden[s] = 1.f / (sum_over_groups(tp + tz) + a.eps);
+                        rden[s] = 1.f / (ones_acc[0] + sum_over_groups(tz) + a.eps);
                     } else {
                         const float r = sum_over_groups(tp + xi[s] * tz);
                         rden[s] = 1.f / fmaxf(fabsf(r), 1.f);
@@ -857,7 +884,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
                     store_pair(pa, oacc);
                 }
             }
-            lds_barrier();  // every O-wave is done reading the old state copy
+            end_step();  // every O-wave is done reading the old state copy
         } else {
             LaneOff lk = lk0, lv = lv0;
             opaque<0>(lk);
@@ -925,7 +952,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 #pragma unroll
                 for (int mi = 0; mi < SKT; ++mi) zacc[mi] = (LIN ? 1.f : gc) * zacc[mi] + sum_over_groups(zsum[mi]);
             }
-            lds_barrier();  // every O-wave is done reading the old state copy
+            end_step();  // every O-wave is done reading the old state copy
             write_state_copy();
         }
     };
