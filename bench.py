@@ -33,8 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = ("chunkwise retention fwd tokens/s + TFLOP/s (% MFMA peak); decode GB/s (% HBM)")
 PROFILES = os.path.join(ROOT, "profiles")
 # sources of the kernels whose HBM counters are committed under profiles/
-FWD_SOURCES = ["retention_chunkwise_amd/csrc/seg_kernel.h", "retention_chunkwise_amd/csrc/kcommon.h",
-               "retention_chunkwise_amd/csrc/internal.h"]
+FWD_SOURCES = ["retention_chunkwise_amd/csrc/seg_kernel.h", "retention_chunkwise_amd/csrc/seg_bwd.h",
+               "retention_chunkwise_amd/csrc/kcommon.h", "retention_chunkwise_amd/csrc/internal.h"]
 DECODE_SOURCES = ["retention_chunkwise_amd/csrc/decode.hip", "retention_chunkwise_amd/csrc/internal.h"]
 F32_SOURCES = ["retention_chunkwise_amd/csrc/walk_kernel.h", "retention_chunkwise_amd/csrc/kcommon.h",
                "retention_chunkwise_amd/csrc/internal.h"]
@@ -267,7 +267,7 @@ def main():
             "workload": w.name + " backward (dq, dk, dv given dout)", "ms_per_call": b_kern,
             "tokens_per_s": tokens / (b_wall * 1e-3), "ratio_to_forward": b_kern / kern_ms,
             "tflops": 3 * fl_dense / (b_kern * 1e-3) / 1e12,
-            "roofline": {"kernel": "retention_bwd: three segment walks (dq forward; dk, dv time-reversed)",
+            "roofline": {"kernel": "retention_bwd: fused time-reversed walk for dk and dv, then the dq walk",
                          "bound": "hbm", "achieved": b_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": b_gbs / M.PEAK_HBM_GBS, "traffic": (b_tr["bytes_per_launch"] if b_tr else None),
                          "algorithmic_bytes_per_launch": b_by},
@@ -284,7 +284,7 @@ def main():
         res["backward_from_fwd"] = {
             "workload": w.name + " backward given the forward's segment states (retention_bwd_from_fwd)",
             "ms_per_call": f_kern, "tokens_per_s": tokens / (f_wall * 1e-3), "ratio_to_forward": f_kern / kern_ms,
-            "roofline": {"kernel": "retention_bwd_from_fwd: dv walk + state pass, dk walk, dq walk (no state pass)",
+            "roofline": {"kernel": "retention_bwd_from_fwd: fused dk/dv walk + its state pass, dq walk (no state pass)",
                          "bound": "hbm", "achieved": f_gbs, "peak": M.PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": f_gbs / M.PEAK_HBM_GBS, "traffic": (f_tr["bytes_per_launch"] if f_tr else None),
                          "algorithmic_bytes_per_launch": b_by},

@@ -250,15 +250,22 @@ bool plan_bwd_walk(long long bh, int T, int chunk, int dk, int dv, int dtype, Se
     return plan_slices(bh, T, chunk, dk, dv, false, false, p);
 }
 
-// The three walks of the backward pass: dq = fwd(dout, v, k) with widths
-// (dv, dk), dk = reversed fwd(v, dout, q) with widths (dv, dk), dv = reversed
-// fwd(k, q, dout) with widths (dk, dv).  They run one after another on one
-// stream (dv, dk, dq) and share the workspace, which must hold the largest
-// plan.
+// The walks of the backward pass: dq = fwd(dout, v, k) with widths (dv, dk)
+// (plans[0]); dk = reversed fwd(v, dout, q) with widths (dv, dk) (plans[1])
+// and dv = reversed fwd(k, q, dout) with widths (dk, dv) (plans[2]).  bf16
+// computes dk and dv in one fused reverse walk of 64-token chunks over the
+// plan of the dv walk (plans[1] = plans[2]).  They run one after another on
+// one stream (dv, dk or the fused walk, then dq) and share the workspace,
+// which must hold the largest plan.
 bool plan_bwd(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan plans[3], size_t* ws_max) {
     if (!plan_bwd_walk(bh, T, chunk, dv, dk, dtype, &plans[0])) return false;
-    plans[1] = plans[0];
-    if (!plan_bwd_walk(bh, T, chunk, dk, dv, dtype, &plans[2])) return false;
+    if (dtype == RET_BF16) {
+        if (!plan_segments(bh, T, 64, dk, dv, false, &plans[2])) return false;
+        plans[1] = plans[2];
+    } else {
+        plans[1] = plans[0];
+        if (!plan_bwd_walk(bh, T, chunk, dk, dv, dtype, &plans[2])) return false;
+    }
     *ws_max = plans[0].ws_bytes > plans[2].ws_bytes ? plans[0].ws_bytes : plans[2].ws_bytes;
     return true;
 }
@@ -679,7 +686,23 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
     const bool share = plans[1].path == plans[2].path && plans[1].G == plans[2].G && plans[1].cps == plans[2].cps &&
                        plans[1].chunk == plans[2].chunk &&
                        (plans[1].path == FwdPath::kSlice || plans[1].pieces == plans[2].pieces);
-    for (int i = 0; i < 3; ++i) {
+    const bool fused = dtype == RET_BF16;
+    if (fused) {
+        // dk and dv from one reverse walk: queries k (for dv) and v (for dk), keys and
+        // values q and dout
+        ret::SegArgs sa{};
+        sa.G = plans[2].G;
+        sa.cps = plans[2].cps;
+        sa.pieces = plans[2].pieces;
+        sa.q = k; sa.k = q; sa.v = dout; sa.out = dv;
+        sa.q2 = v; sa.out2 = dk;
+        sa.ws = plans[2].ws_bytes ? static_cast<float*>(workspace) : nullptr;
+        sa.B = B; sa.H = H; sa.T = T;
+        memcpy(sa.log2g, log2g, sizeof(sa.log2g));
+        const hipError_t e = ret::launch_seg_bwd_kv(sa, d_k, d_v, st);
+        if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    }
+    for (int i = fused ? 2 : 0; i < 3; ++i) {
         const Walk& w = walks[i];
         const SegPlan& pl = *wplans[i];
         const bool tr = (i == 1 && share) || (i == 2 && dq_shares);

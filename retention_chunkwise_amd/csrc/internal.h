@@ -76,6 +76,8 @@ struct SegArgs {
     int ws_tr;           // retention only: ws already holds the segment states of a walk over the same
                          // segments with key and value roles swapped (shape dv x dk); the state pass
                          // is skipped and the walk reads them transposed (ws is then only read)
+    const void* q2;      // fused backward walk only: the second query input (v), width dv
+    void* out2;          // fused backward walk only: the second output (dk), width dk
     float log2g[kMaxHeads];
 };
 
@@ -123,6 +125,9 @@ hipError_t launch_seg_norm_c128(const SegArgs& a, int dk, int dv, bool group, hi
 hipError_t launch_seg_rev(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_rev_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
 hipError_t launch_seg_rev_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
+// Fused reverse walk of the backward pass (64-token chunks): with a.q = k,
+// a.q2 = v, a.k = q, a.v = dout it writes dv to a.out and dk to a.out2.
+hipError_t launch_seg_bwd_kv(const SegArgs& a, int dk, int dv, hipStream_t stream);
 
 // Segment count for the segment-split forward: enough (b, h, segment)
 // workgroups to occupy the chip, at least `min_cps` chunks per segment.

@@ -53,10 +53,10 @@ WORKLOADS = {
                     (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
         "algorithmic": 2149580800, "sources": "FWD_SOURCES"},
     "bwd_ret_fwd_long_bf16": {
-        "what": "retention_bwd on the long workload: dv walk (reversed, with the state pass), dk walk "
-                "(reversed, reading the dv walk's segment states), dq walk (forward)",
+        "what": "retention_bwd on the long workload: the fused reverse walk for dk and dv (with its state "
+                "pass), then the dq walk (forward, with its state pass)",
         "kernels": [(SEG + "state_kernel<128, 128, 0, true>", 1),
-                    (SEG + "walk_kernel<128, 128, 128, 0, true>", 2),
+                    (SEG + "bwd_kv_kernel<128, 128>", 1),
                     (SEG + "state_kernel<128, 128, 0, false>", 1),
                     (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
         "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
@@ -64,7 +64,7 @@ WORKLOADS = {
         "what": "retention_bwd_from_fwd on the long workload: as retention_bwd, but the dq walk reads the "
                 "forward's segment states and runs no state pass",
         "kernels": [(SEG + "state_kernel<128, 128, 0, true>", 1),
-                    (SEG + "walk_kernel<128, 128, 128, 0, true>", 2),
+                    (SEG + "bwd_kv_kernel<128, 128>", 1),
                     (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
         "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
     "fwd_normalized_ret_fwd_long_bf16": {
