@@ -27,8 +27,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libretention.so")
 SOURCES = ["capi.hip", "walk.hip", "walk_ret_bf16.hip", "walk_ret_f32.hip", "walk_lin_bf16.hip",
            "walk_lin_f32.hip", "walk_norm_f32.hip", "rownorm.hip", "decode.hip", "seg_ret_bf16_c64.hip", "seg_ret_bf16_c128.hip",
-           "seg_lin_bf16_c64.hip", "seg_lin_bf16_c128.hip", "seg_rev_bf16_c64.hip", "seg_rev_bf16_c128.hip",
-           "seg_norm_bf16_c64.hip", "seg_norm_bf16_c128.hip", "seg_bwd_bf16.hip", "gla.hip"]
+           "seg_lin_bf16_c64.hip", "seg_lin_bf16_c128.hip", "seg_norm_bf16_c64.hip", "seg_norm_bf16_c128.hip", "seg_bwd_bf16.hip", "gla.hip"]
 ARCH = "gfx950"
 
 

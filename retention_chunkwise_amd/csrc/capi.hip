@@ -226,7 +226,7 @@ struct FwdState {
 // Launches the segment-split forward (bf16) with a checked plan and workspace.
 hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k, const void* v, void* out,
                                const FwdState& fst, void* workspace, const float* log2g, float eps, int B, int H,
-                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st, bool reverse = false,
+                               int T, int chunk, int dk, int dv, bool linattn, hipStream_t st,
                                bool ws_transposed = false) {
     ret::SegArgs sa{};
     sa.G = plan.G;
@@ -239,12 +239,11 @@ hipError_t launch_segment_path(const SegPlan& plan, const void* q, const void* k
     sa.B = B; sa.H = H; sa.T = T; sa.eps = eps;
     sa.ws_tr = ws_transposed ? 1 : 0;
     if (log2g) memcpy(sa.log2g, log2g, sizeof(sa.log2g));
-    if (reverse) return ret::launch_seg_rev(sa, chunk, dk, dv, st);
     return ret::launch_seg(sa, chunk, dk, dv, linattn, st);
 }
 
-// Plan of one walk of the backward pass: bf16 always takes the segment path
-// (its kernels have a time-reversed variant), fp32 the value-slice path.
+// Plan of one walk of the backward pass: bf16 takes the segment path (its dk
+// and dv come from the fused reverse walk), fp32 the value-slice path.
 bool plan_bwd_walk(long long bh, int T, int chunk, int dk, int dv, int dtype, SegPlan* p) {
     if (dtype == RET_BF16) return plan_segments(bh, T, chunk, dk, dv, false, p);
     return plan_slices(bh, T, chunk, dk, dv, false, false, p);
@@ -677,9 +676,9 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
         int wk, wv;
         bool rev;
     };
-    // dv first: its segment states sum q_s dout_s^T, the transpose of what the dk walk needs
-    // (dout_s q_s^T over the same reversed segments), so on the segment path the dk walk reads
-    // them transposed instead of running its own state pass
+    // fp32: dv first; its segment states sum q_s dout_s^T, the transpose of what the dk walk
+    // needs (dout_s q_s^T over the same reversed segments), so the dk walk reads them
+    // transposed instead of running its own state pass
     const Walk walks[3] = {{k, q, dout, dv, d_k, d_v, true}, {v, dout, q, dk, d_v, d_k, true},
                            {dout, v, k, dq, d_v, d_k, false}};
     const SegPlan* wplans[3] = {&plans[2], &plans[1], &plans[0]};
@@ -707,10 +706,14 @@ int bwd_impl(const char* fn, const void* q, const void* k, const void* v, const 
         const SegPlan& pl = *wplans[i];
         const bool tr = (i == 1 && share) || (i == 2 && dq_shares);
         void* ws = (i == 2 && dq_shares) ? const_cast<void*>(fwd_ws) : workspace;  // only read when tr
+        // the segment path runs only the forward-time dq walk here (bf16 dk and dv come
+        // from the fused walk); the reversed walks of fp32 take the value-slice path
+        if (pl.path == FwdPath::kSegment && w.rev)
+            return fail(RET_ERR_HIP, "%s: no time-reversed segment walk for this plan", fn);
         const hipError_t e =
             pl.path == FwdPath::kSegment
                 ? launch_segment_path(pl, w.a, w.b, w.c, w.o, none, ws, log2g, 0.f, B, H, T, chunk, w.wk,
-                                      w.wv, false, st, w.rev, tr)
+                                      w.wv, false, st, tr)
                 : launch_slice_path(pl, w.a, w.b, w.c, w.o, none, ws, log2g, 0.f, B, H, T, w.wk, w.wv,
                                     false, false, st, w.rev, tr);
         if (e != hipSuccess) return fail(RET_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

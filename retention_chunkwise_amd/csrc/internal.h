@@ -121,10 +121,6 @@ hipError_t launch_seg_lin_c128(const SegArgs& a, int dk, int dv, hipStream_t str
 hipError_t launch_seg_norm(const SegArgs& a, int chunk, int dk, int dv, bool group, hipStream_t stream);
 hipError_t launch_seg_norm_c64(const SegArgs& a, int dk, int dv, bool group, hipStream_t stream);
 hipError_t launch_seg_norm_c128(const SegArgs& a, int dk, int dv, bool group, hipStream_t stream);
-// Time-reversed retention walk (token t read from and written to row T - 1 - t).
-hipError_t launch_seg_rev(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream);
-hipError_t launch_seg_rev_c64(const SegArgs& a, int dk, int dv, hipStream_t stream);
-hipError_t launch_seg_rev_c128(const SegArgs& a, int dk, int dv, hipStream_t stream);
 // Fused reverse walk of the backward pass (64-token chunks): with a.q = k,
 // a.q2 = v, a.k = q, a.v = dout it writes dv to a.out and dk to a.out2.
 hipError_t launch_seg_bwd_kv(const SegArgs& a, int dk, int dv, hipStream_t stream);

@@ -401,7 +401,7 @@ __device__ __forceinline__ int perm_row(int dv) {
     return (dv & ~31) | (((dv >> 2) & 1) << 4) | (((dv >> 3) & 3) << 2) | (dv & 3);
 }
 
-template <int C, int DK, int DV, int MODE, int P, bool OW, bool REV>
+template <int C, int DK, int DV, int MODE, int P, bool OW>
 __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
     using Cf = SCfg<C, DK, DV, MODE>;
     constexpr bool LIN = MODE == kModeLin, NRM = MODE >= kModeNorm, GRP = MODE == kModeGroup;
@@ -569,12 +569,6 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
     };
 
     const unsigned koff = dma_offset<KRU>(w, l), voff = dma_offset<VRU>(w, l);
-    const int koffr = dma_offset_rev<KRU>(w, l), voffr = dma_offset_rev<VRU>(w, l);
-    // Time-reversed walks (REV) read and write chunk row r at memory row
-    // T - 1 - (t0 + r): the chunk's memory rows start at T - t0 - clen and run
-    // backwards.
-    auto mem_row0 = [&](long long t0, int cl) -> long long { return REV ? (cl ? T - t0 - cl : 0) : t0; };
-    auto row_in = [&](int r, int cl) -> int { return REV ? cl - 1 - r : r; };
 
     // Issue the loads of chunk c through range-checked resources (rows past
     // the end of the sequence read as zeros).
@@ -591,27 +585,24 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
         constexpr int buf = decltype(bufc)::value;
         const long long t0 = static_cast<long long>(c) * C;
         const int cl = (c < c_end) ? chunk_len(c) : 0;
-        const long long mrow = mem_row0(t0, cl);
-        const u32x4 wk = rsrc_words(kh + mrow * DK, cl * DK * 2);
-        const u32x4 wv = rsrc_words(vh + mrow * DV, cl * DV * 2);
+        const u32x4 wk = rsrc_words(kh + t0 * DK, cl * DK * 2);
+        const u32x4 wv = rsrc_words(vh + t0 * DV, cl * DV * 2);
         const unsigned kbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.k[buf]));
         const unsigned vbase = __builtin_amdgcn_readfirstlane(lds_addr_of(tl.v[buf]));
 #pragma unroll
         for (int m = 0; m < KIW; ++m)
-            dma16(wk, kbase + (w + 8 * m) * 1024,
-                  REV ? static_cast<unsigned>((cl - 1) * DK * 2 + koffr - 8192 * m) : koff + 8192u * m);
+            dma16(wk, kbase + (w + 8 * m) * 1024, koff + 8192u * m);
 #pragma unroll
         for (int m = 0; m < VIW; ++m)
-            dma16(wv, vbase + (w + 8 * m) * 1024,
-                  REV ? static_cast<unsigned>((cl - 1) * DV * 2 + voffr - 8192 * m) : voff + 8192u * m);
+            dma16(wv, vbase + (w + 8 * m) * 1024, voff + 8192u * m);
         if constexpr (OW) {
-            const auto rq = make_rsrc(qh + mrow * DK, cl * DK * 2);
+            const auto rq = make_rsrc(qh + t0 * DK, cl * DK * 2);
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int ks = 0; ks < QF; ++ks)
                     qf[buf][s][ks] = __builtin_bit_cast(
-                        bf16x8, bload16(rq, static_cast<unsigned>(((row_in(16 * its(s) + l16, cl)) * DK + 32 * ks + 8 * g) * 2)));
+                        bf16x8, bload16(rq, static_cast<unsigned>(((16 * its(s) + l16) * DK + 32 * ks + 8 * g) * 2)));
         }
     };
 
@@ -772,7 +763,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             int rowo = rowo0, uo = uo0;
             opaque(rowo);
             opaque(uo);
-            const auto ro = make_rsrc(oh + mem_row0(t0, clen) * DV, clen * DV * 2);
+            const auto ro = make_rsrc(oh + t0 * DV, clen * DV * 2);
             // outputs of value-tile pair pa (columns 32 pa .. +31 in the permuted
             // order) for this wave's query tiles, scaled by their divisors
             auto pair_out = [&](int pa, f32x4 (&oacc)[NS][2]) {
@@ -812,7 +803,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             auto store_pair = [&](int pa, const f32x4 (&oacc)[NS][2]) {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) {
-                    const int row = row_in(16 * its(s) + l16, clen);  // rows past the end are dropped by the resource
+                    const int row = 16 * its(s) + l16;  // rows past the end are dropped by the resource
                     bstore16_bf(ro, static_cast<unsigned>((row * DV + 32 * pa + 8 * g) * 2),
                                 cat_bf16(cvt4_bf16(oacc[s][0]), cvt4_bf16(oacc[s][1])));
                 }
@@ -1003,7 +994,7 @@ __global__ void __launch_bounds__(kThreads, 1) seg_state_kernel(const SegArgs a)
                                                           wave);
 }
 
-template <int C, int DK, int DV, int MODE, bool REV>
+template <int C, int DK, int DV, int MODE>
 __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) {
     constexpr bool LIN = MODE == kModeLin;
     __shared__ __attribute__((aligned(16))) unsigned short k0[C * DK];
@@ -1021,14 +1012,14 @@ __global__ void __launch_bounds__(kThreads, 1) seg_walk_kernel(const SegArgs a) 
     const float lg = LIN ? 0.f : a.log2g[bh % a.H];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     switch (wave) {
-        case 0: walk_body<C, DK, DV, MODE, 0, true, REV>(a, tl, bh, seg, lg); break;
-        case 1: walk_body<C, DK, DV, MODE, 1, true, REV>(a, tl, bh, seg, lg); break;
-        case 2: walk_body<C, DK, DV, MODE, 2, true, REV>(a, tl, bh, seg, lg); break;
-        case 3: walk_body<C, DK, DV, MODE, 3, true, REV>(a, tl, bh, seg, lg); break;
-        case 4: walk_body<C, DK, DV, MODE, 0, false, REV>(a, tl, bh, seg, lg); break;
-        case 5: walk_body<C, DK, DV, MODE, 1, false, REV>(a, tl, bh, seg, lg); break;
-        case 6: walk_body<C, DK, DV, MODE, 2, false, REV>(a, tl, bh, seg, lg); break;
-        default: walk_body<C, DK, DV, MODE, 3, false, REV>(a, tl, bh, seg, lg); break;
+        case 0: walk_body<C, DK, DV, MODE, 0, true>(a, tl, bh, seg, lg); break;
+        case 1: walk_body<C, DK, DV, MODE, 1, true>(a, tl, bh, seg, lg); break;
+        case 2: walk_body<C, DK, DV, MODE, 2, true>(a, tl, bh, seg, lg); break;
+        case 3: walk_body<C, DK, DV, MODE, 3, true>(a, tl, bh, seg, lg); break;
+        case 4: walk_body<C, DK, DV, MODE, 0, false>(a, tl, bh, seg, lg); break;
+        case 5: walk_body<C, DK, DV, MODE, 1, false>(a, tl, bh, seg, lg); break;
+        case 6: walk_body<C, DK, DV, MODE, 2, false>(a, tl, bh, seg, lg); break;
+        default: walk_body<C, DK, DV, MODE, 3, false>(a, tl, bh, seg, lg); break;
     }
 }
 
@@ -1045,7 +1036,7 @@ constexpr bool walk_supported() {
     return walk_fits<C, DK, DV, MODE>() && !(MODE == kModeLin && C == 128 && DK == 128);
 }
 
-template <int C, int DK, int DV, int MODE, bool REV>
+template <int C, int DK, int DV, int MODE>
 hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
     if constexpr (!walk_supported<C, DK, DV, MODE>()) {
         return hipErrorInvalidConfiguration;
@@ -1058,26 +1049,23 @@ hipError_t launch_t(const SegArgs& a, hipStream_t stream) {
         sa.scps = a.cps * (C / kStateBlock);
         // the state kernel is the same for both normalised retention modes
         constexpr int SMODE = (MODE == kModeGroup) ? kModeNorm : MODE;
-        hipLaunchKernelGGL((seg_state_kernel<DK, DV, SMODE, REV>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
+        hipLaunchKernelGGL((seg_state_kernel<DK, DV, SMODE, false>), dim3(static_cast<unsigned>(bh * (a.G - 1) * a.pieces)),
                            dim3(kThreads), 0, stream, sa);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, MODE, REV>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((seg_walk_kernel<C, DK, DV, MODE>), dim3(static_cast<unsigned>(bh * a.G)), dim3(kThreads), 0,
                        stream, a);
     return hipGetLastError();
     }
 }
 
-// REV: the walk runs over the time-reversed sequence (token t read from and
-// written to row T - 1 - t); the gradients of keys and values are such walks.
-template <int C, int MODE, bool REV = false>
+template <int C, int MODE>
 hipError_t launch_chunk(const SegArgs& a, int dk, int dv, hipStream_t stream) {
-    static_assert(!(MODE != kModeRet && REV), "time-reversed walks are retention only");
-    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, MODE, REV>(a, stream);
-    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, MODE, REV>(a, stream);
-    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, MODE, REV>(a, stream);
-    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, MODE, REV>(a, stream);
+    if (dk == 64 && dv == 64) return launch_t<C, 64, 64, MODE>(a, stream);
+    if (dk == 64 && dv == 128) return launch_t<C, 64, 128, MODE>(a, stream);
+    if (dk == 128 && dv == 64) return launch_t<C, 128, 64, MODE>(a, stream);
+    if (dk == 128 && dv == 128) return launch_t<C, 128, 128, MODE>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -43,12 +43,6 @@ hipError_t launch_seg_norm(const SegArgs& a, int chunk, int dk, int dv, bool gro
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_seg_rev(const SegArgs& a, int chunk, int dk, int dv, hipStream_t stream) {
-    if (chunk == 64) return launch_seg_rev_c64(a, dk, dv, stream);
-    if (chunk == 128) return launch_seg_rev_c128(a, dk, dv, stream);
-    return hipErrorInvalidValue;
-}
-
 hipError_t launch_seg(const SegArgs& a, int chunk, int dk, int dv, bool linattn, hipStream_t stream) {
     if (linattn) {
         if (chunk == 64) return launch_seg_lin_c64(a, dk, dv, stream);

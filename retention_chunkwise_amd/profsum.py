@@ -50,7 +50,7 @@ WORKLOADS = {
     "fwd_ret_fwd_long_bf16": {
         "what": "retention_fwd, [1, 32, 65536, 128] bf16, chunk 128",
         "kernels": [(SEG + "state_kernel<128, 128, 0, false>", 1),
-                    (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
+                    (SEG + "walk_kernel<128, 128, 128, 0>", 1)],
         "algorithmic": 2149580800, "sources": "FWD_SOURCES"},
     "bwd_ret_fwd_long_bf16": {
         "what": "retention_bwd on the long workload: the fused reverse walk for dk and dv (with its state "
@@ -58,24 +58,24 @@ WORKLOADS = {
         "kernels": [(SEG + "state_kernel<128, 128, 0, true>", 1),
                     (SEG + "bwd_kv_kernel<128, 128>", 1),
                     (SEG + "state_kernel<128, 128, 0, false>", 1),
-                    (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
+                    (SEG + "walk_kernel<128, 128, 128, 0>", 1)],
         "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
     "bwd_from_fwd_ret_fwd_long_bf16": {
         "what": "retention_bwd_from_fwd on the long workload: as retention_bwd, but the dq walk reads the "
                 "forward's segment states and runs no state pass",
         "kernels": [(SEG + "state_kernel<128, 128, 0, true>", 1),
                     (SEG + "bwd_kv_kernel<128, 128>", 1),
-                    (SEG + "walk_kernel<128, 128, 128, 0, false>", 1)],
+                    (SEG + "walk_kernel<128, 128, 128, 0>", 1)],
         "algorithmic": 3758096384, "sources": "FWD_SOURCES"},
     "fwd_normalized_ret_fwd_long_bf16": {
         "what": "retention_fwd_normalized (row-sum floor + GroupNorm) on the long workload",
         "kernels": [(SEG + "state_kernel<128, 128, 2, false>", 1),
-                    (SEG + "walk_kernel<64, 128, 128, 3, false>", 1)],
+                    (SEG + "walk_kernel<64, 128, 128, 3>", 1)],
         "algorithmic": 2147483648, "sources": "FWD_SOURCES"},
     "linattn_linattn_elu1_bf16": {
         "what": "linear_attn_fwd, elu+1, [8, 16, 8192, 64] bf16",
         "kernels": [(SEG + "state_kernel<64, 64, 1, false>", 1),
-                    (SEG + "walk_kernel<128, 64, 64, 1, false>", 1)],
+                    (SEG + "walk_kernel<128, 64, 64, 1>", 1)],
         "algorithmic": 536870912, "sources": "FWD_SOURCES"},
     "decode_kernel_decode_bf16": {
         "what": "retention_decode_step, 256 x 32 heads, 128 x 128 fp32 state",
@@ -235,7 +235,7 @@ def mfma(mfma_csv: str, stats_csv: str, out_dir: str = PROFILES) -> None:
     b = _bench()
     f_dense = M.fwd_flops(1, 32, 65536, 128, 128, 128)
     f_causal = M.fwd_flops(1, 32, 65536, 128, 128, 128, causal=True)
-    walk = agg.get("void ret::seg::seg_walk_kernel<128, 128, 128, 0, false>")
+    walk = agg.get("void ret::seg::seg_walk_kernel<128, 128, 128, 0>")
     state = agg.get("void ret::seg::seg_state_kernel<128, 128, 0, false>")
     if walk and state:
         def one(a):

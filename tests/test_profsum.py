@@ -43,12 +43,12 @@ def test_traffic_scales_by_the_copy_and_sums_a_call(tmp_path):
     assert abs(d["bytes_per_launch"] - 2 * (500 * 1024 * 2 + 100 * 1024)) < 1e-6
     assert d["source_sha"] == bench.sources_sha(bench.FWD_SOURCES)
     b = json.load(open(tmp_path / "hbm_traffic_bwd_ret_fwd_long_bf16.json"))
-    # the backward runs the reversed walk twice: 5 dispatches per call
-    assert abs(b["bytes_per_launch"] - 5 * (500 * 1024 * 2 + 100 * 1024)) < 1e-6
+    # the backward: two state passes, the fused reverse walk and the dq walk, 4 dispatches per call
+    assert abs(b["bytes_per_launch"] - 4 * (500 * 1024 * 2 + 100 * 1024)) < 1e-6
 
 
 def test_mfma_busy_uses_one_xcd_of_active_cycles(tmp_path):
-    walk = "void ret::seg::seg_walk_kernel<128, 128, 128, 0, false>(ret::SegArgs)"
+    walk = "void ret::seg::seg_walk_kernel<128, 128, 128, 0>(ret::SegArgs)"
     state = "void ret::seg::seg_state_kernel<128, 128, 0, false>(ret::SegArgs)"
     act = 1000.0  # active cycles of one XCD
     rows = []
