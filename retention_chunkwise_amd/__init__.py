@@ -48,8 +48,10 @@ __all__ = ["retention_fwd", "retention_fwd_noalloc", "retention_bwd", "retention
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libretention.so")
+_DEBUG_LIB_PATH = os.path.join(_HERE, "libretention_debug.so")
 _lock = threading.Lock()
 _lib = None
+_dlib = None
 
 RET_F32 = 0
 RET_BF16 = 1
@@ -75,6 +77,68 @@ def library_path() -> str:
     return _LIB_PATH
 
 
+def _declare(lib):
+    """Argument and result types of the C ABI on a loaded library."""
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.c_size_t
+    lib.retention_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.retention_fwd.restype = i
+    lib.retention_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.retention_fwd_workspace_bytes.restype = sz
+    lib.linear_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.linear_attn_workspace_bytes.restype = sz
+    lib.retention_decode_step.argtypes = [vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp]
+    lib.retention_decode_step.restype = i
+    lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
+    lib.retention_fwd_noalloc.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp]
+    lib.retention_fwd_noalloc.restype = i
+    lib.retention_fwd_from_state.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.retention_fwd_from_state.restype = i
+    lib.linear_attn_fwd_from_state.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                               ctypes.c_float, vp, sz, vp]
+    lib.linear_attn_fwd_from_state.restype = i
+    lib.linear_attn_decode_step.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp]
+    lib.linear_attn_decode_step.restype = i
+    lib.retention_bwd.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.retention_bwd.restype = i
+    lib.retention_bwd_from_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, vp,
+                                           sz, vp]
+    lib.retention_bwd_from_fwd.restype = i
+    lib.retention_fwd_normalized.argtypes = [vp, vp, vp, fp, i, i, ctypes.c_float, vp, i, i, i, i, i, i, vp,
+                                             sz, vp]
+    lib.retention_fwd_normalized.restype = i
+    lib.retention_fwd_normalized_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.retention_fwd_normalized_workspace_bytes.restype = sz
+    lib.gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
+    lib.gla_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.gla_fwd_workspace_bytes.restype = sz
+    lib.gla_fwd.restype = i
+    lib.retention_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.retention_bwd_workspace_bytes.restype = sz
+    lib.linear_attn_fwd.restype = i
+    lib.retention_last_error.argtypes = []
+    lib.retention_last_error.restype = ctypes.c_char_p
+    lib.retention_abi_version.argtypes = []
+    lib.retention_abi_version.restype = i
+    lib.retention_set_plan_override.argtypes = [i, i, i, i]
+    lib.retention_set_plan_override.restype = i
+    return lib
+
+
+def load_debug_library():
+    """Load libretention_debug.so, the LDS hazard self-check build (-DRET_DEBUG:
+    every LDS buffer that has gone dead is overwritten with NaN words until it
+    is refilled).  A separate handle with the same C ABI; the functions of this
+    module keep using the normal build."""
+    global _dlib
+    with _lock:
+        if _dlib is None:
+            if not os.path.exists(_DEBUG_LIB_PATH):
+                raise RuntimeError(f"{_DEBUG_LIB_PATH} is missing: build it with "
+                                   "`python -m retention_chunkwise_amd._build --debug`")
+            _dlib = _declare(ctypes.CDLL(_DEBUG_LIB_PATH))
+        return _dlib
+
+
 def load_library():
     """Load libretention.so (raises if it has not been built)."""
     global _lib
@@ -84,50 +148,7 @@ def load_library():
                 raise RuntimeError(
                     f"{_LIB_PATH} is missing: build it with `python -m retention_chunkwise_amd._build` "
                     "(or __graft_entry__.build()); there is no non-HIP fallback")
-            lib = ctypes.CDLL(_LIB_PATH)
-            vp, fp, i, sz = ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int, ctypes.c_size_t
-            lib.retention_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp, sz, vp]
-            lib.retention_fwd.restype = i
-            lib.retention_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
-            lib.retention_fwd_workspace_bytes.restype = sz
-            lib.linear_attn_workspace_bytes.argtypes = [i, i, i, i, i, i]
-            lib.linear_attn_workspace_bytes.restype = sz
-            lib.retention_decode_step.argtypes = [vp, vp, vp, fp, vp, vp, i, i, i, i, i, vp]
-            lib.retention_decode_step.restype = i
-            lib.linear_attn_fwd.argtypes = [vp, vp, vp, i, vp, i, i, i, i, i, i, ctypes.c_float, vp, sz, vp]
-            lib.retention_fwd_noalloc.argtypes = [vp, vp, vp, fp, i, vp, vp, i, i, i, i, i, i, vp]
-            lib.retention_fwd_noalloc.restype = i
-            lib.retention_fwd_from_state.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
-            lib.retention_fwd_from_state.restype = i
-            lib.linear_attn_fwd_from_state.argtypes = [vp, vp, vp, i, vp, vp, vp, vp, vp, i, i, i, i, i, i,
-                                                       ctypes.c_float, vp, sz, vp]
-            lib.linear_attn_fwd_from_state.restype = i
-            lib.linear_attn_decode_step.argtypes = [vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, ctypes.c_float, vp]
-            lib.linear_attn_decode_step.restype = i
-            lib.retention_bwd.argtypes = [vp, vp, vp, fp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
-            lib.retention_bwd.restype = i
-            lib.retention_bwd_from_fwd.argtypes = [vp, vp, vp, fp, i, vp, vp, sz, vp, vp, vp, i, i, i, i, i, i, vp,
-                                                   sz, vp]
-            lib.retention_bwd_from_fwd.restype = i
-            lib.retention_fwd_normalized.argtypes = [vp, vp, vp, fp, i, i, ctypes.c_float, vp, i, i, i, i, i, i, vp,
-                                                     sz, vp]
-            lib.retention_fwd_normalized.restype = i
-            lib.retention_fwd_normalized_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
-            lib.retention_fwd_normalized_workspace_bytes.restype = sz
-            lib.gla_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
-            lib.gla_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
-            lib.gla_fwd_workspace_bytes.restype = sz
-            lib.gla_fwd.restype = i
-            lib.retention_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
-            lib.retention_bwd_workspace_bytes.restype = sz
-            lib.linear_attn_fwd.restype = i
-            lib.retention_last_error.argtypes = []
-            lib.retention_last_error.restype = ctypes.c_char_p
-            lib.retention_abi_version.argtypes = []
-            lib.retention_abi_version.restype = i
-            lib.retention_set_plan_override.argtypes = [i, i, i, i]
-            lib.retention_set_plan_override.restype = i
-            _lib = lib
+            _lib = _declare(ctypes.CDLL(_LIB_PATH))
         return _lib
 
 

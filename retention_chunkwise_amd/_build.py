@@ -12,6 +12,11 @@ _build/asan/libretention.so, whose host code (argument validation, planning,
 launch set-up) runs under AddressSanitizer and UndefinedBehaviorSanitizer; the
 device code is compiled exactly as in the normal build.  Loading it needs the
 clang ASan runtime preloaded (asan_runtime() names it); the CPU tests do that.
+--debug builds retention_chunkwise_amd/libretention_debug.so with -DRET_DEBUG:
+the LDS hazard self-check, where the segment walks, the state kernel, the fused
+backward walk and the gated walk overwrite every LDS buffer that has gone dead
+with NaN words until it is refilled.  Its outputs must equal the normal
+build's bit for bit; a GPU test compares them.
 """
 from __future__ import annotations
 
@@ -25,6 +30,7 @@ import tempfile
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libretention.so")
+DEBUG_LIB = os.path.join(HERE, "libretention_debug.so")
 SOURCES = ["capi.hip", "walk.hip", "walk_ret_bf16.hip", "walk_ret_f32.hip", "walk_lin_bf16.hip",
            "walk_lin_f32.hip", "walk_norm_f32.hip", "rownorm.hip", "decode.hip", "seg_ret_bf16_c64.hip", "seg_ret_bf16_c128.hip",
            "seg_lin_bf16_c64.hip", "seg_lin_bf16_c128.hip", "seg_norm_bf16_c64.hip", "seg_norm_bf16_c128.hip", "seg_bwd_bf16.hip", "gla.hip"]
@@ -73,14 +79,19 @@ def _stale(obj: str, src: str) -> bool:
     return any(not os.path.exists(f) or os.path.getmtime(f) > t for f in files + [src])
 
 
-def build(verbose: bool = False, incremental: bool = False, sanitize_host: bool = False) -> str:
+def build(verbose: bool = False, incremental: bool = False, sanitize_host: bool = False, debug: bool = False) -> str:
     cc = hipcc()
-    extra = SANITIZE_HOST if sanitize_host else []
-    lib = SANITIZED_LIB if sanitize_host else LIB
+    extra = SANITIZE_HOST if sanitize_host else (["-DRET_DEBUG"] if debug else [])
+    lib = SANITIZED_LIB if sanitize_host else (DEBUG_LIB if debug else LIB)
     if sanitize_host:
         incremental = True
     with tempfile.TemporaryDirectory(prefix="retbuild_") as tmp:
-        odir = (os.path.dirname(SANITIZED_LIB) if sanitize_host else OBJ_CACHE) if incremental else tmp
+        if sanitize_host:
+            odir = os.path.dirname(SANITIZED_LIB)
+        elif incremental:
+            odir = os.path.join(OBJ_CACHE, "debug") if debug else OBJ_CACHE
+        else:
+            odir = tmp
         os.makedirs(odir, exist_ok=True)
         objs = []
         cmds = []
@@ -119,4 +130,4 @@ def build(verbose: bool = False, incremental: bool = False, sanitize_host: bool 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv,
-                sanitize_host="--sanitize-host" in sys.argv))
+                sanitize_host="--sanitize-host" in sys.argv, debug="--debug" in sys.argv))

@@ -631,6 +631,9 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             products(sm.op[X], t0, clen, ex_cur);
             vote(c + 2);       // the gates of chunk c + 2 have arrived by now
             lds_barrier();     // operands of c + 1 written; every read of c's operands and of the state copy done
+#ifdef RET_DEBUG
+            lds_poison(&sm.op[X], sizeof(Buf));  // dead until chunk c + 2 is folded into it
+#endif
             write_state_copy();
             lds_barrier();
             ex_cur = ex_next;
@@ -638,6 +641,10 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             products(sm.op[0], t0, clen, ex_cur);
             vote(c + 1);       // the gates of chunk c + 1 have arrived by now
             lds_barrier();     // every read of c's operands and of the state copy done
+#ifdef RET_DEBUG
+            lds_poison(&sm.op[0], sizeof(Buf));  // dead until chunk c + 1 is folded into it
+            lds_barrier();
+#endif
             write_state_copy();
             const bool ex_next = (c + 1 < c_end) && exact_of(c + 1);
             if (c + 1 < c_end) fold(sm.op[0], ex_next);

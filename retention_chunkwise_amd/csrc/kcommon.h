@@ -105,6 +105,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // keeps the compiler from moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// LDS hazard self-check (builds with -DRET_DEBUG): a buffer that no wave may
+// read any more until it is refilled is overwritten with all-ones words, a NaN
+// in bf16 and in fp32, by every thread of the workgroup.  A read that a missing
+// or misplaced barrier lets through then turns outputs into NaN, where a
+// release build would read stale but plausible values.
+#ifdef RET_DEBUG
+__device__ __forceinline__ void lds_poison(void* p, int bytes) {
+    for (int i = static_cast<int>(threadIdx.x) * 16; i < bytes; i += static_cast<int>(blockDim.x) * 16)
+        *reinterpret_cast<uint4*>(static_cast<char*>(p) + i) = uint4{~0u, ~0u, ~0u, ~0u};
+}
+#endif
+
 // Buffer resource words for the LDS-DMA loads (same layout as make_rsrc).
 __device__ __forceinline__ u32x4 rsrc_words(const void* base, int bytes) {
     const unsigned long long p = reinterpret_cast<unsigned long long>(base);

@@ -382,6 +382,11 @@ __device__ __forceinline__ void bwd_kv_body(const SegArgs& a, const STiles& tl, 
             lds_barrier();  // every O-wave is done reading the old U^T copy
             write_state_copy();
         }
+#ifdef RET_DEBUG
+        // chunk c's q and dout are dead until chunk c + 2 is loaded into them
+        lds_poison(tl.k[B], C * DK * 2);
+        lds_poison(tl.v[B], C * DV * 2);
+#endif
     };
 
     load_chunk(c_begin, std::integral_constant<int, 0>{});

@@ -309,6 +309,14 @@ __device__ __forceinline__ void state_body(const SegArgs& a, unsigned short* kri
         // blocks i+1 .. i+NBUF-2 may still be in flight; block i has landed
         wait_vmcnt<(NBUF - 2) * OPS>();
         lds_barrier();  // block i in LDS everywhere; block i-1's buffer is free
+#ifdef RET_DEBUG
+        {
+            const int fb = (i + NBUF - 1) % NBUF;  // block i-1's buffer, refilled next
+            lds_poison(kring + fb * (C * DK), C * DK * 2);
+            lds_poison(vring + fb * (C * DV), C * DV * 2);
+            lds_barrier();
+        }
+#endif
         load_block(i + NBUF - 1);
         LaneOff lk = lk0, lv = lv0;
         opaque<0>(lk);
@@ -946,6 +954,11 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
             end_step();  // every O-wave is done reading the old state copy
             write_state_copy();
         }
+#ifdef RET_DEBUG
+        // chunk c's K and V are dead until chunk c + 2 is loaded into them
+        lds_poison(tl.k[B], C * DK * 2);
+        lds_poison(tl.v[B], C * DV * 2);
+#endif
     };
 
     load_chunk(c_begin, std::integral_constant<int, 0>{});

@@ -37,6 +37,17 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), f"libretention.so does not export {name}"
 
 
+def test_debug_build_exports_the_same_abi():
+    """The LDS hazard self-check build (-DRET_DEBUG) is the same C ABI."""
+    path = os.path.join(os.path.dirname(rc.library_path()), "libretention_debug.so")
+    if not os.path.exists(path):
+        pytest.skip("libretention_debug.so not built (run __graft_entry__.build())")
+    dbg = rc.load_debug_library()
+    for name in _declared_functions():
+        assert hasattr(dbg, name), f"libretention_debug.so does not export {name}"
+    assert dbg.retention_abi_version() == _lib().retention_abi_version()
+
+
 def test_abi_version_matches_header():
     text = open(HEADER).read()
     ver = int(re.search(r"#define RET_ABI_VERSION (\d+)", text).group(1))
