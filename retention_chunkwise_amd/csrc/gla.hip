@@ -258,61 +258,48 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             }
         }
     };
-    if constexpr (!SO && !OW) {
+    if constexpr (!SO) {
+        // ---- the state entering the segment, by every thread of the workgroup:
+        //   S_in = sum_{j<seg} diag(exp(L_{j+1} + ... + L_{seg-1})) dS_j
+        // (all exponents <= 0), newest segment first.  Thread t takes EPT
+        // consecutive columns of one row of the slice and keeps up to SB
+        // segments' values in flight; the sums go to the state copy, from
+        // which the key waves take their tiles after the first barrier.
+        constexpr int EPT = DK * Cf::DVS / kThreads;  // 8 (dk = 64) or 16 (dk = 128)
+        constexpr int V4 = EPT / 4;
+        constexpr int SB = (DK == 64) ? 8 : 4;       // segments' values in flight per thread
+        const int tid = threadIdx.x;
+        const int row = tid / (Cf::DVS / EPT), col0 = (tid % (Cf::DVS / EPT)) * EPT;
+        f32x4 acc[V4];
+#pragma unroll
+        for (int v4 = 0; v4 < V4; ++v4) acc[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (seg > 0) {
-            // S_in = sum_{j<seg} diag(exp(L_{j+1} + ... + L_{seg-1})) dS_j, newest segment first; the
-            // next slot's values are loaded while the current one is added
             const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot;
-            // tiles in groups of up to 4, so that two slots' values stay in registers
-            auto group = [&](auto t0c) {
-                constexpr int T0 = decltype(t0c)::value;
-                constexpr int NG = (TN - T0 < 4) ? TN - T0 : 4;
-                float cv[NG][4], cl[NG][4], dsum[NG][4];
-                auto ld = [&](int j, float (&v)[NG][4], float (&L)[NG][4]) {
-                    const float* sj = wsb + j * slot;
+            float esum = 0.f;  // log-gate total of the segments already added
+            for (int j0 = seg - 1; j0 >= 0; j0 -= SB) {
+                f32x4 x[SB][V4];
+                float L[SB];
 #pragma unroll
-                    for (int t = 0; t < NG; ++t) {
-                        const int m = (TF + T0 + t) % KT, n = (TF + T0 + t) / KT;
+                for (int b = 0; b < SB; ++b) {
+                    const int j = j0 - b;
+                    const float* sj = wsb + static_cast<long long>(j < 0 ? 0 : j) * slot;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            v[t][r] = sj[(16 * m + 4 * g + r) * DV + nbase + 16 * n + l16];
-                            L[t][r] = sj[DK * DV + 16 * m + 4 * g + r];
-                        }
-                    }
-                };
-#pragma unroll
-                for (int t = 0; t < NG; ++t)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dsum[t][r] = 0.f;
-                ld(seg - 1, cv, cl);
-                for (int j = seg - 1; j >= 0; --j) {
-                    float nv[NG][4], nl[NG][4];
-                    if (j > 0) ld(j - 1, nv, nl);
-#pragma unroll
-                    for (int t = 0; t < NG; ++t)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            sacc[T0 + t][r] += fexp(dsum[t][r]) * cv[t][r];
-                            dsum[t][r] += cl[t][r];
-                        }
-                    if (j > 0) {
-#pragma unroll
-                        for (int t = 0; t < NG; ++t)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                cv[t][r] = nv[t][r];
-                                cl[t][r] = nl[t][r];
-                            }
-                    }
+                    for (int v4 = 0; v4 < V4; ++v4)
+                        x[b][v4] = (j >= 0) ? *reinterpret_cast<const f32x4*>(sj + row * DV + nbase + col0 + 4 * v4)
+                                            : f32x4{0.f, 0.f, 0.f, 0.f};
+                    L[b] = (j >= 0) ? sj[DK * DV + row] : 0.f;
                 }
-            };
-            if constexpr (TN > 0) group(std::integral_constant<int, 0>{});
-            if constexpr (TN > 4) group(std::integral_constant<int, 4>{});
-            if constexpr (TN > 8) group(std::integral_constant<int, 8>{});
-            if constexpr (TN > 12) group(std::integral_constant<int, 12>{});
-            static_assert(TN <= 16, "prologue groups");
+#pragma unroll
+                for (int b = 0; b < SB; ++b) {
+                    const float wgt = fexp(esum);
+#pragma unroll
+                    for (int v4 = 0; v4 < V4; ++v4) acc[v4] += wgt * x[b][v4];
+                    esum += L[b];
+                }
+            }
         }
-        write_state_copy();  // for the first chunk (ordered by the barriers before the loop)
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) sm.sc[(col0 + i) * QS + row] = acc[i / 4][i % 4];
     }
 
     // ---- raw chunk registers.  Lane l of wave W covers token group tg = l % 16
@@ -611,6 +598,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         vote(c_begin);
     }
     lds_barrier();  // the first vote and the state copy
+    if constexpr (!SO && !OW) {
+        // this wave's state tiles, from the copy the whole workgroup wrote
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            const int m = (TF + t) % KT, n = (TF + t) / KT;
+            sacc[t] = lds4(&sm.sc[(16 * n + l16) * QS + 16 * m + 4 * g]);
+        }
+    }
     bool ex_cur = (c_begin < c_end) && exact_of(c_begin);
     if (c_begin < c_end) {
         fold(sm.op[0], ex_cur);
