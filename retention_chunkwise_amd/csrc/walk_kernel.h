@@ -205,55 +205,126 @@ __device__ __forceinline__ void walk_body(const WalkArgs& a, Smem<BF16, C, DK, N
 #pragma unroll
     for (int m = 0; m < SPW; ++m) sacc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     const float lseg = static_cast<float>(a.seg_len) * lg;  // log2 of gamma^L
-    if (seg > 0) {
-        constexpr int ZW = ZN ? DK : 0;  // normaliser floats after each state slot
-        const long long slot = static_cast<long long>(DK) * DV + ZW;
-        const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + nbase;
-        for (int j = 0; j < seg; ++j) {
-            const float wj = exp2f(lseg * static_cast<float>(seg - 1 - j));
-            if (!ZN && a.ws_tr) {
-                // S[i][nbase + c] is element (nbase + c) * DK + i of the transposed (DV x DK) state
-                const float* sj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + j) * slot;
+    if constexpr (!BF16) {
+        // fp32: every thread of the workgroup forms EPT consecutive columns of one
+        // row of S_in = sum_{j<seg} gamma^(L (seg-1-j)) dS_j (+ the decayed initial
+        // state), up to SB segments' values in flight, straight into the first
+        // chunk's operand copy Sts[0][j][i] = S[i][nbase + j]; each wave then takes
+        // its tiles from there
+        constexpr int DVS = Cf::DVS;
+        constexpr int TPR = kThreads / DK;          // threads per state row
+        constexpr int EPT = DVS / TPR;              // columns per thread (>= 4)
+        constexpr int V4 = EPT / 4;
+        constexpr int SB = (32 / EPT) > 0 ? 32 / EPT : 1;  // segments' values in flight
+        static_assert(EPT % 4 == 0, "16-byte column groups");
+        const int row = tid / TPR, col0 = (tid % TPR) * EPT;
+        f32x4 acc[V4];
+#pragma unroll
+        for (int v4 = 0; v4 < V4; ++v4) acc[v4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (seg > 0) {
+            constexpr int ZW = ZN ? DK : 0;  // normaliser floats after each state slot
+            const long long slot = static_cast<long long>(DK) * DV + ZW;
+            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot;
+            const bool tr = !ZN && a.ws_tr;
+            for (int j0 = 0; j0 < seg; j0 += SB) {
+                f32x4 x[SB][V4];
+#pragma unroll
+                for (int b = 0; b < SB; ++b) {
+                    const int j = j0 + b;
+                    const float* sj = wsb + static_cast<long long>(j < seg ? j : 0) * slot;
+#pragma unroll
+                    for (int v4 = 0; v4 < V4; ++v4) {
+                        if (j >= seg) {
+                            x[b][v4] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        } else if (tr) {
+                            // S[i][nbase + c] is element (nbase + c) * DK + i of the transposed (DV x DK) state
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                x[b][v4][e] = sj[static_cast<long long>(nbase + col0 + 4 * v4 + e) * DK + row];
+                        } else {
+                            x[b][v4] = *reinterpret_cast<const f32x4*>(sj + static_cast<long long>(row) * DV + nbase +
+                                                                        col0 + 4 * v4);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int b = 0; b < SB; ++b) {
+                    const int j = j0 + b;
+                    const float wj = (j < seg) ? exp2f(lseg * static_cast<float>(seg - 1 - j)) : 0.f;
+#pragma unroll
+                    for (int v4 = 0; v4 < V4; ++v4) acc[v4] += wj * x[b][v4];
+                }
+            }
+        }
+        if (a.init_state) {
+            const float w0 = exp2f(lseg * static_cast<float>(seg));
+            const float* si = a.init_state + static_cast<long long>(bh) * DK * DV + static_cast<long long>(row) * DV +
+                              nbase + col0;
+#pragma unroll
+            for (int v4 = 0; v4 < V4; ++v4) acc[v4] += w0 * *reinterpret_cast<const f32x4*>(si + 4 * v4);
+        }
+        E* st0 = sm.Sts[0];
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) st0[(col0 + e) * KSTR + row] = acc[e / 4][e % 4];
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int qt = TS + m;
+            const int nt = qt / KT, kt = qt % KT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[m][r] = st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16];
+        }
+    } else {
+        if (seg > 0) {
+            constexpr int ZW = ZN ? DK : 0;  // normaliser floats after each state slot
+            const long long slot = static_cast<long long>(DK) * DV + ZW;
+            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * slot + nbase;
+            for (int j = 0; j < seg; ++j) {
+                const float wj = exp2f(lseg * static_cast<float>(seg - 1 - j));
+                if (!ZN && a.ws_tr) {
+                    // S[i][nbase + c] is element (nbase + c) * DK + i of the transposed (DV x DK) state
+                    const float* sj = a.ws + (static_cast<long long>(bh) * (a.G - 1) + j) * slot;
+#pragma unroll
+                    for (int m = 0; m < SPW; ++m) {
+                        const int qt = TS + m;
+                        const int nt = qt / KT, kt = qt % KT;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            sacc[m][r] += wj * sj[static_cast<long long>(nbase + nt * 16 + 4 * g + r) * DK + kt * 16 + l16];
+                    }
+                    continue;
+                }
 #pragma unroll
                 for (int m = 0; m < SPW; ++m) {
                     const int qt = TS + m;
                     const int nt = qt / KT, kt = qt % KT;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sacc[m][r] += wj * sj[static_cast<long long>(nbase + nt * 16 + 4 * g + r) * DK + kt * 16 + l16];
+                    sacc[m] += wj * *reinterpret_cast<const f32x4*>(wsb + j * slot + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
                 }
-                continue;
             }
+        }
+        if (a.init_state) {
+            const float w0 = exp2f(lseg * static_cast<float>(seg));
+            const float* si = a.init_state + static_cast<long long>(bh) * DK * DV + nbase;
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
                 const int qt = TS + m;
                 const int nt = qt / KT, kt = qt % KT;
-                sacc[m] += wj * *reinterpret_cast<const f32x4*>(wsb + j * slot + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
+                sacc[m] += w0 * *reinterpret_cast<const f32x4*>(si + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
             }
         }
-    }
-    if (a.init_state) {
-        const float w0 = exp2f(lseg * static_cast<float>(seg));
-        const float* si = a.init_state + static_cast<long long>(bh) * DK * DV + nbase;
+        {
+            // operand copy for the first chunk: Sts[0][j][i] = S[i][nbase + j] (the
+            // first barrier of the first step orders these writes before any read)
+            E* st0 = sm.Sts[0];
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = TS + m;
-            const int nt = qt / KT, kt = qt % KT;
-            sacc[m] += w0 * *reinterpret_cast<const f32x4*>(si + (kt * 16 + l16) * DV + nt * 16 + 4 * g);
-        }
-    }
-    {
-        // operand copy for the first chunk: Sts[0][j][i] = S[i][nbase + j] (the
-        // first barrier of the first step orders these writes before any read)
-        E* st0 = sm.Sts[0];
+            for (int m = 0; m < SPW; ++m) {
+                const int qt = TS + m;
+                const int nt = qt / KT, kt = qt % KT;
 #pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int qt = TS + m;
-            const int nt = qt / KT, kt = qt % KT;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if constexpr (BF16) st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16] = f2bf(sacc[m][r]);
-                else st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16] = sacc[m][r];
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (BF16) st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16] = f2bf(sacc[m][r]);
+                    else st0[(nt * 16 + 4 * g + r) * KSTR + kt * 16 + l16] = sacc[m][r];
+                }
             }
         }
     }
