@@ -88,7 +88,7 @@ WORKLOADS = {
     "fwd_f32_ret_fwd_mh_f32": {
         "what": "retention_fwd fp32 [4, 8, 2048, 64], chunk 64, final state",
         "kernels": [("::slice_state_kernel<false, 64, 64, 0>", 1),
-                    ("walk::walk_kernel<false, 64, 64, 4, 0>", 1)],
+                    ("walk::walk_kernel<false, 64, 64, 2, 0>", 1)],
         "algorithmic": 4 * 8 * 2048 * 64 * 4 * 4 + 4 * 8 * 64 * 64 * 4, "sources": "F32_SOURCES"},
     "gla_gla_mh_f32": {
         "what": "gla_fwd fp32 [4, 8, 2048, 64], final state (state-only pass + walk)",
