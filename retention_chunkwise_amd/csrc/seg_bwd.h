@@ -108,45 +108,8 @@ __device__ __forceinline__ void bwd_kv_body(const SegArgs& a, const STiles& tl, 
 #pragma unroll
             for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (seg > 0) {
-            // piece p of segment j is decayed by gamma^(L (seg-1-j) + Lp (pieces-1-p)); the next
-            // slot's values are loaded while the current one is added
-            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * a.pieces * Cf::WS;
-            const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
-            const float lpiece = lseg / static_cast<float>(a.pieces);
-            const int nslot = seg * a.pieces;
-            constexpr int NG = NVT < 4 ? NVT : 4;
-            auto group = [&](auto n0c) {
-                constexpr int N0 = decltype(n0c)::value;
-                f32x4 cur[SKT][NG], nxt[SKT][NG];
-                auto ld = [&](int jp, f32x4 (&x)[SKT][NG]) {
-                    const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
-#pragma unroll
-                    for (int mi = 0; mi < SKT; ++mi)
-#pragma unroll
-                        for (int nn = 0; nn < NG; ++nn)
-                            x[mi][nn] = *reinterpret_cast<const f32x4*>(sj + ws_tile_off(SKT * P + mi, N0 + nn, NVT, l));
-                };
-                ld(0, cur);
-                for (int jp = 0; jp < nslot; ++jp) {
-                    if (jp + 1 < nslot) ld(jp + 1, nxt);
-                    const int j = jp / a.pieces, pc = jp % a.pieces;
-                    const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
-                                             lpiece * static_cast<float>(a.pieces - 1 - pc)));
-#pragma unroll
-                    for (int mi = 0; mi < SKT; ++mi)
-#pragma unroll
-                        for (int nn = 0; nn < NG; ++nn) sacc[mi][N0 + nn] += wj * cur[mi][nn];
-                    if (jp + 1 < nslot) {
-#pragma unroll
-                        for (int mi = 0; mi < SKT; ++mi)
-#pragma unroll
-                            for (int nn = 0; nn < NG; ++nn) cur[mi][nn] = nxt[mi][nn];
-                    }
-                }
-            };
-            group(std::integral_constant<int, 0>{});
-            if constexpr (NVT > 4) group(std::integral_constant<int, 4>{});
-            static_assert(NVT <= 8, "prologue groups");
+            float zacc[SKT];  // unused: no normaliser travels with U
+            sum_segment_states<C, DK, DV, kModeRet, P>(a, bh, seg, lg, false, sacc, zacc);
         }
     }
 

@@ -409,6 +409,75 @@ __device__ __forceinline__ int perm_row(int dv) {
     return (dv & ~31) | (((dv >> 2) & 1) << 4) | (((dv >> 3) & 3) << 2) | (dv & 3);
 }
 
+// The state entering segment seg, summed into an S-wave's tiles (wave P + 4:
+// dk tiles SKT P .. + SKT - 1 by every value tile) from the state kernel's
+// workspace:
+//   S_in = sum_{j<seg, pieces p} gamma^(L (seg-1-j) + Lp (pieces-1-p)) dS_{j,p}
+// and for the normalised modes the normaliser beside it.  Value tiles go in
+// groups of NG and SB workspace states of a group are loaded at once, so the
+// loads of a batch are in flight together.  tr: the workspace holds the
+// states of a walk with key and value roles swapped (read transposed).
+template <int C, int DK, int DV, int MODE, int P>
+__device__ __forceinline__ void sum_segment_states(const SegArgs& a, int bh, int seg, float lg, bool tr,
+                                                   f32x4 (&sacc)[SCfg<C, DK, DV, MODE>::SKT][SCfg<C, DK, DV, MODE>::NVT],
+                                                   float (&zacc)[SCfg<C, DK, DV, MODE>::SKT]) {
+    using Cf = SCfg<C, DK, DV, MODE>;
+    constexpr bool ZN = MODE != kModeRet;
+    constexpr int SKT = Cf::SKT, NVT = Cf::NVT, NKT = Cf::NKT;
+    constexpr int NG = NVT < 2 ? NVT : 2;  // value tiles per group
+    constexpr int SB = 8 / SKT;            // workspace states in flight
+    const int l = threadIdx.x & 63, l16 = l & 15, g = l >> 4;
+    const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * a.pieces * Cf::WS;
+    const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
+    const float lpiece = lseg / static_cast<float>(a.pieces);
+    const int nslot = seg * a.pieces;
+#pragma unroll
+    for (int n0 = 0; n0 < NVT; n0 += NG) {
+        const bool zg = ZN && n0 == 0;  // the normaliser travels with the first group
+        for (int j0 = 0; j0 < nslot; j0 += SB) {
+            f32x4 x[SB][SKT][NG];
+            float zx[SB][SKT];
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int jp = (j0 + b < nslot) ? j0 + b : nslot - 1;  // past the end: reloaded, weight 0
+                const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi) {
+                    const int m = SKT * P + mi;
+#pragma unroll
+                    for (int nn = 0; nn < NG; ++nn) {
+                        const int n = n0 + nn;
+                        if (tr) {
+                            // S[16m + 4g + r][16n + l16] is element l16 % 4 of lane 16 (l16 / 4) + 4g + r
+                            // in tile (n, m) of the transposed state
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                x[b][mi][nn][r] = sj[((n * NKT + m) << 8) + ((16 * (l16 >> 2) + 4 * g + r) << 2) + (l16 & 3)];
+                        } else {
+                            x[b][mi][nn] = *reinterpret_cast<const f32x4*>(sj + ws_tile_off(m, n, NVT, l));
+                        }
+                    }
+                    zx[b][mi] = zg ? sj[Cf::STATE + 16 * m + l16] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int jp = j0 + b;
+                const int j = jp / a.pieces, pc = jp % a.pieces;
+                const float wj = (jp < nslot) ? uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
+                                                         lpiece * static_cast<float>(a.pieces - 1 - pc)))
+                                              : 0.f;
+#pragma unroll
+                for (int mi = 0; mi < SKT; ++mi) {
+#pragma unroll
+                    for (int nn = 0; nn < NG; ++nn) sacc[mi][n0 + nn] += wj * x[b][mi][nn];
+                    if (zg) zacc[mi] += wj * zx[b][mi];
+                }
+            }
+        }
+    }
+}
+
 template <int C, int DK, int DV, int MODE, int P, bool OW>
 __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, int bh, int seg, float lg) {
     using Cf = SCfg<C, DK, DV, MODE>;
@@ -478,65 +547,7 @@ __device__ __forceinline__ void walk_body(const SegArgs& a, const STiles& tl, in
 #pragma unroll
             for (int n = 0; n < NVT; ++n) sacc[mi][n] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (seg > 0) {
-            // piece p of segment j is decayed by gamma^(L (seg-1-j) + Lp (pieces-1-p)); the next
-            // slot's values are loaded while the current one is added
-            const float* wsb = a.ws + static_cast<long long>(bh) * (a.G - 1) * a.pieces * Cf::WS;
-            const float lseg = static_cast<float>(a.cps) * static_cast<float>(C) * lg;
-            const float lpiece = lseg / static_cast<float>(a.pieces);
-            const bool tr = !ZN && a.ws_tr;
-            const int nslot = seg * a.pieces;
-            // value tiles in groups of NG, so that two slots' values of a group stay in registers
-            constexpr int NG = NVT < 4 ? NVT : 4;
-            auto group = [&](auto n0c) {
-                constexpr int N0 = decltype(n0c)::value;
-                constexpr bool ZG = ZN && N0 == 0;  // the normaliser travels with the first group
-                struct Slot {
-                    f32x4 s[SKT][NG];
-                    float z[SKT];
-                };
-                auto ld = [&](int jp, Slot& x) {
-                    const float* sj = wsb + static_cast<long long>(jp) * Cf::WS;
-#pragma unroll
-                    for (int mi = 0; mi < SKT; ++mi) {
-                        const int m = SKT * P + mi;
-#pragma unroll
-                        for (int nn = 0; nn < NG; ++nn) {
-                            const int n = N0 + nn;
-                            if (tr) {
-                                // S[16m + 4g + r][16n + l16] is element l16 % 4 of lane 16 (l16 / 4) + 4g + r
-                                // in tile (n, m) of the transposed state
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    x.s[mi][nn][r] = sj[((n * Cf::NKT + m) << 8) +
-                                                        ((16 * (l16 >> 2) + 4 * g + r) << 2) + (l16 & 3)];
-                            } else {
-                                x.s[mi][nn] = *reinterpret_cast<const f32x4*>(sj + ws_tile_off(m, n, NVT, l));
-                            }
-                        }
-                        x.z[mi] = ZG ? sj[Cf::STATE + 16 * m + l16] : 0.f;
-                    }
-                };
-                Slot cur, nxt;
-                ld(0, cur);
-                for (int jp = 0; jp < nslot; ++jp) {
-                    if (jp + 1 < nslot) ld(jp + 1, nxt);
-                    const int j = jp / a.pieces, pc = jp % a.pieces;
-                    const float wj = uni(ex2(lseg * static_cast<float>(seg - 1 - j) +
-                                             lpiece * static_cast<float>(a.pieces - 1 - pc)));
-#pragma unroll
-                    for (int mi = 0; mi < SKT; ++mi) {
-#pragma unroll
-                        for (int nn = 0; nn < NG; ++nn) sacc[mi][N0 + nn] += wj * cur.s[mi][nn];
-                        if constexpr (ZG) zacc[mi] += wj * cur.z[mi];
-                    }
-                    if (jp + 1 < nslot) cur = nxt;
-                }
-            };
-            group(std::integral_constant<int, 0>{});
-            if constexpr (NVT > 4) group(std::integral_constant<int, 4>{});
-            static_assert(NVT <= 8, "prologue groups");
-        }
+        if (seg > 0) sum_segment_states<C, DK, DV, MODE, P>(a, bh, seg, lg, !ZN && a.ws_tr, sacc, zacc);
         if (a.init_state) {
             // the state before token 0, decayed over the seg * L tokens before this segment
             const float w0 = uni(ex2(static_cast<float>(a.cps) * static_cast<float>(C) * lg * static_cast<float>(seg)));
