@@ -98,6 +98,11 @@ def time_launches(fn, steps: int, warmup: int):
     return ev0.elapsed_time(ev1) / steps, wall / steps
 
 
+def progress(msg: str) -> None:
+    """One line per finished leg on stderr (the JSON result stays alone on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -248,6 +253,8 @@ def main():
         },
     }
 
+    progress("headline forward done")
+
     # ---------------- backward (dq, dk, dv) on the same workload
     if not args.no_components:
         g = torch.Generator().manual_seed(1)
@@ -291,6 +298,8 @@ def main():
         }
         del dout, gq, gk, gv, bws
 
+    progress("backward done")
+
     # ---------------- the same forward with the row-sum floor and GroupNorm fused
     if not args.no_components:
         nout = torch.empty_like(v)
@@ -313,6 +322,8 @@ def main():
                          "traffic": (n_tr["bytes_per_launch"] if n_tr else None)},
         }
         del nout, nws
+
+    progress("normalised forward done")
 
     # ---------------- decode step and linear attention
     if not args.no_components:
@@ -391,6 +402,8 @@ def main():
         }
         del lq, lk, lv, lout, lws
 
+    progress("decode and linear attention done")
+
     # ---------------- fp32 forward with final state, [4, 8, 2048, 64], chunk 64
     if not args.no_components:
         wf = wl.WORKLOADS["ret_fwd_mh_f32"]
@@ -418,6 +431,8 @@ def main():
                          "algorithmic_bytes_per_launch": f_by},
         }
         del fq, fk, fv, fout, ffs
+
+    progress("fp32 forward done")
 
     # ---------------- gated linear attention (per-token, per-key-channel gates), [4, 8, 2048, 64],
     # q, k, v and out in fp32 and in bf16 (log-gates and arithmetic fp32)
@@ -454,6 +469,8 @@ def main():
             del gq, gk, gv, gout, gfs
         del glg
 
+    progress("gated linear attention done")
+
     # ---------------- context: a plain device copy of 1 GiB (read + write), the
     # ceiling a kernel that streams each byte once in and once out can expect
     if not args.no_components:
@@ -474,6 +491,8 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = n * 4
         del src, dst
+
+    progress("copy done")
 
     # ---------------- CPU baseline (the oracle on the host cores)
     if not args.no_cpu_baseline:
