@@ -77,15 +77,25 @@ def measured_mfma(name: str, paths) -> dict | None:
     return d if d.get("source_sha") == sources_sha(paths) else None
 
 
-def time_launches(fn, steps: int, warmup: int):
+def time_launches(fn, steps: int, warmup: int, min_warm_ms: float = 0.0):
     """Run fn warmup + steps times; return (avg ms per launch from HIP events,
     wall ms per step).  Events are recorded on torch's current stream, which
-    is the stream the library launches on."""
+    is the stream the library launches on.  min_warm_ms > 0 (the component
+    legs) keeps warming up until that much wall time has passed, so that the
+    GPU's clocks have settled on this leg's load before the timed steps (the
+    long forward's first 55 calls after a cold start ran 3 % slower than the
+    next ones)."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    if min_warm_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < min_warm_ms:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -159,7 +169,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true",
@@ -266,7 +276,7 @@ def main():
         def bstep():
             rc.retention_bwd(q, k, v, gamma, dout, chunk=w.chunk, dq=gq, dk=gk, dv=gv, workspace=bws)
 
-        b_kern, b_wall = time_launches(bstep, max(args.steps // 2, 5), args.warmup)
+        b_kern, b_wall = time_launches(bstep, max(args.steps // 2, 5), args.warmup, min_warm_ms=50.0)
         b_by = M.bwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2)
         b_gbs = b_by / (b_kern * 1e-3) / 1e9
         b_tr = measured_traffic("bwd_ret_fwd_long_bf16", FWD_SOURCES)
@@ -285,7 +295,7 @@ def main():
             rc.retention_bwd(q, k, v, gamma, dout, chunk=w.chunk, dq=gq, dk=gk, dv=gv, workspace=bws,
                              fwd_workspace=ws)
 
-        f_kern, f_wall = time_launches(bstep_ff, max(args.steps // 2, 5), args.warmup)
+        f_kern, f_wall = time_launches(bstep_ff, max(args.steps // 2, 5), args.warmup, min_warm_ms=50.0)
         f_gbs = b_by / (f_kern * 1e-3) / 1e9
         f_tr = measured_traffic("bwd_from_fwd_ret_fwd_long_bf16", FWD_SOURCES)
         res["backward_from_fwd"] = {
@@ -309,7 +319,7 @@ def main():
         def nstep():
             rc.retention_fwd_normalized(q, k, v, gamma, norm="group", chunk=w.chunk, out=nout, workspace=nws)
 
-        n_kern, n_wall = time_launches(nstep, max(args.steps // 2, 5), args.warmup)
+        n_kern, n_wall = time_launches(nstep, max(args.steps // 2, 5), args.warmup, min_warm_ms=50.0)
         n_by = M.fwd_bytes(w.B, w.H, w.T, w.dk, w.dv, 2, final_state=False)
         n_gbs = n_by / (n_kern * 1e-3) / 1e9
         n_tr = measured_traffic("fwd_normalized_ret_fwd_long_bf16", FWD_SOURCES)
@@ -336,7 +346,7 @@ def main():
         def dstep():
             rc.retention_decode_step(dq, dk_, dv_, di["gamma"], state, out=dout)
 
-        d_kern, d_wall = time_launches(dstep, args.decode_steps, 10)
+        d_kern, d_wall = time_launches(dstep, args.decode_steps, 10, min_warm_ms=50.0)
         d_bytes = M.decode_bytes(wd.B, wd.H, wd.dk, wd.dv, 2)
         d_gbs = d_bytes / (d_kern * 1e-3) / 1e9
         d_tr = measured_traffic("decode_kernel_decode_bf16", DECODE_SOURCES)
@@ -359,7 +369,7 @@ def main():
         def lstep_dec():
             rc.linear_attn_decode_step(dq, dk_, dv_, lS, lz, out=dout)
 
-        ld_kern, ld_wall = time_launches(lstep_dec, args.decode_steps, 10)
+        ld_kern, ld_wall = time_launches(lstep_dec, args.decode_steps, 10, min_warm_ms=50.0)
         ld_bytes = M.linattn_decode_bytes(wd.B, wd.H, wd.dk, wd.dv, 2)
         ld_gbs = ld_bytes / (ld_kern * 1e-3) / 1e9
         ld_tr = measured_traffic("linattn_decode_kernel_decode_bf16", DECODE_SOURCES)
@@ -385,7 +395,7 @@ def main():
         def lstep():
             rc.linear_attn_fwd(lq, lk, lv, out=lout, workspace=lws)
 
-        l_kern, l_wall = time_launches(lstep, args.steps, args.warmup)
+        l_kern, l_wall = time_launches(lstep, args.steps, args.warmup, min_warm_ms=50.0)
         l_fl = M.fwd_flops(wa.B, wa.H, wa.T, wa.dk, wa.dv, wa.chunk)
         l_by = M.fwd_bytes(wa.B, wa.H, wa.T, wa.dk, wa.dv, 2, final_state=False)
         l_gbs = l_by / (l_kern * 1e-3) / 1e9
@@ -415,7 +425,7 @@ def main():
         def f32step():
             rc.retention_fwd(fq, fk, fv, fi["gamma"], chunk=wf.chunk, out=fout, final_state=ffs)
 
-        f_kern, f_wall = time_launches(f32step, max(args.steps, 200), args.warmup)
+        f_kern, f_wall = time_launches(f32step, max(args.steps, 200), args.warmup, min_warm_ms=50.0)
         f_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, wf.chunk)
         f_by = M.fwd_bytes(wf.B, wf.H, wf.T, wf.dk, wf.dv, 4, final_state=True)
         f_tf = f_fl / (f_kern * 1e-3) / 1e12
@@ -449,7 +459,7 @@ def main():
             def glastep():
                 rc.gla_fwd(gq, gk, gv, glg, out=gout, final_state=gfs)
 
-            g_kern, g_wall = time_launches(glastep, max(args.steps, 100), args.warmup)
+            g_kern, g_wall = time_launches(glastep, max(args.steps, 100), args.warmup, min_warm_ms=50.0)
             g_fl = M.fwd_flops(wf.B, wf.H, wf.T, wf.dk, wf.dv, 64)
             g_tf = g_fl / (g_kern * 1e-3) / 1e12
             g_tr = measured_traffic(f"gla_gla_mh_{tag}", GLA_SOURCES)
