@@ -41,10 +41,12 @@
 // chunk for the whole slice (the only slice when dv = 64).
 //  - Folding: lane l of wave w covers tokens 4 (l % 16) .. + 3 (in tile
 //    (l % 16) / 4) of the 4 channels 16 (w % 4) + 4 (l / 16) .. + 3 (+ 64 for
-//    dk = 128), loaded as 16-byte (bf16: 8-byte) runs.  Waves 0-3 fold the
-//    queries (and stage the same 4 value columns of the slice over the same
-//    tokens), waves 4-7 the keys; both read the gates of their channels (the
-//    second read hits the cache).  Running sums: a sum over the lane's 4
+//    dk = 128), loaded as 16-byte (bf16: 8-byte) runs.  Waves 4-7 fold the
+//    keys.  The queries (and the same 4 value columns of the slice over the
+//    same tokens) of channel slice w are folded by wave w, except at dk = 64
+//    where slices 2 and 3 go to waves 6 and 7, which share the gate sums with
+//    their own key fold: O-waves 2 and 3, which issue the most MFMAs, then
+//    carry no fold on their serial path.  Running sums: a sum over the lane's 4
 //    tokens, a DPP prefix scan over the 16 lanes of a row, and shuffles for
 //    the tile totals.  The next chunk's raw q or k, gates and values are
 //    loaded straight into registers (range-checked buffer loads: rows past
@@ -93,13 +95,7 @@ struct Cfg {
 //   6      F_31 = e^{B_2 - B_1}
 //   7..9   E_I = e^{B_{I-1}} for I = 1..3 (inter-chunk read)
 constexpr int kFRows = 10;
-template <int I, int J>
-constexpr int frow() {
-    if constexpr (I == J) return I;
-    else if constexpr (I == 2 && J == 0) return 4;
-    else if constexpr (I == 3 && J == 0) return 5;
-    else return 6;  // (3, 1)
-}
+constexpr int frow(int I, int J) { return I == J ? I : (I == 2 && J == 0) ? 4 : (I == 3 && J == 0) ? 5 : 6; }
 
 // Buffer sets of folded operands: two at dk = 64, so that the next chunk is
 // folded while the current one's products run; one at dk = 128 (LDS).
@@ -207,13 +203,24 @@ __device__ __forceinline__ float row_scan16(float x) {
     return x;
 }
 
+// 4 output values at byte offset off of a chunk's range-checked output
+// resource: rows past the chunk's end are dropped without a branch.
 template <bool BF>
-__device__ __forceinline__ void store4(char* p, const f32x4& o) {
-    if constexpr (BF) *reinterpret_cast<u16x4*>(p) = cvt4_bf16(o);
-    else *reinterpret_cast<f32x4*>(p) = o;
+__device__ __forceinline__ void bstore4(__amdgpu_buffer_rsrc_t r, unsigned off, const f32x4& o) {
+    if constexpr (BF) bstore8(r, off, cvt4_bf16(o));
+    else bstore16(r, off, o);
 }
 
 __device__ __forceinline__ f32x4 lds4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// The lane's index, hidden from loop-invariant code motion: re-issued in every
+// chunk step, it keeps the compiler from hoisting each LDS address of the
+// products out of the chunk loop (one register each for the whole walk); the
+// addresses then share a base register per array and immediate offsets.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 __device__ __forceinline__ void sts4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 
 // e^x as 2^(x log2 e) on v_exp_f32 (about 1 ulp).  Results below the normal
@@ -228,16 +235,27 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     constexpr int QS = Cf::QS, CS = Cf::CS, KT = Cf::KT, NTILE = Cf::NTILE;
     constexpr int CPT = Cf::CPT, NQ = DK / 4, NB = nbuf<DK>();
     constexpr int ESZ = BF ? 2 : 4;
-    constexpr bool QW = W8 < 4;         // folds queries and stages values (walk); stages values (state-only pass)
+    constexpr bool QW = W8 < 4;         // waves 0-3
     constexpr bool OW = !SO && QW;      // output wave: query tile W8
     constexpr Split SP = make_split<DK, NT>();
     constexpr int TF = SO ? W8 * (NTILE / 8) : (OW ? 0 : SP.first[W8 - 4]);
     constexpr int TN = SO ? NTILE / 8 : (OW ? 0 : SP.cnt[W8 - 4]);
     constexpr int W = W8 & 3;
-    constexpr bool FOLDX = !(SO && QW);  // waves that fold q or k (and load gates)
+    // Fold roles in the walk: at dk = 64 the channel / value-column slice W of
+    // q and v is folded by O-wave W for W = 0, 1 and by S-wave W + 4 for
+    // W = 2, 3 (which fold k of the same channels anyway and share the gate
+    // sums), so the two O-waves with the most MFMAs do nothing but products.
+    // At dk = 128 (one buffer set, so no fold overlaps the products, and twice
+    // the raw registers per fold) O-wave W folds q slice W.  The state-only
+    // pass: waves 0-3 stage v, waves 4-7 fold k.
+    constexpr bool LQ = !SO && (DK == 64 ? (W8 == 0 || W8 == 1 || W8 == 6 || W8 == 7) : QW);  // folds q
+    constexpr bool LK = !QW;                                               // folds k
+    constexpr bool LV = SO ? QW : LQ;                                      // stages v
+    constexpr bool LG = LQ || LK;                                          // loads gates
     const int T = a.T, DV = a.dv;
     const int l = threadIdx.x & 63, l16 = l & 15, g = l >> 4;
-    const char* xh = static_cast<const char*>(QW ? a.q : a.k) + static_cast<long long>(bh) * T * DK * ESZ;
+    const char* qh = static_cast<const char*>(a.q) + static_cast<long long>(bh) * T * DK * ESZ;
+    const char* kh = static_cast<const char*>(a.k) + static_cast<long long>(bh) * T * DK * ESZ;
     const float* gh = a.lg + static_cast<long long>(bh) * T * DK;
     const char* vh = static_cast<const char*>(a.v) + (static_cast<long long>(bh) * T * DV + nbase) * ESZ;
     char* oh = static_cast<char*>(a.out) + (static_cast<long long>(bh) * T * DV + nbase) * ESZ;
@@ -302,14 +320,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         for (int i = 0; i < EPT; ++i) sm.sc[(col0 + i) * QS + row] = acc[i / 4][i % 4];
     }
 
-    // ---- raw chunk registers.  Lane l of wave W covers token group tg = l % 16
+    // ---- raw chunk registers.  Lane l of wave W8 covers token group tg = l % 16
     // (tokens 4 tg .. 4 tg + 3, tile TT = tg / 4) of channel group cg = l / 16:
-    // channels c0(u) = 16 W + 4 cg + 64 u .. + 3 (q on the O-side, k on the
-    // S-side, and the gates) and value columns 16 W + 4 cg .. + 3 (O-side).  A
-    // channel group's 16 token groups fill one DPP row, so running sums over
-    // the chunk are row scans.
+    // channels c0(u) = 16 W + 4 cg + 64 u .. + 3 (q, k and the gates, as the
+    // wave's roles say) and value columns 16 W + 4 cg .. + 3.  A channel
+    // group's 16 token groups fill one DPP row, so running sums over the chunk
+    // are row scans.
     const int tg = l & 15, cg = l >> 4, TT = tg >> 2;
-    Quad<BF> rx[CPT][4], rv[4];
+    Quad<BF> rq[CPT][4], rk[CPT][4], rv[4];
     f32x4 rgt[CPT][4];
     const int nch = (T + C - 1) / C;
     const int c_begin = seg * a.cps;
@@ -321,21 +339,24 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     // Issued for every step (a chunk past the segment gets a zero-length
     // range and reads zeros), so the compiler's waits see one shape.
     auto load_chunk = [&](int c) {
+        const int tg = opaque(l & 15), cg = opaque(l >> 4);
         const long long t0 = static_cast<long long>(c) * C;
         const int cl = (c < c_end) ? chunk_len(c) : 0;
-        if constexpr (FOLDX) {
-            const auto rsx = make_rsrc(xh + t0 * DK * ESZ, cl * DK * ESZ);
+        if constexpr (LG) {
+            const auto rsq = make_rsrc(qh + t0 * DK * ESZ, cl * DK * ESZ);
+            const auto rsk = make_rsrc(kh + t0 * DK * ESZ, cl * DK * ESZ);
             const auto rsg = make_rsrc(gh + t0 * DK, cl * DK * 4);
 #pragma unroll
             for (int u = 0; u < CPT; ++u)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const unsigned e = static_cast<unsigned>((4 * tg + i) * DK + 16 * W + 4 * cg + 64 * u);
-                    rx[u][i].load(rsx, e * ESZ);
+                    if constexpr (LQ) rq[u][i].load(rsq, e * ESZ);
+                    if constexpr (LK) rk[u][i].load(rsk, e * ESZ);
                     rgt[u][i] = __builtin_bit_cast(f32x4, bload16(rsg, e * 4));
                 }
         }
-        if constexpr (QW) {
+        if constexpr (LV) {
             const auto rsv = make_rsrc(vh + t0 * DV * ESZ, cl * DV * ESZ);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -399,7 +420,8 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
 
     // ---- fold the chunk in the registers into a buffer set
     auto fold = [&](Buf& bf, bool exact) {
-        if constexpr (FOLDX) {
+        const int tg = opaque(l & 15), cg = opaque(l >> 4), TT = tg >> 2;
+        if constexpr (LG) {
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
                 const int c0 = 16 * W + 4 * cg + 64 * u;
@@ -410,10 +432,10 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 const f32x4 boff = (TT == 0) ? zero : (TT == 1) ? B[0] : (TT == 2) ? B[1] : B[2];
                 const f32x4 tI = ((TT == 0) ? B[0] : (TT == 1) ? B[1] : (TT == 2) ? B[2] : B[3]) - boff;
                 const f32x4 bL = B[3];
-                if constexpr (QW) {
+                if constexpr (LQ) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const f32x4 x = rx[u][i].f();
+                        const f32x4 x = rq[u][i].f();
                         f32x4 y;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) y[e] = exact ? x[e] : x[e] * fexp(b[i][e] - boff[e]);
@@ -421,10 +443,11 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                     }
                     if (TT > 0 && (tg & 3) == 0)
                         sts4(&bf.fb[(6 + TT) * DK + c0], f32x4{fexp(boff[0]), fexp(boff[1]), fexp(boff[2]), fexp(boff[3])});
-                } else {
+                }
+                if constexpr (LK) {
                     f32x4 xk[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) xk[i] = rx[u][i].f();
+                    for (int i = 0; i < 4; ++i) xk[i] = rk[u][i].f();
                     if (exact) {
                         // raw k and b^T: the products form every factor on the spot
 #pragma unroll
@@ -469,7 +492,7 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 }
             }
         }
-        if constexpr (QW) {
+        if constexpr (LV) {
             // values: columns 16 W + 4 cg + e of the slice, keys 4 tg .. 4 tg + 3, stored transposed
             f32x4 xv[4];
 #pragma unroll
@@ -481,40 +504,58 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     };
 
     // ---- products of a chunk from buffer set X
+    // Products.  Each runs as one unrolled sequence of groups of 4 MFMAs that
+    // share one 16-byte LDS operand read; every group's operands are read RA
+    // groups ahead (a ring of RA + 1 register sets), so the MFMAs do not wait
+    // on fresh LDS reads.  A scheduling barrier after each group keeps the
+    // compiler from hoisting the whole sequence's reads (and their registers).
+    constexpr int RA = 2;
     auto products = [&](const Buf& bf, long long t0, int clen, bool exact) {
+        const int l16 = opaque(l & 15), g = opaque(l >> 4);
         if constexpr (OW) {
+            constexpr int SG = NQ / 4;  // groups per contraction over the channels
             const int qrow = 16 * W + l16;
             float qo[NQ];  // Q^ of query row qrow, channels NQ g + s (exact path: raw q)
 #pragma unroll
-            for (int s4 = 0; s4 < NQ / 4; ++s4) {
+            for (int s4 = 0; s4 < SG; ++s4) {
                 const f32x4 x = lds4(&bf.qb[qrow * QS + NQ * g + 4 * s4]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) qo[4 * s4 + e] = x[e];
             }
             f32x4 pacc[W + 1];
             if (!exact) {
-                // scores P^T[key 16 J + 4 g + r][query] = K^ (Q^ (.) F_WJ)^T
-                auto tile = [&](auto Jc) {
-                    constexpr int J = decltype(Jc)::value;
-                    pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s4 = 0; s4 < NQ / 4; ++s4) {
-                        const f32x4 kx = lds4(&bf.kb[(16 * J + l16) * QS + NQ * g + 4 * s4]);
-                        f32x4 fx = {1.f, 1.f, 1.f, 1.f};
-                        if constexpr (J != W - 1) fx = lds4(&bf.fb[frow<W, J>() * DK + NQ * g + 4 * s4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) pacc[J] = mfma_f32(kx[e], qo[4 * s4 + e] * fx[e], pacc[J]);
-                    }
+                // scores P^T[key 16 J + 4 g + r][query] = K^ (Q^ (.) F_WJ)^T: group (J, s4)
+                // contracts channels NQ g + 4 s4 .. + 3 of key tile J (F_{W,W-1} = 1 is not read)
+                constexpr int NG = (W + 1) * SG;
+                auto rk = [&](int gi) { return lds4(&bf.kb[(16 * (gi / SG) + l16) * QS + NQ * g + 4 * (gi % SG)]); };
+                auto rf = [&](int gi) {
+                    const int J = gi / SG;
+                    return (J == W - 1) ? f32x4{1.f, 1.f, 1.f, 1.f}
+                                        : lds4(&bf.fb[frow(W, J) * DK + NQ * g + 4 * (gi % SG)]);
                 };
-                tile(std::integral_constant<int, 0>{});
-                if constexpr (W >= 1) tile(std::integral_constant<int, 1>{});
-                if constexpr (W >= 2) tile(std::integral_constant<int, 2>{});
-                if constexpr (W >= 3) tile(std::integral_constant<int, 3>{});
+                f32x4 kr[RA + 1], fr[RA + 1];
+#pragma unroll
+                for (int i = 0; i < RA; ++i) {
+                    kr[i] = rk(i);
+                    fr[i] = rf(i);
+                }
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    if (gi + RA < NG) {
+                        kr[(gi + RA) % (RA + 1)] = rk(gi + RA);
+                        fr[(gi + RA) % (RA + 1)] = rf(gi + RA);
+                    }
+                    const int J = gi / SG, s4 = gi % SG, x = gi % (RA + 1);
+                    if (s4 == 0) pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pacc[J] = mfma_f32(kr[x][e], qo[4 * s4 + e] * fr[x][e], pacc[J]);
+                    __builtin_amdgcn_sched_barrier(0);  // keep the read-ahead distance (and the registers it needs)
+                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) pacc[W][r] = (4 * g + r > l16) ? 0.f : pacc[W][r];
-                if constexpr (W > 0) {  // the inter-chunk read takes Q^ (.) E_W
+                if constexpr (W > 0) {  // the inter-chunk read takes Q^ (.) E_W, E_W = e^{B_{W-1}}
 #pragma unroll
-                    for (int s4 = 0; s4 < NQ / 4; ++s4) {
+                    for (int s4 = 0; s4 < SG; ++s4) {
                         const f32x4 ex = lds4(&bf.fb[(6 + W) * DK + NQ * g + 4 * s4]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) qo[4 * s4 + e] *= ex[e];
@@ -538,39 +579,73 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
 #pragma unroll
                 for (int s = 0; s < NQ; ++s) qo[s] *= fexp(bf.gt[(NQ * g + s) * CS + qrow]);
             }
-            // ---- O^T = S^T Q~^T + V^T P^T per 16-column value tile; rows past the end are not stored
+            // ---- O^T = S^T Q~^T + V^T P^T per 16-column value tile nt: SG groups from the
+            // state copy, then W + 1 from V^T; rows past the chunk's end are dropped
+            constexpr int GPN = SG + W + 1;
+            constexpr int NGO = NT * GPN;
+            auto ro = [&](int gi) {
+                const int nt = gi / GPN, k = gi % GPN;
+                return (k < SG) ? lds4(&sm.sc[(16 * nt + l16) * QS + NQ * g + 4 * k])
+                                : lds4(&bf.vt[(16 * nt + l16) * CS + 16 * (k - SG) + 4 * g]);
+            };
+            const auto rso = make_rsrc(oh + t0 * DV * ESZ, (clen * DV - nbase) * ESZ);
+            f32x4 ar[RA + 1], o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                f32x4 o = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < RA; ++i) ar[i] = ro(i);
 #pragma unroll
-                for (int s4 = 0; s4 < NQ / 4; ++s4) {
-                    const f32x4 sx = lds4(&sm.sc[(16 * nt + l16) * QS + NQ * g + 4 * s4]);
+            for (int gi = 0; gi < NGO; ++gi) {
+                if (gi + RA < NGO) ar[(gi + RA) % (RA + 1)] = ro(gi + RA);
+                const int nt = gi / GPN, k = gi % GPN, x = gi % (RA + 1);
+                if (k == 0) o = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (k < SG) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o = mfma_f32(sx[e], qo[4 * s4 + e], o);
+                    for (int e = 0; e < 4; ++e) o = mfma_f32(ar[x][e], qo[4 * k + e], o);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) o = mfma_f32(ar[x][r], pacc[k - SG][r], o);
                 }
-#pragma unroll
-                for (int J = 0; J <= W; ++J) {
-                    const f32x4 vx = lds4(&bf.vt[(16 * nt + l16) * CS + 16 * J + 4 * g]);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) o = mfma_f32(vx[r], pacc[J][r], o);
-                }
-                if (qrow < clen) store4<BF>(oh + ((t0 + qrow) * DV + 16 * nt + 4 * g) * ESZ, o);
+                if (k == GPN - 1)
+                    bstore4<BF>(rso, static_cast<unsigned>((qrow * DV + 16 * nt + 4 * g) * ESZ), o);
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
             // ---- S = diag(e^{b_L}) S + K'^T V for this wave's tiles; lane group g contracts keys 16 g ..
+            if (!exact) {
+                if constexpr (TN > 0) {
+                    // group (t, s4): keys 16 g + 4 s4 .. + 3 of state tile t
+                    constexpr int NG = 4 * TN;
+                    auto ra = [&](int gi) {
+                        const int m = (TF + gi / 4) % KT;
+                        return lds4(&bf.gt[(16 * m + l16) * CS + 16 * g + 4 * (gi % 4)]);
+                    };
+                    auto rb = [&](int gi) {
+                        const int n = (TF + gi / 4) / KT;
+                        return lds4(&bf.vt[(16 * n + l16) * CS + 16 * g + 4 * (gi % 4)]);
+                    };
 #pragma unroll
-            for (int t = 0; t < TN; ++t) {
-                const int m = (TF + t) % KT, n = (TF + t) / KT;
-                if (!exact) {
-                    sacc[t] *= lds4(&bf.bl[16 * m + 4 * g]);
+                    for (int t = 0; t < TN; ++t) sacc[t] *= lds4(&bf.bl[16 * ((TF + t) % KT) + 4 * g]);
+                    f32x4 xr[RA + 1], yr[RA + 1];
 #pragma unroll
-                    for (int s4 = 0; s4 < 4; ++s4) {
-                        const f32x4 kx = lds4(&bf.gt[(16 * m + l16) * CS + 16 * g + 4 * s4]);
-                        const f32x4 vx = lds4(&bf.vt[(16 * n + l16) * CS + 16 * g + 4 * s4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) sacc[t] = mfma_f32(kx[e], vx[e], sacc[t]);
+                    for (int i = 0; i < RA; ++i) {
+                        xr[i] = ra(i);
+                        yr[i] = rb(i);
                     }
-                } else {
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi) {
+                        if (gi + RA < NG) {
+                            xr[(gi + RA) % (RA + 1)] = ra(gi + RA);
+                            yr[(gi + RA) % (RA + 1)] = rb(gi + RA);
+                        }
+                        const int t = gi / 4, x = gi % (RA + 1);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) sacc[t] = mfma_f32(xr[x][e], yr[x][e], sacc[t]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < TN; ++t) {
+                    const int m = (TF + t) % KT, n = (TF + t) / KT;
                     // exact path: K' = k e^{b_L - b_j} and e^{b_L} from raw k and b^T
                     const int ch = 16 * m + l16;
                     const float bLc = bf.gt[ch * CS + C - 1];
@@ -586,6 +661,7 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                             sacc[t] = mfma_f32(kp, vx[e], sacc[t]);
                         }
                     }
+                    __builtin_amdgcn_sched_barrier(0);  // one tile's exponentials in flight at a time
                 }
             }
         }
@@ -619,17 +695,29 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         const long long t0 = static_cast<long long>(c) * C;
         const int clen = chunk_len(c);
         if constexpr (NB == 2) {
-            // fold the next chunk into the other buffer set while this chunk's products run
+            // fold the next chunk into the other buffer set while this chunk's
+            // products run.  On each SIMD one wave starts with MFMAs while the
+            // other folds: O-waves 0 and 1 (whose partners fold keys) take the
+            // products first, O-waves 2 and 3 have no fold.
             const bool ex_next = (c + 1 < c_end) && exact_of(c + 1);
-            if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
-            load_chunk(c + 2);
-            products(sm.op[X], t0, clen, ex_cur);
-            vote(c + 2);       // the gates of chunk c + 2 have arrived by now
+            if constexpr (OW && W < 2) {
+                products(sm.op[X], t0, clen, ex_cur);
+                if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
+                load_chunk(c + 2);
+            } else {
+                if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
+                load_chunk(c + 2);
+                products(sm.op[X], t0, clen, ex_cur);
+            }
             lds_barrier();     // operands of c + 1 written; every read of c's operands and of the state copy done
 #ifdef RET_DEBUG
             lds_poison(&sm.op[X], sizeof(Buf));  // dead until chunk c + 2 is folded into it
 #endif
             write_state_copy();
+            // The gates of chunk c + 2 were loaded before the products, which
+            // have hidden their latency; its flag slot was last read in the
+            // previous step, and the next barrier publishes the vote.
+            vote(c + 2);
             lds_barrier();
             ex_cur = ex_next;
         } else {
