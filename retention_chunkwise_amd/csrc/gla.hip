@@ -410,8 +410,12 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             if (l == 0) sm.flag[c & 1][W] = wbad ? 1 : 0;
         }
     };
+    // Wave-uniform (a scalar), so the fold and the products branch on it
+    // instead of computing both paths and selecting.
     auto exact_of = [&](int c) {
-        return !SO && (sm.flag[c & 1][0] | sm.flag[c & 1][1] | sm.flag[c & 1][2] | sm.flag[c & 1][3]) != 0;
+        if constexpr (SO) return false;
+        const int f = sm.flag[c & 1][0] | sm.flag[c & 1][1] | sm.flag[c & 1][2] | sm.flag[c & 1][3];
+        return __builtin_amdgcn_readfirstlane(f) != 0;
     };
 
     f32x4 ltot[CPT];  // state-only pass: log-gate totals of this lane's channels over the segment
@@ -430,7 +434,8 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 // B[TT - 1] and B[TT] by selects (TT varies across lanes; no indexed registers)
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
                 const f32x4 boff = (TT == 0) ? zero : (TT == 1) ? B[0] : (TT == 2) ? B[1] : B[2];
-                const f32x4 tI = ((TT == 0) ? B[0] : (TT == 1) ? B[1] : (TT == 2) ? B[2] : B[3]) - boff;
+                const f32x4 bI = (TT == 0) ? B[0] : (TT == 1) ? B[1] : (TT == 2) ? B[2] : B[3];
+                const f32x4 tI = bI - boff;
                 const f32x4 bL = B[3];
                 if constexpr (LQ) {
 #pragma unroll
@@ -456,21 +461,25 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                         for (int e = 0; e < 4; ++e)
                             sts4(&bf.gt[(c0 + e) * CS + 4 * tg], f32x4{b[0][e], b[1][e], b[2][e], b[3][e]});
                     } else {
+                        // K^ = k e^{t_I - cum_j}, and K' = k e^{b_L - b_j} = K^ e^{b_L - B_I}
+                        // (b_L - B_I: the gates of the tiles after token j's, <= 0; when it
+                        // underflows, K' is below 1e-38 |k| and nothing is lost)
+                        f32x4 kh[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) kh[i][e] = xk[i][e] * fexp(tI[e] - (b[i][e] - boff[e]));
                         if constexpr (!SO) {
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                f32x4 y;
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) y[e] = xk[i][e] * fexp(tI[e] - (b[i][e] - boff[e]));
-                                sts4(&bf.kb[(4 * tg + i) * QS + c0], y);
-                            }
+                            for (int i = 0; i < 4; ++i) sts4(&bf.kb[(4 * tg + i) * QS + c0], kh[i]);
                         }
-                        // K' = k e^{b_L - b_j}, stored transposed
+                        f32x4 after;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) after[e] = fexp(bL[e] - bI[e]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             sts4(&bf.gt[(c0 + e) * CS + 4 * tg],
-                                 f32x4{xk[0][e] * fexp(bL[e] - b[0][e]), xk[1][e] * fexp(bL[e] - b[1][e]),
-                                       xk[2][e] * fexp(bL[e] - b[2][e]), xk[3][e] * fexp(bL[e] - b[3][e])});
+                                 f32x4{kh[0][e] * after[e], kh[1][e] * after[e], kh[2][e] * after[e], kh[3][e] * after[e]});
                     }
                     if ((tg & 3) == 0) {
                         if constexpr (SO) {
