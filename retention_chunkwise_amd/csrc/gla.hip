@@ -42,11 +42,10 @@
 //  - Folding: lane l of wave w covers tokens 4 (l % 16) .. + 3 (in tile
 //    (l % 16) / 4) of the 4 channels 16 (w % 4) + 4 (l / 16) .. + 3 (+ 64 for
 //    dk = 128), loaded as 16-byte (bf16: 8-byte) runs.  Waves 4-7 fold the
-//    keys.  The queries (and the same 4 value columns of the slice over the
-//    same tokens) of channel slice w are folded by wave w, except at dk = 64
-//    where slices 2 and 3 go to waves 6 and 7, which share the gate sums with
-//    their own key fold: O-waves 2 and 3, which issue the most MFMAs, then
-//    carry no fold on their serial path.  Running sums: a sum over the lane's 4
+//    keys.  At dk = 64 they also fold the queries and stage the same 4 value
+//    columns of their channel slice over the same tokens, sharing one set of
+//    gate sums, and waves 0-3 do nothing but products; at dk = 128 wave w
+//    folds query slice w and stages value slice w.  Running sums: a sum over the lane's 4
 //    tokens, a DPP prefix scan over the 16 lanes of a row, and shuffles for
 //    the tile totals.  The next chunk's raw q or k, gates and values are
 //    loaded straight into registers (range-checked buffer loads: rows past
@@ -75,7 +74,10 @@ using namespace ::ret::kc;
 
 constexpr int kThreads = 512;
 constexpr int C = 64;
-constexpr float kTileBound = -80.f;  // F_II = e^{-t_I} <= e^{80} = 5.5e34
+constexpr float kLog2e = 1.4426950408889634f;
+// Gate sums are kept in log2 units (log-gate times log2 e), so every factor is
+// one v_exp_f32.  F_II = 2^{-t_I} <= 2^{80 log2 e} = e^{80} = 5.5e34.
+constexpr float kTileBound = -80.f * kLog2e;
 
 template <int DK, int NT>
 struct Cfg {
@@ -223,10 +225,10 @@ __device__ __forceinline__ int opaque(int x) {
 }
 __device__ __forceinline__ void sts4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 
-// e^x as 2^(x log2 e) on v_exp_f32 (about 1 ulp).  Results below the normal
-// range flush to zero: every factor here is a decay or a product with one,
-// and a factor under 1e-38 contributes nothing at fp32 precision.
-__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// 2^x on v_exp_f32 (about 1 ulp), x a gate sum in log2 units.  Results below
+// the normal range flush to zero: every factor here is a decay or a product
+// with one, and a factor under 1e-38 contributes nothing at fp32 precision.
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <bool BF, int DK, int NT, int W8, bool SO>
 __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh, int seg, int nbase) {
@@ -241,14 +243,13 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     constexpr int TF = SO ? W8 * (NTILE / 8) : (OW ? 0 : SP.first[W8 - 4]);
     constexpr int TN = SO ? NTILE / 8 : (OW ? 0 : SP.cnt[W8 - 4]);
     constexpr int W = W8 & 3;
-    // Fold roles in the walk: at dk = 64 the channel / value-column slice W of
-    // q and v is folded by O-wave W for W = 0, 1 and by S-wave W + 4 for
-    // W = 2, 3 (which fold k of the same channels anyway and share the gate
-    // sums), so the two O-waves with the most MFMAs do nothing but products.
-    // At dk = 128 (one buffer set, so no fold overlaps the products, and twice
-    // the raw registers per fold) O-wave W folds q slice W.  The state-only
-    // pass: waves 0-3 stage v, waves 4-7 fold k.
-    constexpr bool LQ = !SO && (DK == 64 ? (W8 == 0 || W8 == 1 || W8 == 6 || W8 == 7) : QW);  // folds q
+    // Fold roles in the walk: at dk = 64 S-wave W + 4 folds the channel /
+    // value-column slice W of q, k and v, sharing one set of gate sums, and
+    // the O-waves do nothing but products (fp32 MFMAs do not overlap VALU work
+    // on the same SIMD, so every gate scan done twice costs its full time).
+    // At dk = 128 (twice the raw registers per fold) O-wave W folds q slice W.
+    // The state-only pass: waves 0-3 stage v, waves 4-7 fold k.
+    constexpr bool LQ = !SO && (DK == 64 ? !QW : QW);  // folds q
     constexpr bool LK = !QW;                                               // folds k
     constexpr bool LV = SO ? QW : LQ;                                      // stages v
     constexpr bool LG = LQ || LK;                                          // loads gates
@@ -276,7 +277,10 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             }
         }
     };
-    if constexpr (!SO) {
+    // Run after the first chunk's loads are issued, so that their latency and
+    // the prologue's overlap.
+    auto prologue = [&]() {
+        if constexpr (SO) return;
         // ---- the state entering the segment, by every thread of the workgroup:
         //   S_in = sum_{j<seg} diag(exp(L_{j+1} + ... + L_{seg-1})) dS_j
         // (all exponents <= 0), newest segment first.  Thread t takes EPT
@@ -309,7 +313,7 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 }
 #pragma unroll
                 for (int b = 0; b < SB; ++b) {
-                    const float wgt = fexp(esum);
+                    const float wgt = fexp2(esum);
 #pragma unroll
                     for (int v4 = 0; v4 < V4; ++v4) acc[v4] += wgt * x[b][v4];
                     esum += L[b];
@@ -318,7 +322,7 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         }
 #pragma unroll
         for (int i = 0; i < EPT; ++i) sm.sc[(col0 + i) * QS + row] = acc[i / 4][i % 4];
-    }
+    };
 
     // ---- raw chunk registers.  Lane l of wave W8 covers token group tg = l % 16
     // (tokens 4 tg .. 4 tg + 3, tile TT = tg / 4) of channel group cg = l / 16:
@@ -363,19 +367,30 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 rv[i].load(rsv, static_cast<unsigned>(((4 * tg + i) * DV + 16 * W + 4 * cg) * ESZ));
         }
     };
-    // Gate sums of this lane's 4 channels: b[i] at its tokens (gates above 0
-    // taken as 0, NaN kept) and the tile boundary sums B[0..3] (B[3] = b_L).
-    auto gate_sums = [&](int u, f32x4 (&b)[4], f32x4 (&B)[4]) {
-        f32x4 run = {0.f, 0.f, 0.f, 0.f};
+    // The log-gates of this lane's 4 channels, taken as 0 above 0 (NaN kept)
+    // and scaled to log2 units, summed over the lane's 4 tokens in place:
+    // rgt[u][i] becomes the sum up to and including token i.  The key waves do
+    // it when they vote on the chunk, the other folding waves in gate_sums.
+    constexpr bool PRESUM = !SO && !QW;
+    auto lane_sums = [&](int u) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < 4; ++e) {
+            float run = 0.f;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
+            for (int i = 0; i < 4; ++i) {
                 const float x = rgt[u][i][e];
-                run[e] += (x > 0.f) ? 0.f : x;
+                run = __builtin_fmaf((x > 0.f) ? 0.f : x, kLog2e, run);
+                rgt[u][i][e] = run;
             }
-            b[i] = run;
         }
+    };
+    // Gate sums of this lane's 4 channels over the chunk: b[i] at its tokens
+    // and the tile boundary sums B[0..3] (B[3] = b_L).
+    auto gate_sums = [&](int u, f32x4 (&b)[4], f32x4 (&B)[4]) {
+        if constexpr (!PRESUM) lane_sums(u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = rgt[u][i];
+        const f32x4 run = rgt[u][3];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float incl = row_scan16(run[e]);
@@ -389,15 +404,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     // Exact-path vote for the chunk now in the registers (key waves only): a
     // 16-token tile whose gate sum in some channel is below the bound, or NaN.
     auto vote = [&](int c) {
-        if constexpr (!SO && !QW) {
+        if constexpr (PRESUM) {
             bool bad = false;
 #pragma unroll
             for (int u = 0; u < CPT; ++u) {
+                lane_sums(u);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float run = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) run += fminf(rgt[u][i][e], 0.f) + (rgt[u][i][e] - rgt[u][i][e]);
+                    const float run = rgt[u][3][e];
                     // the tile's sum: this lane and the next three token groups
                     float tile = run;
                     tile += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, run), 0x101, 0xf, 0xf, true));
@@ -443,11 +457,11 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                         const f32x4 x = rq[u][i].f();
                         f32x4 y;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) y[e] = exact ? x[e] : x[e] * fexp(b[i][e] - boff[e]);
+                        for (int e = 0; e < 4; ++e) y[e] = exact ? x[e] : x[e] * fexp2(b[i][e] - boff[e]);
                         sts4(&bf.qb[(4 * tg + i) * QS + c0], y);
                     }
                     if (TT > 0 && (tg & 3) == 0)
-                        sts4(&bf.fb[(6 + TT) * DK + c0], f32x4{fexp(boff[0]), fexp(boff[1]), fexp(boff[2]), fexp(boff[3])});
+                        sts4(&bf.fb[(6 + TT) * DK + c0], f32x4{fexp2(boff[0]), fexp2(boff[1]), fexp2(boff[2]), fexp2(boff[3])});
                 }
                 if constexpr (LK) {
                     f32x4 xk[4];
@@ -468,14 +482,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) kh[i][e] = xk[i][e] * fexp(tI[e] - (b[i][e] - boff[e]));
+                            for (int e = 0; e < 4; ++e) kh[i][e] = xk[i][e] * fexp2(tI[e] - (b[i][e] - boff[e]));
                         if constexpr (!SO) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i) sts4(&bf.kb[(4 * tg + i) * QS + c0], kh[i]);
                         }
                         f32x4 after;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) after[e] = fexp(bL[e] - bI[e]);
+                        for (int e = 0; e < 4; ++e) after[e] = fexp2(bL[e] - bI[e]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             sts4(&bf.gt[(c0 + e) * CS + 4 * tg],
@@ -486,17 +500,17 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                             if (TT == 0) ltot[u] += bL;
                         } else {
                             if (!exact)
-                                sts4(&bf.fb[TT * DK + c0], f32x4{fexp(-tI[0]), fexp(-tI[1]), fexp(-tI[2]), fexp(-tI[3])});
+                                sts4(&bf.fb[TT * DK + c0], f32x4{fexp2(-tI[0]), fexp2(-tI[1]), fexp2(-tI[2]), fexp2(-tI[3])});
                             if (TT == 0) {
                                 const f32x4 d1 = B[1] - B[0], d2 = B[2] - B[0];
-                                sts4(&bf.fb[4 * DK + c0], f32x4{fexp(d1[0]), fexp(d1[1]), fexp(d1[2]), fexp(d1[3])});
-                                sts4(&bf.fb[5 * DK + c0], f32x4{fexp(d2[0]), fexp(d2[1]), fexp(d2[2]), fexp(d2[3])});
+                                sts4(&bf.fb[4 * DK + c0], f32x4{fexp2(d1[0]), fexp2(d1[1]), fexp2(d1[2]), fexp2(d1[3])});
+                                sts4(&bf.fb[5 * DK + c0], f32x4{fexp2(d2[0]), fexp2(d2[1]), fexp2(d2[2]), fexp2(d2[3])});
                             } else if (TT == 1) {
                                 const f32x4 d3 = B[2] - B[1];
-                                sts4(&bf.fb[6 * DK + c0], f32x4{fexp(d3[0]), fexp(d3[1]), fexp(d3[2]), fexp(d3[3])});
+                                sts4(&bf.fb[6 * DK + c0], f32x4{fexp2(d3[0]), fexp2(d3[1]), fexp2(d3[2]), fexp2(d3[3])});
                             }
                         }
-                        if (TT == 0) sts4(&bf.bl[c0], f32x4{fexp(bL[0]), fexp(bL[1]), fexp(bL[2]), fexp(bL[3])});
+                        if (TT == 0) sts4(&bf.bl[c0], f32x4{fexp2(bL[0]), fexp2(bL[1]), fexp2(bL[2]), fexp2(bL[3])});
                     }
                 }
             }
@@ -581,12 +595,12 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                         if (j <= qrow) {
                             for (int cc = 0; cc < DK; ++cc)
                                 acc += bf.qb[qrow * QS + cc] * bf.kb[j * QS + cc] *
-                                       fexp(bf.gt[cc * CS + qrow] - bf.gt[cc * CS + j]);
+                                       fexp2(bf.gt[cc * CS + qrow] - bf.gt[cc * CS + j]);
                         }
                         pacc[J][r] = acc;
                     }
 #pragma unroll
-                for (int s = 0; s < NQ; ++s) qo[s] *= fexp(bf.gt[(NQ * g + s) * CS + qrow]);
+                for (int s = 0; s < NQ; ++s) qo[s] *= fexp2(bf.gt[(NQ * g + s) * CS + qrow]);
             }
             // ---- O^T = S^T Q~^T + V^T P^T per 16-column value tile nt: SG groups from the
             // state copy, then W + 1 from V^T; rows past the chunk's end are dropped
@@ -659,14 +673,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                     const int ch = 16 * m + l16;
                     const float bLc = bf.gt[ch * CS + C - 1];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sacc[t][r] *= fexp(bf.gt[(16 * m + 4 * g + r) * CS + C - 1]);
+                    for (int r = 0; r < 4; ++r) sacc[t][r] *= fexp2(bf.gt[(16 * m + 4 * g + r) * CS + C - 1]);
 #pragma unroll
                     for (int s4 = 0; s4 < 4; ++s4) {
                         const f32x4 vx = lds4(&bf.vt[(16 * n + l16) * CS + 16 * g + 4 * s4]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int key = 16 * g + 4 * s4 + e;
-                            const float kp = bf.kb[key * QS + ch] * fexp(bLc - bf.gt[ch * CS + key]);
+                            const float kp = bf.kb[key * QS + ch] * fexp2(bLc - bf.gt[ch * CS + key]);
                             sacc[t] = mfma_f32(kp, vx[e], sacc[t]);
                         }
                     }
@@ -678,10 +692,9 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
 
     // ---- the walk.  Chunk c uses buffer set (c - c_begin) % NB; its exact-path
     // flag was voted when its gates arrived and is kept in a register.
-    if (c_begin < c_end) {
-        load_chunk(c_begin);
-        vote(c_begin);
-    }
+    if (c_begin < c_end) load_chunk(c_begin);
+    prologue();
+    if (c_begin < c_end) vote(c_begin);
     lds_barrier();  // the first vote and the state copy
     if constexpr (!SO && !OW) {
         // this wave's state tiles, from the copy the whole workgroup wrote
@@ -704,20 +717,11 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
         const long long t0 = static_cast<long long>(c) * C;
         const int clen = chunk_len(c);
         if constexpr (NB == 2) {
-            // fold the next chunk into the other buffer set while this chunk's
-            // products run.  On each SIMD one wave starts with MFMAs while the
-            // other folds: O-waves 0 and 1 (whose partners fold keys) take the
-            // products first, O-waves 2 and 3 have no fold.
+            // fold the next chunk into the other buffer set while this chunk's products run
             const bool ex_next = (c + 1 < c_end) && exact_of(c + 1);
-            if constexpr (OW && W < 2) {
-                products(sm.op[X], t0, clen, ex_cur);
-                if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
-                load_chunk(c + 2);
-            } else {
-                if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
-                load_chunk(c + 2);
-                products(sm.op[X], t0, clen, ex_cur);
-            }
+            if (c + 1 < c_end) fold(sm.op[1 - X], ex_next);
+            load_chunk(c + 2);
+            products(sm.op[X], t0, clen, ex_cur);
             lds_barrier();     // operands of c + 1 written; every read of c's operands and of the state copy done
 #ifdef RET_DEBUG
             lds_poison(&sm.op[X], sizeof(Buf));  // dead until chunk c + 2 is folded into it
