@@ -60,9 +60,14 @@
 //    split so that each SIMD (O-wave W and S-wave W + 4) issues the same
 //    number of MFMAs.  The state-only pass splits the state tiles over all 8.
 //  - Two barriers per chunk: after the folded operands are written, and after
-//    the products (then the S-waves refresh the LDS copy of S^T).  Whether the
-//    next chunk needs the exact path is voted on as soon as its gates arrive,
-//    one step ahead.
+//    the products (then the S-waves refresh the LDS copy of S^T).  Whether a
+//    chunk needs the exact path is voted on by the key waves between those two
+//    barriers of the step before the one that folds it (at dk = 64; right
+//    after its products at dk = 128), once its gates have arrived.
+//  - On gfx950 fp32 MFMAs and VALU instructions of the two waves of a SIMD do
+//    not overlap (each SIMD's time is its VALU plus its MFMA time), so the
+//    fold is written for few VALU instructions: gate sums in log2 units,
+//    summed once per lane, one v_exp_f32 per factor.
 #include "internal.h"
 #include "kcommon.h"
 
@@ -250,9 +255,9 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     // At dk = 128 (twice the raw registers per fold) O-wave W folds q slice W.
     // The state-only pass: waves 0-3 stage v, waves 4-7 fold k.
     constexpr bool LQ = !SO && (DK == 64 ? !QW : QW);  // folds q
-    constexpr bool LK = !QW;                                               // folds k
-    constexpr bool LV = SO ? QW : LQ;                                      // stages v
-    constexpr bool LG = LQ || LK;                                          // loads gates
+    constexpr bool LK = !QW;                           // folds k
+    constexpr bool LV = SO ? QW : LQ;                  // stages v
+    constexpr bool LG = LQ || LK;                      // loads gates
     const int T = a.T, DV = a.dv;
     const int l = threadIdx.x & 63, l16 = l & 15, g = l >> 4;
     const char* qh = static_cast<const char*>(a.q) + static_cast<long long>(bh) * T * DK * ESZ;
@@ -550,8 +555,8 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 // scores P^T[key 16 J + 4 g + r][query] = K^ (Q^ (.) F_WJ)^T: group (J, s4)
                 // contracts channels NQ g + 4 s4 .. + 3 of key tile J (F_{W,W-1} = 1 is not read)
                 constexpr int NG = (W + 1) * SG;
-                auto rk = [&](int gi) { return lds4(&bf.kb[(16 * (gi / SG) + l16) * QS + NQ * g + 4 * (gi % SG)]); };
-                auto rf = [&](int gi) {
+                auto k_at = [&](int gi) { return lds4(&bf.kb[(16 * (gi / SG) + l16) * QS + NQ * g + 4 * (gi % SG)]); };
+                auto f_at = [&](int gi) {
                     const int J = gi / SG;
                     return (J == W - 1) ? f32x4{1.f, 1.f, 1.f, 1.f}
                                         : lds4(&bf.fb[frow(W, J) * DK + NQ * g + 4 * (gi % SG)]);
@@ -559,14 +564,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 f32x4 kr[RA + 1], fr[RA + 1];
 #pragma unroll
                 for (int i = 0; i < RA; ++i) {
-                    kr[i] = rk(i);
-                    fr[i] = rf(i);
+                    kr[i] = k_at(i);
+                    fr[i] = f_at(i);
                 }
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     if (gi + RA < NG) {
-                        kr[(gi + RA) % (RA + 1)] = rk(gi + RA);
-                        fr[(gi + RA) % (RA + 1)] = rf(gi + RA);
+                        kr[(gi + RA) % (RA + 1)] = k_at(gi + RA);
+                        fr[(gi + RA) % (RA + 1)] = f_at(gi + RA);
                     }
                     const int J = gi / SG, s4 = gi % SG, x = gi % (RA + 1);
                     if (s4 == 0) pacc[J] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -606,7 +611,7 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             // state copy, then W + 1 from V^T; rows past the chunk's end are dropped
             constexpr int GPN = SG + W + 1;
             constexpr int NGO = NT * GPN;
-            auto ro = [&](int gi) {
+            auto o_at = [&](int gi) {
                 const int nt = gi / GPN, k = gi % GPN;
                 return (k < SG) ? lds4(&sm.sc[(16 * nt + l16) * QS + NQ * g + 4 * k])
                                 : lds4(&bf.vt[(16 * nt + l16) * CS + 16 * (k - SG) + 4 * g]);
@@ -614,10 +619,10 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
             const auto rso = make_rsrc(oh + t0 * DV * ESZ, (clen * DV - nbase) * ESZ);
             f32x4 ar[RA + 1], o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < RA; ++i) ar[i] = ro(i);
+            for (int i = 0; i < RA; ++i) ar[i] = o_at(i);
 #pragma unroll
             for (int gi = 0; gi < NGO; ++gi) {
-                if (gi + RA < NGO) ar[(gi + RA) % (RA + 1)] = ro(gi + RA);
+                if (gi + RA < NGO) ar[(gi + RA) % (RA + 1)] = o_at(gi + RA);
                 const int nt = gi / GPN, k = gi % GPN, x = gi % (RA + 1);
                 if (k == 0) o = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (k < SG) {
@@ -637,11 +642,11 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                 if constexpr (TN > 0) {
                     // group (t, s4): keys 16 g + 4 s4 .. + 3 of state tile t
                     constexpr int NG = 4 * TN;
-                    auto ra = [&](int gi) {
+                    auto kp_at = [&](int gi) {
                         const int m = (TF + gi / 4) % KT;
                         return lds4(&bf.gt[(16 * m + l16) * CS + 16 * g + 4 * (gi % 4)]);
                     };
-                    auto rb = [&](int gi) {
+                    auto v_at = [&](int gi) {
                         const int n = (TF + gi / 4) / KT;
                         return lds4(&bf.vt[(16 * n + l16) * CS + 16 * g + 4 * (gi % 4)]);
                     };
@@ -650,14 +655,14 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
                     f32x4 xr[RA + 1], yr[RA + 1];
 #pragma unroll
                     for (int i = 0; i < RA; ++i) {
-                        xr[i] = ra(i);
-                        yr[i] = rb(i);
+                        xr[i] = kp_at(i);
+                        yr[i] = v_at(i);
                     }
 #pragma unroll
                     for (int gi = 0; gi < NG; ++gi) {
                         if (gi + RA < NG) {
-                            xr[(gi + RA) % (RA + 1)] = ra(gi + RA);
-                            yr[(gi + RA) % (RA + 1)] = rb(gi + RA);
+                            xr[(gi + RA) % (RA + 1)] = kp_at(gi + RA);
+                            yr[(gi + RA) % (RA + 1)] = v_at(gi + RA);
                         }
                         const int t = gi / 4, x = gi % (RA + 1);
 #pragma unroll
@@ -691,7 +696,7 @@ __device__ __forceinline__ void body(const GlaArgs& a, Smem<DK, NT>& sm, int bh,
     };
 
     // ---- the walk.  Chunk c uses buffer set (c - c_begin) % NB; its exact-path
-    // flag was voted when its gates arrived and is kept in a register.
+    // flag is read once the vote is published and then kept in a register.
     if (c_begin < c_end) load_chunk(c_begin);
     prologue();
     if (c_begin < c_end) vote(c_begin);

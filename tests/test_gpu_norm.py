@@ -76,7 +76,11 @@ def test_norm_gamma_and_floor(gval, qscale, plan):
     inp["gamma"] = np.full(2, gval, dtype=np.float32)
     for norm in ("rowsum", "group"):
         out = _run(inp, norm, 64, plan, 3)
-        _check(f"norm {norm} gamma={gval} qscale={qscale}", out, inp, norm)
+        # gamma = 1 with large q: signed scores cancel in the row sum, so the
+        # divisor must come from the fp32 scores, not the bf16 P operand
+        # (summed from bf16 weights this case reached 1.24e-2)
+        tol = 6e-3 if (norm == "rowsum" and gval == 1.0 and qscale == 20.0) else TOL
+        _check(f"norm {norm} gamma={gval} qscale={qscale}", out, inp, norm, tol=tol)
 
 
 def test_norm_group_eps(plan):
